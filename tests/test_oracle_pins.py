@@ -1,0 +1,442 @@
+"""Pins for the CPU oracle: hand-derived trees, closed forms, brute force,
+exact rationals, the CART special case and invariants.
+
+None of the expected values below come from the oracle itself or from the GPU
+path: they are hand-derived (tests/golden), exact rational arithmetic over row
+sets, a textbook CART written out here, or sklearn.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+
+
+def _params(d):
+    return oracle.make_params(**d)
+
+
+def _frac(pair):
+    return Fraction(pair[0], pair[1])
+
+
+def _traverse(tree, row):
+    v = 0
+    while not (tree[v]["flags"] & oracle.LEAF):
+        f = int(tree[v]["feature"])
+        v = int(tree[v]["left"]) if int(row[f]) <= int(tree[v]["threshold_bin"]) else int(tree[v]["right"])
+    return v
+
+
+def _node_rows(tree, bins):
+    """Row set of every node, by routing each row down the tree (not via the oracle's partition)."""
+    n_nodes = len(tree)
+    rows = {v: [] for v in range(n_nodes)}
+    for i in range(bins.shape[0]):
+        v = 0
+        rows[0].append(i)
+        while not (tree[v]["flags"] & oracle.LEAF):
+            f = int(tree[v]["feature"])
+            v = int(tree[v]["left"]) if int(bins[i, f]) <= int(tree[v]["threshold_bin"]) else int(tree[v]["right"])
+            rows[v].append(i)
+    return rows
+
+
+def _run_golden(path):
+    with open(path) as fh:
+        gd = json.load(fh)
+    inp = gd["inputs"]
+    bins = np.array(inp["bins"], dtype=np.uint8)
+    label = np.array(inp["label"], dtype=np.float32)
+    p = _params(inp["params"])
+    r = oracle.train(bins, inp["n_bins"], label, p, 1, base_score=inp["base_score"], dump_tree=0)
+    return gd, r
+
+
+@pytest.mark.parametrize("name", ["example_a.json", "example_d.json"])
+def test_hand_trees_node_by_node(golden_dir, name):
+    gd, r = _run_golden(os.path.join(golden_dir, name))
+    exp = gd["expected"]
+    tree = r["nodes"][0]
+    assert int(r["n_nodes"][0]) == len(exp["nodes"])
+    assert int(r["scale"][0]) == exp["scale"]
+    for v, e in enumerate(exp["nodes"]):
+        nd = tree[v]
+        assert int(nd["feature"]) == e["feature"]
+        assert int(nd["threshold_bin"]) == e["threshold_bin"]
+        assert int(nd["left"]) == e["left"]
+        assert int(nd["right"]) == e["right"]
+        assert bool(nd["flags"] & oracle.LEAF) == e["leaf"]
+        if e["leaf"]:
+            want = _frac(e["leaf_value_exact"])
+            got = float(nd["leaf_value"])
+            # one IEEE division of exact operands: the correctly rounded value
+            assert got == float(want)
+            if e.get("leaf_value_negative_zero"):
+                assert got == 0.0 and math.copysign(1.0, got) < 0
+        else:
+            want = _frac(e["gain_exact"])
+            assert abs(Fraction(float(nd["gain"])) - want) <= abs(want) * Fraction(1, 2**50)
+    if "root_gain_fp64_hex" in exp:
+        assert float(tree[0]["gain"]).hex() == exp["root_gain_fp64_hex"]
+    for i, pe in enumerate(exp["pred_exact"]):
+        assert r["pred"][i] == float(_frac(pe))
+    for i in exp.get("pred_positive_zero_rows", []):
+        assert math.copysign(1.0, r["pred"][i]) > 0
+
+
+def test_tie_rules(golden_dir):
+    with open(os.path.join(golden_dir, "ties.json")) as fh:
+        gd = json.load(fh)
+    for case in gd["cases"]:
+        bins = np.array(case["bins"], dtype=np.uint8)
+        label = np.array(case["label"], dtype=np.float32)
+        r = oracle.train(bins, case["n_bins"], label, _params(case["params"]), 1)
+        root = r["nodes"][0][0]
+        assert int(root["feature"]) == case["expected_root"]["feature"], case["name"]
+        assert int(root["threshold_bin"]) == case["expected_root"]["threshold_bin"], case["name"]
+
+
+def _round_half_even(x: Fraction) -> int:
+    return round(x)  # Fraction.__round__ rounds half to even
+
+
+def test_gradient_grid_closed_form():
+    # n = 5 -> L = 3; max |g| = 0.75 = 0.75 * 2^0 -> e = 0 -> S = 49
+    pred = np.array([0.1, 0.2, -0.3, 0.75, 0.0])
+    label = np.zeros(5, dtype=np.float32)
+    k, S, _ = oracle.gradient_grid(pred, label)
+    assert S == 49
+    for i in range(5):
+        assert int(k[i]) == _round_half_even(Fraction(float(pred[i])) * 2**49)
+    # a half-way case: g0 = 1 + 2^-52 (e = 1), n = 2 (L = 1) -> S = 50,
+    # g0 * 2^50 = 2^50 + 2^-2 -> 2^50; g1 = 3 * 2^-51 -> 3/2 * 1 -> ties to 2
+    pred = np.array([1.0 + 2.0**-52, 3.0 * 2.0**-51])
+    label = np.zeros(2, dtype=np.float32)
+    k, S, _ = oracle.gradient_grid(pred, label)
+    assert S == 50
+    assert int(k[0]) == 2**50
+    assert int(k[1]) == 2  # 1.5 rounds half to even
+    pred = np.array([1.0 + 2.0**-52, 5.0 * 2.0**-51])
+    k, S, _ = oracle.gradient_grid(pred, label)
+    assert int(k[1]) == 2  # 2.5 rounds half to even
+    # all-zero gradients -> S = 0, k = 0
+    k, S, _ = oracle.gradient_grid(np.ones(3), np.ones(3, dtype=np.float32))
+    assert S == 0 and not k.any()
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 1000, 4097])
+def test_gradient_grid_bound(n):
+    rng = np.random.default_rng(n)
+    pred = rng.normal(size=n) * 10.0
+    label = rng.normal(size=n).astype(np.float32)
+    k, S, g = oracle.gradient_grid(pred, label)
+    L = math.ceil(math.log2(n)) if n > 1 else 0
+    assert oracle.ceil_log2(n) == L
+    assert np.abs(k).max() <= 2 ** (52 - L)
+    # the grid is within half a step of g, and the total stays below 2^52
+    assert np.all(np.abs(np.ldexp(k.astype(np.float64), -S) - g) <= 2.0 ** (-S - 1))
+    assert abs(int(np.sum(k, dtype=object))) <= 2**52
+    # the largest element uses the top of the range (M >= 2^(e-1))
+    assert np.abs(k).max() >= 2 ** (52 - L - 1) - 1
+
+
+def _tiny_cases():
+    out = []
+    for seed, (n, nbins, D, lam, gam, msl, mcw) in enumerate([
+        (40, [3, 5, 2], 3, 1.0, 0.0, 1, 0.0),
+        (64, [4, 4, 4, 4], 3, 0.0, 0.0, 1, 0.0),
+        (57, [7, 2, 3], 4, 2.5, 0.5, 3, 0.0),
+        (80, [5, 6], 3, 1.0, 0.0, 2, 2.0),
+        (33, [2, 2, 2, 2, 2], 4, 1.0, 0.25, 1, 1.0),
+    ]):
+        out.append(dict(seed=100 + seed, n=n, n_bins=nbins, params=dict(
+            max_depth=D, reg_lambda=lam, gamma=gam, min_samples_leaf=msl, min_child_weight=mcw,
+            learning_rate=0.5)))
+    return out
+
+
+@pytest.mark.parametrize("case", _tiny_cases(), ids=lambda c: "seed%d" % c["seed"])
+def test_histograms_bruteforce_and_invariants(case):
+    bins, label, nb = datagen.make_random(case["n"], case["n_bins"], case["seed"], label_kind=1)
+    p = _params(case["params"])
+    r = oracle.train(bins, nb, label, p, 2, dump_tree=1)
+    tree = r["nodes"][1][: r["n_nodes"][1]]
+    k = r["dump_k"]
+    rows = _node_rows(tree, bins)
+    off = oracle.bin_offsets(nb)
+    for v, nd in enumerate(tree):
+        rv = rows[v]
+        assert int(nd["count"]) == len(rv)
+        assert int(nd["gsum_q"]) == sum(int(k[i]) for i in rv)
+        if int(nd["depth"]) >= p.max_depth:
+            continue
+        cnt = r["dump_cnt"][v]
+        gq = r["dump_gq"][v]
+        for f in range(bins.shape[1]):
+            for c in range(int(nb[f])):
+                sel = [i for i in rv if int(bins[i, f]) == c]
+                assert int(cnt[off[f] + c]) == len(sel)
+                assert int(gq[off[f] + c]) == sum(int(k[i]) for i in sel)
+            assert int(cnt[off[f]:off[f + 1]].sum()) == len(rv)
+            assert int(gq[off[f]:off[f + 1]].sum()) == int(nd["gsum_q"])
+        if not (nd["flags"] & oracle.LEAF) and int(tree[nd["left"]]["depth"]) < p.max_depth:
+            lc, rc = int(nd["left"]), int(nd["right"])
+            assert np.array_equal(cnt, r["dump_cnt"][lc] + r["dump_cnt"][rc])
+            assert np.array_equal(gq, r["dump_gq"][lc] + r["dump_gq"][rc])
+    # every row ends in exactly one leaf, and that leaf is the one it routes to
+    for i in range(bins.shape[0]):
+        assert int(r["dump_leaf_of_row"][i]) == _traverse(tree, bins[i])
+
+
+def _exact_gain(GL, HL, GR, HR, GP, HP, lam, gam):
+    def s(G, H):
+        return G * G / (H + lam)
+    return Fraction(1, 2) * (s(GL, HL) + s(GR, HR) - s(GP, HP)) - gam
+
+
+@pytest.mark.parametrize("case", _tiny_cases(), ids=lambda c: "seed%d" % c["seed"])
+def test_split_choice_against_exact_rationals(case):
+    """Brute force over every (feature, bin), splitting the rows directly."""
+    bins, label, nb = datagen.make_random(case["n"], case["n_bins"], case["seed"], label_kind=1)
+    p = _params(case["params"])
+    r = oracle.train(bins, nb, label, p, 1, dump_tree=0)
+    tree = r["nodes"][0][: r["n_nodes"][0]]
+    S = int(r["scale"][0])
+    # labels are multiples of 1/8 below 8 in magnitude and pred = 0, so the grid is exact
+    g = [Fraction(-float(x)) for x in label]
+    assert all(Fraction(int(kk), 2**S) == gi for kk, gi in zip(r["dump_k"], g))
+    lam, gam = Fraction(p.reg_lambda), Fraction(p.gamma)
+    rows = _node_rows(tree, bins)
+    for v, nd in enumerate(tree):
+        if int(nd["depth"]) >= p.max_depth:
+            continue
+        rv = rows[v]
+        GP, HP = sum(g[i] for i in rv), Fraction(len(rv))
+        cands = []
+        for f in range(bins.shape[1]):
+            for t in range(int(nb[f]) - 1):
+                L = [i for i in rv if int(bins[i, f]) <= t]
+                R = [i for i in rv if int(bins[i, f]) > t]
+                if len(L) < p.min_samples_leaf or len(R) < p.min_samples_leaf:
+                    continue
+                if len(L) < p.min_child_weight or len(R) < p.min_child_weight:
+                    continue
+                if not L or not R:
+                    continue
+                GL = sum(g[i] for i in L)
+                cands.append((_exact_gain(GL, Fraction(len(L)), GP - GL, Fraction(len(R)), GP, HP,
+                                          lam, gam), f, t, len(L)))
+        tol = Fraction(1, 2**40) * (1 + abs(GP * GP))
+        best = max((c[0] for c in cands), default=None)
+        if nd["flags"] & oracle.LEAF:
+            assert best is None or best <= tol, (v, best)
+            continue
+        f, t = int(nd["feature"]), int(nd["threshold_bin"])
+        chosen = [c for c in cands if c[1] == f and c[2] == t]
+        assert chosen, "chosen split is not a valid candidate"
+        assert chosen[0][0] > -tol
+        assert best - chosen[0][0] <= tol
+        assert abs(Fraction(float(nd["gain"])) - chosen[0][0]) <= tol
+        # among candidates whose exact gain is clearly below the best, none may win;
+        # among exact ties with the same partition, the smallest (feature, bin) wins
+        near = [c for c in cands if best - c[0] <= tol]
+        same_part = [c for c in near if c[0] == chosen[0][0] and c[3] == chosen[0][3]]
+        assert (f, t) <= min((c[1], c[2]) for c in same_part)
+
+
+def _cart_fit(X, y, rows, depth_left):
+    """P2-style greedy CART on SSE with exact rationals: thresholds from observed
+    values, first best while folding, none for degenerate splits."""
+    ys = [y[i] for i in rows]
+    mean = sum(ys, Fraction(0)) / len(ys)
+    if depth_left == 0:
+        return ("leaf", mean)
+    best = None
+
+    def sse(idx):
+        if not idx:
+            return Fraction(0)
+        m = sum((y[i] for i in idx), Fraction(0)) / len(idx)
+        return sum(((y[i] - m) ** 2 for i in idx), Fraction(0))
+
+    for f in range(X.shape[1]):
+        for thr in sorted(set(int(X[i, f]) for i in rows)):
+            L = [i for i in rows if int(X[i, f]) <= thr]
+            R = [i for i in rows if int(X[i, f]) > thr]
+            if not L or not R:
+                continue
+            sc = sse(L) + sse(R)
+            if best is None or sc < best[0]:
+                best = (sc, f, thr, L, R)
+    if best is None:
+        return ("leaf", mean)
+    _, f, thr, L, R = best
+    return ("split", f, thr, _cart_fit(X, y, L, depth_left - 1), _cart_fit(X, y, R, depth_left - 1))
+
+
+def _cart_to_bfs(root):
+    out, queue = [], [root]
+    while queue:
+        nxt = []
+        for nd in queue:
+            if nd[0] == "leaf":
+                out.append(("leaf", nd[1]))
+            else:
+                out.append(("split", nd[1], nd[2]))
+                nxt.extend([nd[3], nd[4]])
+        queue = nxt
+    return out
+
+
+@pytest.mark.parametrize("seed", [7, 8, 9])
+def test_cart_special_case(seed):
+    """lambda = 0, gamma = 0, base 0, eta = 1, one tree: gain is half the SSE
+    reduction and the leaf is the mean label, i.e. greedy CART on bins."""
+    rng = np.random.default_rng(seed)
+    n, F, D = 48, 3, 3
+    bins = rng.integers(0, 12, size=(n, F)).astype(np.uint8)
+    label = (rng.integers(-2**12, 2**12, size=n) / 2.0**8).astype(np.float32)
+    y = [Fraction(float(v)) for v in label]
+    cart = _cart_to_bfs(_cart_fit(bins, y, list(range(n)), D))
+    p = oracle.make_params(D, reg_lambda=0.0, gamma=0.0, min_samples_leaf=1, learning_rate=1.0)
+    r = oracle.train(bins, [12] * F, label, p, 1)
+    tree = r["nodes"][0][: r["n_nodes"][0]]
+    assert len(tree) == len(cart)
+    for nd, c in zip(tree, cart):
+        if c[0] == "leaf":
+            assert nd["flags"] & oracle.LEAF
+            assert float(nd["leaf_value"]) == float(c[1])
+        else:
+            assert (int(nd["feature"]), int(nd["threshold_bin"])) == (c[1], c[2])
+
+
+def test_cart_special_case_sklearn():
+    sk = pytest.importorskip("sklearn.tree")
+    rng = np.random.default_rng(3)
+    n, F, D = 200, 4, 4
+    bins = rng.integers(0, 50, size=(n, F)).astype(np.uint8)
+    label = (rng.normal(size=n) * 64).round().astype(np.float32) / np.float32(16)
+    p = oracle.make_params(D, reg_lambda=0.0, gamma=0.0, min_samples_leaf=1, learning_rate=1.0)
+    r = oracle.train(bins, [50] * F, label, p, 1, dump_tree=0)
+    m = sk.DecisionTreeRegressor(max_depth=D, random_state=0).fit(bins.astype(np.float64), label)
+    # same partition of rows into leaves, same leaf means
+    ours = r["dump_leaf_of_row"]
+    theirs = m.apply(bins.astype(np.float64))
+    pairs = set(zip(ours.tolist(), theirs.tolist()))
+    assert len(pairs) == len(set(ours.tolist())) == len(set(theirs.tolist()))
+    np.testing.assert_allclose(r["pred"], m.predict(bins.astype(np.float64)), rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("case", _tiny_cases(), ids=lambda c: "seed%d" % c["seed"])
+def test_leaf_weights_closed_form(case):
+    bins, label, nb = datagen.make_random(case["n"], case["n_bins"], case["seed"], label_kind=1)
+    p = _params(case["params"])
+    r = oracle.train(bins, nb, label, p, 1, dump_tree=0)
+    tree = r["nodes"][0][: r["n_nodes"][0]]
+    leaf = r["dump_leaf_of_row"]
+    for v, nd in enumerate(tree):
+        if not (nd["flags"] & oracle.LEAF):
+            continue
+        idx = np.nonzero(leaf == v)[0]
+        # first tree, base 0: w = -sum(g)/(n + lambda) = sum(label)/(n + lambda),
+        # the label sum is exact (multiples of 1/8), so the FP64 division matches
+        s = float(sum(Fraction(float(label[i])) for i in idx))
+        assert float(nd["leaf_value"]) == s / (len(idx) + p.reg_lambda) or (
+            s == 0.0 and float(nd["leaf_value"]) == 0.0)
+
+
+@pytest.mark.parametrize("k", [1])
+def test_multi_round_predictions_by_traversal(k):
+    bins, label, nb = datagen.make_workload(k)
+    wl = dict(datagen.WORKLOADS[k])
+    p = oracle.make_params(**wl)
+    T = wl["n_trees"]
+    r = oracle.train(bins, nb, label, p, T, keep_pred_per_tree=True)
+    pred = np.zeros(bins.shape[0])
+    for t in range(T):
+        tree = r["nodes"][t][: r["n_nodes"][t]]
+        for i in range(bins.shape[0]):
+            w = float(tree[_traverse(tree, bins[i])]["leaf_value"])
+            pred[i] = pred[i] + (p.learning_rate * w)
+        assert np.array_equal(pred, r["pred_per_tree"][t])
+    assert np.array_equal(pred, r["pred"])
+    # the training loss falls from tree to tree
+    mse = [float(np.mean((r["pred_per_tree"][t] - label) ** 2)) for t in range(T)]
+    assert all(b < a for a, b in zip(mse, mse[1:]))
+
+
+def test_determinism():
+    bins, label, nb = datagen.make_random(3000, [16, 3, 64, 2], 11, label_kind=2)
+    p = oracle.make_params(4, reg_lambda=1.0, gamma=0.1, min_samples_leaf=5, learning_rate=0.3)
+    a = oracle.train(bins, nb, label, p, 4)
+    b = oracle.train(bins, nb, label, p, 4)
+    assert a["nodes"].tobytes() == b["nodes"].tobytes()
+    assert a["pred"].tobytes() == b["pred"].tobytes()
+
+
+def test_sharded_histograms_sum_to_whole():
+    """Integer histograms of row shards add up bit-exactly to the whole."""
+    bins, label, nb = datagen.make_random(5000, [8, 32, 2], 5)
+    k, S, _ = oracle.gradient_grid(np.zeros(5000), label)
+    rows = np.arange(5000, dtype=np.int32)
+    whole = oracle.node_histogram(bins, nb, rows, k, S)
+    parts = [oracle.node_histogram(bins, nb, sh, k, S) for sh in np.array_split(rows, 7)]
+    assert np.array_equal(whole[0], sum(pp[0] for pp in parts))
+    assert np.array_equal(whole[1], sum(pp[1] for pp in parts))
+
+
+@pytest.mark.parametrize("bad", [
+    dict(min_samples_leaf=0), dict(min_child_weight=-1.0), dict(reg_lambda=-0.5),
+    dict(gamma=-1e-9), dict(reg_lambda=float("inf")), dict(gamma=float("nan")),
+    dict(learning_rate=float("inf")), dict(max_depth=-1),
+])
+def test_parameter_rules(bad):
+    kw = dict(max_depth=3)
+    kw.update(bad)
+    assert oracle.validate_params(**kw) != 0
+    assert oracle.validate_params(max_depth=3) == 0
+
+
+@pytest.mark.parametrize("case", _tiny_cases(), ids=lambda c: "seed%d" % c["seed"])
+def test_structure_invariants(case):
+    bins, label, nb = datagen.make_random(case["n"], case["n_bins"], case["seed"], label_kind=0)
+    p = _params(case["params"])
+    r = oracle.train(bins, nb, label, p, 3)
+    for t in range(3):
+        tree = r["nodes"][t][: r["n_nodes"][t]]
+        depth_prev = 0
+        expect_child = 1
+        for v, nd in enumerate(tree):
+            assert int(nd["depth"]) >= depth_prev
+            depth_prev = int(nd["depth"])
+            assert int(nd["depth"]) <= p.max_depth
+            if nd["flags"] & oracle.LEAF:
+                assert (int(nd["feature"]), int(nd["left"]), int(nd["right"])) == (-1, -1, -1)
+                continue
+            # breadth-first: children are appended in parent order, left then right
+            assert int(nd["left"]) == expect_child and int(nd["right"]) == expect_child + 1
+            expect_child += 2
+            assert float(nd["gain"]) > 0.0
+            L, R = tree[int(nd["left"])], tree[int(nd["right"])]
+            assert int(L["count"]) + int(R["count"]) == int(nd["count"])
+            for c in (L, R):
+                assert int(c["count"]) >= p.min_samples_leaf
+                assert int(c["count"]) >= p.min_child_weight
+                assert int(c["depth"]) == int(nd["depth"]) + 1
+
+
+def test_depth_zero_is_single_leaf():
+    bins, label, nb = datagen.make_random(100, [4, 4], 1)
+    p = oracle.make_params(0, learning_rate=1.0)
+    r = oracle.train(bins, nb, label, p, 1)
+    assert int(r["n_nodes"][0]) == 1
+    root = r["nodes"][0][0]
+    assert root["flags"] & oracle.LEAF
+    s = float(sum(Fraction(float(x)) for x in label))
+    assert abs(float(root["leaf_value"]) - s / 101.0) <= 1e-12 * (1 + abs(s))
