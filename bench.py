@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the level-wise histogram GBDT hot path on one MI355X.
+
+A step is one boosting iteration: gradients and the fixed-point grid, the
+tree grown level by level (histograms of the smaller children, sibling
+subtraction, split search, stable partition) and the prediction update,
+over the full synthetic workload resident in HBM.
+
+Default workload: 581,012 rows x 54 features (10 Gaussian features in 256
+equal-width bins, 44 binary features with ~5% ones; integer label 1..7),
+depth 10, 100 trees, lambda 1 -- the covtype-shaped depth-10 configuration.
+
+Output: one JSON line on stdout (progress goes to stderr).
+  value      histogram rows*features per second: rows*features of every
+             directly built node (root and smaller children) divided by the
+             summed device time of the histogram kernel over the timed trees
+  roofline   the histogram kernel against the 8 TB/s HBM peak, algorithmic
+             bytes n_v*(F + 4 + 8) + total_bins*12 per built node
+  trees_per_s / ms_per_step  whole boosting steps, host wall clock
+  cpu_baseline  the CPU oracle (single thread) on a bounded sample of trees
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DIAG_HIST = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def built_work(trees, n_features, total_bins, max_depth, min_split):
+    """(built rows, built nodes) summed over trees: root plus the smaller child
+    of every split pair whose larger child can still split."""
+    rows = 0
+    nodes = 0
+    for tr in trees:
+        if max_depth >= 1 and int(tr[0]["count"]) >= min_split:
+            rows += int(tr[0]["count"])
+            nodes += 1
+        for nd in tr:
+            if nd["flags"] & 1:
+                continue
+            L, R = tr[int(nd["left"])], tr[int(nd["right"])]
+            if int(L["depth"]) >= max_depth:
+                continue
+            nl, nr = int(L["count"]), int(R["count"])
+            if max(nl, nr) >= min_split:
+                rows += min(nl, nr)
+                nodes += 1
+    return rows, nodes
+
+
+def cpu_baseline(k, seconds_budget):
+    """The oracle as it stands, single-threaded, on the first trees of the same workload."""
+    import datagen
+    import oracle
+    bins, label, nb = datagen.make_workload(k)
+    wl = dict(datagen.WORKLOADS[k])
+    p = oracle.make_params(**wl)
+    # one tree to size the sample
+    r = oracle.train(bins, nb, label, p, 1)
+    per_tree = max(r["seconds"], 1e-3)
+    n_trees = int(max(1, min(wl["n_trees"], seconds_budget // per_tree)))
+    r = oracle.train(bins, nb, label, p, n_trees)
+    F = bins.shape[1]
+    cells = 0
+    for t in range(n_trees):
+        tr = r["nodes"][t][: r["n_nodes"][t]]
+        cells += int(sum(int(nd["count"]) for nd in tr if int(nd["depth"]) < p.max_depth)) * F
+    return dict(value=cells / r["hist_seconds"], unit="rows*features/s", cores=1, kind="oracle",
+                trees_per_s=n_trees / r["seconds"],
+                sample="first %d of %d trees of the workload, every node's histogram built directly "
+                       "(no subtraction), single thread" % (n_trees, wl["n_trees"]))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed trees (default: the workload's tree count)")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-diag", action="store_true", help="skip the per-kernel timing pass")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import datagen
+    import histogram_split_finding_amd as g
+
+    k = args.workload
+    wl = dict(datagen.WORKLOADS[k])
+    K = args.steps if args.steps is not None else wl["n_trees"]
+    W = args.warmup
+    log("generating workload %d (%s)" % (k, wl["name"]))
+    bins, label, nb = datagen.make_workload(k)
+    n, F = bins.shape
+    fp_bins, fp_label = datagen.fingerprint(bins), datagen.fingerprint(label)
+    ds = g.Dataset(bins, label, nb, "cuda")
+    del bins
+    params = g.make_params(**wl)
+    bst = g.Booster(ds, params)
+    torch.cuda.synchronize()
+    log("dataset on device: %d x %d, %d bins, blocks %d x %d" % (n, F, ds.ft.total_bins,
+                                                                 ds.X.n_blocks, ds.X.block_stride))
+    for _ in range(W):
+        bst.grow_tree()
+    torch.cuda.synchronize()
+    bst.check()
+    log("warmup done (%d trees)" % W)
+
+    nodes_bufs = [torch.zeros(bst.sizes.max_nodes * g.NODE_DTYPE.itemsize, dtype=torch.uint8,
+                              device="cuda") for _ in range(K)]
+    nn_bufs = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        bst.grow_tree(nodes_bufs[i], nn_bufs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    bst.check()
+    log("timed %d trees in %.3f s (%.2f trees/s)" % (K, wall, K / wall))
+
+    min_split = 2 * max(int(params.min_samples_leaf), int(np.ceil(params.min_child_weight)), 1)
+    TB = ds.ft.total_bins
+    out = {
+        "metric": "histogram rows*features/sec (HBM % of peak) + trees/sec at depth-10",
+        "value": None,
+        "unit": "rows*features/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": 1000.0 * wall / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int64",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "rows": n, "features": F, "total_bins": TB,
+                   "max_depth": params.max_depth, "trees": wl["n_trees"],
+                   "learning_rate": params.learning_rate, "reg_lambda": params.reg_lambda,
+                   "gamma": params.gamma, "min_samples_leaf": params.min_samples_leaf,
+                   "min_child_weight": params.min_child_weight,
+                   "bins_fnv1a64": fp_bins, "label_fnv1a64": fp_label},
+        "trees_per_s": K / wall,
+    }
+
+    if not args.no_diag:
+        # second pass: per-kernel device time with events on the library's stream
+        lib = g.load()
+        cap = 64 * (params.max_depth + 4) * K + 64
+        assert lib.gbdt_diag_enable(cap) == 0
+        for i in range(K):
+            bst.grow_tree(nodes_bufs[i], nn_bufs[i])
+        import ctypes
+        kinds = np.zeros(cap, dtype=np.int32)
+        ms = np.zeros(cap, dtype=np.float32)
+        cnt = ctypes.c_int32()
+        rc = lib.gbdt_diag_read(cap, kinds.ctypes.data_as(ctypes.c_void_p),
+                                ms.ctypes.data_as(ctypes.c_void_p), ctypes.byref(cnt))
+        lib.gbdt_diag_disable()
+        assert rc == 0
+        bst.check()
+        kinds, ms = kinds[: cnt.value], ms[: cnt.value]
+        trees = [g.nodes_to_host(nodes_bufs[i], int(nn_bufs[i].item())) for i in range(K)]
+        rows, nbuilt = built_work(trees, F, TB, params.max_depth, min_split)
+        hist_ms = float(ms[kinds == DIAG_HIST].sum())
+        launches = int((kinds == DIAG_HIST).sum())
+        cells = rows * F
+        alg_bytes = rows * (F + 4 + 8) + nbuilt * TB * 12
+        achieved = alg_bytes / (hist_ms * 1e-3) / 1e9
+        out["value"] = cells / (hist_ms * 1e-3)
+        out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                           "kernel": "k_hist", "launches": launches,
+                           "avg_launch_us": 1000.0 * hist_ms / max(launches, 1),
+                           "alg_bytes_per_launch": alg_bytes / max(launches, 1)}
+        names = {1: "grad_max", 2: "grad_q", 3: "plan", 4: "hist", 5: "hist_reduce", 6: "subtract",
+                 7: "find", 8: "tree_init", 9: "level", 10: "partition", 11: "update", 12: "pack"}
+        out["device_ms_per_tree"] = {names.get(int(kk), str(kk)): float(ms[kinds == kk].sum()) / K
+                                     for kk in sorted(set(kinds.tolist()))}
+        out["built_rows_per_tree"] = rows / K
+        log("hist: %d launches, %.3f ms total, %.1f GB/s algorithmic (%.1f%% of 8 TB/s)" % (
+            launches, hist_ms, achieved, 100 * achieved / HBM_PEAK_GBS))
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(k, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

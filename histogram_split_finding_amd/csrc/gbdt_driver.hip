@@ -1,0 +1,397 @@
+// Level-wise tree growth driver: the seven steps of "Module Design: Training
+// Core" (MPSBoost spec), section 6, run on the device without a host round
+// trip per level.  The host enqueues a fixed sequence of launches per level;
+// the level's node lists and counts live in device memory and are written by
+// k_level, so every launch is sized by a static bound and surplus workgroups
+// exit early (the one-sync-per-level idea of the ExaBoost PR, taken to zero
+// host syncs per tree).
+//
+// Per level d: histograms of the listed nodes (root, or the smaller child of
+// every split pair), subtraction for the larger siblings, split search,
+// k_level (breadth-first children, frozen leaves, next level's lists), and
+// the stable partition of the splitting nodes' rows into the other row
+// buffer.  After the last level the prediction update runs over all leaves.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "gbdt.h"
+#include "gbdt_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace gbdt {
+
+struct TreeCtrl {
+  int32_t scale;
+  int32_t n_leaves;
+  int64_t gsum_root;
+  int32_t level_start[GBDT_MAX_DEPTH + 2];
+  int32_t level_count[GBDT_MAX_DEPTH + 2];
+  int32_t n_build[GBDT_MAX_DEPTH + 2];
+  int32_t n_pairs[GBDT_MAX_DEPTH + 2];
+  int32_t n_find[GBDT_MAX_DEPTH + 2];
+  int32_t n_split[GBDT_MAX_DEPTH + 2];
+};
+
+struct ListLayout {
+  int64_t per_type;  // 2^D - 1 words: level d occupies [2^d - 1, 2^(d+1) - 1)
+  int64_t build, find, split, pairs, leaves, total;
+};
+
+static ListLayout list_layout(int32_t D) {
+  ListLayout L{};
+  const int64_t m = (int64_t(1) << D) - 1;
+  L.per_type = m < 1 ? 1 : m;
+  L.build = 0;
+  L.find = L.per_type;
+  L.split = 2 * L.per_type;
+  L.pairs = 3 * L.per_type;
+  L.leaves = 7 * L.per_type;
+  L.total = L.leaves + (int64_t(1) << D) + 4;
+  return L;
+}
+
+__device__ __forceinline__ double leaf_weight(int64_t gsum, int32_t count, int32_t S, double lambda) {
+  const double G = ldexp((double)gsum, -S);
+  const double den = (double)count + lambda;
+  return -G / den;
+}
+
+__device__ __forceinline__ void make_leaf(gbdt_node* nd, double w) {
+  nd->feature = -1;
+  nd->threshold_bin = -1;
+  nd->left = -1;
+  nd->right = -1;
+  nd->leaf_value = w;
+  nd->gain = 0.0;
+  nd->flags = GBDT_NODE_LEAF;
+}
+
+__device__ int32_t blk_scan(int32_t v, int32_t* total, int32_t* sh) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int32_t x = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    int32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[wid] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int w = 0; w < nw; ++w) {
+      int32_t t = sh[w];
+      sh[w] = acc;
+      acc += t;
+    }
+    sh[31] = acc;
+  }
+  __syncthreads();
+  const int32_t r = sh[wid] + x - v;
+  *total = sh[31];
+  __syncthreads();
+  return r;
+}
+
+// Step 1 at the root: node 0 holds every row, lists of level 0.
+__global__ void k_tree_init(gbdt_node* __restrict__ nodes, gbdt_split* __restrict__ splits,
+                            TreeCtrl* __restrict__ tc, int32_t* __restrict__ lists, ListLayout LL,
+                            int32_t n, int64_t min_split, int32_t D, double lambda,
+                            int32_t* __restrict__ n_nodes_out) {
+  for (int i = threadIdx.x; i < GBDT_MAX_DEPTH + 2; i += blockDim.x) {
+    tc->level_start[i] = 0;
+    tc->level_count[i] = 0;
+    tc->n_build[i] = 0;
+    tc->n_pairs[i] = 0;
+    tc->n_find[i] = 0;
+    tc->n_split[i] = 0;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  gbdt_node r;
+  r.feature = -1;
+  r.threshold_bin = -1;
+  r.left = -1;
+  r.right = -1;
+  r.leaf_value = 0.0;
+  r.gain = 0.0;
+  r.flags = 0u;
+  r.depth = 0;
+  r.begin = 0;
+  r.count = n;
+  r.gsum = tc->gsum_root;
+  r.reserved = 0;
+  tc->level_start[0] = 0;
+  tc->level_count[0] = 1;
+  tc->n_leaves = 0;
+  splits[0].valid = 0;
+  if (D == 0) {
+    make_leaf(&r, leaf_weight(r.gsum, n, tc->scale, lambda));
+    lists[LL.leaves] = 0;
+    tc->n_leaves = 1;
+  } else if ((int64_t)n >= min_split) {
+    lists[LL.build] = 0;
+    lists[LL.find] = 0;
+    tc->n_build[0] = 1;
+    tc->n_find[0] = 1;
+  }
+  nodes[0] = r;
+  *n_nodes_out = 1;
+}
+
+// Steps 3-6 bookkeeping for level d, one workgroup: each level-d node either
+// splits (its children are appended breadth-first: left then right, in the
+// order of the parents) or is frozen as a leaf with weight -G/(H+lambda).
+// Writes the lists of level d+1 (nodes to build, sibling pairs, nodes to
+// search), the splitting nodes of level d (for the partition) and appends
+// the new leaves.
+__global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node* __restrict__ nodes,
+                                                gbdt_split* __restrict__ splits,
+                                                TreeCtrl* __restrict__ tc,
+                                                int32_t* __restrict__ lists, ListLayout LL,
+                                                int64_t min_split, double lambda,
+                                                int32_t* __restrict__ n_nodes_out) {
+  __shared__ int32_t sh[32];
+  const int32_t first = tc->level_start[d];
+  const int32_t cnt = tc->level_count[d];
+  const int32_t S = tc->scale;
+  const int32_t leaf_base = tc->n_leaves;
+  const int32_t child_first = first + cnt;
+  const bool last = (d + 1 == D);
+  const int32_t per = (cnt + blockDim.x - 1) / blockDim.x;
+  const int32_t i0 = threadIdx.x * per;
+  int32_t i1 = i0 + per;
+  if (i1 > cnt) i1 = cnt;
+
+  int32_t c_split = 0, c_pair = 0, c_find = 0, c_leaf = 0;
+  for (int32_t i = i0; i < i1; ++i) {
+    const int32_t v = first + i;
+    const gbdt_split s = splits[v];
+    if (s.valid) {
+      const int32_t nl = s.n_left, nr = nodes[v].count - s.n_left;
+      ++c_split;
+      if (last) {
+        c_leaf += 2;
+      } else if ((int64_t)(nl > nr ? nl : nr) >= min_split) {
+        ++c_pair;
+        c_find += ((int64_t)nl >= min_split) + ((int64_t)nr >= min_split);
+      }
+    } else {
+      ++c_leaf;
+    }
+  }
+  int32_t t_split, t_pair, t_find, t_leaf;
+  int32_t r_split = blk_scan(c_split, &t_split, sh);
+  int32_t r_pair = blk_scan(c_pair, &t_pair, sh);
+  int32_t r_find = blk_scan(c_find, &t_find, sh);
+  int32_t r_leaf = blk_scan(c_leaf, &t_leaf, sh);
+
+  const int64_t lvl_off = (int64_t(1) << d) - 1;
+  const int64_t nxt_off = (int64_t(1) << (d + 1)) - 1;
+  int32_t* split_list = lists + LL.split + lvl_off;
+  int32_t* leaves = lists + LL.leaves;
+  int32_t* build_n = lists + LL.build + nxt_off;
+  int32_t* find_n = lists + LL.find + nxt_off;
+  gbdt_pair* pairs_n = reinterpret_cast<gbdt_pair*>(lists + LL.pairs) + nxt_off;
+
+  for (int32_t i = i0; i < i1; ++i) {
+    const int32_t v = first + i;
+    const gbdt_split s = splits[v];
+    gbdt_node nd = nodes[v];
+    if (s.valid) {
+      const int32_t lc = child_first + 2 * r_split;
+      const int32_t rc = lc + 1;
+      const int32_t nl = s.n_left, nr = nd.count - s.n_left;
+      nd.feature = s.feature;
+      nd.threshold_bin = s.threshold_bin;
+      nd.left = lc;
+      nd.right = rc;
+      nd.gain = s.gain;
+      nd.leaf_value = 0.0;
+      nd.flags = 0u;
+      nodes[v] = nd;
+      gbdt_node L, R;
+      L.feature = R.feature = -1;
+      L.threshold_bin = R.threshold_bin = -1;
+      L.left = L.right = R.left = R.right = -1;
+      L.leaf_value = R.leaf_value = 0.0;
+      L.gain = R.gain = 0.0;
+      L.flags = R.flags = 0u;
+      L.depth = R.depth = d + 1;
+      L.begin = nd.begin;
+      L.count = nl;
+      L.gsum = s.g_left;
+      R.begin = nd.begin + nl;
+      R.count = nr;
+      R.gsum = nd.gsum - s.g_left;
+      L.reserved = R.reserved = 0;
+      if (last) {
+        make_leaf(&L, leaf_weight(L.gsum, L.count, S, lambda));
+        make_leaf(&R, leaf_weight(R.gsum, R.count, S, lambda));
+        leaves[leaf_base + r_leaf] = lc;
+        leaves[leaf_base + r_leaf + 1] = rc;
+        r_leaf += 2;
+      } else if ((int64_t)(nl > nr ? nl : nr) >= min_split) {
+        const int32_t sm = (nl <= nr) ? lc : rc;
+        const int32_t lg = (nl <= nr) ? rc : lc;
+        build_n[r_pair] = sm;
+        gbdt_pair pr;
+        pr.parent = v;
+        pr.smaller = sm;
+        pr.larger = lg;
+        pr.pad = 0;
+        pairs_n[r_pair] = pr;
+        ++r_pair;
+        if ((int64_t)nl >= min_split) find_n[r_find++] = lc;
+        if ((int64_t)nr >= min_split) find_n[r_find++] = rc;
+      }
+      nodes[lc] = L;
+      nodes[rc] = R;
+      splits[lc].valid = 0;
+      splits[rc].valid = 0;
+      split_list[r_split] = v;
+      ++r_split;
+    } else {
+      make_leaf(&nd, leaf_weight(nd.gsum, nd.count, S, lambda));
+      nodes[v] = nd;
+      leaves[leaf_base + r_leaf] = v;
+      ++r_leaf;
+    }
+  }
+  if (threadIdx.x == 0) {
+    tc->n_split[d] = t_split;
+    tc->level_start[d + 1] = child_first;
+    tc->level_count[d + 1] = 2 * t_split;
+    if (!last) {
+      tc->n_build[d + 1] = t_pair;
+      tc->n_pairs[d + 1] = t_pair;
+      tc->n_find[d + 1] = t_find;
+    }
+    tc->n_leaves = leaf_base + t_leaf;
+    *n_nodes_out = child_first + 2 * t_split;
+  }
+}
+
+static int64_t min_split_count(const gbdt_params* p, int64_t n) {
+  double mc = std::ceil(p->min_child_weight);
+  int64_t m = p->min_samples_leaf;
+  if (mc > double(n) + 1.0) return 2 * (n + 1);
+  if (int64_t(mc) > m) m = int64_t(mc);
+  if (m < 1) m = 1;
+  return 2 * m;
+}
+
+}  // namespace gbdt
+
+using namespace gbdt;
+
+extern "C" {
+
+int gbdt_grow_sizes(int64_t n_rows, int32_t total_bins, int32_t max_depth, gbdt_grow_sizes_t* out) {
+  if (!out) return fail(GBDT_E_ARG, "out is null");
+  if (max_depth < 0 || max_depth > GBDT_MAX_DEPTH) return fail(GBDT_E_ARG, "max_depth out of range");
+  if (n_rows < 1 || n_rows > 0x7fffffffLL) return fail(GBDT_E_ARG, "n_rows out of range");
+  if (total_bins < 1) return fail(GBDT_E_ARG, "total_bins out of range");
+  out->max_nodes = (int64_t(1) << (max_depth + 1)) - 1;
+  out->hist_slots = (int64_t(1) << max_depth) - 1;
+  if (out->hist_slots < 1) out->hist_slots = 1;
+  out->list_words = list_layout(max_depth).total;
+  out->ctrl_bytes = int64_t((sizeof(TreeCtrl) + 255) & ~size_t(255));
+  out->ws_bytes = int64_t(ws_layout(n_rows, int32_t(1) << max_depth, total_bins).total);
+  return GBDT_OK;
+}
+
+int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* label, double* pred,
+                   const gbdt_params* p, gbdt_node* nodes_out, int32_t* n_nodes_dev,
+                   const gbdt_grow_buffers* b, void* stream) {
+  if (!X || !ft || !label || !pred || !p || !nodes_out || !n_nodes_dev || !b)
+    return fail(GBDT_E_ARG, "null argument");
+  int rc = gbdt_validate_params(p);
+  if (rc) return rc;
+  const int64_t n = X->n_rows;
+  if (n < 1 || n > 0x7fffffffLL) return fail(GBDT_E_ARG, "n_rows out of range");
+  if (ft->n_features != X->n_features) return fail(GBDT_E_SHAPE, "feature table does not match the matrix");
+  if (!b->q || !b->hist_g || !b->hist_cnt || !b->splits || !b->lists || !b->ctrl || !b->ws)
+    return fail(GBDT_E_ARG, "a driver buffer is null");
+  for (int k = 0; k < 2; ++k) {
+    const gbdt_rows& r = b->pp[k];
+    if (!r.X.bins || !r.q || !r.rid) return fail(GBDT_E_ARG, "a row buffer is null");
+    if (r.X.n_rows != n || r.X.row_capacity != X->row_capacity || r.X.n_blocks != X->n_blocks ||
+        r.X.block_stride != X->block_stride || r.X.block_features != X->block_features ||
+        r.X.n_features != X->n_features)
+      return fail(GBDT_E_SHAPE, "row buffers must have the layout of X");
+  }
+  const int32_t D = p->max_depth;
+  gbdt_grow_sizes_t sz;
+  rc = gbdt_grow_sizes(n, ft->total_bins, D, &sz);
+  if (rc) return rc;
+  if (b->ws_bytes < size_t(sz.ws_bytes)) return fail(GBDT_E_ARG, "workspace too small for this tree");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  TreeCtrl* tc = reinterpret_cast<TreeCtrl*>(b->ctrl);
+  const ListLayout LL = list_layout(D);
+  const int64_t min_split = min_split_count(p, n);
+
+  rc = gbdt_compute_gradients(pred, label, n, b->q, &tc->scale, &tc->gsum_root, b->ws, b->ws_bytes,
+                              stream);
+  if (rc) return rc;
+  diag_begin(kDiagTreeInit, s);
+  hipLaunchKernelGGL(k_tree_init, dim3(1), dim3(64), 0, s, nodes_out, b->splits, tc, b->lists, LL,
+                     (int32_t)n, min_split, D, p->reg_lambda, n_nodes_dev);
+  diag_end(s);
+  {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "k_tree_init");
+  }
+
+  gbdt_rows src;
+  src.X = *X;
+  src.q = b->q;
+  src.rid = nullptr;
+  for (int32_t d = 0; d < D; ++d) {
+    const gbdt_rows& dst = b->pp[d & 1];
+    const int64_t lvl_off = (int64_t(1) << d) - 1;
+    const int32_t cap_lvl = int32_t(1) << d;
+    const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
+    const int64_t rows_build = d == 0 ? n : n / 2;
+    rc = gbdt_build_histograms(&src, ft, nodes_out, b->lists + LL.build + lvl_off, &tc->n_build[d],
+                               cap_build, rows_build, b->hist_g, b->hist_cnt, b->ws, b->ws_bytes,
+                               stream);
+    if (rc) return rc;
+    if (d >= 1) {
+      rc = gbdt_subtract_histograms(b->hist_g, b->hist_cnt, ft->total_bins,
+                                    reinterpret_cast<const gbdt_pair*>(b->lists + LL.pairs) + lvl_off,
+                                    &tc->n_pairs[d], cap_build, b->ws, b->ws_bytes, stream);
+      if (rc) return rc;
+    }
+    rc = gbdt_find_best_splits(b->hist_g, b->hist_cnt, ft, nodes_out, b->lists + LL.find + lvl_off,
+                               &tc->n_find[d], cap_lvl, p, &tc->scale, b->splits, b->ws,
+                               b->ws_bytes, stream);
+    if (rc) return rc;
+    diag_begin(kDiagLevel, s);
+    hipLaunchKernelGGL(k_level, dim3(1), dim3(1024), 0, s, d, D, nodes_out, b->splits, tc, b->lists,
+                       LL, min_split, p->reg_lambda, n_nodes_dev);
+    diag_end(s);
+    {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "k_level");
+    }
+    rc = gbdt_partition_rows(&src, &dst, nodes_out, b->splits, b->lists + LL.split + lvl_off,
+                             &tc->n_split[d], cap_lvl, n, b->ws, b->ws_bytes, stream);
+    if (rc) return rc;
+    src = dst;
+  }
+  const int32_t* rid_by_depth[GBDT_MAX_DEPTH + 1];
+  rid_by_depth[0] = nullptr;
+  for (int32_t d = 1; d <= D; ++d) rid_by_depth[d] = b->pp[(d - 1) & 1].rid;
+  rc = gbdt_update_predictions(pred, n, rid_by_depth, D + 1, nodes_out, b->lists + LL.leaves,
+                               &tc->n_leaves, int32_t(1) << D, p->learning_rate, b->ws, b->ws_bytes,
+                               stream);
+  return rc;
+}
+
+}  // extern "C"

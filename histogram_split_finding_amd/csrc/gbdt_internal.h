@@ -1,0 +1,74 @@
+// Internal declarations shared by the HIP translation units of libgbdt.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "gbdt.h"
+
+namespace gbdt {
+
+// Workspace layout.  Offsets are multiples of 256 bytes.
+struct WsCtrl {
+  int32_t err;          // first device-side error code (0 = none)
+  int32_t err_detail;   // call-specific detail (e.g. offending node)
+  uint32_t ticket;      // in-order tile ticket for the partition look-back
+  int32_t plan_total;   // tiles planned by the last planner launch
+  int32_t pad[60];
+};
+static_assert(sizeof(WsCtrl) == 256, "control block is 256 bytes");
+
+constexpr int kGradBlocks = 1024;     // grid of the gradient kernels
+constexpr int kPartTileRows = 2048;   // rows per partition tile
+constexpr int kUpdTileRows = 4096;    // rows per prediction-update tile
+constexpr int kHistMinTileRows = 1024;
+constexpr int kHistTargetTiles = 1024;
+constexpr int kLdsHistBudgetBins = 7936;  // uint64 LDS slots per histogram workgroup (62 KiB)
+
+struct WsLayout {
+  size_t ctrl;        // WsCtrl
+  size_t gpart;       // double[kGradBlocks]
+  size_t prefix;      // int32[max_list + 2]
+  size_t status;      // uint64[status_cap]
+  size_t hpart;       // uint64[hpart_tiles * total_bins]
+  size_t total;
+  int64_t status_cap;
+  int64_t hpart_tiles;
+};
+
+WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins);
+
+// Error plumbing (thread-local text).
+int fail(int code, const std::string& msg);
+int hip_fail(hipError_t e, const char* what);
+
+inline int32_t ceil_log2(int64_t n) {
+  int32_t L = 0;
+  while ((int64_t(1) << L) < n) ++L;
+  return L;
+}
+
+// Fixed-point packing of one histogram cell in LDS: (q << bits) + 1, so the
+// low `bits` bits count rows and the rest sums q.  Exact while a tile holds
+// fewer than 2^bits rows and 2*bits + 52 - ceil(log2 n) <= 63.
+inline int32_t pack_bits_for(int64_t n_rows) {
+  int32_t L = ceil_log2(n_rows < 1 ? 1 : n_rows);
+  int32_t b = (11 + L) / 2;
+  if (b > 24) b = 24;
+  return b;
+}
+
+int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows);
+
+// Per-kernel device timing (the backend's diagnostics): when enabled, every
+// launch of the library is bracketed by two hipEvents on its stream.
+enum DiagKind {
+  kDiagGradMax = 1, kDiagGradQ, kDiagPlan, kDiagHist, kDiagHistReduce, kDiagSubtract, kDiagFind,
+  kDiagTreeInit, kDiagLevel, kDiagPartition, kDiagUpdate, kDiagPack
+};
+void diag_begin(int kind, hipStream_t s);
+void diag_end(hipStream_t s);
+
+}  // namespace gbdt

@@ -1,0 +1,1312 @@
+// HIP kernels (gfx950) and the C ABI of the level-wise histogram GBDT hot
+// path.  The operations are those of "Module Design: Training Core"
+// (MPSBoost spec), sections 2, 3 and 6; see include/gbdt.h for the contract
+// of each entry point.
+//
+// Compiled with -ffp-contract=off: every FP64 expression below is evaluated
+// as written, one IEEE rounding per operation, no fused multiply-add.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "gbdt.h"
+#include "gbdt_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace gbdt {
+
+// ------------------------------------------------------------------ errors --
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return GBDT_E_DEVICE;
+}
+
+#define GBDT_LAUNCH_CHECK(what)                        \
+  do {                                                 \
+    hipError_t e_ = hipGetLastError();                 \
+    if (e_ != hipSuccess) return hip_fail(e_, (what)); \
+  } while (0)
+
+// ------------------------------------------------------------ diagnostics --
+
+struct DiagState {
+  bool enabled = false;
+  int32_t capacity = 0;
+  int32_t count = 0;
+  bool open = false;
+  std::vector<hipEvent_t> ev;  // 2 per record
+  std::vector<int32_t> kind;
+};
+static DiagState g_diag;
+
+void diag_begin(int kind, hipStream_t s) {
+  if (!g_diag.enabled || g_diag.count >= g_diag.capacity) return;
+  g_diag.kind[g_diag.count] = kind;
+  (void)hipEventRecord(g_diag.ev[2 * g_diag.count], s);
+  g_diag.open = true;
+}
+
+void diag_end(hipStream_t s) {
+  if (!g_diag.open) return;
+  (void)hipEventRecord(g_diag.ev[2 * g_diag.count + 1], s);
+  ++g_diag.count;
+  g_diag.open = false;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
+  WsLayout L{};
+  if (n_rows < 1) n_rows = 1;
+  if (max_list < 1) max_list = 1;
+  if (total_bins < 1) total_bins = 1;
+  L.status_cap = (n_rows + kPartTileRows - 1) / kPartTileRows + int64_t(max_list) + 2;
+  L.hpart_tiles = int64_t(kHistTargetTiles) + int64_t(max_list) + 2;
+  size_t off = 0;
+  L.ctrl = off;
+  off = align256(off + sizeof(WsCtrl));
+  L.gpart = off;
+  off = align256(off + sizeof(double) * kGradBlocks);
+  L.prefix = off;
+  off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
+  L.status = off;
+  off = align256(off + sizeof(uint64_t) * size_t(L.status_cap));
+  L.hpart = off;
+  size_t hp = sizeof(uint64_t) * size_t(L.hpart_tiles) * size_t(total_bins);
+  // the setup-time bin census of gbdt_pack_matrix reuses this region
+  size_t census = sizeof(uint32_t) * size_t(GBDT_MAX_FEATURES) * GBDT_MAX_BINS;
+  off = align256(off + (hp > census ? hp : census));
+  L.total = off;
+  return L;
+}
+
+int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows) {
+  const int64_t tmax = (int64_t(1) << pack_bits_for(n_rows)) - 1;
+  int64_t t = (rows_bound + kHistTargetTiles - 1) / kHistTargetTiles;
+  if (t < kHistMinTileRows) t = kHistMinTileRows;
+  if (t > tmax) t = tmax;
+  if (t < 1) t = 1;
+  return int32_t(t);
+}
+
+// ------------------------------------------------------- device helpers --
+
+__device__ __forceinline__ void dev_error(int32_t* err, int code) {
+  atomicCAS(err, 0, code);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_max(double v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Exclusive scan of one int32 per thread across a workgroup of nthreads
+// (multiple of 64, <= 1024).  Returns the exclusive prefix; *total = sum.
+__device__ int32_t block_exclusive_scan(int32_t v, int32_t* total, int32_t* sh /*[32]*/) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int nw = (blockDim.x + 63) >> 6;
+  int32_t x = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    int32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[wid] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int w = 0; w < nw; ++w) {
+      int32_t t = sh[w];
+      sh[w] = acc;
+      acc += t;
+    }
+    sh[31] = acc;
+  }
+  __syncthreads();
+  int32_t res = sh[wid] + x - v;
+  *total = sh[31];
+  __syncthreads();
+  return res;
+}
+
+// Tile lookup: largest j in [0, n) with prefix[j] <= tile (prefix ascending).
+__device__ __forceinline__ int32_t find_tile_owner(const int32_t* prefix, int32_t n, int32_t tile) {
+  int32_t lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int32_t mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int32_t clamp_len(const int32_t* len, int32_t cap) {
+  int32_t n = *len;
+  return n < 0 ? 0 : (n > cap ? cap : n);
+}
+
+// ---------------------------------------------------------------- planner --
+// One workgroup: tiles per listed node (at least one), their exclusive
+// prefix, the total, and (optionally) a cleared look-back status array and
+// ticket for the launch that follows.
+__global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nodes,
+                                               const int32_t* __restrict__ list,
+                                               const int32_t* __restrict__ list_len,
+                                               int32_t list_cap, int32_t tile_rows,
+                                               int32_t max_tiles, int32_t* __restrict__ prefix,
+                                               WsCtrl* __restrict__ ctrl,
+                                               uint64_t* __restrict__ status) {
+  __shared__ int32_t sh[32];
+  int32_t raw = *list_len;
+  if (threadIdx.x == 0 && (raw < 0 || raw > list_cap)) dev_error(&ctrl->err, GBDT_E_SHAPE);
+  const int32_t n = clamp_len(list_len, list_cap);
+  const int32_t per = (n + blockDim.x - 1) / blockDim.x;
+  const int32_t j0 = threadIdx.x * per;
+  int32_t local = 0;
+  for (int32_t j = j0; j < j0 + per && j < n; ++j) {
+    int32_t c = nodes[list[j]].count;
+    if (c < 0) c = 0;
+    local += c == 0 ? 1 : (c + tile_rows - 1) / tile_rows;
+  }
+  int32_t total;
+  int32_t excl = block_exclusive_scan(local, &total, sh);
+  for (int32_t j = j0; j < j0 + per && j < n; ++j) {
+    prefix[j] = excl;
+    int32_t c = nodes[list[j]].count;
+    if (c < 0) c = 0;
+    excl += c == 0 ? 1 : (c + tile_rows - 1) / tile_rows;
+  }
+  if (threadIdx.x == 0) {
+    prefix[n] = total;
+    if (total > max_tiles) dev_error(&ctrl->err, GBDT_E_SHAPE);
+    ctrl->plan_total = total;
+    ctrl->ticket = 0u;
+  }
+  if (status != nullptr) {
+    const int32_t lim = total < max_tiles ? total : max_tiles;
+    for (int32_t t = threadIdx.x; t < lim; t += blockDim.x) status[t] = 0ull;
+  }
+}
+
+// -------------------------------------------------------------- gradients --
+// Pass 1: g_i = pred_i - (double)label_i; per-block max |g| (Training Core
+// section 2; the grid of the fixed-point reading).
+__global__ void __launch_bounds__(256) k_grad_max(const double* __restrict__ pred,
+                                                  const float* __restrict__ label, int64_t n,
+                                                  double* __restrict__ part,
+                                                  int64_t* __restrict__ gsum,
+                                                  WsCtrl* __restrict__ ctrl) {
+  __shared__ double sh[4];
+  double m = 0.0;
+  bool bad = false;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const double g = pred[i] - (double)label[i];
+    if (!isfinite(g)) bad = true;
+    m = fmax(m, fabs(g));
+  }
+  if (bad) dev_error(&ctrl->err, GBDT_E_RANGE);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double r = fmax(fmax(sh[0], sh[1]), fmax(sh[2], sh[3]));
+    part[blockIdx.x] = r;
+    if (blockIdx.x == 0) *gsum = 0;
+  }
+}
+
+// Pass 2: M = max of the partial maxima (every block derives the same S),
+// S = 52 - e - L, q_i = rint(ldexp(g_i, S)) and the sum of q.
+__global__ void __launch_bounds__(256) k_grad_q(const double* __restrict__ pred,
+                                                const float* __restrict__ label, int64_t n,
+                                                int32_t log2n, const double* __restrict__ part,
+                                                int32_t nparts, int64_t* __restrict__ q,
+                                                int32_t* __restrict__ scale,
+                                                int64_t* __restrict__ gsum) {
+  __shared__ double shm[4];
+  __shared__ int64_t shs[4];
+  double m = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = fmax(m, part[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) shm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const double M = fmax(fmax(shm[0], shm[1]), fmax(shm[2], shm[3]));
+  int32_t S = 0;
+  if (M > 0.0) {
+    int e = 0;
+    (void)frexp(M, &e);
+    S = 52 - e - log2n;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = S;
+  int64_t s = 0;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const double g = pred[i] - (double)label[i];
+    const int64_t k = (int64_t)rint(ldexp(g, S));
+    q[i] = k;
+    s += k;
+  }
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) shs[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t t = shs[0] + shs[1] + shs[2] + shs[3];
+    atomicAdd(reinterpret_cast<unsigned long long*>(gsum), (unsigned long long)t);
+  }
+}
+
+// -------------------------------------------------------------- histogram --
+// One workgroup = one (tile of one node's rows, feature block).  Lanes are
+// laid out as (row group, dword column): lane reads the dword of 4 bins at
+// its column for rows rg, rg + rows_per_iter, ... of the tile (consecutive
+// lanes read consecutive dwords, so a wave streams contiguous bytes), and
+// adds the packed cell (q << bits) + 1 to the LDS slot of each bin with a
+// 64-bit LDS atomic.  Each feature's skip bin is not accumulated: it is set
+// afterwards to the tile total minus the feature's other bins (exact
+// integers).  A node covered by one tile writes its decoded histogram
+// straight to hist; otherwise the tile writes its packed partial and
+// k_hist_reduce sums the partials.
+__global__ void __launch_bounds__(256) k_hist(
+    const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t block_features,
+    int32_t block_stride, int32_t n_features, const int64_t* __restrict__ q,
+    const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ skip_bin,
+    int32_t total_bins, const gbdt_node* __restrict__ nodes, const int32_t* __restrict__ list,
+    const int32_t* __restrict__ list_len, int32_t list_cap, const int32_t* __restrict__ prefix,
+    int32_t tile_rows, int32_t bits, int64_t q_bound, int64_t* __restrict__ hist_g,
+    uint32_t* __restrict__ hist_cnt, uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl) {
+  extern __shared__ uint64_t lds[];
+  __shared__ uint64_t sh_tot[4];
+  const int32_t n = clamp_len(list_len, list_cap);
+  const int32_t tile = blockIdx.x;
+  if (n == 0 || tile >= prefix[n]) return;
+  const int32_t j = find_tile_owner(prefix, n, tile);
+  const int32_t v = list[j];
+  const int32_t ntiles = prefix[j + 1] - prefix[j];
+  const int32_t tin = tile - prefix[j];
+  const gbdt_node nd = nodes[v];
+  const int64_t r0 = int64_t(nd.begin) + int64_t(tin) * tile_rows;
+  int64_t r1 = r0 + tile_rows;
+  if (r1 > int64_t(nd.begin) + nd.count) r1 = int64_t(nd.begin) + nd.count;
+
+  const int32_t blk = blockIdx.y;
+  const int32_t f0 = blk * block_features;
+  int32_t f1 = f0 + block_features;
+  if (f1 > n_features) f1 = n_features;
+  const int32_t lb0 = bin_offset[f0];
+  const int32_t nbb = bin_offset[f1] - lb0;
+
+  for (int32_t b = threadIdx.x; b < nbb; b += blockDim.x) lds[b] = 0ull;
+
+  const int32_t lpr = block_stride >> 2;         // lanes per row
+  const int32_t rpi = blockDim.x / lpr;          // rows per iteration
+  const int32_t col = threadIdx.x % lpr;
+  const int32_t rg = threadIdx.x / lpr;
+  int32_t base[4];
+  int32_t skip[4];
+  int32_t nb[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int32_t f = f0 + 4 * col + m;
+    const bool ok = (f < f1) && (rg < rpi);
+    base[m] = ok ? bin_offset[f] - lb0 : 0;
+    nb[m] = ok ? bin_offset[f + 1] - bin_offset[f] : 0;
+    skip[m] = ok ? (skip_bin != nullptr ? skip_bin[f] : -1) : -1;
+  }
+  __syncthreads();
+
+  const uint8_t* __restrict__ bb = bins + int64_t(blk) * row_capacity * block_stride + 4 * col;
+  uint64_t tot = 0ull;
+  bool bad_q = false;
+  bool bad_bin = false;
+  if (rg < rpi) {
+    for (int64_t r = r0 + rg; r < r1; r += rpi) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(bb + r * block_stride);
+      const int64_t qq = q[r];
+      bad_q |= (qq > q_bound) || (qq < -q_bound);
+      const uint64_t pk = ((uint64_t)qq << bits) + 1ull;
+      tot += pk;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int32_t b = (w >> (8 * m)) & 0xff;
+        if (nb[m] > 0) {
+          bad_bin |= b >= nb[m];
+          if (b != skip[m] && b < nb[m])
+            __hip_atomic_fetch_add(&lds[base[m] + b], pk, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+    }
+  }
+  if (bad_q) dev_error(&ctrl->err, GBDT_E_OVERFLOW);
+  if (bad_bin) dev_error(&ctrl->err, GBDT_E_RANGE);
+  // tile total: every row was added once by each lane of its row group; take
+  // the column-0 lanes only
+  uint64_t t0 = (col == 0 && rg < rpi) ? tot : 0ull;
+  t0 = wave_sum(t0);
+  if ((threadIdx.x & 63) == 0) sh_tot[threadIdx.x >> 6] = t0;
+  __syncthreads();
+  const uint64_t tile_total = sh_tot[0] + sh_tot[1] + sh_tot[2] + sh_tot[3];
+
+  // skip bins: total minus the feature's other bins, one wave per feature
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  for (int32_t f = f0 + wid; f < f1; f += 4) {
+    const int32_t sb = skip_bin != nullptr ? skip_bin[f] : -1;
+    if (sb < 0) continue;
+    const int32_t fb = bin_offset[f] - lb0;
+    const int32_t fn = bin_offset[f + 1] - bin_offset[f];
+    uint64_t s = 0ull;
+    for (int32_t c = lane; c < fn; c += 64) s += lds[fb + c];
+    s = wave_sum(s);
+    if (lane == 0 && sb < fn) lds[fb + sb] = tile_total - s;
+  }
+  __syncthreads();
+
+  const uint64_t mask = (1ull << bits) - 1ull;
+  if (ntiles == 1) {
+    int64_t* __restrict__ hg = hist_g + int64_t(v) * total_bins + lb0;
+    uint32_t* __restrict__ hc = hist_cnt + int64_t(v) * total_bins + lb0;
+    for (int32_t b = threadIdx.x; b < nbb; b += blockDim.x) {
+      const uint64_t x = lds[b];
+      const uint64_t c = x & mask;
+      hg[b] = (int64_t)(x - c) >> bits;
+      hc[b] = (uint32_t)c;
+    }
+  } else {
+    uint64_t* __restrict__ pp = partial + int64_t(tile) * total_bins + lb0;
+    for (int32_t b = threadIdx.x; b < nbb; b += blockDim.x) pp[b] = lds[b];
+  }
+}
+
+// Sums the packed partials of every multi-tile node (in tile order; the sums
+// are exact integers, so any order gives the same bits).
+__global__ void __launch_bounds__(64) k_hist_reduce(const int32_t* __restrict__ list,
+                                                    const int32_t* __restrict__ list_len,
+                                                    int32_t list_cap,
+                                                    const int32_t* __restrict__ prefix,
+                                                    int32_t max_tiles, int32_t bits,
+                                                    int32_t total_bins,
+                                                    const uint64_t* __restrict__ partial,
+                                                    int64_t* __restrict__ hist_g,
+                                                    uint32_t* __restrict__ hist_cnt) {
+  const int32_t n = clamp_len(list_len, list_cap);
+  const int32_t j = blockIdx.y;
+  if (j >= n) return;
+  const int32_t t0 = prefix[j];
+  int32_t t1 = prefix[j + 1];
+  if (t1 > max_tiles) t1 = max_tiles;  // an over-full plan is already flagged
+  if (t1 - t0 <= 1) return;
+  const int32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= total_bins) return;
+  const uint64_t mask = (1ull << bits) - 1ull;
+  int64_t g = 0;
+  uint64_t c = 0;
+  for (int32_t t = t0; t < t1; ++t) {
+    const uint64_t x = partial[int64_t(t) * total_bins + b];
+    const uint64_t cc = x & mask;
+    g += (int64_t)(x - cc) >> bits;
+    c += cc;
+  }
+  const int32_t v = list[j];
+  hist_g[int64_t(v) * total_bins + b] = g;
+  hist_cnt[int64_t(v) * total_bins + b] = (uint32_t)c;
+}
+
+// ------------------------------------------------------------ subtraction --
+__global__ void __launch_bounds__(256) k_subtract(int64_t* __restrict__ hist_g,
+                                                  uint32_t* __restrict__ hist_cnt,
+                                                  int32_t total_bins,
+                                                  const gbdt_pair* __restrict__ pairs,
+                                                  const int32_t* __restrict__ n_pairs,
+                                                  int32_t pair_cap, WsCtrl* __restrict__ ctrl) {
+  const int32_t n = clamp_len(n_pairs, pair_cap);
+  const int32_t j = blockIdx.y;
+  if (j >= n) return;
+  const gbdt_pair pr = pairs[j];
+  const int64_t P = int64_t(pr.parent) * total_bins, Sm = int64_t(pr.smaller) * total_bins,
+                Lg = int64_t(pr.larger) * total_bins;
+  bool bad = false;
+  for (int32_t b = blockIdx.x * blockDim.x + threadIdx.x; b < total_bins;
+       b += gridDim.x * blockDim.x) {
+    const uint32_t cp = hist_cnt[P + b], cs = hist_cnt[Sm + b];
+    bad |= cs > cp;
+    hist_cnt[Lg + b] = cp - cs;
+    hist_g[Lg + b] = hist_g[P + b] - hist_g[Sm + b];
+  }
+  if (bad) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+}
+
+// ------------------------------------------------------------- split find --
+struct FindParams {
+  double lambda, gamma, mcw;
+  int32_t msl;
+};
+
+__device__ __forceinline__ double score_of(double G, double H, double lambda) {
+  const double num = G * G;
+  const double den = H + lambda;
+  return num / den;
+}
+
+// One workgroup per node.  The node's histogram is walked in chunks of 256
+// bins in global bin order (feature-major, bins ascending); a segmented
+// inclusive scan (segments = features) over each chunk gives every bin's
+// left prefix (G_L, n_L) with a carry across chunks; each candidate's gain is
+// then evaluated exactly as the formula is written.  The workgroup keeps the
+// candidate with the largest gain and, among bit-equal gains, the smallest
+// global bin index, which is the smaller feature and then the smaller bin.
+__global__ void __launch_bounds__(256) k_find(const int64_t* __restrict__ hist_g,
+                                              const uint32_t* __restrict__ hist_cnt,
+                                              const int32_t* __restrict__ bin_offset,
+                                              const int32_t* __restrict__ bin_feature,
+                                              const int32_t* __restrict__ n_bins,
+                                              int32_t total_bins,
+                                              const gbdt_node* __restrict__ nodes,
+                                              const int32_t* __restrict__ list,
+                                              const int32_t* __restrict__ list_len,
+                                              int32_t list_cap, FindParams fp,
+                                              const int32_t* __restrict__ scale,
+                                              gbdt_split* __restrict__ splits) {
+  __shared__ int64_t sw_g[4];
+  __shared__ int32_t sw_c[4];
+  __shared__ int32_t sw_f[4];
+  __shared__ int64_t s_carry_g;
+  __shared__ int32_t s_carry_c;
+  __shared__ double r_gain[256];
+  __shared__ int32_t r_bin[256];
+  __shared__ int64_t r_gl[256];
+  __shared__ int32_t r_nl[256];
+  const int32_t n = clamp_len(list_len, list_cap);
+  const int32_t j = blockIdx.x;
+  if (j >= n) return;
+  const int32_t v = list[j];
+  const gbdt_node nd = nodes[v];
+  const int32_t S = *scale;
+  const int64_t nv = nd.count;
+  const double Gv = ldexp((double)nd.gsum, -S);
+  const double Hv = (double)nd.count;
+  const double sP = score_of(Gv, Hv, fp.lambda);
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int64_t* __restrict__ hg = hist_g + int64_t(v) * total_bins;
+  const uint32_t* __restrict__ hc = hist_cnt + int64_t(v) * total_bins;
+
+  double best_gain = 0.0;
+  int32_t best_bin = 0x7fffffff;
+  int64_t best_gl = 0;
+  int32_t best_nl = 0;
+  if (threadIdx.x == 0) {
+    s_carry_g = 0;
+    s_carry_c = 0;
+  }
+  __syncthreads();
+  for (int32_t base = 0; base < total_bins; base += 256) {
+    const int32_t b = base + threadIdx.x;
+    const bool inb = b < total_bins;
+    int32_t f = 0, t = 0;
+    int64_t g = 0;
+    int32_t c = 0;
+    int32_t head = 1;
+    if (inb) {
+      f = bin_feature[b];
+      t = b - bin_offset[f];
+      g = hg[b];
+      c = (int32_t)hc[b];
+      head = (t == 0) ? 1 : 0;
+    }
+    // segmented inclusive scan inside the wave
+    int32_t fl = head;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t gu = __shfl_up(g, off, 64);
+      const int32_t cu = __shfl_up(c, off, 64);
+      const int32_t fu = __shfl_up(fl, off, 64);
+      if (lane >= off && !fl) {
+        g += gu;
+        c += cu;
+        fl |= fu;
+      }
+    }
+    if (lane == 63) {
+      sw_g[wid] = g;
+      sw_c[wid] = c;
+      sw_f[wid] = fl;
+    }
+    __syncthreads();
+    // carry into this wave from the chunk carry and the earlier waves
+    int64_t cg = s_carry_g;
+    int32_t cc = s_carry_c;
+    for (int w = 0; w < wid; ++w) {
+      if (sw_f[w]) {
+        cg = sw_g[w];
+        cc = sw_c[w];
+      } else {
+        cg += sw_g[w];
+        cc += sw_c[w];
+      }
+    }
+    if (!fl) {
+      g += cg;
+      c += cc;
+    }
+    __syncthreads();
+    if (threadIdx.x == 255) {
+      s_carry_g = g;
+      s_carry_c = c;
+    }
+    // candidate (f, t): t <= n_bins[f] - 2
+    if (inb && t <= n_bins[f] - 2) {
+      const int64_t nl = c;
+      const int64_t nr = nv - nl;
+      const double GL = ldexp((double)g, -S);
+      const double HL = (double)nl;
+      const double GR = Gv - GL;
+      const double HR = Hv - HL;
+      if (nl >= fp.msl && nr >= fp.msl && HL >= fp.mcw && HR >= fp.mcw && HL > 0.0 && HR > 0.0) {
+        const double sL = score_of(GL, HL, fp.lambda);
+        const double sR = score_of(GR, HR, fp.lambda);
+        const double sum = sL + sR;
+        const double diff = sum - sP;
+        const double half = 0.5 * diff;
+        const double gain = half - fp.gamma;
+        if (gain > best_gain || (gain == best_gain && gain > 0.0 && b < best_bin)) {
+          best_gain = gain;
+          best_bin = b;
+          best_gl = g;
+          best_nl = c;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  r_gain[threadIdx.x] = best_gain;
+  r_bin[threadIdx.x] = best_bin;
+  r_gl[threadIdx.x] = best_gl;
+  r_nl[threadIdx.x] = best_nl;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      const double g2 = r_gain[threadIdx.x + s];
+      const int32_t b2 = r_bin[threadIdx.x + s];
+      const double g1 = r_gain[threadIdx.x];
+      const int32_t b1 = r_bin[threadIdx.x];
+      if (g2 > g1 || (g2 == g1 && b2 < b1)) {
+        r_gain[threadIdx.x] = g2;
+        r_bin[threadIdx.x] = b2;
+        r_gl[threadIdx.x] = r_gl[threadIdx.x + s];
+        r_nl[threadIdx.x] = r_nl[threadIdx.x + s];
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    gbdt_split sp;
+    const int32_t bb = r_bin[0];
+    if (bb != 0x7fffffff && r_gain[0] > 0.0) {
+      const int32_t f = bin_feature[bb];
+      sp.gain = r_gain[0];
+      sp.feature = f;
+      sp.threshold_bin = bb - bin_offset[f];
+      sp.g_left = r_gl[0];
+      sp.n_left = r_nl[0];
+      sp.valid = 1;
+    } else {
+      sp.gain = 0.0;
+      sp.feature = -1;
+      sp.threshold_bin = -1;
+      sp.g_left = 0;
+      sp.n_left = 0;
+      sp.valid = 0;
+    }
+    splits[v] = sp;
+  }
+}
+
+// -------------------------------------------------------------- partition --
+// Stable partition in one pass with a decoupled look-back across the tiles
+// of a node.  Tiles are taken in ticket order, so every tile a workgroup
+// waits on has already started.  Each status word packs a 2-bit state
+// (1 = tile count available, 2 = inclusive prefix available) with a 32-bit
+// value; the wait is bounded and reports GBDT_E_INTERNAL if it runs out.
+constexpr uint64_t kStAgg = 1ull << 62;
+constexpr uint64_t kStInc = 2ull << 62;
+constexpr uint64_t kStMask = 3ull << 62;
+
+__device__ __forceinline__ void st_publish(uint64_t* p, uint64_t word) {
+  __hip_atomic_store(p, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t st_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kPartThreads = 256;
+constexpr int kPartRowsPerThread = kPartTileRows / kPartThreads;  // 8
+
+__global__ void __launch_bounds__(kPartThreads) k_partition(
+    const uint8_t* __restrict__ sbins, const int64_t* __restrict__ sq,
+    const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, int64_t* __restrict__ dq,
+    int32_t* __restrict__ drid, int64_t row_capacity, int32_t n_blocks, int32_t block_features,
+    int32_t block_stride, int32_t n_features, const gbdt_node* __restrict__ nodes,
+    const gbdt_split* __restrict__ splits, const int32_t* __restrict__ list,
+    const int32_t* __restrict__ list_len, int32_t list_cap, const int32_t* __restrict__ prefix,
+    uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl) {
+  __shared__ int32_t s_tile;
+  __shared__ int32_t s_cnt[kPartRowsPerThread][kPartThreads / 64];
+  __shared__ int32_t s_excl;
+  __shared__ int32_t s_dpos[kPartTileRows];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  if (threadIdx.x == 0) s_tile = (int32_t)atomicAdd(&ctrl->ticket, 1u);
+  __syncthreads();
+  const int32_t tile = s_tile;
+  const int32_t n = clamp_len(list_len, list_cap);
+  if (n == 0 || tile >= prefix[n]) return;
+  const int32_t j = find_tile_owner(prefix, n, tile);
+  const int32_t v = list[j];
+  const gbdt_node nd = nodes[v];
+  const gbdt_split sp = splits[v];
+  const int32_t tfirst = prefix[j];
+  const int32_t tlast = prefix[j + 1] - 1;
+  const int32_t tin = tile - tfirst;
+  const int64_t r0 = int64_t(nd.begin) + int64_t(tin) * kPartTileRows;
+  int64_t r1 = r0 + kPartTileRows;
+  if (r1 > int64_t(nd.begin) + nd.count) r1 = int64_t(nd.begin) + nd.count;
+  // a listed node must carry a valid split; otherwise nothing is moved, the
+  // tile still publishes (so later tiles never wait on it) and the error word
+  // is set
+  const bool split_ok = sp.valid && sp.feature >= 0 && sp.feature < n_features;
+  const int32_t rows = split_ok ? (int32_t)(r1 - r0 > 0 ? r1 - r0 : 0) : 0;
+  if (!split_ok && threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+
+  const int32_t fblk = split_ok ? sp.feature / block_features : 0;
+  const int32_t fcol = split_ok ? sp.feature % block_features : 0;
+  const uint8_t* __restrict__ fcolp =
+      sbins + int64_t(fblk) * row_capacity * block_stride + fcol;
+  bool left[kPartRowsPerThread];
+  uint64_t bal[kPartRowsPerThread];
+#pragma unroll
+  for (int k = 0; k < kPartRowsPerThread; ++k) {
+    const int32_t i = k * kPartThreads + threadIdx.x;
+    left[k] = (i < rows) && ((int32_t)fcolp[(r0 + i) * block_stride] <= sp.threshold_bin);
+    bal[k] = __ballot(left[k]);
+    if (lane == 0) s_cnt[k][wid] = __popcll(bal[k]);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int k = 0; k < kPartRowsPerThread; ++k)
+      for (int w = 0; w < kPartThreads / 64; ++w) {
+        const int32_t t = s_cnt[k][w];
+        s_cnt[k][w] = acc;
+        acc += t;
+      }
+    // acc = lefts in this tile; look back for the lefts of earlier tiles
+    if (tin == 0) {
+      st_publish(&status[tile], kStInc | (uint64_t)(uint32_t)acc);
+      s_excl = 0;
+    } else {
+      st_publish(&status[tile], kStAgg | (uint64_t)(uint32_t)acc);
+      int64_t excl = 0;
+      int32_t idx = tile - 1;
+      uint32_t spins = 0;
+      bool ok = true;
+      while (true) {
+        const uint64_t w = st_load(&status[idx]);
+        const uint64_t st = w & kStMask;
+        if (st == 0ull) {
+          if (++spins > (1u << 20)) {
+            ok = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+          continue;
+        }
+        excl += (int64_t)(uint32_t)(w & 0xffffffffull);
+        if (st == kStInc || idx == tfirst) break;
+        --idx;
+      }
+      if (!ok) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+      st_publish(&status[tile], kStInc | (uint64_t)(uint32_t)(excl + acc));
+      s_excl = (int32_t)excl;
+    }
+    if (tile == tlast && s_excl + acc != sp.n_left) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+  }
+  __syncthreads();
+  const int32_t excl = s_excl;
+  const int64_t lbase = int64_t(nd.begin) + excl;
+  const int64_t rbase = int64_t(nd.begin) + sp.n_left + (int64_t(tin) * kPartTileRows - excl);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t seg_end = int64_t(nd.begin) + nd.count;
+  bool bad_pos = false;
+#pragma unroll
+  for (int k = 0; k < kPartRowsPerThread; ++k) {
+    const int32_t i = k * kPartThreads + threadIdx.x;
+    if (i < rows) {
+      const int32_t rl = s_cnt[k][wid] + __popcll(bal[k] & lt_mask);
+      const int64_t d = left[k] ? lbase + rl : rbase + (i - rl);
+      // a split record whose left count disagrees with the rows could send a
+      // row outside its node's segment: such a row is not written
+      const bool in_seg = d >= nd.begin && d < seg_end;
+      bad_pos |= !in_seg;
+      s_dpos[i] = in_seg ? (int32_t)d : -1;
+    }
+  }
+  if (bad_pos) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+  __syncthreads();
+  // q and row id, one row per lane
+  for (int32_t i = threadIdx.x; i < rows; i += kPartThreads) {
+    const int64_t s = r0 + i;
+    const int32_t d = s_dpos[i];
+    if (d < 0) continue;
+    dq[d] = sq[s];
+    drid[d] = srid != nullptr ? srid[s] : (int32_t)s;
+  }
+  // bins: (row group, dword column) lanes, every block
+  const int32_t lpr = block_stride >> 2;
+  const int32_t rpi = kPartThreads / lpr;
+  const int32_t col = threadIdx.x % lpr;
+  const int32_t rg = threadIdx.x / lpr;
+  if (rg < rpi) {
+    for (int32_t b = 0; b < n_blocks; ++b) {
+      const uint8_t* __restrict__ sb = sbins + int64_t(b) * row_capacity * block_stride + 4 * col;
+      uint8_t* __restrict__ db = dbins + int64_t(b) * row_capacity * block_stride + 4 * col;
+      for (int32_t i = rg; i < rows; i += rpi) {
+        const int32_t d = s_dpos[i];
+        if (d < 0) continue;
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(sb + (r0 + i) * block_stride);
+        *reinterpret_cast<uint32_t*>(db + int64_t(d) * block_stride) = w;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------ prediction update --
+struct RidTable {
+  const int32_t* p[GBDT_MAX_DEPTH + 1];
+};
+
+__global__ void __launch_bounds__(256) k_update(double* __restrict__ pred, int64_t n_pred,
+                                                RidTable rt, int32_t n_depths,
+                                                const gbdt_node* __restrict__ nodes,
+                                                const int32_t* __restrict__ list,
+                                                const int32_t* __restrict__ list_len,
+                                                int32_t list_cap,
+                                                const int32_t* __restrict__ prefix,
+                                                double eta, WsCtrl* __restrict__ ctrl) {
+  const int32_t n = clamp_len(list_len, list_cap);
+  const int32_t tile = blockIdx.x;
+  if (n == 0 || tile >= prefix[n]) return;
+  const int32_t j = find_tile_owner(prefix, n, tile);
+  const int32_t v = list[j];
+  const gbdt_node nd = nodes[v];
+  if (nd.depth < 0 || nd.depth >= n_depths) {
+    if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+    return;
+  }
+  const int32_t* __restrict__ rid = rt.p[nd.depth];
+  const int64_t r0 = int64_t(nd.begin) + int64_t(tile - prefix[j]) * kUpdTileRows;
+  int64_t r1 = r0 + kUpdTileRows;
+  if (r1 > int64_t(nd.begin) + nd.count) r1 = int64_t(nd.begin) + nd.count;
+  const double delta = eta * nd.leaf_value;
+  bool bad = false;
+  for (int64_t p = r0 + threadIdx.x; p < r1; p += blockDim.x) {
+    const int64_t r = rid != nullptr ? rid[p] : p;
+    if (r < 0 || r >= n_pred) {
+      bad = true;
+      continue;
+    }
+    pred[r] = pred[r] + delta;
+  }
+  if (bad) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+}
+
+// ------------------------------------------------------- setup: packing --
+__global__ void __launch_bounds__(256) k_pack(const uint8_t* __restrict__ src, int64_t n,
+                                              int32_t F, uint8_t* __restrict__ dst,
+                                              int64_t row_capacity, int32_t n_blocks,
+                                              int32_t block_features, int32_t block_stride,
+                                              const int32_t* __restrict__ n_bins,
+                                              WsCtrl* __restrict__ ctrl) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  bool bad = false;
+  for (int32_t b = 0; b < n_blocks; ++b) {
+    uint8_t* d = dst + int64_t(b) * row_capacity * block_stride + i * block_stride;
+    for (int32_t jj = 0; jj < block_stride; ++jj) {
+      const int32_t f = b * block_features + jj;
+      uint8_t x = 0;
+      if (jj < block_features && f < F) {
+        x = src[i * F + f];
+        bad |= (int32_t)x >= n_bins[f];
+      }
+      d[jj] = x;
+    }
+  }
+  if (bad) dev_error(&ctrl->err, GBDT_E_RANGE);
+}
+
+// bin census for the skip-bin choice: counts[f][bin] over all rows
+__global__ void __launch_bounds__(256) k_census(const uint8_t* __restrict__ src, int64_t n,
+                                                int32_t F, uint32_t* __restrict__ counts) {
+  __shared__ uint32_t c[64 * 256];
+  const int32_t fg = blockIdx.y * 64;
+  const int32_t nf = (F - fg) < 64 ? (F - fg) : 64;
+  for (int t = threadIdx.x; t < 64 * 256; t += blockDim.x) c[t] = 0u;
+  __syncthreads();
+  const int64_t rows_per_block = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t a = int64_t(blockIdx.x) * rows_per_block;
+  int64_t e = a + rows_per_block;
+  if (e > n) e = n;
+  for (int64_t x = a * nf + threadIdx.x; x < e * nf; x += blockDim.x) {
+    const int64_t i = x / nf;
+    const int32_t f = (int32_t)(x - i * nf);
+    atomicAdd(&c[f * 256 + src[i * F + fg + f]], 1u);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < nf * 256; t += blockDim.x)
+    if (c[t]) atomicAdd(&counts[int64_t(fg) * 256 + t], c[t]);
+}
+
+__global__ void __launch_bounds__(64) k_pick_skip(const uint32_t* __restrict__ counts, int32_t F,
+                                                  const int32_t* __restrict__ n_bins,
+                                                  int32_t* __restrict__ skip_bin) {
+  const int32_t f = blockIdx.x;
+  if (f >= F || threadIdx.x != 0) return;
+  uint32_t best = 0u;
+  int32_t bi = -1;
+  for (int32_t c = 0; c < n_bins[f]; ++c) {
+    const uint32_t x = counts[int64_t(f) * 256 + c];
+    if (x > best) {
+      best = x;
+      bi = c;
+    }
+  }
+  skip_bin[f] = bi;
+}
+
+__global__ void k_zero_u32(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+// ------------------------------------------------------------ host checks --
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static int check_ws(void* ws, size_t ws_bytes, const WsLayout& L) {
+  if (ws == nullptr || !aligned(ws, 256)) return fail(GBDT_E_ARG, "workspace is null or not 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(GBDT_E_ARG, "workspace too small: need " + std::to_string(L.total) + " bytes, got " +
+                                std::to_string(ws_bytes));
+  return GBDT_OK;
+}
+
+static int check_matrix(const gbdt_matrix& X) {
+  if (X.bins == nullptr) return fail(GBDT_E_ARG, "matrix bins pointer is null");
+  if (X.n_rows < 0 || X.n_rows > 0x7fffffffLL) return fail(GBDT_E_ARG, "n_rows out of range");
+  if (X.row_capacity < X.n_rows) return fail(GBDT_E_SHAPE, "row_capacity < n_rows");
+  if (X.n_features < 1 || X.n_features > GBDT_MAX_FEATURES) return fail(GBDT_E_ARG, "n_features out of range");
+  if (X.block_features < 1 || X.block_stride < X.block_features || (X.block_stride & 3) ||
+      X.block_stride > 1024)
+    return fail(GBDT_E_ARG, "bad block_features / block_stride");
+  if (int64_t(X.n_blocks) * X.block_features < X.n_features ||
+      int64_t(X.n_blocks - 1) * X.block_features >= X.n_features)
+    return fail(GBDT_E_SHAPE, "n_blocks does not match n_features / block_features");
+  if (!aligned(X.bins, 4)) return fail(GBDT_E_ARG, "bins not 4-byte aligned");
+  return GBDT_OK;
+}
+
+static int check_features(const gbdt_features& ft, int32_t n_features) {
+  if (ft.n_features != n_features) return fail(GBDT_E_SHAPE, "feature table does not match the matrix");
+  if (ft.total_bins < 1 || ft.total_bins > GBDT_MAX_FEATURES * GBDT_MAX_BINS)
+    return fail(GBDT_E_ARG, "total_bins out of range");
+  if (!ft.n_bins || !ft.bin_offset || !ft.bin_feature) return fail(GBDT_E_ARG, "feature table pointer is null");
+  return GBDT_OK;
+}
+
+
+}  // namespace gbdt
+
+using namespace gbdt;
+
+// ==================================================================== C ABI ==
+
+extern "C" {
+
+int gbdt_abi_version(void) { return GBDT_ABI_VERSION; }
+
+int gbdt_diag_enable(int32_t capacity) {
+  if (capacity < 1 || capacity > (1 << 20)) return fail(GBDT_E_ARG, "capacity out of range");
+  if (g_diag.capacity < capacity) {
+    const int32_t old = g_diag.capacity;
+    g_diag.ev.resize(size_t(2) * capacity);
+    g_diag.kind.resize(capacity);
+    for (int32_t i = 2 * old; i < 2 * capacity; ++i) {
+      hipError_t e = hipEventCreate(&g_diag.ev[i]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    g_diag.capacity = capacity;
+  }
+  g_diag.count = 0;
+  g_diag.open = false;
+  g_diag.enabled = true;
+  return GBDT_OK;
+}
+
+int gbdt_diag_disable(void) {
+  g_diag.enabled = false;
+  return GBDT_OK;
+}
+
+int gbdt_diag_read(int32_t max_records, int32_t* kinds, float* ms, int32_t* n_out) {
+  if (!kinds || !ms || !n_out || max_records < 0) return fail(GBDT_E_ARG, "null argument");
+  const int32_t n = g_diag.count < max_records ? g_diag.count : max_records;
+  if (g_diag.count > 0) {
+    hipError_t e = hipEventSynchronize(g_diag.ev[2 * g_diag.count - 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    kinds[i] = g_diag.kind[i];
+    float t = 0.f;
+    hipError_t e = hipEventElapsedTime(&t, g_diag.ev[2 * i], g_diag.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    ms[i] = t;
+  }
+  *n_out = n;
+  g_diag.count = 0;
+  return GBDT_OK;
+}
+
+const char* gbdt_last_error(void) { return g_last_error.c_str(); }
+
+int gbdt_validate_params(const gbdt_params* p) {
+  if (!p) return fail(GBDT_E_ARG, "params is null");
+  if (!std::isfinite(p->reg_lambda) || !std::isfinite(p->gamma) ||
+      !std::isfinite(p->min_child_weight) || !std::isfinite(p->learning_rate))
+    return fail(GBDT_E_ARG, "every floating parameter must be finite");
+  if (p->min_samples_leaf < 1) return fail(GBDT_E_ARG, "min_samples_leaf must be >= 1");
+  if (p->min_child_weight < 0.0) return fail(GBDT_E_ARG, "min_child_weight must be >= 0");
+  if (p->reg_lambda < 0.0) return fail(GBDT_E_ARG, "reg_lambda must be >= 0");
+  if (p->gamma < 0.0) return fail(GBDT_E_ARG, "gamma must be >= 0");
+  if (p->max_depth < 0 || p->max_depth > GBDT_MAX_DEPTH) return fail(GBDT_E_ARG, "max_depth out of range");
+  return GBDT_OK;
+}
+
+size_t gbdt_workspace_bytes(int64_t n_rows, int32_t max_list, int32_t total_bins) {
+  return ws_layout(n_rows, max_list, total_bins).total;
+}
+
+int gbdt_choose_blocking(int32_t n_features, const int32_t* n_bins_host, gbdt_matrix* X,
+                         int32_t* max_block_bins) {
+  if (!X || !n_bins_host || !max_block_bins) return fail(GBDT_E_ARG, "null argument");
+  if (n_features < 1 || n_features > GBDT_MAX_FEATURES) return fail(GBDT_E_ARG, "n_features out of range");
+  for (int32_t f = 0; f < n_features; ++f)
+    if (n_bins_host[f] < 1 || n_bins_host[f] > GBDT_MAX_BINS) return fail(GBDT_E_ARG, "n_bins out of range");
+  // fewest blocks of equal width (<= 64 features) whose bins fit the budget
+  for (int32_t nb = 1; nb <= n_features; ++nb) {
+    const int32_t bf = (n_features + nb - 1) / nb;
+    if (bf > 64) continue;
+    int32_t worst = 0;
+    for (int32_t f0 = 0; f0 < n_features; f0 += bf) {
+      int32_t s = 0;
+      for (int32_t f = f0; f < f0 + bf && f < n_features; ++f) s += n_bins_host[f];
+      if (s > worst) worst = s;
+    }
+    if (worst > kLdsHistBudgetBins) continue;
+    X->n_features = n_features;
+    X->block_features = bf;
+    X->n_blocks = (n_features + bf - 1) / bf;
+    X->block_stride = (bf + 3) & ~3;
+    *max_block_bins = worst;
+    return GBDT_OK;
+  }
+  return fail(GBDT_E_UNSUPPORTED, "no feature blocking fits the LDS budget");
+}
+
+int gbdt_read_error(void* ws, void* stream) {
+  if (!ws) return fail(GBDT_E_ARG, "workspace is null");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  WsCtrl c;
+  hipError_t e = hipMemcpyAsync(&c, ws, sizeof(WsCtrl), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the error word");
+  if (c.err != 0) {
+    int32_t zero[2] = {0, 0};
+    e = hipMemcpyAsync(ws, zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "clearing the error word");
+    return fail(c.err, "device-side check failed (code " + std::to_string(c.err) + ")");
+  }
+  return GBDT_OK;
+}
+
+int gbdt_pack_matrix(const uint8_t* rowmajor, const gbdt_matrix* dst, const gbdt_features* ft,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!rowmajor || !dst || !ft) return fail(GBDT_E_ARG, "null argument");
+  int rc = check_matrix(*dst);
+  if (rc) return rc;
+  rc = check_features(*ft, dst->n_features);
+  if (rc) return rc;
+  const WsLayout L = ws_layout(dst->n_rows, 1, ft->total_bins);
+  rc = check_ws(ws, ws_bytes, L);
+  if (rc) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
+  const int64_t n = dst->n_rows;
+  if (n > 0) {
+    const int64_t grid = (n + 255) / 256;
+    diag_begin(kDiagPack, s);
+    hipLaunchKernelGGL(k_pack, dim3((unsigned)grid), dim3(256), 0, s, rowmajor, n,
+                       dst->n_features, dst->bins, dst->row_capacity, dst->n_blocks,
+                       dst->block_features, dst->block_stride, ft->n_bins, ctrl);
+    diag_end(s);
+    GBDT_LAUNCH_CHECK("k_pack");
+  }
+  if (ft->skip_bin) {
+    uint32_t* counts = reinterpret_cast<uint32_t*>(w + L.hpart);
+    const int64_t nc = int64_t(dst->n_features) * 256;
+    diag_begin(kDiagPack, s);
+    hipLaunchKernelGGL(k_zero_u32, dim3(256), dim3(256), 0, s, counts, nc);
+    diag_end(s);
+    GBDT_LAUNCH_CHECK("k_zero_u32");
+    if (n > 0) {
+      int64_t gx = n / 4096 + 1;
+      if (gx > 512) gx = 512;
+      const int32_t gy = (dst->n_features + 63) / 64;
+      diag_begin(kDiagPack, s);
+      hipLaunchKernelGGL(k_census, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, rowmajor, n,
+                         dst->n_features, counts);
+      diag_end(s);
+      GBDT_LAUNCH_CHECK("k_census");
+    }
+    diag_begin(kDiagPack, s);
+    hipLaunchKernelGGL(k_pick_skip, dim3((unsigned)dst->n_features), dim3(64), 0, s, counts,
+                       dst->n_features, ft->n_bins, ft->skip_bin);
+    diag_end(s);
+    GBDT_LAUNCH_CHECK("k_pick_skip");
+  }
+  return GBDT_OK;
+}
+
+int gbdt_compute_gradients(const double* pred, const float* label, int64_t n, int64_t* q,
+                           int32_t* scale, int64_t* gsum, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!pred || !label || !q || !scale || !gsum) return fail(GBDT_E_ARG, "null argument");
+  if (n < 1 || n > 0x7fffffffLL) return fail(GBDT_E_ARG, "n out of range");
+  const WsLayout L = ws_layout(n, 1, 1);
+  int rc = check_ws(ws, ws_bytes, L);
+  if (rc) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
+  double* part = reinterpret_cast<double*>(w + L.gpart);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > kGradBlocks) blocks = kGradBlocks;
+  diag_begin(kDiagGradMax, s);
+  hipLaunchKernelGGL(k_grad_max, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n, part,
+                     gsum, ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_grad_max");
+  diag_begin(kDiagGradQ, s);
+  hipLaunchKernelGGL(k_grad_q, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n,
+                     ceil_log2(n), part, (int32_t)blocks, q, scale, gsum);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_grad_q");
+  return GBDT_OK;
+}
+
+int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const gbdt_node* nodes,
+                          const int32_t* list, const int32_t* list_len, int32_t list_cap,
+                          int64_t rows_bound, int64_t* hist_g, uint32_t* hist_cnt, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!src || !ft || !nodes || !list || !list_len || !hist_g || !hist_cnt)
+    return fail(GBDT_E_ARG, "null argument");
+  int rc = check_matrix(src->X);
+  if (rc) return rc;
+  rc = check_features(*ft, src->X.n_features);
+  if (rc) return rc;
+  if (!src->q) return fail(GBDT_E_ARG, "q is null");
+  if (list_cap < 0 || rows_bound < 0) return fail(GBDT_E_ARG, "negative capacity");
+  if (list_cap == 0) return GBDT_OK;
+  const WsLayout L = ws_layout(src->X.n_rows, list_cap, ft->total_bins);
+  rc = check_ws(ws, ws_bytes, L);
+  if (rc) return rc;
+  if (ft->max_block_bins < 1 || ft->max_block_bins > kLdsHistBudgetBins)
+    return fail(GBDT_E_UNSUPPORTED, "max_block_bins outside the LDS histogram budget");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
+  int32_t* prefix = reinterpret_cast<int32_t*>(w + L.prefix);
+  uint64_t* hpart = reinterpret_cast<uint64_t*>(w + L.hpart);
+  const int32_t n_rows_for_bits = (int32_t)(src->X.n_rows > 0 ? src->X.n_rows : 1);
+  const int32_t bits = pack_bits_for(n_rows_for_bits);
+  const int32_t T = hist_tile_rows(rows_bound, n_rows_for_bits);
+  const int64_t max_tiles = (rows_bound + T - 1) / T + list_cap;
+  if (max_tiles > L.hpart_tiles) return fail(GBDT_E_SHAPE, "too many histogram tiles for the workspace");
+  const int64_t q_bound = int64_t(1) << (52 - ceil_log2(n_rows_for_bits));
+  diag_begin(kDiagPlan, s);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap, T,
+                     (int32_t)max_tiles, prefix, ctrl, (uint64_t*)nullptr);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_plan");
+  const size_t lds = sizeof(uint64_t) * size_t(ft->max_block_bins);
+  diag_begin(kDiagHist, s);
+  hipLaunchKernelGGL(k_hist, dim3((unsigned)max_tiles, (unsigned)src->X.n_blocks), dim3(256), lds,
+                     s, src->X.bins, src->X.row_capacity, src->X.block_features,
+                     src->X.block_stride, src->X.n_features, src->q, ft->bin_offset,
+                     ft->skip_bin, ft->total_bins, nodes, list, list_len, list_cap, prefix, T,
+                     bits, q_bound, hist_g, hist_cnt, hpart, ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_hist");
+  diag_begin(kDiagHistReduce, s);
+  hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)((ft->total_bins + 63) / 64), (unsigned)list_cap),
+                     dim3(64), 0, s, list, list_len, list_cap, prefix, (int32_t)max_tiles, bits,
+                     ft->total_bins, hpart, hist_g, hist_cnt);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_hist_reduce");
+  return GBDT_OK;
+}
+
+int gbdt_subtract_histograms(int64_t* hist_g, uint32_t* hist_cnt, int32_t total_bins,
+                             const gbdt_pair* pairs, const int32_t* n_pairs, int32_t pair_cap,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!hist_g || !hist_cnt || !pairs || !n_pairs) return fail(GBDT_E_ARG, "null argument");
+  if (total_bins < 1 || pair_cap < 0) return fail(GBDT_E_ARG, "bad size");
+  if (pair_cap == 0) return GBDT_OK;
+  const WsLayout L = ws_layout(1, 1, 1);
+  if (!ws || ws_bytes < sizeof(WsCtrl)) return fail(GBDT_E_ARG, "workspace too small");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(static_cast<char*>(ws) + L.ctrl);
+  int32_t gx = (total_bins + 255) / 256;
+  if (gx > 64) gx = 64;
+  diag_begin(kDiagSubtract, s);
+  hipLaunchKernelGGL(k_subtract, dim3((unsigned)gx, (unsigned)pair_cap), dim3(256), 0, s, hist_g,
+                     hist_cnt, total_bins, pairs, n_pairs, pair_cap, ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_subtract");
+  return GBDT_OK;
+}
+
+int gbdt_find_best_splits(const int64_t* hist_g, const uint32_t* hist_cnt,
+                          const gbdt_features* ft, const gbdt_node* nodes, const int32_t* list,
+                          const int32_t* list_len, int32_t list_cap, const gbdt_params* p,
+                          const int32_t* scale, gbdt_split* splits, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!hist_g || !hist_cnt || !ft || !nodes || !list || !list_len || !p || !scale || !splits)
+    return fail(GBDT_E_ARG, "null argument");
+  int rc = gbdt_validate_params(p);
+  if (rc) return rc;
+  if (ft->total_bins < 1 || !ft->bin_offset || !ft->bin_feature || !ft->n_bins)
+    return fail(GBDT_E_ARG, "bad feature table");
+  if (list_cap < 0) return fail(GBDT_E_ARG, "negative capacity");
+  if (list_cap == 0) return GBDT_OK;
+  (void)ws;
+  (void)ws_bytes;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  FindParams fp{p->reg_lambda, p->gamma, p->min_child_weight, p->min_samples_leaf};
+  diag_begin(kDiagFind, s);
+  hipLaunchKernelGGL(k_find, dim3((unsigned)list_cap), dim3(256), 0, s, hist_g, hist_cnt,
+                     ft->bin_offset, ft->bin_feature, ft->n_bins, ft->total_bins, nodes, list,
+                     list_len, list_cap, fp, scale, splits);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_find");
+  return GBDT_OK;
+}
+
+int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_node* nodes,
+                        const gbdt_split* splits, const int32_t* list, const int32_t* list_len,
+                        int32_t list_cap, int64_t rows_bound, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (!src || !dst || !nodes || !splits || !list || !list_len) return fail(GBDT_E_ARG, "null argument");
+  int rc = check_matrix(src->X);
+  if (rc) return rc;
+  rc = check_matrix(dst->X);
+  if (rc) return rc;
+  if (src->X.n_blocks != dst->X.n_blocks || src->X.block_stride != dst->X.block_stride ||
+      src->X.block_features != dst->X.block_features || src->X.row_capacity != dst->X.row_capacity ||
+      src->X.n_rows != dst->X.n_rows)
+    return fail(GBDT_E_SHAPE, "source and destination layouts differ");
+  if (!src->q || !dst->q || !dst->rid) return fail(GBDT_E_ARG, "q / rid pointer is null");
+  if (list_cap < 0 || rows_bound < 0) return fail(GBDT_E_ARG, "negative capacity");
+  if (list_cap == 0) return GBDT_OK;
+  const WsLayout L = ws_layout(src->X.n_rows, list_cap, 1);
+  rc = check_ws(ws, ws_bytes, L);
+  if (rc) return rc;
+  const int64_t max_tiles = (rows_bound + kPartTileRows - 1) / kPartTileRows + list_cap;
+  if (max_tiles > L.status_cap) return fail(GBDT_E_SHAPE, "too many partition tiles for the workspace");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
+  int32_t* prefix = reinterpret_cast<int32_t*>(w + L.prefix);
+  uint64_t* status = reinterpret_cast<uint64_t*>(w + L.status);
+  diag_begin(kDiagPlan, s);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap,
+                     kPartTileRows, (int32_t)max_tiles, prefix, ctrl, status);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_plan");
+  diag_begin(kDiagPartition, s);
+  hipLaunchKernelGGL(k_partition, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s,
+                     src->X.bins, src->q, src->rid, dst->X.bins, dst->q, dst->rid,
+                     src->X.row_capacity, src->X.n_blocks, src->X.block_features,
+                     src->X.block_stride, src->X.n_features, nodes, splits, list, list_len,
+                     list_cap, prefix, status, ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_partition");
+  return GBDT_OK;
+}
+
+int gbdt_update_predictions(double* pred, int64_t n, const int32_t* const* rid_by_depth,
+                            int32_t n_depths, const gbdt_node* nodes, const int32_t* list,
+                            const int32_t* list_len, int32_t list_cap, double learning_rate,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (!pred || !nodes || !list || !list_len || !rid_by_depth) return fail(GBDT_E_ARG, "null argument");
+  if (n < 1 || n > 0x7fffffffLL) return fail(GBDT_E_ARG, "n out of range");
+  if (n_depths < 1 || n_depths > GBDT_MAX_DEPTH + 1) return fail(GBDT_E_ARG, "n_depths out of range");
+  if (!std::isfinite(learning_rate)) return fail(GBDT_E_ARG, "learning_rate must be finite");
+  if (list_cap < 0) return fail(GBDT_E_ARG, "negative capacity");
+  if (list_cap == 0) return GBDT_OK;
+  const WsLayout L = ws_layout(n, list_cap, 1);
+  int rc = check_ws(ws, ws_bytes, L);
+  if (rc) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
+  int32_t* prefix = reinterpret_cast<int32_t*>(w + L.prefix);
+  RidTable rt{};
+  for (int d = 0; d < n_depths; ++d) rt.p[d] = rid_by_depth[d];
+  const int64_t max_tiles = (n + kUpdTileRows - 1) / kUpdTileRows + list_cap;
+  diag_begin(kDiagPlan, s);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap,
+                     kUpdTileRows, (int32_t)max_tiles, prefix, ctrl, (uint64_t*)nullptr);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_plan");
+  diag_begin(kDiagUpdate, s);
+  hipLaunchKernelGGL(k_update, dim3((unsigned)max_tiles), dim3(256), 0, s, pred, n, rt, n_depths,
+                     nodes, list, list_len, list_cap, prefix, learning_rate, ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_update");
+  return GBDT_OK;
+}
+
+}  // extern "C"

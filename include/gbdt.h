@@ -1,0 +1,374 @@
+/*
+ * gbdt.h -- C ABI of the MI355X (gfx950) level-wise histogram GBDT hot path
+ * for squared-error boosting.
+ *
+ * What the calls compute is fixed by "Module Design: Training Core"
+ * (MPSBoost spec):
+ *   section 2 (Single Mathematical Semantics): g_i = prediction_i - label_i,
+ *     h_i = 1, score(G,H) = G^2/(H+lambda), weight(G,H) = -G/(H+lambda),
+ *     gain = 0.5*(score_left + score_right - score_parent) - gamma;
+ *   section 3 (Tree Model): flat node array, stable tie-break (larger gain,
+ *     then smaller feature, then smaller threshold bin, then the first
+ *     candidate) on strict FP64 '>', strictly positive gain, bin <=
+ *     threshold_bin goes left, parameter and child constraints;
+ *   section 4 (Backend Interface): POD views and preallocated outputs, the
+ *     caller decides when, the library decides how;
+ *   section 6 (Tree Growth): the seven level-wise steps;
+ *   section 7 (CPU Oracle): no hidden CPU fallback -- a call that cannot run
+ *     on the GPU returns an error.
+ * The per-level batching (one launch per level for all nodes, smaller child
+ * built and larger child obtained by subtraction) follows the idea of the
+ * ExaBoost PR "[cuda] hybrid level-batched tree growth" (its batched
+ * construct / subtract / find / sync and batched apply commits); the kernels
+ * are written for gfx950 from that description, not ported.
+ *
+ * Fixed-point gradients.  Within one tree the gradient of row i is carried as
+ * the int64 q_i = rint(ldexp(g_i, S)) with S = 52 - e - ceil(log2 n), where
+ * max_i |g_i| < 2^e (frexp exponent); S = 0 when every g_i is 0.  Every sum of
+ * q over any row subset is exact in int64 and, times 2^-S, exact in FP64, so
+ * histograms do not depend on the order of accumulation.
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers (hipMalloc or torch tensors) unless marked
+ *    "host".  All buffers are caller-owned; the library allocates nothing.
+ *  - stream is a hipStream_t passed as void*.  Calls enqueue work on it and
+ *    return without synchronising.  Calls on one stream run in order.
+ *  - Return value: GBDT_OK or a negative gbdt_status.  Conditions checkable
+ *    on the host are checked before anything is enqueued, and on failure no
+ *    output is touched.  Conditions only visible on the device (a bin out of
+ *    range, a fixed-point bound, an internal consistency check) are recorded
+ *    in the workspace's error word; gbdt_read_error() returns it.
+ *  - gbdt_last_error() returns a thread-local description of the last failure.
+ *  - Every call that takes a workspace needs at least gbdt_workspace_bytes()
+ *    bytes, 256-byte aligned.  Calls that share a workspace must be ordered
+ *    (same stream).  The workspace must be zero-filled once before first use
+ *    (its error word); after that the library keeps it consistent.
+ */
+#ifndef GBDT_H_
+#define GBDT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GBDT_ABI_VERSION 1
+#define GBDT_MAX_DEPTH 16       /* deepest tree the level loop supports */
+#define GBDT_MAX_FEATURES 4096
+#define GBDT_MAX_BINS 256       /* bins per feature */
+
+typedef enum {
+  GBDT_OK = 0,
+  GBDT_E_ARG = -1,          /* null / misaligned pointer, bad size or parameter */
+  GBDT_E_SHAPE = -2,        /* inconsistent shapes or capacities */
+  GBDT_E_RANGE = -3,        /* a value out of range: bin >= n_bins, non-finite g */
+  GBDT_E_OVERFLOW = -4,     /* a fixed-point bound would be exceeded */
+  GBDT_E_DEVICE = -5,       /* HIP runtime error */
+  GBDT_E_UNSUPPORTED = -6,  /* shape outside what the kernels support */
+  GBDT_E_INTERNAL = -7      /* a device-side consistency check failed */
+} gbdt_status;
+
+/* Node flags. */
+#define GBDT_NODE_LEAF 1u
+
+/*
+ * Bin matrix, column-blocked.  Features are cut into n_blocks contiguous
+ * groups of block_features (the last group may be shorter).  Block b is a
+ * row-major [row_capacity][block_stride] uint8 array starting at
+ * bins + b * row_capacity * block_stride; byte j of a row in block b is
+ * feature b * block_features + j (bytes past the block's features are
+ * padding).  block_stride is a multiple of 4, so each row of a block is a run
+ * of whole dwords that consecutive lanes load with coalesced accesses.
+ * Host struct holding a device pointer.
+ */
+typedef struct gbdt_matrix {
+  uint8_t* bins;
+  int64_t n_rows;
+  int64_t row_capacity;
+  int32_t n_features;
+  int32_t n_blocks;
+  int32_t block_features;
+  int32_t block_stride;
+} gbdt_matrix;
+
+/*
+ * Feature table (host struct, device arrays).  n_bins[f] in [1, 256];
+ * bin_offset[f] = sum of n_bins[g] for g < f (bin_offset[F] = total_bins);
+ * bin_feature[b] = the feature of global bin b ([total_bins]); skip_bin[f] is
+ * a bin of feature f whose count and gradient sum the histogram kernel
+ * derives from the node total instead of accumulating (the most frequent bin,
+ * set by gbdt_pack_matrix), or -1.  The choice changes speed only, never a
+ * bit of the result.  max_block_bins sizes the histogram kernel's LDS; it
+ * must be at least the bin count of every feature block (written by
+ * gbdt_choose_blocking).
+ */
+typedef struct gbdt_features {
+  int32_t n_features;
+  int32_t total_bins;
+  int32_t max_block_bins; /* host value: most bins in one feature block of the matrix */
+  int32_t pad;
+  const int32_t* n_bins;
+  const int32_t* bin_offset;
+  const int32_t* bin_feature;
+  int32_t* skip_bin;
+} gbdt_features;
+
+/*
+ * Rows in one order: the bin matrix, the fixed-point gradients q and the
+ * original row id of each position (rid == NULL means position == row id).
+ * Host struct holding device pointers.
+ */
+typedef struct gbdt_rows {
+  gbdt_matrix X;
+  int64_t* q;
+  int32_t* rid;
+} gbdt_rows;
+
+/*
+ * Flat breadth-first tree node (Training Core, section 3).  Leaves carry
+ * GBDT_NODE_LEAF, feature = threshold_bin = left = right = -1, gain = 0 and
+ * their weight in leaf_value; internal nodes carry the split, the child ids
+ * and the gain, and leaf_value = 0.  The working fields say where the node's
+ * rows sit in the row order of its level: positions [begin, begin + count),
+ * with gsum = sum of q over them.
+ */
+typedef struct gbdt_node {
+  int32_t feature;
+  int32_t threshold_bin;
+  int32_t left;
+  int32_t right;
+  double leaf_value;
+  double gain;
+  uint32_t flags;
+  int32_t depth;
+  int32_t begin;
+  int32_t count;
+  int64_t gsum;
+  int64_t reserved;
+} gbdt_node; /* 64 bytes */
+
+/*
+ * Best split of a node: FP64 gain, split feature and bin, and the left
+ * child's fixed-point gradient sum and row count.  valid = 1 iff a candidate
+ * with strictly positive gain passed every constraint.
+ */
+typedef struct gbdt_split {
+  double gain;
+  int32_t feature;
+  int32_t threshold_bin;
+  int64_t g_left;
+  int32_t n_left;
+  int32_t valid;
+} gbdt_split; /* 32 bytes */
+
+/* Sibling triple for subtraction: hist[larger] = hist[parent] - hist[smaller]. */
+typedef struct gbdt_pair {
+  int32_t parent;
+  int32_t smaller;
+  int32_t larger;
+  int32_t pad;
+} gbdt_pair;
+
+/*
+ * Training parameters (Training Core, section 3): min_samples_leaf >= 1,
+ * min_child_weight >= 0, reg_lambda >= 0, gamma >= 0, every float finite;
+ * 0 <= max_depth <= GBDT_MAX_DEPTH.  Host struct.
+ */
+typedef struct gbdt_params {
+  double reg_lambda;
+  double gamma;
+  double min_child_weight;
+  double learning_rate;
+  int32_t min_samples_leaf;
+  int32_t max_depth;
+} gbdt_params;
+
+/* ---------------------------------------------------------------- setup -- */
+
+/* Library ABI version (GBDT_ABI_VERSION). */
+int gbdt_abi_version(void);
+
+/* Thread-local text describing the last non-OK status of this thread. */
+const char* gbdt_last_error(void);
+
+/* Parameter rules of Training Core section 3: GBDT_OK or GBDT_E_ARG. */
+int gbdt_validate_params(const gbdt_params* p /* host */);
+
+/*
+ * Workspace size for every call below, for matrices of up to n_rows rows,
+ * lists of up to max_list entries and histograms of total_bins bins.
+ */
+size_t gbdt_workspace_bytes(int64_t n_rows, int32_t max_list, int32_t total_bins);
+
+/*
+ * Column blocking for features with n_bins_host[f] bins (host array): writes
+ * n_features, n_blocks, block_features and block_stride of *X and
+ * *max_block_bins, so that one block holds at most 64 features and its
+ * histogram fits a workgroup's LDS budget (7936 bins).
+ */
+int gbdt_choose_blocking(int32_t n_features, const int32_t* n_bins_host, gbdt_matrix* X /* host */,
+                         int32_t* max_block_bins /* host */);
+
+/*
+ * Packs a row-major uint8 [n_rows][n_features] bin matrix (device) into the
+ * column-blocked layout of *dst (dst->bins allocated by the caller with
+ * n_blocks * row_capacity * block_stride bytes), checks every bin against
+ * n_bins (a violation sets GBDT_E_RANGE in the error word) and writes
+ * ft->skip_bin (most frequent bin of each feature, smallest on ties).
+ * Setup step, not part of the per-tree path.
+ */
+int gbdt_pack_matrix(const uint8_t* rowmajor, const gbdt_matrix* dst /* host */,
+                     const gbdt_features* ft /* host */, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Diagnostics (Training Core section 4, diagnostics()): per-kernel device
+ * time.  While enabled, each kernel launch of the library is bracketed by two
+ * hipEvents on its stream (up to `capacity` launches are kept).
+ * gbdt_diag_read waits for the last one, copies (kind, milliseconds) of each
+ * launch into host arrays and clears the record.  Kinds: 1 gradient max,
+ * 2 gradient grid, 3 tile planner, 4 histogram, 5 histogram partial reduce,
+ * 6 subtraction, 7 split search, 8 tree init, 9 level bookkeeping,
+ * 10 partition, 11 prediction update, 12 packing.  One process-wide record;
+ * not for concurrent use from several threads.
+ */
+int gbdt_diag_enable(int32_t capacity);
+int gbdt_diag_disable(void);
+int gbdt_diag_read(int32_t max_records, int32_t* kinds /* host */, float* ms /* host */,
+                   int32_t* n_out /* host */);
+
+/* Reads (synchronously) and clears the workspace error word. */
+int gbdt_read_error(void* ws, void* stream);
+
+/* ------------------------------------------------------- hot-path calls -- */
+
+/*
+ * Step 1 of a tree (Training Core section 2): g_i = pred_i - (double)label_i,
+ * h_i = 1 (not stored), the per-tree grid S and q_i = rint(ldexp(g_i, S)).
+ * Writes q[n], *scale (S) and *gsum (sum of q) in device memory; nothing is
+ * read back.  A non-finite g sets GBDT_E_RANGE.
+ */
+int gbdt_compute_gradients(const double* pred, const float* label, int64_t n, int64_t* q,
+                           int32_t* scale, int64_t* gsum, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * Step 2 (Training Core sections 6-7): for every node v = list[j],
+ * j < *list_len (device count), adds to hist_g[v][b] / hist_cnt[v][b] the sum
+ * of q and the number of rows among positions [nodes[v].begin,
+ * nodes[v].begin + nodes[v].count) of src whose bin of feature f equals c,
+ * for every global bin b = bin_offset[f] + c.  The slots of listed nodes must
+ * be zero on entry for an overwrite (they are accumulated into, so shards can
+ * be added).  hist_g, hist_cnt: [slots][total_bins], slot = node id.
+ * rows_bound bounds the sum of the listed counts (sizes the launch);
+ * list_cap bounds *list_len.  Requires |q_i| <= 2^(52 - ceil(log2 n_rows))
+ * (as written by gbdt_compute_gradients); a violation sets GBDT_E_OVERFLOW.
+ */
+int gbdt_build_histograms(const gbdt_rows* src /* host */, const gbdt_features* ft /* host */,
+                          const gbdt_node* nodes, const int32_t* list, const int32_t* list_len,
+                          int32_t list_cap, int64_t rows_bound, int64_t* hist_g,
+                          uint32_t* hist_cnt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sibling subtraction: for each pairs[j], j < *n_pairs,
+ * hist[larger] = hist[parent] - hist[smaller] elementwise over G (int64) and
+ * count (uint32).  Exact, so identical to building the larger child directly.
+ * A count that would go negative sets GBDT_E_INTERNAL.
+ */
+int gbdt_subtract_histograms(int64_t* hist_g, uint32_t* hist_cnt, int32_t total_bins,
+                             const gbdt_pair* pairs, const int32_t* n_pairs, int32_t pair_cap,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Steps 3-4 (Training Core sections 2-3): for each node v = list[j], scans
+ * every candidate (f, t), t in [0, n_bins[f]-2], of hist[v]: left = bins
+ * <= t, right = the rest; a candidate competes only if both children have
+ * >= min_samples_leaf rows, Hessian >= min_child_weight and Hessian > 0; the
+ * gain is evaluated in FP64 as 0.5*((s_L + s_R) - s_P) - gamma with
+ * s = (G*G)/(H+lambda), G = ldexp(sum q, -S), H = count (IEEE operations in
+ * that order, no contraction).  splits[v] gets the candidate with the largest
+ * gain, ties to the smaller feature, then the smaller bin; valid = 1 iff that
+ * gain is strictly positive.  Node totals come from nodes[v].gsum / count;
+ * S from *scale.
+ */
+int gbdt_find_best_splits(const int64_t* hist_g, const uint32_t* hist_cnt,
+                          const gbdt_features* ft /* host */, const gbdt_node* nodes,
+                          const int32_t* list, const int32_t* list_len, int32_t list_cap,
+                          const gbdt_params* p /* host */, const int32_t* scale,
+                          gbdt_split* splits, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 5 (Training Core section 3 routing, section 6 step 5): for each node
+ * v = list[j] with s = splits[v], the rows at positions [begin, begin+count)
+ * of src (bins of every block, q and row id) are written to the same
+ * positions of dst, rows with bin(s.feature) <= s.threshold_bin first, each
+ * side in its original order (stable).  Rows of unlisted nodes are not
+ * touched.  The left count must equal s.n_left, else GBDT_E_INTERNAL.
+ * dst->rid must be non-NULL; src->rid == NULL means identity.
+ */
+int gbdt_partition_rows(const gbdt_rows* src /* host */, const gbdt_rows* dst /* host */,
+                        const gbdt_node* nodes, const gbdt_split* splits, const int32_t* list,
+                        const int32_t* list_len, int32_t list_cap, int64_t rows_bound, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * Step 7 (Training Core section 6; ensemble sum of "Gradient boosted trees
+ * (spec model)", Forward pass): for each leaf v = list[j], every row id r at
+ * positions [begin, begin+count) of rid_by_depth[nodes[v].depth] (NULL entry
+ * = identity) gets pred[r] = pred[r] + (learning_rate * leaf_value), two
+ * roundings.  rid_by_depth is a host array of n_depths device pointers.
+ */
+int gbdt_update_predictions(double* pred, int64_t n, const int32_t* const* rid_by_depth,
+                            int32_t n_depths, const gbdt_node* nodes, const int32_t* list,
+                            const int32_t* list_len, int32_t list_cap, double learning_rate,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------ level-wise driver -- */
+
+/*
+ * Device buffers for gbdt_grow_tree (host struct of device pointers); sizes
+ * from gbdt_grow_sizes.  pp[0], pp[1]: two row orders (bins in the blocking
+ * of X, q, rid) used in turn by the partition of each level.
+ */
+typedef struct gbdt_grow_buffers {
+  gbdt_rows pp[2];
+  int64_t* q;            /* [n] gradients in row-id order */
+  int64_t* hist_g;       /* [hist_slots][total_bins] */
+  uint32_t* hist_cnt;    /* [hist_slots][total_bins] */
+  gbdt_split* splits;    /* [max_nodes] */
+  int32_t* lists;        /* [list_words] */
+  void* ctrl;            /* [ctrl_bytes] */
+  void* ws;
+  size_t ws_bytes;
+} gbdt_grow_buffers;
+
+/* Sizes (in elements / bytes as named) of the driver's buffers. */
+typedef struct gbdt_grow_sizes_t {
+  int64_t max_nodes;     /* 2^(max_depth+1) - 1 */
+  int64_t hist_slots;    /* 2^max_depth - 1 (at least 1) */
+  int64_t list_words;
+  int64_t ctrl_bytes;
+  int64_t ws_bytes;
+} gbdt_grow_sizes_t;
+
+int gbdt_grow_sizes(int64_t n_rows, int32_t total_bins, int32_t max_depth,
+                    gbdt_grow_sizes_t* out /* host */);
+
+/*
+ * One boosting step (Training Core section 6, steps 1-7): gradients from
+ * pred and label, the tree grown level by level into nodes_out
+ * ([max_nodes], breadth-first; *n_nodes_dev gets the node count), and
+ * pred updated with learning_rate times the leaf weights.  All levels are
+ * enqueued without host synchronisation.
+ */
+int gbdt_grow_tree(const gbdt_matrix* X /* host */, const gbdt_features* ft /* host */,
+                   const float* label, double* pred, const gbdt_params* p /* host */,
+                   gbdt_node* nodes_out, int32_t* n_nodes_dev, const gbdt_grow_buffers* b /* host */,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GBDT_H_ */

@@ -1,0 +1,137 @@
+"""Host-side checks of the C-ABI library: it loads without a GPU, exports every
+entry point include/gbdt.h declares, and validates arguments before any
+device work (parameter rules of "Module Design: Training Core", section 3)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import histogram_split_finding_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    txt = open(os.path.join(ROOT, "include", "gbdt.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(gbdt_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = g.load()
+    names = _declared_functions()
+    assert len(names) >= 14
+    for name in ["gbdt_compute_gradients", "gbdt_build_histograms", "gbdt_subtract_histograms",
+                 "gbdt_find_best_splits", "gbdt_partition_rows", "gbdt_update_predictions"]:
+        assert name in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert g.gbdt_abi_version() == 1
+
+
+def test_library_is_not_linked_to_the_oracle():
+    import subprocess
+    out = subprocess.run(["nm", "-D", g.LIB_PATH], capture_output=True, text=True).stdout
+    assert "orc_" not in out
+    ldd = subprocess.run(["ldd", g.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in ldd
+
+
+@pytest.mark.parametrize("bad", [
+    dict(min_samples_leaf=0), dict(min_child_weight=-1.0), dict(reg_lambda=-0.5), dict(gamma=-1e-9),
+    dict(reg_lambda=float("inf")), dict(gamma=float("nan")), dict(learning_rate=float("nan")),
+    dict(max_depth=-1), dict(max_depth=17),
+])
+def test_parameter_rules(bad):
+    kw = dict(max_depth=3)
+    kw.update(bad)
+    assert g.gbdt_validate_params(g.make_params(**kw)) == -1
+    assert g.last_error()
+    assert g.gbdt_validate_params(g.make_params(max_depth=3)) == 0
+
+
+@pytest.mark.parametrize("nbins", [[32] * 8, [256] * 32, [256] * 10 + [2] * 44, [256] * 100, [64] * 28,
+                                   [2] * 200, [7, 256, 3] * 11, [1] * 5])
+def test_blocking_fits_budget(nbins):
+    X, mbb = g.gbdt_choose_blocking(nbins)
+    F = len(nbins)
+    assert X.n_blocks * X.block_features >= F > (X.n_blocks - 1) * X.block_features
+    assert X.block_stride % 4 == 0 and X.block_stride >= X.block_features and X.block_features <= 64
+    worst = max(sum(nbins[f0:f0 + X.block_features]) for f0 in range(0, F, X.block_features))
+    assert mbb == worst <= 7936
+
+
+def test_blocking_rejects_bad_bins():
+    with pytest.raises(g.GbdtError):
+        g.gbdt_choose_blocking([0, 4])
+    with pytest.raises(g.GbdtError):
+        g.gbdt_choose_blocking([257])
+
+
+def test_sizes():
+    s = g.gbdt_grow_sizes(581012, 2648, 10)
+    assert s.max_nodes == 2047 and s.hist_slots == 1023
+    assert s.ws_bytes == g.gbdt_workspace_bytes(581012, 1024, 2648)
+    s0 = g.gbdt_grow_sizes(10, 4, 0)
+    assert s0.max_nodes == 1 and s0.hist_slots == 1
+    with pytest.raises(g.GbdtError):
+        g.gbdt_grow_sizes(0, 4, 3)
+    with pytest.raises(g.GbdtError):
+        g.gbdt_grow_sizes(10, 4, 17)
+
+
+def test_null_arguments_fail_before_device_work():
+    lib = g.load()
+    # every hot-path call checks its pointers on the host and returns GBDT_E_ARG
+    assert lib.gbdt_compute_gradients(None, None, 10, None, None, None, None, 0, None) == -1
+    assert lib.gbdt_build_histograms(None, None, None, None, None, 1, 1, None, None, None, 0, None) == -1
+    assert lib.gbdt_subtract_histograms(None, None, 4, None, None, 1, None, 0, None) == -1
+    assert lib.gbdt_find_best_splits(None, None, None, None, None, None, 1, None, None, None, None, 0,
+                                     None) == -1
+    assert lib.gbdt_partition_rows(None, None, None, None, None, None, 1, 1, None, 0, None) == -1
+    assert lib.gbdt_update_predictions(None, 10, None, 1, None, None, None, 1, 0.3, None, 0, None) == -1
+    assert lib.gbdt_grow_tree(None, None, None, None, None, None, None, None, None) == -1
+
+
+def test_workspace_and_shape_checks():
+    lib = g.load()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: rejected on the host
+    X = g.Matrix(fake, 100, 100, 4, 1, 4, 4)
+    ft = g.Features(4, 16, 16, 0, fake, fake, fake, None)
+    src = g.Rows(X, fake, None)
+    # workspace too small
+    rc = lib.gbdt_build_histograms(ctypes.byref(src), ctypes.byref(ft), fake, fake, fake, 4, 100, fake,
+                                   fake, fake, 16, None)
+    assert rc == -1 and "workspace" in g.last_error()
+    # misaligned workspace
+    rc = lib.gbdt_build_histograms(ctypes.byref(src), ctypes.byref(ft), fake, fake, fake, 4, 100, fake,
+                                   fake, ctypes.c_void_p((1 << 20) + 8), 1 << 30, None)
+    assert rc == -1
+    # bad blocking
+    Xb = g.Matrix(fake, 100, 100, 4, 2, 4, 4)
+    srcb = g.Rows(Xb, fake, None)
+    rc = lib.gbdt_build_histograms(ctypes.byref(srcb), ctypes.byref(ft), fake, fake, fake, 4, 100, fake,
+                                   fake, fake, 1 << 30, None)
+    assert rc == -2
+    # row_capacity < n_rows
+    Xc = g.Matrix(fake, 100, 50, 4, 1, 4, 4)
+    srcc = g.Rows(Xc, fake, None)
+    rc = lib.gbdt_build_histograms(ctypes.byref(srcc), ctypes.byref(ft), fake, fake, fake, 4, 100, fake,
+                                   fake, fake, 1 << 30, None)
+    assert rc == -2
+    # feature table mismatch
+    ft2 = g.Features(5, 16, 16, 0, fake, fake, fake, None)
+    rc = lib.gbdt_build_histograms(ctypes.byref(src), ctypes.byref(ft2), fake, fake, fake, 4, 100, fake,
+                                   fake, fake, 1 << 30, None)
+    assert rc == -2
+    # invalid parameters are rejected by the split search before any launch
+    p = g.make_params(3, min_samples_leaf=0)
+    rc = lib.gbdt_find_best_splits(fake, fake, ctypes.byref(ft), fake, fake, fake, 4, ctypes.byref(p), fake,
+                                   fake, fake, 1 << 30, None)
+    assert rc == -1
+    # an empty list is a no-op that needs no device
+    rc = lib.gbdt_build_histograms(ctypes.byref(src), ctypes.byref(ft), fake, fake, fake, 0, 0, fake,
+                                   fake, fake, 1 << 30, None)
+    assert rc == 0
