@@ -297,23 +297,32 @@ def test_partition_count_mismatch_is_reported():
 # --------------------------------------------------------- prediction update --
 
 def test_update_predictions():
+    """Leaves whose rows sit in the row orders of different depths; as in a
+    real tree every row belongs to exactly one leaf."""
     say("update_predictions")
     rng = np.random.default_rng(8)
     n = 70000
     pred = rng.normal(size=n)
+    cuts = [0, 5, 9000, 9001, 40000, n]
+    depths = [j % 3 for j in range(len(cuts) - 1)]
+    # final arrangement: identity on the positions of depth-0 leaves, a random
+    # permutation of the other rows elsewhere
+    pi = np.arange(n, dtype=np.int32)
+    other = np.concatenate([np.arange(cuts[j], cuts[j + 1]) for j in range(len(cuts) - 1) if depths[j] != 0])
+    pi[other] = rng.permutation(other).astype(np.int32)
     ridA = rng.permutation(n).astype(np.int32)
     ridB = rng.permutation(n).astype(np.int32)
-    # leaves: cover every position of the row order of their depth
     leaves, expect = [], pred.copy()
-    cuts = [0, 5, 9000, 9001, 40000, n]
     eta = 0.3
     for j in range(len(cuts) - 1):
-        depth = j % 3
+        b, e, d = cuts[j], cuts[j + 1], depths[j]
         w = float(rng.normal())
-        leaves.append(dict(begin=cuts[j], count=cuts[j + 1] - cuts[j], depth=depth, leaf_value=w,
-                           flags=1))
-        rid = [np.arange(n, dtype=np.int32), ridA, ridB][depth]
-        idx = rid[cuts[j]:cuts[j + 1]]
+        leaves.append(dict(begin=b, count=e - b, depth=d, leaf_value=w, flags=1))
+        if d == 1:
+            ridA[b:e] = pi[b:e]
+        if d == 2:
+            ridB[b:e] = pi[b:e]
+        idx = pi[b:e]
         expect[idx] = expect[idx] + eta * w
     dpred = to_dev(pred)
     ws = _ws(n, len(leaves), 1)
