@@ -23,12 +23,26 @@ static_assert(sizeof(WsCtrl) == 256, "control block is 256 bytes");
 constexpr int kGradBlocks = 1024;     // grid of the gradient kernels
 constexpr int kPartTileRows = 2048;   // rows per partition tile
 constexpr int kUpdTileRows = 4096;    // rows per prediction-update tile
-constexpr int kHistMinTileRows = 1024;
+constexpr int kHistMinTileRows = 2048;
 constexpr int kHistTargetTiles = 1024;
-constexpr int kLdsHistBudgetBins = 7936;  // uint64 LDS slots per histogram workgroup (62 KiB)
+constexpr int kLdsHistBudgetBins = 7680;  // histogram bins per feature block (60 KiB of LDS)
+constexpr int kLdsHistSlack = 256;         // extra LDS slots: any bin byte stays inside the allocation
+
+// Work assignment of one tile (written by the planner).
+struct TileDesc {
+  int32_t node;    // node id
+  int32_t r0, r1;  // rows [r0, r1) of the tile
+  int32_t ntiles;  // tiles of the node
+  int32_t tfirst;  // first tile of the node
+  int32_t j;       // list position of the node
+  int32_t begin;   // the node's segment
+  int32_t count;
+};
+static_assert(sizeof(TileDesc) == 32, "tile descriptor is 32 bytes");
 
 struct WsLayout {
   size_t ctrl;        // WsCtrl
+  size_t tdesc;       // TileDesc[tdesc_cap]
   size_t gpart;       // double[kGradBlocks]
   size_t prefix;      // int32[max_list + 2]
   size_t status;      // uint64[status_cap]
@@ -36,6 +50,7 @@ struct WsLayout {
   size_t total;
   int64_t status_cap;
   int64_t hpart_tiles;
+  int64_t tdesc_cap;
 };
 
 WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins);

@@ -76,9 +76,12 @@ WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
   if (total_bins < 1) total_bins = 1;
   L.status_cap = (n_rows + kPartTileRows - 1) / kPartTileRows + int64_t(max_list) + 2;
   L.hpart_tiles = int64_t(kHistTargetTiles) + int64_t(max_list) + 2;
+  L.tdesc_cap = L.status_cap > L.hpart_tiles ? L.status_cap : L.hpart_tiles;
   size_t off = 0;
   L.ctrl = off;
   off = align256(off + sizeof(WsCtrl));
+  L.tdesc = off;
+  off = align256(off + sizeof(TileDesc) * size_t(L.tdesc_cap));
   L.gpart = off;
   off = align256(off + sizeof(double) * kGradBlocks);
   L.prefix = off;
@@ -166,16 +169,21 @@ __device__ __forceinline__ int32_t clamp_len(const int32_t* len, int32_t cap) {
 
 // ---------------------------------------------------------------- planner --
 // One workgroup: tiles per listed node (at least one), their exclusive
-// prefix, the total, and (optionally) a cleared look-back status array and
-// ticket for the launch that follows.
+// prefix, the total, one descriptor per tile (so a workgroup of the launch
+// that follows reads its whole assignment with a single load), and
+// (optionally) a cleared look-back status array and ticket.
+constexpr int kPlanLdsEntries = 8192;
+
 __global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nodes,
                                                const int32_t* __restrict__ list,
                                                const int32_t* __restrict__ list_len,
                                                int32_t list_cap, int32_t tile_rows,
                                                int32_t max_tiles, int32_t* __restrict__ prefix,
+                                               TileDesc* __restrict__ desc,
                                                WsCtrl* __restrict__ ctrl,
                                                uint64_t* __restrict__ status) {
   __shared__ int32_t sh[32];
+  __shared__ int32_t spre[kPlanLdsEntries + 1];
   int32_t raw = *list_len;
   if (threadIdx.x == 0 && (raw < 0 || raw > list_cap)) dev_error(&ctrl->err, GBDT_E_SHAPE);
   const int32_t n = clamp_len(list_len, list_cap);
@@ -189,21 +197,46 @@ __global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nod
   }
   int32_t total;
   int32_t excl = block_exclusive_scan(local, &total, sh);
+  const bool in_lds = n <= kPlanLdsEntries;
   for (int32_t j = j0; j < j0 + per && j < n; ++j) {
     prefix[j] = excl;
+    if (in_lds) spre[j] = excl;
     int32_t c = nodes[list[j]].count;
     if (c < 0) c = 0;
     excl += c == 0 ? 1 : (c + tile_rows - 1) / tile_rows;
   }
   if (threadIdx.x == 0) {
     prefix[n] = total;
+    if (in_lds) spre[n] = total;
     if (total > max_tiles) dev_error(&ctrl->err, GBDT_E_SHAPE);
-    ctrl->plan_total = total;
+    ctrl->plan_total = total < max_tiles ? total : max_tiles;
     ctrl->ticket = 0u;
   }
-  if (status != nullptr) {
-    const int32_t lim = total < max_tiles ? total : max_tiles;
-    for (int32_t t = threadIdx.x; t < lim; t += blockDim.x) status[t] = 0ull;
+  __syncthreads();
+  const int32_t lim = total < max_tiles ? total : max_tiles;
+  for (int32_t t = threadIdx.x; t < lim; t += blockDim.x) {
+    const int32_t* pre = in_lds ? spre : prefix;
+    int32_t lo = 0, hi = n - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int32_t v = list[lo];
+    const gbdt_node nd = nodes[v];
+    const int32_t tf = pre[lo];
+    const int32_t nt = pre[lo + 1] - tf;
+    const int32_t cnt = nd.count < 0 ? 0 : nd.count;
+    TileDesc d;
+    d.node = v;
+    d.r0 = nd.begin + (t - tf) * tile_rows;
+    d.r1 = d.r0 + tile_rows < nd.begin + cnt ? d.r0 + tile_rows : nd.begin + cnt;
+    d.ntiles = nt;
+    d.tfirst = tf;
+    d.j = lo;
+    d.begin = nd.begin;
+    d.count = cnt;
+    desc[t] = d;
+    if (status != nullptr) status[t] = 0ull;
   }
 }
 
@@ -276,37 +309,83 @@ __global__ void __launch_bounds__(256) k_grad_q(const double* __restrict__ pred,
 }
 
 // -------------------------------------------------------------- histogram --
+constexpr int kHistThreads = 1024;
+
+// Vector load of UNIT bytes (4, 8 or 16) as dwords.
+template <int UNIT>
+struct VecLoad;
+template <>
+struct VecLoad<4> {
+  static __device__ __forceinline__ void load(const uint8_t* p, uint32_t* d) {
+    d[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+  static __device__ __forceinline__ void store(uint8_t* p, const uint32_t* d) {
+    *reinterpret_cast<uint32_t*>(p) = d[0];
+  }
+};
+template <>
+struct VecLoad<8> {
+  static __device__ __forceinline__ void load(const uint8_t* p, uint32_t* d) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    d[0] = v.x;
+    d[1] = v.y;
+  }
+  static __device__ __forceinline__ void store(uint8_t* p, const uint32_t* d) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(d[0], d[1]);
+  }
+};
+template <>
+struct VecLoad<16> {
+  static __device__ __forceinline__ void load(const uint8_t* p, uint32_t* d) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+  }
+  static __device__ __forceinline__ void store(uint8_t* p, const uint32_t* d) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+};
+
+// Widest of 16, 8, 4 bytes that divides the row stride of a block.
+inline int load_unit_for(int32_t block_stride) {
+  if (block_stride % 16 == 0) return 16;
+  if (block_stride % 8 == 0) return 8;
+  return 4;
+}
+
 // One workgroup = one (tile of one node's rows, feature block).  Lanes are
-// laid out as (row group, dword column): lane reads the dword of 4 bins at
-// its column for rows rg, rg + rows_per_iter, ... of the tile (consecutive
-// lanes read consecutive dwords, so a wave streams contiguous bytes), and
-// adds the packed cell (q << bits) + 1 to the LDS slot of each bin with a
-// 64-bit LDS atomic.  Each feature's skip bin is not accumulated: it is set
-// afterwards to the tile total minus the feature's other bins (exact
-// integers).  A node covered by one tile writes its decoded histogram
-// straight to hist; otherwise the tile writes its packed partial and
-// k_hist_reduce sums the partials.
-__global__ void __launch_bounds__(256) k_hist(
+// laid out as (row group, column of UNIT bytes): a lane loads UNIT bins of a
+// row with one vector load (consecutive lanes read consecutive bytes, so a
+// wave streams contiguous memory) and adds the packed cell (q << bits) + 1 to
+// the LDS slot of each bin with a 64-bit LDS atomic.  Loads of BATCH rows are
+// issued before their atomics so each wave keeps several loads in flight.
+// Each feature's skip bin is not accumulated: it is set afterwards to the
+// tile total minus the feature's other bins (exact integers).  A node
+// covered by one tile writes its decoded histogram straight to hist;
+// otherwise the tile writes its packed partial for k_hist_reduce.
+template <int UNIT>
+__global__ void __launch_bounds__(kHistThreads) k_hist(
     const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t block_features,
     int32_t block_stride, int32_t n_features, const int64_t* __restrict__ q,
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ skip_bin,
-    int32_t total_bins, const gbdt_node* __restrict__ nodes, const int32_t* __restrict__ list,
-    const int32_t* __restrict__ list_len, int32_t list_cap, const int32_t* __restrict__ prefix,
-    int32_t tile_rows, int32_t bits, int64_t q_bound, int64_t* __restrict__ hist_g,
-    uint32_t* __restrict__ hist_cnt, uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl) {
+    int32_t total_bins, const TileDesc* __restrict__ desc, int32_t bits, int64_t q_bound,
+    int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt, uint64_t* __restrict__ partial,
+    WsCtrl* __restrict__ ctrl) {
+  constexpr int NB = UNIT;                 // bins per lane per row
+  constexpr int BATCH = UNIT == 4 ? 4 : 32 / UNIT;  // rows per lane per step (4, 4, 2)
+  constexpr int NW = kHistThreads / 64;
   extern __shared__ uint64_t lds[];
-  __shared__ uint64_t sh_tot[4];
-  const int32_t n = clamp_len(list_len, list_cap);
+  __shared__ uint64_t sh_tot[NW];
   const int32_t tile = blockIdx.x;
-  if (n == 0 || tile >= prefix[n]) return;
-  const int32_t j = find_tile_owner(prefix, n, tile);
-  const int32_t v = list[j];
-  const int32_t ntiles = prefix[j + 1] - prefix[j];
-  const int32_t tin = tile - prefix[j];
-  const gbdt_node nd = nodes[v];
-  const int64_t r0 = int64_t(nd.begin) + int64_t(tin) * tile_rows;
-  int64_t r1 = r0 + tile_rows;
-  if (r1 > int64_t(nd.begin) + nd.count) r1 = int64_t(nd.begin) + nd.count;
+  const int32_t total = ctrl->plan_total;
+  const TileDesc td = desc[tile];
+  if (tile >= total) return;
+  const int32_t v = td.node;
+  const int32_t ntiles = td.ntiles;
+  const int64_t r0 = td.r0;
+  const int64_t r1 = td.r1;
 
   const int32_t blk = blockIdx.y;
   const int32_t f0 = blk * block_features;
@@ -315,62 +394,77 @@ __global__ void __launch_bounds__(256) k_hist(
   const int32_t lb0 = bin_offset[f0];
   const int32_t nbb = bin_offset[f1] - lb0;
 
-  for (int32_t b = threadIdx.x; b < nbb; b += blockDim.x) lds[b] = 0ull;
+  for (int32_t b = threadIdx.x; b < nbb; b += kHistThreads) lds[b] = 0ull;
 
-  const int32_t lpr = block_stride >> 2;         // lanes per row
-  const int32_t rpi = blockDim.x / lpr;          // rows per iteration
+  const int32_t lpr = block_stride / UNIT;  // lanes per row
+  const int32_t rpi = kHistThreads / lpr;   // rows per step of the workgroup
   const int32_t col = threadIdx.x % lpr;
   const int32_t rg = threadIdx.x / lpr;
-  int32_t base[4];
-  int32_t skip[4];
-  int32_t nb[4];
+  // per byte of the lane's column: LDS slot base and skip bin.  Padding bytes
+  // (past the block's features) are always 0 and get skip bin 0, so they
+  // never reach an atomic.  Bins are range-checked when the matrix is packed;
+  // here any byte value stays inside the LDS allocation (kLdsHistSlack).
+  int32_t base[NB];
+  int32_t skip[NB];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int32_t f = f0 + 4 * col + m;
+  for (int m = 0; m < NB; ++m) {
+    const int32_t f = f0 + UNIT * col + m;
     const bool ok = (f < f1) && (rg < rpi);
     base[m] = ok ? bin_offset[f] - lb0 : 0;
-    nb[m] = ok ? bin_offset[f + 1] - bin_offset[f] : 0;
-    skip[m] = ok ? (skip_bin != nullptr ? skip_bin[f] : -1) : -1;
+    skip[m] = ok ? (skip_bin != nullptr ? skip_bin[f] : -1) : 0;
   }
   __syncthreads();
 
-  const uint8_t* __restrict__ bb = bins + int64_t(blk) * row_capacity * block_stride + 4 * col;
+  const uint8_t* __restrict__ bb = bins + int64_t(blk) * row_capacity * block_stride + UNIT * col;
   uint64_t tot = 0ull;
-  bool bad_q = false;
-  bool bad_bin = false;
+  int64_t qmax = 0;
   if (rg < rpi) {
-    for (int64_t r = r0 + rg; r < r1; r += rpi) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(bb + r * block_stride);
-      const int64_t qq = q[r];
-      bad_q |= (qq > q_bound) || (qq < -q_bound);
-      const uint64_t pk = ((uint64_t)qq << bits) + 1ull;
-      tot += pk;
+    for (int64_t r = r0 + rg; r < r1; r += int64_t(BATCH) * rpi) {
+      uint32_t w[BATCH][UNIT / 4];
+      uint64_t pk[BATCH];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int32_t b = (w >> (8 * m)) & 0xff;
-        if (nb[m] > 0) {
-          bad_bin |= b >= nb[m];
-          if (b != skip[m] && b < nb[m])
-            __hip_atomic_fetch_add(&lds[base[m] + b], pk, __ATOMIC_RELAXED,
+      for (int u = 0; u < BATCH; ++u) {
+        const int64_t rr = r + int64_t(u) * rpi;
+        const bool ok = rr < r1;
+        if (ok) {
+          VecLoad<UNIT>::load(bb + rr * block_stride, w[u]);
+        } else {
+#pragma unroll
+          for (int x = 0; x < UNIT / 4; ++x) w[u][x] = 0u;
+        }
+        const int64_t qq = ok ? q[rr] : 0;
+        const int64_t aq = qq < 0 ? -qq : qq;
+        qmax = aq > qmax ? aq : qmax;
+        pk[u] = ok ? ((uint64_t)qq << bits) + 1ull : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        if (pk[u] == 0ull) continue;  // past the tile end (a real cell is odd)
+        tot += pk[u];
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+          const uint32_t b = (w[u][m >> 2] >> (8 * (m & 3))) & 0xffu;
+          if ((int32_t)b != skip[m])
+            __hip_atomic_fetch_add(&lds[base[m] + b], pk[u], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
         }
       }
     }
   }
-  if (bad_q) dev_error(&ctrl->err, GBDT_E_OVERFLOW);
-  if (bad_bin) dev_error(&ctrl->err, GBDT_E_RANGE);
-  // tile total: every row was added once by each lane of its row group; take
-  // the column-0 lanes only
+  if (qmax > q_bound) dev_error(&ctrl->err, GBDT_E_OVERFLOW);
+  // tile total from the column-0 lanes (one per row)
   uint64_t t0 = (col == 0 && rg < rpi) ? tot : 0ull;
   t0 = wave_sum(t0);
-  if ((threadIdx.x & 63) == 0) sh_tot[threadIdx.x >> 6] = t0;
-  __syncthreads();
-  const uint64_t tile_total = sh_tot[0] + sh_tot[1] + sh_tot[2] + sh_tot[3];
-
-  // skip bins: total minus the feature's other bins, one wave per feature
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  for (int32_t f = f0 + wid; f < f1; f += 4) {
+  if (lane == 0) sh_tot[wid] = t0;
+  __syncthreads();
+  uint64_t tile_total = 0ull;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tile_total += sh_tot[w];
+
+  // skip bins: total minus the feature's other bins, one wave per feature
+  for (int32_t f = f0 + wid; f < f1; f += NW) {
     const int32_t sb = skip_bin != nullptr ? skip_bin[f] : -1;
     if (sb < 0) continue;
     const int32_t fb = bin_offset[f] - lb0;
@@ -386,7 +480,7 @@ __global__ void __launch_bounds__(256) k_hist(
   if (ntiles == 1) {
     int64_t* __restrict__ hg = hist_g + int64_t(v) * total_bins + lb0;
     uint32_t* __restrict__ hc = hist_cnt + int64_t(v) * total_bins + lb0;
-    for (int32_t b = threadIdx.x; b < nbb; b += blockDim.x) {
+    for (int32_t b = threadIdx.x; b < nbb; b += kHistThreads) {
       const uint64_t x = lds[b];
       const uint64_t c = x & mask;
       hg[b] = (int64_t)(x - c) >> bits;
@@ -394,21 +488,25 @@ __global__ void __launch_bounds__(256) k_hist(
     }
   } else {
     uint64_t* __restrict__ pp = partial + int64_t(tile) * total_bins + lb0;
-    for (int32_t b = threadIdx.x; b < nbb; b += blockDim.x) pp[b] = lds[b];
+    for (int32_t b = threadIdx.x; b < nbb; b += kHistThreads) pp[b] = lds[b];
   }
 }
 
-// Sums the packed partials of every multi-tile node (in tile order; the sums
-// are exact integers, so any order gives the same bits).
-__global__ void __launch_bounds__(64) k_hist_reduce(const int32_t* __restrict__ list,
-                                                    const int32_t* __restrict__ list_len,
-                                                    int32_t list_cap,
-                                                    const int32_t* __restrict__ prefix,
-                                                    int32_t max_tiles, int32_t bits,
-                                                    int32_t total_bins,
-                                                    const uint64_t* __restrict__ partial,
-                                                    int64_t* __restrict__ hist_g,
-                                                    uint32_t* __restrict__ hist_cnt) {
+// Sums the packed partials of every multi-tile node.  A workgroup owns 64
+// bins of one node; its 16 waves take the node's tiles round-robin (loads
+// batched four deep) and combine through LDS.  The sums are exact integers,
+// so any order gives the same bits.
+__global__ void __launch_bounds__(1024) k_hist_reduce(const int32_t* __restrict__ list,
+                                                     const int32_t* __restrict__ list_len,
+                                                     int32_t list_cap,
+                                                     const int32_t* __restrict__ prefix,
+                                                     int32_t max_tiles, int32_t bits,
+                                                     int32_t total_bins,
+                                                     const uint64_t* __restrict__ partial,
+                                                     int64_t* __restrict__ hist_g,
+                                                     uint32_t* __restrict__ hist_cnt) {
+  __shared__ int64_t sg[16][64];
+  __shared__ uint64_t sc[16][64];
   const int32_t n = clamp_len(list_len, list_cap);
   const int32_t j = blockIdx.y;
   if (j >= n) return;
@@ -416,20 +514,41 @@ __global__ void __launch_bounds__(64) k_hist_reduce(const int32_t* __restrict__ 
   int32_t t1 = prefix[j + 1];
   if (t1 > max_tiles) t1 = max_tiles;  // an over-full plan is already flagged
   if (t1 - t0 <= 1) return;
-  const int32_t b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= total_bins) return;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int32_t b = blockIdx.x * 64 + lane;
+  const bool inb = b < total_bins;
   const uint64_t mask = (1ull << bits) - 1ull;
   int64_t g = 0;
   uint64_t c = 0;
-  for (int32_t t = t0; t < t1; ++t) {
-    const uint64_t x = partial[int64_t(t) * total_bins + b];
-    const uint64_t cc = x & mask;
-    g += (int64_t)(x - cc) >> bits;
-    c += cc;
+  for (int32_t t = t0 + wid; t < t1; t += 16 * 4) {
+    uint64_t x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int32_t tt = t + 16 * u;
+      x[u] = (inb && tt < t1) ? partial[int64_t(tt) * total_bins + b] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t cc = x[u] & mask;
+      g += (int64_t)(x[u] - cc) >> bits;
+      c += cc;
+    }
   }
-  const int32_t v = list[j];
-  hist_g[int64_t(v) * total_bins + b] = g;
-  hist_cnt[int64_t(v) * total_bins + b] = (uint32_t)c;
+  sg[wid][lane] = g;
+  sc[wid][lane] = c;
+  __syncthreads();
+  if (wid == 0 && inb) {
+    int64_t gg = 0;
+    uint64_t ccs = 0;
+    for (int w = 0; w < 16; ++w) {
+      gg += sg[w][lane];
+      ccs += sc[w][lane];
+    }
+    const int32_t v = list[j];
+    hist_g[int64_t(v) * total_bins + b] = gg;
+    hist_cnt[int64_t(v) * total_bins + b] = (uint32_t)ccs;
+  }
 }
 
 // ------------------------------------------------------------ subtraction --
@@ -468,34 +587,40 @@ __device__ __forceinline__ double score_of(double G, double H, double lambda) {
   return num / den;
 }
 
-// One workgroup per node.  The node's histogram is walked in chunks of 256
-// bins in global bin order (feature-major, bins ascending); a segmented
-// inclusive scan (segments = features) over each chunk gives every bin's
-// left prefix (G_L, n_L) with a carry across chunks; each candidate's gain is
-// then evaluated exactly as the formula is written.  The workgroup keeps the
-// candidate with the largest gain and, among bit-equal gains, the smallest
-// global bin index, which is the smaller feature and then the smaller bin.
-__global__ void __launch_bounds__(256) k_find(const int64_t* __restrict__ hist_g,
-                                              const uint32_t* __restrict__ hist_cnt,
-                                              const int32_t* __restrict__ bin_offset,
-                                              const int32_t* __restrict__ bin_feature,
-                                              const int32_t* __restrict__ n_bins,
-                                              int32_t total_bins,
-                                              const gbdt_node* __restrict__ nodes,
-                                              const int32_t* __restrict__ list,
-                                              const int32_t* __restrict__ list_len,
-                                              int32_t list_cap, FindParams fp,
-                                              const int32_t* __restrict__ scale,
-                                              gbdt_split* __restrict__ splits) {
-  __shared__ int64_t sw_g[4];
-  __shared__ int32_t sw_c[4];
-  __shared__ int32_t sw_f[4];
+// Better of two candidates: larger gain, then smaller global bin (the
+// smaller feature, then the smaller threshold).  Gains are only ever
+// positive here, so IEEE equality is bit equality.
+__device__ __forceinline__ bool better(double g1, int32_t b1, double g2, int32_t b2) {
+  return g1 > g2 || (g1 == g2 && b1 < b2);
+}
+
+constexpr int kFindThreads = 1024;
+constexpr int kFindE = 8;  // bins per thread per pass
+
+// One workgroup per node.  The node's histogram is read in passes of
+// kFindThreads * kFindE bins in global bin order (feature-major, bins
+// ascending); thread t holds kFindE consecutive bins in registers, all loads
+// issued at once.  A segmented prefix sum (segments = features) -- serial
+// inside the thread, a wave scan of the per-thread tails across threads, and
+// a carry across passes -- gives every bin's left totals (G_L, n_L); each
+// candidate's gain is evaluated exactly as the formula is written, and the
+// workgroup keeps the largest gain, ties to the smaller global bin.
+__global__ void __launch_bounds__(kFindThreads) k_find(
+    const int64_t* __restrict__ hist_g, const uint32_t* __restrict__ hist_cnt,
+    const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ bin_feature,
+    const int32_t* __restrict__ n_bins, int32_t total_bins, const gbdt_node* __restrict__ nodes,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ list_len, int32_t list_cap,
+    FindParams fp, const int32_t* __restrict__ scale, gbdt_split* __restrict__ splits) {
+  constexpr int NW = kFindThreads / 64;
+  __shared__ int64_t sw_g[NW];
+  __shared__ int32_t sw_c[NW];
+  __shared__ int32_t sw_f[NW];
   __shared__ int64_t s_carry_g;
   __shared__ int32_t s_carry_c;
-  __shared__ double r_gain[256];
-  __shared__ int32_t r_bin[256];
-  __shared__ int64_t r_gl[256];
-  __shared__ int32_t r_nl[256];
+  __shared__ double r_gain[NW];
+  __shared__ int32_t r_bin[NW];
+  __shared__ int64_t r_gl[NW];
+  __shared__ int32_t r_nl[NW];
   const int32_t n = clamp_len(list_len, list_cap);
   const int32_t j = blockIdx.x;
   if (j >= n) return;
@@ -519,65 +644,91 @@ __global__ void __launch_bounds__(256) k_find(const int64_t* __restrict__ hist_g
     s_carry_g = 0;
     s_carry_c = 0;
   }
-  __syncthreads();
-  for (int32_t base = 0; base < total_bins; base += 256) {
-    const int32_t b = base + threadIdx.x;
-    const bool inb = b < total_bins;
-    int32_t f = 0, t = 0;
-    int64_t g = 0;
-    int32_t c = 0;
-    int32_t head = 1;
-    if (inb) {
-      f = bin_feature[b];
-      t = b - bin_offset[f];
-      g = hg[b];
-      c = (int32_t)hc[b];
-      head = (t == 0) ? 1 : 0;
+  for (int32_t pass = 0; pass < total_bins; pass += kFindThreads * kFindE) {
+    const int32_t b0 = pass + threadIdx.x * kFindE;
+    int64_t g[kFindE];
+    int32_t c[kFindE];
+    int32_t f[kFindE + 2];  // features of bins b0-1 .. b0+kFindE
+#pragma unroll
+    for (int e = 0; e < kFindE; ++e) {
+      const int32_t b = b0 + e;
+      const bool inb = b < total_bins;
+      g[e] = inb ? hg[b] : 0;
+      c[e] = inb ? (int32_t)hc[b] : 0;
     }
-    // segmented inclusive scan inside the wave
-    int32_t fl = head;
+#pragma unroll
+    for (int e = 0; e < kFindE + 2; ++e) {
+      const int32_t b = b0 - 1 + e;
+      f[e] = (b >= 0 && b < total_bins) ? bin_feature[b] : -1 - e;
+    }
+    // serial segmented scan inside the thread
+    int32_t first_head = kFindE;
+    int64_t rg = 0;
+    int32_t rc = 0;
+#pragma unroll
+    for (int e = 0; e < kFindE; ++e) {
+      const bool head = (b0 + e >= total_bins) || (f[e] != f[e + 1]);
+      if (head && first_head == kFindE) first_head = e;
+      rg = head ? g[e] : rg + g[e];
+      rc = head ? c[e] : rc + c[e];
+      g[e] = rg;
+      c[e] = rc;
+    }
+    // segmented scan of the thread tails across the workgroup
+    int32_t fl = first_head < kFindE ? 1 : 0;
+    int64_t wg = rg;
+    int32_t wc = rc;
     for (int off = 1; off < 64; off <<= 1) {
-      const int64_t gu = __shfl_up(g, off, 64);
-      const int32_t cu = __shfl_up(c, off, 64);
+      const int64_t gu = __shfl_up(wg, off, 64);
+      const int32_t cu = __shfl_up(wc, off, 64);
       const int32_t fu = __shfl_up(fl, off, 64);
       if (lane >= off && !fl) {
-        g += gu;
-        c += cu;
+        wg += gu;
+        wc += cu;
         fl |= fu;
       }
     }
     if (lane == 63) {
-      sw_g[wid] = g;
-      sw_c[wid] = c;
+      sw_g[wid] = wg;
+      sw_c[wid] = wc;
       sw_f[wid] = fl;
     }
     __syncthreads();
-    // carry into this wave from the chunk carry and the earlier waves
-    int64_t cg = s_carry_g;
-    int32_t cc = s_carry_c;
+    int64_t cgw = s_carry_g;  // open segment entering this wave
+    int32_t ccw = s_carry_c;
     for (int w = 0; w < wid; ++w) {
       if (sw_f[w]) {
-        cg = sw_g[w];
-        cc = sw_c[w];
+        cgw = sw_g[w];
+        ccw = sw_c[w];
       } else {
-        cg += sw_g[w];
-        cc += sw_c[w];
+        cgw += sw_g[w];
+        ccw += sw_c[w];
       }
     }
-    if (!fl) {
-      g += cg;
-      c += cc;
+    const int64_t incl_g = fl ? wg : cgw + wg;  // open segment at this thread's end
+    const int32_t incl_c = fl ? wc : ccw + wc;
+    int64_t cin_g = __shfl_up(incl_g, 1, 64);
+    int32_t cin_c = __shfl_up(incl_c, 1, 64);
+    if (lane == 0) {
+      cin_g = cgw;
+      cin_c = ccw;
     }
     __syncthreads();
-    if (threadIdx.x == 255) {
-      s_carry_g = g;
-      s_carry_c = c;
+    if (threadIdx.x == kFindThreads - 1) {
+      s_carry_g = incl_g;
+      s_carry_c = incl_c;
     }
-    // candidate (f, t): t <= n_bins[f] - 2
-    if (inb && t <= n_bins[f] - 2) {
-      const int64_t nl = c;
+    // candidates: bin b with its right neighbour in the same feature
+#pragma unroll
+    for (int e = 0; e < kFindE; ++e) {
+      const int32_t b = b0 + e;
+      if (b >= total_bins) break;
+      const int64_t gl = e < first_head ? g[e] + cin_g : g[e];
+      const int32_t nlc = e < first_head ? c[e] + cin_c : c[e];
+      if (f[e + 2] != f[e + 1]) continue;
+      const int64_t nl = nlc;
       const int64_t nr = nv - nl;
-      const double GL = ldexp((double)g, -S);
+      const double GL = ldexp((double)gl, -S);
       const double HL = (double)nl;
       const double GR = Gv - GL;
       const double HR = Hv - HL;
@@ -588,46 +739,52 @@ __global__ void __launch_bounds__(256) k_find(const int64_t* __restrict__ hist_g
         const double diff = sum - sP;
         const double half = 0.5 * diff;
         const double gain = half - fp.gamma;
-        if (gain > best_gain || (gain == best_gain && gain > 0.0 && b < best_bin)) {
+        if (gain > 0.0 && better(gain, b, best_gain, best_bin)) {
           best_gain = gain;
           best_bin = b;
-          best_gl = g;
-          best_nl = c;
+          best_gl = gl;
+          best_nl = nlc;
         }
       }
     }
     __syncthreads();
   }
-  r_gain[threadIdx.x] = best_gain;
-  r_bin[threadIdx.x] = best_bin;
-  r_gl[threadIdx.x] = best_gl;
-  r_nl[threadIdx.x] = best_nl;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) {
-      const double g2 = r_gain[threadIdx.x + s];
-      const int32_t b2 = r_bin[threadIdx.x + s];
-      const double g1 = r_gain[threadIdx.x];
-      const int32_t b1 = r_bin[threadIdx.x];
-      if (g2 > g1 || (g2 == g1 && b2 < b1)) {
-        r_gain[threadIdx.x] = g2;
-        r_bin[threadIdx.x] = b2;
-        r_gl[threadIdx.x] = r_gl[threadIdx.x + s];
-        r_nl[threadIdx.x] = r_nl[threadIdx.x + s];
-      }
+  // argmax over the workgroup
+  for (int off = 32; off > 0; off >>= 1) {
+    const double og = __shfl_xor(best_gain, off, 64);
+    const int32_t ob = __shfl_xor(best_bin, off, 64);
+    const int64_t ol = __shfl_xor(best_gl, off, 64);
+    const int32_t on = __shfl_xor(best_nl, off, 64);
+    if (better(og, ob, best_gain, best_bin)) {
+      best_gain = og;
+      best_bin = ob;
+      best_gl = ol;
+      best_nl = on;
     }
-    __syncthreads();
   }
+  if (lane == 0) {
+    r_gain[wid] = best_gain;
+    r_bin[wid] = best_bin;
+    r_gl[wid] = best_gl;
+    r_nl[wid] = best_nl;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
+    for (int w = 1; w < NW; ++w)
+      if (better(r_gain[w], r_bin[w], best_gain, best_bin)) {
+        best_gain = r_gain[w];
+        best_bin = r_bin[w];
+        best_gl = r_gl[w];
+        best_nl = r_nl[w];
+      }
     gbdt_split sp;
-    const int32_t bb = r_bin[0];
-    if (bb != 0x7fffffff && r_gain[0] > 0.0) {
-      const int32_t f = bin_feature[bb];
-      sp.gain = r_gain[0];
-      sp.feature = f;
-      sp.threshold_bin = bb - bin_offset[f];
-      sp.g_left = r_gl[0];
-      sp.n_left = r_nl[0];
+    if (best_bin != 0x7fffffff && best_gain > 0.0) {
+      const int32_t ff = bin_feature[best_bin];
+      sp.gain = best_gain;
+      sp.feature = ff;
+      sp.threshold_bin = best_bin - bin_offset[ff];
+      sp.g_left = best_gl;
+      sp.n_left = best_nl;
       sp.valid = 1;
     } else {
       sp.gain = 0.0;
@@ -658,38 +815,72 @@ __device__ __forceinline__ uint64_t st_load(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kPartThreads = 256;
-constexpr int kPartRowsPerThread = kPartTileRows / kPartThreads;  // 8
+constexpr int kPartThreads = 1024;
+constexpr int kPartRowsPerThread = kPartTileRows / kPartThreads;  // 2
+constexpr int kPartWaves = kPartThreads / 64;
 
+// Wave 0 of the workgroup: exclusive count of left rows over the tiles of the
+// node before `tile`, 64 predecessors per step.  Tiles before the node's first
+// tile count as an inclusive prefix of 0, so the walk stops there.
+__device__ int64_t lookback_excl(uint64_t* status, int32_t tile, int32_t tfirst, bool* ok) {
+  const int lane = threadIdx.x & 63;
+  int64_t excl = 0;
+  int32_t idx = tile - 1;
+  uint32_t spins = 0;
+  while (true) {
+    const int32_t p = idx - lane;
+    const uint64_t w = p >= tfirst ? st_load(&status[p]) : kStInc;
+    const uint64_t st = w & kStMask;
+    const uint64_t inc = __ballot(st == kStInc);
+    const uint64_t zero = __ballot(st == 0ull);
+    const int first_inc = inc ? (__ffsll((unsigned long long)inc) - 1) : 64;
+    const uint64_t need = first_inc >= 63 ? ~0ull : ((2ull << first_inc) - 1ull);
+    if (zero & need) {
+      if (++spins > (1u << 20)) {
+        *ok = false;
+        return excl;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    const int64_t val = ((need >> lane) & 1ull) ? (int64_t)(uint32_t)(w & 0xffffffffull) : 0;
+    excl += wave_sum(val);
+    if (first_inc < 64) return excl;
+    idx -= 64;
+  }
+}
+
+template <int UNIT>
 __global__ void __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const int64_t* __restrict__ sq,
     const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, int64_t* __restrict__ dq,
     int32_t* __restrict__ drid, int64_t row_capacity, int32_t n_blocks, int32_t block_features,
-    int32_t block_stride, int32_t n_features, const gbdt_node* __restrict__ nodes,
-    const gbdt_split* __restrict__ splits, const int32_t* __restrict__ list,
-    const int32_t* __restrict__ list_len, int32_t list_cap, const int32_t* __restrict__ prefix,
-    uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl) {
+    int32_t block_stride, int32_t n_features, const gbdt_split* __restrict__ splits,
+    const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl) {
+  constexpr int BATCH = 32 / UNIT;
   __shared__ int32_t s_tile;
-  __shared__ int32_t s_cnt[kPartRowsPerThread][kPartThreads / 64];
+  __shared__ int32_t s_cnt[kPartRowsPerThread][kPartWaves];
   __shared__ int32_t s_excl;
+  __shared__ int32_t s_acc;
   __shared__ int32_t s_dpos[kPartTileRows];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   if (threadIdx.x == 0) s_tile = (int32_t)atomicAdd(&ctrl->ticket, 1u);
   __syncthreads();
   const int32_t tile = s_tile;
-  const int32_t n = clamp_len(list_len, list_cap);
-  if (n == 0 || tile >= prefix[n]) return;
-  const int32_t j = find_tile_owner(prefix, n, tile);
-  const int32_t v = list[j];
-  const gbdt_node nd = nodes[v];
+  const int32_t total = ctrl->plan_total;
+  if (tile >= total) return;
+  const TileDesc td = desc[tile];
+  const int32_t v = td.node;
   const gbdt_split sp = splits[v];
-  const int32_t tfirst = prefix[j];
-  const int32_t tlast = prefix[j + 1] - 1;
+  const int32_t tfirst = td.tfirst;
+  const int32_t tlast = td.tfirst + td.ntiles - 1;
   const int32_t tin = tile - tfirst;
-  const int64_t r0 = int64_t(nd.begin) + int64_t(tin) * kPartTileRows;
-  int64_t r1 = r0 + kPartTileRows;
-  if (r1 > int64_t(nd.begin) + nd.count) r1 = int64_t(nd.begin) + nd.count;
+  const int64_t r0 = td.r0;
+  const int64_t r1 = td.r1;
+  struct {
+    int32_t begin, count;
+  } nd = {td.begin, td.count};
   // a listed node must carry a valid split; otherwise nothing is moved, the
   // tile still publishes (so later tiles never wait on it) and the error word
   // is set
@@ -699,8 +890,7 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
 
   const int32_t fblk = split_ok ? sp.feature / block_features : 0;
   const int32_t fcol = split_ok ? sp.feature % block_features : 0;
-  const uint8_t* __restrict__ fcolp =
-      sbins + int64_t(fblk) * row_capacity * block_stride + fcol;
+  const uint8_t* __restrict__ fcolp = sbins + int64_t(fblk) * row_capacity * block_stride + fcol;
   bool left[kPartRowsPerThread];
   uint64_t bal[kPartRowsPerThread];
 #pragma unroll
@@ -714,41 +904,26 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
   if (threadIdx.x == 0) {
     int32_t acc = 0;
     for (int k = 0; k < kPartRowsPerThread; ++k)
-      for (int w = 0; w < kPartThreads / 64; ++w) {
+      for (int w = 0; w < kPartWaves; ++w) {
         const int32_t t = s_cnt[k][w];
         s_cnt[k][w] = acc;
         acc += t;
       }
-    // acc = lefts in this tile; look back for the lefts of earlier tiles
-    if (tin == 0) {
-      st_publish(&status[tile], kStInc | (uint64_t)(uint32_t)acc);
-      s_excl = 0;
-    } else {
-      st_publish(&status[tile], kStAgg | (uint64_t)(uint32_t)acc);
-      int64_t excl = 0;
-      int32_t idx = tile - 1;
-      uint32_t spins = 0;
-      bool ok = true;
-      while (true) {
-        const uint64_t w = st_load(&status[idx]);
-        const uint64_t st = w & kStMask;
-        if (st == 0ull) {
-          if (++spins > (1u << 20)) {
-            ok = false;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-          continue;
-        }
-        excl += (int64_t)(uint32_t)(w & 0xffffffffull);
-        if (st == kStInc || idx == tfirst) break;
-        --idx;
-      }
+    s_acc = acc;
+    // publish this tile's left count at once, so later tiles never wait long
+    st_publish(&status[tile], (tin == 0 ? kStInc : kStAgg) | (uint64_t)(uint32_t)acc);
+  }
+  __syncthreads();
+  if (wid == 0) {
+    int64_t excl = 0;
+    bool ok = true;
+    if (tin > 0) excl = lookback_excl(status, tile, tfirst, &ok);
+    if (lane == 0) {
       if (!ok) dev_error(&ctrl->err, GBDT_E_INTERNAL);
-      st_publish(&status[tile], kStInc | (uint64_t)(uint32_t)(excl + acc));
+      if (tin > 0) st_publish(&status[tile], kStInc | (uint64_t)(uint32_t)(excl + s_acc));
       s_excl = (int32_t)excl;
+      if (tile == tlast && excl + s_acc != sp.n_left) dev_error(&ctrl->err, GBDT_E_INTERNAL);
     }
-    if (tile == tlast && s_excl + acc != sp.n_left) dev_error(&ctrl->err, GBDT_E_INTERNAL);
   }
   __syncthreads();
   const int32_t excl = s_excl;
@@ -757,9 +932,11 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t seg_end = int64_t(nd.begin) + nd.count;
   bool bad_pos = false;
+  int32_t dpos[kPartRowsPerThread];
 #pragma unroll
   for (int k = 0; k < kPartRowsPerThread; ++k) {
     const int32_t i = k * kPartThreads + threadIdx.x;
+    dpos[k] = -1;
     if (i < rows) {
       const int32_t rl = s_cnt[k][wid] + __popcll(bal[k] & lt_mask);
       const int64_t d = left[k] ? lbase + rl : rbase + (i - rl);
@@ -767,33 +944,57 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
       // row outside its node's segment: such a row is not written
       const bool in_seg = d >= nd.begin && d < seg_end;
       bad_pos |= !in_seg;
-      s_dpos[i] = in_seg ? (int32_t)d : -1;
+      dpos[k] = in_seg ? (int32_t)d : -1;
+      s_dpos[i] = dpos[k];
     }
   }
   if (bad_pos) dev_error(&ctrl->err, GBDT_E_INTERNAL);
-  __syncthreads();
-  // q and row id, one row per lane
-  for (int32_t i = threadIdx.x; i < rows; i += kPartThreads) {
-    const int64_t s = r0 + i;
-    const int32_t d = s_dpos[i];
-    if (d < 0) continue;
-    dq[d] = sq[s];
-    drid[d] = srid != nullptr ? srid[s] : (int32_t)s;
+  // q and row id of the lane's own rows
+  {
+    int64_t qv[kPartRowsPerThread];
+    int32_t rv[kPartRowsPerThread];
+#pragma unroll
+    for (int k = 0; k < kPartRowsPerThread; ++k) {
+      const int32_t i = k * kPartThreads + threadIdx.x;
+      const int64_t s = r0 + i;
+      const bool ok = i < rows;
+      qv[k] = ok ? sq[s] : 0;
+      rv[k] = ok ? (srid != nullptr ? srid[s] : (int32_t)s) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPartRowsPerThread; ++k) {
+      if (dpos[k] >= 0) {
+        dq[dpos[k]] = qv[k];
+        drid[dpos[k]] = rv[k];
+      }
+    }
   }
-  // bins: (row group, dword column) lanes, every block
-  const int32_t lpr = block_stride >> 2;
+  __syncthreads();
+  // bins: (row group, column of UNIT bytes) lanes, every block, BATCH rows of
+  // loads in flight per lane
+  const int32_t lpr = block_stride / UNIT;
   const int32_t rpi = kPartThreads / lpr;
   const int32_t col = threadIdx.x % lpr;
   const int32_t rg = threadIdx.x / lpr;
   if (rg < rpi) {
     for (int32_t b = 0; b < n_blocks; ++b) {
-      const uint8_t* __restrict__ sb = sbins + int64_t(b) * row_capacity * block_stride + 4 * col;
-      uint8_t* __restrict__ db = dbins + int64_t(b) * row_capacity * block_stride + 4 * col;
-      for (int32_t i = rg; i < rows; i += rpi) {
-        const int32_t d = s_dpos[i];
-        if (d < 0) continue;
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(sb + (r0 + i) * block_stride);
-        *reinterpret_cast<uint32_t*>(db + int64_t(d) * block_stride) = w;
+      const uint8_t* __restrict__ sb = sbins + int64_t(b) * row_capacity * block_stride + UNIT * col;
+      uint8_t* __restrict__ db = dbins + int64_t(b) * row_capacity * block_stride + UNIT * col;
+      for (int32_t i = rg; i < rows; i += BATCH * rpi) {
+        uint32_t w[BATCH][UNIT / 4];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int32_t ii = i + u * rpi;
+          if (ii < rows) VecLoad<UNIT>::load(sb + (r0 + ii) * block_stride, w[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int32_t ii = i + u * rpi;
+          if (ii < rows) {
+            const int32_t d = s_dpos[ii];
+            if (d >= 0) VecLoad<UNIT>::store(db + int64_t(d) * block_stride, w[u]);
+          }
+        }
       }
     }
   }
@@ -807,34 +1008,40 @@ struct RidTable {
 __global__ void __launch_bounds__(256) k_update(double* __restrict__ pred, int64_t n_pred,
                                                 RidTable rt, int32_t n_depths,
                                                 const gbdt_node* __restrict__ nodes,
-                                                const int32_t* __restrict__ list,
-                                                const int32_t* __restrict__ list_len,
-                                                int32_t list_cap,
-                                                const int32_t* __restrict__ prefix,
-                                                double eta, WsCtrl* __restrict__ ctrl) {
-  const int32_t n = clamp_len(list_len, list_cap);
+                                                const TileDesc* __restrict__ desc, double eta,
+                                                WsCtrl* __restrict__ ctrl) {
   const int32_t tile = blockIdx.x;
-  if (n == 0 || tile >= prefix[n]) return;
-  const int32_t j = find_tile_owner(prefix, n, tile);
-  const int32_t v = list[j];
-  const gbdt_node nd = nodes[v];
+  const int32_t total = ctrl->plan_total;
+  const TileDesc td = desc[tile];
+  if (tile >= total) return;
+  const gbdt_node nd = nodes[td.node];
   if (nd.depth < 0 || nd.depth >= n_depths) {
     if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
     return;
   }
   const int32_t* __restrict__ rid = rt.p[nd.depth];
-  const int64_t r0 = int64_t(nd.begin) + int64_t(tile - prefix[j]) * kUpdTileRows;
-  int64_t r1 = r0 + kUpdTileRows;
-  if (r1 > int64_t(nd.begin) + nd.count) r1 = int64_t(nd.begin) + nd.count;
+  const int64_t r0 = td.r0;
+  const int64_t r1 = td.r1;
   const double delta = eta * nd.leaf_value;
   bool bad = false;
-  for (int64_t p = r0 + threadIdx.x; p < r1; p += blockDim.x) {
-    const int64_t r = rid != nullptr ? rid[p] : p;
-    if (r < 0 || r >= n_pred) {
-      bad = true;
-      continue;
+  constexpr int U = 8;
+  for (int64_t p = r0 + threadIdx.x; p < r1; p += int64_t(U) * blockDim.x) {
+    int64_t r[U];
+    double x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t pp = p + int64_t(u) * blockDim.x;
+      r[u] = pp < r1 ? (rid != nullptr ? (int64_t)rid[pp] : pp) : -1;
     }
-    pred[r] = pred[r] + delta;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = r[u] >= 0 && r[u] < n_pred;
+      bad |= (r[u] != -1) && !ok;
+      x[u] = ok ? pred[r[u]] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (r[u] >= 0 && r[u] < n_pred) pred[r[u]] = x[u] + delta;
   }
   if (bad) dev_error(&ctrl->err, GBDT_E_INTERNAL);
 }
@@ -1158,6 +1365,7 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   char* w = static_cast<char*>(ws);
   WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
   int32_t* prefix = reinterpret_cast<int32_t*>(w + L.prefix);
+  TileDesc* tdesc = reinterpret_cast<TileDesc*>(w + L.tdesc);
   uint64_t* hpart = reinterpret_cast<uint64_t*>(w + L.hpart);
   const int32_t n_rows_for_bits = (int32_t)(src->X.n_rows > 0 ? src->X.n_rows : 1);
   const int32_t bits = pack_bits_for(n_rows_for_bits);
@@ -1167,21 +1375,23 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   const int64_t q_bound = int64_t(1) << (52 - ceil_log2(n_rows_for_bits));
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap, T,
-                     (int32_t)max_tiles, prefix, ctrl, (uint64_t*)nullptr);
+                     (int32_t)max_tiles, prefix, tdesc, ctrl, (uint64_t*)nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
-  const size_t lds = sizeof(uint64_t) * size_t(ft->max_block_bins);
+  const size_t lds = sizeof(uint64_t) * size_t(ft->max_block_bins + kLdsHistSlack);
+  const int unit = load_unit_for(src->X.block_stride);
+  auto kern = unit == 16 ? k_hist<16> : (unit == 8 ? k_hist<8> : k_hist<4>);
   diag_begin(kDiagHist, s);
-  hipLaunchKernelGGL(k_hist, dim3((unsigned)max_tiles, (unsigned)src->X.n_blocks), dim3(256), lds,
-                     s, src->X.bins, src->X.row_capacity, src->X.block_features,
+  hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles, (unsigned)src->X.n_blocks), dim3(kHistThreads),
+                     lds, s, src->X.bins, src->X.row_capacity, src->X.block_features,
                      src->X.block_stride, src->X.n_features, src->q, ft->bin_offset,
-                     ft->skip_bin, ft->total_bins, nodes, list, list_len, list_cap, prefix, T,
-                     bits, q_bound, hist_g, hist_cnt, hpart, ctrl);
+                     ft->skip_bin, ft->total_bins, tdesc, bits, q_bound, hist_g, hist_cnt, hpart,
+                     ctrl);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist");
   diag_begin(kDiagHistReduce, s);
   hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)((ft->total_bins + 63) / 64), (unsigned)list_cap),
-                     dim3(64), 0, s, list, list_len, list_cap, prefix, (int32_t)max_tiles, bits,
+                     dim3(1024), 0, s, list, list_len, list_cap, prefix, (int32_t)max_tiles, bits,
                      ft->total_bins, hpart, hist_g, hist_cnt);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist_reduce");
@@ -1226,7 +1436,7 @@ int gbdt_find_best_splits(const int64_t* hist_g, const uint32_t* hist_cnt,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   FindParams fp{p->reg_lambda, p->gamma, p->min_child_weight, p->min_samples_leaf};
   diag_begin(kDiagFind, s);
-  hipLaunchKernelGGL(k_find, dim3((unsigned)list_cap), dim3(256), 0, s, hist_g, hist_cnt,
+  hipLaunchKernelGGL(k_find, dim3((unsigned)list_cap), dim3(kFindThreads), 0, s, hist_g, hist_cnt,
                      ft->bin_offset, ft->bin_feature, ft->n_bins, ft->total_bins, nodes, list,
                      list_len, list_cap, fp, scale, splits);
   diag_end(s);
@@ -1259,18 +1469,20 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
   char* w = static_cast<char*>(ws);
   WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
   int32_t* prefix = reinterpret_cast<int32_t*>(w + L.prefix);
+  TileDesc* tdesc = reinterpret_cast<TileDesc*>(w + L.tdesc);
   uint64_t* status = reinterpret_cast<uint64_t*>(w + L.status);
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap,
-                     kPartTileRows, (int32_t)max_tiles, prefix, ctrl, status);
+                     kPartTileRows, (int32_t)max_tiles, prefix, tdesc, ctrl, status);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
   diag_begin(kDiagPartition, s);
-  hipLaunchKernelGGL(k_partition, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s,
+  const int unit = load_unit_for(src->X.block_stride);
+  auto kern = unit == 16 ? k_partition<16> : (unit == 8 ? k_partition<8> : k_partition<4>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s,
                      src->X.bins, src->q, src->rid, dst->X.bins, dst->q, dst->rid,
                      src->X.row_capacity, src->X.n_blocks, src->X.block_features,
-                     src->X.block_stride, src->X.n_features, nodes, splits, list, list_len,
-                     list_cap, prefix, status, ctrl);
+                     src->X.block_stride, src->X.n_features, splits, tdesc, status, ctrl);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_partition");
   return GBDT_OK;
@@ -1293,17 +1505,19 @@ int gbdt_update_predictions(double* pred, int64_t n, const int32_t* const* rid_b
   char* w = static_cast<char*>(ws);
   WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
   int32_t* prefix = reinterpret_cast<int32_t*>(w + L.prefix);
+  TileDesc* tdesc = reinterpret_cast<TileDesc*>(w + L.tdesc);
   RidTable rt{};
   for (int d = 0; d < n_depths; ++d) rt.p[d] = rid_by_depth[d];
   const int64_t max_tiles = (n + kUpdTileRows - 1) / kUpdTileRows + list_cap;
+  if (max_tiles > L.tdesc_cap) return fail(GBDT_E_SHAPE, "too many update tiles for the workspace");
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap,
-                     kUpdTileRows, (int32_t)max_tiles, prefix, ctrl, (uint64_t*)nullptr);
+                     kUpdTileRows, (int32_t)max_tiles, prefix, tdesc, ctrl, (uint64_t*)nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
   diag_begin(kDiagUpdate, s);
   hipLaunchKernelGGL(k_update, dim3((unsigned)max_tiles), dim3(256), 0, s, pred, n, rt, n_depths,
-                     nodes, list, list_len, list_cap, prefix, learning_rate, ctrl);
+                     nodes, tdesc, learning_rate, ctrl);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_update");
   return GBDT_OK;

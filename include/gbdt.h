@@ -206,7 +206,7 @@ size_t gbdt_workspace_bytes(int64_t n_rows, int32_t max_list, int32_t total_bins
  * Column blocking for features with n_bins_host[f] bins (host array): writes
  * n_features, n_blocks, block_features and block_stride of *X and
  * *max_block_bins, so that one block holds at most 64 features and its
- * histogram fits a workgroup's LDS budget (7936 bins).
+ * histogram fits a workgroup's LDS budget (7680 bins).
  */
 int gbdt_choose_blocking(int32_t n_features, const int32_t* n_bins_host, gbdt_matrix* X /* host */,
                          int32_t* max_block_bins /* host */);
@@ -264,6 +264,9 @@ int gbdt_compute_gradients(const double* pred, const float* label, int64_t n, in
  * rows_bound bounds the sum of the listed counts (sizes the launch);
  * list_cap bounds *list_len.  Requires |q_i| <= 2^(52 - ceil(log2 n_rows))
  * (as written by gbdt_compute_gradients); a violation sets GBDT_E_OVERFLOW.
+ * Requires every bin < n_bins[f] and padding bytes 0, which holds for rows
+ * written by gbdt_pack_matrix (which checks the bins) and gbdt_partition_rows;
+ * other bytes give wrong counts but never an access outside the buffers.
  */
 int gbdt_build_histograms(const gbdt_rows* src /* host */, const gbdt_features* ft /* host */,
                           const gbdt_node* nodes, const int32_t* list, const int32_t* list_len,

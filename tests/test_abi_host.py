@@ -60,7 +60,7 @@ def test_blocking_fits_budget(nbins):
     assert X.n_blocks * X.block_features >= F > (X.n_blocks - 1) * X.block_features
     assert X.block_stride % 4 == 0 and X.block_stride >= X.block_features and X.block_features <= 64
     worst = max(sum(nbins[f0:f0 + X.block_features]) for f0 in range(0, F, X.block_features))
-    assert mbb == worst <= 7936
+    assert mbb == worst <= 7680
 
 
 def test_blocking_rejects_bad_bins():
