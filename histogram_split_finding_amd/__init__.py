@@ -111,8 +111,11 @@ def load():
                                                  vp, vp, ctypes.c_size_t, vp]),
         "gbdt_partition_rows": (ctypes.c_int, [P(Rows), P(Rows), vp, vp, vp, vp, i32, i64, vp,
                                                ctypes.c_size_t, vp]),
-        "gbdt_update_predictions": (ctypes.c_int, [vp, i64, vp, i32, vp, vp, vp, i32, ctypes.c_double,
-                                                   vp, ctypes.c_size_t, vp]),
+        "gbdt_update_predictions": (ctypes.c_int, [vp, P(Matrix), vp, vp, i32, ctypes.c_double, vp,
+                                                   ctypes.c_size_t, vp]),
+        "gbdt_diag_enable": (ctypes.c_int, [i32]),
+        "gbdt_diag_disable": (ctypes.c_int, []),
+        "gbdt_diag_read": (ctypes.c_int, [i32, vp, vp, vp]),
         "gbdt_grow_sizes": (ctypes.c_int, [i64, i32, i32, P(GrowSizes)]),
         "gbdt_grow_tree": (ctypes.c_int, [P(Matrix), P(Features), vp, vp, P(Params), vp, vp,
                                           P(GrowBuffers), vp]),
@@ -240,7 +243,7 @@ class RowBuffer:
                       self.n_blocks, self.block_features, self.block_stride)
 
     def rows(self, identity_rid=False) -> Rows:
-        return Rows(self.matrix(), _ptr(self.q), None if identity_rid else _ptr(self.rid))
+        return Rows(self.matrix(), _ptr(self.q), None if (identity_rid or self.rid is None) else _ptr(self.rid))
 
     def blocked_to_rowmajor(self):
         """Bins back in row-major [n, F] order (for tests)."""
@@ -303,13 +306,9 @@ def gbdt_partition_rows(src: Rows, dst: Rows, nodes, splits, lst, list_len, list
     _check(rc, "gbdt_partition_rows")
 
 
-def gbdt_update_predictions(pred, rid_by_depth, nodes, lst, list_len, list_cap, learning_rate, ws,
-                            stream=None):
-    arr = (ctypes.c_void_p * len(rid_by_depth))(*[None if r is None else r.data_ptr()
-                                                  for r in rid_by_depth])
-    rc = load().gbdt_update_predictions(_ptr(pred), pred.numel(), ctypes.cast(arr, vp),
-                                        len(rid_by_depth), _ptr(nodes), _ptr(lst), _ptr(list_len),
-                                        int(list_cap), float(learning_rate), _ptr(ws), ws.numel(),
+def gbdt_update_predictions(pred, X: Matrix, nodes, n_nodes, max_nodes, learning_rate, ws, stream=None):
+    rc = load().gbdt_update_predictions(_ptr(pred), ctypes.byref(X), _ptr(nodes), _ptr(n_nodes),
+                                        int(max_nodes), float(learning_rate), _ptr(ws), ws.numel(),
                                         _stream(stream))
     _check(rc, "gbdt_update_predictions")
 
@@ -348,7 +347,7 @@ class Booster:
         sz = gbdt_grow_sizes(n, TB, D)
         self.sizes = sz
         self.pred = torch.full((n,), float(base_score), dtype=torch.float64, device=device)
-        self.pp = [RowBuffer(ds.ft, n, device), RowBuffer(ds.ft, n, device)]
+        self.pp = [RowBuffer(ds.ft, n, device, with_rid=False), RowBuffer(ds.ft, n, device, with_rid=False)]
         self.q = torch.zeros(n, dtype=torch.int64, device=device)
         self.hist_g = torch.zeros(sz.hist_slots * TB, dtype=torch.int64, device=device)
         self.hist_cnt = torch.zeros(sz.hist_slots * TB, dtype=torch.int32, device=device)

@@ -10,7 +10,8 @@
 // every split pair), subtraction for the larger siblings, split search,
 // k_level (breadth-first children, frozen leaves, next level's lists), and
 // the stable partition of the splitting nodes' rows into the other row
-// buffer.  After the last level the prediction update runs over all leaves.
+// buffer (skipped at the last level).  After the last level every row is
+// routed through the finished tree and its prediction updated.
 
 #include <hip/hip_runtime.h>
 
@@ -319,7 +320,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     return fail(GBDT_E_ARG, "a driver buffer is null");
   for (int k = 0; k < 2; ++k) {
     const gbdt_rows& r = b->pp[k];
-    if (!r.X.bins || !r.q || !r.rid) return fail(GBDT_E_ARG, "a row buffer is null");
+    if (!r.X.bins || !r.q) return fail(GBDT_E_ARG, "a row buffer is null");
     if (r.X.n_rows != n || r.X.row_capacity != X->row_capacity || r.X.n_blocks != X->n_blocks ||
         r.X.block_stride != X->block_stride || r.X.block_features != X->block_features ||
         r.X.n_features != X->n_features)
@@ -380,17 +381,17 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return hip_fail(e, "k_level");
     }
-    rc = gbdt_partition_rows(&src, &dst, nodes_out, b->splits, b->lists + LL.split + lvl_off,
-                             &tc->n_split[d], cap_lvl, n, b->ws, b->ws_bytes, stream);
-    if (rc) return rc;
-    src = dst;
+    // the rows of the last level's children are never read again: the
+    // prediction update routes rows through the finished tree instead
+    if (d + 1 < D) {
+      rc = gbdt_partition_rows(&src, &dst, nodes_out, b->splits, b->lists + LL.split + lvl_off,
+                               &tc->n_split[d], cap_lvl, n, b->ws, b->ws_bytes, stream);
+      if (rc) return rc;
+      src = dst;
+    }
   }
-  const int32_t* rid_by_depth[GBDT_MAX_DEPTH + 1];
-  rid_by_depth[0] = nullptr;
-  for (int32_t d = 1; d <= D; ++d) rid_by_depth[d] = b->pp[(d - 1) & 1].rid;
-  rc = gbdt_update_predictions(pred, n, rid_by_depth, D + 1, nodes_out, b->lists + LL.leaves,
-                               &tc->n_leaves, int32_t(1) << D, p->learning_rate, b->ws, b->ws_bytes,
-                               stream);
+  rc = gbdt_update_predictions(pred, X, nodes_out, n_nodes_dev, int32_t(sz.max_nodes),
+                               p->learning_rate, b->ws, b->ws_bytes, stream);
   return rc;
 }
 

@@ -959,13 +959,13 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
       const int64_t s = r0 + i;
       const bool ok = i < rows;
       qv[k] = ok ? sq[s] : 0;
-      rv[k] = ok ? (srid != nullptr ? srid[s] : (int32_t)s) : 0;
+      rv[k] = (ok && drid != nullptr) ? (srid != nullptr ? srid[s] : (int32_t)s) : 0;
     }
 #pragma unroll
     for (int k = 0; k < kPartRowsPerThread; ++k) {
       if (dpos[k] >= 0) {
         dq[dpos[k]] = qv[k];
-        drid[dpos[k]] = rv[k];
+        if (drid != nullptr) drid[dpos[k]] = rv[k];
       }
     }
   }
@@ -1001,49 +1001,169 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
 }
 
 // ------------------------------------------------------ prediction update --
-struct RidTable {
-  const int32_t* p[GBDT_MAX_DEPTH + 1];
-};
+// Forward pass of one tree over the rows of X in their original order, in two
+// launches.  k_compact_tree copies the tree into a table of 8 bytes per node
+// (left child or leaf slot, feature, threshold) plus a table of leaf values,
+// checking each node.  k_update is persistent (a few workgroups per CU): each
+// workgroup first copies both tables into LDS (96 KiB for a depth-12 tree),
+// then walks rows in a grid-stride loop, ROWS rows per lane at once, each
+// lane holding its rows' bins (every feature block, MAXDW dwords at most) in
+// registers.  HBM traffic is the bins once and the predictions read and
+// written once, sequentially in rows -- no gather or scatter through row ids.
+// Trees must be breadth-first with right = left + 1; a node whose children
+// are not in (id, n_nodes) stops the walk and sets GBDT_E_INTERNAL (the row
+// keeps its prediction).  A tree too large for LDS is walked from the global
+// tables (TREE_IN_LDS = false).
+constexpr int kUpdThreads = 1024;
+constexpr int kUpdMaxRowBytes = 256;
+constexpr size_t kUpdTreeLds = 96 * 1024;
+constexpr uint32_t kLeafTag = 0x80000000u;
+constexpr uint32_t kBadTag = 0x40000000u;
 
-__global__ void __launch_bounds__(256) k_update(double* __restrict__ pred, int64_t n_pred,
-                                                RidTable rt, int32_t n_depths,
-                                                const gbdt_node* __restrict__ nodes,
-                                                const TileDesc* __restrict__ desc, double eta,
-                                                WsCtrl* __restrict__ ctrl) {
-  const int32_t tile = blockIdx.x;
-  const int32_t total = ctrl->plan_total;
-  const TileDesc td = desc[tile];
-  if (tile >= total) return;
-  const gbdt_node nd = nodes[td.node];
-  if (nd.depth < 0 || nd.depth >= n_depths) {
-    if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+// One workgroup: leaves get consecutive slots in lval (order of arrival; a
+// slot is only ever read through its own leaf's entry).
+__global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restrict__ nodes,
+                                                       const int32_t* __restrict__ n_nodes_dev,
+                                                       int32_t max_nodes, int32_t n_features,
+                                                       uint2* __restrict__ ctab,
+                                                       double* __restrict__ lval) {
+  __shared__ int32_t s_leaves;
+  if (threadIdx.x == 0) s_leaves = 0;
+  __syncthreads();
+  int32_t nn = *n_nodes_dev;
+  if (nn > max_nodes) nn = max_nodes;
+  const int32_t leaf_cap = (max_nodes + 1) / 2;
+  for (int32_t v = threadIdx.x; v < nn; v += blockDim.x) {
+    const int4 nd = *reinterpret_cast<const int4*>(&nodes[v]);
+    uint2 e;
+    e.y = 0u;
+    if (nd.z < 0) {
+      const int32_t slot = atomicAdd(&s_leaves, 1);
+      if (slot < leaf_cap) {
+        e.x = kLeafTag | (uint32_t)slot;
+        lval[slot] = nodes[v].leaf_value;
+      } else {
+        e.x = kBadTag;  // more leaves than a tree of max_nodes nodes can hold
+      }
+    } else if (nd.z <= v || nd.z >= nn || nd.w != nd.z + 1 || nd.x < 0 || nd.x >= n_features) {
+      e.x = kBadTag;
+    } else {
+      e.x = (uint32_t)nd.z;
+      e.y = (uint32_t)nd.x | ((uint32_t)(nd.y & 0xffff) << 16);
+    }
+    ctab[v] = e;
+  }
+}
+
+template <int MAXDW, int ROWS, bool TREE_IN_LDS>
+__global__ void __launch_bounds__(kUpdThreads) k_update(
+    double* __restrict__ pred, int64_t n, const uint8_t* __restrict__ bins, int64_t row_capacity,
+    int32_t n_blocks, int32_t block_features, int32_t block_stride,
+    const uint2* __restrict__ ctab_g, const double* __restrict__ lval_g,
+    const int32_t* __restrict__ n_nodes_dev, int32_t max_nodes, double eta,
+    WsCtrl* __restrict__ ctrl) {
+  extern __shared__ uint64_t smem[];
+  int32_t nn = *n_nodes_dev;
+  if (nn > max_nodes) nn = max_nodes;
+  if (nn < 1) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
     return;
   }
-  const int32_t* __restrict__ rid = rt.p[nd.depth];
-  const int64_t r0 = td.r0;
-  const int64_t r1 = td.r1;
-  const double delta = eta * nd.leaf_value;
+  const uint2* ctab = ctab_g;
+  const double* lval = lval_g;
+  if (TREE_IN_LDS) {
+    uint2* ct = reinterpret_cast<uint2*>(smem);
+    double* lv = reinterpret_cast<double*>(smem + max_nodes);
+    for (int32_t v = threadIdx.x; v < nn; v += kUpdThreads) {
+      const uint2 e = ctab_g[v];
+      ct[v] = e;
+      if ((e.x & kLeafTag) && !(e.x & kBadTag)) lv[e.x & ~kLeafTag] = lval_g[e.x & ~kLeafTag];
+    }
+    __syncthreads();
+    ctab = ct;
+    lval = lv;
+  }
+  const int32_t dw = block_stride >> 2;
+  const int32_t ndw = n_blocks * dw;
   bool bad = false;
-  constexpr int U = 8;
-  for (int64_t p = r0 + threadIdx.x; p < r1; p += int64_t(U) * blockDim.x) {
-    int64_t r[U];
-    double x[U];
+  const int64_t stride = int64_t(gridDim.x) * kUpdThreads * ROWS;
+  for (int64_t base = int64_t(blockIdx.x) * kUpdThreads * ROWS + threadIdx.x; base < n;
+       base += stride) {
+    uint32_t row[ROWS][MAXDW];
+    uint32_t v[ROWS];
+    bool live[ROWS];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t pp = p + int64_t(u) * blockDim.x;
-      r[u] = pp < r1 ? (rid != nullptr ? (int64_t)rid[pp] : pp) : -1;
+    for (int u = 0; u < ROWS; ++u) {
+      const int64_t i = base + int64_t(u) * kUpdThreads;
+      live[u] = i < n;
+      v[u] = 0u;
+#pragma unroll
+      for (int x = 0; x < MAXDW; ++x) {
+        row[u][x] = 0u;
+        if (live[u] && x < ndw) {
+          const int32_t b = x / dw;
+          row[u][x] = *reinterpret_cast<const uint32_t*>(
+              bins + (int64_t(b) * row_capacity + i) * block_stride + 4 * (x - b * dw));
+        }
+      }
+    }
+    for (int step = 0; step <= GBDT_MAX_DEPTH; ++step) {
+      bool any = false;
+#pragma unroll
+      for (int u = 0; u < ROWS; ++u) {
+        if (!live[u] || (v[u] & kLeafTag)) continue;
+        const uint2 e = ctab[v[u]];
+        if (e.x & kLeafTag) {
+          v[u] = e.x;
+          continue;
+        }
+        if (e.x & kBadTag) {
+          live[u] = false;
+          bad = true;
+          continue;
+        }
+        const int32_t f = (int32_t)(e.y & 0xffffu);
+        const int32_t thr = (int32_t)(e.y >> 16);
+        const int32_t blk = f / block_features;
+        const int32_t byte = blk * block_stride + (f - blk * block_features);
+        // select the dword with a fixed chain of selects: a per-lane dynamic
+        // index into registers would become a loop over the distinct indices
+        const int32_t kk = byte >> 2;
+        uint32_t word = row[u][0];
+#pragma unroll
+        for (int x = 1; x < MAXDW; ++x) word = (x == kk) ? row[u][x] : word;
+        const int32_t bv = (word >> (8 * (byte & 3))) & 0xff;
+        v[u] = bv <= thr ? e.x : e.x + 1u;
+        any = true;
+      }
+      if (!any) break;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = r[u] >= 0 && r[u] < n_pred;
-      bad |= (r[u] != -1) && !ok;
-      x[u] = ok ? pred[r[u]] : 0.0;
+    for (int u = 0; u < ROWS; ++u) {
+      if (!live[u]) continue;
+      if (!(v[u] & kLeafTag)) {  // no leaf within the depth bound
+        bad = true;
+        continue;
+      }
+      const int64_t i = base + int64_t(u) * kUpdThreads;
+      const double delta = eta * lval[v[u] & ~kLeafTag];
+      pred[i] = pred[i] + delta;
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (r[u] >= 0 && r[u] < n_pred) pred[r[u]] = x[u] + delta;
   }
   if (bad) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+}
+
+template <int MAXDW>
+static void launch_update(bool in_lds, int rows, dim3 grid, size_t lds, hipStream_t s, double* pred,
+                          int64_t n, const gbdt_matrix* X, const uint2* ctab, const double* lval,
+                          const int32_t* n_nodes, int32_t max_nodes, double eta, WsCtrl* ctrl) {
+  // two rows per lane only where both rows' bins fit registers without scratch
+  constexpr int R2 = MAXDW <= 16 ? 2 : 1;
+  auto kern = in_lds ? (rows == 2 ? k_update<MAXDW, R2, true> : k_update<MAXDW, 1, true>)
+                     : (rows == 2 ? k_update<MAXDW, R2, false> : k_update<MAXDW, 1, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(kUpdThreads), lds, s, pred, n, X->bins, X->row_capacity,
+                     X->n_blocks, X->block_features, X->block_stride, ctab, lval, n_nodes,
+                     max_nodes, eta, ctrl);
 }
 
 // ------------------------------------------------------- setup: packing --
@@ -1457,7 +1577,7 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
       src->X.block_features != dst->X.block_features || src->X.row_capacity != dst->X.row_capacity ||
       src->X.n_rows != dst->X.n_rows)
     return fail(GBDT_E_SHAPE, "source and destination layouts differ");
-  if (!src->q || !dst->q || !dst->rid) return fail(GBDT_E_ARG, "q / rid pointer is null");
+  if (!src->q || !dst->q) return fail(GBDT_E_ARG, "q pointer is null");
   if (list_cap < 0 || rows_bound < 0) return fail(GBDT_E_ARG, "negative capacity");
   if (list_cap == 0) return GBDT_OK;
   const WsLayout L = ws_layout(src->X.n_rows, list_cap, 1);
@@ -1488,36 +1608,52 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
   return GBDT_OK;
 }
 
-int gbdt_update_predictions(double* pred, int64_t n, const int32_t* const* rid_by_depth,
-                            int32_t n_depths, const gbdt_node* nodes, const int32_t* list,
-                            const int32_t* list_len, int32_t list_cap, double learning_rate,
+int gbdt_update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* nodes,
+                            const int32_t* n_nodes, int32_t max_nodes, double learning_rate,
                             void* ws, size_t ws_bytes, void* stream) {
-  if (!pred || !nodes || !list || !list_len || !rid_by_depth) return fail(GBDT_E_ARG, "null argument");
-  if (n < 1 || n > 0x7fffffffLL) return fail(GBDT_E_ARG, "n out of range");
-  if (n_depths < 1 || n_depths > GBDT_MAX_DEPTH + 1) return fail(GBDT_E_ARG, "n_depths out of range");
-  if (!std::isfinite(learning_rate)) return fail(GBDT_E_ARG, "learning_rate must be finite");
-  if (list_cap < 0) return fail(GBDT_E_ARG, "negative capacity");
-  if (list_cap == 0) return GBDT_OK;
-  const WsLayout L = ws_layout(n, list_cap, 1);
-  int rc = check_ws(ws, ws_bytes, L);
+  if (!pred || !X || !nodes || !n_nodes) return fail(GBDT_E_ARG, "null argument");
+  int rc = check_matrix(*X);
   if (rc) return rc;
+  if (max_nodes < 1) return fail(GBDT_E_ARG, "max_nodes must be >= 1");
+  if (!std::isfinite(learning_rate)) return fail(GBDT_E_ARG, "learning_rate must be finite");
+  const int64_t n = X->n_rows;
+  if (n == 0) return GBDT_OK;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return fail(GBDT_E_ARG, "workspace is null or misaligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
-  int32_t* prefix = reinterpret_cast<int32_t*>(w + L.prefix);
-  TileDesc* tdesc = reinterpret_cast<TileDesc*>(w + L.tdesc);
-  RidTable rt{};
-  for (int d = 0; d < n_depths; ++d) rt.p[d] = rid_by_depth[d];
-  const int64_t max_tiles = (n + kUpdTileRows - 1) / kUpdTileRows + list_cap;
-  if (max_tiles > L.tdesc_cap) return fail(GBDT_E_SHAPE, "too many update tiles for the workspace");
-  diag_begin(kDiagPlan, s);
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap,
-                     kUpdTileRows, (int32_t)max_tiles, prefix, tdesc, ctrl, (uint64_t*)nullptr);
-  diag_end(s);
-  GBDT_LAUNCH_CHECK("k_plan");
+  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(static_cast<char*>(ws));
+  const int64_t row_bytes = int64_t(X->n_blocks) * X->block_stride;
+  if (row_bytes > kUpdMaxRowBytes) return fail(GBDT_E_UNSUPPORTED, "rows wider than 256 bytes");
+  const WsLayout L = ws_layout(n, 1, 1);
+  const size_t tables = size_t(max_nodes) * sizeof(uint2) + size_t((max_nodes + 1) / 2) * sizeof(double);
+  if (ws_bytes < L.total || tables > L.total - L.hpart)
+    return fail(GBDT_E_ARG, "workspace too small for the tree tables");
+  uint2* ctab = reinterpret_cast<uint2*>(static_cast<char*>(ws) + L.hpart);
+  double* lval = reinterpret_cast<double*>(static_cast<char*>(ws) + L.hpart +
+                                           sizeof(uint2) * size_t(max_nodes));
   diag_begin(kDiagUpdate, s);
-  hipLaunchKernelGGL(k_update, dim3((unsigned)max_tiles), dim3(256), 0, s, pred, n, rt, n_depths,
-                     nodes, tdesc, learning_rate, ctrl);
+  hipLaunchKernelGGL(k_compact_tree, dim3(1), dim3(1024), 0, s, nodes, n_nodes, max_nodes,
+                     X->n_features, ctab, lval);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_compact_tree");
+  const bool in_lds = tables <= kUpdTreeLds;
+  const size_t lds = in_lds ? tables : 0;
+  const int64_t ndw = row_bytes / 4;
+  const int rows = ndw <= 16 ? 2 : 1;
+  int64_t grid = (n + int64_t(kUpdThreads) * rows - 1) / (int64_t(kUpdThreads) * rows);
+  if (grid > 512) grid = 512;  // persistent: the tree is copied to LDS once per workgroup
+  diag_begin(kDiagUpdate, s);
+  if (ndw <= 8)
+    launch_update<8>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
+                     max_nodes, learning_rate, ctrl);
+  else if (ndw <= 16)
+    launch_update<16>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
+                      max_nodes, learning_rate, ctrl);
+  else if (ndw <= 32)
+    launch_update<32>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
+                      max_nodes, learning_rate, ctrl);
+  else
+    launch_update<64>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
+                      max_nodes, learning_rate, ctrl);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_update");
   return GBDT_OK;

@@ -308,7 +308,8 @@ int gbdt_find_best_splits(const int64_t* hist_g, const uint32_t* hist_cnt,
  * positions of dst, rows with bin(s.feature) <= s.threshold_bin first, each
  * side in its original order (stable).  Rows of unlisted nodes are not
  * touched.  The left count must equal s.n_left, else GBDT_E_INTERNAL.
- * dst->rid must be non-NULL; src->rid == NULL means identity.
+ * src->rid == NULL means identity; dst->rid == NULL skips the row ids (the
+ * level-wise driver does not need them).
  */
 int gbdt_partition_rows(const gbdt_rows* src /* host */, const gbdt_rows* dst /* host */,
                         const gbdt_node* nodes, const gbdt_split* splits, const int32_t* list,
@@ -316,15 +317,21 @@ int gbdt_partition_rows(const gbdt_rows* src /* host */, const gbdt_rows* dst /*
                         size_t ws_bytes, void* stream);
 
 /*
- * Step 7 (Training Core section 6; ensemble sum of "Gradient boosted trees
- * (spec model)", Forward pass): for each leaf v = list[j], every row id r at
- * positions [begin, begin+count) of rid_by_depth[nodes[v].depth] (NULL entry
- * = identity) gets pred[r] = pred[r] + (learning_rate * leaf_value), two
- * roundings.  rid_by_depth is a host array of n_depths device pointers.
+ * Step 7 (Training Core section 6), by the forward pass of "Gradient boosted
+ * trees (spec model)" (Forward pass): every row i of X (rows in their
+ * original order) is routed from node 0 -- bin <= threshold_bin goes left,
+ * otherwise right -- to a leaf v, and pred[i] = pred[i] + (learning_rate *
+ * nodes[v].leaf_value), two roundings.  nodes is a flat breadth-first tree
+ * of *n_nodes (device count, <= max_nodes) nodes in which siblings are
+ * adjacent (right = left + 1, as the level-wise driver writes them); a node
+ * whose children break that, are not larger than its own id or not below
+ * *n_nodes stops the walk, leaves the row's prediction unchanged and sets
+ * GBDT_E_INTERNAL.  With pred holding a
+ * base score, one call per tree gives the ensemble prediction of held-out
+ * rows.
  */
-int gbdt_update_predictions(double* pred, int64_t n, const int32_t* const* rid_by_depth,
-                            int32_t n_depths, const gbdt_node* nodes, const int32_t* list,
-                            const int32_t* list_len, int32_t list_cap, double learning_rate,
+int gbdt_update_predictions(double* pred, const gbdt_matrix* X /* host */, const gbdt_node* nodes,
+                            const int32_t* n_nodes, int32_t max_nodes, double learning_rate,
                             void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------ level-wise driver -- */
@@ -332,7 +339,7 @@ int gbdt_update_predictions(double* pred, int64_t n, const int32_t* const* rid_b
 /*
  * Device buffers for gbdt_grow_tree (host struct of device pointers); sizes
  * from gbdt_grow_sizes.  pp[0], pp[1]: two row orders (bins in the blocking
- * of X, q, rid) used in turn by the partition of each level.
+ * of X and q; rid may be NULL) used in turn by the partition of each level.
  */
 typedef struct gbdt_grow_buffers {
   gbdt_rows pp[2];

@@ -91,7 +91,7 @@ def test_null_arguments_fail_before_device_work():
     assert lib.gbdt_find_best_splits(None, None, None, None, None, None, 1, None, None, None, None, 0,
                                      None) == -1
     assert lib.gbdt_partition_rows(None, None, None, None, None, None, 1, 1, None, 0, None) == -1
-    assert lib.gbdt_update_predictions(None, 10, None, 1, None, None, None, 1, 0.3, None, 0, None) == -1
+    assert lib.gbdt_update_predictions(None, None, None, None, 1, 0.3, None, 0, None) == -1
     assert lib.gbdt_grow_tree(None, None, None, None, None, None, None, None, None) == -1
 
 

@@ -296,40 +296,81 @@ def test_partition_count_mismatch_is_reported():
 
 # --------------------------------------------------------- prediction update --
 
-def test_update_predictions():
-    """Leaves whose rows sit in the row orders of different depths; as in a
-    real tree every row belongs to exactly one leaf."""
-    say("update_predictions")
-    rng = np.random.default_rng(8)
-    n = 70000
+def _random_tree(rng, F, nb, depth, p_leaf=0.25):
+    """A flat breadth-first tree with random splits (children appended in order)."""
+    nodes = [dict(depth=0)]
+    v = 0
+    while v < len(nodes):
+        nd = nodes[v]
+        if nd["depth"] < depth and (v == 0 or rng.random() > p_leaf):
+            f = int(rng.integers(0, F))
+            nd.update(feature=f, threshold_bin=int(rng.integers(0, nb[f])), left=len(nodes),
+                      right=len(nodes) + 1, flags=0)
+            nodes.append(dict(depth=nd["depth"] + 1))
+            nodes.append(dict(depth=nd["depth"] + 1))
+        else:
+            nd.update(feature=-1, threshold_bin=-1, left=-1, right=-1, flags=1,
+                      leaf_value=float(rng.normal()))
+        v += 1
+    return nodes
+
+
+def _route(nodes, bins):
+    leaf = np.zeros(bins.shape[0], dtype=np.int64)
+    active = np.ones(bins.shape[0], dtype=bool)
+    while active.any():
+        idx = np.nonzero(active)[0]
+        for v in np.unique(leaf[idx]):
+            nd = nodes[v]
+            sel = idx[leaf[idx] == v]
+            if nd["flags"] & 1:
+                active[sel] = False
+                continue
+            go_left = bins[sel, nd["feature"]] <= nd["threshold_bin"]
+            leaf[sel] = np.where(go_left, nd["left"], nd["right"])
+    return leaf
+
+
+@pytest.mark.parametrize("n,nbins,depth,seed", [(70001, [2, 64, 256, 7, 33], 7, 8), (5000, [256] * 70, 5, 9),
+                                                (1, [4], 3, 10)])
+def test_update_predictions(n, nbins, depth, seed):
+    """Step 7 by routing every row through the finished tree."""
+    say("update_predictions n=%d" % n)
+    rng = np.random.default_rng(seed)
+    bins, label, nb = datagen.make_random(n, nbins, seed, bin_kind=1)
+    nodes = _random_tree(rng, len(nbins), nb, depth)
     pred = rng.normal(size=n)
-    cuts = [0, 5, 9000, 9001, 40000, n]
-    depths = [j % 3 for j in range(len(cuts) - 1)]
-    # final arrangement: identity on the positions of depth-0 leaves, a random
-    # permutation of the other rows elsewhere
-    pi = np.arange(n, dtype=np.int32)
-    other = np.concatenate([np.arange(cuts[j], cuts[j + 1]) for j in range(len(cuts) - 1) if depths[j] != 0])
-    pi[other] = rng.permutation(other).astype(np.int32)
-    ridA = rng.permutation(n).astype(np.int32)
-    ridB = rng.permutation(n).astype(np.int32)
-    leaves, expect = [], pred.copy()
     eta = 0.3
-    for j in range(len(cuts) - 1):
-        b, e, d = cuts[j], cuts[j + 1], depths[j]
-        w = float(rng.normal())
-        leaves.append(dict(begin=b, count=e - b, depth=d, leaf_value=w, flags=1))
-        if d == 1:
-            ridA[b:e] = pi[b:e]
-        if d == 2:
-            ridB[b:e] = pi[b:e]
-        idx = pi[b:e]
-        expect[idx] = expect[idx] + eta * w
+    leaf = _route(nodes, bins)
+    w = np.array([nd.get("leaf_value", 0.0) for nd in nodes])
+    expect = pred + eta * w[leaf]
+    ft = g.FeatureTable(nb, DEV)
+    X = packed_rows(bins, ft)
     dpred = to_dev(pred)
-    ws = _ws(n, len(leaves), 1)
-    g.gbdt_update_predictions(dpred, [None, to_dev(ridA), to_dev(ridB)], nodes_tensor(leaves),
-                              i32(range(len(leaves))), i32([len(leaves)]), len(leaves), eta, ws)
+    ws = _ws(n, 1, 1)
+    g.gbdt_update_predictions(dpred, X.matrix(), nodes_tensor(nodes), i32([len(nodes)]), len(nodes), eta, ws)
     assert g.gbdt_read_error(ws) == 0
     assert np.array_equal(dpred.cpu().numpy(), expect)
+
+
+def test_update_predictions_rejects_bad_tree():
+    say("update_predictions bad tree")
+    bins, label, nb = datagen.make_random(1000, [4, 4], 3)
+    ft = g.FeatureTable(nb, DEV)
+    X = packed_rows(bins, ft)
+    # node 1 points back to node 0: a cycle the walk must refuse
+    nodes = [dict(feature=0, threshold_bin=1, left=1, right=2, flags=0),
+             dict(feature=1, threshold_bin=1, left=0, right=2, flags=0),
+             dict(flags=1, leaf_value=1.0)]
+    pred = np.zeros(1000)
+    dpred = to_dev(pred)
+    ws = _ws(1000, 1, 1)
+    g.gbdt_update_predictions(dpred, X.matrix(), nodes_tensor(nodes), i32([3]), 3, 1.0, ws)
+    assert g.gbdt_read_error(ws) == -7
+    out = dpred.cpu().numpy()
+    right = bins[:, 0] > 1
+    assert np.array_equal(out[right], np.ones(right.sum()))  # rows that reach the leaf
+    assert not out[~right].any()                              # rows that hit the bad node
 
 
 # ------------------------------------------------------------ whole tree path --
