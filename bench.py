@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-diag", action="store_true", help="skip the per-kernel timing pass")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -104,6 +106,20 @@ def main():
     import torch
     import datagen
     import histogram_split_finding_amd as g
+
+    if args.calibrate_copy:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 3
+        print(json.dumps({"calibration": "plain device copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "copies": 3, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
+        return
 
     k = args.workload
     wl = dict(datagen.WORKLOADS[k])

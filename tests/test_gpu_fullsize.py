@@ -1,0 +1,139 @@
+"""Parity at the five workloads' full sizes, in the launch configuration the
+bench times (Dataset + Booster + gbdt_grow_tree).
+
+Workloads 1-3: every node of the first trees and every prediction against
+the oracle, bit for bit.  Workloads 4-5 (10M x 100, 50M x 28): the oracle
+computes sampled outputs one by one -- the gradient grid of the last tree,
+the root histogram and split, histograms and splits of sampled deeper
+nodes -- and properties that hold at any size are checked on everything:
+per-node row counts and gradient sums by routing every row through the GPU
+tree, leaf weights from those sums, and the prediction update.
+"""
+import numpy as np
+import pytest
+
+import datagen
+import histogram_split_finding_amd as g
+import oracle
+from gpu_util import DEV, compare_tree, hist_from_device, min_split_count, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _train_gpu(k, T):
+    bins, label, nb = datagen.make_workload(k)
+    wl = dict(datagen.WORKLOADS[k])
+    ds = g.Dataset(bins, label, nb, DEV)
+    bst = g.Booster(ds, g.make_params(**wl))
+    preds = [bst.pred.cpu().numpy().copy()]
+    for _ in range(T):
+        bst.trees.append(bst.grow_tree())
+        preds.append(bst.pred.cpu().numpy().copy())
+    bst.check()
+    return bins, label, nb, wl, bst, preds
+
+
+@pytest.mark.parametrize("k,T", [(1, 5), (2, 4), (3, 3)])
+def test_small_workloads_every_node(k, T):
+    say("full-size workload %d: %d trees against the oracle" % (k, T))
+    bins, label, nb, wl, bst, preds = _train_gpu(k, T)
+    r = oracle.train(bins, nb, label, oracle.make_params(**wl), T, keep_pred_per_tree=True)
+    trees = bst.host_trees()
+    for t in range(T):
+        compare_tree(trees[t], r["nodes"][t][: r["n_nodes"][t]])
+        assert np.array_equal(preds[t + 1], r["pred_per_tree"][t]), (k, t)
+
+
+def _route(tree, bins):
+    """Node of every row at every depth (rows routed from the root)."""
+    n = bins.shape[0]
+    at = np.zeros(n, dtype=np.int32)
+    per_depth = [at.copy()]
+    feat = tree["feature"]
+    thr = tree["threshold_bin"]
+    left = tree["left"]
+    right = tree["right"]
+    leaf = (tree["flags"] & 1).astype(bool)
+    while True:
+        internal = ~leaf[at]
+        if not internal.any():
+            break
+        idx = np.nonzero(internal)[0]
+        v = at[idx]
+        b = bins[idx, feat[v]]
+        at = at.copy()
+        at[idx] = np.where(b <= thr[v], left[v], right[v])
+        per_depth.append(at)
+    return per_depth
+
+
+def _exact_group_sums(groups, k, n_groups):
+    """int64 sums of k per group, exact (two float64 bincounts of 24-bit parts)."""
+    lo = (k & ((1 << 24) - 1)).astype(np.float64)
+    hi = (k >> 24).astype(np.float64)
+    s_lo = np.bincount(groups, weights=lo, minlength=n_groups)
+    s_hi = np.bincount(groups, weights=hi, minlength=n_groups)
+    return s_hi.astype(np.int64) * (1 << 24) + s_lo.astype(np.int64)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("k,T", [(4, 2), (5, 2)])
+def test_large_workloads_sampled_and_properties(k, T):
+    say("full-size workload %d: %d trees, sampled oracle outputs + properties" % (k, T))
+    bins, label, nb, wl, bst, preds = _train_gpu(k, T)
+    p = oracle.make_params(**wl)
+    t = T - 1
+    tree = bst.host_trees()[t]
+    n = bins.shape[0]
+    # gradient grid of the last tree
+    kq, S, _ = oracle.gradient_grid(preds[t], label)
+    assert np.array_equal(bst.q.cpu().numpy(), kq)
+    # row counts, gradient sums and leaf weights of every node, by routing
+    depth_nodes = _route(tree, bins)
+    nn = len(tree)
+    count = np.zeros(nn, dtype=np.int64)
+    gsum = np.zeros(nn, dtype=np.int64)
+    seen = np.zeros(nn, dtype=bool)
+    for at in depth_nodes:
+        c = np.bincount(at, minlength=nn)
+        s = _exact_group_sums(at, kq, nn)
+        nodes_here = np.unique(at)
+        count[nodes_here] = c[nodes_here]
+        gsum[nodes_here] = s[nodes_here]
+        seen[nodes_here] = True
+    assert seen.all(), "every node holds rows"
+    assert np.array_equal(tree["count"].astype(np.int64), count)
+    assert np.array_equal(tree["gsum"], gsum)
+    lam = float(p.reg_lambda)
+    for v in range(nn):
+        if tree[v]["flags"] & 1:
+            G = np.ldexp(np.float64(gsum[v]), -S)
+            w = -G / (np.float64(count[v]) + lam)
+            assert float(tree[v]["leaf_value"]) == float(w), v
+    # prediction update: pred + (eta * w(leaf of the row))
+    leaf_of = depth_nodes[-1]
+    w_all = tree["leaf_value"]
+    expect = preds[t] + (p.learning_rate * w_all[leaf_of])
+    assert np.array_equal(preds[t + 1], expect)
+    # sampled oracle histograms and splits: the root and nodes down the tree
+    TB = bst.ds.ft.total_bins
+    ms = min_split_count(p)
+    sample = [0]
+    for d in (1, p.max_depth // 2, p.max_depth - 1):
+        cand = [v for v in range(1, nn) if tree[v]["depth"] == d and tree[v]["count"] >= ms]
+        if cand:
+            sample.append(cand[len(cand) // 2])
+    for v in sample:
+        rows = np.nonzero(depth_nodes[int(tree[v]["depth"])] == v)[0].astype(np.int32)
+        cnt, gq = oracle.node_histogram(bins, nb, rows, kq, S)
+        dc, dg = hist_from_device(bst.hist_g, bst.hist_cnt, v, TB)
+        assert np.array_equal(dc, cnt), ("hist cnt", k, v)
+        assert np.array_equal(dg, gq), ("hist G", k, v)
+        sp = oracle.best_split(cnt, gq, nb, int(gsum[v]), len(rows), S, p)
+        nd = tree[v]
+        if sp["valid"]:
+            assert (int(nd["feature"]), int(nd["threshold_bin"])) == (int(sp["feature"]), int(sp["threshold_bin"])), v
+            assert float(nd["gain"]) == float(sp["gain"]), v
+        else:
+            assert nd["flags"] & 1, v
+        say("  node %d (depth %d, %d rows) matches the oracle" % (v, int(nd["depth"]), len(rows)))
