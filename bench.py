@@ -62,6 +62,31 @@ def built_work(trees, n_features, total_bins, max_depth, min_split):
     return rows, nodes
 
 
+def profiled_traffic(workload_name):
+    """HBM bytes per k_hist launch from the committed rocprofv3 counter summary
+    of this workload, if it was taken on the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_hist_%s_counters.txt" % workload_name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    csrc = os.path.join(ROOT, "histogram_split_finding_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("gbdt_kernels.hip", "gbdt_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest()[:16]:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(k, seconds_budget):
     """The oracle as it stands, single-threaded, on the first trees of the same workload."""
     import datagen
@@ -204,7 +229,7 @@ def main():
         achieved = alg_bytes / (hist_ms * 1e-3) / 1e9
         out["value"] = cells / (hist_ms * 1e-3)
         out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                           "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(wl["name"]),
                            "kernel": "k_hist", "launches": launches,
                            "avg_launch_us": 1000.0 * hist_ms / max(launches, 1),
                            "alg_bytes_per_launch": alg_bytes / max(launches, 1)}

@@ -1289,7 +1289,7 @@ int gbdt_diag_enable(int32_t capacity) {
     g_diag.ev.resize(size_t(2) * capacity);
     g_diag.kind.resize(capacity);
     for (int32_t i = 2 * old; i < 2 * capacity; ++i) {
-      hipError_t e = hipEventCreate(&g_diag.ev[i]);
+      hipError_t e = hipEventCreateWithFlags(&g_diag.ev[i], hipEventDisableSystemFence);
       if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
     }
     g_diag.capacity = capacity;
