@@ -17,11 +17,15 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -ffp-contract=off: FP64 gain / weight / prediction arithmetic is evaluated
 # one IEEE operation at a time, as on the CPU.  The packed-FP32 target
-# feature is switched off for all device code.
+# feature is switched off for all device code.  Kernel arguments are
+# preloaded into SGPRs at wave launch (the first 16 dwords), which saves the
+# kernels' first scalar round trip; without firmware support the code object's
+# own prologue loads them instead.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function",
     "-I" + INCLUDE, "-I" + CSRC,
 ]

@@ -22,7 +22,7 @@ static_assert(sizeof(WsCtrl) == 256, "control block is 256 bytes");
 
 constexpr int kGradBlocks = 1024;     // grid of the gradient kernels
 constexpr int kPartTileRows = 2048;   // rows per partition tile
-constexpr int kHistMinTileRows = 2048;
+constexpr int kHistMinTileRows = 1024;
 constexpr int kHistTargetTiles = 1024;
 constexpr int kLdsHistBudgetBins = 7680;  // histogram bins per feature block (60 KiB of LDS)
 constexpr int kLdsHistSlack = 256;         // extra LDS slots: any bin byte stays inside the allocation

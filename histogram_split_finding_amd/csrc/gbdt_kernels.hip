@@ -118,6 +118,28 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// Sum of a 64-bit value over the 64 lanes of a wave with DPP lane moves (no
+// LDS round trips): pairs and quads, half rows, rows, then rows 0+1 into row
+// 1, 2+3 into row 3, and row 1 into row 3.  Every lane must be active; the
+// total is returned in every lane (read from lane 63).  Exact mod 2^64.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t wave_sum_dpp(uint64_t v) {
+  v += dpp_u64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_u64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_u64<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_u64<0x140, 0xF>(v);  // row_mirror
+  v += dpp_u64<0x142, 0xA>(v);  // row_bcast:15 (rows 1 and 3 receive)
+  v += dpp_u64<0x143, 0xC>(v);  // row_bcast:31 (rows 2 and 3 receive)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ double wave_max(double v) {
   for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
   return v;
@@ -238,6 +260,8 @@ __global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nod
     desc[t] = d;
     if (status != nullptr) status[t] = 0ull;
   }
+  // tiles of the launch beyond the plan read a descriptor with node -1
+  for (int32_t t = lim + threadIdx.x; t < max_tiles; t += blockDim.x) desc[t].node = -1;
 }
 
 // -------------------------------------------------------------- gradients --
@@ -310,6 +334,7 @@ __global__ void __launch_bounds__(256) k_grad_q(const double* __restrict__ pred,
 
 // -------------------------------------------------------------- histogram --
 constexpr int kHistThreads = 1024;
+constexpr int kMaxBlockFeatures = 64;  // features per column block, at most
 
 // Vector load of UNIT bytes (4, 8 or 16) as dwords.
 template <int UNIT>
@@ -370,32 +395,27 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(
     const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t block_features,
     int32_t block_stride, int32_t n_features, const int64_t* __restrict__ q,
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ skip_bin,
-    int32_t total_bins, const TileDesc* __restrict__ desc, int32_t bits, int64_t q_bound,
-    int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt, uint64_t* __restrict__ partial,
-    WsCtrl* __restrict__ ctrl) {
+    int32_t total_bins, int32_t lds_bins, const TileDesc* __restrict__ desc, int32_t bits,
+    int64_t q_bound, int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
+    uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl) {
   constexpr int NB = UNIT;                 // bins per lane per row
   constexpr int BATCH = UNIT == 4 ? 4 : 32 / UNIT;  // rows per lane per step (4, 4, 2)
   constexpr int NW = kHistThreads / 64;
   extern __shared__ uint64_t lds[];
   __shared__ uint64_t sh_tot[NW];
+  __shared__ int32_t s_fbase[kMaxBlockFeatures];
+  __shared__ int32_t s_fbins[kMaxBlockFeatures];
+  __shared__ int32_t s_fskip[kMaxBlockFeatures];
+  __shared__ uint64_t s_slice[kHistThreads / 64][kMaxBlockFeatures];
+  // Every load of the prologue is issued before the first branch (a cold
+  // cache makes each dependent round trip cost about a microsecond).
   const int32_t tile = blockIdx.x;
-  const int32_t total = ctrl->plan_total;
-  const TileDesc td = desc[tile];
-  if (tile >= total) return;
-  const int32_t v = td.node;
-  const int32_t ntiles = td.ntiles;
-  const int64_t r0 = td.r0;
-  const int64_t r1 = td.r1;
-
   const int32_t blk = blockIdx.y;
   const int32_t f0 = blk * block_features;
-  int32_t f1 = f0 + block_features;
-  if (f1 > n_features) f1 = n_features;
+  const int32_t f1 = f0 + block_features < n_features ? f0 + block_features : n_features;
+  const TileDesc td = desc[tile];
   const int32_t lb0 = bin_offset[f0];
-  const int32_t nbb = bin_offset[f1] - lb0;
-
-  for (int32_t b = threadIdx.x; b < nbb; b += kHistThreads) lds[b] = 0ull;
-
+  const int32_t lb1 = bin_offset[f1];
   const int32_t lpr = block_stride / UNIT;  // lanes per row
   const int32_t rpi = kHistThreads / lpr;   // rows per step of the workgroup
   const int32_t col = threadIdx.x % lpr;
@@ -404,14 +424,45 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(
   // (past the block's features) are always 0 and get skip bin 0, so they
   // never reach an atomic.  Bins are range-checked when the matrix is packed;
   // here any byte value stays inside the LDS allocation (kLdsHistSlack).
+  int32_t bo[NB];
+  int32_t sk[NB];
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    const int32_t f = f0 + UNIT * col + m;
+    const int32_t fc = f < f1 ? f : f0;
+    bo[m] = bin_offset[fc];
+    sk[m] = skip_bin != nullptr ? skip_bin[fc] : -1;
+  }
+  // the block's feature table (lane j: feature f0 + j) for the skip-bin pass
+  const int32_t tj = f0 + (int32_t)(threadIdx.x & (kMaxBlockFeatures - 1));
+  const int32_t tjc = tj < f1 ? tj : f0;
+  const int32_t t_lo = bin_offset[tjc];
+  const int32_t t_hi = bin_offset[tjc + 1];
+  const int32_t t_sk = skip_bin != nullptr ? skip_bin[tjc] : -1;
+  asm volatile("" ::: "memory");
+  if (td.node < 0) return;  // beyond the plan
+  const int32_t v = td.node;
+  const int32_t ntiles = td.ntiles;
+  const int64_t r0 = td.r0;
+  const int64_t r1 = td.r1;
+  const int32_t nbb = lb1 - lb0;
+  if (nbb < 0 || nbb > lds_bins) {  // the LDS holds lds_bins slots (+ slack)
+    if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
+    return;
+  }
+  for (int32_t b = threadIdx.x; b < lds_bins + kLdsHistSlack; b += kHistThreads) lds[b] = 0ull;
   int32_t base[NB];
   int32_t skip[NB];
 #pragma unroll
   for (int m = 0; m < NB; ++m) {
-    const int32_t f = f0 + UNIT * col + m;
-    const bool ok = (f < f1) && (rg < rpi);
-    base[m] = ok ? bin_offset[f] - lb0 : 0;
-    skip[m] = ok ? (skip_bin != nullptr ? skip_bin[f] : -1) : 0;
+    const bool ok = (f0 + UNIT * col + m < f1) && (rg < rpi);
+    base[m] = ok ? bo[m] - lb0 : 0;
+    skip[m] = ok ? sk[m] : 0;
+  }
+  if (threadIdx.x < kMaxBlockFeatures) {
+    s_fbase[threadIdx.x] = t_lo - lb0;
+    s_fbins[threadIdx.x] = t_hi - t_lo;
+    s_fskip[threadIdx.x] = tj < f1 ? t_sk : -1;
   }
   __syncthreads();
 
@@ -453,26 +504,35 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(
   }
   if (qmax > q_bound) dev_error(&ctrl->err, GBDT_E_OVERFLOW);
   // tile total from the column-0 lanes (one per row)
-  uint64_t t0 = (col == 0 && rg < rpi) ? tot : 0ull;
-  t0 = wave_sum(t0);
+  const uint64_t t0 = wave_sum_dpp((col == 0 && rg < rpi) ? tot : 0ull);
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   if (lane == 0) sh_tot[wid] = t0;
   __syncthreads();
-  uint64_t tile_total = 0ull;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) tile_total += sh_tot[w];
-
-  // skip bins: total minus the feature's other bins, one wave per feature
-  for (int32_t f = f0 + wid; f < f1; f += NW) {
-    const int32_t sb = skip_bin != nullptr ? skip_bin[f] : -1;
-    if (sb < 0) continue;
-    const int32_t fb = bin_offset[f] - lb0;
-    const int32_t fn = bin_offset[f + 1] - bin_offset[f];
+  // skip bins: tile total minus the feature's other bins.  Lane j sums bins
+  // [16 w, 16 w + 16) of feature f0 + j in wave w; wave 0 adds the slices.
+  const int32_t nf = f1 - f0;
+  if (lane < nf) {
+    const int32_t fb = s_fbase[lane];
+    const int32_t fn = s_fbins[lane];
     uint64_t s = 0ull;
-    for (int32_t c = lane; c < fn; c += 64) s += lds[fb + c];
-    s = wave_sum(s);
-    if (lane == 0 && sb < fn) lds[fb + sb] = tile_total - s;
+#pragma unroll
+    for (int c = 0; c < GBDT_MAX_BINS / NW; ++c) {
+      const int32_t cc = wid * (GBDT_MAX_BINS / NW) + c;
+      if (cc < fn) s += lds[fb + cc];
+    }
+    s_slice[wid][lane] = s;
+  }
+  __syncthreads();
+  if (wid == 0 && lane < nf && s_fskip[lane] >= 0 && s_fskip[lane] < s_fbins[lane]) {
+    uint64_t tile_total = 0ull;
+    uint64_t s = 0ull;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      tile_total += sh_tot[w];
+      s += s_slice[w][lane];
+    }
+    lds[s_fbase[lane] + s_fskip[lane]] = tile_total - s;
   }
   __syncthreads();
 
@@ -1481,6 +1541,8 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   if (rc) return rc;
   if (ft->max_block_bins < 1 || ft->max_block_bins > kLdsHistBudgetBins)
     return fail(GBDT_E_UNSUPPORTED, "max_block_bins outside the LDS histogram budget");
+  if (src->X.block_features > kMaxBlockFeatures)
+    return fail(GBDT_E_UNSUPPORTED, "more than 64 features in a column block");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
@@ -1505,8 +1567,8 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles, (unsigned)src->X.n_blocks), dim3(kHistThreads),
                      lds, s, src->X.bins, src->X.row_capacity, src->X.block_features,
                      src->X.block_stride, src->X.n_features, src->q, ft->bin_offset,
-                     ft->skip_bin, ft->total_bins, tdesc, bits, q_bound, hist_g, hist_cnt, hpart,
-                     ctrl);
+                     ft->skip_bin, ft->total_bins, ft->max_block_bins, tdesc, bits, q_bound, hist_g,
+                     hist_cnt, hpart, ctrl);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist");
   diag_begin(kDiagHistReduce, s);

@@ -258,9 +258,12 @@ int gbdt_compute_gradients(const double* pred, const float* label, int64_t n, in
  * j < *list_len (device count), adds to hist_g[v][b] / hist_cnt[v][b] the sum
  * of q and the number of rows among positions [nodes[v].begin,
  * nodes[v].begin + nodes[v].count) of src whose bin of feature f equals c,
- * for every global bin b = bin_offset[f] + c.  The slots of listed nodes must
- * be zero on entry for an overwrite (they are accumulated into, so shards can
- * be added).  hist_g, hist_cnt: [slots][total_bins], slot = node id.
+ * for every global bin b = bin_offset[f] + c.  The slots of listed nodes are
+ * overwritten (their previous contents are ignored); other slots are not
+ * touched.  hist_g, hist_cnt: [slots][total_bins], slot = node id.
+ * Requires block_features <= 64 (GBDT_E_UNSUPPORTED otherwise) and
+ * ft->max_block_bins at least the bins of every block; a block with more
+ * bins is skipped and sets GBDT_E_SHAPE.
  * rows_bound bounds the sum of the listed counts (sizes the launch);
  * list_cap bounds *list_len.  Requires |q_i| <= 2^(52 - ceil(log2 n_rows))
  * (as written by gbdt_compute_gradients); a violation sets GBDT_E_OVERFLOW.
