@@ -647,80 +647,134 @@ __device__ __forceinline__ double score_of(double G, double H, double lambda) {
   return num / den;
 }
 
-// Better of two candidates: larger gain, then smaller global bin (the
-// smaller feature, then the smaller threshold).  Gains are only ever
-// positive here, so IEEE equality is bit equality.
-__device__ __forceinline__ bool better(double g1, int32_t b1, double g2, int32_t b2) {
-  return g1 > g2 || (g1 == g2 && b1 < b2);
-}
-
-constexpr int kFindThreads = 1024;
 constexpr int kFindE = 8;  // bins per thread per pass
 
-// One workgroup per node.  The node's histogram is read in passes of
-// kFindThreads * kFindE bins in global bin order (feature-major, bins
-// ascending); thread t holds kFindE consecutive bins in registers, all loads
-// issued at once.  A segmented prefix sum (segments = features) -- serial
-// inside the thread, a wave scan of the per-thread tails across threads, and
-// a carry across passes -- gives every bin's left totals (G_L, n_L); each
-// candidate's gain is evaluated exactly as the formula is written, and the
-// workgroup keeps the largest gain, ties to the smaller global bin.
-__global__ void __launch_bounds__(kFindThreads) k_find(
+// DPP lane move of a 32-bit value; lanes whose source is outside the row (or
+// whose row is masked off) read 0, the identity of both combines below.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int32_t dpp_i32(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int64_t dpp_i64(int64_t v) {
+  return (int64_t)dpp_u64<CTRL, ROW_MASK>((uint64_t)v);
+}
+
+// One step of the inclusive segmented scan: the running value of the lane
+// CTRL moves in from (earlier lanes) is added unless this lane's run already
+// holds a segment head.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void seg_scan_step(int32_t& fl, int64_t& g, int32_t& c) {
+  const int32_t fu = dpp_i32<CTRL, ROW_MASK>(fl);
+  const int64_t gu = dpp_i64<CTRL, ROW_MASK>(g);
+  const int32_t cu = dpp_i32<CTRL, ROW_MASK>(c);
+  if (!fl) {
+    g += gu;
+    c += cu;
+    fl = fu;
+  }
+}
+
+// Candidate order: larger gain, then larger key (key = INT32_MAX - global
+// bin, so the smaller feature and then the smaller threshold win).  The
+// empty candidate is (0.0, 0): all zero bits.  Gains compared here are only
+// ever positive, so IEEE equality is bit equality.
+__device__ __forceinline__ bool better(double g1, int32_t k1, double g2, int32_t k2) {
+  return g1 > g2 || (g1 == g2 && k1 > k2);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(double& g, int32_t& key) {
+  const double og = __longlong_as_double(dpp_i64<CTRL, ROW_MASK>(__double_as_longlong(g)));
+  const int32_t ok = dpp_i32<CTRL, ROW_MASK>(key);
+  if (better(og, ok, g, key)) {
+    g = og;
+    key = ok;
+  }
+}
+
+// One workgroup of THREADS per node.  The node's histogram is read in passes
+// of THREADS * kFindE bins in global bin order (feature-major, bins
+// ascending); thread t holds kFindE consecutive bins in registers.  A
+// segmented prefix sum (segments = features) -- serial inside the thread,
+// a DPP scan of the per-thread tails across the wave, the waves' tails
+// through LDS, and a carry across passes -- gives every bin's left totals
+// (G_L, n_L); each candidate's gain is evaluated exactly as the formula is
+// written, and the workgroup keeps the largest gain, ties to the smaller
+// global bin.  The loads that do not depend on the node id are issued with
+// the list loads; the thread that owns the winning bin writes the split.
+template <int THREADS>
+__global__ void __launch_bounds__(THREADS) k_find(
     const int64_t* __restrict__ hist_g, const uint32_t* __restrict__ hist_cnt,
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ bin_feature,
     const int32_t* __restrict__ n_bins, int32_t total_bins, const gbdt_node* __restrict__ nodes,
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_len, int32_t list_cap,
     FindParams fp, const int32_t* __restrict__ scale, gbdt_split* __restrict__ splits) {
-  constexpr int NW = kFindThreads / 64;
+  constexpr int NW = THREADS / 64;
   __shared__ int64_t sw_g[NW];
   __shared__ int32_t sw_c[NW];
   __shared__ int32_t sw_f[NW];
   __shared__ int64_t s_carry_g;
   __shared__ int32_t s_carry_c;
   __shared__ double r_gain[NW];
-  __shared__ int32_t r_bin[NW];
-  __shared__ int64_t r_gl[NW];
-  __shared__ int32_t r_nl[NW];
-  const int32_t n = clamp_len(list_len, list_cap);
-  const int32_t j = blockIdx.x;
-  if (j >= n) return;
-  const int32_t v = list[j];
-  const gbdt_node nd = nodes[v];
-  const int32_t S = *scale;
-  const int64_t nv = nd.count;
-  const double Gv = ldexp((double)nd.gsum, -S);
-  const double Hv = (double)nd.count;
-  const double sP = score_of(Gv, Hv, fp.lambda);
+  __shared__ int32_t r_key[NW];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
+  const int32_t j = blockIdx.x;  // < list_cap (the grid)
+  const int32_t raw_len = *list_len;
+  const int32_t v = list[j];
+  const int32_t S = *scale;
+  int32_t f[kFindE + 2];  // features of bins b0-1 .. b0+kFindE of the first pass
+  {
+    const int32_t b0 = threadIdx.x * kFindE;
+#pragma unroll
+    for (int e = 0; e < kFindE + 2; ++e) {
+      const int32_t b = b0 - 1 + e;
+      const bool inb = b >= 0 && b < total_bins;
+      const int32_t fv = bin_feature[inb ? b : 0];
+      f[e] = inb ? fv : -1 - e;
+    }
+  }
+  asm volatile("" ::: "memory");
+  const int32_t n = raw_len < 0 ? 0 : (raw_len > list_cap ? list_cap : raw_len);
+  if (j >= n) return;
+  const gbdt_node nd = nodes[v];
   const int64_t* __restrict__ hg = hist_g + int64_t(v) * total_bins;
   const uint32_t* __restrict__ hc = hist_cnt + int64_t(v) * total_bins;
 
   double best_gain = 0.0;
-  int32_t best_bin = 0x7fffffff;
+  int32_t best_key = 0;
+  int32_t best_thr = -1, best_f = -1, best_nl = 0;
   int64_t best_gl = 0;
-  int32_t best_nl = 0;
   if (threadIdx.x == 0) {
     s_carry_g = 0;
     s_carry_c = 0;
   }
-  for (int32_t pass = 0; pass < total_bins; pass += kFindThreads * kFindE) {
+  for (int32_t pass = 0; pass < total_bins; pass += THREADS * kFindE) {
     const int32_t b0 = pass + threadIdx.x * kFindE;
+    if (pass > 0) {
+#pragma unroll
+      for (int e = 0; e < kFindE + 2; ++e) {
+        const int32_t b = b0 - 1 + e;
+        const bool inb = b >= 0 && b < total_bins;
+        const int32_t fv = bin_feature[inb ? b : 0];
+        f[e] = inb ? fv : -1 - e;
+      }
+    }
     int64_t g[kFindE];
     int32_t c[kFindE];
-    int32_t f[kFindE + 2];  // features of bins b0-1 .. b0+kFindE
+    int32_t fo[kFindE];  // first global bin of the feature of bin b0 + e
 #pragma unroll
     for (int e = 0; e < kFindE; ++e) {
       const int32_t b = b0 + e;
       const bool inb = b < total_bins;
       g[e] = inb ? hg[b] : 0;
       c[e] = inb ? (int32_t)hc[b] : 0;
+      fo[e] = bin_offset[inb ? f[e + 1] : 0];
     }
-#pragma unroll
-    for (int e = 0; e < kFindE + 2; ++e) {
-      const int32_t b = b0 - 1 + e;
-      f[e] = (b >= 0 && b < total_bins) ? bin_feature[b] : -1 - e;
-    }
+    const double Gv = ldexp((double)nd.gsum, -S);
+    const double Hv = (double)nd.count;
+    const double sP = score_of(Gv, Hv, fp.lambda);
+    const int64_t nv = nd.count;
     // serial segmented scan inside the thread
     int32_t first_head = kFindE;
     int64_t rg = 0;
@@ -734,20 +788,17 @@ __global__ void __launch_bounds__(kFindThreads) k_find(
       g[e] = rg;
       c[e] = rc;
     }
-    // segmented scan of the thread tails across the workgroup
+    // segmented scan of the thread tails across the wave (DPP row shifts,
+    // then rows 0 -> 1, 2 -> 3, row 1 -> rows 2 and 3)
     int32_t fl = first_head < kFindE ? 1 : 0;
     int64_t wg = rg;
     int32_t wc = rc;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int64_t gu = __shfl_up(wg, off, 64);
-      const int32_t cu = __shfl_up(wc, off, 64);
-      const int32_t fu = __shfl_up(fl, off, 64);
-      if (lane >= off && !fl) {
-        wg += gu;
-        wc += cu;
-        fl |= fu;
-      }
-    }
+    seg_scan_step<0x111, 0xF>(fl, wg, wc);  // row_shr:1
+    seg_scan_step<0x112, 0xF>(fl, wg, wc);  // row_shr:2
+    seg_scan_step<0x114, 0xF>(fl, wg, wc);  // row_shr:4
+    seg_scan_step<0x118, 0xF>(fl, wg, wc);  // row_shr:8
+    seg_scan_step<0x142, 0xA>(fl, wg, wc);  // row_bcast:15
+    seg_scan_step<0x143, 0xC>(fl, wg, wc);  // row_bcast:31
     if (lane == 63) {
       sw_g[wid] = wg;
       sw_c[wid] = wc;
@@ -767,14 +818,16 @@ __global__ void __launch_bounds__(kFindThreads) k_find(
     }
     const int64_t incl_g = fl ? wg : cgw + wg;  // open segment at this thread's end
     const int32_t incl_c = fl ? wc : ccw + wc;
-    int64_t cin_g = __shfl_up(incl_g, 1, 64);
-    int32_t cin_c = __shfl_up(incl_c, 1, 64);
+    // the open segment entering this thread: the previous lane's, or the
+    // wave's carry in lane 0 (wave_shr:1 gives lane 0 a zero)
+    int64_t cin_g = dpp_i64<0x138, 0xF>(incl_g);
+    int32_t cin_c = dpp_i32<0x138, 0xF>(incl_c);
     if (lane == 0) {
       cin_g = cgw;
       cin_c = ccw;
     }
     __syncthreads();
-    if (threadIdx.x == kFindThreads - 1) {
+    if (threadIdx.x == THREADS - 1) {
       s_carry_g = incl_g;
       s_carry_c = incl_c;
     }
@@ -799,61 +852,61 @@ __global__ void __launch_bounds__(kFindThreads) k_find(
         const double diff = sum - sP;
         const double half = 0.5 * diff;
         const double gain = half - fp.gamma;
-        if (gain > 0.0 && better(gain, b, best_gain, best_bin)) {
+        const int32_t key = 0x7fffffff - b;
+        if (gain > 0.0 && better(gain, key, best_gain, best_key)) {
           best_gain = gain;
-          best_bin = b;
+          best_key = key;
           best_gl = gl;
           best_nl = nlc;
+          best_f = f[e + 1];
+          best_thr = b - fo[e];
         }
       }
     }
     __syncthreads();
   }
-  // argmax over the workgroup
-  for (int off = 32; off > 0; off >>= 1) {
-    const double og = __shfl_xor(best_gain, off, 64);
-    const int32_t ob = __shfl_xor(best_bin, off, 64);
-    const int64_t ol = __shfl_xor(best_gl, off, 64);
-    const int32_t on = __shfl_xor(best_nl, off, 64);
-    if (better(og, ob, best_gain, best_bin)) {
-      best_gain = og;
-      best_bin = ob;
-      best_gl = ol;
-      best_nl = on;
-    }
-  }
-  if (lane == 0) {
-    r_gain[wid] = best_gain;
-    r_bin[wid] = best_bin;
-    r_gl[wid] = best_gl;
-    r_nl[wid] = best_nl;
+  // argmax over the wave (DPP), then over the waves
+  double wg_gain = best_gain;
+  int32_t wg_key = best_key;
+  argmax_step<0xB1, 0xF>(wg_gain, wg_key);   // quad_perm [1,0,3,2]
+  argmax_step<0x4E, 0xF>(wg_gain, wg_key);   // quad_perm [2,3,0,1]
+  argmax_step<0x141, 0xF>(wg_gain, wg_key);  // row_half_mirror
+  argmax_step<0x140, 0xF>(wg_gain, wg_key);  // row_mirror
+  argmax_step<0x142, 0xA>(wg_gain, wg_key);  // row_bcast:15
+  argmax_step<0x143, 0xC>(wg_gain, wg_key);  // row_bcast:31
+  if (lane == 63) {
+    r_gain[wid] = wg_gain;
+    r_key[wid] = wg_key;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < NW; ++w)
-      if (better(r_gain[w], r_bin[w], best_gain, best_bin)) {
-        best_gain = r_gain[w];
-        best_bin = r_bin[w];
-        best_gl = r_gl[w];
-        best_nl = r_nl[w];
-      }
-    gbdt_split sp;
-    if (best_bin != 0x7fffffff && best_gain > 0.0) {
-      const int32_t ff = bin_feature[best_bin];
+  double top_gain = r_gain[0];
+  int32_t top_key = r_key[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w)
+    if (better(r_gain[w], r_key[w], top_gain, top_key)) {
+      top_gain = r_gain[w];
+      top_key = r_key[w];
+    }
+  if (top_key != 0 && top_gain > 0.0) {
+    // the owner of the winning bin (each bin has one owner) writes the split
+    if (best_key == top_key) {
+      gbdt_split sp;
       sp.gain = best_gain;
-      sp.feature = ff;
-      sp.threshold_bin = best_bin - bin_offset[ff];
+      sp.feature = best_f;
+      sp.threshold_bin = best_thr;
       sp.g_left = best_gl;
       sp.n_left = best_nl;
       sp.valid = 1;
-    } else {
-      sp.gain = 0.0;
-      sp.feature = -1;
-      sp.threshold_bin = -1;
-      sp.g_left = 0;
-      sp.n_left = 0;
-      sp.valid = 0;
+      splits[v] = sp;
     }
+  } else if (threadIdx.x == 0) {
+    gbdt_split sp;
+    sp.gain = 0.0;
+    sp.feature = -1;
+    sp.threshold_bin = -1;
+    sp.g_left = 0;
+    sp.n_left = 0;
+    sp.valid = 0;
     splits[v] = sp;
   }
 }
@@ -1618,7 +1671,11 @@ int gbdt_find_best_splits(const int64_t* hist_g, const uint32_t* hist_cnt,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   FindParams fp{p->reg_lambda, p->gamma, p->min_child_weight, p->min_samples_leaf};
   diag_begin(kDiagFind, s);
-  hipLaunchKernelGGL(k_find, dim3((unsigned)list_cap), dim3(kFindThreads), 0, s, hist_g, hist_cnt,
+  // the fewest threads whose kFindE bins each cover the bins in one pass
+  const int32_t per_pass = (ft->total_bins + kFindE - 1) / kFindE;
+  const int threads = per_pass <= 256 ? 256 : (per_pass <= 512 ? 512 : 1024);
+  auto kern = threads == 256 ? k_find<256> : (threads == 512 ? k_find<512> : k_find<1024>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)list_cap), dim3(threads), 0, s, hist_g, hist_cnt,
                      ft->bin_offset, ft->bin_feature, ft->n_bins, ft->total_bins, nodes, list,
                      list_len, list_cap, fp, scale, splits);
   diag_end(s);
