@@ -1,17 +1,19 @@
 // Level-wise tree growth driver: the seven steps of "Module Design: Training
 // Core" (MPSBoost spec), section 6, run on the device without a host round
 // trip per level.  The host enqueues a fixed sequence of launches per level;
-// the level's node lists and counts live in device memory and are written by
-// k_level, so every launch is sized by a static bound and surplus workgroups
-// exit early (the one-sync-per-level idea of the ExaBoost PR, taken to zero
-// host syncs per tree).
+// the level's node lists, counts and tile plans live in device memory and are
+// written by k_level, so every launch is sized by a static bound and surplus
+// workgroups exit early (the one-sync-per-level idea of the ExaBoost PR,
+// taken to zero host syncs per tree).
 //
 // Per level d: histograms of the listed nodes (root, or the smaller child of
-// every split pair), subtraction for the larger siblings, split search,
-// k_level (breadth-first children, frozen leaves, next level's lists), and
-// the stable partition of the splitting nodes' rows into the other row
-// buffer (skipped at the last level).  After the last level every row is
-// routed through the finished tree and its prediction updated.
+// every split pair) and the reduction of multi-tile partials; split search,
+// which also derives each larger sibling's histogram (parent minus smaller);
+// k_level (breadth-first children, frozen leaves, next level's lists, this
+// level's partition plan and the next level's histogram plan); and the
+// stable partition of the splitting nodes' rows into the other row buffer
+// (skipped at the last level).  After the last level every row is routed
+// through the finished tree and its prediction updated.
 
 #include <hip/hip_runtime.h>
 
@@ -20,6 +22,7 @@
 
 #include "gbdt.h"
 #include "gbdt_internal.h"
+#include "gbdt_device.h"
 
 #pragma clang fp contract(off)
 
@@ -32,14 +35,17 @@ struct TreeCtrl {
   int32_t level_start[GBDT_MAX_DEPTH + 2];
   int32_t level_count[GBDT_MAX_DEPTH + 2];
   int32_t n_build[GBDT_MAX_DEPTH + 2];
-  int32_t n_pairs[GBDT_MAX_DEPTH + 2];
   int32_t n_find[GBDT_MAX_DEPTH + 2];
   int32_t n_split[GBDT_MAX_DEPTH + 2];
 };
 
+// Per-level lists (level d occupies words [2^d - 1, 2^(d+1) - 1) of each):
+// nodes whose histograms are built, nodes searched for a split (with, for a
+// larger sibling, its parent and built sibling, else -1), splitting nodes;
+// then the leaves of the tree.
 struct ListLayout {
-  int64_t per_type;  // 2^D - 1 words: level d occupies [2^d - 1, 2^(d+1) - 1)
-  int64_t build, find, split, pairs, leaves, total;
+  int64_t per_type;  // 2^D - 1 words
+  int64_t build, find, find_par, find_sib, split, leaves, total;
 };
 
 static ListLayout list_layout(int32_t D) {
@@ -48,12 +54,23 @@ static ListLayout list_layout(int32_t D) {
   L.per_type = m < 1 ? 1 : m;
   L.build = 0;
   L.find = L.per_type;
-  L.split = 2 * L.per_type;
-  L.pairs = 3 * L.per_type;
-  L.leaves = 7 * L.per_type;
+  L.find_par = 2 * L.per_type;
+  L.find_sib = 3 * L.per_type;
+  L.split = 4 * L.per_type;
+  L.leaves = 5 * L.per_type;
   L.total = L.leaves + (int64_t(1) << D) + 4;
   return L;
 }
+
+// Where the level kernel writes the two tile plans.
+struct PlanArgs {
+  int32_t* prefix;   // partition plan
+  TileDesc* desc;
+  uint64_t* status;
+  int32_t* hprefix;  // histogram plan
+  TileDesc* hdesc;
+  WsCtrl* ctrl;
+};
 
 __device__ __forceinline__ double leaf_weight(int64_t gsum, int32_t count, int32_t S, double lambda) {
   const double G = ldexp((double)gsum, -S);
@@ -71,77 +88,63 @@ __device__ __forceinline__ void make_leaf(gbdt_node* nd, double w) {
   nd->flags = GBDT_NODE_LEAF;
 }
 
-__device__ int32_t blk_scan(int32_t v, int32_t* total, int32_t* sh) {
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  int32_t x = v;
-  for (int off = 1; off < 64; off <<= 1) {
-    int32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) sh[wid] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int w = 0; w < nw; ++w) {
-      int32_t t = sh[w];
-      sh[w] = acc;
-      acc += t;
-    }
-    sh[31] = acc;
-  }
-  __syncthreads();
-  const int32_t r = sh[wid] + x - v;
-  *total = sh[31];
-  __syncthreads();
-  return r;
-}
-
-// Step 1 at the root: node 0 holds every row, lists of level 0.
-__global__ void k_tree_init(gbdt_node* __restrict__ nodes, gbdt_split* __restrict__ splits,
-                            TreeCtrl* __restrict__ tc, int32_t* __restrict__ lists, ListLayout LL,
-                            int32_t n, int64_t min_split, int32_t D, double lambda,
-                            int32_t* __restrict__ n_nodes_out) {
+// Step 1 at the root: node 0 holds every row, lists of level 0 and the
+// histogram plan of the root (tile_rows, max_tiles: the first level's).
+__global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ nodes,
+                                                    gbdt_split* __restrict__ splits,
+                                                    TreeCtrl* __restrict__ tc,
+                                                    int32_t* __restrict__ lists, ListLayout LL,
+                                                    int32_t n, int64_t min_split, int32_t D,
+                                                    double lambda, int32_t* __restrict__ n_nodes_out,
+                                                    PlanArgs pa, int32_t tile_rows,
+                                                    int32_t max_tiles) {
+  __shared__ int32_t sh[32];
+  __shared__ int32_t spre[kPlanLdsEntries + 1];
   for (int i = threadIdx.x; i < GBDT_MAX_DEPTH + 2; i += blockDim.x) {
     tc->level_start[i] = 0;
     tc->level_count[i] = 0;
     tc->n_build[i] = 0;
-    tc->n_pairs[i] = 0;
     tc->n_find[i] = 0;
     tc->n_split[i] = 0;
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  gbdt_node r;
-  r.feature = -1;
-  r.threshold_bin = -1;
-  r.left = -1;
-  r.right = -1;
-  r.leaf_value = 0.0;
-  r.gain = 0.0;
-  r.flags = 0u;
-  r.depth = 0;
-  r.begin = 0;
-  r.count = n;
-  r.gsum = tc->gsum_root;
-  r.reserved = 0;
-  tc->level_start[0] = 0;
-  tc->level_count[0] = 1;
-  tc->n_leaves = 0;
-  splits[0].valid = 0;
-  if (D == 0) {
-    make_leaf(&r, leaf_weight(r.gsum, n, tc->scale, lambda));
-    lists[LL.leaves] = 0;
-    tc->n_leaves = 1;
-  } else if ((int64_t)n >= min_split) {
-    lists[LL.build] = 0;
-    lists[LL.find] = 0;
-    tc->n_build[0] = 1;
-    tc->n_find[0] = 1;
+  const bool grow = D >= 1 && (int64_t)n >= min_split;
+  if (threadIdx.x == 0) {
+    gbdt_node r;
+    r.feature = -1;
+    r.threshold_bin = -1;
+    r.left = -1;
+    r.right = -1;
+    r.leaf_value = 0.0;
+    r.gain = 0.0;
+    r.flags = 0u;
+    r.depth = 0;
+    r.begin = 0;
+    r.count = n;
+    r.gsum = tc->gsum_root;
+    r.reserved = 0;
+    tc->level_start[0] = 0;
+    tc->level_count[0] = 1;
+    tc->n_leaves = 0;
+    splits[0].valid = 0;
+    if (D == 0) {
+      make_leaf(&r, leaf_weight(r.gsum, n, tc->scale, lambda));
+      lists[LL.leaves] = 0;
+      tc->n_leaves = 1;
+    } else if (grow) {
+      lists[LL.build] = 0;
+      lists[LL.find] = 0;
+      lists[LL.find_par] = -1;
+      lists[LL.find_sib] = -1;
+      tc->n_build[0] = 1;
+      tc->n_find[0] = 1;
+    }
+    nodes[0] = r;
+    *n_nodes_out = 1;
   }
-  nodes[0] = r;
-  *n_nodes_out = 1;
+  __syncthreads();
+  plan_tiles(nodes, lists + LL.build, grow ? 1 : 0, tile_rows, max_tiles, pa.hprefix, pa.hdesc,
+             nullptr, pa.ctrl, sh, spre);
 }
 
 // Steps 3-6 bookkeeping for level d, one workgroup: each level-d node either
@@ -155,8 +158,11 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 TreeCtrl* __restrict__ tc,
                                                 int32_t* __restrict__ lists, ListLayout LL,
                                                 int64_t min_split, double lambda,
-                                                int32_t* __restrict__ n_nodes_out) {
+                                                int32_t* __restrict__ n_nodes_out, PlanArgs pa,
+                                                int32_t part_max_tiles, int32_t hist_tile_rows_next,
+                                                int32_t hist_max_tiles_next) {
   __shared__ int32_t sh[32];
+  __shared__ int32_t spre[kPlanLdsEntries + 1];
   const int32_t first = tc->level_start[d];
   const int32_t cnt = tc->level_count[d];
   const int32_t S = tc->scale;
@@ -186,10 +192,10 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
     }
   }
   int32_t t_split, t_pair, t_find, t_leaf;
-  int32_t r_split = blk_scan(c_split, &t_split, sh);
-  int32_t r_pair = blk_scan(c_pair, &t_pair, sh);
-  int32_t r_find = blk_scan(c_find, &t_find, sh);
-  int32_t r_leaf = blk_scan(c_leaf, &t_leaf, sh);
+  int32_t r_split = block_exclusive_scan(c_split, &t_split, sh);
+  int32_t r_pair = block_exclusive_scan(c_pair, &t_pair, sh);
+  int32_t r_find = block_exclusive_scan(c_find, &t_find, sh);
+  int32_t r_leaf = block_exclusive_scan(c_leaf, &t_leaf, sh);
 
   const int64_t lvl_off = (int64_t(1) << d) - 1;
   const int64_t nxt_off = (int64_t(1) << (d + 1)) - 1;
@@ -197,7 +203,8 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   int32_t* leaves = lists + LL.leaves;
   int32_t* build_n = lists + LL.build + nxt_off;
   int32_t* find_n = lists + LL.find + nxt_off;
-  gbdt_pair* pairs_n = reinterpret_cast<gbdt_pair*>(lists + LL.pairs) + nxt_off;
+  int32_t* find_par_n = lists + LL.find_par + nxt_off;
+  int32_t* find_sib_n = lists + LL.find_sib + nxt_off;
 
   for (int32_t i = i0; i < i1; ++i) {
     const int32_t v = first + i;
@@ -237,18 +244,23 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
         leaves[leaf_base + r_leaf + 1] = rc;
         r_leaf += 2;
       } else if ((int64_t)(nl > nr ? nl : nr) >= min_split) {
+        // the smaller child is built; the larger one is derived in the
+        // split search (parent minus smaller)
         const int32_t sm = (nl <= nr) ? lc : rc;
-        const int32_t lg = (nl <= nr) ? rc : lc;
         build_n[r_pair] = sm;
-        gbdt_pair pr;
-        pr.parent = v;
-        pr.smaller = sm;
-        pr.larger = lg;
-        pr.pad = 0;
-        pairs_n[r_pair] = pr;
         ++r_pair;
-        if ((int64_t)nl >= min_split) find_n[r_find++] = lc;
-        if ((int64_t)nr >= min_split) find_n[r_find++] = rc;
+        if ((int64_t)nl >= min_split) {
+          find_n[r_find] = lc;
+          find_par_n[r_find] = lc == sm ? -1 : v;
+          find_sib_n[r_find] = lc == sm ? -1 : sm;
+          ++r_find;
+        }
+        if ((int64_t)nr >= min_split) {
+          find_n[r_find] = rc;
+          find_par_n[r_find] = rc == sm ? -1 : v;
+          find_sib_n[r_find] = rc == sm ? -1 : sm;
+          ++r_find;
+        }
       }
       nodes[lc] = L;
       nodes[rc] = R;
@@ -269,12 +281,19 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
     tc->level_count[d + 1] = 2 * t_split;
     if (!last) {
       tc->n_build[d + 1] = t_pair;
-      tc->n_pairs[d + 1] = t_pair;
       tc->n_find[d + 1] = t_find;
     }
     tc->n_leaves = leaf_base + t_leaf;
     *n_nodes_out = child_first + 2 * t_split;
   }
+  if (last) return;
+  __syncthreads();  // the lists and the children's counts are visible to the workgroup
+  // this level's partition plan (splitting nodes) and the next level's
+  // histogram plan (nodes to build)
+  plan_tiles(nodes, split_list, t_split, kPartTileRows, part_max_tiles, pa.prefix, pa.desc, pa.status,
+             pa.ctrl, sh, spre);
+  plan_tiles(nodes, build_n, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix, pa.hdesc,
+             nullptr, pa.ctrl, sh, spre);
 }
 
 static int64_t min_split_count(const gbdt_params* p, int64_t n) {
@@ -332,50 +351,75 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   if (rc) return rc;
   if (b->ws_bytes < size_t(sz.ws_bytes)) return fail(GBDT_E_ARG, "workspace too small for this tree");
 
+  gbdt_rows src;
+  src.X = *X;
+  src.q = b->q;
+  src.rid = nullptr;
+  rc = check_hist_inputs(src, *ft);
+  if (rc) return rc;
+  rc = check_partition_inputs(b->pp[0], b->pp[1]);
+  if (rc) return rc;
+
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   TreeCtrl* tc = reinterpret_cast<TreeCtrl*>(b->ctrl);
   const ListLayout LL = list_layout(D);
   const int64_t min_split = min_split_count(p, n);
+  const WsLayout WL = ws_layout(n, int32_t(1) << D, ft->total_bins);
+  char* w = static_cast<char*>(b->ws);
+  PlanArgs pa;
+  pa.ctrl = reinterpret_cast<WsCtrl*>(w + WL.ctrl);
+  pa.prefix = reinterpret_cast<int32_t*>(w + WL.prefix);
+  pa.desc = reinterpret_cast<TileDesc*>(w + WL.tdesc);
+  pa.status = reinterpret_cast<uint64_t*>(w + WL.status);
+  pa.hprefix = reinterpret_cast<int32_t*>(w + WL.hprefix);
+  pa.hdesc = reinterpret_cast<TileDesc*>(w + WL.hdesc);
+  uint64_t* hpart = reinterpret_cast<uint64_t*>(w + WL.hpart);
+  // per level: histogram tile rows and launch bounds (level d builds at most
+  // 2^(d-1) nodes holding at most n/2 rows; the root builds n rows)
+  int32_t h_rows[GBDT_MAX_DEPTH + 1];
+  int64_t h_tiles[GBDT_MAX_DEPTH + 1];
+  int64_t p_tiles[GBDT_MAX_DEPTH + 1];
+  for (int32_t d = 0; d <= D; ++d) {
+    const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
+    const int64_t rows_build = d == 0 ? n : n / 2;
+    h_rows[d] = hist_tile_rows(rows_build, n);
+    h_tiles[d] = (rows_build + h_rows[d] - 1) / h_rows[d] + cap_build;
+    p_tiles[d] = (n + kPartTileRows - 1) / kPartTileRows + (int64_t(1) << d);
+    if (h_tiles[d] > WL.hpart_tiles || p_tiles[d] > WL.status_cap)
+      return fail(GBDT_E_INTERNAL, "tile bound exceeds the workspace");
+  }
 
   rc = gbdt_compute_gradients(pred, label, n, b->q, &tc->scale, &tc->gsum_root, b->ws, b->ws_bytes,
                               stream);
   if (rc) return rc;
   diag_begin(kDiagTreeInit, s);
-  hipLaunchKernelGGL(k_tree_init, dim3(1), dim3(64), 0, s, nodes_out, b->splits, tc, b->lists, LL,
-                     (int32_t)n, min_split, D, p->reg_lambda, n_nodes_dev);
+  hipLaunchKernelGGL(k_tree_init, dim3(1), dim3(1024), 0, s, nodes_out, b->splits, tc, b->lists, LL,
+                     (int32_t)n, min_split, D, p->reg_lambda, n_nodes_dev, pa, h_rows[0],
+                     (int32_t)h_tiles[0]);
   diag_end(s);
   {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "k_tree_init");
   }
 
-  gbdt_rows src;
-  src.X = *X;
-  src.q = b->q;
-  src.rid = nullptr;
   for (int32_t d = 0; d < D; ++d) {
     const gbdt_rows& dst = b->pp[d & 1];
     const int64_t lvl_off = (int64_t(1) << d) - 1;
     const int32_t cap_lvl = int32_t(1) << d;
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
-    const int64_t rows_build = d == 0 ? n : n / 2;
-    rc = gbdt_build_histograms(&src, ft, nodes_out, b->lists + LL.build + lvl_off, &tc->n_build[d],
-                               cap_build, rows_build, b->hist_g, b->hist_cnt, b->ws, b->ws_bytes,
-                               stream);
+    rc = launch_hist(src, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s);
     if (rc) return rc;
-    if (d >= 1) {
-      rc = gbdt_subtract_histograms(b->hist_g, b->hist_cnt, ft->total_bins,
-                                    reinterpret_cast<const gbdt_pair*>(b->lists + LL.pairs) + lvl_off,
-                                    &tc->n_pairs[d], cap_build, b->ws, b->ws_bytes, stream);
-      if (rc) return rc;
-    }
-    rc = gbdt_find_best_splits(b->hist_g, b->hist_cnt, ft, nodes_out, b->lists + LL.find + lvl_off,
-                               &tc->n_find[d], cap_lvl, p, &tc->scale, b->splits, b->ws,
-                               b->ws_bytes, stream);
+    rc = launch_hist_reduce(b->lists + LL.build + lvl_off, &tc->n_build[d], cap_build, pa.hprefix,
+                            h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s);
+    if (rc) return rc;
+    rc = launch_find(b->hist_g, b->hist_cnt, *ft, nodes_out, b->lists + LL.find + lvl_off,
+                     &tc->n_find[d], cap_lvl, *p, &tc->scale, b->splits,
+                     b->lists + LL.find_par + lvl_off, b->lists + LL.find_sib + lvl_off, pa.ctrl, s);
     if (rc) return rc;
     diag_begin(kDiagLevel, s);
     hipLaunchKernelGGL(k_level, dim3(1), dim3(1024), 0, s, d, D, nodes_out, b->splits, tc, b->lists,
-                       LL, min_split, p->reg_lambda, n_nodes_dev);
+                       LL, min_split, p->reg_lambda, n_nodes_dev, pa, (int32_t)p_tiles[d],
+                       h_rows[d + 1], (int32_t)h_tiles[d + 1]);
     diag_end(s);
     {
       hipError_t e = hipGetLastError();
@@ -384,8 +428,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     // the rows of the last level's children are never read again: the
     // prediction update routes rows through the finished tree instead
     if (d + 1 < D) {
-      rc = gbdt_partition_rows(&src, &dst, nodes_out, b->splits, b->lists + LL.split + lvl_off,
-                               &tc->n_split[d], cap_lvl, n, b->ws, b->ws_bytes, stream);
+      rc = launch_partition(src, dst, b->splits, pa.desc, pa.status, pa.ctrl, p_tiles[d], s);
       if (rc) return rc;
       src = dst;
     }

@@ -39,11 +39,17 @@ struct TileDesc {
 };
 static_assert(sizeof(TileDesc) == 32, "tile descriptor is 32 bytes");
 
+// Two tile plans live in the workspace at once: the partition plan
+// (tdesc, prefix, status, ctrl->ticket / plan_total) and the histogram plan
+// (hdesc, hprefix), so the level kernel of the tree driver can write this
+// level's partition plan and the next level's histogram plan together.
 struct WsLayout {
   size_t ctrl;        // WsCtrl
-  size_t tdesc;       // TileDesc[tdesc_cap]
+  size_t tdesc;       // TileDesc[tdesc_cap]: partition plan
+  size_t hdesc;       // TileDesc[hpart_tiles]: histogram plan
   size_t gpart;       // double[kGradBlocks]
-  size_t prefix;      // int32[max_list + 2]
+  size_t prefix;      // int32[max_list + 2]: partition plan
+  size_t hprefix;     // int32[max_list + 2]: histogram plan
   size_t status;      // uint64[status_cap]
   size_t hpart;       // uint64[hpart_tiles * total_bins]
   size_t total;
@@ -75,6 +81,24 @@ inline int32_t pack_bits_for(int64_t n_rows) {
 }
 
 int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows);
+
+// Argument checks and launches shared by the per-call entry points and the
+// tree driver (the driver's level kernel writes the tile plans itself).
+int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft);
+int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
+int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
+                int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
+                WsCtrl* ctrl, hipStream_t s);
+int launch_hist_reduce(const int32_t* list, const int32_t* list_len, int32_t list_cap,
+                       const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
+                       const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s);
+int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,
+                const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
+                const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
+                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s);
+int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const gbdt_split* splits,
+                     const TileDesc* desc, uint64_t* status, WsCtrl* ctrl, int64_t max_tiles,
+                     hipStream_t s);
 
 // Per-kernel device timing (the backend's diagnostics): when enabled, every
 // launch of the library is bracketed by two hipEvents on its stream.

@@ -16,6 +16,7 @@
 
 #include "gbdt.h"
 #include "gbdt_internal.h"
+#include "gbdt_device.h"
 
 #pragma clang fp contract(off)
 
@@ -76,15 +77,19 @@ WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
   if (total_bins < 1) total_bins = 1;
   L.status_cap = (n_rows + kPartTileRows - 1) / kPartTileRows + int64_t(max_list) + 2;
   L.hpart_tiles = int64_t(kHistTargetTiles) + int64_t(max_list) + 2;
-  L.tdesc_cap = L.status_cap > L.hpart_tiles ? L.status_cap : L.hpart_tiles;
+  L.tdesc_cap = L.status_cap;
   size_t off = 0;
   L.ctrl = off;
   off = align256(off + sizeof(WsCtrl));
   L.tdesc = off;
   off = align256(off + sizeof(TileDesc) * size_t(L.tdesc_cap));
+  L.hdesc = off;
+  off = align256(off + sizeof(TileDesc) * size_t(L.hpart_tiles));
   L.gpart = off;
   off = align256(off + sizeof(double) * kGradBlocks);
   L.prefix = off;
+  off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
+  L.hprefix = off;
   off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
   L.status = off;
   off = align256(off + sizeof(uint64_t) * size_t(L.status_cap));
@@ -107,16 +112,6 @@ int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows) {
 }
 
 // ------------------------------------------------------- device helpers --
-
-__device__ __forceinline__ void dev_error(int32_t* err, int code) {
-  atomicCAS(err, 0, code);
-}
-
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
 
 // Sum of a 64-bit value over the 64 lanes of a wave with DPP lane moves (no
 // LDS round trips): pairs and quads, half rows, rows, then rows 0+1 into row
@@ -145,57 +140,9 @@ __device__ __forceinline__ double wave_max(double v) {
   return v;
 }
 
-// Exclusive scan of one int32 per thread across a workgroup of nthreads
-// (multiple of 64, <= 1024).  Returns the exclusive prefix; *total = sum.
-__device__ int32_t block_exclusive_scan(int32_t v, int32_t* total, int32_t* sh /*[32]*/) {
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int nw = (blockDim.x + 63) >> 6;
-  int32_t x = v;
-  for (int off = 1; off < 64; off <<= 1) {
-    int32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) sh[wid] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int w = 0; w < nw; ++w) {
-      int32_t t = sh[w];
-      sh[w] = acc;
-      acc += t;
-    }
-    sh[31] = acc;
-  }
-  __syncthreads();
-  int32_t res = sh[wid] + x - v;
-  *total = sh[31];
-  __syncthreads();
-  return res;
-}
-
-// Tile lookup: largest j in [0, n) with prefix[j] <= tile (prefix ascending).
-__device__ __forceinline__ int32_t find_tile_owner(const int32_t* prefix, int32_t n, int32_t tile) {
-  int32_t lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int32_t mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-__device__ __forceinline__ int32_t clamp_len(const int32_t* len, int32_t cap) {
-  int32_t n = *len;
-  return n < 0 ? 0 : (n > cap ? cap : n);
-}
-
 // ---------------------------------------------------------------- planner --
-// One workgroup: tiles per listed node (at least one), their exclusive
-// prefix, the total, one descriptor per tile (so a workgroup of the launch
-// that follows reads its whole assignment with a single load), and
-// (optionally) a cleared look-back status array and ticket.
-constexpr int kPlanLdsEntries = 8192;
-
+// Standalone planner launch for the per-call entry points: plans
+// list[0..*list_len) (see plan_tiles).
 __global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nodes,
                                                const int32_t* __restrict__ list,
                                                const int32_t* __restrict__ list_len,
@@ -206,62 +153,10 @@ __global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nod
                                                uint64_t* __restrict__ status) {
   __shared__ int32_t sh[32];
   __shared__ int32_t spre[kPlanLdsEntries + 1];
-  int32_t raw = *list_len;
+  const int32_t raw = *list_len;
   if (threadIdx.x == 0 && (raw < 0 || raw > list_cap)) dev_error(&ctrl->err, GBDT_E_SHAPE);
   const int32_t n = clamp_len(list_len, list_cap);
-  const int32_t per = (n + blockDim.x - 1) / blockDim.x;
-  const int32_t j0 = threadIdx.x * per;
-  int32_t local = 0;
-  for (int32_t j = j0; j < j0 + per && j < n; ++j) {
-    int32_t c = nodes[list[j]].count;
-    if (c < 0) c = 0;
-    local += c == 0 ? 1 : (c + tile_rows - 1) / tile_rows;
-  }
-  int32_t total;
-  int32_t excl = block_exclusive_scan(local, &total, sh);
-  const bool in_lds = n <= kPlanLdsEntries;
-  for (int32_t j = j0; j < j0 + per && j < n; ++j) {
-    prefix[j] = excl;
-    if (in_lds) spre[j] = excl;
-    int32_t c = nodes[list[j]].count;
-    if (c < 0) c = 0;
-    excl += c == 0 ? 1 : (c + tile_rows - 1) / tile_rows;
-  }
-  if (threadIdx.x == 0) {
-    prefix[n] = total;
-    if (in_lds) spre[n] = total;
-    if (total > max_tiles) dev_error(&ctrl->err, GBDT_E_SHAPE);
-    ctrl->plan_total = total < max_tiles ? total : max_tiles;
-    ctrl->ticket = 0u;
-  }
-  __syncthreads();
-  const int32_t lim = total < max_tiles ? total : max_tiles;
-  for (int32_t t = threadIdx.x; t < lim; t += blockDim.x) {
-    const int32_t* pre = in_lds ? spre : prefix;
-    int32_t lo = 0, hi = n - 1;
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int32_t v = list[lo];
-    const gbdt_node nd = nodes[v];
-    const int32_t tf = pre[lo];
-    const int32_t nt = pre[lo + 1] - tf;
-    const int32_t cnt = nd.count < 0 ? 0 : nd.count;
-    TileDesc d;
-    d.node = v;
-    d.r0 = nd.begin + (t - tf) * tile_rows;
-    d.r1 = d.r0 + tile_rows < nd.begin + cnt ? d.r0 + tile_rows : nd.begin + cnt;
-    d.ntiles = nt;
-    d.tfirst = tf;
-    d.j = lo;
-    d.begin = nd.begin;
-    d.count = cnt;
-    desc[t] = d;
-    if (status != nullptr) status[t] = 0ull;
-  }
-  // tiles of the launch beyond the plan read a descriptor with node -1
-  for (int32_t t = lim + threadIdx.x; t < max_tiles; t += blockDim.x) desc[t].node = -1;
+  plan_tiles(nodes, list, n, tile_rows, max_tiles, prefix, desc, status, ctrl, sh, spre);
 }
 
 // -------------------------------------------------------------- gradients --
@@ -702,13 +597,19 @@ __device__ __forceinline__ void argmax_step(double& g, int32_t& key) {
 // written, and the workgroup keeps the largest gain, ties to the smaller
 // global bin.  The loads that do not depend on the node id are issued with
 // the list loads; the thread that owns the winning bin writes the split.
+// With sub_par / sub_sib (the tree driver), a node whose entry names a parent
+// is the larger child of a split pair: its histogram is the parent's minus
+// its built sibling's (exact integers), computed here and written to its own
+// slot for the next level; a negative count sets GBDT_E_INTERNAL.
 template <int THREADS>
 __global__ void __launch_bounds__(THREADS) k_find(
-    const int64_t* __restrict__ hist_g, const uint32_t* __restrict__ hist_cnt,
+    int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ bin_feature,
     const int32_t* __restrict__ n_bins, int32_t total_bins, const gbdt_node* __restrict__ nodes,
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_len, int32_t list_cap,
-    FindParams fp, const int32_t* __restrict__ scale, gbdt_split* __restrict__ splits) {
+    FindParams fp, const int32_t* __restrict__ scale, gbdt_split* __restrict__ splits,
+    const int32_t* __restrict__ sub_par, const int32_t* __restrict__ sub_sib,
+    int32_t* __restrict__ err) {
   constexpr int NW = THREADS / 64;
   __shared__ int64_t sw_g[NW];
   __shared__ int32_t sw_c[NW];
@@ -723,6 +624,8 @@ __global__ void __launch_bounds__(THREADS) k_find(
   const int32_t raw_len = *list_len;
   const int32_t v = list[j];
   const int32_t S = *scale;
+  const int32_t par = sub_par != nullptr ? sub_par[j] : -1;
+  const int32_t sib = sub_par != nullptr ? sub_sib[j] : -1;
   int32_t f[kFindE + 2];  // features of bins b0-1 .. b0+kFindE of the first pass
   {
     const int32_t b0 = threadIdx.x * kFindE;
@@ -738,8 +641,14 @@ __global__ void __launch_bounds__(THREADS) k_find(
   const int32_t n = raw_len < 0 ? 0 : (raw_len > list_cap ? list_cap : raw_len);
   if (j >= n) return;
   const gbdt_node nd = nodes[v];
-  const int64_t* __restrict__ hg = hist_g + int64_t(v) * total_bins;
-  const uint32_t* __restrict__ hc = hist_cnt + int64_t(v) * total_bins;
+  int64_t* __restrict__ hg = hist_g + int64_t(v) * total_bins;
+  uint32_t* __restrict__ hc = hist_cnt + int64_t(v) * total_bins;
+  const bool derive = par >= 0;
+  const int64_t* __restrict__ hg_p = hist_g + int64_t(derive ? par : v) * total_bins;
+  const uint32_t* __restrict__ hc_p = hist_cnt + int64_t(derive ? par : v) * total_bins;
+  const int64_t* __restrict__ hg_s = hist_g + int64_t(derive ? sib : v) * total_bins;
+  const uint32_t* __restrict__ hc_s = hist_cnt + int64_t(derive ? sib : v) * total_bins;
+  bool bad = false;
 
   double best_gain = 0.0;
   int32_t best_key = 0;
@@ -763,13 +672,34 @@ __global__ void __launch_bounds__(THREADS) k_find(
     int64_t g[kFindE];
     int32_t c[kFindE];
     int32_t fo[kFindE];  // first global bin of the feature of bin b0 + e
+    if (derive) {
 #pragma unroll
-    for (int e = 0; e < kFindE; ++e) {
-      const int32_t b = b0 + e;
-      const bool inb = b < total_bins;
-      g[e] = inb ? hg[b] : 0;
-      c[e] = inb ? (int32_t)hc[b] : 0;
-      fo[e] = bin_offset[inb ? f[e + 1] : 0];
+      for (int e = 0; e < kFindE; ++e) {
+        const int32_t b = b0 + e;
+        const bool inb = b < total_bins;
+        const uint32_t cp = inb ? hc_p[b] : 0u, cs = inb ? hc_s[b] : 0u;
+        g[e] = inb ? hg_p[b] - hg_s[b] : 0;
+        c[e] = (int32_t)(cp - cs);
+        bad |= cs > cp;
+        fo[e] = bin_offset[inb ? f[e + 1] : 0];
+      }
+#pragma unroll
+      for (int e = 0; e < kFindE; ++e) {
+        const int32_t b = b0 + e;
+        if (b < total_bins) {
+          hg[b] = g[e];
+          hc[b] = (uint32_t)c[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kFindE; ++e) {
+        const int32_t b = b0 + e;
+        const bool inb = b < total_bins;
+        g[e] = inb ? hg[b] : 0;
+        c[e] = inb ? (int32_t)hc[b] : 0;
+        fo[e] = bin_offset[inb ? f[e + 1] : 0];
+      }
     }
     const double Gv = ldexp((double)nd.gsum, -S);
     const double Hv = (double)nd.count;
@@ -865,6 +795,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
     }
     __syncthreads();
   }
+  if (bad) dev_error(err, GBDT_E_INTERNAL);
   // argmax over the wave (DPP), then over the waves
   double wg_gain = best_gain;
   int32_t wg_key = best_key;
@@ -1385,6 +1316,99 @@ static int check_features(const gbdt_features& ft, int32_t n_features) {
 }
 
 
+int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft) {
+  int rc = check_matrix(src.X);
+  if (rc) return rc;
+  rc = check_features(ft, src.X.n_features);
+  if (rc) return rc;
+  if (!src.q) return fail(GBDT_E_ARG, "q is null");
+  if (ft.max_block_bins < 1 || ft.max_block_bins > kLdsHistBudgetBins)
+    return fail(GBDT_E_UNSUPPORTED, "max_block_bins outside the LDS histogram budget");
+  if (src.X.block_features > kMaxBlockFeatures)
+    return fail(GBDT_E_UNSUPPORTED, "more than 64 features in a column block");
+  return GBDT_OK;
+}
+
+int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst) {
+  int rc = check_matrix(src.X);
+  if (rc) return rc;
+  rc = check_matrix(dst.X);
+  if (rc) return rc;
+  if (src.X.n_blocks != dst.X.n_blocks || src.X.block_stride != dst.X.block_stride ||
+      src.X.block_features != dst.X.block_features || src.X.row_capacity != dst.X.row_capacity ||
+      src.X.n_rows != dst.X.n_rows)
+    return fail(GBDT_E_SHAPE, "source and destination layouts differ");
+  if (!src.q || !dst.q) return fail(GBDT_E_ARG, "q pointer is null");
+  return GBDT_OK;
+}
+
+int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
+                int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
+                WsCtrl* ctrl, hipStream_t s) {
+  const int64_t n_rows = src.X.n_rows > 0 ? src.X.n_rows : 1;
+  const int32_t bits = pack_bits_for(n_rows);
+  const int64_t q_bound = int64_t(1) << (52 - ceil_log2(n_rows));
+  const size_t lds = sizeof(uint64_t) * size_t(ft.max_block_bins + kLdsHistSlack);
+  const int unit = load_unit_for(src.X.block_stride);
+  auto kern = unit == 16 ? k_hist<16> : (unit == 8 ? k_hist<8> : k_hist<4>);
+  diag_begin(kDiagHist, s);
+  hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles, (unsigned)src.X.n_blocks), dim3(kHistThreads),
+                     lds, s, src.X.bins, src.X.row_capacity, src.X.block_features,
+                     src.X.block_stride, src.X.n_features, src.q, ft.bin_offset, ft.skip_bin,
+                     ft.total_bins, ft.max_block_bins, desc, bits, q_bound, hist_g, hist_cnt, hpart,
+                     ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_hist");
+  return GBDT_OK;
+}
+
+int launch_hist_reduce(const int32_t* list, const int32_t* list_len, int32_t list_cap,
+                       const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
+                       const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s) {
+  const int32_t bits = pack_bits_for(n_rows > 0 ? n_rows : 1);
+  diag_begin(kDiagHistReduce, s);
+  hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)((total_bins + 63) / 64), (unsigned)list_cap),
+                     dim3(1024), 0, s, list, list_len, list_cap, prefix, (int32_t)max_tiles, bits,
+                     total_bins, hpart, hist_g, hist_cnt);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_hist_reduce");
+  return GBDT_OK;
+}
+
+int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,
+                const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
+                const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
+                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s) {
+  FindParams fp{p.reg_lambda, p.gamma, p.min_child_weight, p.min_samples_leaf};
+  // the fewest threads whose kFindE bins each cover the bins in one pass
+  const int32_t per_pass = (ft.total_bins + kFindE - 1) / kFindE;
+  const int threads = per_pass <= 256 ? 256 : (per_pass <= 512 ? 512 : 1024);
+  auto kern = threads == 256 ? k_find<256> : (threads == 512 ? k_find<512> : k_find<1024>);
+  diag_begin(kDiagFind, s);
+  hipLaunchKernelGGL(kern, dim3((unsigned)list_cap), dim3(threads), 0, s, hist_g, hist_cnt,
+                     ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
+                     list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
+                     ctrl != nullptr ? &ctrl->err : nullptr);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_find");
+  return GBDT_OK;
+}
+
+int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const gbdt_split* splits,
+                     const TileDesc* desc, uint64_t* status, WsCtrl* ctrl, int64_t max_tiles,
+                     hipStream_t s) {
+  const int unit = load_unit_for(src.X.block_stride);
+  auto kern = unit == 16 ? k_partition<16> : (unit == 8 ? k_partition<8> : k_partition<4>);
+  diag_begin(kDiagPartition, s);
+  hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s, src.X.bins, src.q,
+                     src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
+                     src.X.block_features, src.X.block_stride, src.X.n_features, splits, desc,
+                     status, ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_partition");
+  return GBDT_OK;
+}
+
 }  // namespace gbdt
 
 using namespace gbdt;
@@ -1582,55 +1606,31 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
                           size_t ws_bytes, void* stream) {
   if (!src || !ft || !nodes || !list || !list_len || !hist_g || !hist_cnt)
     return fail(GBDT_E_ARG, "null argument");
-  int rc = check_matrix(src->X);
+  int rc = check_hist_inputs(*src, *ft);
   if (rc) return rc;
-  rc = check_features(*ft, src->X.n_features);
-  if (rc) return rc;
-  if (!src->q) return fail(GBDT_E_ARG, "q is null");
   if (list_cap < 0 || rows_bound < 0) return fail(GBDT_E_ARG, "negative capacity");
   if (list_cap == 0) return GBDT_OK;
   const WsLayout L = ws_layout(src->X.n_rows, list_cap, ft->total_bins);
   rc = check_ws(ws, ws_bytes, L);
   if (rc) return rc;
-  if (ft->max_block_bins < 1 || ft->max_block_bins > kLdsHistBudgetBins)
-    return fail(GBDT_E_UNSUPPORTED, "max_block_bins outside the LDS histogram budget");
-  if (src->X.block_features > kMaxBlockFeatures)
-    return fail(GBDT_E_UNSUPPORTED, "more than 64 features in a column block");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
-  int32_t* prefix = reinterpret_cast<int32_t*>(w + L.prefix);
-  TileDesc* tdesc = reinterpret_cast<TileDesc*>(w + L.tdesc);
+  int32_t* hprefix = reinterpret_cast<int32_t*>(w + L.hprefix);
+  TileDesc* hdesc = reinterpret_cast<TileDesc*>(w + L.hdesc);
   uint64_t* hpart = reinterpret_cast<uint64_t*>(w + L.hpart);
-  const int32_t n_rows_for_bits = (int32_t)(src->X.n_rows > 0 ? src->X.n_rows : 1);
-  const int32_t bits = pack_bits_for(n_rows_for_bits);
-  const int32_t T = hist_tile_rows(rows_bound, n_rows_for_bits);
+  const int32_t T = hist_tile_rows(rows_bound, src->X.n_rows);
   const int64_t max_tiles = (rows_bound + T - 1) / T + list_cap;
   if (max_tiles > L.hpart_tiles) return fail(GBDT_E_SHAPE, "too many histogram tiles for the workspace");
-  const int64_t q_bound = int64_t(1) << (52 - ceil_log2(n_rows_for_bits));
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap, T,
-                     (int32_t)max_tiles, prefix, tdesc, ctrl, (uint64_t*)nullptr);
+                     (int32_t)max_tiles, hprefix, hdesc, ctrl, (uint64_t*)nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
-  const size_t lds = sizeof(uint64_t) * size_t(ft->max_block_bins + kLdsHistSlack);
-  const int unit = load_unit_for(src->X.block_stride);
-  auto kern = unit == 16 ? k_hist<16> : (unit == 8 ? k_hist<8> : k_hist<4>);
-  diag_begin(kDiagHist, s);
-  hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles, (unsigned)src->X.n_blocks), dim3(kHistThreads),
-                     lds, s, src->X.bins, src->X.row_capacity, src->X.block_features,
-                     src->X.block_stride, src->X.n_features, src->q, ft->bin_offset,
-                     ft->skip_bin, ft->total_bins, ft->max_block_bins, tdesc, bits, q_bound, hist_g,
-                     hist_cnt, hpart, ctrl);
-  diag_end(s);
-  GBDT_LAUNCH_CHECK("k_hist");
-  diag_begin(kDiagHistReduce, s);
-  hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)((ft->total_bins + 63) / 64), (unsigned)list_cap),
-                     dim3(1024), 0, s, list, list_len, list_cap, prefix, (int32_t)max_tiles, bits,
-                     ft->total_bins, hpart, hist_g, hist_cnt);
-  diag_end(s);
-  GBDT_LAUNCH_CHECK("k_hist_reduce");
-  return GBDT_OK;
+  rc = launch_hist(*src, *ft, hdesc, max_tiles, hist_g, hist_cnt, hpart, ctrl, s);
+  if (rc) return rc;
+  return launch_hist_reduce(list, list_len, list_cap, hprefix, max_tiles, src->X.n_rows,
+                            ft->total_bins, hpart, hist_g, hist_cnt, s);
 }
 
 int gbdt_subtract_histograms(int64_t* hist_g, uint32_t* hist_cnt, int32_t total_bins,
@@ -1668,19 +1668,10 @@ int gbdt_find_best_splits(const int64_t* hist_g, const uint32_t* hist_cnt,
   if (list_cap == 0) return GBDT_OK;
   (void)ws;
   (void)ws_bytes;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  FindParams fp{p->reg_lambda, p->gamma, p->min_child_weight, p->min_samples_leaf};
-  diag_begin(kDiagFind, s);
-  // the fewest threads whose kFindE bins each cover the bins in one pass
-  const int32_t per_pass = (ft->total_bins + kFindE - 1) / kFindE;
-  const int threads = per_pass <= 256 ? 256 : (per_pass <= 512 ? 512 : 1024);
-  auto kern = threads == 256 ? k_find<256> : (threads == 512 ? k_find<512> : k_find<1024>);
-  hipLaunchKernelGGL(kern, dim3((unsigned)list_cap), dim3(threads), 0, s, hist_g, hist_cnt,
-                     ft->bin_offset, ft->bin_feature, ft->n_bins, ft->total_bins, nodes, list,
-                     list_len, list_cap, fp, scale, splits);
-  diag_end(s);
-  GBDT_LAUNCH_CHECK("k_find");
-  return GBDT_OK;
+  // without the subtraction lists the kernel only reads the histograms
+  return launch_find(const_cast<int64_t*>(hist_g), const_cast<uint32_t*>(hist_cnt), *ft, nodes, list,
+                     list_len, list_cap, *p, scale, splits, nullptr, nullptr, nullptr,
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_node* nodes,
@@ -1688,15 +1679,8 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
                         int32_t list_cap, int64_t rows_bound, void* ws, size_t ws_bytes,
                         void* stream) {
   if (!src || !dst || !nodes || !splits || !list || !list_len) return fail(GBDT_E_ARG, "null argument");
-  int rc = check_matrix(src->X);
+  int rc = check_partition_inputs(*src, *dst);
   if (rc) return rc;
-  rc = check_matrix(dst->X);
-  if (rc) return rc;
-  if (src->X.n_blocks != dst->X.n_blocks || src->X.block_stride != dst->X.block_stride ||
-      src->X.block_features != dst->X.block_features || src->X.row_capacity != dst->X.row_capacity ||
-      src->X.n_rows != dst->X.n_rows)
-    return fail(GBDT_E_SHAPE, "source and destination layouts differ");
-  if (!src->q || !dst->q) return fail(GBDT_E_ARG, "q pointer is null");
   if (list_cap < 0 || rows_bound < 0) return fail(GBDT_E_ARG, "negative capacity");
   if (list_cap == 0) return GBDT_OK;
   const WsLayout L = ws_layout(src->X.n_rows, list_cap, 1);
@@ -1715,16 +1699,7 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
                      kPartTileRows, (int32_t)max_tiles, prefix, tdesc, ctrl, status);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
-  diag_begin(kDiagPartition, s);
-  const int unit = load_unit_for(src->X.block_stride);
-  auto kern = unit == 16 ? k_partition<16> : (unit == 8 ? k_partition<8> : k_partition<4>);
-  hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s,
-                     src->X.bins, src->q, src->rid, dst->X.bins, dst->q, dst->rid,
-                     src->X.row_capacity, src->X.n_blocks, src->X.block_features,
-                     src->X.block_stride, src->X.n_features, splits, tdesc, status, ctrl);
-  diag_end(s);
-  GBDT_LAUNCH_CHECK("k_partition");
-  return GBDT_OK;
+  return launch_partition(*src, *dst, splits, tdesc, status, ctrl, max_tiles, s);
 }
 
 int gbdt_update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* nodes,
