@@ -53,7 +53,25 @@ __device__ __forceinline__ int32_t clamp_len(const int32_t* len, int32_t cap) {
   return n < 0 ? 0 : (n > cap ? cap : n);
 }
 
-constexpr int kPlanLdsEntries = 8192;
+constexpr int kPlanLdsEntries = 8192;  // list entries whose tile prefix is kept in LDS
+constexpr int kPlanStage = 2048;       // list entries whose node data is kept in LDS
+
+// One list entry as the planner needs it (node, its segment, its split).
+struct PlanEntry {
+  int32_t node, begin, count, feature, threshold_bin, n_left;
+};
+
+// LDS of the planner: sh [32], spre [kPlanLdsEntries + 1], stage [kPlanStage].
+struct PlanLds {
+  int32_t sh[32];
+  int32_t spre[kPlanLdsEntries + 1];
+  PlanEntry stage[kPlanStage];
+};
+
+__device__ __forceinline__ int32_t tiles_of(int32_t c, int32_t tile_rows) {
+  if (c < 0) c = 0;
+  return c == 0 ? 1 : (c + tile_rows - 1) / tile_rows;
+}
 
 // Tile plan of the nodes list[0..n), run by every thread of one workgroup:
 // tiles per node (ceil(count / tile_rows), at least one), their exclusive
@@ -61,36 +79,52 @@ constexpr int kPlanLdsEntries = 8192;
 // launch that follows reads its whole assignment with one load), descriptors
 // with node -1 for the launch's tiles [total, max_tiles), and, for a
 // partition plan (status != nullptr), a cleared look-back status array and
-// the ticket and plan total in ctrl.  More tiles than max_tiles sets
-// GBDT_E_SHAPE; the surplus is not planned.  sh: LDS [32];
-// spre: LDS [kPlanLdsEntries + 1].  The list and the nodes' counts must be
-// visible to the workgroup (written before a barrier or a previous launch).
+// the ticket and plan total in ctrl, and (splits != nullptr) each node's
+// split in its tiles' descriptors.  More tiles than max_tiles sets
+// GBDT_E_SHAPE; the surplus is not planned.  Each entry's node (and split)
+// is read once; up to kPlanStage entries are kept in LDS, so writing the
+// descriptors reads no global memory.  The list and the nodes' counts must
+// be visible to the workgroup (written before a barrier or a previous
+// launch).
 __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int32_t* __restrict__ list,
                                   int32_t n, int32_t tile_rows, int32_t max_tiles,
                                   int32_t* __restrict__ prefix, TileDesc* __restrict__ desc,
                                   uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
-                                  int32_t* sh, int32_t* spre) {
+                                  const gbdt_split* __restrict__ splits, PlanLds& L) {
+  const bool staged = n <= kPlanStage;
+  const bool in_lds = n <= kPlanLdsEntries;
   const int32_t per = (n + blockDim.x - 1) / blockDim.x;
   const int32_t j0 = threadIdx.x * per;
   int32_t local = 0;
   for (int32_t j = j0; j < j0 + per && j < n; ++j) {
-    int32_t c = nodes[list[j]].count;
-    if (c < 0) c = 0;
-    local += c == 0 ? 1 : (c + tile_rows - 1) / tile_rows;
+    const int32_t v = list[j];
+    const gbdt_node nd = nodes[v];
+    local += tiles_of(nd.count, tile_rows);
+    if (staged) {
+      PlanEntry pe;
+      pe.node = v;
+      pe.begin = nd.begin;
+      pe.count = nd.count < 0 ? 0 : nd.count;
+      pe.feature = pe.threshold_bin = pe.n_left = 0;
+      if (splits != nullptr) {
+        const gbdt_split sp = splits[v];
+        pe.feature = sp.valid ? sp.feature : -1;
+        pe.threshold_bin = sp.threshold_bin;
+        pe.n_left = sp.n_left;
+      }
+      L.stage[j] = pe;
+    }
   }
   int32_t total;
-  int32_t excl = block_exclusive_scan(local, &total, sh);
-  const bool in_lds = n <= kPlanLdsEntries;
+  int32_t excl = block_exclusive_scan(local, &total, L.sh);
   for (int32_t j = j0; j < j0 + per && j < n; ++j) {
     prefix[j] = excl;
-    if (in_lds) spre[j] = excl;
-    int32_t c = nodes[list[j]].count;
-    if (c < 0) c = 0;
-    excl += c == 0 ? 1 : (c + tile_rows - 1) / tile_rows;
+    if (in_lds) L.spre[j] = excl;
+    excl += tiles_of(staged ? L.stage[j].count : nodes[list[j]].count, tile_rows);
   }
   if (threadIdx.x == 0) {
     prefix[n] = total;
-    if (in_lds) spre[n] = total;
+    if (in_lds) L.spre[n] = total;
     if (total > max_tiles) dev_error(&ctrl->err, GBDT_E_SHAPE);
     if (status != nullptr) {
       ctrl->plan_total = total < max_tiles ? total : max_tiles;
@@ -100,26 +134,43 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
   __syncthreads();
   const int32_t lim = total < max_tiles ? total : max_tiles;
   for (int32_t t = threadIdx.x; t < lim; t += blockDim.x) {
-    const int32_t* pre = in_lds ? spre : prefix;
+    const int32_t* pre = in_lds ? L.spre : prefix;
     int32_t lo = 0, hi = n - 1;
     while (lo < hi) {
       const int32_t mid = (lo + hi + 1) >> 1;
       if (pre[mid] <= t) lo = mid; else hi = mid - 1;
     }
-    const int32_t v = list[lo];
-    const gbdt_node nd = nodes[v];
+    PlanEntry pe;
+    if (staged) {
+      pe = L.stage[lo];
+    } else {
+      const int32_t v = list[lo];
+      const gbdt_node nd = nodes[v];
+      pe.node = v;
+      pe.begin = nd.begin;
+      pe.count = nd.count < 0 ? 0 : nd.count;
+      pe.feature = pe.threshold_bin = pe.n_left = 0;
+      if (splits != nullptr) {
+        const gbdt_split sp = splits[v];
+        pe.feature = sp.valid ? sp.feature : -1;
+        pe.threshold_bin = sp.threshold_bin;
+        pe.n_left = sp.n_left;
+      }
+    }
     const int32_t tf = pre[lo];
-    const int32_t nt = pre[lo + 1] - tf;
-    const int32_t cnt = nd.count < 0 ? 0 : nd.count;
     TileDesc d;
-    d.node = v;
-    d.r0 = nd.begin + (t - tf) * tile_rows;
-    d.r1 = d.r0 + tile_rows < nd.begin + cnt ? d.r0 + tile_rows : nd.begin + cnt;
-    d.ntiles = nt;
+    d.node = pe.node;
+    d.r0 = pe.begin + (t - tf) * tile_rows;
+    d.r1 = d.r0 + tile_rows < pe.begin + pe.count ? d.r0 + tile_rows : pe.begin + pe.count;
+    d.ntiles = pre[lo + 1] - tf;
     d.tfirst = tf;
     d.j = lo;
-    d.begin = nd.begin;
-    d.count = cnt;
+    d.begin = pe.begin;
+    d.count = pe.count;
+    d.feature = pe.feature;
+    d.threshold_bin = pe.threshold_bin;
+    d.n_left = pe.n_left;
+    d.split_valid = splits != nullptr && pe.feature >= 0;
     desc[t] = d;
     if (status != nullptr) status[t] = 0ull;
   }

@@ -98,8 +98,7 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
                                                     double lambda, int32_t* __restrict__ n_nodes_out,
                                                     PlanArgs pa, int32_t tile_rows,
                                                     int32_t max_tiles) {
-  __shared__ int32_t sh[32];
-  __shared__ int32_t spre[kPlanLdsEntries + 1];
+  __shared__ PlanLds lds;
   for (int i = threadIdx.x; i < GBDT_MAX_DEPTH + 2; i += blockDim.x) {
     tc->level_start[i] = 0;
     tc->level_count[i] = 0;
@@ -144,7 +143,7 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
   }
   __syncthreads();
   plan_tiles(nodes, lists + LL.build, grow ? 1 : 0, tile_rows, max_tiles, pa.hprefix, pa.hdesc,
-             nullptr, pa.ctrl, sh, spre);
+             nullptr, pa.ctrl, nullptr, lds);
 }
 
 // Steps 3-6 bookkeeping for level d, one workgroup: each level-d node either
@@ -161,8 +160,8 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t* __restrict__ n_nodes_out, PlanArgs pa,
                                                 int32_t part_max_tiles, int32_t hist_tile_rows_next,
                                                 int32_t hist_max_tiles_next) {
-  __shared__ int32_t sh[32];
-  __shared__ int32_t spre[kPlanLdsEntries + 1];
+  __shared__ PlanLds lds;
+  int32_t* sh = lds.sh;
   const int32_t first = tc->level_start[d];
   const int32_t cnt = tc->level_count[d];
   const int32_t S = tc->scale;
@@ -291,9 +290,9 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   // this level's partition plan (splitting nodes) and the next level's
   // histogram plan (nodes to build)
   plan_tiles(nodes, split_list, t_split, kPartTileRows, part_max_tiles, pa.prefix, pa.desc, pa.status,
-             pa.ctrl, sh, spre);
+             pa.ctrl, splits, lds);
   plan_tiles(nodes, build_n, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix, pa.hdesc,
-             nullptr, pa.ctrl, sh, spre);
+             nullptr, pa.ctrl, nullptr, lds);
 }
 
 static int64_t min_split_count(const gbdt_params* p, int64_t n) {
@@ -428,7 +427,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     // the rows of the last level's children are never read again: the
     // prediction update routes rows through the finished tree instead
     if (d + 1 < D) {
-      rc = launch_partition(src, dst, b->splits, pa.desc, pa.status, pa.ctrl, p_tiles[d], s);
+      rc = launch_partition(src, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], s);
       if (rc) return rc;
       src = dst;
     }

@@ -27,7 +27,8 @@ constexpr int kHistTargetTiles = 1024;
 constexpr int kLdsHistBudgetBins = 7680;  // histogram bins per feature block (60 KiB of LDS)
 constexpr int kLdsHistSlack = 256;         // extra LDS slots: any bin byte stays inside the allocation
 
-// Work assignment of one tile (written by the planner).
+// Work assignment of one tile (written by the planner).  A partition plan
+// also carries the node's split, so a partition tile needs no second load.
 struct TileDesc {
   int32_t node;    // node id
   int32_t r0, r1;  // rows [r0, r1) of the tile
@@ -36,8 +37,12 @@ struct TileDesc {
   int32_t j;       // list position of the node
   int32_t begin;   // the node's segment
   int32_t count;
+  int32_t feature;        // partition plans: the node's split
+  int32_t threshold_bin;
+  int32_t n_left;
+  int32_t split_valid;
 };
-static_assert(sizeof(TileDesc) == 32, "tile descriptor is 32 bytes");
+static_assert(sizeof(TileDesc) == 48, "tile descriptor is 48 bytes");
 
 // Two tile plans live in the workspace at once: the partition plan
 // (tdesc, prefix, status, ctrl->ticket / plan_total) and the histogram plan
@@ -96,9 +101,8 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
                 const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
                 const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
                 const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s);
-int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const gbdt_split* splits,
-                     const TileDesc* desc, uint64_t* status, WsCtrl* ctrl, int64_t max_tiles,
-                     hipStream_t s);
+int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
+                     uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, hipStream_t s);
 
 // Per-kernel device timing (the backend's diagnostics): when enabled, every
 // launch of the library is bracketed by two hipEvents on its stream.

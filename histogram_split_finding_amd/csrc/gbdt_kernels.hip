@@ -150,13 +150,13 @@ __global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nod
                                                int32_t max_tiles, int32_t* __restrict__ prefix,
                                                TileDesc* __restrict__ desc,
                                                WsCtrl* __restrict__ ctrl,
-                                               uint64_t* __restrict__ status) {
-  __shared__ int32_t sh[32];
-  __shared__ int32_t spre[kPlanLdsEntries + 1];
+                                               uint64_t* __restrict__ status,
+                                               const gbdt_split* __restrict__ splits) {
+  __shared__ PlanLds lds;
   const int32_t raw = *list_len;
   if (threadIdx.x == 0 && (raw < 0 || raw > list_cap)) dev_error(&ctrl->err, GBDT_E_SHAPE);
   const int32_t n = clamp_len(list_len, list_cap);
-  plan_tiles(nodes, list, n, tile_rows, max_tiles, prefix, desc, status, ctrl, sh, spre);
+  plan_tiles(nodes, list, n, tile_rows, max_tiles, prefix, desc, status, ctrl, splits, lds);
 }
 
 // -------------------------------------------------------------- gradients --
@@ -683,14 +683,6 @@ __global__ void __launch_bounds__(THREADS) k_find(
         bad |= cs > cp;
         fo[e] = bin_offset[inb ? f[e + 1] : 0];
       }
-#pragma unroll
-      for (int e = 0; e < kFindE; ++e) {
-        const int32_t b = b0 + e;
-        if (b < total_bins) {
-          hg[b] = g[e];
-          hc[b] = (uint32_t)c[e];
-        }
-      }
     } else {
 #pragma unroll
       for (int e = 0; e < kFindE; ++e) {
@@ -790,6 +782,20 @@ __global__ void __launch_bounds__(THREADS) k_find(
           best_nl = nlc;
           best_f = f[e + 1];
           best_thr = b - fo[e];
+        }
+      }
+    }
+    if (derive) {
+      // the derived histogram, for the next level: each bin's value is its
+      // in-thread running sum minus the previous bin's (or itself at a head).
+      // Stored last, so no wait above covers these writes.
+#pragma unroll
+      for (int e = 0; e < kFindE; ++e) {
+        const int32_t b = b0 + e;
+        if (b < total_bins) {
+          const bool head = e == 0 || f[e] != f[e + 1];
+          hg[b] = head ? g[e] : g[e] - g[e - 1 < 0 ? 0 : e - 1];
+          hc[b] = (uint32_t)(head ? c[e] : c[e] - c[e - 1 < 0 ? 0 : e - 1]);
         }
       }
     }
@@ -894,13 +900,19 @@ __device__ int64_t lookback_excl(uint64_t* status, int32_t tile, int32_t tfirst,
   }
 }
 
+// One workgroup per tile of a splitting node, taken in ticket order.  The
+// tile descriptor carries the node's split, so right after it arrives the
+// workgroup issues the loads of its rows' split-feature bytes and q; then it
+// publishes its left count, looks back for the exclusive prefix, scatters q
+// (and row ids) and copies the bins in batches of BATCH rows per lane
+// (lanes = (row group, column of UNIT bytes)).
 template <int UNIT>
 __global__ void __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const int64_t* __restrict__ sq,
     const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, int64_t* __restrict__ dq,
     int32_t* __restrict__ drid, int64_t row_capacity, int32_t n_blocks, int32_t block_features,
-    int32_t block_stride, int32_t n_features, const gbdt_split* __restrict__ splits,
-    const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl) {
+    int32_t block_stride, int32_t n_features, const TileDesc* __restrict__ desc,
+    uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl) {
   constexpr int BATCH = 32 / UNIT;
   __shared__ int32_t s_tile;
   __shared__ int32_t s_cnt[kPartRowsPerThread][kPartWaves];
@@ -915,32 +927,45 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
   const int32_t total = ctrl->plan_total;
   if (tile >= total) return;
   const TileDesc td = desc[tile];
-  const int32_t v = td.node;
-  const gbdt_split sp = splits[v];
   const int32_t tfirst = td.tfirst;
   const int32_t tlast = td.tfirst + td.ntiles - 1;
   const int32_t tin = tile - tfirst;
   const int64_t r0 = td.r0;
-  const int64_t r1 = td.r1;
-  struct {
-    int32_t begin, count;
-  } nd = {td.begin, td.count};
+  const int64_t span = int64_t(td.r1) - td.r0;
+  const int32_t rows_all = (int32_t)(span < 0 ? 0 : (span > kPartTileRows ? kPartTileRows : span));
   // a listed node must carry a valid split; otherwise nothing is moved, the
   // tile still publishes (so later tiles never wait on it) and the error word
   // is set
-  const bool split_ok = sp.valid && sp.feature >= 0 && sp.feature < n_features;
-  const int32_t rows = split_ok ? (int32_t)(r1 - r0 > 0 ? r1 - r0 : 0) : 0;
+  const bool split_ok = td.split_valid && td.feature >= 0 && td.feature < n_features;
+  const int32_t rows = split_ok ? rows_all : 0;
+  const int32_t fblk = split_ok ? td.feature / block_features : 0;
+  const int32_t fcol = split_ok ? td.feature % block_features : 0;
+  const uint8_t* __restrict__ fcolp = sbins + int64_t(fblk) * row_capacity * block_stride + fcol;
+  // loads that need only the descriptor: split-feature bytes, q, row ids
+  int32_t fb[kPartRowsPerThread];
+  int64_t qv[kPartRowsPerThread];
+  int32_t rv[kPartRowsPerThread];
+#pragma unroll
+  for (int k = 0; k < kPartRowsPerThread; ++k) {
+    const int32_t i = k * kPartThreads + threadIdx.x;
+    const bool ok = i < rows;
+    const int64_t s = r0 + i;
+    fb[k] = ok ? (int32_t)fcolp[s * block_stride] : 0;
+    qv[k] = ok ? sq[s] : 0;
+    rv[k] = (ok && drid != nullptr) ? (srid != nullptr ? srid[s] : (int32_t)s) : 0;
+  }
+  const int32_t lpr = block_stride / UNIT;
+  const int32_t rpi = kPartThreads / lpr;
+  const int32_t col = threadIdx.x % lpr;
+  const int32_t rg = threadIdx.x / lpr;
   if (!split_ok && threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
 
-  const int32_t fblk = split_ok ? sp.feature / block_features : 0;
-  const int32_t fcol = split_ok ? sp.feature % block_features : 0;
-  const uint8_t* __restrict__ fcolp = sbins + int64_t(fblk) * row_capacity * block_stride + fcol;
   bool left[kPartRowsPerThread];
   uint64_t bal[kPartRowsPerThread];
 #pragma unroll
   for (int k = 0; k < kPartRowsPerThread; ++k) {
     const int32_t i = k * kPartThreads + threadIdx.x;
-    left[k] = (i < rows) && ((int32_t)fcolp[(r0 + i) * block_stride] <= sp.threshold_bin);
+    left[k] = (i < rows) && (fb[k] <= td.threshold_bin);
     bal[k] = __ballot(left[k]);
     if (lane == 0) s_cnt[k][wid] = __popcll(bal[k]);
   }
@@ -966,60 +991,38 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
       if (!ok) dev_error(&ctrl->err, GBDT_E_INTERNAL);
       if (tin > 0) st_publish(&status[tile], kStInc | (uint64_t)(uint32_t)(excl + s_acc));
       s_excl = (int32_t)excl;
-      if (tile == tlast && excl + s_acc != sp.n_left) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+      if (tile == tlast && excl + s_acc != td.n_left) dev_error(&ctrl->err, GBDT_E_INTERNAL);
     }
   }
   __syncthreads();
   const int32_t excl = s_excl;
-  const int64_t lbase = int64_t(nd.begin) + excl;
-  const int64_t rbase = int64_t(nd.begin) + sp.n_left + (int64_t(tin) * kPartTileRows - excl);
+  const int64_t lbase = int64_t(td.begin) + excl;
+  const int64_t rbase = int64_t(td.begin) + td.n_left + (int64_t(tin) * kPartTileRows - excl);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t seg_end = int64_t(nd.begin) + nd.count;
+  const int64_t seg_end = int64_t(td.begin) + td.count;
   bool bad_pos = false;
-  int32_t dpos[kPartRowsPerThread];
 #pragma unroll
   for (int k = 0; k < kPartRowsPerThread; ++k) {
     const int32_t i = k * kPartThreads + threadIdx.x;
-    dpos[k] = -1;
     if (i < rows) {
       const int32_t rl = s_cnt[k][wid] + __popcll(bal[k] & lt_mask);
       const int64_t d = left[k] ? lbase + rl : rbase + (i - rl);
       // a split record whose left count disagrees with the rows could send a
       // row outside its node's segment: such a row is not written
-      const bool in_seg = d >= nd.begin && d < seg_end;
+      const bool in_seg = d >= td.begin && d < seg_end;
       bad_pos |= !in_seg;
-      dpos[k] = in_seg ? (int32_t)d : -1;
-      s_dpos[i] = dpos[k];
-    }
-  }
-  if (bad_pos) dev_error(&ctrl->err, GBDT_E_INTERNAL);
-  // q and row id of the lane's own rows
-  {
-    int64_t qv[kPartRowsPerThread];
-    int32_t rv[kPartRowsPerThread];
-#pragma unroll
-    for (int k = 0; k < kPartRowsPerThread; ++k) {
-      const int32_t i = k * kPartThreads + threadIdx.x;
-      const int64_t s = r0 + i;
-      const bool ok = i < rows;
-      qv[k] = ok ? sq[s] : 0;
-      rv[k] = (ok && drid != nullptr) ? (srid != nullptr ? srid[s] : (int32_t)s) : 0;
-    }
-#pragma unroll
-    for (int k = 0; k < kPartRowsPerThread; ++k) {
-      if (dpos[k] >= 0) {
-        dq[dpos[k]] = qv[k];
-        if (drid != nullptr) drid[dpos[k]] = rv[k];
+      const int32_t dd = in_seg ? (int32_t)d : -1;
+      s_dpos[i] = dd;
+      if (dd >= 0) {
+        dq[dd] = qv[k];
+        if (drid != nullptr) drid[dd] = rv[k];
       }
     }
   }
+  if (bad_pos) dev_error(&ctrl->err, GBDT_E_INTERNAL);
   __syncthreads();
-  // bins: (row group, column of UNIT bytes) lanes, every block, BATCH rows of
-  // loads in flight per lane
-  const int32_t lpr = block_stride / UNIT;
-  const int32_t rpi = kPartThreads / lpr;
-  const int32_t col = threadIdx.x % lpr;
-  const int32_t rg = threadIdx.x / lpr;
+  // bins: (row group, column of UNIT bytes) lanes, every block, BATCH rows
+  // of loads in flight per lane
   if (rg < rpi) {
     for (int32_t b = 0; b < n_blocks; ++b) {
       const uint8_t* __restrict__ sb = sbins + int64_t(b) * row_capacity * block_stride + UNIT * col;
@@ -1394,16 +1397,15 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
   return GBDT_OK;
 }
 
-int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const gbdt_split* splits,
-                     const TileDesc* desc, uint64_t* status, WsCtrl* ctrl, int64_t max_tiles,
-                     hipStream_t s) {
+int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
+                     uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, hipStream_t s) {
   const int unit = load_unit_for(src.X.block_stride);
   auto kern = unit == 16 ? k_partition<16> : (unit == 8 ? k_partition<8> : k_partition<4>);
   diag_begin(kDiagPartition, s);
   hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s, src.X.bins, src.q,
                      src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
-                     src.X.block_features, src.X.block_stride, src.X.n_features, splits, desc,
-                     status, ctrl);
+                     src.X.block_features, src.X.block_stride, src.X.n_features, desc, status,
+                     ctrl);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_partition");
   return GBDT_OK;
@@ -1624,7 +1626,8 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   if (max_tiles > L.hpart_tiles) return fail(GBDT_E_SHAPE, "too many histogram tiles for the workspace");
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap, T,
-                     (int32_t)max_tiles, hprefix, hdesc, ctrl, (uint64_t*)nullptr);
+                     (int32_t)max_tiles, hprefix, hdesc, ctrl, (uint64_t*)nullptr,
+                     (const gbdt_split*)nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
   rc = launch_hist(*src, *ft, hdesc, max_tiles, hist_g, hist_cnt, hpart, ctrl, s);
@@ -1696,10 +1699,10 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
   uint64_t* status = reinterpret_cast<uint64_t*>(w + L.status);
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap,
-                     kPartTileRows, (int32_t)max_tiles, prefix, tdesc, ctrl, status);
+                     kPartTileRows, (int32_t)max_tiles, prefix, tdesc, ctrl, status, splits);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
-  return launch_partition(*src, *dst, splits, tdesc, status, ctrl, max_tiles, s);
+  return launch_partition(*src, *dst, tdesc, status, ctrl, max_tiles, s);
 }
 
 int gbdt_update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* nodes,
