@@ -64,6 +64,7 @@ struct PlanEntry {
 // LDS of the planner: sh [32], spre [kPlanLdsEntries + 1], stage [kPlanStage].
 struct PlanLds {
   int32_t sh[32];
+  int32_t n_multi;
   int32_t spre[kPlanLdsEntries + 1];
   PlanEntry stage[kPlanStage];
 };
@@ -80,7 +81,9 @@ __device__ __forceinline__ int32_t tiles_of(int32_t c, int32_t tile_rows) {
 // with node -1 for the launch's tiles [total, max_tiles), and, for a
 // partition plan (status != nullptr), a cleared look-back status array and
 // the ticket and plan total in ctrl, and (splits != nullptr) each node's
-// split in its tiles' descriptors.  More tiles than max_tiles sets
+// split in its tiles' descriptors, and (multi != nullptr) the list positions
+// of the nodes with more than one tile (multi[0] = their count, in no
+// particular order; for the partial reduction).  More tiles than max_tiles sets
 // GBDT_E_SHAPE; the surplus is not planned.  Each entry's node (and split)
 // is read once; up to kPlanStage entries are kept in LDS, so writing the
 // descriptors reads no global memory.  The list and the nodes' counts must
@@ -90,7 +93,8 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
                                   int32_t n, int32_t tile_rows, int32_t max_tiles,
                                   int32_t* __restrict__ prefix, TileDesc* __restrict__ desc,
                                   uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
-                                  const gbdt_split* __restrict__ splits, PlanLds& L) {
+                                  const gbdt_split* __restrict__ splits,
+                                  int32_t* __restrict__ multi, PlanLds& L) {
   const bool staged = n <= kPlanStage;
   const bool in_lds = n <= kPlanLdsEntries;
   const int32_t per = (n + blockDim.x - 1) / blockDim.x;
@@ -115,14 +119,19 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
       L.stage[j] = pe;
     }
   }
+  if (threadIdx.x == 0) L.n_multi = 0;
   int32_t total;
   int32_t excl = block_exclusive_scan(local, &total, L.sh);
   for (int32_t j = j0; j < j0 + per && j < n; ++j) {
     prefix[j] = excl;
     if (in_lds) L.spre[j] = excl;
-    excl += tiles_of(staged ? L.stage[j].count : nodes[list[j]].count, tile_rows);
+    const int32_t nt = tiles_of(staged ? L.stage[j].count : nodes[list[j]].count, tile_rows);
+    if (multi != nullptr && nt > 1) multi[1 + atomicAdd(&L.n_multi, 1)] = j;
+    excl += nt;
   }
+  __syncthreads();
   if (threadIdx.x == 0) {
+    if (multi != nullptr) multi[0] = L.n_multi;
     prefix[n] = total;
     if (in_lds) L.spre[n] = total;
     if (total > max_tiles) dev_error(&ctrl->err, GBDT_E_SHAPE);

@@ -68,6 +68,7 @@ struct PlanArgs {
   TileDesc* desc;
   uint64_t* status;
   int32_t* hprefix;  // histogram plan
+  int32_t* hmulti;
   TileDesc* hdesc;
   WsCtrl* ctrl;
 };
@@ -143,7 +144,7 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
   }
   __syncthreads();
   plan_tiles(nodes, lists + LL.build, grow ? 1 : 0, tile_rows, max_tiles, pa.hprefix, pa.hdesc,
-             nullptr, pa.ctrl, nullptr, lds);
+             nullptr, pa.ctrl, nullptr, pa.hmulti, lds);
 }
 
 // Steps 3-6 bookkeeping for level d, one workgroup: each level-d node either
@@ -290,9 +291,9 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   // this level's partition plan (splitting nodes) and the next level's
   // histogram plan (nodes to build)
   plan_tiles(nodes, split_list, t_split, kPartTileRows, part_max_tiles, pa.prefix, pa.desc, pa.status,
-             pa.ctrl, splits, lds);
+             pa.ctrl, splits, nullptr, lds);
   plan_tiles(nodes, build_n, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix, pa.hdesc,
-             nullptr, pa.ctrl, nullptr, lds);
+             nullptr, pa.ctrl, nullptr, pa.hmulti, lds);
 }
 
 static int64_t min_split_count(const gbdt_params* p, int64_t n) {
@@ -371,6 +372,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   pa.desc = reinterpret_cast<TileDesc*>(w + WL.tdesc);
   pa.status = reinterpret_cast<uint64_t*>(w + WL.status);
   pa.hprefix = reinterpret_cast<int32_t*>(w + WL.hprefix);
+  pa.hmulti = reinterpret_cast<int32_t*>(w + WL.hmulti);
   pa.hdesc = reinterpret_cast<TileDesc*>(w + WL.hdesc);
   uint64_t* hpart = reinterpret_cast<uint64_t*>(w + WL.hpart);
   // per level: histogram tile rows and launch bounds (level d builds at most
@@ -408,7 +410,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
     rc = launch_hist(src, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s);
     if (rc) return rc;
-    rc = launch_hist_reduce(b->lists + LL.build + lvl_off, &tc->n_build[d], cap_build, pa.hprefix,
+    rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
                             h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s);
     if (rc) return rc;
     rc = launch_find(b->hist_g, b->hist_cnt, *ft, nodes_out, b->lists + LL.find + lvl_off,

@@ -24,6 +24,7 @@ constexpr int kGradBlocks = 1024;     // grid of the gradient kernels
 constexpr int kPartTileRows = 2048;   // rows per partition tile
 constexpr int kHistMinTileRows = 1024;
 constexpr int kHistTargetTiles = 1024;
+constexpr int kReduceNodeSlots = 64;  // y extent of the partial-reduction grid
 constexpr int kLdsHistBudgetBins = 7680;  // histogram bins per feature block (60 KiB of LDS)
 constexpr int kLdsHistSlack = 256;         // extra LDS slots: any bin byte stays inside the allocation
 
@@ -55,6 +56,7 @@ struct WsLayout {
   size_t gpart;       // double[kGradBlocks]
   size_t prefix;      // int32[max_list + 2]: partition plan
   size_t hprefix;     // int32[max_list + 2]: histogram plan
+  size_t hmulti;      // int32[max_list + 2]: histogram plan, nodes of several tiles
   size_t status;      // uint64[status_cap]
   size_t hpart;       // uint64[hpart_tiles * total_bins]
   size_t total;
@@ -94,7 +96,7 @@ int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
                 WsCtrl* ctrl, hipStream_t s);
-int launch_hist_reduce(const int32_t* list, const int32_t* list_len, int32_t list_cap,
+int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_cap,
                        const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
                        const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s);
 int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,

@@ -91,6 +91,8 @@ WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
   off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
   L.hprefix = off;
   off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
+  L.hmulti = off;
+  off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
   L.status = off;
   off = align256(off + sizeof(uint64_t) * size_t(L.status_cap));
   L.hpart = off;
@@ -151,12 +153,13 @@ __global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nod
                                                TileDesc* __restrict__ desc,
                                                WsCtrl* __restrict__ ctrl,
                                                uint64_t* __restrict__ status,
-                                               const gbdt_split* __restrict__ splits) {
+                                               const gbdt_split* __restrict__ splits,
+                                               int32_t* __restrict__ multi) {
   __shared__ PlanLds lds;
   const int32_t raw = *list_len;
   if (threadIdx.x == 0 && (raw < 0 || raw > list_cap)) dev_error(&ctrl->err, GBDT_E_SHAPE);
   const int32_t n = clamp_len(list_len, list_cap);
-  plan_tiles(nodes, list, n, tile_rows, max_tiles, prefix, desc, status, ctrl, splits, lds);
+  plan_tiles(nodes, list, n, tile_rows, max_tiles, prefix, desc, status, ctrl, splits, multi, lds);
 }
 
 // -------------------------------------------------------------- gradients --
@@ -447,12 +450,13 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(
   }
 }
 
-// Sums the packed partials of every multi-tile node.  A workgroup owns 64
-// bins of one node; its 16 waves take the node's tiles round-robin (loads
-// batched four deep) and combine through LDS.  The sums are exact integers,
-// so any order gives the same bits.
+// Sums the packed partials of every multi-tile node.  The planner lists those
+// nodes (multi[0] = count, multi[1..] = list positions); workgroups stride
+// over them along y.  A workgroup owns 64 bins of one node; its 16 waves take
+// the node's tiles round-robin (loads batched four deep) and combine through
+// LDS.  The sums are exact integers, so any order gives the same bits.
 __global__ void __launch_bounds__(1024) k_hist_reduce(const int32_t* __restrict__ list,
-                                                     const int32_t* __restrict__ list_len,
+                                                     const int32_t* __restrict__ multi,
                                                      int32_t list_cap,
                                                      const int32_t* __restrict__ prefix,
                                                      int32_t max_tiles, int32_t bits,
@@ -462,47 +466,49 @@ __global__ void __launch_bounds__(1024) k_hist_reduce(const int32_t* __restrict_
                                                      uint32_t* __restrict__ hist_cnt) {
   __shared__ int64_t sg[16][64];
   __shared__ uint64_t sc[16][64];
-  const int32_t n = clamp_len(list_len, list_cap);
-  const int32_t j = blockIdx.y;
-  if (j >= n) return;
-  const int32_t t0 = prefix[j];
-  int32_t t1 = prefix[j + 1];
-  if (t1 > max_tiles) t1 = max_tiles;  // an over-full plan is already flagged
-  if (t1 - t0 <= 1) return;
+  const int32_t nm = clamp_len(multi, list_cap);
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int32_t b = blockIdx.x * 64 + lane;
   const bool inb = b < total_bins;
   const uint64_t mask = (1ull << bits) - 1ull;
-  int64_t g = 0;
-  uint64_t c = 0;
-  for (int32_t t = t0 + wid; t < t1; t += 16 * 4) {
-    uint64_t x[4];
+  for (int32_t m = blockIdx.y; m < nm; m += gridDim.y) {
+    int32_t j = multi[1 + m];
+    j = j < 0 ? 0 : (j >= list_cap ? list_cap - 1 : j);
+    const int32_t t0 = prefix[j];
+    int32_t t1 = prefix[j + 1];
+    if (t1 > max_tiles) t1 = max_tiles;  // an over-full plan is already flagged
+    int64_t g = 0;
+    uint64_t c = 0;
+    for (int32_t t = t0 + wid; t < t1; t += 16 * 4) {
+      uint64_t x[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int32_t tt = t + 16 * u;
-      x[u] = (inb && tt < t1) ? partial[int64_t(tt) * total_bins + b] : 0ull;
-    }
+      for (int u = 0; u < 4; ++u) {
+        const int32_t tt = t + 16 * u;
+        x[u] = (inb && tt < t1) ? partial[int64_t(tt) * total_bins + b] : 0ull;
+      }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint64_t cc = x[u] & mask;
-      g += (int64_t)(x[u] - cc) >> bits;
-      c += cc;
+      for (int u = 0; u < 4; ++u) {
+        const uint64_t cc = x[u] & mask;
+        g += (int64_t)(x[u] - cc) >> bits;
+        c += cc;
+      }
     }
-  }
-  sg[wid][lane] = g;
-  sc[wid][lane] = c;
-  __syncthreads();
-  if (wid == 0 && inb) {
-    int64_t gg = 0;
-    uint64_t ccs = 0;
-    for (int w = 0; w < 16; ++w) {
-      gg += sg[w][lane];
-      ccs += sc[w][lane];
+    sg[wid][lane] = g;
+    sc[wid][lane] = c;
+    __syncthreads();
+    if (wid == 0 && inb) {
+      int64_t gg = 0;
+      uint64_t ccs = 0;
+      for (int w = 0; w < 16; ++w) {
+        gg += sg[w][lane];
+        ccs += sc[w][lane];
+      }
+      const int32_t v = list[j];
+      hist_g[int64_t(v) * total_bins + b] = gg;
+      hist_cnt[int64_t(v) * total_bins + b] = (uint32_t)ccs;
     }
-    const int32_t v = list[j];
-    hist_g[int64_t(v) * total_bins + b] = gg;
-    hist_cnt[int64_t(v) * total_bins + b] = (uint32_t)ccs;
+    __syncthreads();
   }
 }
 
@@ -1365,13 +1371,18 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
   return GBDT_OK;
 }
 
-int launch_hist_reduce(const int32_t* list, const int32_t* list_len, int32_t list_cap,
+int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_cap,
                        const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
                        const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s) {
   const int32_t bits = pack_bits_for(n_rows > 0 ? n_rows : 1);
+  // multi-tile nodes hold more than one tile of rows each, so there are at
+  // most max_tiles / 2 of them; the y stride covers the rest
+  int64_t gy = max_tiles / 2 < list_cap ? max_tiles / 2 : list_cap;
+  if (gy > kReduceNodeSlots) gy = kReduceNodeSlots;
+  if (gy < 1) gy = 1;
   diag_begin(kDiagHistReduce, s);
-  hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)((total_bins + 63) / 64), (unsigned)list_cap),
-                     dim3(1024), 0, s, list, list_len, list_cap, prefix, (int32_t)max_tiles, bits,
+  hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)((total_bins + 63) / 64), (unsigned)gy),
+                     dim3(1024), 0, s, list, multi, list_cap, prefix, (int32_t)max_tiles, bits,
                      total_bins, hpart, hist_g, hist_cnt);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist_reduce");
@@ -1619,6 +1630,7 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   char* w = static_cast<char*>(ws);
   WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
   int32_t* hprefix = reinterpret_cast<int32_t*>(w + L.hprefix);
+  int32_t* hmulti = reinterpret_cast<int32_t*>(w + L.hmulti);
   TileDesc* hdesc = reinterpret_cast<TileDesc*>(w + L.hdesc);
   uint64_t* hpart = reinterpret_cast<uint64_t*>(w + L.hpart);
   const int32_t T = hist_tile_rows(rows_bound, src->X.n_rows);
@@ -1627,12 +1639,12 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap, T,
                      (int32_t)max_tiles, hprefix, hdesc, ctrl, (uint64_t*)nullptr,
-                     (const gbdt_split*)nullptr);
+                     (const gbdt_split*)nullptr, hmulti);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
   rc = launch_hist(*src, *ft, hdesc, max_tiles, hist_g, hist_cnt, hpart, ctrl, s);
   if (rc) return rc;
-  return launch_hist_reduce(list, list_len, list_cap, hprefix, max_tiles, src->X.n_rows,
+  return launch_hist_reduce(list, hmulti, list_cap, hprefix, max_tiles, src->X.n_rows,
                             ft->total_bins, hpart, hist_g, hist_cnt, s);
 }
 
@@ -1699,7 +1711,8 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
   uint64_t* status = reinterpret_cast<uint64_t*>(w + L.status);
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap,
-                     kPartTileRows, (int32_t)max_tiles, prefix, tdesc, ctrl, status, splits);
+                     kPartTileRows, (int32_t)max_tiles, prefix, tdesc, ctrl, status, splits,
+                     (int32_t*)nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
   return launch_partition(*src, *dst, tdesc, status, ctrl, max_tiles, s);
