@@ -53,7 +53,9 @@ i64 = ctypes.c_int64
 
 class Matrix(ctypes.Structure):
     _fields_ = [("bins", vp), ("n_rows", i64), ("row_capacity", i64), ("n_features", i32),
-                ("n_blocks", i32), ("block_features", i32), ("block_stride", i32)]
+                ("n_blocks", i32), ("block_features", i32), ("block_stride", i32),
+                ("n_bit_features", i32), ("bit_stride", i32), ("col_feature", vp),
+                ("feature_col", vp)]
 
 
 class Features(ctypes.Structure):
@@ -100,6 +102,7 @@ def load():
         "gbdt_validate_params": (ctypes.c_int, [P(Params)]),
         "gbdt_workspace_bytes": (ctypes.c_size_t, [i64, i32, i32]),
         "gbdt_choose_blocking": (ctypes.c_int, [i32, vp, P(Matrix), P(i32)]),
+        "gbdt_choose_layout": (ctypes.c_int, [i32, vp, i32, P(Matrix), P(i32), vp, vp]),
         "gbdt_pack_matrix": (ctypes.c_int, [vp, P(Matrix), P(Features), vp, ctypes.c_size_t, vp]),
         "gbdt_read_error": (ctypes.c_int, [vp, vp]),
         "gbdt_compute_gradients": (ctypes.c_int, [vp, vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]),
@@ -182,6 +185,21 @@ def gbdt_choose_blocking(n_bins):
     return X, int(mbb.value)
 
 
+def gbdt_choose_layout(n_bins, pack_bits=True):
+    """(Matrix layout fields, max_block_bins, col_feature, feature_col) for the
+    features' bin counts; with pack_bits, features of at most 2 bins are bits."""
+    nb = np.ascontiguousarray(np.asarray(n_bins, dtype=np.int32))
+    X = Matrix()
+    mbb = i32()
+    cf = np.zeros(nb.shape[0], dtype=np.int32)
+    fc = np.zeros(nb.shape[0], dtype=np.int32)
+    rc = load().gbdt_choose_layout(nb.shape[0], nb.ctypes.data_as(vp), int(bool(pack_bits)),
+                                   ctypes.byref(X), ctypes.byref(mbb), cf.ctypes.data_as(vp),
+                                   fc.ctypes.data_as(vp))
+    _check(rc, "gbdt_choose_layout")
+    return X, int(mbb.value), cf, fc
+
+
 def gbdt_grow_sizes(n_rows: int, total_bins: int, max_depth: int) -> GrowSizes:
     out = GrowSizes()
     _check(load().gbdt_grow_sizes(n_rows, total_bins, max_depth, ctypes.byref(out)), "gbdt_grow_sizes")
@@ -199,9 +217,11 @@ def new_workspace(nbytes: int, device="cuda"):
 
 
 class FeatureTable:
-    """Device feature table (n_bins, bin_offset, bin_feature, skip_bin)."""
+    """Device feature table (n_bins, bin_offset, bin_feature, skip_bin) and the
+    matrix layout chosen for it (with pack_bits, features of at most 2 bins
+    are stored as bits; the column maps live on the device)."""
 
-    def __init__(self, n_bins, device="cuda"):
+    def __init__(self, n_bins, device="cuda", pack_bits=True):
         import torch
         nb = np.ascontiguousarray(np.asarray(n_bins, dtype=np.int32))
         self.n_bins_host = nb
@@ -211,7 +231,11 @@ class FeatureTable:
         self.bin_offset_host = off
         self.total_bins = int(off[-1])
         bf = np.repeat(np.arange(self.n_features, dtype=np.int32), nb)
-        self.layout, self.max_block_bins = gbdt_choose_blocking(nb)
+        self.layout, self.max_block_bins, cf, fc = gbdt_choose_layout(nb, pack_bits)
+        self.col_feature_host, self.feature_col_host = cf, fc
+        self.mapped = bool(pack_bits)
+        self.col_feature = torch.from_numpy(cf).to(device) if self.mapped else None
+        self.feature_col = torch.from_numpy(fc).to(device) if self.mapped else None
         self.n_bins = torch.from_numpy(nb).to(device)
         self.bin_offset = torch.from_numpy(off).to(device)
         self.bin_feature = torch.from_numpy(bf).to(device)
@@ -229,29 +253,45 @@ class RowBuffer:
     def __init__(self, ft: FeatureTable, n_rows: int, device="cuda", with_rid=True):
         import torch
         L = ft.layout
+        self.ft = ft
         self.n_rows = int(n_rows)
         self.row_capacity = max(self.n_rows, 1)
         self.n_blocks, self.block_features, self.block_stride = L.n_blocks, L.block_features, L.block_stride
+        self.n_bit_features, self.bit_stride = L.n_bit_features, L.bit_stride
         self.n_features = ft.n_features
-        self.bins = torch.zeros(self.n_blocks * self.row_capacity * self.block_stride,
+        self.byte_bytes = self.n_blocks * self.row_capacity * self.block_stride
+        self.bins = torch.zeros(self.byte_bytes + self.row_capacity * self.bit_stride,
                                 dtype=torch.uint8, device=device)
         self.q = torch.zeros(self.row_capacity, dtype=torch.int64, device=device)
         self.rid = torch.zeros(self.row_capacity, dtype=torch.int32, device=device) if with_rid else None
 
     def matrix(self) -> Matrix:
         return Matrix(_ptr(self.bins), self.n_rows, self.row_capacity, self.n_features,
-                      self.n_blocks, self.block_features, self.block_stride)
+                      self.n_blocks, self.block_features, self.block_stride, self.n_bit_features,
+                      self.bit_stride, _ptr(self.ft.col_feature), _ptr(self.ft.feature_col))
 
     def rows(self, identity_rid=False) -> Rows:
         return Rows(self.matrix(), _ptr(self.q), None if (identity_rid or self.rid is None) else _ptr(self.rid))
 
     def blocked_to_rowmajor(self):
         """Bins back in row-major [n, F] order (for tests)."""
-        b = self.bins.view(self.n_blocks, self.row_capacity, self.block_stride)[:, : self.n_rows]
-        cols = [b[k, :, : min(self.block_features, self.n_features - k * self.block_features)]
-                for k in range(self.n_blocks)]
         import torch
-        return torch.cat(cols, dim=1)
+        n, F = self.n_rows, self.n_features
+        out = torch.zeros((n, F), dtype=torch.uint8, device=self.bins.device)
+        nbc = F - self.n_bit_features
+        cf = torch.from_numpy(self.ft.col_feature_host).long().to(self.bins.device)
+        if self.n_blocks > 0:
+            b = self.bins[: self.byte_bytes].view(self.n_blocks, self.row_capacity, self.block_stride)[:, :n]
+            cols = [b[k, :, : min(self.block_features, nbc - k * self.block_features)]
+                    for k in range(self.n_blocks)]
+            out[:, cf[:nbc]] = torch.cat(cols, dim=1)
+        if self.n_bit_features > 0:
+            nw = self.bit_stride // 4
+            w = self.bins[self.byte_bytes:].view(torch.int32).view(self.row_capacity, nw)[:n]
+            k = torch.arange(self.n_bit_features, device=self.bins.device)
+            bitv = (w[:, k // 32] >> (k % 32)) & 1
+            out[:, cf[nbc:]] = bitv.to(torch.uint8)
+        return out
 
 
 # -------------------------------------------------------- hot-path wrappers --
@@ -318,11 +358,11 @@ def gbdt_update_predictions(pred, X: Matrix, nodes, n_nodes, max_nodes, learning
 class Dataset:
     """Bins packed on the device in the column-blocked layout, plus labels."""
 
-    def __init__(self, bins_rowmajor, label, n_bins, device="cuda", use_skip_bins=True):
+    def __init__(self, bins_rowmajor, label, n_bins, device="cuda", use_skip_bins=True, pack_bits=True):
         import torch
         bins_rowmajor = np.ascontiguousarray(bins_rowmajor, dtype=np.uint8)
         self.n_rows, self.n_features = bins_rowmajor.shape
-        self.ft = FeatureTable(n_bins, device)
+        self.ft = FeatureTable(n_bins, device, pack_bits=pack_bits)
         self.use_skip_bins = use_skip_bins
         self.X = RowBuffer(self.ft, self.n_rows, device, with_rid=False)
         self.label = torch.from_numpy(np.ascontiguousarray(label, dtype=np.float32)).to(device)

@@ -69,6 +69,14 @@ struct PlanLds {
   PlanEntry stage[kPlanStage];
 };
 
+// The matrix column of a split's feature (-1 for an invalid split or a
+// feature outside the map's range).
+__device__ __forceinline__ int32_t split_column(const gbdt_split& sp, const int32_t* feature_col,
+                                                int32_t n_features) {
+  if (!sp.valid || sp.feature < 0 || sp.feature >= n_features) return -1;
+  return feature_col != nullptr ? feature_col[sp.feature] : sp.feature;
+}
+
 __device__ __forceinline__ int32_t tiles_of(int32_t c, int32_t tile_rows) {
   if (c < 0) c = 0;
   return c == 0 ? 1 : (c + tile_rows - 1) / tile_rows;
@@ -81,7 +89,9 @@ __device__ __forceinline__ int32_t tiles_of(int32_t c, int32_t tile_rows) {
 // with node -1 for the launch's tiles [total, max_tiles), and, for a
 // partition plan (status != nullptr), a cleared look-back status array and
 // the ticket and plan total in ctrl, and (splits != nullptr) each node's
-// split in its tiles' descriptors, and (multi != nullptr) the list positions
+// split in its tiles' descriptors (the split feature as its matrix column:
+// feature_col[feature], or the feature itself when feature_col is NULL),
+// and (multi != nullptr) the list positions
 // of the nodes with more than one tile (multi[0] = their count, in no
 // particular order; for the partial reduction).  More tiles than max_tiles sets
 // GBDT_E_SHAPE; the surplus is not planned.  Each entry's node (and split)
@@ -94,6 +104,7 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
                                   int32_t* __restrict__ prefix, TileDesc* __restrict__ desc,
                                   uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
                                   const gbdt_split* __restrict__ splits,
+                                  const int32_t* __restrict__ feature_col, int32_t n_features,
                                   int32_t* __restrict__ multi, PlanLds& L) {
   const bool staged = n <= kPlanStage;
   const bool in_lds = n <= kPlanLdsEntries;
@@ -112,7 +123,7 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
       pe.feature = pe.threshold_bin = pe.n_left = 0;
       if (splits != nullptr) {
         const gbdt_split sp = splits[v];
-        pe.feature = sp.valid ? sp.feature : -1;
+        pe.feature = split_column(sp, feature_col, n_features);
         pe.threshold_bin = sp.threshold_bin;
         pe.n_left = sp.n_left;
       }
@@ -161,7 +172,7 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
       pe.feature = pe.threshold_bin = pe.n_left = 0;
       if (splits != nullptr) {
         const gbdt_split sp = splits[v];
-        pe.feature = sp.valid ? sp.feature : -1;
+        pe.feature = split_column(sp, feature_col, n_features);
         pe.threshold_bin = sp.threshold_bin;
         pe.n_left = sp.n_left;
       }

@@ -71,6 +71,8 @@ struct PlanArgs {
   int32_t* hmulti;
   TileDesc* hdesc;
   WsCtrl* ctrl;
+  const int32_t* feature_col;  // the matrix's map (partition plans store split columns)
+  int32_t n_features;
 };
 
 __device__ __forceinline__ double leaf_weight(int64_t gsum, int32_t count, int32_t S, double lambda) {
@@ -144,7 +146,7 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
   }
   __syncthreads();
   plan_tiles(nodes, lists + LL.build, grow ? 1 : 0, tile_rows, max_tiles, pa.hprefix, pa.hdesc,
-             nullptr, pa.ctrl, nullptr, pa.hmulti, lds);
+             nullptr, pa.ctrl, nullptr, nullptr, 0, pa.hmulti, lds);
 }
 
 // Steps 3-6 bookkeeping for level d, one workgroup: each level-d node either
@@ -291,9 +293,9 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   // this level's partition plan (splitting nodes) and the next level's
   // histogram plan (nodes to build)
   plan_tiles(nodes, split_list, t_split, kPartTileRows, part_max_tiles, pa.prefix, pa.desc, pa.status,
-             pa.ctrl, splits, nullptr, lds);
+             pa.ctrl, splits, pa.feature_col, pa.n_features, nullptr, lds);
   plan_tiles(nodes, build_n, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix, pa.hdesc,
-             nullptr, pa.ctrl, nullptr, pa.hmulti, lds);
+             nullptr, pa.ctrl, nullptr, nullptr, 0, pa.hmulti, lds);
 }
 
 static int64_t min_split_count(const gbdt_params* p, int64_t n) {
@@ -340,10 +342,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   for (int k = 0; k < 2; ++k) {
     const gbdt_rows& r = b->pp[k];
     if (!r.X.bins || !r.q) return fail(GBDT_E_ARG, "a row buffer is null");
-    if (r.X.n_rows != n || r.X.row_capacity != X->row_capacity || r.X.n_blocks != X->n_blocks ||
-        r.X.block_stride != X->block_stride || r.X.block_features != X->block_features ||
-        r.X.n_features != X->n_features)
-      return fail(GBDT_E_SHAPE, "row buffers must have the layout of X");
+    if (!same_layout(r.X, *X)) return fail(GBDT_E_SHAPE, "row buffers must have the layout of X");
   }
   const int32_t D = p->max_depth;
   gbdt_grow_sizes_t sz;
@@ -374,6 +373,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   pa.hprefix = reinterpret_cast<int32_t*>(w + WL.hprefix);
   pa.hmulti = reinterpret_cast<int32_t*>(w + WL.hmulti);
   pa.hdesc = reinterpret_cast<TileDesc*>(w + WL.hdesc);
+  pa.feature_col = X->feature_col;
+  pa.n_features = X->n_features;
   uint64_t* hpart = reinterpret_cast<uint64_t*>(w + WL.hpart);
   // per level: histogram tile rows and launch bounds (level d builds at most
   // 2^(d-1) nodes holding at most n/2 rows; the root builds n rows)

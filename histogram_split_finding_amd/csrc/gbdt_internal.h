@@ -91,6 +91,7 @@ int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows);
 
 // Argument checks and launches shared by the per-call entry points and the
 // tree driver (the driver's level kernel writes the tile plans itself).
+bool same_layout(const gbdt_matrix& a, const gbdt_matrix& b);
 int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft);
 int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,

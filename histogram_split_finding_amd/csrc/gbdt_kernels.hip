@@ -154,12 +154,14 @@ __global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nod
                                                WsCtrl* __restrict__ ctrl,
                                                uint64_t* __restrict__ status,
                                                const gbdt_split* __restrict__ splits,
-                                               int32_t* __restrict__ multi) {
+                                               const int32_t* __restrict__ feature_col,
+                                               int32_t n_features, int32_t* __restrict__ multi) {
   __shared__ PlanLds lds;
   const int32_t raw = *list_len;
   if (threadIdx.x == 0 && (raw < 0 || raw > list_cap)) dev_error(&ctrl->err, GBDT_E_SHAPE);
   const int32_t n = clamp_len(list_len, list_cap);
-  plan_tiles(nodes, list, n, tile_rows, max_tiles, prefix, desc, status, ctrl, splits, multi, lds);
+  plan_tiles(nodes, list, n, tile_rows, max_tiles, prefix, desc, status, ctrl, splits, feature_col,
+             n_features, multi, lds);
 }
 
 // -------------------------------------------------------------- gradients --
@@ -278,20 +280,150 @@ inline int load_unit_for(int32_t block_stride) {
   return 4;
 }
 
-// One workgroup = one (tile of one node's rows, feature block).  Lanes are
+// Histogram of a tile's bit features (the bit block), with 2 LDS slots per
+// bit feature k (its bins 0 and 1).  Per feature the rarer value is
+// accumulated -- the skip bin, 0 when none is set, is the frequent one -- by
+// walking the set bits of (word ^ inverse mask) of each row: one LDS atomic
+// per rare cell; the frequent bin is the tile total minus the rare one.
+// Lanes are (row group, word of 32 bit features).
+constexpr int kBitStage = 1024;   // bit features whose output table is staged in LDS
+constexpr int kMaxBitWords = 128; // words per row of the bit block, at most
+
+template <int NW>
+__device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* __restrict__ bins,
+                               int64_t row_capacity, int32_t n_blocks, int32_t block_stride,
+                               int32_t n_features, int32_t n_bit, int32_t bit_stride,
+                               const int32_t* __restrict__ col_feature, const int64_t* __restrict__ q,
+                               const int32_t* __restrict__ bin_offset,
+                               const int32_t* __restrict__ skip_bin, int32_t total_bins,
+                               int32_t lds_bins, int32_t bits, int64_t q_bound,
+                               int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
+                               uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl,
+                               uint64_t* lds, uint32_t* s_inv, int32_t* s_bit, uint64_t* sh_tot) {
+  const int32_t nbc = n_features - n_bit;
+  const int32_t nwords = bit_stride >> 2;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  if (2 * n_bit > lds_bins) {
+    if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
+    return;
+  }
+  for (int32_t b = threadIdx.x; b < lds_bins + kLdsHistSlack; b += blockDim.x) lds[b] = 0ull;
+  for (int32_t w = threadIdx.x; w < nwords; w += blockDim.x) s_inv[w] = 0u;
+  __syncthreads();
+  // per bit feature: its global bins and whether its skip bin is 1
+  for (int32_t kk = threadIdx.x; kk < n_bit; kk += blockDim.x) {
+    int32_t f = col_feature[nbc + kk];
+    f = f < 0 ? 0 : (f >= n_features ? n_features - 1 : f);
+    const int32_t lo = bin_offset[f];
+    const int32_t nb = bin_offset[f + 1] - lo;
+    const int32_t sk = skip_bin != nullptr ? skip_bin[f] : -1;
+    const uint32_t inv = (sk == 1 && nb == 2) ? 1u : 0u;
+    if (inv) atomicOr(&s_inv[kk >> 5], 1u << (kk & 31));
+    if (kk < kBitStage) s_bit[kk] = (lo << 2) | ((nb == 2 ? 1 : 0) << 1) | (int32_t)inv;
+  }
+  __syncthreads();
+  const int64_t r0 = td.r0;
+  const int64_t r1 = td.r1;
+  const int32_t rpi = (int32_t)blockDim.x / nwords;  // rows per step
+  const int32_t w = (int32_t)threadIdx.x % nwords;
+  const int32_t rg = (int32_t)threadIdx.x / nwords;
+  const uint32_t inv = s_inv[w < nwords ? w : 0];
+  const int32_t kbase = 32 * w;
+  const uint32_t valid = kbase + 32 <= n_bit ? 0xffffffffu
+                                             : (kbase >= n_bit ? 0u : ((1u << (n_bit - kbase)) - 1u));
+  const uint32_t* __restrict__ wb = reinterpret_cast<const uint32_t*>(
+      bins + int64_t(n_blocks) * row_capacity * block_stride);
+  uint64_t tot = 0ull;
+  int64_t qmax = 0;
+  constexpr int BATCH = 4;
+  if (rg < rpi) {
+    for (int64_t r = r0 + rg; r < r1; r += int64_t(BATCH) * rpi) {
+      uint32_t x[BATCH];
+      int64_t qq[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int64_t rr = r + int64_t(u) * rpi;
+        const bool ok = rr < r1;
+        x[u] = ok ? wb[rr * nwords + w] : 0u;
+        qq[u] = ok ? q[rr] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int64_t rr = r + int64_t(u) * rpi;
+        if (rr >= r1) continue;
+        const int64_t aq = qq[u] < 0 ? -qq[u] : qq[u];
+        qmax = aq > qmax ? aq : qmax;
+        const uint64_t pk = ((uint64_t)qq[u] << bits) + 1ull;
+        tot += pk;
+        uint32_t m = (x[u] ^ inv) & valid;
+        while (m) {
+          const int32_t t = __builtin_ctz(m);
+          m &= m - 1u;
+          const int32_t slot = 2 * (kbase + t) + (int32_t)(1u ^ ((inv >> t) & 1u));
+          __hip_atomic_fetch_add(&lds[slot], pk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+    }
+  }
+  if (qmax > q_bound) dev_error(&ctrl->err, GBDT_E_OVERFLOW);
+  const uint64_t t0 = wave_sum_dpp((w == 0 && rg < rpi) ? tot : 0ull);
+  if (lane == 0) sh_tot[wid] = t0;
+  __syncthreads();
+  uint64_t tile_total = 0ull;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) tile_total += sh_tot[ww];
+  // the frequent bin of each bit feature: tile total minus the rare one
+  for (int32_t kk = threadIdx.x; kk < n_bit; kk += blockDim.x) {
+    const int32_t iv = (int32_t)((s_inv[kk >> 5] >> (kk & 31)) & 1u);
+    lds[2 * kk + iv] = tile_total - lds[2 * kk + (1 - iv)];
+  }
+  __syncthreads();
+  const uint64_t mask = (1ull << bits) - 1ull;
+  const int32_t v = td.node;
+  for (int32_t e = threadIdx.x; e < 2 * n_bit; e += blockDim.x) {
+    const int32_t kk = e >> 1, b = e & 1;
+    int32_t lo, two;
+    if (kk < kBitStage) {
+      lo = s_bit[kk] >> 2;
+      two = (s_bit[kk] >> 1) & 1;
+    } else {
+      int32_t f = col_feature[nbc + kk];
+      f = f < 0 ? 0 : (f >= n_features ? n_features - 1 : f);
+      lo = bin_offset[f];
+      two = bin_offset[f + 1] - lo == 2;
+    }
+    if (b == 1 && !two) continue;  // a one-bin feature
+    const uint64_t xv = lds[e];
+    if (td.ntiles == 1) {
+      const uint64_t c = xv & mask;
+      hist_g[int64_t(v) * total_bins + lo + b] = (int64_t)(xv - c) >> bits;
+      hist_cnt[int64_t(v) * total_bins + lo + b] = (uint32_t)c;
+    } else {
+      partial[int64_t(tile) * total_bins + lo + b] = xv;
+    }
+  }
+}
+
+// One workgroup = one (tile of one node's rows, column block); the block
+// index n_blocks is the bit block (hist_bit_block).  Byte blocks: lanes are
 // laid out as (row group, column of UNIT bytes): a lane loads UNIT bins of a
 // row with one vector load (consecutive lanes read consecutive bytes, so a
 // wave streams contiguous memory) and adds the packed cell (q << bits) + 1 to
 // the LDS slot of each bin with a 64-bit LDS atomic.  Loads of BATCH rows are
 // issued before their atomics so each wave keeps several loads in flight.
-// Each feature's skip bin is not accumulated: it is set afterwards to the
-// tile total minus the feature's other bins (exact integers).  A node
-// covered by one tile writes its decoded histogram straight to hist;
-// otherwise the tile writes its packed partial for k_hist_reduce.
-template <int UNIT>
+// The block's histogram sits in LDS column after column (a column's feature
+// is col_feature[c]).  Each feature's skip bin is not accumulated: it is set
+// afterwards to the tile total minus the feature's other bins (exact
+// integers).  A node covered by one tile writes its decoded histogram
+// straight to hist; otherwise the tile writes its packed partial (global bin
+// order) for k_hist_reduce.  BITS: the layout has a bit block (the kernel
+// without it is leaner: fewer registers and LDS).
+template <int UNIT, bool BITS>
 __global__ void __launch_bounds__(kHistThreads) k_hist(
-    const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t block_features,
-    int32_t block_stride, int32_t n_features, const int64_t* __restrict__ q,
+    const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t n_blocks,
+    int32_t block_features, int32_t block_stride, int32_t n_features, int32_t n_bit,
+    int32_t bit_stride, const int32_t* __restrict__ col_feature, const int64_t* __restrict__ q,
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ skip_bin,
     int32_t total_bins, int32_t lds_bins, const TileDesc* __restrict__ desc, int32_t bits,
     int64_t q_bound, int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
@@ -301,68 +433,91 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(
   constexpr int NW = kHistThreads / 64;
   extern __shared__ uint64_t lds[];
   __shared__ uint64_t sh_tot[NW];
-  __shared__ int32_t s_fbase[kMaxBlockFeatures];
+  __shared__ int32_t s_fbase[kMaxBlockFeatures + 1];
   __shared__ int32_t s_fbins[kMaxBlockFeatures];
   __shared__ int32_t s_fskip[kMaxBlockFeatures];
+  __shared__ int32_t s_fgb[kMaxBlockFeatures];
   __shared__ uint64_t s_slice[kHistThreads / 64][kMaxBlockFeatures];
-  // Every load of the prologue is issued before the first branch (a cold
-  // cache makes each dependent round trip cost about a microsecond).
+  __shared__ uint32_t s_inv[kMaxBitWords];
+  __shared__ int32_t s_bit[kBitStage];
   const int32_t tile = blockIdx.x;
   const int32_t blk = blockIdx.y;
-  const int32_t f0 = blk * block_features;
-  const int32_t f1 = f0 + block_features < n_features ? f0 + block_features : n_features;
   const TileDesc td = desc[tile];
-  const int32_t lb0 = bin_offset[f0];
-  const int32_t lb1 = bin_offset[f1];
-  const int32_t lpr = block_stride / UNIT;  // lanes per row
-  const int32_t rpi = kHistThreads / lpr;   // rows per step of the workgroup
-  const int32_t col = threadIdx.x % lpr;
-  const int32_t rg = threadIdx.x / lpr;
-  // per byte of the lane's column: LDS slot base and skip bin.  Padding bytes
-  // (past the block's features) are always 0 and get skip bin 0, so they
-  // never reach an atomic.  Bins are range-checked when the matrix is packed;
-  // here any byte value stays inside the LDS allocation (kLdsHistSlack).
-  int32_t bo[NB];
-  int32_t sk[NB];
-#pragma unroll
-  for (int m = 0; m < NB; ++m) {
-    const int32_t f = f0 + UNIT * col + m;
-    const int32_t fc = f < f1 ? f : f0;
-    bo[m] = bin_offset[fc];
-    sk[m] = skip_bin != nullptr ? skip_bin[fc] : -1;
+  if (BITS && blk == n_blocks) {  // the bit block
+    if (td.node < 0 || n_bit <= 0) return;
+    if ((bit_stride >> 2) > kMaxBitWords) {  // the host checks bit_stride <= 4 * kMaxBitWords
+      if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
+      return;
+    }
+    hist_bit_block<NW>(td, tile, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
+                       bit_stride, col_feature, q, bin_offset, skip_bin, total_bins, lds_bins, bits,
+                       q_bound, hist_g, hist_cnt, partial, ctrl, lds, s_inv, s_bit, sh_tot);
+    return;
   }
-  // the block's feature table (lane j: feature f0 + j) for the skip-bin pass
-  const int32_t tj = f0 + (int32_t)(threadIdx.x & (kMaxBlockFeatures - 1));
-  const int32_t tjc = tj < f1 ? tj : f0;
-  const int32_t t_lo = bin_offset[tjc];
-  const int32_t t_hi = bin_offset[tjc + 1];
-  const int32_t t_sk = skip_bin != nullptr ? skip_bin[tjc] : -1;
+  if (blk >= n_blocks) return;
+  // Every load of the prologue is issued before the first branch (a cold
+  // cache makes each dependent round trip cost about a microsecond): the
+  // descriptor and wave 0's column table (lane j: column f0 + j).
+  const int32_t nbc = n_features - n_bit;
+  const int32_t f0 = blk * block_features;  // first byte column of the block
+  const int32_t c1 = f0 + block_features < nbc ? f0 + block_features : nbc;
+  const int32_t nf = c1 - f0;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int32_t tc = f0 + lane;
+  const bool tval = tc < c1;
+  int32_t tf = col_feature != nullptr ? col_feature[tval ? tc : f0] : (tval ? tc : f0);
+  tf = tf < 0 ? 0 : (tf >= n_features ? n_features - 1 : tf);
+  int32_t t_lo = 0, t_hi = 0, t_sk = -1;
+  if (wid == 0) {
+    t_lo = bin_offset[tf];
+    t_hi = bin_offset[tf + 1];
+    t_sk = skip_bin != nullptr ? skip_bin[tf] : -1;
+  }
   asm volatile("" ::: "memory");
   if (td.node < 0) return;  // beyond the plan
   const int32_t v = td.node;
   const int32_t ntiles = td.ntiles;
   const int64_t r0 = td.r0;
   const int64_t r1 = td.r1;
-  const int32_t nbb = lb1 - lb0;
+  for (int32_t b = threadIdx.x; b < lds_bins + kLdsHistSlack; b += kHistThreads) lds[b] = 0ull;
+  if (wid == 0) {
+    // exclusive prefix of the columns' bin counts: each column's LDS base
+    const int32_t cnt = tval ? t_hi - t_lo : 0;
+    int32_t x = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    s_fbase[lane] = x - cnt;
+    if (lane == 63) s_fbase[kMaxBlockFeatures] = x;
+    s_fbins[lane] = cnt;
+    s_fskip[lane] = tval ? t_sk : -1;
+    s_fgb[lane] = t_lo;
+  }
+  __syncthreads();
+  const int32_t nbb = s_fbase[kMaxBlockFeatures];
   if (nbb < 0 || nbb > lds_bins) {  // the LDS holds lds_bins slots (+ slack)
     if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
     return;
   }
-  for (int32_t b = threadIdx.x; b < lds_bins + kLdsHistSlack; b += kHistThreads) lds[b] = 0ull;
+  const int32_t lpr = block_stride / UNIT;  // lanes per row
+  const int32_t rpi = kHistThreads / lpr;   // rows per step of the workgroup
+  const int32_t col = threadIdx.x % lpr;
+  const int32_t rg = threadIdx.x / lpr;
+  // per byte of the lane's column: LDS slot base and skip bin.  Padding bytes
+  // (past the block's columns) are always 0 and get skip bin 0, so they
+  // never reach an atomic.  Bins are range-checked when the matrix is packed;
+  // here any byte value stays inside the LDS allocation (kLdsHistSlack).
   int32_t base[NB];
   int32_t skip[NB];
 #pragma unroll
   for (int m = 0; m < NB; ++m) {
-    const bool ok = (f0 + UNIT * col + m < f1) && (rg < rpi);
-    base[m] = ok ? bo[m] - lb0 : 0;
-    skip[m] = ok ? sk[m] : 0;
+    const int32_t j = UNIT * col + m;
+    const bool ok = (f0 + j < c1) && (rg < rpi);
+    base[m] = ok ? s_fbase[j] : 0;
+    skip[m] = ok ? s_fskip[j] : 0;
   }
-  if (threadIdx.x < kMaxBlockFeatures) {
-    s_fbase[threadIdx.x] = t_lo - lb0;
-    s_fbins[threadIdx.x] = t_hi - t_lo;
-    s_fskip[threadIdx.x] = tj < f1 ? t_sk : -1;
-  }
-  __syncthreads();
 
   const uint8_t* __restrict__ bb = bins + int64_t(blk) * row_capacity * block_stride + UNIT * col;
   uint64_t tot = 0ull;
@@ -403,13 +558,10 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(
   if (qmax > q_bound) dev_error(&ctrl->err, GBDT_E_OVERFLOW);
   // tile total from the column-0 lanes (one per row)
   const uint64_t t0 = wave_sum_dpp((col == 0 && rg < rpi) ? tot : 0ull);
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
   if (lane == 0) sh_tot[wid] = t0;
   __syncthreads();
   // skip bins: tile total minus the feature's other bins.  Lane j sums bins
-  // [16 w, 16 w + 16) of feature f0 + j in wave w; wave 0 adds the slices.
-  const int32_t nf = f1 - f0;
+  // [16 w, 16 w + 16) of column j in wave w; wave 0 adds the slices.
   if (lane < nf) {
     const int32_t fb = s_fbase[lane];
     const int32_t fn = s_fbins[lane];
@@ -434,19 +586,23 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(
   }
   __syncthreads();
 
+  // output, column by column (a wave per column): global bins of the
+  // column's feature
   const uint64_t mask = (1ull << bits) - 1ull;
-  if (ntiles == 1) {
-    int64_t* __restrict__ hg = hist_g + int64_t(v) * total_bins + lb0;
-    uint32_t* __restrict__ hc = hist_cnt + int64_t(v) * total_bins + lb0;
-    for (int32_t b = threadIdx.x; b < nbb; b += kHistThreads) {
-      const uint64_t x = lds[b];
-      const uint64_t c = x & mask;
-      hg[b] = (int64_t)(x - c) >> bits;
-      hc[b] = (uint32_t)c;
+  for (int32_t j = wid; j < nf; j += NW) {
+    const int32_t fb = s_fbase[j];
+    const int32_t fn = s_fbins[j];
+    const int64_t gb = s_fgb[j];
+    for (int32_t c = lane; c < fn; c += 64) {
+      const uint64_t x = lds[fb + c];
+      if (ntiles == 1) {
+        const uint64_t cc = x & mask;
+        hist_g[int64_t(v) * total_bins + gb + c] = (int64_t)(x - cc) >> bits;
+        hist_cnt[int64_t(v) * total_bins + gb + c] = (uint32_t)cc;
+      } else {
+        partial[int64_t(tile) * total_bins + gb + c] = x;
+      }
     }
-  } else {
-    uint64_t* __restrict__ pp = partial + int64_t(tile) * total_bins + lb0;
-    for (int32_t b = threadIdx.x; b < nbb; b += kHistThreads) pp[b] = lds[b];
   }
 }
 
@@ -917,8 +1073,8 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const int64_t* __restrict__ sq,
     const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, int64_t* __restrict__ dq,
     int32_t* __restrict__ drid, int64_t row_capacity, int32_t n_blocks, int32_t block_features,
-    int32_t block_stride, int32_t n_features, const TileDesc* __restrict__ desc,
-    uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl) {
+    int32_t block_stride, int32_t n_features, int32_t n_bit, int32_t bit_stride,
+    const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl) {
   constexpr int BATCH = 32 / UNIT;
   __shared__ int32_t s_tile;
   __shared__ int32_t s_cnt[kPartRowsPerThread][kPartWaves];
@@ -942,12 +1098,21 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
   // a listed node must carry a valid split; otherwise nothing is moved, the
   // tile still publishes (so later tiles never wait on it) and the error word
   // is set
+  // the descriptor's feature is the split's matrix column: a byte column
+  // (c < n_features - n_bit) or a bit of the bit block
   const bool split_ok = td.split_valid && td.feature >= 0 && td.feature < n_features;
   const int32_t rows = split_ok ? rows_all : 0;
-  const int32_t fblk = split_ok ? td.feature / block_features : 0;
-  const int32_t fcol = split_ok ? td.feature % block_features : 0;
+  const int32_t nbc = n_features - n_bit;
+  const int32_t sc = split_ok ? td.feature : 0;
+  const bool fbit = sc >= nbc;
+  const int32_t fblk = fbit ? 0 : sc / block_features;
+  const int32_t fcol = fbit ? 0 : sc % block_features;
+  const int32_t fk = fbit ? sc - nbc : 0;
   const uint8_t* __restrict__ fcolp = sbins + int64_t(fblk) * row_capacity * block_stride + fcol;
-  // loads that need only the descriptor: split-feature bytes, q, row ids
+  const uint8_t* __restrict__ sbits = sbins + int64_t(n_blocks) * row_capacity * block_stride;
+  const uint32_t* __restrict__ fwordp =
+      reinterpret_cast<const uint32_t*>(sbits) + (fk >> 5);
+  // loads that need only the descriptor: split-feature bins, q, row ids
   int32_t fb[kPartRowsPerThread];
   int64_t qv[kPartRowsPerThread];
   int32_t rv[kPartRowsPerThread];
@@ -956,7 +1121,10 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
     const int32_t i = k * kPartThreads + threadIdx.x;
     const bool ok = i < rows;
     const int64_t s = r0 + i;
-    fb[k] = ok ? (int32_t)fcolp[s * block_stride] : 0;
+    if (fbit)
+      fb[k] = ok ? (int32_t)((fwordp[s * (bit_stride >> 2)] >> (fk & 31)) & 1u) : 0;
+    else
+      fb[k] = ok ? (int32_t)fcolp[s * block_stride] : 0;
     qv[k] = ok ? sq[s] : 0;
     rv[k] = (ok && drid != nullptr) ? (srid != nullptr ? srid[s] : (int32_t)s) : 0;
   }
@@ -1027,6 +1195,34 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
   }
   if (bad_pos) dev_error(&ctrl->err, GBDT_E_INTERNAL);
   __syncthreads();
+  // bit block: (row group, word) lanes, 8 rows of loads in flight per lane
+  if (n_bit > 0) {
+    const int32_t nwords = bit_stride >> 2;
+    const int32_t brpi = kPartThreads / nwords;
+    const int32_t bw = threadIdx.x % nwords;
+    const int32_t brg = threadIdx.x / nwords;
+    const uint32_t* __restrict__ sw = reinterpret_cast<const uint32_t*>(sbits) + bw;
+    uint32_t* __restrict__ dw = reinterpret_cast<uint32_t*>(
+        dbins + int64_t(n_blocks) * row_capacity * block_stride) + bw;
+    if (brg < brpi) {
+      for (int32_t i = brg; i < rows; i += 8 * brpi) {
+        uint32_t x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t ii = i + u * brpi;
+          if (ii < rows) x[u] = sw[(r0 + ii) * nwords];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t ii = i + u * brpi;
+          if (ii < rows) {
+            const int32_t d = s_dpos[ii];
+            if (d >= 0) dw[int64_t(d) * nwords] = x[u];
+          }
+        }
+      }
+    }
+  }
   // bins: (row group, column of UNIT bytes) lanes, every block, BATCH rows
   // of loads in flight per lane
   if (rg < rpi) {
@@ -1056,28 +1252,38 @@ __global__ void __launch_bounds__(kPartThreads) k_partition(
 // ------------------------------------------------------ prediction update --
 // Forward pass of one tree over the rows of X in their original order, in two
 // launches.  k_compact_tree copies the tree into a table of 8 bytes per node
-// (left child or leaf slot, feature, threshold) plus a table of leaf values,
-// checking each node.  k_update is persistent (a few workgroups per CU): each
-// workgroup first copies both tables into LDS (96 KiB for a depth-12 tree),
-// then walks rows in a grid-stride loop, ROWS rows per lane at once, each
-// lane holding its rows' bins (every feature block, MAXDW dwords at most) in
-// registers.  HBM traffic is the bins once and the predictions read and
+// (left child or leaf slot; where the split feature's bin sits in a row's
+// dwords -- byte blocks, then bit words -- and the threshold) plus a table of
+// leaf values, checking each node.  k_update is persistent (a few workgroups
+// per CU): each workgroup first copies the node table into LDS (64 KiB for a
+// depth-12 tree), then walks rows in a grid-stride loop, ROWS rows per lane
+// at once, each lane holding its rows' bins (every block, MAXDW dwords at
+// most) in registers.  The walk is branch-free: every step reads each row's
+// node, picks the split feature's dword with a select tree over the bits of
+// its index, and moves the row to a child unless it sits on a leaf; the wave
+// stops when all its rows do.  The leaf value is read from global memory
+// once per row.  HBM traffic is the bins once and the predictions read and
 // written once, sequentially in rows -- no gather or scatter through row ids.
 // Trees must be breadth-first with right = left + 1; a node whose children
 // are not in (id, n_nodes) stops the walk and sets GBDT_E_INTERNAL (the row
 // keeps its prediction).  A tree too large for LDS is walked from the global
-// tables (TREE_IN_LDS = false).
+// table (TREE_IN_LDS = false).
 constexpr int kUpdThreads = 1024;
 constexpr int kUpdMaxRowBytes = 256;
-constexpr size_t kUpdTreeLds = 96 * 1024;
+constexpr size_t kUpdTreeLds = 64 * 1024;
 constexpr uint32_t kLeafTag = 0x80000000u;
 constexpr uint32_t kBadTag = 0x40000000u;
 
 // One workgroup: leaves get consecutive slots in lval (order of arrival; a
 // slot is only ever read through its own leaf's entry).
+// Entry of a split node: e.x = left child, e.y = dword index (6 bits) |
+// shift << 6 (5 bits) | bit flag << 11 | threshold << 16.
 __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restrict__ nodes,
                                                        const int32_t* __restrict__ n_nodes_dev,
                                                        int32_t max_nodes, int32_t n_features,
+                                                       const int32_t* __restrict__ feature_col,
+                                                       int32_t n_blocks, int32_t block_features,
+                                                       int32_t block_stride, int32_t n_bit,
                                                        uint2* __restrict__ ctab,
                                                        double* __restrict__ lval) {
   __shared__ int32_t s_leaves;
@@ -1098,11 +1304,27 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
       } else {
         e.x = kBadTag;  // more leaves than a tree of max_nodes nodes can hold
       }
-    } else if (nd.z <= v || nd.z >= nn || nd.w != nd.z + 1 || nd.x < 0 || nd.x >= n_features) {
+    } else if (nd.z <= v || nd.z + 1 >= nn || nd.w != nd.z + 1 || nd.x < 0 || nd.x >= n_features) {
       e.x = kBadTag;
     } else {
-      e.x = (uint32_t)nd.z;
-      e.y = (uint32_t)nd.x | ((uint32_t)(nd.y & 0xffff) << 16);
+      const int32_t c = feature_col != nullptr ? feature_col[nd.x] : nd.x;
+      const int32_t nbc = n_features - n_bit;
+      uint32_t loc;
+      if (c >= 0 && c < nbc) {
+        const int32_t blk = c / block_features;
+        const int32_t byte = blk * block_stride + (c - blk * block_features);
+        loc = (uint32_t)(byte >> 2) | ((uint32_t)(8 * (byte & 3)) << 6);
+      } else {
+        const int32_t kk = c - nbc;
+        loc = (uint32_t)(n_blocks * (block_stride >> 2) + (kk >> 5)) | ((uint32_t)(kk & 31) << 6) |
+              (1u << 11);
+      }
+      if (c < 0 || c >= n_features) {
+        e.x = kBadTag;
+      } else {
+        e.x = (uint32_t)nd.z;
+        e.y = loc | ((uint32_t)(nd.y & 0xffff) << 16);
+      }
     }
     ctab[v] = e;
   }
@@ -1111,10 +1333,11 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
 template <int MAXDW, int ROWS, bool TREE_IN_LDS>
 __global__ void __launch_bounds__(kUpdThreads) k_update(
     double* __restrict__ pred, int64_t n, const uint8_t* __restrict__ bins, int64_t row_capacity,
-    int32_t n_blocks, int32_t block_features, int32_t block_stride,
-    const uint2* __restrict__ ctab_g, const double* __restrict__ lval_g,
+    int32_t n_blocks, int32_t block_stride, int32_t bit_stride,
+    const uint2* __restrict__ ctab_g, const double* __restrict__ lval,
     const int32_t* __restrict__ n_nodes_dev, int32_t max_nodes, double eta,
     WsCtrl* __restrict__ ctrl) {
+  static_assert((MAXDW & (MAXDW - 1)) == 0, "MAXDW is a power of two");
   extern __shared__ uint64_t smem[];
   int32_t nn = *n_nodes_dev;
   if (nn > max_nodes) nn = max_nodes;
@@ -1123,84 +1346,96 @@ __global__ void __launch_bounds__(kUpdThreads) k_update(
     return;
   }
   const uint2* ctab = ctab_g;
-  const double* lval = lval_g;
   if (TREE_IN_LDS) {
     uint2* ct = reinterpret_cast<uint2*>(smem);
-    double* lv = reinterpret_cast<double*>(smem + max_nodes);
-    for (int32_t v = threadIdx.x; v < nn; v += kUpdThreads) {
-      const uint2 e = ctab_g[v];
-      ct[v] = e;
-      if ((e.x & kLeafTag) && !(e.x & kBadTag)) lv[e.x & ~kLeafTag] = lval_g[e.x & ~kLeafTag];
-    }
+    for (int32_t v = threadIdx.x; v < nn; v += kUpdThreads) ct[v] = ctab_g[v];
     __syncthreads();
     ctab = ct;
-    lval = lv;
   }
   const int32_t dw = block_stride >> 2;
-  const int32_t ndw = n_blocks * dw;
+  const int32_t ndw = n_blocks * dw;            // byte-block dwords of a row
+  const int32_t nwords = bit_stride >> 2;       // then its bit words
+  const uint32_t* __restrict__ bitw =
+      reinterpret_cast<const uint32_t*>(bins + int64_t(n_blocks) * row_capacity * block_stride);
   bool bad = false;
   const int64_t stride = int64_t(gridDim.x) * kUpdThreads * ROWS;
   for (int64_t base = int64_t(blockIdx.x) * kUpdThreads * ROWS + threadIdx.x; base < n;
        base += stride) {
     uint32_t row[ROWS][MAXDW];
-    uint32_t v[ROWS];
+    int32_t v[ROWS];
+    uint32_t fin[ROWS];  // leaf entry once reached (kLeafTag | slot), 0 while walking
     bool live[ROWS];
+    double pv[ROWS];
 #pragma unroll
     for (int u = 0; u < ROWS; ++u) {
-      const int64_t i = base + int64_t(u) * kUpdThreads;
-      live[u] = i < n;
-      v[u] = 0u;
+      const int64_t i0 = base + int64_t(u) * kUpdThreads;
+      live[u] = i0 < n;
+      v[u] = 0;
+      fin[u] = live[u] ? 0u : kLeafTag;
+      const int64_t i = live[u] ? i0 : n - 1;  // a valid row: loads need no branch
+      pv[u] = pred[i];
+      // dword x of the row: byte block b, dword xb of its run (a uniform
+      // walk, no division), then the bit words.  The loads are unconditional
+      // (uniform pointer selects), so all of them are in flight together.
+      const uint32_t* __restrict__ bp =
+          reinterpret_cast<const uint32_t*>(bins + i * block_stride);
+      const uint32_t* __restrict__ wp = bitw + i * nwords;
+      int32_t xb = 0;
+      int64_t boff = 0;  // dwords from bins to block b's run
 #pragma unroll
       for (int x = 0; x < MAXDW; ++x) {
-        row[u][x] = 0u;
-        if (live[u] && x < ndw) {
-          const int32_t b = x / dw;
-          row[u][x] = *reinterpret_cast<const uint32_t*>(
-              bins + (int64_t(b) * row_capacity + i) * block_stride + 4 * (x - b * dw));
+        const bool in_bytes = x < ndw;
+        const bool in_bits = !in_bytes && x < ndw + nwords;
+        const uint32_t* p = in_bytes ? bp + boff + xb : (in_bits ? wp + (x - ndw) : bp);
+        const uint32_t val = *p;
+        row[u][x] = (in_bytes || in_bits) ? val : 0u;
+        if (in_bytes && ++xb == dw) {
+          xb = 0;
+          boff += (row_capacity * block_stride) >> 2;
         }
       }
     }
+    // the walk: branch-free steps until every row of the wave sits on a leaf
     for (int step = 0; step <= GBDT_MAX_DEPTH; ++step) {
-      bool any = false;
+      bool walking = false;
 #pragma unroll
       for (int u = 0; u < ROWS; ++u) {
-        if (!live[u] || (v[u] & kLeafTag)) continue;
         const uint2 e = ctab[v[u]];
-        if (e.x & kLeafTag) {
-          v[u] = e.x;
-          continue;
-        }
-        if (e.x & kBadTag) {
-          live[u] = false;
-          bad = true;
-          continue;
-        }
-        const int32_t f = (int32_t)(e.y & 0xffffu);
-        const int32_t thr = (int32_t)(e.y >> 16);
-        const int32_t blk = f / block_features;
-        const int32_t byte = blk * block_stride + (f - blk * block_features);
-        // select the dword with a fixed chain of selects: a per-lane dynamic
-        // index into registers would become a loop over the distinct indices
-        const int32_t kk = byte >> 2;
-        uint32_t word = row[u][0];
+        const bool leaf = (e.x & kLeafTag) != 0u;
+        const bool badn = (e.x & kBadTag) != 0u;
+        // the split feature's dword: a select tree over the bits of its index
+        const uint32_t kk = e.y & 63u;
+        uint32_t t[MAXDW];
 #pragma unroll
-        for (int x = 1; x < MAXDW; ++x) word = (x == kk) ? row[u][x] : word;
-        const int32_t bv = (word >> (8 * (byte & 3))) & 0xff;
-        v[u] = bv <= thr ? e.x : e.x + 1u;
-        any = true;
+        for (int x = 0; x < MAXDW; ++x) t[x] = row[u][x];
+#pragma unroll
+        for (int lvl = 0, w = MAXDW; w > 1; ++lvl, w >>= 1) {
+          const bool hi = (kk >> lvl) & 1u;
+#pragma unroll
+          for (int x = 0; x < w / 2; ++x) t[x] = hi ? t[2 * x + 1] : t[2 * x];
+        }
+        const uint32_t shift = (e.y >> 6) & 31u;
+        const uint32_t vmask = (e.y & (1u << 11)) ? 1u : 0xffu;
+        const uint32_t bv = (t[0] >> shift) & vmask;
+        const int32_t next = (int32_t)e.x + (bv <= (e.y >> 16) ? 0 : 1);
+        const bool moving = fin[u] == 0u && !leaf && !badn;
+        bad |= fin[u] == 0u && badn;
+        fin[u] = fin[u] != 0u ? fin[u] : (leaf ? e.x : (badn ? kBadTag : 0u));
+        v[u] = moving ? next : v[u];
+        walking |= moving;
       }
-      if (!any) break;
+      if (!__any(walking)) break;
     }
 #pragma unroll
     for (int u = 0; u < ROWS; ++u) {
       if (!live[u]) continue;
-      if (!(v[u] & kLeafTag)) {  // no leaf within the depth bound
+      if (!(fin[u] & kLeafTag)) {  // a bad node, or no leaf within the depth bound
         bad = true;
         continue;
       }
       const int64_t i = base + int64_t(u) * kUpdThreads;
-      const double delta = eta * lval[v[u] & ~kLeafTag];
-      pred[i] = pred[i] + delta;
+      const double delta = eta * lval[fin[u] & ~kLeafTag];
+      pred[i] = pv[u] + delta;
     }
   }
   if (bad) dev_error(&ctrl->err, GBDT_E_INTERNAL);
@@ -1215,30 +1450,54 @@ static void launch_update(bool in_lds, int rows, dim3 grid, size_t lds, hipStrea
   auto kern = in_lds ? (rows == 2 ? k_update<MAXDW, R2, true> : k_update<MAXDW, 1, true>)
                      : (rows == 2 ? k_update<MAXDW, R2, false> : k_update<MAXDW, 1, false>);
   hipLaunchKernelGGL(kern, grid, dim3(kUpdThreads), lds, s, pred, n, X->bins, X->row_capacity,
-                     X->n_blocks, X->block_features, X->block_stride, ctab, lval, n_nodes,
-                     max_nodes, eta, ctrl);
+                     X->n_blocks, X->block_stride, X->bit_stride, ctab, lval, n_nodes, max_nodes, eta,
+                     ctrl);
 }
 
 // ------------------------------------------------------- setup: packing --
+// One thread per row: byte columns into their blocks (feature of column c =
+// col_feature[c], identity when NULL), bit features into the bit words.
 __global__ void __launch_bounds__(256) k_pack(const uint8_t* __restrict__ src, int64_t n,
                                               int32_t F, uint8_t* __restrict__ dst,
                                               int64_t row_capacity, int32_t n_blocks,
                                               int32_t block_features, int32_t block_stride,
+                                              int32_t n_bit, int32_t bit_stride,
+                                              const int32_t* __restrict__ col_feature,
                                               const int32_t* __restrict__ n_bins,
                                               WsCtrl* __restrict__ ctrl) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  const int32_t nbc = F - n_bit;
   bool bad = false;
   for (int32_t b = 0; b < n_blocks; ++b) {
     uint8_t* d = dst + int64_t(b) * row_capacity * block_stride + i * block_stride;
     for (int32_t jj = 0; jj < block_stride; ++jj) {
-      const int32_t f = b * block_features + jj;
+      const int32_t c = b * block_features + jj;
       uint8_t x = 0;
-      if (jj < block_features && f < F) {
+      if (jj < block_features && c < nbc) {
+        int32_t f = col_feature != nullptr ? col_feature[c] : c;
+        f = f < 0 ? 0 : (f >= F ? F - 1 : f);
         x = src[i * F + f];
         bad |= (int32_t)x >= n_bins[f];
       }
       d[jj] = x;
+    }
+  }
+  if (n_bit > 0) {
+    uint32_t* wd = reinterpret_cast<uint32_t*>(dst + int64_t(n_blocks) * row_capacity * block_stride +
+                                               i * bit_stride);
+    for (int32_t w = 0; w < (bit_stride >> 2); ++w) {
+      uint32_t word = 0u;
+      for (int32_t t = 0; t < 32; ++t) {
+        const int32_t kk = 32 * w + t;
+        if (kk >= n_bit) break;
+        int32_t f = col_feature[nbc + kk];
+        f = f < 0 ? 0 : (f >= F ? F - 1 : f);
+        const uint8_t x = src[i * F + f];
+        bad |= (int32_t)x >= n_bins[f] || x > 1;
+        word |= uint32_t(x & 1) << t;
+      }
+      wd[w] = word;
     }
   }
   if (bad) dev_error(&ctrl->err, GBDT_E_RANGE);
@@ -1306,12 +1565,26 @@ static int check_matrix(const gbdt_matrix& X) {
   if (X.n_rows < 0 || X.n_rows > 0x7fffffffLL) return fail(GBDT_E_ARG, "n_rows out of range");
   if (X.row_capacity < X.n_rows) return fail(GBDT_E_SHAPE, "row_capacity < n_rows");
   if (X.n_features < 1 || X.n_features > GBDT_MAX_FEATURES) return fail(GBDT_E_ARG, "n_features out of range");
-  if (X.block_features < 1 || X.block_stride < X.block_features || (X.block_stride & 3) ||
-      X.block_stride > 1024)
-    return fail(GBDT_E_ARG, "bad block_features / block_stride");
-  if (int64_t(X.n_blocks) * X.block_features < X.n_features ||
-      int64_t(X.n_blocks - 1) * X.block_features >= X.n_features)
-    return fail(GBDT_E_SHAPE, "n_blocks does not match n_features / block_features");
+  if (X.n_bit_features < 0 || X.n_bit_features > X.n_features)
+    return fail(GBDT_E_ARG, "n_bit_features out of range");
+  if ((X.col_feature == nullptr) != (X.feature_col == nullptr))
+    return fail(GBDT_E_ARG, "col_feature and feature_col must both be set or both be NULL");
+  if (X.col_feature == nullptr && X.n_bit_features != 0)
+    return fail(GBDT_E_ARG, "a bit block needs the column maps");
+  const int32_t nbc = X.n_features - X.n_bit_features;
+  if (nbc > 0) {
+    if (X.block_features < 1 || X.block_stride < X.block_features || (X.block_stride & 3) ||
+        X.block_stride > 1024)
+      return fail(GBDT_E_ARG, "bad block_features / block_stride");
+    if (int64_t(X.n_blocks) * X.block_features < nbc || int64_t(X.n_blocks - 1) * X.block_features >= nbc)
+      return fail(GBDT_E_SHAPE, "n_blocks does not match the byte columns / block_features");
+  } else if (X.n_blocks != 0) {
+    return fail(GBDT_E_SHAPE, "n_blocks must be 0 when every feature is a bit");
+  }
+  if (X.n_bit_features > 0 &&
+      (X.bit_stride < 4 * ((X.n_bit_features + 31) / 32) || (X.bit_stride & 3) ||
+       X.bit_stride > 4 * kMaxBitWords))
+    return fail(GBDT_E_ARG, "bad bit_stride");
   if (!aligned(X.bins, 4)) return fail(GBDT_E_ARG, "bins not 4-byte aligned");
   return GBDT_OK;
 }
@@ -1324,6 +1597,14 @@ static int check_features(const gbdt_features& ft, int32_t n_features) {
   return GBDT_OK;
 }
 
+
+bool same_layout(const gbdt_matrix& a, const gbdt_matrix& b) {
+  return a.n_rows == b.n_rows && a.row_capacity == b.row_capacity && a.n_features == b.n_features &&
+         a.n_blocks == b.n_blocks && a.block_features == b.block_features &&
+         a.block_stride == b.block_stride && a.n_bit_features == b.n_bit_features &&
+         a.bit_stride == b.bit_stride && a.col_feature == b.col_feature &&
+         a.feature_col == b.feature_col;
+}
 
 int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft) {
   int rc = check_matrix(src.X);
@@ -1343,10 +1624,7 @@ int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst) {
   if (rc) return rc;
   rc = check_matrix(dst.X);
   if (rc) return rc;
-  if (src.X.n_blocks != dst.X.n_blocks || src.X.block_stride != dst.X.block_stride ||
-      src.X.block_features != dst.X.block_features || src.X.row_capacity != dst.X.row_capacity ||
-      src.X.n_rows != dst.X.n_rows)
-    return fail(GBDT_E_SHAPE, "source and destination layouts differ");
+  if (!same_layout(src.X, dst.X)) return fail(GBDT_E_SHAPE, "source and destination layouts differ");
   if (!src.q || !dst.q) return fail(GBDT_E_ARG, "q pointer is null");
   return GBDT_OK;
 }
@@ -1358,14 +1636,17 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
   const int32_t bits = pack_bits_for(n_rows);
   const int64_t q_bound = int64_t(1) << (52 - ceil_log2(n_rows));
   const size_t lds = sizeof(uint64_t) * size_t(ft.max_block_bins + kLdsHistSlack);
-  const int unit = load_unit_for(src.X.block_stride);
-  auto kern = unit == 16 ? k_hist<16> : (unit == 8 ? k_hist<8> : k_hist<4>);
+  const int unit = src.X.n_blocks > 0 ? load_unit_for(src.X.block_stride) : 4;
+  const bool has_bits = src.X.n_bit_features > 0;
+  auto kern = has_bits ? (unit == 16 ? k_hist<16, true> : (unit == 8 ? k_hist<8, true> : k_hist<4, true>))
+                       : (unit == 16 ? k_hist<16, false> : (unit == 8 ? k_hist<8, false> : k_hist<4, false>));
+  const unsigned gy = (unsigned)(src.X.n_blocks + (has_bits ? 1 : 0));
   diag_begin(kDiagHist, s);
-  hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles, (unsigned)src.X.n_blocks), dim3(kHistThreads),
-                     lds, s, src.X.bins, src.X.row_capacity, src.X.block_features,
-                     src.X.block_stride, src.X.n_features, src.q, ft.bin_offset, ft.skip_bin,
-                     ft.total_bins, ft.max_block_bins, desc, bits, q_bound, hist_g, hist_cnt, hpart,
-                     ctrl);
+  hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles, gy), dim3(kHistThreads), lds, s, src.X.bins,
+                     src.X.row_capacity, src.X.n_blocks, src.X.block_features, src.X.block_stride,
+                     src.X.n_features, src.X.n_bit_features, src.X.bit_stride, src.X.col_feature,
+                     src.q, ft.bin_offset, ft.skip_bin, ft.total_bins, ft.max_block_bins, desc, bits,
+                     q_bound, hist_g, hist_cnt, hpart, ctrl);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist");
   return GBDT_OK;
@@ -1410,13 +1691,13 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
 
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, hipStream_t s) {
-  const int unit = load_unit_for(src.X.block_stride);
+  const int unit = src.X.n_blocks > 0 ? load_unit_for(src.X.block_stride) : 4;
   auto kern = unit == 16 ? k_partition<16> : (unit == 8 ? k_partition<8> : k_partition<4>);
   diag_begin(kDiagPartition, s);
   hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s, src.X.bins, src.q,
                      src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
-                     src.X.block_features, src.X.block_stride, src.X.n_features, desc, status,
-                     ctrl);
+                     src.X.block_features, src.X.block_stride, src.X.n_features,
+                     src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_partition");
   return GBDT_OK;
@@ -1493,31 +1774,69 @@ size_t gbdt_workspace_bytes(int64_t n_rows, int32_t max_list, int32_t total_bins
   return ws_layout(n_rows, max_list, total_bins).total;
 }
 
+int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t pack_bits,
+                       gbdt_matrix* X, int32_t* max_block_bins, int32_t* col_feature_host,
+                       int32_t* feature_col_host) {
+  if (!X || !n_bins_host || !max_block_bins || !col_feature_host || !feature_col_host)
+    return fail(GBDT_E_ARG, "null argument");
+  if (n_features < 1 || n_features > GBDT_MAX_FEATURES) return fail(GBDT_E_ARG, "n_features out of range");
+  for (int32_t f = 0; f < n_features; ++f)
+    if (n_bins_host[f] < 1 || n_bins_host[f] > GBDT_MAX_BINS) return fail(GBDT_E_ARG, "n_bins out of range");
+  // byte columns first (feature order), then the bit features (feature order)
+  std::vector<int32_t> cols;
+  int32_t n_bit = 0;
+  for (int32_t f = 0; f < n_features; ++f)
+    if (!(pack_bits && n_bins_host[f] <= 2)) cols.push_back(f);
+  const int32_t nbc = (int32_t)cols.size();
+  for (int32_t f = 0; f < n_features; ++f)
+    if (pack_bits && n_bins_host[f] <= 2) {
+      cols.push_back(f);
+      ++n_bit;
+    }
+  if (2 * n_bit > kLdsHistBudgetBins) return fail(GBDT_E_UNSUPPORTED, "too many bit features for the LDS budget");
+  int32_t worst = 2 * n_bit;
+  int32_t bf = 0, nb = 0;
+  if (nbc > 0) {
+    // fewest blocks of equal width (<= 64 columns) whose bins fit the budget
+    bool found = false;
+    for (nb = 1; nb <= nbc && !found; ++nb) {
+      bf = (nbc + nb - 1) / nb;
+      if (bf > 64) continue;
+      int32_t w = 0;
+      for (int32_t c0 = 0; c0 < nbc; c0 += bf) {
+        int32_t s = 0;
+        for (int32_t c = c0; c < c0 + bf && c < nbc; ++c) s += n_bins_host[cols[c]];
+        if (s > w) w = s;
+      }
+      if (w > kLdsHistBudgetBins) continue;
+      found = true;
+      if (w > worst) worst = w;
+    }
+    if (!found) return fail(GBDT_E_UNSUPPORTED, "no feature blocking fits the LDS budget");
+    nb = (nbc + bf - 1) / bf;
+  }
+  X->n_features = n_features;
+  X->n_blocks = nb;
+  X->block_features = bf;
+  X->block_stride = nbc > 0 ? ((bf + 3) & ~3) : 0;
+  X->n_bit_features = n_bit;
+  X->bit_stride = n_bit > 0 ? 4 * ((n_bit + 31) / 32) : 0;
+  X->col_feature = nullptr;
+  X->feature_col = nullptr;
+  for (int32_t c = 0; c < n_features; ++c) {
+    col_feature_host[c] = cols[c];
+    feature_col_host[cols[c]] = c;
+  }
+  *max_block_bins = worst;
+  return GBDT_OK;
+}
+
 int gbdt_choose_blocking(int32_t n_features, const int32_t* n_bins_host, gbdt_matrix* X,
                          int32_t* max_block_bins) {
   if (!X || !n_bins_host || !max_block_bins) return fail(GBDT_E_ARG, "null argument");
   if (n_features < 1 || n_features > GBDT_MAX_FEATURES) return fail(GBDT_E_ARG, "n_features out of range");
-  for (int32_t f = 0; f < n_features; ++f)
-    if (n_bins_host[f] < 1 || n_bins_host[f] > GBDT_MAX_BINS) return fail(GBDT_E_ARG, "n_bins out of range");
-  // fewest blocks of equal width (<= 64 features) whose bins fit the budget
-  for (int32_t nb = 1; nb <= n_features; ++nb) {
-    const int32_t bf = (n_features + nb - 1) / nb;
-    if (bf > 64) continue;
-    int32_t worst = 0;
-    for (int32_t f0 = 0; f0 < n_features; f0 += bf) {
-      int32_t s = 0;
-      for (int32_t f = f0; f < f0 + bf && f < n_features; ++f) s += n_bins_host[f];
-      if (s > worst) worst = s;
-    }
-    if (worst > kLdsHistBudgetBins) continue;
-    X->n_features = n_features;
-    X->block_features = bf;
-    X->n_blocks = (n_features + bf - 1) / bf;
-    X->block_stride = (bf + 3) & ~3;
-    *max_block_bins = worst;
-    return GBDT_OK;
-  }
-  return fail(GBDT_E_UNSUPPORTED, "no feature blocking fits the LDS budget");
+  std::vector<int32_t> cf(n_features), fc(n_features);
+  return gbdt_choose_layout(n_features, n_bins_host, 0, X, max_block_bins, cf.data(), fc.data());
 }
 
 int gbdt_read_error(void* ws, void* stream) {
@@ -1556,7 +1875,8 @@ int gbdt_pack_matrix(const uint8_t* rowmajor, const gbdt_matrix* dst, const gbdt
     diag_begin(kDiagPack, s);
     hipLaunchKernelGGL(k_pack, dim3((unsigned)grid), dim3(256), 0, s, rowmajor, n,
                        dst->n_features, dst->bins, dst->row_capacity, dst->n_blocks,
-                       dst->block_features, dst->block_stride, ft->n_bins, ctrl);
+                       dst->block_features, dst->block_stride, dst->n_bit_features,
+                       dst->bit_stride, dst->col_feature, ft->n_bins, ctrl);
     diag_end(s);
     GBDT_LAUNCH_CHECK("k_pack");
   }
@@ -1639,7 +1959,7 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap, T,
                      (int32_t)max_tiles, hprefix, hdesc, ctrl, (uint64_t*)nullptr,
-                     (const gbdt_split*)nullptr, hmulti);
+                     (const gbdt_split*)nullptr, (const int32_t*)nullptr, 0, hmulti);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
   rc = launch_hist(*src, *ft, hdesc, max_tiles, hist_g, hist_cnt, hpart, ctrl, s);
@@ -1712,7 +2032,7 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap,
                      kPartTileRows, (int32_t)max_tiles, prefix, tdesc, ctrl, status, splits,
-                     (int32_t*)nullptr);
+                     src->X.feature_col, src->X.n_features, (int32_t*)nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
   return launch_partition(*src, *dst, tdesc, status, ctrl, max_tiles, s);
@@ -1731,7 +2051,7 @@ int gbdt_update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node*
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return fail(GBDT_E_ARG, "workspace is null or misaligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(static_cast<char*>(ws));
-  const int64_t row_bytes = int64_t(X->n_blocks) * X->block_stride;
+  const int64_t row_bytes = int64_t(X->n_blocks) * X->block_stride + X->bit_stride;
   if (row_bytes > kUpdMaxRowBytes) return fail(GBDT_E_UNSUPPORTED, "rows wider than 256 bytes");
   const WsLayout L = ws_layout(n, 1, 1);
   const size_t tables = size_t(max_nodes) * sizeof(uint2) + size_t((max_nodes + 1) / 2) * sizeof(double);
@@ -1742,11 +2062,15 @@ int gbdt_update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node*
                                            sizeof(uint2) * size_t(max_nodes));
   diag_begin(kDiagUpdate, s);
   hipLaunchKernelGGL(k_compact_tree, dim3(1), dim3(1024), 0, s, nodes, n_nodes, max_nodes,
-                     X->n_features, ctab, lval);
+                     X->n_features, X->feature_col, X->n_blocks, X->block_features, X->block_stride,
+                     X->n_bit_features, ctab, lval);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_compact_tree");
-  const bool in_lds = tables <= kUpdTreeLds;
-  const size_t lds = in_lds ? tables : 0;
+  // the node table goes to LDS (8 B per node); leaf values stay in global
+  // memory (read once per row, after the walk)
+  const size_t node_table = size_t(max_nodes) * sizeof(uint2);
+  const bool in_lds = node_table <= kUpdTreeLds;
+  const size_t lds = in_lds ? node_table : 0;
   const int64_t ndw = row_bytes / 4;
   const int rows = ndw <= 16 ? 2 : 1;
   int64_t grid = (n + int64_t(kUpdThreads) * rows - 1) / (int64_t(kUpdThreads) * rows);

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GBDT_ABI_VERSION 1
+#define GBDT_ABI_VERSION 2
 #define GBDT_MAX_DEPTH 16       /* deepest tree the level loop supports */
 #define GBDT_MAX_FEATURES 4096
 #define GBDT_MAX_BINS 256       /* bins per feature */
@@ -74,14 +74,31 @@ typedef enum {
 #define GBDT_NODE_LEAF 1u
 
 /*
- * Bin matrix, column-blocked.  Features are cut into n_blocks contiguous
- * groups of block_features (the last group may be shorter).  Block b is a
- * row-major [row_capacity][block_stride] uint8 array starting at
+ * Bin matrix, column-blocked, with an optional bit block.
+ *
+ * Byte columns: the first n_features - n_bit_features columns hold one uint8
+ * bin each.  They are cut into n_blocks groups of block_features (the last
+ * group may be shorter; n_blocks is 0 when every feature is a bit).  Block b
+ * is a row-major [row_capacity][block_stride] uint8 array starting at
  * bins + b * row_capacity * block_stride; byte j of a row in block b is
- * feature b * block_features + j (bytes past the block's features are
- * padding).  block_stride is a multiple of 4, so each row of a block is a run
- * of whole dwords that consecutive lanes load with coalesced accesses.
- * Host struct holding a device pointer.
+ * byte column c = b * block_features + j (bytes past the block's columns are
+ * padding, 0).  block_stride is a multiple of 4, so each row of a block is a
+ * run of whole dwords that consecutive lanes load with coalesced accesses.
+ *
+ * Bit block (n_bit_features > 0): features with at most 2 bins stored as one
+ * bit each (the idea of the ExaBoost PR's commit that packs two 4-bit cells
+ * per byte when every column has at most 16 bins, taken to 1 bit for binary
+ * features).  It is a row-major [row_capacity][bit_stride] array of uint32
+ * words starting right after the byte blocks, at
+ * bins + n_blocks * row_capacity * block_stride; bit k of a row (the k-th bit
+ * feature) is bit (k & 31) of word k >> 5.  bit_stride is a multiple of 4 and
+ * at least 4 * ceil(n_bit_features / 32).
+ *
+ * col_feature (device, [n_features]) names the feature of byte column c
+ * (c < n_features - n_bit_features), then of bit k (entry
+ * n_features - n_bit_features + k); feature_col (device, [n_features]) is its
+ * inverse.  Both NULL means the identity (byte column c is feature c), which
+ * requires n_bit_features == 0.  Host struct holding device pointers.
  */
 typedef struct gbdt_matrix {
   uint8_t* bins;
@@ -91,6 +108,10 @@ typedef struct gbdt_matrix {
   int32_t n_blocks;
   int32_t block_features;
   int32_t block_stride;
+  int32_t n_bit_features;
+  int32_t bit_stride;
+  const int32_t* col_feature;
+  const int32_t* feature_col;
 } gbdt_matrix;
 
 /*
@@ -101,8 +122,8 @@ typedef struct gbdt_matrix {
  * derives from the node total instead of accumulating (the most frequent bin,
  * set by gbdt_pack_matrix), or -1.  The choice changes speed only, never a
  * bit of the result.  max_block_bins sizes the histogram kernel's LDS; it
- * must be at least the bin count of every feature block (written by
- * gbdt_choose_blocking).
+ * must be at least the bin count of every byte block and 2 per bit feature
+ * (written by gbdt_choose_blocking / gbdt_choose_layout).
  */
 typedef struct gbdt_features {
   int32_t n_features;
@@ -204,17 +225,33 @@ size_t gbdt_workspace_bytes(int64_t n_rows, int32_t max_list, int32_t total_bins
 
 /*
  * Column blocking for features with n_bins_host[f] bins (host array): writes
- * n_features, n_blocks, block_features and block_stride of *X and
- * *max_block_bins, so that one block holds at most 64 features and its
- * histogram fits a workgroup's LDS budget (7680 bins).
+ * n_features, n_blocks, block_features and block_stride of *X (no bit block:
+ * n_bit_features 0, identity columns, NULL maps) and *max_block_bins, so that
+ * one block holds at most 64 features and its histogram fits a workgroup's
+ * LDS budget (7680 bins).
  */
 int gbdt_choose_blocking(int32_t n_features, const int32_t* n_bins_host, gbdt_matrix* X /* host */,
                          int32_t* max_block_bins /* host */);
 
 /*
+ * Layout with a bit block: with pack_bits != 0 every feature of at most 2
+ * bins becomes a bit (in feature order) and the others byte columns (in
+ * feature order); with pack_bits == 0 as gbdt_choose_blocking.  Writes the
+ * layout fields of *X (the map pointers are left NULL: the caller uploads
+ * col_feature_host / feature_col_host, host arrays of n_features entries that
+ * this call fills, and stores the device copies in X), and *max_block_bins
+ * (the LDS slots one histogram workgroup needs: the largest byte block's
+ * bins, or 2 per bit feature for the bit block).
+ */
+int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t pack_bits,
+                       gbdt_matrix* X /* host */, int32_t* max_block_bins /* host */,
+                       int32_t* col_feature_host /* host */, int32_t* feature_col_host /* host */);
+
+/*
  * Packs a row-major uint8 [n_rows][n_features] bin matrix (device) into the
  * column-blocked layout of *dst (dst->bins allocated by the caller with
- * n_blocks * row_capacity * block_stride bytes), checks every bin against
+ * n_blocks * row_capacity * block_stride + row_capacity * bit_stride bytes;
+ * bit features must have at most 2 bins), checks every bin against
  * n_bins (a violation sets GBDT_E_RANGE in the error word) and writes
  * ft->skip_bin (most frequent bin of each feature, smallest on ties).
  * Setup step, not part of the per-tree path.

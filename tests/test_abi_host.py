@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
         assert name in names
     for name in names:
         assert hasattr(lib, name), name
-    assert g.gbdt_abi_version() == 1
+    assert g.gbdt_abi_version() == 2
 
 
 def test_library_is_not_linked_to_the_oracle():
@@ -61,6 +61,61 @@ def test_blocking_fits_budget(nbins):
     assert X.block_stride % 4 == 0 and X.block_stride >= X.block_features and X.block_features <= 64
     worst = max(sum(nbins[f0:f0 + X.block_features]) for f0 in range(0, F, X.block_features))
     assert mbb == worst <= 7680
+
+
+@pytest.mark.parametrize("nbins", [[256] * 10 + [2] * 44, [2, 256, 1, 13, 2, 64, 2] * 9, [2] * 200,
+                                   [1] * 5, [64] * 28, [256] * 100 + [2] * 3])
+def test_layout_with_bits(nbins):
+    X, mbb, cf, fc = g.gbdt_choose_layout(nbins, pack_bits=True)
+    F = len(nbins)
+    bits = [f for f in range(F) if nbins[f] <= 2]
+    byte = [f for f in range(F) if nbins[f] > 2]
+    assert X.n_bit_features == len(bits)
+    # byte columns first, then bits, each in feature order; fc is the inverse
+    assert list(cf) == byte + bits
+    assert all(cf[fc[f]] == f for f in range(F)) and sorted(cf) == list(range(F))
+    nbc = len(byte)
+    if nbc:
+        assert X.n_blocks * X.block_features >= nbc > (X.n_blocks - 1) * X.block_features
+        assert X.block_stride % 4 == 0 and X.block_stride >= X.block_features and X.block_features <= 64
+        worst = max(sum(nbins[cf[c]] for c in range(c0, min(c0 + X.block_features, nbc)))
+                    for c0 in range(0, nbc, X.block_features))
+    else:
+        assert X.n_blocks == 0
+        worst = 0
+    if bits:
+        assert X.bit_stride % 4 == 0 and X.bit_stride >= 4 * ((len(bits) + 31) // 32)
+    assert mbb == max(worst, 2 * len(bits)) <= 7680
+    # without bits: identity columns, as gbdt_choose_blocking
+    X0, mbb0, cf0, _ = g.gbdt_choose_layout(nbins, pack_bits=False)
+    Xb, mbbb = g.gbdt_choose_blocking(nbins)
+    assert X0.n_bit_features == 0 and list(cf0) == list(range(F))
+    assert (X0.n_blocks, X0.block_features, X0.block_stride, mbb0) == \
+        (Xb.n_blocks, Xb.block_features, Xb.block_stride, mbbb)
+
+
+def test_bit_layout_checks():
+    lib = g.load()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: rejected on the host
+    ft = g.Features(4, 10, 16, 0, fake, fake, fake, None)
+    # 2 byte columns + 2 bits: maps required, bit_stride >= 4, n_blocks matching the byte columns
+    ok = g.Matrix(fake, 100, 100, 4, 1, 2, 4, 2, 4, fake, fake)
+    rc = lib.gbdt_build_histograms(ctypes.byref(g.Rows(ok, fake, None)), ctypes.byref(ft), fake, fake,
+                                   fake, 4, 100, fake, fake, fake, 16, None)
+    assert rc == -1 and "workspace" in g.last_error()  # the layout itself passed
+    bad = [
+        (g.Matrix(fake, 100, 100, 4, 1, 2, 4, 2, 4, None, None), -1),   # bits without maps
+        (g.Matrix(fake, 100, 100, 4, 1, 2, 4, 2, 4, fake, None), -1),   # one map only
+        (g.Matrix(fake, 100, 100, 4, 1, 2, 4, 2, 0, fake, fake), -1),   # bit_stride too small
+        (g.Matrix(fake, 100, 100, 4, 1, 2, 4, 2, 6, fake, fake), -1),   # bit_stride not a multiple of 4
+        (g.Matrix(fake, 100, 100, 4, 2, 2, 4, 2, 4, fake, fake), -2),   # blocks beyond the byte columns
+        (g.Matrix(fake, 100, 100, 4, 1, 2, 4, 4, 4, fake, fake), -2),   # all bits but a byte block
+        (g.Matrix(fake, 100, 100, 4, 1, 2, 4, 5, 4, fake, fake), -1),   # more bits than features
+    ]
+    for X, code in bad:
+        rc = lib.gbdt_build_histograms(ctypes.byref(g.Rows(X, fake, None)), ctypes.byref(ft), fake, fake,
+                                       fake, 4, 100, fake, fake, fake, 1 << 30, None)
+        assert rc == code, (X.n_blocks, X.n_bit_features, X.bit_stride, rc, g.last_error())
 
 
 def test_blocking_rejects_bad_bins():

@@ -71,15 +71,16 @@ HIST_CASES = [
 
 @pytest.mark.parametrize("case", HIST_CASES, ids=[c[0] for c in HIST_CASES])
 @pytest.mark.parametrize("use_skip", [True, False])
-def test_build_histograms(case, use_skip):
+@pytest.mark.parametrize("pack_bits", [True, False])
+def test_build_histograms(case, use_skip, pack_bits):
     name, n, nbins, segs, seed = case
-    say("build_histograms %s skip=%s" % (name, use_skip))
+    say("build_histograms %s skip=%s bits=%s" % (name, use_skip, pack_bits))
     bins, label, nb = datagen.make_random(n, nbins, seed, bin_kind=1)
     rng = np.random.default_rng(seed)
     pred = rng.normal(size=n)
     k, S, _ = oracle.gradient_grid(pred, label)
     perm = rng.permutation(n).astype(np.int32)
-    ft = g.FeatureTable(nb, DEV)
+    ft = g.FeatureTable(nb, DEV, pack_bits=pack_bits)
     # skip bins from the whole matrix (the pack step's census)
     rb_full = packed_rows(bins, ft)
     if not use_skip:
@@ -237,14 +238,16 @@ def test_find_best_splits(case):
 # ------------------------------------------------------------------ partition --
 
 @pytest.mark.parametrize("n,nbins,seed", [(50000, [2, 256, 13, 64, 2, 2, 9], 31), (20011, [256] * 70, 32),
-                                          (3, [4], 33)])
-def test_partition_rows(n, nbins, seed):
-    say("partition n=%d F=%d" % (n, len(nbins)))
+                                          (3, [4], 33), (30000, [256] * 10 + [2] * 44, 34),
+                                          (9000, [2] * 40 + [1] * 3, 35)])
+@pytest.mark.parametrize("pack_bits", [True, False])
+def test_partition_rows(n, nbins, seed, pack_bits):
+    say("partition n=%d F=%d bits=%s" % (n, len(nbins), pack_bits))
     bins, label, nb = datagen.make_random(n, nbins, seed, bin_kind=1)
     rng = np.random.default_rng(seed)
     k = rng.integers(-2**30, 2**30, size=n)
     perm = rng.permutation(n).astype(np.int32)
-    ft = g.FeatureTable(nb, DEV)
+    ft = g.FeatureTable(nb, DEV, pack_bits=pack_bits)
     src = packed_rows(bins[perm], ft, q=k[perm], rid=perm)
     dst = packed_rows(np.zeros_like(bins), ft, q=np.full(n, -5, dtype=np.int64), rid=np.full(n, -9, dtype=np.int32))
     # segments: a few nodes, some listed (split), some not
@@ -332,10 +335,12 @@ def _route(nodes, bins):
 
 
 @pytest.mark.parametrize("n,nbins,depth,seed", [(70001, [2, 64, 256, 7, 33], 7, 8), (5000, [256] * 70, 5, 9),
-                                                (1, [4], 3, 10)])
-def test_update_predictions(n, nbins, depth, seed):
+                                                (1, [4], 3, 10), (40000, [256] * 10 + [2] * 44, 8, 11),
+                                                (3000, [2] * 37, 6, 12)])
+@pytest.mark.parametrize("pack_bits", [True, False])
+def test_update_predictions(n, nbins, depth, seed, pack_bits):
     """Step 7 by routing every row through the finished tree."""
-    say("update_predictions n=%d" % n)
+    say("update_predictions n=%d bits=%s" % (n, pack_bits))
     rng = np.random.default_rng(seed)
     bins, label, nb = datagen.make_random(n, nbins, seed, bin_kind=1)
     nodes = _random_tree(rng, len(nbins), nb, depth)
@@ -344,7 +349,7 @@ def test_update_predictions(n, nbins, depth, seed):
     leaf = _route(nodes, bins)
     w = np.array([nd.get("leaf_value", 0.0) for nd in nodes])
     expect = pred + eta * w[leaf]
-    ft = g.FeatureTable(nb, DEV)
+    ft = g.FeatureTable(nb, DEV, pack_bits=pack_bits)
     X = packed_rows(bins, ft)
     dpred = to_dev(pred)
     ws = _ws(n, 1, 1)
@@ -443,14 +448,14 @@ def test_repeat_runs_are_bit_identical():
     assert outs[0] == outs[1]
 
 
-def test_skip_bins_do_not_change_bits():
-    say("skip bins on/off")
-    bins, label, nb = datagen.make_random(25000, [256, 2, 2, 64, 8], 52, bin_kind=1, label_kind=2)
+def test_skip_bins_and_bit_layout_do_not_change_bits():
+    say("skip bins on/off, bit block on/off")
+    bins, label, nb = datagen.make_random(25000, [256, 2, 2, 64, 8, 1, 2], 52, bin_kind=1, label_kind=2)
     pk = dict(max_depth=5)
     res = []
-    for use_skip in (True, False):
-        ds = g.Dataset(bins, label, nb, DEV, use_skip_bins=use_skip)
+    for use_skip, pack_bits in ((True, True), (False, True), (True, False), (False, False)):
+        ds = g.Dataset(bins, label, nb, DEV, use_skip_bins=use_skip, pack_bits=pack_bits)
         bst = g.Booster(ds, g.make_params(**pk)).train(2)
         bst.check()
         res.append((b"".join(t.tobytes() for t in bst.host_trees()), bst.pred.cpu().numpy().tobytes()))
-    assert res[0] == res[1]
+    assert res[0] == res[1] == res[2] == res[3]
