@@ -48,6 +48,48 @@ __device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* total, int32_
   return res;
 }
 
+// Exclusive scans of K int32 values per thread across a workgroup at once
+// (one pair of barriers for all K).  sh: LDS [K * 17].
+template <int K>
+__device__ inline void block_exclusive_scan_multi(const int32_t (&v)[K], int32_t (&excl)[K],
+                                                  int32_t (&total)[K], int32_t* sh) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int nw = (blockDim.x + 63) >> 6;
+  int32_t x[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) x[k] = v[k];
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int32_t y = __shfl_up(x[k], off, 64);
+      if (lane >= off) x[k] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) sh[k * 17 + wid] = x[k];
+  }
+  __syncthreads();
+  if (threadIdx.x < K) {
+    const int k = threadIdx.x;
+    int32_t acc = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int32_t t = sh[k * 17 + w];
+      sh[k * 17 + w] = acc;
+      acc += t;
+    }
+    sh[k * 17 + 16] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    excl[k] = sh[k * 17 + wid] + x[k] - v[k];
+    total[k] = sh[k * 17 + 16];
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ int32_t clamp_len(const int32_t* len, int32_t cap) {
   int32_t n = *len;
   return n < 0 ? 0 : (n > cap ? cap : n);
@@ -80,6 +122,61 @@ __device__ __forceinline__ int32_t split_column(const gbdt_split& sp, const int3
 __device__ __forceinline__ int32_t tiles_of(int32_t c, int32_t tile_rows) {
   if (c < 0) c = 0;
   return c == 0 ? 1 : (c + tile_rows - 1) / tile_rows;
+}
+
+// Second half of a tile plan, from entries already staged in LDS: stage[j]
+// the j-th list entry and spre[0..n] the exclusive prefix of its tiles
+// (spre[n] = total), both visible to the workgroup.  Writes prefix[0..n],
+// the multi-tile list (multi != nullptr), the plan total, ticket and cleared
+// look-back status (status != nullptr) and every tile's descriptor (from LDS
+// only), then descriptors with node -1 up to max_tiles.  with_split: the
+// entries carry a split (partition plans).  *n_multi (LDS) must be 0 and
+// visible, like the staged entries.
+__device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, int32_t* n_multi,
+                                 int32_t n, int32_t tile_rows, int32_t max_tiles,
+                                 int32_t* __restrict__ prefix, TileDesc* __restrict__ desc,
+                                 uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
+                                 bool with_split, int32_t* __restrict__ multi) {
+  const int32_t total = spre[n];
+  for (int32_t j = threadIdx.x; j <= n; j += blockDim.x) {
+    prefix[j] = spre[j];
+    if (multi != nullptr && j < n && spre[j + 1] - spre[j] > 1) multi[1 + atomicAdd(n_multi, 1)] = j;
+  }
+  if (threadIdx.x == 0) {
+    if (total > max_tiles) dev_error(&ctrl->err, GBDT_E_SHAPE);
+    if (status != nullptr) {
+      ctrl->plan_total = total < max_tiles ? total : max_tiles;
+      ctrl->ticket = 0u;
+    }
+  }
+  const int32_t lim = total < max_tiles ? total : max_tiles;
+  for (int32_t t = threadIdx.x; t < lim; t += blockDim.x) {
+    int32_t lo = 0, hi = n - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (spre[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const PlanEntry pe = stage[lo];
+    const int32_t tf = spre[lo];
+    TileDesc d;
+    d.node = pe.node;
+    d.r0 = pe.begin + (t - tf) * tile_rows;
+    d.r1 = d.r0 + tile_rows < pe.begin + pe.count ? d.r0 + tile_rows : pe.begin + pe.count;
+    d.ntiles = spre[lo + 1] - tf;
+    d.tfirst = tf;
+    d.j = lo;
+    d.begin = pe.begin;
+    d.count = pe.count;
+    d.feature = pe.feature;
+    d.threshold_bin = pe.threshold_bin;
+    d.n_left = pe.n_left;
+    d.split_valid = with_split && pe.feature >= 0;
+    desc[t] = d;
+    if (status != nullptr) status[t] = 0ull;
+  }
+  for (int32_t t = lim + threadIdx.x; t < max_tiles; t += blockDim.x) desc[t].node = -1;
+  __syncthreads();
+  if (threadIdx.x == 0 && multi != nullptr) multi[0] = *n_multi;
 }
 
 // Tile plan of the nodes list[0..n), run by every thread of one workgroup:
@@ -133,10 +230,23 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
   if (threadIdx.x == 0) L.n_multi = 0;
   int32_t total;
   int32_t excl = block_exclusive_scan(local, &total, L.sh);
+  if (staged) {
+    for (int32_t j = j0; j < j0 + per && j < n; ++j) {
+      L.spre[j] = excl;
+      excl += tiles_of(L.stage[j].count, tile_rows);
+    }
+    if (threadIdx.x == 0) L.spre[n] = total;
+    __syncthreads();
+    plan_emit(L.stage, L.spre, &L.n_multi, n, tile_rows, max_tiles, prefix, desc, status, ctrl,
+              splits != nullptr, multi);
+    return;
+  }
+  // long lists: the prefix in LDS (up to kPlanLdsEntries) or global memory,
+  // entries read from global memory
   for (int32_t j = j0; j < j0 + per && j < n; ++j) {
     prefix[j] = excl;
     if (in_lds) L.spre[j] = excl;
-    const int32_t nt = tiles_of(staged ? L.stage[j].count : nodes[list[j]].count, tile_rows);
+    const int32_t nt = tiles_of(nodes[list[j]].count, tile_rows);
     if (multi != nullptr && nt > 1) multi[1 + atomicAdd(&L.n_multi, 1)] = j;
     excl += nt;
   }
@@ -160,22 +270,18 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
       const int32_t mid = (lo + hi + 1) >> 1;
       if (pre[mid] <= t) lo = mid; else hi = mid - 1;
     }
+    const int32_t v = list[lo];
+    const gbdt_node nd = nodes[v];
     PlanEntry pe;
-    if (staged) {
-      pe = L.stage[lo];
-    } else {
-      const int32_t v = list[lo];
-      const gbdt_node nd = nodes[v];
-      pe.node = v;
-      pe.begin = nd.begin;
-      pe.count = nd.count < 0 ? 0 : nd.count;
-      pe.feature = pe.threshold_bin = pe.n_left = 0;
-      if (splits != nullptr) {
-        const gbdt_split sp = splits[v];
-        pe.feature = split_column(sp, feature_col, n_features);
-        pe.threshold_bin = sp.threshold_bin;
-        pe.n_left = sp.n_left;
-      }
+    pe.node = v;
+    pe.begin = nd.begin;
+    pe.count = nd.count < 0 ? 0 : nd.count;
+    pe.feature = pe.threshold_bin = pe.n_left = 0;
+    if (splits != nullptr) {
+      const gbdt_split sp = splits[v];
+      pe.feature = split_column(sp, feature_col, n_features);
+      pe.threshold_bin = sp.threshold_bin;
+      pe.n_left = sp.n_left;
     }
     const int32_t tf = pre[lo];
     TileDesc d;

@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t part_max_tiles, int32_t hist_tile_rows_next,
                                                 int32_t hist_max_tiles_next) {
   __shared__ PlanLds lds;
-  int32_t* sh = lds.sh;
+  __shared__ int32_t shm[6 * 17];
   const int32_t first = tc->level_start[d];
   const int32_t cnt = tc->level_count[d];
   const int32_t S = tc->scale;
@@ -175,29 +175,42 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   const int32_t i0 = threadIdx.x * per;
   int32_t i1 = i0 + per;
   if (i1 > cnt) i1 = cnt;
+  // at most one level node per thread: the plans are staged from registers
+  // (no second read of the lists, nodes and splits just written)
+  const bool fast = cnt <= (int32_t)blockDim.x;
 
-  int32_t c_split = 0, c_pair = 0, c_find = 0, c_leaf = 0;
+  // counts: splits, pairs, searched children, leaves, partition tiles,
+  // histogram tiles of the next level
+  int32_t c[6] = {0, 0, 0, 0, 0, 0};
   for (int32_t i = i0; i < i1; ++i) {
     const int32_t v = first + i;
     const gbdt_split s = splits[v];
+    const int32_t count = nodes[v].count;
     if (s.valid) {
-      const int32_t nl = s.n_left, nr = nodes[v].count - s.n_left;
-      ++c_split;
+      const int32_t nl = s.n_left, nr = count - s.n_left;
+      ++c[0];
       if (last) {
-        c_leaf += 2;
-      } else if ((int64_t)(nl > nr ? nl : nr) >= min_split) {
-        ++c_pair;
-        c_find += ((int64_t)nl >= min_split) + ((int64_t)nr >= min_split);
+        c[3] += 2;
+      } else {
+        c[4] += tiles_of(count, kPartTileRows);
+        if ((int64_t)(nl > nr ? nl : nr) >= min_split) {
+          ++c[1];
+          c[2] += ((int64_t)nl >= min_split) + ((int64_t)nr >= min_split);
+          c[5] += tiles_of(nl <= nr ? nl : nr, hist_tile_rows_next);
+        }
       }
     } else {
-      ++c_leaf;
+      ++c[3];
     }
   }
-  int32_t t_split, t_pair, t_find, t_leaf;
-  int32_t r_split = block_exclusive_scan(c_split, &t_split, sh);
-  int32_t r_pair = block_exclusive_scan(c_pair, &t_pair, sh);
-  int32_t r_find = block_exclusive_scan(c_find, &t_find, sh);
-  int32_t r_leaf = block_exclusive_scan(c_leaf, &t_leaf, sh);
+  int32_t r[6], t[6];
+  block_exclusive_scan_multi<6>(c, r, t, shm);
+  int32_t r_split = r[0], r_pair = r[1], r_find = r[2], r_leaf = r[3];
+  const int32_t t_split = t[0], t_pair = t[1], t_find = t[2], t_leaf = t[3];
+  PlanEntry* stP = lds.stage;                    // partition plan entries
+  PlanEntry* stH = lds.stage + kPlanStage / 2;   // next level's histogram plan entries
+  int32_t* spP = lds.spre;
+  int32_t* spH = lds.spre + kPlanStage;
 
   const int64_t lvl_off = (int64_t(1) << d) - 1;
   const int64_t nxt_off = (int64_t(1) << (d + 1)) - 1;
@@ -216,6 +229,17 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
       const int32_t lc = child_first + 2 * r_split;
       const int32_t rc = lc + 1;
       const int32_t nl = s.n_left, nr = nd.count - s.n_left;
+      if (fast && !last) {
+        PlanEntry pe;
+        pe.node = v;
+        pe.begin = nd.begin;
+        pe.count = nd.count < 0 ? 0 : nd.count;
+        pe.feature = split_column(s, pa.feature_col, pa.n_features);
+        pe.threshold_bin = s.threshold_bin;
+        pe.n_left = s.n_left;
+        stP[r_split] = pe;
+        spP[r_split] = r[4];
+      }
       nd.feature = s.feature;
       nd.threshold_bin = s.threshold_bin;
       nd.left = lc;
@@ -249,6 +273,15 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
         // the smaller child is built; the larger one is derived in the
         // split search (parent minus smaller)
         const int32_t sm = (nl <= nr) ? lc : rc;
+        if (fast) {
+          PlanEntry pe;
+          pe.node = sm;
+          pe.begin = sm == lc ? L.begin : R.begin;
+          pe.count = sm == lc ? nl : nr;
+          pe.feature = pe.threshold_bin = pe.n_left = 0;
+          stH[r_pair] = pe;
+          spH[r_pair] = r[5];
+        }
         build_n[r_pair] = sm;
         ++r_pair;
         if ((int64_t)nl >= min_split) {
@@ -287,15 +320,27 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
     }
     tc->n_leaves = leaf_base + t_leaf;
     *n_nodes_out = child_first + 2 * t_split;
+    if (fast) {
+      spP[t_split] = t[4];
+      spH[t_pair] = t[5];
+      lds.n_multi = 0;
+    }
   }
   if (last) return;
-  __syncthreads();  // the lists and the children's counts are visible to the workgroup
+  __syncthreads();  // the lists, the children's counts and the staged entries are visible
   // this level's partition plan (splitting nodes) and the next level's
   // histogram plan (nodes to build)
-  plan_tiles(nodes, split_list, t_split, kPartTileRows, part_max_tiles, pa.prefix, pa.desc, pa.status,
-             pa.ctrl, splits, pa.feature_col, pa.n_features, nullptr, lds);
-  plan_tiles(nodes, build_n, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix, pa.hdesc,
-             nullptr, pa.ctrl, nullptr, nullptr, 0, pa.hmulti, lds);
+  if (fast) {
+    plan_emit(stP, spP, &lds.n_multi, t_split, kPartTileRows, part_max_tiles, pa.prefix, pa.desc,
+              pa.status, pa.ctrl, true, nullptr);
+    plan_emit(stH, spH, &lds.n_multi, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix,
+              pa.hdesc, nullptr, pa.ctrl, false, pa.hmulti);
+  } else {
+    plan_tiles(nodes, split_list, t_split, kPartTileRows, part_max_tiles, pa.prefix, pa.desc,
+               pa.status, pa.ctrl, splits, pa.feature_col, pa.n_features, nullptr, lds);
+    plan_tiles(nodes, build_n, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix,
+               pa.hdesc, nullptr, pa.ctrl, nullptr, nullptr, 0, pa.hmulti, lds);
+  }
 }
 
 static int64_t min_split_count(const gbdt_params* p, int64_t n) {
