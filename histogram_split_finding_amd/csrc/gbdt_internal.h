@@ -21,6 +21,12 @@ struct WsCtrl {
 static_assert(sizeof(WsCtrl) == 256, "control block is 256 bytes");
 
 constexpr int kGradBlocks = 1024;     // grid of the gradient kernels
+// A wave's SGPRs are allocated in blocks of 16 plus a fixed 16 from an
+// 800-entry file per SIMD (measured on gfx950): kernels reporting at most 80
+// SGPRs keep eight waves per SIMD, i.e. two 1024-thread workgroups per CU;
+// 81 already drops a 1024-thread kernel to one workgroup per CU.
+#define GBDT_SGPR_CAP __attribute__((amdgpu_num_sgpr(80)))
+
 constexpr int kPartTileRows = 2048;   // rows per partition tile
 constexpr int kHistMinTileRows = 1024;
 constexpr int kHistTargetTiles = 1024;

@@ -420,7 +420,7 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
 // order) for k_hist_reduce.  BITS: the layout has a bit block (the kernel
 // without it is leaner: fewer registers and LDS).
 template <int UNIT, bool BITS>
-__global__ void __launch_bounds__(kHistThreads) k_hist(
+__global__ void GBDT_SGPR_CAP __launch_bounds__(kHistThreads) k_hist(
     const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t n_blocks,
     int32_t block_features, int32_t block_stride, int32_t n_features, int32_t n_bit,
     int32_t bit_stride, const int32_t* __restrict__ col_feature, const int64_t* __restrict__ q,
@@ -1069,7 +1069,7 @@ __device__ int64_t lookback_excl(uint64_t* status, int32_t tile, int32_t tfirst,
 // (and row ids) and copies the bins in batches of BATCH rows per lane
 // (lanes = (row group, column of UNIT bytes)).
 template <int UNIT>
-__global__ void __launch_bounds__(kPartThreads) k_partition(
+__global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const int64_t* __restrict__ sq,
     const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, int64_t* __restrict__ dq,
     int32_t* __restrict__ drid, int64_t row_capacity, int32_t n_blocks, int32_t block_features,
@@ -1331,7 +1331,7 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
 }
 
 template <int MAXDW, int ROWS, bool TREE_IN_LDS>
-__global__ void __launch_bounds__(kUpdThreads) k_update(
+__global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
     double* __restrict__ pred, int64_t n, const uint8_t* __restrict__ bins, int64_t row_capacity,
     int32_t n_blocks, int32_t block_stride, int32_t bit_stride,
     const uint2* __restrict__ ctab_g, const double* __restrict__ lval,
