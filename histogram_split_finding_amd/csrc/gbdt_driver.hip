@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t* __restrict__ lists, ListLayout LL,
                                                 int64_t min_split, double lambda,
                                                 int32_t* __restrict__ n_nodes_out, PlanArgs pa,
-                                                int32_t part_max_tiles, int32_t hist_tile_rows_next,
+                                                int32_t part_max_tiles, int32_t hist_tile_max,
                                                 int32_t hist_max_tiles_next) {
   __shared__ PlanLds lds;
   __shared__ int32_t shm[6 * 17];
@@ -179,9 +179,10 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   // (no second read of the lists, nodes and splits just written)
   const bool fast = cnt <= (int32_t)blockDim.x;
 
-  // counts: splits, pairs, searched children, leaves, partition tiles,
-  // histogram tiles of the next level
+  // counts: splits, pairs, searched children, leaves, partition tiles, rows
+  // the next level builds (the smaller child of each pair)
   int32_t c[6] = {0, 0, 0, 0, 0, 0};
+  int32_t my_small = -1;  // fast path: the smaller child's rows of this thread's pair
   for (int32_t i = i0; i < i1; ++i) {
     const int32_t v = first + i;
     const gbdt_split s = splits[v];
@@ -196,7 +197,8 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
         if ((int64_t)(nl > nr ? nl : nr) >= min_split) {
           ++c[1];
           c[2] += ((int64_t)nl >= min_split) + ((int64_t)nr >= min_split);
-          c[5] += tiles_of(nl <= nr ? nl : nr, hist_tile_rows_next);
+          c[5] += nl <= nr ? nl : nr;
+          my_small = nl <= nr ? nl : nr;
         }
       }
     } else {
@@ -205,6 +207,27 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   }
   int32_t r[6], t[6];
   block_exclusive_scan_multi<6>(c, r, t, shm);
+  // histogram tile rows of the next level from the rows it actually builds:
+  // about kHistTargetTiles tiles, none below kHistMinTileRows (or above the
+  // packed cells' limit)
+  const int32_t hist_tile_rows_next = hist_tile_rows_for(t[5], hist_tile_max);
+  {
+    int32_t nt = 0;
+    if (fast) {
+      nt = my_small >= 0 ? tiles_of(my_small, hist_tile_rows_next) : 0;
+    } else if (!last) {
+      for (int32_t i = i0; i < i1; ++i) {
+        const int32_t v = first + i;
+        const gbdt_split sp = splits[v];
+        if (!sp.valid) continue;
+        const int32_t nl = sp.n_left, nr = nodes[v].count - sp.n_left;
+        if ((int64_t)(nl > nr ? nl : nr) >= min_split) nt += tiles_of(nl <= nr ? nl : nr, hist_tile_rows_next);
+      }
+    }
+    int32_t tot;
+    r[5] = block_exclusive_scan(nt, &tot, shm);
+    t[5] = tot;
+  }
   int32_t r_split = r[0], r_pair = r[1], r_find = r[2], r_leaf = r[3];
   const int32_t t_split = t[0], t_pair = t[1], t_find = t[2], t_leaf = t[3];
   PlanEntry* stP = lds.stage;                    // partition plan entries
@@ -426,11 +449,20 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   int32_t h_rows[GBDT_MAX_DEPTH + 1];
   int64_t h_tiles[GBDT_MAX_DEPTH + 1];
   int64_t p_tiles[GBDT_MAX_DEPTH + 1];
+  // the level kernel sizes levels >= 1 from their actual rows (about
+  // kHistTargetTiles tiles of at least min(kHistMinTileRows, tile_max) rows,
+  // at most tile_max); the bound below holds for every size it can choose
+  const int32_t tile_max = hist_tile_max(n);
   for (int32_t d = 0; d <= D; ++d) {
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
     const int64_t rows_build = d == 0 ? n : n / 2;
     h_rows[d] = hist_tile_rows(rows_build, n);
-    h_tiles[d] = (rows_build + h_rows[d] - 1) / h_rows[d] + cap_build;
+    if (d == 0) {
+      h_tiles[d] = (rows_build + h_rows[d] - 1) / h_rows[d] + cap_build;
+    } else {
+      const int64_t by_max = (rows_build + tile_max - 1) / tile_max;
+      h_tiles[d] = (by_max > kHistTargetTiles ? by_max : kHistTargetTiles) + cap_build;
+    }
     p_tiles[d] = (n + kPartTileRows - 1) / kPartTileRows + (int64_t(1) << d);
     if (h_tiles[d] > WL.hpart_tiles || p_tiles[d] > WL.status_cap)
       return fail(GBDT_E_INTERNAL, "tile bound exceeds the workspace");
@@ -466,7 +498,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     diag_begin(kDiagLevel, s);
     hipLaunchKernelGGL(k_level, dim3(1), dim3(1024), 0, s, d, D, nodes_out, b->splits, tc, b->lists,
                        LL, min_split, p->reg_lambda, n_nodes_dev, pa, (int32_t)p_tiles[d],
-                       h_rows[d + 1], (int32_t)h_tiles[d + 1]);
+                       tile_max, (int32_t)h_tiles[d + 1]);
     diag_end(s);
     {
       hipError_t e = hipGetLastError();

@@ -26,13 +26,18 @@ constexpr int kGradBlocks = 1024;     // grid of the gradient kernels
 // SGPRs keep eight waves per SIMD, i.e. two 1024-thread workgroups per CU;
 // 81 already drops a 1024-thread kernel to one workgroup per CU.
 #define GBDT_SGPR_CAP __attribute__((amdgpu_num_sgpr(80)))
+// Eight waves per SIMD (two 1024-thread workgroups per CU) also caps a
+// wave at 64 VGPRs (512 per SIMD lane); the attribute makes the register
+// allocator hold to that.
+#define GBDT_TWO_GROUPS __attribute__((amdgpu_waves_per_eu(8, 8)))
 
 constexpr int kPartTileRows = 2048;   // rows per partition tile
 constexpr int kHistMinTileRows = 1024;
 constexpr int kHistTargetTiles = 1024;
 constexpr int kReduceNodeSlots = 64;  // y extent of the partial-reduction grid
-constexpr int kLdsHistBudgetBins = 7680;  // histogram bins per feature block (60 KiB of LDS)
-constexpr int kLdsHistSlack = 256;         // extra LDS slots: any bin byte stays inside the allocation
+constexpr int kLdsHistBudgetBins = 8192;  // LDS slots (8 bytes) of one histogram workgroup: 64 KiB
+constexpr int kHistRowSlots = 32;          // LDS slots per bin row of a byte block's histogram
+constexpr int kHistMaxBlockStride = 32;    // bytes per row of a byte block, at most (8 dwords)
 
 // Work assignment of one tile (written by the planner).  A partition plan
 // also carries the node's split, so a partition tile needs no second load.
@@ -94,6 +99,23 @@ inline int32_t pack_bits_for(int64_t n_rows) {
 }
 
 int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows);
+
+// Most rows one histogram tile may hold for n rows: the packed LDS cells
+// count a tile's rows in `bits` bits.
+inline int32_t hist_tile_max(int64_t n_rows) {
+  return int32_t((int64_t(1) << pack_bits_for(n_rows < 1 ? 1 : n_rows)) - 1);
+}
+
+// Histogram tile rows for a level that builds `rows` rows (device and host):
+// about kHistTargetTiles tiles, at least min(kHistMinTileRows, tile_max) rows
+// and at most tile_max.
+__host__ __device__ inline int32_t hist_tile_rows_for(int32_t rows, int32_t tile_max) {
+  int32_t t = (rows + kHistTargetTiles - 1) / kHistTargetTiles;
+  const int32_t lo = kHistMinTileRows < tile_max ? kHistMinTileRows : tile_max;
+  if (t < lo) t = lo;
+  if (t > tile_max) t = tile_max;
+  return t < 1 ? 1 : t;
+}
 
 // Argument checks and launches shared by the per-call entry points and the
 // tree driver (the driver's level kernel writes the tile plans itself).

@@ -232,9 +232,47 @@ __global__ void __launch_bounds__(256) k_grad_q(const double* __restrict__ pred,
   }
 }
 
+// Range check of caller-supplied fixed-point gradients (the per-call
+// histogram entry point): |q_i| <= 2^(52 - ceil(log2 n)) for every row, the
+// bound the packed LDS cells are sized for.  The tree driver's q comes from
+// k_grad_q, which meets it by construction (|g| < 2^e, so |g 2^S| < 2^(52-L)).
+__global__ void __launch_bounds__(256) k_check_q(const int64_t* __restrict__ q, int64_t n,
+                                                 int64_t bound, WsCtrl* __restrict__ ctrl) {
+  bool bad = false;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t x = q[i];
+    bad |= (x > bound) || (x < -bound);
+  }
+  if (bad) dev_error(&ctrl->err, GBDT_E_OVERFLOW);
+}
+
 // -------------------------------------------------------------- histogram --
 constexpr int kHistThreads = 1024;
-constexpr int kMaxBlockFeatures = 64;  // features per column block, at most
+// An LDS address as a pointer: a 32-bit byte address used by the ds
+// instruction as it stands (the dynamic LDS of the histogram starts at 0).
+typedef __attribute__((address_space(3))) uint64_t LdsU64;
+
+// A 64-bit value moved within each quad of lanes by a DPP quad_perm (CTL).
+template <int CTL>
+__device__ __forceinline__ uint64_t dpp_quad64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+// The q of batch u for every lane of a row, from the lane of its quad that
+// loaded it: quad position u (rows of 4 or 8 lanes), or u within each pair
+// (rows of 2 lanes).  u is a constant after unrolling.
+template <int D>
+__device__ __forceinline__ uint64_t quad_bcast_batch(uint64_t v, int u) {
+  constexpr bool P = D == 2;
+  switch (u & 3) {
+    case 0: return dpp_quad64<P ? 0xA0 : 0x00>(v);
+    case 1: return dpp_quad64<P ? 0xF5 : 0x55>(v);
+    case 2: return dpp_quad64<0xAA>(v);
+    default: return dpp_quad64<0xFF>(v);
+  }
+}
 
 // Vector load of UNIT bytes (4, 8 or 16) as dwords.
 template <int UNIT>
@@ -296,7 +334,7 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
                                const int32_t* __restrict__ col_feature, const int64_t* __restrict__ q,
                                const int32_t* __restrict__ bin_offset,
                                const int32_t* __restrict__ skip_bin, int32_t total_bins,
-                               int32_t lds_bins, int32_t bits, int64_t q_bound,
+                               int32_t lds_bins, int32_t bits,
                                int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
                                uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl,
                                uint64_t* lds, uint32_t* s_inv, int32_t* s_bit, uint64_t* sh_tot) {
@@ -308,7 +346,7 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
     if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
     return;
   }
-  for (int32_t b = threadIdx.x; b < lds_bins + kLdsHistSlack; b += blockDim.x) lds[b] = 0ull;
+  for (int32_t b = threadIdx.x; b < 2 * n_bit; b += blockDim.x) lds[b] = 0ull;
   for (int32_t w = threadIdx.x; w < nwords; w += blockDim.x) s_inv[w] = 0u;
   __syncthreads();
   // per bit feature: its global bins and whether its skip bin is 1
@@ -335,7 +373,6 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
   const uint32_t* __restrict__ wb = reinterpret_cast<const uint32_t*>(
       bins + int64_t(n_blocks) * row_capacity * block_stride);
   uint64_t tot = 0ull;
-  int64_t qmax = 0;
   constexpr int BATCH = 4;
   if (rg < rpi) {
     for (int64_t r = r0 + rg; r < r1; r += int64_t(BATCH) * rpi) {
@@ -352,8 +389,6 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
       for (int u = 0; u < BATCH; ++u) {
         const int64_t rr = r + int64_t(u) * rpi;
         if (rr >= r1) continue;
-        const int64_t aq = qq[u] < 0 ? -qq[u] : qq[u];
-        qmax = aq > qmax ? aq : qmax;
         const uint64_t pk = ((uint64_t)qq[u] << bits) + 1ull;
         tot += pk;
         uint32_t m = (x[u] ^ inv) & valid;
@@ -366,7 +401,6 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
       }
     }
   }
-  if (qmax > q_bound) dev_error(&ctrl->err, GBDT_E_OVERFLOW);
   const uint64_t t0 = wave_sum_dpp((w == 0 && rg < rpi) ? tot : 0ull);
   if (lane == 0) sh_tot[wid] = t0;
   __syncthreads();
@@ -406,40 +440,57 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
 }
 
 // One workgroup = one (tile of one node's rows, column block); the block
-// index n_blocks is the bit block (hist_bit_block).  Byte blocks: lanes are
-// laid out as (row group, column of UNIT bytes): a lane loads UNIT bins of a
-// row with one vector load (consecutive lanes read consecutive bytes, so a
-// wave streams contiguous memory) and adds the packed cell (q << bits) + 1 to
-// the LDS slot of each bin with a 64-bit LDS atomic.  Loads of BATCH rows are
-// issued before their atomics so each wave keeps several loads in flight.
-// The block's histogram sits in LDS column after column (a column's feature
-// is col_feature[c]).  Each feature's skip bin is not accumulated: it is set
-// afterwards to the tile total minus the feature's other bins (exact
-// integers).  A node covered by one tile writes its decoded histogram
-// straight to hist; otherwise the tile writes its packed partial (global bin
-// order) for k_hist_reduce.  BITS: the layout has a bit block (the kernel
-// without it is leaner: fewer registers and LDS).
-template <int UNIT, bool BITS>
-__global__ void GBDT_SGPR_CAP __launch_bounds__(kHistThreads) k_hist(
+// index n_blocks is the bit block (hist_bit_block).
+//
+// Byte blocks (at most 32 columns, rows of at most 8 dwords).  Lanes are
+// (row group rg, dword c of the row) with D lanes per row (D = the row's
+// dwords rounded up to a power of two); each lane loads one dword of a row
+// and adds the packed cell (q << bits) + 1 to the LDS slot of each of its 4
+// bytes with a 64-bit LDS atomic.  The LDS histogram is bank-skewed: the
+// slot of (copy k, column j, bin b) is 32 b + 4 D k + j, so a slot's bank
+// pair (slot mod 16 for 8-byte slots) does not depend on the bin.  gfx950
+// serves a wave's 64-bit LDS atomic one quarter-wave (16 lanes) at a time
+// and a quarter takes as many passes as lanes meet on one bank pair; each
+// lane therefore walks its 4 bytes in a rotated order (byte (m + rot) & 3 in
+// step m) chosen so that the 16 lanes of every quarter-wave always address
+// 16 different bank pairs, whatever the bin values (a hot bin included):
+//   D = 8: rot = (rg & 1) + 2 (c >> 2), one copy (32 columns);
+//   D = 4: rot = rg & 3, one copy;
+//   D = 2 or 1: rot = rg & 3 and 4 / D copies picked by (rg >> 2), summed at
+//   the end.
+// The slot's byte address, bin * 256 + lane offset, is one v_perm_b32 of the
+// row dword and a register holding the lane's four offsets.  Rows past the
+// tile end add 0; lanes past the row's dwords and padding bytes (always 0)
+// land in columns that are never read.  256 bin rows are allocated, so any
+// byte value stays inside the allocation; the first lds_bins / 32 rows are
+// zeroed and read back.  A node covered by one tile writes its decoded
+// histogram straight to hist; otherwise the tile writes its packed partial
+// (global bin order) for k_hist_reduce.  BITS: the layout has a bit block.
+template <int D, bool BITS>
+__global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_hist(
     const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t n_blocks,
     int32_t block_features, int32_t block_stride, int32_t n_features, int32_t n_bit,
     int32_t bit_stride, const int32_t* __restrict__ col_feature, const int64_t* __restrict__ q,
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ skip_bin,
     int32_t total_bins, int32_t lds_bins, const TileDesc* __restrict__ desc, int32_t bits,
-    int64_t q_bound, int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
+    int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
     uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl) {
-  constexpr int NB = UNIT;                 // bins per lane per row
-  constexpr int BATCH = UNIT == 4 ? 4 : 32 / UNIT;  // rows per lane per step (4, 4, 2)
+  static_assert(D == 1 || D == 2 || D == 4 || D == 8, "lanes per row");
+  constexpr int RPW = 64 / D;               // rows per wave per batch
+  constexpr int RPI = kHistThreads / D;     // rows per workgroup per batch
+  constexpr int BATCH = D >= 4 ? D : 4;     // batches per step (1024 rows a step for D >= 4)
+  constexpr int NCOPY = D >= 4 ? 1 : 4 / D; // histogram copies (bank skew of narrow rows)
+  constexpr int W = 4 * D;                  // slots of one copy in a bin row
   constexpr int NW = kHistThreads / 64;
+  // All LDS is dynamic, so the histogram slots start at LDS address 0 and a
+  // v_perm result is the atomic's address as it stands; the small tables
+  // follow the kLdsHistBudgetBins slots.
   extern __shared__ uint64_t lds[];
-  __shared__ uint64_t sh_tot[NW];
-  __shared__ int32_t s_fbase[kMaxBlockFeatures + 1];
-  __shared__ int32_t s_fbins[kMaxBlockFeatures];
-  __shared__ int32_t s_fskip[kMaxBlockFeatures];
-  __shared__ int32_t s_fgb[kMaxBlockFeatures];
-  __shared__ uint64_t s_slice[kHistThreads / 64][kMaxBlockFeatures];
-  __shared__ uint32_t s_inv[kMaxBitWords];
-  __shared__ int32_t s_bit[kBitStage];
+  uint64_t* const sh_tot = lds + kLdsHistBudgetBins;                        // [NW]
+  int32_t* const s_fbins = reinterpret_cast<int32_t*>(sh_tot + NW);        // [kHistRowSlots]
+  int32_t* const s_fgb = s_fbins + kHistRowSlots;                          // [kHistRowSlots]
+  uint32_t* const s_inv = reinterpret_cast<uint32_t*>(s_fgb + kHistRowSlots);  // [kMaxBitWords]
+  int32_t* const s_bit = reinterpret_cast<int32_t*>(s_inv + kMaxBitWords);  // [kBitStage]
   const int32_t tile = blockIdx.x;
   const int32_t blk = blockIdx.y;
   const TileDesc td = desc[tile];
@@ -451,157 +502,183 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kHistThreads) k_hist(
     }
     hist_bit_block<NW>(td, tile, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
                        bit_stride, col_feature, q, bin_offset, skip_bin, total_bins, lds_bins, bits,
-                       q_bound, hist_g, hist_cnt, partial, ctrl, lds, s_inv, s_bit, sh_tot);
+                       hist_g, hist_cnt, partial, ctrl, lds, s_inv, s_bit, sh_tot);
     return;
   }
   if (blk >= n_blocks) return;
-  // Every load of the prologue is issued before the first branch (a cold
-  // cache makes each dependent round trip cost about a microsecond): the
-  // descriptor and wave 0's column table (lane j: column f0 + j).
+  // The column table (lane j of wave 0: column f0 + j) is needed only by the
+  // output, so its loads are issued here and consumed after the row loop.
   const int32_t nbc = n_features - n_bit;
   const int32_t f0 = blk * block_features;  // first byte column of the block
   const int32_t c1 = f0 + block_features < nbc ? f0 + block_features : nbc;
   const int32_t nf = c1 - f0;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  const int32_t tc = f0 + lane;
-  const bool tval = tc < c1;
-  int32_t tf = col_feature != nullptr ? col_feature[tval ? tc : f0] : (tval ? tc : f0);
+  const bool tval = lane < nf;
+  int32_t tf = col_feature != nullptr ? col_feature[tval ? f0 + lane : f0] : (tval ? f0 + lane : f0);
   tf = tf < 0 ? 0 : (tf >= n_features ? n_features - 1 : tf);
-  int32_t t_lo = 0, t_hi = 0, t_sk = -1;
+  int32_t t_lo = 0, t_hi = 0;
   if (wid == 0) {
     t_lo = bin_offset[tf];
     t_hi = bin_offset[tf + 1];
-    t_sk = skip_bin != nullptr ? skip_bin[tf] : -1;
   }
   asm volatile("" ::: "memory");
   if (td.node < 0) return;  // beyond the plan
-  const int32_t v = td.node;
-  const int32_t ntiles = td.ntiles;
-  const int64_t r0 = td.r0;
-  const int64_t r1 = td.r1;
-  for (int32_t b = threadIdx.x; b < lds_bins + kLdsHistSlack; b += kHistThreads) lds[b] = 0ull;
-  if (wid == 0) {
-    // exclusive prefix of the columns' bin counts: each column's LDS base
-    const int32_t cnt = tval ? t_hi - t_lo : 0;
-    int32_t x = cnt;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
-    s_fbase[lane] = x - cnt;
-    if (lane == 63) s_fbase[kMaxBlockFeatures] = x;
-    s_fbins[lane] = cnt;
-    s_fskip[lane] = tval ? t_sk : -1;
+  const int32_t rows_out = lds_bins >> 5;  // bin rows zeroed and read back (<= 256)
+  {
+    uint4* z = reinterpret_cast<uint4*>(lds);
+    for (int32_t i = threadIdx.x; i < rows_out * (kHistRowSlots / 2); i += kHistThreads)
+      z[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (wid == 0 && lane < kHistRowSlots) {
+    s_fbins[lane] = tval ? t_hi - t_lo : 0;
     s_fgb[lane] = t_lo;
   }
+  // lane roles and the four LDS byte offsets of the lane's bytes
+  const int32_t c = threadIdx.x % D;
+  const int32_t rg = threadIdx.x / D;
+  const int32_t rot = D == 8 ? (((rg & 1) + 2 * (c >> 2)) & 3) : (rg & 3);
+  const int32_t copy = NCOPY == 1 ? 0 : ((rg >> 2) & (NCOPY - 1));
+  uint32_t offs = 0u;
+  uint32_t sel[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t bm = (uint32_t)((m + rot) & 3);
+    const uint32_t off = 8u * (uint32_t)(copy * W + 4 * c + (int32_t)bm);  // < 256
+    offs |= off << (8 * m);
+    // result byte 0 = offs byte m, byte 1 = row byte bm, bytes 2-3 = 0
+    sel[m] = (uint32_t)m | ((4u + bm) << 8) | 0x0c0c0000u;
+  }
+  const int32_t nd = block_stride >> 2;  // dwords of a row (>= 1)
+  const uint32_t lane_off = 4u * (uint32_t)(c < nd ? c : nd - 1);  // loads stay inside the row
+  const int64_t r0 = td.r0;
+  const int64_t r1 = td.r1;
   __syncthreads();
-  const int32_t nbb = s_fbase[kMaxBlockFeatures];
-  if (nbb < 0 || nbb > lds_bins) {  // the LDS holds lds_bins slots (+ slack)
-    if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
-    return;
-  }
-  const int32_t lpr = block_stride / UNIT;  // lanes per row
-  const int32_t rpi = kHistThreads / lpr;   // rows per step of the workgroup
-  const int32_t col = threadIdx.x % lpr;
-  const int32_t rg = threadIdx.x / lpr;
-  // per byte of the lane's column: LDS slot base and skip bin.  Padding bytes
-  // (past the block's columns) are always 0 and get skip bin 0, so they
-  // never reach an atomic.  Bins are range-checked when the matrix is packed;
-  // here any byte value stays inside the LDS allocation (kLdsHistSlack).
-  int32_t base[NB];
-  int32_t skip[NB];
+  // A step covers RPI * BATCH rows in two halves of H batches; batch u of a
+  // step holds rows [base + u RPI, base + u RPI + RPW) of this wave.  The
+  // loop is a two-stage pipeline: while one half's atomics run, the other
+  // half's loads (already issued) are in flight, and each half reloads for
+  // the next step as soon as its atomics are issued.  Loads are
+  // unconditional: a row past the tile end reads the tile's last row (the
+  // wave's first row of the step is < r1, so it exists) and adds 0; the
+  // reload after the last step reads rows that are never used.  Loop bounds
+  // are wave-uniform.
+  constexpr int H = BATCH / 2;
+  constexpr int32_t STEP = RPI * BATCH;
+  // rows are addressed from the tile's first row: a uniform base plus a
+  // 32-bit lane offset (a tile holds < 2^24 rows of at most 32 bytes)
+  const int32_t nt = (int32_t)(r1 - r0);    // rows of the tile
+  const uint8_t* __restrict__ tb = bins + (int64_t(blk) * row_capacity + r0) * block_stride;
+  const char* __restrict__ tq = reinterpret_cast<const char*>(q + r0);
+  const int32_t first_row = wid * RPW + lane / D;  // the lane's first row in the tile
+  int32_t base = wid * RPW;
+  if (base < nt) {
+    const int32_t lr = nt - 1;
+    // q: with D >= 2 lanes per row, lane (row group, c) loads q of its row
+    // in batch c % H of the half, so one load per half serves H batches and
+    // batch u's q is taken from a lane of the same quad with a DPP move
+    // (c % H == u: quad position u, or u and u + 2 for D == 2 pairs); with
+    // D == 1 every lane loads its own row's q per batch.
+    constexpr int NQ = D >= 2 ? 1 : H;
+    uint32_t xa[H], xb[H];
+    int64_t qa[NQ], qb[NQ];
+    // Rows past the tile end are clamped to its last row and added like any
+    // other row; the exact correction after the loop subtracts those copies
+    // (packed sums are exact mod 2^64), so the loop needs no masks.  Lanes
+    // past the row's dwords reread its last dword into columns >= 4 nd,
+    // which are never read.  The empty asm takes the loaded values as
+    // operands where they are used, so the compiler can neither drop a load
+    // nor wait for it early.
+    auto load_half = [&](int32_t first, uint32_t* x, int64_t* qq) {
 #pragma unroll
-  for (int m = 0; m < NB; ++m) {
-    const int32_t j = UNIT * col + m;
-    const bool ok = (f0 + j < c1) && (rg < rpi);
-    base[m] = ok ? s_fbase[j] : 0;
-    skip[m] = ok ? s_fskip[j] : 0;
-  }
-
-  const uint8_t* __restrict__ bb = bins + int64_t(blk) * row_capacity * block_stride + UNIT * col;
-  uint64_t tot = 0ull;
-  int64_t qmax = 0;
-  if (rg < rpi) {
-    for (int64_t r = r0 + rg; r < r1; r += int64_t(BATCH) * rpi) {
-      uint32_t w[BATCH][UNIT / 4];
-      uint64_t pk[BATCH];
+      for (int u = 0; u < H; ++u) {
+        const int32_t rr = first + u * RPI + (lane / D);
+        const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
+        x[u] = *reinterpret_cast<const uint32_t*>(tb + (__umul24(rc, (uint32_t)block_stride) + lane_off));
+        if (D == 1) qq[u < NQ ? u : 0] = *reinterpret_cast<const int64_t*>(tq + (rc << 3));
+      }
+      if (D >= 2) {
+        const int32_t rr = first + (c % H) * RPI + (lane / D);
+        const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
+        qq[0] = *reinterpret_cast<const int64_t*>(tq + (rc << 3));
+      }
+    };
+    auto add_half = [&](uint32_t* x, int64_t* qq) {
+      uint64_t pkh = 0ull;
+      if (D >= 2) {
+        asm volatile("" : "+v"(qq[0]));
+        pkh = ((uint64_t)qq[0] << bits) | 1ull;
+      }
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int64_t rr = r + int64_t(u) * rpi;
-        const bool ok = rr < r1;
-        if (ok) {
-          VecLoad<UNIT>::load(bb + rr * block_stride, w[u]);
+      for (int u = 0; u < H; ++u) {
+        uint64_t pk;
+        if (D >= 2) {
+          asm volatile("" : "+v"(x[u]));
+          pk = quad_bcast_batch<D>(pkh, u);
         } else {
-#pragma unroll
-          for (int x = 0; x < UNIT / 4; ++x) w[u][x] = 0u;
+          asm volatile("" : "+v"(x[u]), "+v"(qq[u < NQ ? u : 0]));
+          pk = ((uint64_t)qq[u < NQ ? u : 0] << bits) | 1ull;
         }
-        const int64_t qq = ok ? q[rr] : 0;
-        const int64_t aq = qq < 0 ? -qq : qq;
-        qmax = aq > qmax ? aq : qmax;
-        pk[u] = ok ? ((uint64_t)qq << bits) + 1ull : 0ull;
-      }
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        if (pk[u] == 0ull) continue;  // past the tile end (a real cell is odd)
-        tot += pk[u];
-#pragma unroll
-        for (int m = 0; m < NB; ++m) {
-          const uint32_t b = (w[u][m >> 2] >> (8 * (m & 3))) & 0xffu;
-          if ((int32_t)b != skip[m])
-            __hip_atomic_fetch_add(&lds[base[m] + b], pk[u], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t a = __builtin_amdgcn_perm(x[u], offs, sel[m]);
+          __hip_atomic_fetch_add(reinterpret_cast<LdsU64*>((uintptr_t)a), pk, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
         }
       }
+    };
+    load_half(base, xa, qa);
+    load_half(base + H * RPI, xb, qb);
+    int32_t steps = 0;
+    while (true) {
+      const int32_t next = base + STEP;
+      add_half(xa, qa);
+      load_half(next, xa, qa);
+      add_half(xb, qb);
+      load_half(next + H * RPI, xb, qb);
+      ++steps;
+      base = next;
+      if (base >= nt) break;
     }
-  }
-  if (qmax > q_bound) dev_error(&ctrl->err, GBDT_E_OVERFLOW);
-  // tile total from the column-0 lanes (one per row)
-  const uint64_t t0 = wave_sum_dpp((col == 0 && rg < rpi) ? tot : 0ull);
-  if (lane == 0) sh_tot[wid] = t0;
-  __syncthreads();
-  // skip bins: tile total minus the feature's other bins.  Lane j sums bins
-  // [16 w, 16 w + 16) of column j in wave w; wave 0 adds the slices.
-  if (lane < nf) {
-    const int32_t fb = s_fbase[lane];
-    const int32_t fn = s_fbins[lane];
-    uint64_t s = 0ull;
+    // the lane visited rows first_row + k RPI, k < steps * BATCH; those at or
+    // past nt were row lr
+    const int32_t valid = first_row < nt ? (nt - first_row + RPI - 1) / RPI : 0;
+    const int32_t extra = steps * BATCH - valid;
+    if (extra > 0) {
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(
+          tb + (__umul24((uint32_t)lr, (uint32_t)block_stride) + lane_off));
+      const int64_t qq = *reinterpret_cast<const int64_t*>(tq + (uint32_t(lr) << 3));
+      const uint64_t pk = (((uint64_t)qq << bits) | 1ull) * (0ull - (uint64_t)extra);
 #pragma unroll
-    for (int c = 0; c < GBDT_MAX_BINS / NW; ++c) {
-      const int32_t cc = wid * (GBDT_MAX_BINS / NW) + c;
-      if (cc < fn) s += lds[fb + cc];
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t a = __builtin_amdgcn_perm(x, offs, sel[m]);
+        __hip_atomic_fetch_add(reinterpret_cast<LdsU64*>((uintptr_t)a), pk, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
     }
-    s_slice[wid][lane] = s;
   }
   __syncthreads();
-  if (wid == 0 && lane < nf && s_fskip[lane] >= 0 && s_fskip[lane] < s_fbins[lane]) {
-    uint64_t tile_total = 0ull;
-    uint64_t s = 0ull;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      tile_total += sh_tot[w];
-      s += s_slice[w][lane];
-    }
-    lds[s_fbase[lane] + s_fskip[lane]] = tile_total - s;
-  }
-  __syncthreads();
-
-  // output, column by column (a wave per column): global bins of the
-  // column's feature
+  // output: thread t takes (bin row t / W, column t % W); a quarter-wave reads
+  // 16 columns of one row, i.e. 16 bank pairs
   const uint64_t mask = (1ull << bits) - 1ull;
-  for (int32_t j = wid; j < nf; j += NW) {
-    const int32_t fb = s_fbase[j];
+  const int32_t v = td.node;
+  for (int32_t t = threadIdx.x; t < rows_out * W; t += kHistThreads) {
+    const int32_t j = t % W;
+    const int32_t cb = t / W;
+    if (j >= nf) continue;
     const int32_t fn = s_fbins[j];
-    const int64_t gb = s_fgb[j];
-    for (int32_t c = lane; c < fn; c += 64) {
-      const uint64_t x = lds[fb + c];
-      if (ntiles == 1) {
-        const uint64_t cc = x & mask;
-        hist_g[int64_t(v) * total_bins + gb + c] = (int64_t)(x - cc) >> bits;
-        hist_cnt[int64_t(v) * total_bins + gb + c] = (uint32_t)cc;
-      } else {
-        partial[int64_t(tile) * total_bins + gb + c] = x;
-      }
+    if (fn > rows_out && cb == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
+    if (cb >= fn) continue;
+    uint64_t x = 0ull;
+#pragma unroll
+    for (int k = 0; k < NCOPY; ++k) x += lds[cb * kHistRowSlots + k * W + j];
+    const int64_t gidx = int64_t(s_fgb[j]) + cb;
+    if (td.ntiles == 1) {
+      const uint64_t cc = x & mask;
+      hist_g[int64_t(v) * total_bins + gidx] = (int64_t)(x - cc) >> bits;
+      hist_cnt[int64_t(v) * total_bins + gidx] = (uint32_t)cc;
+    } else {
+      partial[int64_t(tile) * total_bins + gidx] = x;
     }
   }
 }
@@ -1614,8 +1691,11 @@ int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft) {
   if (!src.q) return fail(GBDT_E_ARG, "q is null");
   if (ft.max_block_bins < 1 || ft.max_block_bins > kLdsHistBudgetBins)
     return fail(GBDT_E_UNSUPPORTED, "max_block_bins outside the LDS histogram budget");
-  if (src.X.block_features > kMaxBlockFeatures)
-    return fail(GBDT_E_UNSUPPORTED, "more than 64 features in a column block");
+  if (src.X.n_features > src.X.n_bit_features &&
+      (src.X.block_stride > kHistMaxBlockStride || src.X.block_features > kHistRowSlots))
+    return fail(GBDT_E_UNSUPPORTED, "a column block wider than 32 bytes");
+  if (2 * src.X.n_bit_features > ft.max_block_bins)
+    return fail(GBDT_E_SHAPE, "max_block_bins below 2 slots per bit feature");
   return GBDT_OK;
 }
 
@@ -1634,19 +1714,26 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
                 WsCtrl* ctrl, hipStream_t s) {
   const int64_t n_rows = src.X.n_rows > 0 ? src.X.n_rows : 1;
   const int32_t bits = pack_bits_for(n_rows);
-  const int64_t q_bound = int64_t(1) << (52 - ceil_log2(n_rows));
-  const size_t lds = sizeof(uint64_t) * size_t(ft.max_block_bins + kLdsHistSlack);
-  const int unit = src.X.n_blocks > 0 ? load_unit_for(src.X.block_stride) : 4;
+  const bool has_bytes = src.X.n_features > src.X.n_bit_features;
   const bool has_bits = src.X.n_bit_features > 0;
-  auto kern = has_bits ? (unit == 16 ? k_hist<16, true> : (unit == 8 ? k_hist<8, true> : k_hist<4, true>))
-                       : (unit == 16 ? k_hist<16, false> : (unit == 8 ? k_hist<8, false> : k_hist<4, false>));
+  // byte blocks: 256 bin rows of 32 slots (any byte value stays inside);
+  // the bit block: 2 slots per bit feature
+  // (both within kLdsHistBudgetBins slots), then the kernel's small tables
+  const size_t lds = sizeof(uint64_t) * size_t(kLdsHistBudgetBins + kHistThreads / 64) +
+                     sizeof(int32_t) * size_t(2 * kHistRowSlots + kMaxBitWords + kBitStage);
+  const int32_t nd = has_bytes ? src.X.block_stride / 4 : 1;  // dwords per row (<= 8)
+  const int D = nd <= 1 ? 1 : (nd <= 2 ? 2 : (nd <= 4 ? 4 : 8));
+  auto kern = has_bits ? (D == 8 ? k_hist<8, true> : D == 4 ? k_hist<4, true>
+                                    : D == 2 ? k_hist<2, true> : k_hist<1, true>)
+                       : (D == 8 ? k_hist<8, false> : D == 4 ? k_hist<4, false>
+                                    : D == 2 ? k_hist<2, false> : k_hist<1, false>);
   const unsigned gy = (unsigned)(src.X.n_blocks + (has_bits ? 1 : 0));
   diag_begin(kDiagHist, s);
   hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles, gy), dim3(kHistThreads), lds, s, src.X.bins,
                      src.X.row_capacity, src.X.n_blocks, src.X.block_features, src.X.block_stride,
                      src.X.n_features, src.X.n_bit_features, src.X.bit_stride, src.X.col_feature,
                      src.q, ft.bin_offset, ft.skip_bin, ft.total_bins, ft.max_block_bins, desc, bits,
-                     q_bound, hist_g, hist_cnt, hpart, ctrl);
+                     hist_g, hist_cnt, hpart, ctrl);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist");
   return GBDT_OK;
@@ -1797,23 +1884,14 @@ int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t p
   int32_t worst = 2 * n_bit;
   int32_t bf = 0, nb = 0;
   if (nbc > 0) {
-    // fewest blocks of equal width (<= 64 columns) whose bins fit the budget
-    bool found = false;
-    for (nb = 1; nb <= nbc && !found; ++nb) {
-      bf = (nbc + nb - 1) / nb;
-      if (bf > 64) continue;
-      int32_t w = 0;
-      for (int32_t c0 = 0; c0 < nbc; c0 += bf) {
-        int32_t s = 0;
-        for (int32_t c = c0; c < c0 + bf && c < nbc; ++c) s += n_bins_host[cols[c]];
-        if (s > w) w = s;
-      }
-      if (w > kLdsHistBudgetBins) continue;
-      found = true;
-      if (w > worst) worst = w;
-    }
-    if (!found) return fail(GBDT_E_UNSUPPORTED, "no feature blocking fits the LDS budget");
+    // fewest blocks of equal width, at most 32 columns (8 dwords per row);
+    // the histogram of a byte block takes 32 LDS slots per bin row
+    nb = (nbc + kHistRowSlots - 1) / kHistRowSlots;
+    bf = (nbc + nb - 1) / nb;
     nb = (nbc + bf - 1) / bf;
+    int32_t bmax = 0;
+    for (int32_t c = 0; c < nbc; ++c) bmax = n_bins_host[cols[c]] > bmax ? n_bins_host[cols[c]] : bmax;
+    if (kHistRowSlots * bmax > worst) worst = kHistRowSlots * bmax;
   }
   X->n_features = n_features;
   X->n_blocks = nb;
@@ -1962,6 +2040,13 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
                      (const gbdt_split*)nullptr, (const int32_t*)nullptr, 0, hmulti);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
+  if (src->X.n_rows > 0) {
+    const int64_t nq = src->X.n_rows;
+    const int64_t q_bound = int64_t(1) << (52 - ceil_log2(nq));
+    const int64_t gq = (nq + 255) / 256 < 1024 ? (nq + 255) / 256 : 1024;
+    hipLaunchKernelGGL(k_check_q, dim3((unsigned)gq), dim3(256), 0, s, src->q, nq, q_bound, ctrl);
+    GBDT_LAUNCH_CHECK("k_check_q");
+  }
   rc = launch_hist(*src, *ft, hdesc, max_tiles, hist_g, hist_cnt, hpart, ctrl, s);
   if (rc) return rc;
   return launch_hist_reduce(list, hmulti, list_cap, hprefix, max_tiles, src->X.n_rows,

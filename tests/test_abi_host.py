@@ -57,10 +57,12 @@ def test_parameter_rules(bad):
 def test_blocking_fits_budget(nbins):
     X, mbb = g.gbdt_choose_blocking(nbins)
     F = len(nbins)
+    # fewest equal blocks of at most 32 columns (rows of at most 8 dwords);
+    # the histogram LDS holds 32 slots per bin row of the widest feature
+    assert X.n_blocks == -(-F // 32)
     assert X.n_blocks * X.block_features >= F > (X.n_blocks - 1) * X.block_features
-    assert X.block_stride % 4 == 0 and X.block_stride >= X.block_features and X.block_features <= 64
-    worst = max(sum(nbins[f0:f0 + X.block_features]) for f0 in range(0, F, X.block_features))
-    assert mbb == worst <= 7680
+    assert X.block_stride % 4 == 0 and X.block_features <= X.block_stride <= 32
+    assert mbb == 32 * max(nbins) <= 8192
 
 
 @pytest.mark.parametrize("nbins", [[256] * 10 + [2] * 44, [2, 256, 1, 13, 2, 64, 2] * 9, [2] * 200,
@@ -76,16 +78,16 @@ def test_layout_with_bits(nbins):
     assert all(cf[fc[f]] == f for f in range(F)) and sorted(cf) == list(range(F))
     nbc = len(byte)
     if nbc:
+        assert X.n_blocks == -(-nbc // 32)
         assert X.n_blocks * X.block_features >= nbc > (X.n_blocks - 1) * X.block_features
-        assert X.block_stride % 4 == 0 and X.block_stride >= X.block_features and X.block_features <= 64
-        worst = max(sum(nbins[cf[c]] for c in range(c0, min(c0 + X.block_features, nbc)))
-                    for c0 in range(0, nbc, X.block_features))
+        assert X.block_stride % 4 == 0 and X.block_features <= X.block_stride <= 32
+        worst = 32 * max(nbins[f] for f in byte)
     else:
         assert X.n_blocks == 0
         worst = 0
     if bits:
         assert X.bit_stride % 4 == 0 and X.bit_stride >= 4 * ((len(bits) + 31) // 32)
-    assert mbb == max(worst, 2 * len(bits)) <= 7680
+    assert mbb == max(worst, 2 * len(bits)) <= 8192
     # without bits: identity columns, as gbdt_choose_blocking
     X0, mbb0, cf0, _ = g.gbdt_choose_layout(nbins, pack_bits=False)
     Xb, mbbb = g.gbdt_choose_blocking(nbins)
