@@ -161,8 +161,9 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t* __restrict__ lists, ListLayout LL,
                                                 int64_t min_split, double lambda,
                                                 int32_t* __restrict__ n_nodes_out, PlanArgs pa,
-                                                int32_t part_max_tiles, int32_t hist_tile_max,
-                                                int32_t hist_max_tiles_next) {
+                                                int32_t part_tile, int32_t part_max_tiles,
+                                                int32_t hist_tile_max,
+                                                int32_t hist_target, int32_t hist_max_tiles_next) {
   __shared__ PlanLds lds;
   __shared__ int32_t shm[6 * 17];
   const int32_t first = tc->level_start[d];
@@ -193,7 +194,7 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
       if (last) {
         c[3] += 2;
       } else {
-        c[4] += tiles_of(count, kPartTileRows);
+        c[4] += tiles_of(count, part_tile);
         if ((int64_t)(nl > nr ? nl : nr) >= min_split) {
           ++c[1];
           c[2] += ((int64_t)nl >= min_split) + ((int64_t)nr >= min_split);
@@ -208,9 +209,9 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   int32_t r[6], t[6];
   block_exclusive_scan_multi<6>(c, r, t, shm);
   // histogram tile rows of the next level from the rows it actually builds:
-  // about kHistTargetTiles tiles, none below kHistMinTileRows (or above the
-  // packed cells' limit)
-  const int32_t hist_tile_rows_next = hist_tile_rows_for(t[5], hist_tile_max);
+  // about hist_target tiles, none below kHistMinTileRows (or above the packed
+  // cells' limit)
+  const int32_t hist_tile_rows_next = hist_tile_rows_for(t[5], hist_tile_max, hist_target);
   {
     int32_t nt = 0;
     if (fast) {
@@ -354,12 +355,12 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   // this level's partition plan (splitting nodes) and the next level's
   // histogram plan (nodes to build)
   if (fast) {
-    plan_emit(stP, spP, &lds.n_multi, t_split, kPartTileRows, part_max_tiles, pa.prefix, pa.desc,
+    plan_emit(stP, spP, &lds.n_multi, t_split, part_tile, part_max_tiles, pa.prefix, pa.desc,
               pa.status, pa.ctrl, true, nullptr);
     plan_emit(stH, spH, &lds.n_multi, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix,
               pa.hdesc, nullptr, pa.ctrl, false, pa.hmulti);
   } else {
-    plan_tiles(nodes, split_list, t_split, kPartTileRows, part_max_tiles, pa.prefix, pa.desc,
+    plan_tiles(nodes, split_list, t_split, part_tile, part_max_tiles, pa.prefix, pa.desc,
                pa.status, pa.ctrl, splits, pa.feature_col, pa.n_features, nullptr, lds);
     plan_tiles(nodes, build_n, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix,
                pa.hdesc, nullptr, pa.ctrl, nullptr, nullptr, 0, pa.hmulti, lds);
@@ -450,20 +451,22 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   int64_t h_tiles[GBDT_MAX_DEPTH + 1];
   int64_t p_tiles[GBDT_MAX_DEPTH + 1];
   // the level kernel sizes levels >= 1 from their actual rows (about
-  // kHistTargetTiles tiles of at least min(kHistMinTileRows, tile_max) rows,
-  // at most tile_max); the bound below holds for every size it can choose
+  // `target` tiles of at least min(kHistMinTileRows, tile_max) rows, at most
+  // tile_max); the bound below holds for every size it can choose
   const int32_t tile_max = hist_tile_max(n);
+  const int32_t part_tile = part_tile_rows(n, X->n_blocks);
+  const int32_t target = hist_target_tiles(X->n_blocks + (X->n_bit_features > 0 ? 1 : 0));
   for (int32_t d = 0; d <= D; ++d) {
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
     const int64_t rows_build = d == 0 ? n : n / 2;
-    h_rows[d] = hist_tile_rows(rows_build, n);
+    h_rows[d] = hist_tile_rows(rows_build, n, target);
     if (d == 0) {
       h_tiles[d] = (rows_build + h_rows[d] - 1) / h_rows[d] + cap_build;
     } else {
       const int64_t by_max = (rows_build + tile_max - 1) / tile_max;
-      h_tiles[d] = (by_max > kHistTargetTiles ? by_max : kHistTargetTiles) + cap_build;
+      h_tiles[d] = (by_max > target ? by_max : target) + cap_build;
     }
-    p_tiles[d] = (n + kPartTileRows - 1) / kPartTileRows + (int64_t(1) << d);
+    p_tiles[d] = (n + part_tile - 1) / part_tile + (int64_t(1) << d);
     if (h_tiles[d] > WL.hpart_tiles || p_tiles[d] > WL.status_cap)
       return fail(GBDT_E_INTERNAL, "tile bound exceeds the workspace");
   }
@@ -497,8 +500,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     if (rc) return rc;
     diag_begin(kDiagLevel, s);
     hipLaunchKernelGGL(k_level, dim3(1), dim3(1024), 0, s, d, D, nodes_out, b->splits, tc, b->lists,
-                       LL, min_split, p->reg_lambda, n_nodes_dev, pa, (int32_t)p_tiles[d],
-                       tile_max, (int32_t)h_tiles[d + 1]);
+                       LL, min_split, p->reg_lambda, n_nodes_dev, pa, part_tile, (int32_t)p_tiles[d],
+                       tile_max, target, (int32_t)h_tiles[d + 1]);
     diag_end(s);
     {
       hipError_t e = hipGetLastError();
@@ -507,7 +510,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     // the rows of the last level's children are never read again: the
     // prediction update routes rows through the finished tree instead
     if (d + 1 < D) {
-      rc = launch_partition(src, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], s);
+      rc = launch_partition(src, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], part_tile, s);
       if (rc) return rc;
       src = dst;
     }

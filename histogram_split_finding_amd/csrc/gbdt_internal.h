@@ -31,9 +31,21 @@ constexpr int kGradBlocks = 1024;     // grid of the gradient kernels
 // allocator hold to that.
 #define GBDT_TWO_GROUPS __attribute__((amdgpu_waves_per_eu(8, 8)))
 
-constexpr int kPartTileRows = 2048;   // rows per partition tile
+constexpr int kPartTileRows = 2048;   // rows per partition tile (the smaller size; bounds use it)
+constexpr int kPartTileRowsLarge = 4096;
+constexpr int64_t kPartLargeRows = int64_t(1) << 22;  // matrices from this size take the larger tiles
+
+// Rows per partition tile for a matrix of n rows in n_blocks byte blocks:
+// larger tiles carry more bytes per latency chain (ticket, descriptor,
+// flags, look-back) on large matrices of one block; small matrices keep more
+// tiles than workgroup slots, and several blocks need the registers for
+// double-buffering the blocks.
+inline int32_t part_tile_rows(int64_t n_rows, int32_t n_blocks) {
+  return (n_rows >= kPartLargeRows && n_blocks <= 1) ? kPartTileRowsLarge : kPartTileRows;
+}
 constexpr int kHistMinTileRows = 1024;
-constexpr int kHistTargetTiles = 1024;
+constexpr int kHistTargetTiles = 1024;    // workgroups per histogram launch to aim for
+constexpr int kHistMinTargetTiles = 128;
 constexpr int kReduceNodeSlots = 64;  // y extent of the partial-reduction grid
 constexpr int kLdsHistBudgetBins = 8192;  // LDS slots (8 bytes) of one histogram workgroup: 64 KiB
 constexpr int kHistRowSlots = 32;          // LDS slots per bin row of a byte block's histogram
@@ -98,7 +110,15 @@ inline int32_t pack_bits_for(int64_t n_rows) {
   return b;
 }
 
-int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows);
+int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows, int32_t target);
+
+// Histogram tiles per launch to aim for: about kHistTargetTiles workgroups
+// over the tile x column-block grid (gy blocks), at least kHistMinTargetTiles
+// tiles.
+inline int32_t hist_target_tiles(int32_t gy) {
+  const int32_t t = kHistTargetTiles / (gy < 1 ? 1 : gy);
+  return t < kHistMinTargetTiles ? kHistMinTargetTiles : t;
+}
 
 // Most rows one histogram tile may hold for n rows: the packed LDS cells
 // count a tile's rows in `bits` bits.
@@ -107,10 +127,10 @@ inline int32_t hist_tile_max(int64_t n_rows) {
 }
 
 // Histogram tile rows for a level that builds `rows` rows (device and host):
-// about kHistTargetTiles tiles, at least min(kHistMinTileRows, tile_max) rows
-// and at most tile_max.
-__host__ __device__ inline int32_t hist_tile_rows_for(int32_t rows, int32_t tile_max) {
-  int32_t t = (rows + kHistTargetTiles - 1) / kHistTargetTiles;
+// about `target` tiles, at least min(kHistMinTileRows, tile_max) rows and at
+// most tile_max.
+__host__ __device__ inline int32_t hist_tile_rows_for(int32_t rows, int32_t tile_max, int32_t target) {
+  int32_t t = (rows + target - 1) / target;
   const int32_t lo = kHistMinTileRows < tile_max ? kHistMinTileRows : tile_max;
   if (t < lo) t = lo;
   if (t > tile_max) t = tile_max;
@@ -133,7 +153,8 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
                 const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
                 const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s);
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
-                     uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, hipStream_t s);
+                     uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
+                     hipStream_t s);
 
 // Per-kernel device timing (the backend's diagnostics): when enabled, every
 // launch of the library is bracketed by two hipEvents on its stream.

@@ -104,9 +104,9 @@ WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
   return L;
 }
 
-int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows) {
+int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows, int32_t target) {
   const int64_t tmax = (int64_t(1) << pack_bits_for(n_rows)) - 1;
-  int64_t t = (rows_bound + kHistTargetTiles - 1) / kHistTargetTiles;
+  int64_t t = (rows_bound + target - 1) / target;
   if (t < kHistMinTileRows) t = kHistMinTileRows;
   if (t > tmax) t = tmax;
   if (t < 1) t = 1;
@@ -1105,7 +1105,6 @@ __device__ __forceinline__ uint64_t st_load(const uint64_t* p) {
 }
 
 constexpr int kPartThreads = 1024;
-constexpr int kPartRowsPerThread = kPartTileRows / kPartThreads;  // 2
 constexpr int kPartWaves = kPartThreads / 64;
 
 // Wave 0 of the workgroup: exclusive count of left rows over the tiles of the
@@ -1139,25 +1138,65 @@ __device__ int64_t lookback_excl(uint64_t* status, int32_t tile, int32_t tfirst,
   }
 }
 
-// One workgroup per tile of a splitting node, taken in ticket order.  The
-// tile descriptor carries the node's split, so right after it arrives the
-// workgroup issues the loads of its rows' split-feature bytes and q; then it
-// publishes its left count, looks back for the exclusive prefix, scatters q
-// (and row ids) and copies the bins in batches of BATCH rows per lane
-// (lanes = (row group, column of UNIT bytes)).
-template <int UNIT>
+// ND dwords of one row (4-byte aligned) as wide loads and stores: the first
+// min(ND, 4) dwords in `a`, the rest in `b` (two register quads, so each
+// load writes its own aligned registers).
+template <int ND>
+struct RowData {
+  static_assert(ND >= 1 && ND <= 8, "row of 1..8 dwords");
+  uint4 a, b;
+};
+template <int N>
+__device__ __forceinline__ uint4 load_dwords(const uint8_t* p) {
+  if constexpr (N == 4) return *reinterpret_cast<const uint4*>(p);
+  if constexpr (N == 3) { const uint3 v = *reinterpret_cast<const uint3*>(p); return make_uint4(v.x, v.y, v.z, 0u); }
+  if constexpr (N == 2) { const uint2 v = *reinterpret_cast<const uint2*>(p); return make_uint4(v.x, v.y, 0u, 0u); }
+  if constexpr (N == 1) return make_uint4(*reinterpret_cast<const uint32_t*>(p), 0u, 0u, 0u);
+  return make_uint4(0u, 0u, 0u, 0u);
+}
+template <int N>
+__device__ __forceinline__ void store_dwords(uint8_t* p, const uint4& v) {
+  if constexpr (N == 4) *reinterpret_cast<uint4*>(p) = v;
+  if constexpr (N == 3) *reinterpret_cast<uint3*>(p) = make_uint3(v.x, v.y, v.z);
+  if constexpr (N == 2) *reinterpret_cast<uint2*>(p) = make_uint2(v.x, v.y);
+  if constexpr (N == 1) *reinterpret_cast<uint32_t*>(p) = v.x;
+}
+template <int ND>
+__device__ __forceinline__ void row_load(const uint8_t* p, RowData<ND>& d) {
+  d.a = load_dwords<(ND < 4 ? ND : 4)>(p);
+  if constexpr (ND > 4) d.b = load_dwords<ND - 4>(p + 16);
+}
+template <int ND>
+__device__ __forceinline__ void row_store(uint8_t* p, const RowData<ND>& d) {
+  store_dwords<(ND < 4 ? ND : 4)>(p, d.a);
+  if constexpr (ND > 4) store_dwords<ND - 4>(p + 16, d.b);
+}
+
+// One workgroup per tile of K * kPartThreads rows of a splitting node, taken
+// in ticket order.  Thread t owns rows t + k kPartThreads of the tile and
+// moves each whole row itself: the row's bytes of a column block (ND dwords)
+// with one or two wide loads and stores, its q and row id, so a wave's
+// accesses cover 64 consecutive source rows and two runs of destinations
+// (left and right).  The tile descriptor carries the node's split, so right
+// after it arrives the workgroup issues every load that does not depend on
+// the destinations: the split feature's byte (or bit), q, row ids and block
+// 0 of the first two rows per thread.  Then it ballots the go-left flags,
+// publishes its left count, looks back for the exclusive prefix (decoupled
+// look-back), loads block 0 of its other rows and stores; the other blocks
+// and the bit block are loaded and stored row by row after that.
+template <int ND, int K>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const int64_t* __restrict__ sq,
     const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, int64_t* __restrict__ dq,
     int32_t* __restrict__ drid, int64_t row_capacity, int32_t n_blocks, int32_t block_features,
     int32_t block_stride, int32_t n_features, int32_t n_bit, int32_t bit_stride,
     const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl) {
-  constexpr int BATCH = 32 / UNIT;
+  constexpr int TILE = K * kPartThreads;
+  constexpr int KE = K < 2 ? K : 2;  // rows per thread whose block 0 is loaded early
   __shared__ int32_t s_tile;
-  __shared__ int32_t s_cnt[kPartRowsPerThread][kPartWaves];
+  __shared__ int32_t s_cnt[K][kPartWaves];
   __shared__ int32_t s_excl;
   __shared__ int32_t s_acc;
-  __shared__ int32_t s_dpos[kPartTileRows];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   if (threadIdx.x == 0) s_tile = (int32_t)atomicAdd(&ctrl->ticket, 1u);
@@ -1171,12 +1210,11 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   const int32_t tin = tile - tfirst;
   const int64_t r0 = td.r0;
   const int64_t span = int64_t(td.r1) - td.r0;
-  const int32_t rows_all = (int32_t)(span < 0 ? 0 : (span > kPartTileRows ? kPartTileRows : span));
+  const int32_t rows_all = (int32_t)(span < 0 ? 0 : (span > TILE ? TILE : span));
   // a listed node must carry a valid split; otherwise nothing is moved, the
   // tile still publishes (so later tiles never wait on it) and the error word
-  // is set
-  // the descriptor's feature is the split's matrix column: a byte column
-  // (c < n_features - n_bit) or a bit of the bit block
+  // is set.  The descriptor's feature is the split's matrix column: a byte
+  // column (c < n_features - n_bit) or a bit of the bit block.
   const bool split_ok = td.split_valid && td.feature >= 0 && td.feature < n_features;
   const int32_t rows = split_ok ? rows_all : 0;
   const int32_t nbc = n_features - n_bit;
@@ -1185,36 +1223,49 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   const int32_t fblk = fbit ? 0 : sc / block_features;
   const int32_t fcol = fbit ? 0 : sc % block_features;
   const int32_t fk = fbit ? sc - nbc : 0;
+  const int32_t nwords = bit_stride >> 2;
   const uint8_t* __restrict__ fcolp = sbins + int64_t(fblk) * row_capacity * block_stride + fcol;
   const uint8_t* __restrict__ sbits = sbins + int64_t(n_blocks) * row_capacity * block_stride;
-  const uint32_t* __restrict__ fwordp =
-      reinterpret_cast<const uint32_t*>(sbits) + (fk >> 5);
-  // loads that need only the descriptor: split-feature bins, q, row ids
-  int32_t fb[kPartRowsPerThread];
-  int64_t qv[kPartRowsPerThread];
-  int32_t rv[kPartRowsPerThread];
+  const uint32_t* __restrict__ fwordp = reinterpret_cast<const uint32_t*>(sbits) + (fk >> 5);
+  // loads that need only the descriptor, unconditional (a row past the tile
+  // end rereads its last row and is ignored), so none waits behind a branch
+  int32_t fb[K];
+  int64_t qv[K];
+  int32_t rv[K];
+  RowData<ND> rd[K];
+  // (the split feature's bytes first: loads complete in order, and the
+  // flags wait only for them while the rows are still in flight)
+  if (rows > 0) {
 #pragma unroll
-  for (int k = 0; k < kPartRowsPerThread; ++k) {
-    const int32_t i = k * kPartThreads + threadIdx.x;
-    const bool ok = i < rows;
-    const int64_t s = r0 + i;
-    if (fbit)
-      fb[k] = ok ? (int32_t)((fwordp[s * (bit_stride >> 2)] >> (fk & 31)) & 1u) : 0;
-    else
-      fb[k] = ok ? (int32_t)fcolp[s * block_stride] : 0;
-    qv[k] = ok ? sq[s] : 0;
-    rv[k] = (ok && drid != nullptr) ? (srid != nullptr ? srid[s] : (int32_t)s) : 0;
+    for (int k = 0; k < K; ++k) {
+      const int32_t i = k * kPartThreads + threadIdx.x;
+      const int64_t sr = r0 + (i < rows ? i : rows - 1);
+      if (fbit)
+        fb[k] = (int32_t)fwordp[sr * nwords];
+      else
+        fb[k] = (int32_t)fcolp[sr * block_stride];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int32_t i = k * kPartThreads + threadIdx.x;
+      const int64_t sr = r0 + (i < rows ? i : rows - 1);
+      qv[k] = sq[sr];
+      rv[k] = drid != nullptr ? (srid != nullptr ? srid[sr] : (int32_t)sr) : 0;
+      // with no byte block (ND == 1, block_stride 0) this rereads the first
+      // dword of the bit block, and the value is never stored
+      if (k < KE) row_load<ND>(sbins + sr * block_stride, rd[k]);
+    }
+    if (fbit) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) fb[k] = (int32_t)(((uint32_t)fb[k] >> (fk & 31)) & 1u);
+    }
   }
-  const int32_t lpr = block_stride / UNIT;
-  const int32_t rpi = kPartThreads / lpr;
-  const int32_t col = threadIdx.x % lpr;
-  const int32_t rg = threadIdx.x / lpr;
   if (!split_ok && threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
 
-  bool left[kPartRowsPerThread];
-  uint64_t bal[kPartRowsPerThread];
+  bool left[K];
+  uint64_t bal[K];
 #pragma unroll
-  for (int k = 0; k < kPartRowsPerThread; ++k) {
+  for (int k = 0; k < K; ++k) {
     const int32_t i = k * kPartThreads + threadIdx.x;
     left[k] = (i < rows) && (fb[k] <= td.threshold_bin);
     bal[k] = __ballot(left[k]);
@@ -1223,7 +1274,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   __syncthreads();
   if (threadIdx.x == 0) {
     int32_t acc = 0;
-    for (int k = 0; k < kPartRowsPerThread; ++k)
+    for (int k = 0; k < K; ++k)
       for (int w = 0; w < kPartWaves; ++w) {
         const int32_t t = s_cnt[k][w];
         s_cnt[k][w] = acc;
@@ -1248,13 +1299,15 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   __syncthreads();
   const int32_t excl = s_excl;
   const int64_t lbase = int64_t(td.begin) + excl;
-  const int64_t rbase = int64_t(td.begin) + td.n_left + (int64_t(tin) * kPartTileRows - excl);
+  const int64_t rbase = int64_t(td.begin) + td.n_left + (int64_t(tin) * TILE - excl);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t seg_end = int64_t(td.begin) + td.count;
   bool bad_pos = false;
+  int32_t dpos[K];
 #pragma unroll
-  for (int k = 0; k < kPartRowsPerThread; ++k) {
+  for (int k = 0; k < K; ++k) {
     const int32_t i = k * kPartThreads + threadIdx.x;
+    dpos[k] = -1;
     if (i < rows) {
       const int32_t rl = s_cnt[k][wid] + __popcll(bal[k] & lt_mask);
       const int64_t d = left[k] ? lbase + rl : rbase + (i - rl);
@@ -1262,66 +1315,95 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       // row outside its node's segment: such a row is not written
       const bool in_seg = d >= td.begin && d < seg_end;
       bad_pos |= !in_seg;
-      const int32_t dd = in_seg ? (int32_t)d : -1;
-      s_dpos[i] = dd;
-      if (dd >= 0) {
-        dq[dd] = qv[k];
-        if (drid != nullptr) drid[dd] = rv[k];
-      }
+      dpos[k] = in_seg ? (int32_t)d : -1;
     }
   }
   if (bad_pos) dev_error(&ctrl->err, GBDT_E_INTERNAL);
-  __syncthreads();
-  // bit block: (row group, word) lanes, 8 rows of loads in flight per lane
-  if (n_bit > 0) {
-    const int32_t nwords = bit_stride >> 2;
-    const int32_t brpi = kPartThreads / nwords;
-    const int32_t bw = threadIdx.x % nwords;
-    const int32_t brg = threadIdx.x / nwords;
-    const uint32_t* __restrict__ sw = reinterpret_cast<const uint32_t*>(sbits) + bw;
-    uint32_t* __restrict__ dw = reinterpret_cast<uint32_t*>(
-        dbins + int64_t(n_blocks) * row_capacity * block_stride) + bw;
-    if (brg < brpi) {
-      for (int32_t i = brg; i < rows; i += 8 * brpi) {
-        uint32_t x[8];
+  // block 0 of the late rows, then every row's stores
+  if (n_blocks > 0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int32_t ii = i + u * brpi;
-          if (ii < rows) x[u] = sw[(r0 + ii) * nwords];
-        }
+    for (int k = KE; k < K; ++k) {
+      const int32_t i = k * kPartThreads + threadIdx.x;
+      if (dpos[k] >= 0) row_load<ND>(sbins + (r0 + i) * block_stride, rd[k]);
+    }
+  }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int32_t ii = i + u * brpi;
-          if (ii < rows) {
-            const int32_t d = s_dpos[ii];
-            if (d >= 0) dw[int64_t(d) * nwords] = x[u];
-          }
+  for (int k = 0; k < K; ++k) {
+    const int32_t d = dpos[k];
+    if (d < 0) continue;
+    dq[d] = qv[k];
+    if (drid != nullptr) drid[d] = rv[k];
+    if (n_blocks > 0) row_store<ND>(dbins + int64_t(d) * block_stride, rd[k]);
+  }
+  // the other byte blocks, double-buffered: block b + 1 is loaded before
+  // block b is stored (loads are unconditional, from clamped rows).  Tiles
+  // of more than two rows per thread are used only with one block (the
+  // registers of two buffers would not fit); the plain loop covers them.
+  if constexpr (K > 2) {
+    for (int32_t b = 1; b < n_blocks; ++b) {
+      const int64_t boff = int64_t(b) * row_capacity * block_stride;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int32_t i = k * kPartThreads + threadIdx.x;
+        if (dpos[k] >= 0) {
+          row_load<ND>(sbins + boff + (r0 + i) * block_stride, rd[k]);
+          row_store<ND>(dbins + boff + int64_t(dpos[k]) * block_stride, rd[k]);
         }
       }
     }
-  }
-  // bins: (row group, column of UNIT bytes) lanes, every block, BATCH rows
-  // of loads in flight per lane
-  if (rg < rpi) {
-    for (int32_t b = 0; b < n_blocks; ++b) {
-      const uint8_t* __restrict__ sb = sbins + int64_t(b) * row_capacity * block_stride + UNIT * col;
-      uint8_t* __restrict__ db = dbins + int64_t(b) * row_capacity * block_stride + UNIT * col;
-      for (int32_t i = rg; i < rows; i += BATCH * rpi) {
-        uint32_t w[BATCH][UNIT / 4];
+  } else if (n_blocks > 1) {
+    RowData<ND> nx[K];
+    auto load_block = [&](int32_t b, RowData<ND>* dst) {
+      const uint8_t* __restrict__ src = sbins + int64_t(b) * row_capacity * block_stride;
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-          const int32_t ii = i + u * rpi;
-          if (ii < rows) VecLoad<UNIT>::load(sb + (r0 + ii) * block_stride, w[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-          const int32_t ii = i + u * rpi;
-          if (ii < rows) {
-            const int32_t d = s_dpos[ii];
-            if (d >= 0) VecLoad<UNIT>::store(db + int64_t(d) * block_stride, w[u]);
-          }
-        }
+      for (int k = 0; k < K; ++k) {
+        const int32_t i = k * kPartThreads + threadIdx.x;
+        row_load<ND>(src + (r0 + (i < rows ? i : rows - 1)) * block_stride, dst[k]);
       }
+    };
+    auto store_block = [&](int32_t b, const RowData<ND>* src) {
+      uint8_t* __restrict__ dstp = dbins + int64_t(b) * row_capacity * block_stride;
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (dpos[k] >= 0) row_store<ND>(dstp + int64_t(dpos[k]) * block_stride, src[k]);
+    };
+    if (rows > 0) load_block(1, nx);
+    int32_t b = 1;
+    while (b < n_blocks) {
+      if (b + 1 < n_blocks && rows > 0) load_block(b + 1, rd);
+      store_block(b, nx);
+      if (++b >= n_blocks) break;
+      if (b + 1 < n_blocks && rows > 0) load_block(b + 1, nx);
+      store_block(b, rd);
+      ++b;
+    }
+  }
+  // the bit block: nwords words per row, 4 at a time
+  if (n_bit > 0) {
+    const uint32_t* __restrict__ sw = reinterpret_cast<const uint32_t*>(sbits);
+    uint32_t* __restrict__ dw = reinterpret_cast<uint32_t*>(dbins + int64_t(n_blocks) * row_capacity * block_stride);
+    int32_t w0 = 0;
+    for (; w0 + 4 <= nwords; w0 += 4) {
+      RowData<4> x[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int32_t i = k * kPartThreads + threadIdx.x;
+        if (dpos[k] >= 0) row_load<4>(reinterpret_cast<const uint8_t*>(sw + (r0 + i) * nwords + w0), x[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (dpos[k] >= 0) row_store<4>(reinterpret_cast<uint8_t*>(dw + int64_t(dpos[k]) * nwords + w0), x[k]);
+    }
+    for (; w0 < nwords; ++w0) {
+      uint32_t x[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int32_t i = k * kPartThreads + threadIdx.x;
+        if (dpos[k] >= 0) x[k] = sw[(r0 + i) * nwords + w0];
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (dpos[k] >= 0) dw[int64_t(dpos[k]) * nwords + w0] = x[k];
     }
   }
 }
@@ -1706,6 +1788,8 @@ int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst) {
   if (rc) return rc;
   if (!same_layout(src.X, dst.X)) return fail(GBDT_E_SHAPE, "source and destination layouts differ");
   if (!src.q || !dst.q) return fail(GBDT_E_ARG, "q pointer is null");
+  if (src.X.n_blocks > 0 && src.X.block_stride > kHistMaxBlockStride)
+    return fail(GBDT_E_UNSUPPORTED, "a column block wider than 32 bytes");
   return GBDT_OK;
 }
 
@@ -1776,10 +1860,33 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
   return GBDT_OK;
 }
 
+template <int K>
+static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K>) {
+  switch (nd) {
+    case 1: return k_partition<1, K>;
+    case 2: return k_partition<2, K>;
+    case 3: return k_partition<3, K>;
+    case 4: return k_partition<4, K>;
+    case 5: return k_partition<5, K>;
+    case 6: return k_partition<6, K>;
+    case 7: return k_partition<7, K>;
+    case 8: return k_partition<8, K>;
+    default: return nullptr;
+  }
+}
+
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
-                     uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, hipStream_t s) {
-  const int unit = src.X.n_blocks > 0 ? load_unit_for(src.X.block_stride) : 4;
-  auto kern = unit == 16 ? k_partition<16> : (unit == 8 ? k_partition<8> : k_partition<4>);
+                     uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
+                     hipStream_t s) {
+  const int32_t nd = src.X.n_blocks > 0 ? src.X.block_stride / 4 : 1;
+  decltype(&k_partition<1, 2>) kern = nullptr;
+  if (tile_rows == 2 * kPartThreads)
+    kern = partition_kernel<2>(nd);
+  else if (tile_rows == 4 * kPartThreads)
+    kern = partition_kernel<4>(nd);
+  else
+    return fail(GBDT_E_INTERNAL, "unsupported partition tile size");
+  if (kern == nullptr) return fail(GBDT_E_UNSUPPORTED, "a column block wider than 32 bytes");
   diag_begin(kDiagPartition, s);
   hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s, src.X.bins, src.q,
                      src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
@@ -2031,7 +2138,8 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   int32_t* hmulti = reinterpret_cast<int32_t*>(w + L.hmulti);
   TileDesc* hdesc = reinterpret_cast<TileDesc*>(w + L.hdesc);
   uint64_t* hpart = reinterpret_cast<uint64_t*>(w + L.hpart);
-  const int32_t T = hist_tile_rows(rows_bound, src->X.n_rows);
+  const int32_t gy = src->X.n_blocks + (src->X.n_bit_features > 0 ? 1 : 0);
+  const int32_t T = hist_tile_rows(rows_bound, src->X.n_rows, hist_target_tiles(gy));
   const int64_t max_tiles = (rows_bound + T - 1) / T + list_cap;
   if (max_tiles > L.hpart_tiles) return fail(GBDT_E_SHAPE, "too many histogram tiles for the workspace");
   diag_begin(kDiagPlan, s);
@@ -2106,7 +2214,8 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
   const WsLayout L = ws_layout(src->X.n_rows, list_cap, 1);
   rc = check_ws(ws, ws_bytes, L);
   if (rc) return rc;
-  const int64_t max_tiles = (rows_bound + kPartTileRows - 1) / kPartTileRows + list_cap;
+  const int32_t ptr = part_tile_rows(src->X.n_rows, src->X.n_blocks);
+  const int64_t max_tiles = (rows_bound + ptr - 1) / ptr + list_cap;
   if (max_tiles > L.status_cap) return fail(GBDT_E_SHAPE, "too many partition tiles for the workspace");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
@@ -2116,11 +2225,11 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
   uint64_t* status = reinterpret_cast<uint64_t*>(w + L.status);
   diag_begin(kDiagPlan, s);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, nodes, list, list_len, list_cap,
-                     kPartTileRows, (int32_t)max_tiles, prefix, tdesc, ctrl, status, splits,
+                     ptr, (int32_t)max_tiles, prefix, tdesc, ctrl, status, splits,
                      src->X.feature_col, src->X.n_features, (int32_t*)nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_plan");
-  return launch_partition(*src, *dst, tdesc, status, ctrl, max_tiles, s);
+  return launch_partition(*src, *dst, tdesc, status, ctrl, max_tiles, ptr, s);
 }
 
 int gbdt_update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* nodes,
