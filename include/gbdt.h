@@ -118,17 +118,19 @@ typedef struct gbdt_matrix {
  * Feature table (host struct, device arrays).  n_bins[f] in [1, 256];
  * bin_offset[f] = sum of n_bins[g] for g < f (bin_offset[F] = total_bins);
  * bin_feature[b] = the feature of global bin b ([total_bins]); skip_bin[f] is
- * a bin of feature f whose count and gradient sum the histogram kernel
+ * a bin of a bit feature f whose count and gradient sum the histogram kernel
  * derives from the node total instead of accumulating (the most frequent bin,
- * set by gbdt_pack_matrix), or -1.  The choice changes speed only, never a
- * bit of the result.  max_block_bins sizes the histogram kernel's LDS; it
- * must be at least the bin count of every byte block and 2 per bit feature
- * (written by gbdt_choose_blocking / gbdt_choose_layout).
+ * set by gbdt_pack_matrix), or -1; byte features ignore it.  The choice
+ * changes speed only, never a bit of the result.  max_block_bins is the
+ * histogram kernel's LDS slot count: at least 32 times the most bins of any
+ * byte feature (a byte block's histogram takes 32 slots per bin row) and 2
+ * per bit feature, at most 8192 (written by gbdt_choose_blocking /
+ * gbdt_choose_layout).
  */
 typedef struct gbdt_features {
   int32_t n_features;
   int32_t total_bins;
-  int32_t max_block_bins; /* host value: most bins in one feature block of the matrix */
+  int32_t max_block_bins; /* host value: LDS slots of one histogram workgroup */
   int32_t pad;
   const int32_t* n_bins;
   const int32_t* bin_offset;
@@ -226,9 +228,10 @@ size_t gbdt_workspace_bytes(int64_t n_rows, int32_t max_list, int32_t total_bins
 /*
  * Column blocking for features with n_bins_host[f] bins (host array): writes
  * n_features, n_blocks, block_features and block_stride of *X (no bit block:
- * n_bit_features 0, identity columns, NULL maps) and *max_block_bins, so that
- * one block holds at most 64 features and its histogram fits a workgroup's
- * LDS budget (7680 bins).
+ * n_bit_features 0, identity columns, NULL maps) and *max_block_bins: the
+ * fewest blocks of equal width with at most 32 features each (rows of at
+ * most 8 dwords), and 32 LDS slots per bin row of the widest feature (at
+ * most 8192 slots, 64 KiB).
  */
 int gbdt_choose_blocking(int32_t n_features, const int32_t* n_bins_host, gbdt_matrix* X /* host */,
                          int32_t* max_block_bins /* host */);
@@ -240,8 +243,8 @@ int gbdt_choose_blocking(int32_t n_features, const int32_t* n_bins_host, gbdt_ma
  * layout fields of *X (the map pointers are left NULL: the caller uploads
  * col_feature_host / feature_col_host, host arrays of n_features entries that
  * this call fills, and stores the device copies in X), and *max_block_bins
- * (the LDS slots one histogram workgroup needs: the largest byte block's
- * bins, or 2 per bit feature for the bit block).
+ * (the LDS slots one histogram workgroup needs: 32 per bin of the widest
+ * byte feature, or 2 per bit feature for the bit block).
  */
 int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t pack_bits,
                        gbdt_matrix* X /* host */, int32_t* max_block_bins /* host */,
@@ -253,7 +256,8 @@ int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t p
  * n_blocks * row_capacity * block_stride + row_capacity * bit_stride bytes;
  * bit features must have at most 2 bins), checks every bin against
  * n_bins (a violation sets GBDT_E_RANGE in the error word) and writes
- * ft->skip_bin (most frequent bin of each feature, smallest on ties).
+ * ft->skip_bin (most frequent bin of each feature, smallest on ties; used for
+ * bit features).
  * Setup step, not part of the per-tree path.
  */
 int gbdt_pack_matrix(const uint8_t* rowmajor, const gbdt_matrix* dst /* host */,
@@ -298,12 +302,13 @@ int gbdt_compute_gradients(const double* pred, const float* label, int64_t n, in
  * for every global bin b = bin_offset[f] + c.  The slots of listed nodes are
  * overwritten (their previous contents are ignored); other slots are not
  * touched.  hist_g, hist_cnt: [slots][total_bins], slot = node id.
- * Requires block_features <= 64 (GBDT_E_UNSUPPORTED otherwise) and
- * ft->max_block_bins at least the bins of every block; a block with more
- * bins is skipped and sets GBDT_E_SHAPE.
+ * Requires block_stride <= 32 bytes (GBDT_E_UNSUPPORTED otherwise) and
+ * ft->max_block_bins at least 32 times the bins of every byte feature; a
+ * feature with more bins sets GBDT_E_SHAPE.
  * rows_bound bounds the sum of the listed counts (sizes the launch);
  * list_cap bounds *list_len.  Requires |q_i| <= 2^(52 - ceil(log2 n_rows))
- * (as written by gbdt_compute_gradients); a violation sets GBDT_E_OVERFLOW.
+ * (as written by gbdt_compute_gradients); a violation, found by a check of
+ * every q of src before the histograms, sets GBDT_E_OVERFLOW.
  * Requires every bin < n_bins[f] and padding bytes 0, which holds for rows
  * written by gbdt_pack_matrix (which checks the bins) and gbdt_partition_rows;
  * other bytes give wrong counts but never an access outside the buffers.
@@ -349,7 +354,8 @@ int gbdt_find_best_splits(const int64_t* hist_g, const uint32_t* hist_cnt,
  * side in its original order (stable).  Rows of unlisted nodes are not
  * touched.  The left count must equal s.n_left, else GBDT_E_INTERNAL.
  * src->rid == NULL means identity; dst->rid == NULL skips the row ids (the
- * level-wise driver does not need them).
+ * level-wise driver does not need them).  Requires block_stride <= 32 bytes
+ * (GBDT_E_UNSUPPORTED otherwise).
  */
 int gbdt_partition_rows(const gbdt_rows* src /* host */, const gbdt_rows* dst /* host */,
                         const gbdt_node* nodes, const gbdt_split* splits, const int32_t* list,
