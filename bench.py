@@ -18,6 +18,10 @@ Output: one JSON line on stdout (progress goes to stderr).
              bytes n_v*(F + 4 + 8) + total_bins*12 per built node
   trees_per_s / ms_per_step  whole boosting steps, host wall clock
   cpu_baseline  the CPU oracle (single thread) on a bounded sample of trees
+  also       the same figures (value, roofline, trees_per_s, per-kernel
+             device time) for further workloads, 10 trees each: by default
+             the 50,000,000 x 28 one (64 uniform bins, depth 12), the largest,
+             whose histogram build is bound by HBM rather than by latency
 """
 from __future__ import annotations
 
@@ -110,46 +114,10 @@ def cpu_baseline(k, seconds_budget):
                        "(no subtraction), single thread" % (n_trees, wl["n_trees"]))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed trees (default: the workload's tree count)")
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-diag", action="store_true", help="skip the per-kernel timing pass")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="run only a plain 1 GiB device copy (reference for the HBM byte counters)")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import datagen
-    import histogram_split_finding_amd as g
-
-    if args.calibrate_copy:
-        nbytes = 1 << 30
-        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / 3
-        print(json.dumps({"calibration": "plain device copy", "bytes_read": nbytes, "bytes_written": nbytes,
-                          "copies": 3, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
-        return
-
-    k = args.workload
+def measure(g, datagen, torch, k, K, W, diag):
+    """Grows W untimed then K timed trees of workload k on the GPU; with diag,
+    K more trees with per-kernel events for the histogram roofline."""
     wl = dict(datagen.WORKLOADS[k])
-    K = args.steps if args.steps is not None else wl["n_trees"]
-    W = args.warmup
     log("generating workload %d (%s)" % (k, wl["name"]))
     bins, label, nb = datagen.make_workload(k)
     n, F = bins.shape
@@ -203,7 +171,7 @@ def main():
         "trees_per_s": K / wall,
     }
 
-    if not args.no_diag:
+    if diag:
         # second pass: per-kernel device time with events on the library's stream
         lib = g.load()
         cap = 64 * (params.max_depth + 4) * K + 64
@@ -240,10 +208,68 @@ def main():
         out["built_rows_per_tree"] = rows / K
         log("hist: %d launches, %.3f ms total, %.1f GB/s algorithmic (%.1f%% of 8 TB/s)" % (
             launches, hist_ms, achieved, 100 * achieved / HBM_PEAK_GBS))
+    del bst, ds
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed trees (default: the workload's tree count)")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--also", type=int, nargs="*", default=[5],
+                    help="further workloads reported under 'also' (default: the 50M x 28 one, "
+                         "the largest; 10 trees each)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-diag", action="store_true", help="skip the per-kernel timing pass")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (reference for the HBM byte counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import datagen
+    import histogram_split_finding_amd as g
+
+    if args.calibrate_copy:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 3
+        print(json.dumps({"calibration": "plain device copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "copies": 3, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
+        return
+
+    out = None
+    secondary = []
+    for idx, k in enumerate([args.workload] + [w for w in args.also if w != args.workload]):
+        wl = dict(datagen.WORKLOADS[k])
+        K = (args.steps if args.steps is not None else wl["n_trees"]) if idx == 0 else min(wl["n_trees"], 10)
+        res = measure(g, datagen, torch, k, K, args.warmup, not args.no_diag)
+        if idx == 0:
+            out = res
+        else:
+            secondary.append({key: res[key] for key in ("config", "value", "unit", "steps", "ms_per_step",
+                                                        "trees_per_s", "roofline", "device_ms_per_tree")
+                              if key in res})
+    if secondary:
+        out["also"] = secondary
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)
-        out["cpu_baseline"] = cpu_baseline(k, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
