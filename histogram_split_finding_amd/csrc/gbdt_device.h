@@ -103,13 +103,67 @@ struct PlanEntry {
   int32_t node, begin, count, feature, threshold_bin, n_left;
 };
 
-// LDS of the planner: sh [32], spre [kPlanLdsEntries + 1], stage [kPlanStage].
+constexpr int kPlanSizeBuckets = 64;  // size classes of the histogram tiles' largest-first order
+constexpr int kPlanSortMinTiles = 768;  // smaller histogram plans (about one round) keep node order
+
+// LDS of the planner: sh [32], spre [kPlanLdsEntries + 1], stage
+// [kPlanStage], and the size-class counters of the largest-first order.
 struct PlanLds {
   int32_t sh[32];
   int32_t n_multi;
   int32_t spre[kPlanLdsEntries + 1];
   PlanEntry stage[kPlanStage];
+  int32_t bucket[kPlanSizeBuckets];
 };
+
+// Size class of a tile of `size` rows (tiles hold at most tile_rows): 0 for
+// the largest, kPlanSizeBuckets - 1 for the smallest.
+__device__ __forceinline__ int32_t tile_size_class(int32_t size, int32_t tile_rows) {
+  // tile_rows < 2^24, so size * 64 fits 32 bits
+  const uint32_t k = ((uint32_t)(size < 0 ? 0 : size) * (uint32_t)kPlanSizeBuckets) /
+                     ((uint32_t)tile_rows + 1u);
+  return kPlanSizeBuckets - 1 - (int32_t)(k > kPlanSizeBuckets - 1 ? kPlanSizeBuckets - 1 : k);
+}
+
+// Launch position of a tile of class cls in a histogram plan: the tiles are
+// ordered by size class, largest first, so that the workgroups dispatched
+// last -- whose end is the launch's end -- carry the smallest tiles.  The
+// order within a class is arbitrary; each tile keeps its own index as its
+// partial slot, so no result depends on it.  bucket[] holds the classes'
+// next positions.
+__device__ __forceinline__ int32_t tile_order(int32_t* bucket, int32_t cls) {
+  return atomicAdd(&bucket[cls], 1);
+}
+
+// Counts the tiles of a node of `count` rows into their size classes: its
+// full tiles and, if any, its last partial tile (an empty node has one empty
+// tile).
+__device__ __forceinline__ void count_node_tiles(int32_t* bucket, int32_t count, int32_t tile_rows) {
+  const int32_t c = count < 0 ? 0 : count;
+  const int32_t full = c / tile_rows;
+  const int32_t rem = c - full * tile_rows;
+  if (full > 0) atomicAdd(&bucket[tile_size_class(tile_rows, tile_rows)], full);
+  if (rem > 0 || c == 0) atomicAdd(&bucket[tile_size_class(rem, tile_rows)], 1);
+}
+
+// bucket[c] := first launch position of class c (exclusive prefix of the
+// counts), by wave 0 (one class per lane); the workgroup synchronises
+// around it.
+__device__ __forceinline__ void tile_order_prefix(int32_t* bucket) {
+  static_assert(kPlanSizeBuckets == 64, "one size class per lane");
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int32_t v = bucket[lane];
+    int32_t x = v;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    bucket[lane] = x - v;
+  }
+  __syncthreads();
+}
 
 // The matrix column of a split's feature (-1 for an invalid split or a
 // feature outside the map's range).
@@ -136,7 +190,8 @@ __device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, in
                                  int32_t n, int32_t tile_rows, int32_t max_tiles,
                                  int32_t* __restrict__ prefix, TileDesc* __restrict__ desc,
                                  uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
-                                 bool with_split, int32_t* __restrict__ multi) {
+                                 bool with_split, int32_t* __restrict__ multi,
+                                 int32_t* bucket /* LDS [kPlanSizeBuckets] or nullptr */) {
   const int32_t total = spre[n];
   for (int32_t j = threadIdx.x; j <= n; j += blockDim.x) {
     prefix[j] = spre[j];
@@ -150,29 +205,40 @@ __device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, in
     }
   }
   const int32_t lim = total < max_tiles ? total : max_tiles;
-  for (int32_t t = threadIdx.x; t < lim; t += blockDim.x) {
-    int32_t lo = 0, hi = n - 1;
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) >> 1;
-      if (spre[mid] <= t) lo = mid; else hi = mid - 1;
+  // with `bucket`, the tiles' size classes are counted per node first (not
+  // when the plan overflows: its positions must stay below max_tiles)
+  if (total > max_tiles || total <= kPlanSortMinTiles) bucket = nullptr;
+  if (bucket != nullptr) {
+    for (int32_t j = threadIdx.x; j < n; j += blockDim.x) count_node_tiles(bucket, stage[j].count, tile_rows);
+    tile_order_prefix(bucket);
+  }
+  {
+    for (int32_t t = threadIdx.x; t < lim; t += blockDim.x) {
+      int32_t lo = 0, hi = n - 1;
+      while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (spre[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const PlanEntry pe = stage[lo];
+      const int32_t tf = spre[lo];
+      TileDesc d;
+      d.node = pe.node;
+      d.r0 = pe.begin + (t - tf) * tile_rows;
+      d.r1 = d.r0 + tile_rows < pe.begin + pe.count ? d.r0 + tile_rows : pe.begin + pe.count;
+      int32_t pos = t;
+      if (bucket != nullptr) pos = tile_order(bucket, tile_size_class(d.r1 - d.r0, tile_rows));
+      d.ntiles = spre[lo + 1] - tf;
+      d.tfirst = tf;
+      d.begin = pe.begin;
+      d.count = pe.count;
+      d.feature = pe.feature;
+      d.threshold_bin = pe.threshold_bin;
+      d.n_left = pe.n_left;
+      d.split_valid = with_split && pe.feature >= 0;
+      d.slot = t;
+      desc[pos] = d;
+      if (status != nullptr) status[t] = 0ull;
     }
-    const PlanEntry pe = stage[lo];
-    const int32_t tf = spre[lo];
-    TileDesc d;
-    d.node = pe.node;
-    d.r0 = pe.begin + (t - tf) * tile_rows;
-    d.r1 = d.r0 + tile_rows < pe.begin + pe.count ? d.r0 + tile_rows : pe.begin + pe.count;
-    d.ntiles = spre[lo + 1] - tf;
-    d.tfirst = tf;
-    d.j = lo;
-    d.begin = pe.begin;
-    d.count = pe.count;
-    d.feature = pe.feature;
-    d.threshold_bin = pe.threshold_bin;
-    d.n_left = pe.n_left;
-    d.split_valid = with_split && pe.feature >= 0;
-    desc[t] = d;
-    if (status != nullptr) status[t] = 0ull;
   }
   for (int32_t t = lim + threadIdx.x; t < max_tiles; t += blockDim.x) desc[t].node = -1;
   __syncthreads();
@@ -202,7 +268,7 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
                                   uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
                                   const gbdt_split* __restrict__ splits,
                                   const int32_t* __restrict__ feature_col, int32_t n_features,
-                                  int32_t* __restrict__ multi, PlanLds& L) {
+                                  int32_t* __restrict__ multi, PlanLds& L, bool by_size) {
   const bool staged = n <= kPlanStage;
   const bool in_lds = n <= kPlanLdsEntries;
   const int32_t per = (n + blockDim.x - 1) / blockDim.x;
@@ -228,6 +294,7 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
     }
   }
   if (threadIdx.x == 0) L.n_multi = 0;
+  for (int c = threadIdx.x; c < kPlanSizeBuckets; c += blockDim.x) L.bucket[c] = 0;
   int32_t total;
   int32_t excl = block_exclusive_scan(local, &total, L.sh);
   if (staged) {
@@ -238,7 +305,7 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
     if (threadIdx.x == 0) L.spre[n] = total;
     __syncthreads();
     plan_emit(L.stage, L.spre, &L.n_multi, n, tile_rows, max_tiles, prefix, desc, status, ctrl,
-              splits != nullptr, multi);
+              splits != nullptr, multi, by_size ? L.bucket : nullptr);
     return;
   }
   // long lists: the prefix in LDS (up to kPlanLdsEntries) or global memory,
@@ -263,6 +330,15 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
   }
   __syncthreads();
   const int32_t lim = total < max_tiles ? total : max_tiles;
+  // an overflowing plan keeps positions below max_tiles; a plan of one round
+  // of workgroups has no tail to shorten
+  if (total > max_tiles || total <= kPlanSortMinTiles) by_size = false;
+  if (by_size) {
+    for (int32_t j = threadIdx.x; j < n; j += blockDim.x)
+      count_node_tiles(L.bucket, nodes[list[j]].count, tile_rows);
+    tile_order_prefix(L.bucket);
+  }
+  {
   for (int32_t t = threadIdx.x; t < lim; t += blockDim.x) {
     const int32_t* pre = in_lds ? L.spre : prefix;
     int32_t lo = 0, hi = n - 1;
@@ -290,15 +366,18 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
     d.r1 = d.r0 + tile_rows < pe.begin + pe.count ? d.r0 + tile_rows : pe.begin + pe.count;
     d.ntiles = pre[lo + 1] - tf;
     d.tfirst = tf;
-    d.j = lo;
     d.begin = pe.begin;
     d.count = pe.count;
     d.feature = pe.feature;
     d.threshold_bin = pe.threshold_bin;
     d.n_left = pe.n_left;
     d.split_valid = splits != nullptr && pe.feature >= 0;
-    desc[t] = d;
+    d.slot = t;
+    int32_t pos = t;
+    if (by_size) pos = tile_order(L.bucket, tile_size_class(d.r1 - d.r0, tile_rows));
+    desc[pos] = d;
     if (status != nullptr) status[t] = 0ull;
+  }
   }
   for (int32_t t = lim + threadIdx.x; t < max_tiles; t += blockDim.x) desc[t].node = -1;
   __syncthreads();

@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
   }
   __syncthreads();
   plan_tiles(nodes, lists + LL.build, grow ? 1 : 0, tile_rows, max_tiles, pa.hprefix, pa.hdesc,
-             nullptr, pa.ctrl, nullptr, nullptr, 0, pa.hmulti, lds);
+             nullptr, pa.ctrl, nullptr, nullptr, 0, pa.hmulti, lds, true);
 }
 
 // Steps 3-6 bookkeeping for level d, one workgroup: each level-d node either
@@ -166,6 +166,7 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t hist_target, int32_t hist_max_tiles_next) {
   __shared__ PlanLds lds;
   __shared__ int32_t shm[6 * 17];
+  for (int c = threadIdx.x; c < kPlanSizeBuckets; c += blockDim.x) lds.bucket[c] = 0;
   const int32_t first = tc->level_start[d];
   const int32_t cnt = tc->level_count[d];
   const int32_t S = tc->scale;
@@ -356,14 +357,14 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   // histogram plan (nodes to build)
   if (fast) {
     plan_emit(stP, spP, &lds.n_multi, t_split, part_tile, part_max_tiles, pa.prefix, pa.desc,
-              pa.status, pa.ctrl, true, nullptr);
+              pa.status, pa.ctrl, true, nullptr, nullptr);
     plan_emit(stH, spH, &lds.n_multi, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix,
-              pa.hdesc, nullptr, pa.ctrl, false, pa.hmulti);
+              pa.hdesc, nullptr, pa.ctrl, false, pa.hmulti, lds.bucket);
   } else {
     plan_tiles(nodes, split_list, t_split, part_tile, part_max_tiles, pa.prefix, pa.desc,
-               pa.status, pa.ctrl, splits, pa.feature_col, pa.n_features, nullptr, lds);
+               pa.status, pa.ctrl, splits, pa.feature_col, pa.n_features, nullptr, lds, false);
     plan_tiles(nodes, build_n, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix,
-               pa.hdesc, nullptr, pa.ctrl, nullptr, nullptr, 0, pa.hmulti, lds);
+               pa.hdesc, nullptr, pa.ctrl, nullptr, nullptr, 0, pa.hmulti, lds, true);
   }
 }
 
@@ -463,6 +464,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     if (d == 0) {
       h_tiles[d] = (rows_build + h_rows[d] - 1) / h_rows[d] + cap_build;
     } else {
+      // tiles <= t_eff <= target + nodes, or rows / tile_max + nodes when
+      // tile_max caps the size
       const int64_t by_max = (rows_build + tile_max - 1) / tile_max;
       h_tiles[d] = (by_max > target ? by_max : target) + cap_build;
     }

@@ -58,7 +58,8 @@ struct TileDesc {
   int32_t r0, r1;  // rows [r0, r1) of the tile
   int32_t ntiles;  // tiles of the node
   int32_t tfirst;  // first tile of the node
-  int32_t j;       // list position of the node
+  int32_t slot;    // the tile's index in its plan: histogram plans launch largest tiles
+                   // first, and a tile's partial lives at this index
   int32_t begin;   // the node's segment
   int32_t count;
   int32_t feature;        // partition plans: the node's split
@@ -127,8 +128,10 @@ inline int32_t hist_tile_max(int64_t n_rows) {
 }
 
 // Histogram tile rows for a level that builds `rows` rows (device and host):
-// about `target` tiles, at least min(kHistMinTileRows, tile_max) rows and at
-// most tile_max.
+// about `target` tiles of equal size, at least min(kHistMinTileRows,
+// tile_max) rows and at most tile_max.  A node's last tile is partial, so a
+// level has at most target + nodes tiles; the plan launches them largest
+// first.
 __host__ __device__ inline int32_t hist_tile_rows_for(int32_t rows, int32_t tile_max, int32_t target) {
   int32_t t = (rows + target - 1) / target;
   const int32_t lo = kHistMinTileRows < tile_max ? kHistMinTileRows : tile_max;

@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nod
   if (threadIdx.x == 0 && (raw < 0 || raw > list_cap)) dev_error(&ctrl->err, GBDT_E_SHAPE);
   const int32_t n = clamp_len(list_len, list_cap);
   plan_tiles(nodes, list, n, tile_rows, max_tiles, prefix, desc, status, ctrl, splits, feature_col,
-             n_features, multi, lds);
+             n_features, multi, lds, status == nullptr);
 }
 
 // -------------------------------------------------------------- gradients --
@@ -500,7 +500,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
       if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
       return;
     }
-    hist_bit_block<NW>(td, tile, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
+    hist_bit_block<NW>(td, td.slot, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
                        bit_stride, col_feature, q, bin_offset, skip_bin, total_bins, lds_bins, bits,
                        hist_g, hist_cnt, partial, ctrl, lds, s_inv, s_bit, sh_tot);
     return;
@@ -627,6 +627,11 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
         }
       }
     };
+    // the tile's last row, for the correction below, loaded with the first
+    // rows so that no round trip follows the loop
+    uint32_t x_last = *reinterpret_cast<const uint32_t*>(
+        tb + (__umul24((uint32_t)lr, (uint32_t)block_stride) + lane_off));
+    int64_t q_last = *reinterpret_cast<const int64_t*>(tq + (uint32_t(lr) << 3));
     load_half(base, xa, qa);
     load_half(base + H * RPI, xb, qb);
     int32_t steps = 0;
@@ -640,14 +645,14 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
       base = next;
       if (base >= nt) break;
     }
+    asm volatile("" : "+v"(x_last), "+v"(q_last));
     // the lane visited rows first_row + k RPI, k < steps * BATCH; those at or
     // past nt were row lr
     const int32_t valid = first_row < nt ? (nt - first_row + RPI - 1) / RPI : 0;
     const int32_t extra = steps * BATCH - valid;
     if (extra > 0) {
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(
-          tb + (__umul24((uint32_t)lr, (uint32_t)block_stride) + lane_off));
-      const int64_t qq = *reinterpret_cast<const int64_t*>(tq + (uint32_t(lr) << 3));
+      const uint32_t x = x_last;
+      const int64_t qq = q_last;
       const uint64_t pk = (((uint64_t)qq << bits) | 1ull) * (0ull - (uint64_t)extra);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -678,7 +683,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
       hist_g[int64_t(v) * total_bins + gidx] = (int64_t)(x - cc) >> bits;
       hist_cnt[int64_t(v) * total_bins + gidx] = (uint32_t)cc;
     } else {
-      partial[int64_t(tile) * total_bins + gidx] = x;
+      partial[int64_t(td.slot) * total_bins + gidx] = x;
     }
   }
 }
