@@ -456,6 +456,9 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   // tile_max); the bound below holds for every size it can choose
   const int32_t tile_max = hist_tile_max(n);
   const int32_t part_tile = part_tile_rows(n, X->n_blocks);
+  // the row buffers hold q as int32 when that is exact; the root level reads
+  // the int64 q of X's order
+  const bool q32 = driver_q32(n);
   const int32_t target = hist_target_tiles(X->n_blocks + (X->n_bit_features > 0 ? 1 : 0));
   for (int32_t d = 0; d <= D; ++d) {
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
@@ -492,7 +495,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     const int64_t lvl_off = (int64_t(1) << d) - 1;
     const int32_t cap_lvl = int32_t(1) << d;
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
-    rc = launch_hist(src, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s);
+    rc = launch_hist(src, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s,
+                     q32 && d > 0);
     if (rc) return rc;
     rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
                             h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s);
@@ -513,7 +517,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     // the rows of the last level's children are never read again: the
     // prediction update routes rows through the finished tree instead
     if (d + 1 < D) {
-      rc = launch_partition(src, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], part_tile, s);
+      rc = launch_partition(src, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], part_tile, s,
+                            q32 && d > 0, q32);
       if (rc) return rc;
       src = dst;
     }

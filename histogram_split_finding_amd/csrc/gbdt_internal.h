@@ -145,9 +145,11 @@ __host__ __device__ inline int32_t hist_tile_rows_for(int32_t rows, int32_t tile
 bool same_layout(const gbdt_matrix& a, const gbdt_matrix& b);
 int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft);
 int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
+// q32: src.q holds int32 elements (the tree driver's row buffers, see
+// driver_q32); otherwise int64 as the ABI declares.
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
-                WsCtrl* ctrl, hipStream_t s);
+                WsCtrl* ctrl, hipStream_t s, bool q32 = false);
 int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_cap,
                        const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
                        const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s);
@@ -155,9 +157,17 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
                 const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
                 const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
                 const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s);
+// qin32 / qout32: src.q / dst.q hold int32 elements (the tree driver's row
+// buffers); otherwise int64.
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
-                     hipStream_t s);
+                     hipStream_t s, bool qin32 = false, bool qout32 = false);
+
+// Whether the tree driver stores q as int32 in its two row buffers: exact
+// when every |q| <= 2^(52 - ceil(log2 n)) fits 31 bits, i.e. n >= 2^22 rows
+// (|q| <= 2^30); it saves 4 of 8 bytes per row in every partition and every
+// histogram below the root.
+inline bool driver_q32(int64_t n_rows) { return ceil_log2(n_rows) >= 22; }
 
 // Per-kernel device timing (the backend's diagnostics): when enabled, every
 // launch of the library is bracketed by two hipEvents on its stream.

@@ -249,6 +249,14 @@ __global__ void __launch_bounds__(256) k_check_q(const int64_t* __restrict__ q, 
 
 // -------------------------------------------------------------- histogram --
 constexpr int kHistThreads = 1024;
+
+// q of row r from a buffer of int64 or, with Q32, int32 elements (the tree
+// driver stores q as int32 in its row buffers when |q| <= 2^30).
+template <bool Q32>
+__device__ __forceinline__ int64_t q_at(const void* q, int64_t r) {
+  if (Q32) return (int64_t) reinterpret_cast<const int32_t*>(q)[r];
+  return reinterpret_cast<const int64_t*>(q)[r];
+}
 // An LDS address as a pointer: a 32-bit byte address used by the ds
 // instruction as it stands (the dynamic LDS of the histogram starts at 0).
 typedef __attribute__((address_space(3))) uint64_t LdsU64;
@@ -327,11 +335,11 @@ inline int load_unit_for(int32_t block_stride) {
 constexpr int kBitStage = 1024;   // bit features whose output table is staged in LDS
 constexpr int kMaxBitWords = 128; // words per row of the bit block, at most
 
-template <int NW>
+template <int NW, bool Q32>
 __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* __restrict__ bins,
                                int64_t row_capacity, int32_t n_blocks, int32_t block_stride,
                                int32_t n_features, int32_t n_bit, int32_t bit_stride,
-                               const int32_t* __restrict__ col_feature, const int64_t* __restrict__ q,
+                               const int32_t* __restrict__ col_feature, const void* __restrict__ q,
                                const int32_t* __restrict__ bin_offset,
                                const int32_t* __restrict__ skip_bin, int32_t total_bins,
                                int32_t lds_bins, int32_t bits,
@@ -383,7 +391,7 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
         const int64_t rr = r + int64_t(u) * rpi;
         const bool ok = rr < r1;
         x[u] = ok ? wb[rr * nwords + w] : 0u;
-        qq[u] = ok ? q[rr] : 0;
+        qq[u] = ok ? q_at<Q32>(q, rr) : 0;
       }
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
@@ -466,11 +474,11 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
 // zeroed and read back.  A node covered by one tile writes its decoded
 // histogram straight to hist; otherwise the tile writes its packed partial
 // (global bin order) for k_hist_reduce.  BITS: the layout has a bit block.
-template <int D, bool BITS>
+template <int D, bool BITS, bool Q32>
 __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_hist(
     const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t n_blocks,
     int32_t block_features, int32_t block_stride, int32_t n_features, int32_t n_bit,
-    int32_t bit_stride, const int32_t* __restrict__ col_feature, const int64_t* __restrict__ q,
+    int32_t bit_stride, const int32_t* __restrict__ col_feature, const void* __restrict__ q,
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ skip_bin,
     int32_t total_bins, int32_t lds_bins, const TileDesc* __restrict__ desc, int32_t bits,
     int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
@@ -500,7 +508,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
       if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
       return;
     }
-    hist_bit_block<NW>(td, td.slot, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
+    hist_bit_block<NW, Q32>(td, td.slot, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
                        bit_stride, col_feature, q, bin_offset, skip_bin, total_bins, lds_bins, bits,
                        hist_g, hist_cnt, partial, ctrl, lds, s_inv, s_bit, sh_tot);
     return;
@@ -569,7 +577,8 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   // 32-bit lane offset (a tile holds < 2^24 rows of at most 32 bytes)
   const int32_t nt = (int32_t)(r1 - r0);    // rows of the tile
   const uint8_t* __restrict__ tb = bins + (int64_t(blk) * row_capacity + r0) * block_stride;
-  const char* __restrict__ tq = reinterpret_cast<const char*>(q + r0);
+  constexpr uint32_t QSH = Q32 ? 2u : 3u;  // log2 of q's element size
+  const char* __restrict__ tq = reinterpret_cast<const char*>(q) + (r0 << QSH);
   const int32_t first_row = wid * RPW + lane / D;  // the lane's first row in the tile
   int32_t base = wid * RPW;
   if (base < nt) {
@@ -595,12 +604,12 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
         const int32_t rr = first + u * RPI + (lane / D);
         const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
         x[u] = *reinterpret_cast<const uint32_t*>(tb + (__umul24(rc, (uint32_t)block_stride) + lane_off));
-        if (D == 1) qq[u < NQ ? u : 0] = *reinterpret_cast<const int64_t*>(tq + (rc << 3));
+        if (D == 1) qq[u < NQ ? u : 0] = q_at<Q32>(tq + (rc << QSH), 0);
       }
       if (D >= 2) {
         const int32_t rr = first + (c % H) * RPI + (lane / D);
         const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
-        qq[0] = *reinterpret_cast<const int64_t*>(tq + (rc << 3));
+        qq[0] = q_at<Q32>(tq + (rc << QSH), 0);
       }
     };
     auto add_half = [&](uint32_t* x, int64_t* qq) {
@@ -631,7 +640,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     // rows so that no round trip follows the loop
     uint32_t x_last = *reinterpret_cast<const uint32_t*>(
         tb + (__umul24((uint32_t)lr, (uint32_t)block_stride) + lane_off));
-    int64_t q_last = *reinterpret_cast<const int64_t*>(tq + (uint32_t(lr) << 3));
+    int64_t q_last = q_at<Q32>(tq + (uint32_t(lr) << QSH), 0);
     load_half(base, xa, qa);
     load_half(base + H * RPI, xb, qb);
     int32_t steps = 0;
@@ -1191,11 +1200,12 @@ __device__ __forceinline__ void row_store(uint8_t* p, const RowData<ND>& d) {
 // and the bit block are loaded and stored row by row after that.
 template <int ND, int K>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
-    const uint8_t* __restrict__ sbins, const int64_t* __restrict__ sq,
-    const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, int64_t* __restrict__ dq,
+    const uint8_t* __restrict__ sbins, const void* __restrict__ sq,
+    const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, void* __restrict__ dq,
     int32_t* __restrict__ drid, int64_t row_capacity, int32_t n_blocks, int32_t block_features,
     int32_t block_stride, int32_t n_features, int32_t n_bit, int32_t bit_stride,
-    const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl) {
+    const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
+    int32_t qmode /* bit 0: sq holds int32, bit 1: dq holds int32 */) {
   constexpr int TILE = K * kPartThreads;
   constexpr int KE = K < 2 ? K : 2;  // rows per thread whose block 0 is loaded early
   __shared__ int32_t s_tile;
@@ -1232,6 +1242,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   const uint8_t* __restrict__ fcolp = sbins + int64_t(fblk) * row_capacity * block_stride + fcol;
   const uint8_t* __restrict__ sbits = sbins + int64_t(n_blocks) * row_capacity * block_stride;
   const uint32_t* __restrict__ fwordp = reinterpret_cast<const uint32_t*>(sbits) + (fk >> 5);
+  const uint32_t qsh = (qmode & 1) ? 2u : 3u;  // log2 of the source q's element size
   // loads that need only the descriptor, unconditional (a row past the tile
   // end rereads its last row and is ignored), so none waits behind a branch
   int32_t fb[K];
@@ -1241,29 +1252,36 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   // (the split feature's bytes first: loads complete in order, and the
   // flags wait only for them while the rows are still in flight)
   if (rows > 0) {
+    // one dword load either way (the byte's aligned dword, or the bit's
+    // word), so no branch separates these loads from the ones below
+    const uint8_t* __restrict__ fbase =
+        fbit ? reinterpret_cast<const uint8_t*>(fwordp) : fcolp - (fcol & 3);
+    const int64_t frow = fbit ? int64_t(nwords) * 4 : int64_t(block_stride);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int32_t i = k * kPartThreads + threadIdx.x;
       const int64_t sr = r0 + (i < rows ? i : rows - 1);
-      if (fbit)
-        fb[k] = (int32_t)fwordp[sr * nwords];
-      else
-        fb[k] = (int32_t)fcolp[sr * block_stride];
+      fb[k] = (int32_t)*reinterpret_cast<const uint32_t*>(fbase + sr * frow);
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int32_t i = k * kPartThreads + threadIdx.x;
       const int64_t sr = r0 + (i < rows ? i : rows - 1);
-      qv[k] = sq[sr];
+      // one 8-byte load either way, so no branch separates the loads: an
+      // int32 q is the low half (the buffer holds 8 bytes per row, so the
+      // read stays inside it); an int32 destination takes the low half of
+      // either (the driver narrows only q that fit), an int64 one comes from
+      // an int64 source
+      qv[k] = *reinterpret_cast<const int64_t*>(reinterpret_cast<const char*>(sq) + (sr << qsh));
       rv[k] = drid != nullptr ? (srid != nullptr ? srid[sr] : (int32_t)sr) : 0;
       // with no byte block (ND == 1, block_stride 0) this rereads the first
       // dword of the bit block, and the value is never stored
       if (k < KE) row_load<ND>(sbins + sr * block_stride, rd[k]);
     }
-    if (fbit) {
+    const uint32_t fsh = fbit ? (uint32_t)(fk & 31) : 8u * (uint32_t)(fcol & 3);
+    const uint32_t fmask = fbit ? 1u : 0xffu;
 #pragma unroll
-      for (int k = 0; k < K; ++k) fb[k] = (int32_t)(((uint32_t)fb[k] >> (fk & 31)) & 1u);
-    }
+    for (int k = 0; k < K; ++k) fb[k] = (int32_t)(((uint32_t)fb[k] >> fsh) & fmask);
   }
   if (!split_ok && threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
 
@@ -1336,7 +1354,10 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   for (int k = 0; k < K; ++k) {
     const int32_t d = dpos[k];
     if (d < 0) continue;
-    dq[d] = qv[k];
+    if (qmode & 2)
+      reinterpret_cast<int32_t*>(dq)[d] = (int32_t)qv[k];
+    else
+      reinterpret_cast<int64_t*>(dq)[d] = qv[k];
     if (drid != nullptr) drid[d] = rv[k];
     if (n_blocks > 0) row_store<ND>(dbins + int64_t(d) * block_stride, rd[k]);
   }
@@ -1798,9 +1819,14 @@ int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst) {
   return GBDT_OK;
 }
 
+template <bool B, bool Q>
+static auto hist_kernel(int D) -> decltype(&k_hist<8, B, Q>) {
+  return D == 8 ? k_hist<8, B, Q> : D == 4 ? k_hist<4, B, Q> : D == 2 ? k_hist<2, B, Q> : k_hist<1, B, Q>;
+}
+
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
-                WsCtrl* ctrl, hipStream_t s) {
+                WsCtrl* ctrl, hipStream_t s, bool q32) {
   const int64_t n_rows = src.X.n_rows > 0 ? src.X.n_rows : 1;
   const int32_t bits = pack_bits_for(n_rows);
   const bool has_bytes = src.X.n_features > src.X.n_bit_features;
@@ -1812,10 +1838,8 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
                      sizeof(int32_t) * size_t(2 * kHistRowSlots + kMaxBitWords + kBitStage);
   const int32_t nd = has_bytes ? src.X.block_stride / 4 : 1;  // dwords per row (<= 8)
   const int D = nd <= 1 ? 1 : (nd <= 2 ? 2 : (nd <= 4 ? 4 : 8));
-  auto kern = has_bits ? (D == 8 ? k_hist<8, true> : D == 4 ? k_hist<4, true>
-                                    : D == 2 ? k_hist<2, true> : k_hist<1, true>)
-                       : (D == 8 ? k_hist<8, false> : D == 4 ? k_hist<4, false>
-                                    : D == 2 ? k_hist<2, false> : k_hist<1, false>);
+  auto kern = has_bits ? (q32 ? hist_kernel<true, true>(D) : hist_kernel<true, false>(D))
+                       : (q32 ? hist_kernel<false, true>(D) : hist_kernel<false, false>(D));
   const unsigned gy = (unsigned)(src.X.n_blocks + (has_bits ? 1 : 0));
   diag_begin(kDiagHist, s);
   hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles, gy), dim3(kHistThreads), lds, s, src.X.bins,
@@ -1882,7 +1906,7 @@ static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K>) {
 
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
-                     hipStream_t s) {
+                     hipStream_t s, bool qin32, bool qout32) {
   const int32_t nd = src.X.n_blocks > 0 ? src.X.block_stride / 4 : 1;
   decltype(&k_partition<1, 2>) kern = nullptr;
   if (tile_rows == 2 * kPartThreads)
@@ -1896,7 +1920,8 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
   hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s, src.X.bins, src.q,
                      src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
                      src.X.block_features, src.X.block_stride, src.X.n_features,
-                     src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl);
+                     src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl,
+                     (qin32 ? 1 : 0) | (qout32 ? 2 : 0));
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_partition");
   return GBDT_OK;
