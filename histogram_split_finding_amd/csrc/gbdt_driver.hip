@@ -503,7 +503,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     if (rc) return rc;
     rc = launch_find(b->hist_g, b->hist_cnt, *ft, nodes_out, b->lists + LL.find + lvl_off,
                      &tc->n_find[d], cap_lvl, *p, &tc->scale, b->splits,
-                     b->lists + LL.find_par + lvl_off, b->lists + LL.find_sib + lvl_off, pa.ctrl, s);
+                     b->lists + LL.find_par + lvl_off, b->lists + LL.find_sib + lvl_off, pa.ctrl, s,
+                     reinterpret_cast<FindCand*>(w + WL.fcand));
     if (rc) return rc;
     diag_begin(kDiagLevel, s);
     hipLaunchKernelGGL(k_level, dim3(1), dim3(1024), 0, s, d, D, nodes_out, b->splits, tc, b->lists,

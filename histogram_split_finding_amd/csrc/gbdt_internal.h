@@ -10,6 +10,23 @@
 
 namespace gbdt {
 
+// Split search over wide histograms: a node's features are cut into chunks
+// (a feature belongs to the chunk of its first bin, chunks of kFindChunk
+// bins), one workgroup per (node, chunk), and a merge picks each node's
+// best chunk candidate.
+constexpr int kFindChunk = 2048;
+constexpr int kFindChunkMinBins = 4096;  // histograms of more bins take the chunked search
+inline int32_t find_chunks(int32_t total_bins) {
+  return total_bins > kFindChunkMinBins ? (total_bins + kFindChunk - 1) / kFindChunk : 1;
+}
+// The best candidate of one (node, chunk): gain and order key (0 = none).
+struct FindCand {
+  double gain;
+  int32_t key, feature, threshold_bin, n_left;
+  int64_t g_left;
+};
+static_assert(sizeof(FindCand) == 32, "candidate record is 32 bytes");
+
 // Workspace layout.  Offsets are multiples of 256 bytes.
 struct WsCtrl {
   int32_t err;          // first device-side error code (0 = none)
@@ -81,6 +98,7 @@ struct WsLayout {
   size_t prefix;      // int32[max_list + 2]: partition plan
   size_t hprefix;     // int32[max_list + 2]: histogram plan
   size_t hmulti;      // int32[max_list + 2]: histogram plan, nodes of several tiles
+  size_t fcand;       // FindCand[max_list * find_chunks]: split search, best per chunk
   size_t status;      // uint64[status_cap]
   size_t hpart;       // uint64[hpart_tiles * total_bins]
   size_t total;
@@ -156,7 +174,7 @@ int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_c
 int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,
                 const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
                 const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
-                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s);
+                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s, FindCand* cand = nullptr);
 // qin32 / qout32: src.q / dst.q hold int32 elements (the tree driver's row
 // buffers); otherwise int64.
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,

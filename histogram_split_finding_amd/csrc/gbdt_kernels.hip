@@ -93,6 +93,8 @@ WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
   off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
   L.hmulti = off;
   off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
+  L.fcand = off;
+  off = align256(off + sizeof(FindCand) * size_t(max_list) * size_t(find_chunks(total_bins)));
   L.status = off;
   off = align256(off + sizeof(uint64_t) * size_t(L.status_cap));
   L.hpart = off;
@@ -862,7 +864,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_len, int32_t list_cap,
     FindParams fp, const int32_t* __restrict__ scale, gbdt_split* __restrict__ splits,
     const int32_t* __restrict__ sub_par, const int32_t* __restrict__ sub_sib,
-    int32_t* __restrict__ err) {
+    int32_t* __restrict__ err, int32_t n_chunks, FindCand* __restrict__ cand) {
   constexpr int NW = THREADS / 64;
   __shared__ int64_t sw_g[NW];
   __shared__ int32_t sw_c[NW];
@@ -874,18 +876,33 @@ __global__ void __launch_bounds__(THREADS) k_find(
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int32_t j = blockIdx.x;  // < list_cap (the grid)
+  const int32_t chunk = blockIdx.y;
   const int32_t raw_len = *list_len;
   const int32_t v = list[j];
   const int32_t S = *scale;
   const int32_t par = sub_par != nullptr ? sub_par[j] : -1;
   const int32_t sib = sub_par != nullptr ? sub_sib[j] : -1;
+  // this workgroup's bins [blo, bhi): all of them, or with n_chunks > 1 the
+  // features whose first bin lies in [chunk * kFindChunk, + kFindChunk)
+  int32_t blo = 0, bhi = total_bins;
+  if (n_chunks > 1) {
+    const int32_t nlo = chunk * kFindChunk;
+    const int32_t nhi = nlo + kFindChunk < total_bins ? nlo + kFindChunk : total_bins;
+    const int32_t fa = bin_feature[nlo < total_bins ? nlo : total_bins - 1];
+    const int32_t fz = bin_feature[nhi - 1];
+    const int32_t oa = bin_offset[fa];
+    const int32_t ff = oa < nlo ? fa + 1 : fa;  // the chunk's first feature
+    blo = ff <= fz ? bin_offset[ff] : 0;
+    bhi = ff <= fz ? bin_offset[fz + 1] : 0;
+    if (nlo >= total_bins) blo = bhi = 0;
+  }
   int32_t f[kFindE + 2];  // features of bins b0-1 .. b0+kFindE of the first pass
   {
-    const int32_t b0 = threadIdx.x * kFindE;
+    const int32_t b0 = blo + threadIdx.x * kFindE;
 #pragma unroll
     for (int e = 0; e < kFindE + 2; ++e) {
       const int32_t b = b0 - 1 + e;
-      const bool inb = b >= 0 && b < total_bins;
+      const bool inb = b >= blo && b < bhi;
       const int32_t fv = bin_feature[inb ? b : 0];
       f[e] = inb ? fv : -1 - e;
     }
@@ -911,13 +928,13 @@ __global__ void __launch_bounds__(THREADS) k_find(
     s_carry_g = 0;
     s_carry_c = 0;
   }
-  for (int32_t pass = 0; pass < total_bins; pass += THREADS * kFindE) {
+  for (int32_t pass = blo; pass < bhi; pass += THREADS * kFindE) {
     const int32_t b0 = pass + threadIdx.x * kFindE;
-    if (pass > 0) {
+    if (pass > blo) {
 #pragma unroll
       for (int e = 0; e < kFindE + 2; ++e) {
         const int32_t b = b0 - 1 + e;
-        const bool inb = b >= 0 && b < total_bins;
+        const bool inb = b >= blo && b < bhi;
         const int32_t fv = bin_feature[inb ? b : 0];
         f[e] = inb ? fv : -1 - e;
       }
@@ -929,7 +946,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
 #pragma unroll
       for (int e = 0; e < kFindE; ++e) {
         const int32_t b = b0 + e;
-        const bool inb = b < total_bins;
+        const bool inb = b < bhi;
         const uint32_t cp = inb ? hc_p[b] : 0u, cs = inb ? hc_s[b] : 0u;
         g[e] = inb ? hg_p[b] - hg_s[b] : 0;
         c[e] = (int32_t)(cp - cs);
@@ -940,7 +957,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
 #pragma unroll
       for (int e = 0; e < kFindE; ++e) {
         const int32_t b = b0 + e;
-        const bool inb = b < total_bins;
+        const bool inb = b < bhi;
         g[e] = inb ? hg[b] : 0;
         c[e] = inb ? (int32_t)hc[b] : 0;
         fo[e] = bin_offset[inb ? f[e + 1] : 0];
@@ -956,7 +973,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
     int32_t rc = 0;
 #pragma unroll
     for (int e = 0; e < kFindE; ++e) {
-      const bool head = (b0 + e >= total_bins) || (f[e] != f[e + 1]);
+      const bool head = (b0 + e >= bhi) || (f[e] != f[e + 1]);
       if (head && first_head == kFindE) first_head = e;
       rg = head ? g[e] : rg + g[e];
       rc = head ? c[e] : rc + c[e];
@@ -1010,7 +1027,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
 #pragma unroll
     for (int e = 0; e < kFindE; ++e) {
       const int32_t b = b0 + e;
-      if (b >= total_bins) break;
+      if (b >= bhi) break;
       const int64_t gl = e < first_head ? g[e] + cin_g : g[e];
       const int32_t nlc = e < first_head ? c[e] + cin_c : c[e];
       if (f[e + 2] != f[e + 1]) continue;
@@ -1045,7 +1062,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
 #pragma unroll
       for (int e = 0; e < kFindE; ++e) {
         const int32_t b = b0 + e;
-        if (b < total_bins) {
+        if (b < bhi) {
           const bool head = e == 0 || f[e] != f[e + 1];
           hg[b] = head ? g[e] : g[e] - g[e - 1 < 0 ? 0 : e - 1];
           hc[b] = (uint32_t)(head ? c[e] : c[e] - c[e - 1 < 0 ? 0 : e - 1]);
@@ -1077,6 +1094,32 @@ __global__ void __launch_bounds__(THREADS) k_find(
       top_gain = r_gain[w];
       top_key = r_key[w];
     }
+  if (n_chunks > 1) {
+    // this chunk's best candidate for the merge (key 0: none)
+    FindCand* __restrict__ c = cand + int64_t(j) * n_chunks + chunk;
+    if (top_key != 0 && top_gain > 0.0) {
+      if (best_key == top_key) {
+        FindCand x;
+        x.gain = best_gain;
+        x.key = best_key;
+        x.feature = best_f;
+        x.threshold_bin = best_thr;
+        x.n_left = best_nl;
+        x.g_left = best_gl;
+        *c = x;
+      }
+    } else if (threadIdx.x == 0) {
+      FindCand x;
+      x.gain = 0.0;
+      x.key = 0;
+      x.feature = -1;
+      x.threshold_bin = -1;
+      x.n_left = 0;
+      x.g_left = 0;
+      *c = x;
+    }
+    return;
+  }
   if (top_key != 0 && top_gain > 0.0) {
     // the owner of the winning bin (each bin has one owner) writes the split
     if (best_key == top_key) {
@@ -1090,6 +1133,64 @@ __global__ void __launch_bounds__(THREADS) k_find(
       splits[v] = sp;
     }
   } else if (threadIdx.x == 0) {
+    gbdt_split sp;
+    sp.gain = 0.0;
+    sp.feature = -1;
+    sp.threshold_bin = -1;
+    sp.g_left = 0;
+    sp.n_left = 0;
+    sp.valid = 0;
+    splits[v] = sp;
+  }
+}
+
+// Merge of the chunked split search: one wave per listed node takes the best
+// of its chunks' candidates (larger gain, then the larger key: the smaller
+// global bin; keys are unique across chunks) and writes the split, or an
+// invalid split when no chunk has one.
+__global__ void __launch_bounds__(64) k_find_merge(const int32_t* __restrict__ list,
+                                                   const int32_t* __restrict__ list_len,
+                                                   int32_t list_cap, int32_t n_chunks,
+                                                   const FindCand* __restrict__ cand,
+                                                   gbdt_split* __restrict__ splits) {
+  const int32_t j = blockIdx.x;
+  const int32_t raw = *list_len;
+  const int32_t n = raw < 0 ? 0 : (raw > list_cap ? list_cap : raw);
+  if (j >= n) return;
+  const int32_t v = list[j];
+  const int lane = threadIdx.x;
+  double bg = 0.0;
+  int32_t bk = 0, bc = -1;
+  for (int32_t c = lane; c < n_chunks; c += 64) {
+    const FindCand x = cand[int64_t(j) * n_chunks + c];
+    if (x.key != 0 && better(x.gain, x.key, bg, bk)) {
+      bg = x.gain;
+      bk = x.key;
+      bc = c;
+    }
+  }
+  double wg = bg;
+  int32_t wk = bk;
+  argmax_step<0xB1, 0xF>(wg, wk);
+  argmax_step<0x4E, 0xF>(wg, wk);
+  argmax_step<0x141, 0xF>(wg, wk);
+  argmax_step<0x140, 0xF>(wg, wk);
+  argmax_step<0x142, 0xA>(wg, wk);
+  argmax_step<0x143, 0xC>(wg, wk);
+  const int32_t top_k = __builtin_amdgcn_readlane(wk, 63);  // the wave's best key (row_bcast:31 ends in lane 63)
+  if (top_k != 0) {
+    if (bk == top_k && bc >= 0) {
+      const FindCand x = cand[int64_t(j) * n_chunks + bc];
+      gbdt_split sp;
+      sp.gain = x.gain;
+      sp.feature = x.feature;
+      sp.threshold_bin = x.threshold_bin;
+      sp.g_left = x.g_left;
+      sp.n_left = x.n_left;
+      sp.valid = 1;
+      splits[v] = sp;
+    }
+  } else if (lane == 0) {
     gbdt_split sp;
     sp.gain = 0.0;
     sp.feature = -1;
@@ -1873,17 +1974,31 @@ int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_c
 int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,
                 const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
                 const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
-                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s) {
+                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s, FindCand* cand) {
   FindParams fp{p.reg_lambda, p.gamma, p.min_child_weight, p.min_samples_leaf};
+  const int32_t nch = cand != nullptr ? find_chunks(ft.total_bins) : 1;
+  diag_begin(kDiagFind, s);
+  if (nch > 1) {
+    // whole features of up to kFindChunk + 255 bins: one or two passes of 256 x kFindE
+    hipLaunchKernelGGL(k_find<256>, dim3((unsigned)list_cap, (unsigned)nch), dim3(256), 0, s, hist_g,
+                       hist_cnt, ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
+                       list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
+                       ctrl != nullptr ? &ctrl->err : nullptr, nch, cand);
+    GBDT_LAUNCH_CHECK("k_find");
+    hipLaunchKernelGGL(k_find_merge, dim3((unsigned)list_cap), dim3(64), 0, s, list, list_len,
+                       list_cap, nch, (const FindCand*)cand, splits);
+    diag_end(s);
+    GBDT_LAUNCH_CHECK("k_find_merge");
+    return GBDT_OK;
+  }
   // the fewest threads whose kFindE bins each cover the bins in one pass
   const int32_t per_pass = (ft.total_bins + kFindE - 1) / kFindE;
   const int threads = per_pass <= 256 ? 256 : (per_pass <= 512 ? 512 : 1024);
   auto kern = threads == 256 ? k_find<256> : (threads == 512 ? k_find<512> : k_find<1024>);
-  diag_begin(kDiagFind, s);
   hipLaunchKernelGGL(kern, dim3((unsigned)list_cap), dim3(threads), 0, s, hist_g, hist_cnt,
                      ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
                      list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
-                     ctrl != nullptr ? &ctrl->err : nullptr);
+                     ctrl != nullptr ? &ctrl->err : nullptr, 1, (FindCand*)nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_find");
   return GBDT_OK;
@@ -2224,12 +2339,17 @@ int gbdt_find_best_splits(const int64_t* hist_g, const uint32_t* hist_cnt,
     return fail(GBDT_E_ARG, "bad feature table");
   if (list_cap < 0) return fail(GBDT_E_ARG, "negative capacity");
   if (list_cap == 0) return GBDT_OK;
-  (void)ws;
-  (void)ws_bytes;
+  // a workspace sized for list_cap entries and these bins holds the chunked
+  // search's candidates; without one the search runs one workgroup per node
+  FindCand* cand = nullptr;
+  if (ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255) == 0) {
+    const WsLayout L = ws_layout(1, list_cap, ft->total_bins);
+    if (ws_bytes >= L.total) cand = reinterpret_cast<FindCand*>(static_cast<char*>(ws) + L.fcand);
+  }
   // without the subtraction lists the kernel only reads the histograms
   return launch_find(const_cast<int64_t*>(hist_g), const_cast<uint32_t*>(hist_cnt), *ft, nodes, list,
                      list_len, list_cap, *p, scale, splits, nullptr, nullptr, nullptr,
-                     reinterpret_cast<hipStream_t>(stream));
+                     reinterpret_cast<hipStream_t>(stream), cand);
 }
 
 int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_node* nodes,
