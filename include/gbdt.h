@@ -338,7 +338,10 @@ int gbdt_subtract_histograms(int64_t* hist_g, uint32_t* hist_cnt, int32_t total_
  * that order, no contraction).  splits[v] gets the candidate with the largest
  * gain, ties to the smaller feature, then the smaller bin; valid = 1 iff that
  * gain is strictly positive.  Node totals come from nodes[v].gsum / count;
- * S from *scale.
+ * S from *scale.  ws may be NULL; a 256-byte aligned workspace of at least
+ * gbdt_workspace_bytes(1, list_cap, total_bins) bytes lets a histogram of
+ * more than 4096 bins be searched by several workgroups per node (chunks of
+ * whole features) and a merge; the result is the same either way.
  */
 int gbdt_find_best_splits(const int64_t* hist_g, const uint32_t* hist_cnt,
                           const gbdt_features* ft /* host */, const gbdt_node* nodes,
