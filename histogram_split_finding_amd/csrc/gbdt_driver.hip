@@ -455,10 +455,9 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   // `target` tiles of at least min(kHistMinTileRows, tile_max) rows, at most
   // tile_max); the bound below holds for every size it can choose
   const int32_t tile_max = hist_tile_max(n);
-  const int32_t part_tile = part_tile_rows(n, X->n_blocks);
-  // the row buffers hold q as int32 when that is exact; the root level reads
-  // the int64 q of X's order
+  // q is int32 (original order and both row buffers) when that is exact
   const bool q32 = driver_q32(n);
+  const int32_t part_tile = part_tile_rows(n, X->n_blocks, q32);
   const int32_t target = hist_target_tiles(X->n_blocks + (X->n_bit_features > 0 ? 1 : 0));
   for (int32_t d = 0; d <= D; ++d) {
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
@@ -477,8 +476,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
       return fail(GBDT_E_INTERNAL, "tile bound exceeds the workspace");
   }
 
-  rc = gbdt_compute_gradients(pred, label, n, b->q, &tc->scale, &tc->gsum_root, b->ws, b->ws_bytes,
-                              stream);
+  rc = launch_gradients(pred, label, n, b->q, q32, &tc->scale, &tc->gsum_root, b->ws, b->ws_bytes, s);
   if (rc) return rc;
   diag_begin(kDiagTreeInit, s);
   hipLaunchKernelGGL(k_tree_init, dim3(1), dim3(1024), 0, s, nodes_out, b->splits, tc, b->lists, LL,
@@ -495,8 +493,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     const int64_t lvl_off = (int64_t(1) << d) - 1;
     const int32_t cap_lvl = int32_t(1) << d;
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
-    rc = launch_hist(src, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s,
-                     q32 && d > 0);
+    rc = launch_hist(src, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s, q32);
     if (rc) return rc;
     rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
                             h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s);
@@ -518,8 +515,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     // the rows of the last level's children are never read again: the
     // prediction update routes rows through the finished tree instead
     if (d + 1 < D) {
-      rc = launch_partition(src, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], part_tile, s,
-                            q32 && d > 0, q32);
+      rc = launch_partition(src, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], part_tile, s, q32, q32);
       if (rc) return rc;
       src = dst;
     }

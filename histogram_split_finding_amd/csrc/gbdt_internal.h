@@ -49,16 +49,20 @@ constexpr int kGradBlocks = 1024;     // grid of the gradient kernels
 #define GBDT_TWO_GROUPS __attribute__((amdgpu_waves_per_eu(8, 8)))
 
 constexpr int kPartTileRows = 2048;   // rows per partition tile (the smaller size; bounds use it)
-constexpr int kPartTileRowsLarge = 4096;
+constexpr int kPartTileRowsMid = 4096;
+constexpr int kPartTileRowsLarge = 8192;
 constexpr int64_t kPartLargeRows = int64_t(1) << 22;  // matrices from this size take the larger tiles
 
-// Rows per partition tile for a matrix of n rows in n_blocks byte blocks:
-// larger tiles carry more bytes per latency chain (ticket, descriptor,
-// flags, look-back) on large matrices of one block; small matrices keep more
-// tiles than workgroup slots, and several blocks need the registers for
-// double-buffering the blocks.
-inline int32_t part_tile_rows(int64_t n_rows, int32_t n_blocks) {
-  return (n_rows >= kPartLargeRows && n_blocks <= 1) ? kPartTileRowsLarge : kPartTileRows;
+// Rows per partition tile for a matrix of n rows in n_blocks byte blocks
+// whose moved q is int32 (q32) or int64: larger tiles carry more bytes per
+// latency chain (ticket, descriptor, flags, look-back) on large matrices of
+// one block (8192 rows when q moves as int32; with int64 q that kernel would
+// exceed the 64 registers of two workgroups per CU, so 4096); small matrices
+// keep more tiles than workgroup slots, and several blocks need the
+// registers for double-buffering the blocks.
+inline int32_t part_tile_rows(int64_t n_rows, int32_t n_blocks, bool q32) {
+  if (n_rows < kPartLargeRows || n_blocks > 1) return kPartTileRows;
+  return q32 ? kPartTileRowsLarge : kPartTileRowsMid;
 }
 constexpr int kHistMinTileRows = 1024;
 constexpr int kHistTargetTiles = 1024;    // workgroups per histogram launch to aim for
@@ -181,10 +185,15 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
                      hipStream_t s, bool qin32 = false, bool qout32 = false);
 
-// Whether the tree driver stores q as int32 in its two row buffers: exact
-// when every |q| <= 2^(52 - ceil(log2 n)) fits 31 bits, i.e. n >= 2^22 rows
-// (|q| <= 2^30); it saves 4 of 8 bytes per row in every partition and every
-// histogram below the root.
+// Gradients and the fixed-point grid (gbdt_compute_gradients); q32: q gets
+// int32 elements (the tree driver, ceil(log2 n) >= 22), otherwise int64.
+int launch_gradients(const double* pred, const float* label, int64_t n, void* q, bool q32,
+                     int32_t* scale, int64_t* gsum, void* ws, size_t ws_bytes, hipStream_t s);
+
+// Whether the tree driver stores q as int32 (in its original-order buffer and
+// its two row buffers): exact when every |q| <= 2^(52 - ceil(log2 n)) fits 31
+// bits, i.e. n > 2^21 rows (|q| <= 2^30); it saves 4 of 8 bytes per row in
+// every histogram and every partition.
 inline bool driver_q32(int64_t n_rows) { return ceil_log2(n_rows) >= 22; }
 
 // Per-kernel device timing (the backend's diagnostics): when enabled, every

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "gbdt.h"
@@ -195,11 +196,13 @@ __global__ void __launch_bounds__(256) k_grad_max(const double* __restrict__ pre
 }
 
 // Pass 2: M = max of the partial maxima (every block derives the same S),
-// S = 52 - e - L, q_i = rint(ldexp(g_i, S)) and the sum of q.
+// S = 52 - e - L, q_i = rint(ldexp(g_i, S)) and the sum of q.  QT: int64, or
+// int32 for the tree driver when L >= 22 (then |q_i| <= 2^(52-L) <= 2^30).
+template <typename QT>
 __global__ void __launch_bounds__(256) k_grad_q(const double* __restrict__ pred,
                                                 const float* __restrict__ label, int64_t n,
                                                 int32_t log2n, const double* __restrict__ part,
-                                                int32_t nparts, int64_t* __restrict__ q,
+                                                int32_t nparts, QT* __restrict__ q,
                                                 int32_t* __restrict__ scale,
                                                 int64_t* __restrict__ gsum) {
   __shared__ double shm[4];
@@ -222,7 +225,7 @@ __global__ void __launch_bounds__(256) k_grad_q(const double* __restrict__ pred,
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
     const double g = pred[i] - (double)label[i];
     const int64_t k = (int64_t)rint(ldexp(g, S));
-    q[i] = k;
+    q[i] = (QT)k;
     s += k;
   }
   s = wave_sum(s);
@@ -1299,20 +1302,24 @@ __device__ __forceinline__ void row_store(uint8_t* p, const RowData<ND>& d) {
 // publishes its left count, looks back for the exclusive prefix (decoupled
 // look-back), loads block 0 of its other rows and stores; the other blocks
 // and the bit block are loaded and stored row by row after that.
-template <int ND, int K>
+template <int ND, int K, bool Q32OUT>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const void* __restrict__ sq,
     const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, void* __restrict__ dq,
     int32_t* __restrict__ drid, int64_t row_capacity, int32_t n_blocks, int32_t block_features,
     int32_t block_stride, int32_t n_features, int32_t n_bit, int32_t bit_stride,
     const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
-    int32_t qmode /* bit 0: sq holds int32, bit 1: dq holds int32 */) {
+    int32_t qsh /* log2 of the source q's element size: 2 (int32) or 3 (int64) */) {
+  static_assert(K == 2 || K == 4 || K == 8, "rows per thread");
   constexpr int TILE = K * kPartThreads;
-  constexpr int KE = K < 2 ? K : 2;  // rows per thread whose block 0 is loaded early
+  constexpr int KE = 2;       // rows per thread whose block 0 is loaded early (one group)
+  constexpr int NG = K / KE;  // groups of KE rows; block 0 of group g + 1 is loaded before g is stored
+  constexpr int NCNT = K * kPartWaves;  // per-(row k, wave) left counts
+  // an int32 destination q is the low half of the source element
+  using QT = typename std::conditional<Q32OUT, int32_t, int64_t>::type;
   __shared__ int32_t s_tile;
-  __shared__ int32_t s_cnt[K][kPartWaves];
+  __shared__ int32_t s_cnt[NCNT];
   __shared__ int32_t s_excl;
-  __shared__ int32_t s_acc;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   if (threadIdx.x == 0) s_tile = (int32_t)atomicAdd(&ctrl->ticket, 1u);
@@ -1343,41 +1350,42 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   const uint8_t* __restrict__ fcolp = sbins + int64_t(fblk) * row_capacity * block_stride + fcol;
   const uint8_t* __restrict__ sbits = sbins + int64_t(n_blocks) * row_capacity * block_stride;
   const uint32_t* __restrict__ fwordp = reinterpret_cast<const uint32_t*>(sbits) + (fk >> 5);
-  const uint32_t qsh = (qmode & 1) ? 2u : 3u;  // log2 of the source q's element size
   // loads that need only the descriptor, unconditional (a row past the tile
   // end rereads its last row and is ignored), so none waits behind a branch
   int32_t fb[K];
-  int64_t qv[K];
-  int32_t rv[K];
-  RowData<ND> rd[K];
+  QT qv[K];
+  RowData<ND> rd[2][KE];  // block 0 of two groups of rows (group g in rd[g & 1])
+  // Addresses are a uniform base at the tile's first row plus a 32-bit lane
+  // offset (a tile spans at most 8192 rows of at most 512 bytes).
+  const uint8_t* __restrict__ tb = sbins + r0 * block_stride;
+  const uint32_t bs = (uint32_t)block_stride;
   // (the split feature's bytes first: loads complete in order, and the
   // flags wait only for them while the rows are still in flight)
   if (rows > 0) {
     // one dword load either way (the byte's aligned dword, or the bit's
     // word), so no branch separates these loads from the ones below
-    const uint8_t* __restrict__ fbase =
-        fbit ? reinterpret_cast<const uint8_t*>(fwordp) : fcolp - (fcol & 3);
-    const int64_t frow = fbit ? int64_t(nwords) * 4 : int64_t(block_stride);
+    const uint32_t frow = fbit ? (uint32_t)nwords * 4u : bs;
+    const uint8_t* __restrict__ tf =
+        (fbit ? reinterpret_cast<const uint8_t*>(fwordp) : fcolp - (fcol & 3)) + r0 * int64_t(frow);
+    const char* __restrict__ tq = reinterpret_cast<const char*>(sq) + (r0 << qsh);
+    const uint32_t lr = (uint32_t)(rows - 1);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int32_t i = k * kPartThreads + threadIdx.x;
-      const int64_t sr = r0 + (i < rows ? i : rows - 1);
-      fb[k] = (int32_t)*reinterpret_cast<const uint32_t*>(fbase + sr * frow);
+      const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
+      const uint32_t ic = i < lr ? i : lr;
+      fb[k] = (int32_t)*reinterpret_cast<const uint32_t*>(tf + ic * frow);
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int32_t i = k * kPartThreads + threadIdx.x;
-      const int64_t sr = r0 + (i < rows ? i : rows - 1);
-      // one 8-byte load either way, so no branch separates the loads: an
-      // int32 q is the low half (the buffer holds 8 bytes per row, so the
-      // read stays inside it); an int32 destination takes the low half of
-      // either (the driver narrows only q that fit), an int64 one comes from
-      // an int64 source
-      qv[k] = *reinterpret_cast<const int64_t*>(reinterpret_cast<const char*>(sq) + (sr << qsh));
-      rv[k] = drid != nullptr ? (srid != nullptr ? srid[sr] : (int32_t)sr) : 0;
+      const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
+      const uint32_t ic = i < lr ? i : lr;
+      // an int32 destination reads the low half of the source element
+      // (int32 or int64: the driver narrows only q that fit); an int64 one
+      // comes from an int64 source
+      qv[k] = *reinterpret_cast<const QT*>(tq + (ic << qsh));
       // with no byte block (ND == 1, block_stride 0) this rereads the first
       // dword of the bit block, and the value is never stored
-      if (k < KE) row_load<ND>(sbins + sr * block_stride, rd[k]);
+      if (k < KE) row_load<ND>(tb + ic * bs, rd[0][k]);
     }
     const uint32_t fsh = fbit ? (uint32_t)(fk & 31) : 8u * (uint32_t)(fcol & 3);
     const uint32_t fmask = fbit ? 1u : 0xffu;
@@ -1386,38 +1394,51 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   }
   if (!split_ok && threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
 
-  bool left[K];
-  uint64_t bal[K];
+  uint64_t bal[K];  // go-left flags of the wave's rows k (a row's own flag is its bit)
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int32_t i = k * kPartThreads + threadIdx.x;
-    left[k] = (i < rows) && (fb[k] <= td.threshold_bin);
-    bal[k] = __ballot(left[k]);
-    if (lane == 0) s_cnt[k][wid] = __popcll(bal[k]);
+    bal[k] = __ballot((i < rows) && (fb[k] <= td.threshold_bin));
+    if (lane == 0) s_cnt[k * kPartWaves + wid] = __popcll(bal[k]);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int k = 0; k < K; ++k)
-      for (int w = 0; w < kPartWaves; ++w) {
-        const int32_t t = s_cnt[k][w];
-        s_cnt[k][w] = acc;
-        acc += t;
-      }
-    s_acc = acc;
-    // publish this tile's left count at once, so later tiles never wait long
-    st_publish(&status[tile], (tin == 0 ? kStInc : kStAgg) | (uint64_t)(uint32_t)acc);
-  }
-  __syncthreads();
+  // wave 0: exclusive scan of the (row k, wave) counts in row order, then
+  // publish the tile's left count at once (so later tiles never wait long),
+  // look back for the exclusive prefix of the node's earlier tiles and
+  // publish the inclusive one
   if (wid == 0) {
+    constexpr int E = NCNT >= 64 ? NCNT / 64 : 1;  // counts per lane
+    int32_t c[E];
+    int32_t own = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = lane * E + e;
+      c[e] = idx < NCNT ? s_cnt[idx] : 0;
+      own += c[e];
+    }
+    int32_t x = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    int32_t run = x - own;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = lane * E + e;
+      if (idx < NCNT) s_cnt[idx] = run;
+      run += c[e];
+    }
+    const int32_t acc = __shfl(x, 63, 64);
+    if (lane == 0) st_publish(&status[tile], (tin == 0 ? kStInc : kStAgg) | (uint64_t)(uint32_t)acc);
     int64_t excl = 0;
     bool ok = true;
     if (tin > 0) excl = lookback_excl(status, tile, tfirst, &ok);
     if (lane == 0) {
       if (!ok) dev_error(&ctrl->err, GBDT_E_INTERNAL);
-      if (tin > 0) st_publish(&status[tile], kStInc | (uint64_t)(uint32_t)(excl + s_acc));
+      if (tin > 0) st_publish(&status[tile], kStInc | (uint64_t)(uint32_t)(excl + acc));
       s_excl = (int32_t)excl;
-      if (tile == tlast && excl + s_acc != td.n_left) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+      if (tile == tlast && excl + acc != td.n_left) dev_error(&ctrl->err, GBDT_E_INTERNAL);
     }
   }
   __syncthreads();
@@ -1433,8 +1454,9 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     const int32_t i = k * kPartThreads + threadIdx.x;
     dpos[k] = -1;
     if (i < rows) {
-      const int32_t rl = s_cnt[k][wid] + __popcll(bal[k] & lt_mask);
-      const int64_t d = left[k] ? lbase + rl : rbase + (i - rl);
+      const int32_t rl = s_cnt[k * kPartWaves + wid] + __popcll(bal[k] & lt_mask);
+      const bool left = (bal[k] >> lane) & 1ull;
+      const int64_t d = left ? lbase + rl : rbase + (i - rl);
       // a split record whose left count disagrees with the rows could send a
       // row outside its node's segment: such a row is not written
       const bool in_seg = d >= td.begin && d < seg_end;
@@ -1443,24 +1465,36 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     }
   }
   if (bad_pos) dev_error(&ctrl->err, GBDT_E_INTERNAL);
-  // block 0 of the late rows, then every row's stores
-  if (n_blocks > 0) {
+  // q of every row, then block 0 group by group: group g + 1 is loaded
+  // before group g is stored
 #pragma unroll
-    for (int k = KE; k < K; ++k) {
-      const int32_t i = k * kPartThreads + threadIdx.x;
-      if (dpos[k] >= 0) row_load<ND>(sbins + (r0 + i) * block_stride, rd[k]);
+  for (int k = 0; k < K; ++k)
+    if (dpos[k] >= 0) reinterpret_cast<QT*>(dq)[dpos[k]] = qv[k];
+  // row ids (moved only when the destination has them)
+  if (drid != nullptr) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t sr = r0 + k * kPartThreads + threadIdx.x;
+      if (dpos[k] >= 0) drid[dpos[k]] = srid != nullptr ? srid[sr] : (int32_t)sr;
     }
   }
+  if (n_blocks > 0) {
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int32_t d = dpos[k];
-    if (d < 0) continue;
-    if (qmode & 2)
-      reinterpret_cast<int32_t*>(dq)[d] = (int32_t)qv[k];
-    else
-      reinterpret_cast<int64_t*>(dq)[d] = qv[k];
-    if (drid != nullptr) drid[d] = rv[k];
-    if (n_blocks > 0) row_store<ND>(dbins + int64_t(d) * block_stride, rd[k]);
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) {
+#pragma unroll
+        for (int e = 0; e < KE; ++e) {
+          const int k = (g + 1) * KE + e;
+          const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
+          if (dpos[k] >= 0) row_load<ND>(tb + i * bs, rd[(g + 1) & 1][e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < KE; ++e) {
+        const int k = g * KE + e;
+        if (dpos[k] >= 0) row_store<ND>(dbins + int64_t(dpos[k]) * block_stride, rd[g & 1][e]);
+      }
+    }
   }
   // the other byte blocks, double-buffered: block b + 1 is loaded before
   // block b is stored (loads are unconditional, from clamped rows).  Tiles
@@ -1471,10 +1505,13 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       const int64_t boff = int64_t(b) * row_capacity * block_stride;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const int32_t i = k * kPartThreads + threadIdx.x;
-        if (dpos[k] >= 0) {
-          row_load<ND>(sbins + boff + (r0 + i) * block_stride, rd[k]);
-          row_store<ND>(dbins + boff + int64_t(dpos[k]) * block_stride, rd[k]);
+        const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
+        int32_t d = dpos[k];
+        asm volatile("" : "+v"(d));  // (no destination address hoisted out of the block loop)
+        if (d >= 0) {
+          RowData<ND> x;
+          row_load<ND>(tb + boff + i * bs, x);
+          row_store<ND>(dbins + boff + int64_t(d) * block_stride, x);
         }
       }
     }
@@ -1497,40 +1534,54 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     if (rows > 0) load_block(1, nx);
     int32_t b = 1;
     while (b < n_blocks) {
-      if (b + 1 < n_blocks && rows > 0) load_block(b + 1, rd);
+      if (b + 1 < n_blocks && rows > 0) load_block(b + 1, rd[0]);
       store_block(b, nx);
       if (++b >= n_blocks) break;
       if (b + 1 < n_blocks && rows > 0) load_block(b + 1, nx);
-      store_block(b, rd);
+      store_block(b, rd[0]);
       ++b;
     }
   }
-  // the bit block: nwords words per row, 4 at a time
+  // the bit block: nwords words per row, 4 at a time, rows in groups of at
+  // most 4 per thread
   if (n_bit > 0) {
-    const uint32_t* __restrict__ sw = reinterpret_cast<const uint32_t*>(sbits);
-    uint32_t* __restrict__ dw = reinterpret_cast<uint32_t*>(dbins + int64_t(n_blocks) * row_capacity * block_stride);
+    constexpr int GB = K < 4 ? K : 4;
+    const uint32_t rowb = (uint32_t)nwords * 4u;
+    const uint8_t* __restrict__ tw = sbits + r0 * int64_t(rowb);
+    uint8_t* __restrict__ dw = dbins + int64_t(n_blocks) * row_capacity * block_stride;
     int32_t w0 = 0;
     for (; w0 + 4 <= nwords; w0 += 4) {
-      RowData<4> x[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int32_t i = k * kPartThreads + threadIdx.x;
-        if (dpos[k] >= 0) row_load<4>(reinterpret_cast<const uint8_t*>(sw + (r0 + i) * nwords + w0), x[k]);
+      for (int kb = 0; kb < K; kb += GB) {
+        RowData<4> x[GB];
+#pragma unroll
+        for (int e = 0; e < GB; ++e) {
+          const uint32_t i = (uint32_t)((kb + e) * kPartThreads) + threadIdx.x;
+          if (dpos[kb + e] >= 0) row_load<4>(tw + (i * rowb + 4u * (uint32_t)w0), x[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < GB; ++e) {
+          // (the empty asm keeps the 64-bit destination addresses from being
+          // hoisted out of the word loop, where all K would stay live)
+          int32_t d = dpos[kb + e];
+          asm volatile("" : "+v"(d));
+          if (d >= 0) row_store<4>(dw + int64_t(d) * rowb + 4 * w0, x[e]);
+        }
       }
-#pragma unroll
-      for (int k = 0; k < K; ++k)
-        if (dpos[k] >= 0) row_store<4>(reinterpret_cast<uint8_t*>(dw + int64_t(dpos[k]) * nwords + w0), x[k]);
     }
     for (; w0 < nwords; ++w0) {
       uint32_t x[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const int32_t i = k * kPartThreads + threadIdx.x;
-        if (dpos[k] >= 0) x[k] = sw[(r0 + i) * nwords + w0];
+        const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
+        if (dpos[k] >= 0) x[k] = *reinterpret_cast<const uint32_t*>(tw + (i * rowb + 4u * (uint32_t)w0));
       }
 #pragma unroll
-      for (int k = 0; k < K; ++k)
-        if (dpos[k] >= 0) dw[int64_t(dpos[k]) * nwords + w0] = x[k];
+      for (int k = 0; k < K; ++k) {
+        int32_t d = dpos[k];
+        asm volatile("" : "+v"(d));
+        if (d >= 0) *reinterpret_cast<uint32_t*>(dw + int64_t(d) * rowb + 4 * w0) = x[k];
+      }
     }
   }
 }
@@ -2004,17 +2055,17 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
   return GBDT_OK;
 }
 
-template <int K>
-static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K>) {
+template <int K, bool Q>
+static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K, Q>) {
   switch (nd) {
-    case 1: return k_partition<1, K>;
-    case 2: return k_partition<2, K>;
-    case 3: return k_partition<3, K>;
-    case 4: return k_partition<4, K>;
-    case 5: return k_partition<5, K>;
-    case 6: return k_partition<6, K>;
-    case 7: return k_partition<7, K>;
-    case 8: return k_partition<8, K>;
+    case 1: return k_partition<1, K, Q>;
+    case 2: return k_partition<2, K, Q>;
+    case 3: return k_partition<3, K, Q>;
+    case 4: return k_partition<4, K, Q>;
+    case 5: return k_partition<5, K, Q>;
+    case 6: return k_partition<6, K, Q>;
+    case 7: return k_partition<7, K, Q>;
+    case 8: return k_partition<8, K, Q>;
     default: return nullptr;
   }
 }
@@ -2023,11 +2074,14 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
                      hipStream_t s, bool qin32, bool qout32) {
   const int32_t nd = src.X.n_blocks > 0 ? src.X.block_stride / 4 : 1;
-  decltype(&k_partition<1, 2>) kern = nullptr;
+  if (qin32 && !qout32) return fail(GBDT_E_INTERNAL, "an int64 q destination needs an int64 source");
+  decltype(&k_partition<1, 2, false>) kern = nullptr;
   if (tile_rows == 2 * kPartThreads)
-    kern = partition_kernel<2>(nd);
+    kern = qout32 ? partition_kernel<2, true>(nd) : partition_kernel<2, false>(nd);
   else if (tile_rows == 4 * kPartThreads)
-    kern = partition_kernel<4>(nd);
+    kern = qout32 ? partition_kernel<4, true>(nd) : partition_kernel<4, false>(nd);
+  else if (tile_rows == 8 * kPartThreads)
+    kern = qout32 ? partition_kernel<8, true>(nd) : partition_kernel<8, false>(nd);
   else
     return fail(GBDT_E_INTERNAL, "unsupported partition tile size");
   if (kern == nullptr) return fail(GBDT_E_UNSUPPORTED, "a column block wider than 32 bytes");
@@ -2035,8 +2089,7 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
   hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s, src.X.bins, src.q,
                      src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
                      src.X.block_features, src.X.block_stride, src.X.n_features,
-                     src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl,
-                     (qin32 ? 1 : 0) | (qout32 ? 2 : 0));
+                     src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl, qin32 ? 2 : 3);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_partition");
   return GBDT_OK;
@@ -2239,12 +2292,22 @@ int gbdt_pack_matrix(const uint8_t* rowmajor, const gbdt_matrix* dst, const gbdt
 int gbdt_compute_gradients(const double* pred, const float* label, int64_t n, int64_t* q,
                            int32_t* scale, int64_t* gsum, void* ws, size_t ws_bytes,
                            void* stream) {
+  return launch_gradients(pred, label, n, q, false, scale, gsum, ws, ws_bytes,
+                          reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace gbdt {
+
+int launch_gradients(const double* pred, const float* label, int64_t n, void* q, bool q32,
+                     int32_t* scale, int64_t* gsum, void* ws, size_t ws_bytes, hipStream_t s) {
   if (!pred || !label || !q || !scale || !gsum) return fail(GBDT_E_ARG, "null argument");
   if (n < 1 || n > 0x7fffffffLL) return fail(GBDT_E_ARG, "n out of range");
+  if (q32 && ceil_log2(n) < 22) return fail(GBDT_E_INTERNAL, "int32 q needs ceil(log2 n) >= 22");
   const WsLayout L = ws_layout(n, 1, 1);
   int rc = check_ws(ws, ws_bytes, L);
   if (rc) return rc;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
   double* part = reinterpret_cast<double*>(w + L.gpart);
@@ -2256,12 +2319,20 @@ int gbdt_compute_gradients(const double* pred, const float* label, int64_t n, in
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_grad_max");
   diag_begin(kDiagGradQ, s);
-  hipLaunchKernelGGL(k_grad_q, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n,
-                     ceil_log2(n), part, (int32_t)blocks, q, scale, gsum);
+  if (q32)
+    hipLaunchKernelGGL(k_grad_q<int32_t>, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n,
+                       ceil_log2(n), part, (int32_t)blocks, static_cast<int32_t*>(q), scale, gsum);
+  else
+    hipLaunchKernelGGL(k_grad_q<int64_t>, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n,
+                       ceil_log2(n), part, (int32_t)blocks, static_cast<int64_t*>(q), scale, gsum);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_grad_q");
   return GBDT_OK;
 }
+
+}  // namespace gbdt
+
+extern "C" {
 
 int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const gbdt_node* nodes,
                           const int32_t* list, const int32_t* list_len, int32_t list_cap,
@@ -2364,7 +2435,7 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
   const WsLayout L = ws_layout(src->X.n_rows, list_cap, 1);
   rc = check_ws(ws, ws_bytes, L);
   if (rc) return rc;
-  const int32_t ptr = part_tile_rows(src->X.n_rows, src->X.n_blocks);
+  const int32_t ptr = part_tile_rows(src->X.n_rows, src->X.n_blocks, false);
   const int64_t max_tiles = (rows_bound + ptr - 1) / ptr + list_cap;
   if (max_tiles > L.status_cap) return fail(GBDT_E_SHAPE, "too many partition tiles for the workspace");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -389,10 +389,14 @@ int gbdt_update_predictions(double* pred, const gbdt_matrix* X /* host */, const
  * Device buffers for gbdt_grow_tree (host struct of device pointers); sizes
  * from gbdt_grow_sizes.  pp[0], pp[1]: two row orders (bins in the blocking
  * of X and q; rid may be NULL) used in turn by the partition of each level.
+ * q and the row buffers' q are working storage of 8 bytes per row: when
+ * ceil(log2 n_rows) >= 22 (n_rows > 2^21), every |q| <= 2^(52 - ceil(log2 n))
+ * <= 2^30 and the driver keeps q as int32 in the first 4 n bytes (exact);
+ * otherwise as int64.
  */
 typedef struct gbdt_grow_buffers {
   gbdt_rows pp[2];
-  int64_t* q;            /* [n] gradients in row-id order */
+  int64_t* q;            /* [n] gradients in row-id order (int32 [n] when n > 2^21) */
   int64_t* hist_g;       /* [hist_slots][total_bins] */
   uint32_t* hist_cnt;    /* [hist_slots][total_bins] */
   gbdt_split* splits;    /* [max_nodes] */
