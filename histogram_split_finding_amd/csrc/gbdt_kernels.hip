@@ -467,7 +467,11 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
 // lane therefore walks its 4 bytes in a rotated order (byte (m + rot) & 3 in
 // step m) chosen so that the 16 lanes of every quarter-wave always address
 // 16 different bank pairs, whatever the bin values (a hot bin included):
-//   D = 8: rot = (rg & 1) + 2 (c >> 2), one copy (32 columns);
+//   D = 8: rot = (rg & 1) + 2 ((c >> 2) xor ((rg >> 1) & 1)), one copy (32
+//   columns); rows of adjacent quarter-waves then never share a (column,
+//   byte) slot, so a hot bin cannot make consecutive passes of one
+//   instruction update the same address (the earlier rot = (rg & 1) +
+//   2 (c >> 2) shared it between all rows of one parity);
 //   D = 4: rot = rg & 3, one copy;
 //   D = 2 or 1: rot = rg & 3 and 4 / D copies picked by (rg >> 2), summed at
 //   the end.
@@ -550,7 +554,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   // lane roles and the four LDS byte offsets of the lane's bytes
   const int32_t c = threadIdx.x % D;
   const int32_t rg = threadIdx.x / D;
-  const int32_t rot = D == 8 ? (((rg & 1) + 2 * (c >> 2)) & 3) : (rg & 3);
+  const int32_t rot = D == 8 ? (((rg & 1) + 2 * (((c >> 2) ^ (rg >> 1)) & 1)) & 3) : (rg & 3);
   const int32_t copy = NCOPY == 1 ? 0 : ((rg >> 2) & (NCOPY - 1));
   uint32_t offs = 0u;
   uint32_t sel[4];
