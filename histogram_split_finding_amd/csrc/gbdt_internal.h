@@ -49,6 +49,15 @@ constexpr int kGradBlocks = 1024;     // grid of the gradient kernels
 #define GBDT_TWO_GROUPS __attribute__((amdgpu_waves_per_eu(8, 8)))
 
 constexpr int kPartTileRows = 2048;   // rows per partition tile (the smaller size; bounds use it)
+// Bytes of the partition's output (the plan's last tiles) written with
+// streaming stores when the large tiles are used: a level's row copy that
+// ends with that much dirty data in the memory-side cache leaves its
+// write-back to the next kernel, the histogram of the next level, which then
+// streams its rows at a fraction of its rate.  Measured on 50M x 28 rows:
+// histogram 1.81 -> 1.51 ms, partition 8.40 -> 8.63 ms per tree; with
+// several column blocks (10M x 100) streaming stores slowed the partition
+// by 18 % and the large tiles are not used there.
+constexpr int64_t kPartStreamBytes = int64_t(512) << 20;
 constexpr int kPartTileRowsMid = 4096;
 constexpr int kPartTileRowsLarge = 8192;
 constexpr int64_t kPartLargeRows = int64_t(1) << 22;  // matrices from this size take the larger tiles

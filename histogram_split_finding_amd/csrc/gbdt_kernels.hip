@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -571,17 +572,22 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   const int64_t r0 = td.r0;
   const int64_t r1 = td.r1;
   __syncthreads();
-  // A step covers RPI * BATCH rows in two halves of H batches; batch u of a
-  // step holds rows [base + u RPI, base + u RPI + RPW) of this wave.  The
-  // loop is a two-stage pipeline: while one half's atomics run, the other
-  // half's loads (already issued) are in flight, and each half reloads for
-  // the next step as soon as its atomics are issued.  Loads are
-  // unconditional: a row past the tile end reads the tile's last row (the
-  // wave's first row of the step is < r1, so it exists) and adds 0; the
-  // reload after the last step reads rows that are never used.  Loop bounds
-  // are wave-uniform.
+  // A stage covers SROWS = RPI * H rows in H batches; batch u of a stage
+  // holds rows [first + u RPI, first + u RPI + RPW) of this wave.  The loop
+  // is an NS-stage pipeline: while one stage's atomics run, the loads of the
+  // next NS - 1 stages are in flight, and each stage reloads NS stages ahead
+  // as soon as its atomics are issued.  Loads are unconditional: a row past
+  // the tile end reads the tile's last row (the wave's first row of the
+  // stage is < r1, so it exists); the reloads after the last stage read rows
+  // that are never used.  The loop leaves after the first stage that reaches
+  // the tile end; its bounds are wave-uniform.
   constexpr int H = BATCH / 2;
-  constexpr int32_t STEP = RPI * BATCH;
+#ifdef GBDT_HIST_STAGES
+  constexpr int NS = GBDT_HIST_STAGES;
+#else
+  constexpr int NS = 2;
+#endif
+  constexpr int32_t SROWS = RPI * H;
   // rows are addressed from the tile's first row: a uniform base plus a
   // 32-bit lane offset (a tile holds < 2^24 rows of at most 32 bytes)
   const int32_t nt = (int32_t)(r1 - r0);    // rows of the tile
@@ -589,7 +595,9 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   constexpr uint32_t QSH = Q32 ? 2u : 3u;  // log2 of q's element size
   const char* __restrict__ tq = reinterpret_cast<const char*>(q) + (r0 << QSH);
   const int32_t first_row = wid * RPW + lane / D;  // the lane's first row in the tile
-  int32_t base = wid * RPW;
+  // (the wave's row base in a scalar register, so the loop exits are
+  // uniform branches and the load counters stay exact across them)
+  int32_t base = __builtin_amdgcn_readfirstlane(wid * RPW);
   if (base < nt) {
     const int32_t lr = nt - 1;
     // q: with D >= 2 lanes per row, lane (row group, c) loads q of its row
@@ -598,8 +606,11 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     // (c % H == u: quad position u, or u and u + 2 for D == 2 pairs); with
     // D == 1 every lane loads its own row's q per batch.
     constexpr int NQ = D >= 2 ? 1 : H;
-    uint32_t xa[H], xb[H];
-    int64_t qa[NQ], qb[NQ];
+    // q stays in its stored width until it is used (a widening right after
+    // the load would make the wave wait for it there)
+    using QT = typename std::conditional<Q32, int32_t, int64_t>::type;
+    uint32_t xs[NS][H];
+    QT qs[NS][NQ];
     // Rows past the tile end are clamped to its last row and added like any
     // other row; the exact correction after the loop subtracts those copies
     // (packed sums are exact mod 2^64), so the loop needs no masks.  Lanes
@@ -607,25 +618,25 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     // which are never read.  The empty asm takes the loaded values as
     // operands where they are used, so the compiler can neither drop a load
     // nor wait for it early.
-    auto load_half = [&](int32_t first, uint32_t* x, int64_t* qq) {
+    auto load_half = [&](int32_t first, uint32_t* x, QT* qq) {
 #pragma unroll
       for (int u = 0; u < H; ++u) {
         const int32_t rr = first + u * RPI + (lane / D);
         const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
         x[u] = *reinterpret_cast<const uint32_t*>(tb + (__umul24(rc, (uint32_t)block_stride) + lane_off));
-        if (D == 1) qq[u < NQ ? u : 0] = q_at<Q32>(tq + (rc << QSH), 0);
+        if (D == 1) qq[u < NQ ? u : 0] = *reinterpret_cast<const QT*>(tq + (rc << QSH));
       }
       if (D >= 2) {
         const int32_t rr = first + (c % H) * RPI + (lane / D);
         const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
-        qq[0] = q_at<Q32>(tq + (rc << QSH), 0);
+        qq[0] = *reinterpret_cast<const QT*>(tq + (rc << QSH));
       }
     };
-    auto add_half = [&](uint32_t* x, int64_t* qq) {
+    auto add_half = [&](uint32_t* x, QT* qq) {
       uint64_t pkh = 0ull;
       if (D >= 2) {
         asm volatile("" : "+v"(qq[0]));
-        pkh = ((uint64_t)qq[0] << bits) | 1ull;
+        pkh = ((uint64_t)(int64_t)qq[0] << bits) | 1ull;
       }
 #pragma unroll
       for (int u = 0; u < H; ++u) {
@@ -635,7 +646,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
           pk = quad_bcast_batch<D>(pkh, u);
         } else {
           asm volatile("" : "+v"(x[u]), "+v"(qq[u < NQ ? u : 0]));
-          pk = ((uint64_t)qq[u < NQ ? u : 0] << bits) | 1ull;
+          pk = ((uint64_t)(int64_t)qq[u < NQ ? u : 0] << bits) | 1ull;
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -645,32 +656,47 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
         }
       }
     };
+    // The first stages are issued in stage order (the empty asm with a
+    // memory clobber keeps the compiler from interleaving them), so the load
+    // counter at the loop head is the same from the prologue as from the
+    // previous iteration, and stage 0 waits only for its own loads.
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      load_half(base + st * SROWS, xs[st], qs[st]);
+      asm volatile("" ::: "memory");
+    }
     // the tile's last row, for the correction below, loaded with the first
     // rows so that no round trip follows the loop
     uint32_t x_last = *reinterpret_cast<const uint32_t*>(
         tb + (__umul24((uint32_t)lr, (uint32_t)block_stride) + lane_off));
-    int64_t q_last = q_at<Q32>(tq + (uint32_t(lr) << QSH), 0);
-    load_half(base, xa, qa);
-    load_half(base + H * RPI, xb, qb);
-    int32_t steps = 0;
-    while (true) {
-      const int32_t next = base + STEP;
-      add_half(xa, qa);
-      load_half(next, xa, qa);
-      add_half(xb, qb);
-      load_half(next + H * RPI, xb, qb);
-      ++steps;
-      base = next;
-      if (base >= nt) break;
+    QT q_last = *reinterpret_cast<const QT*>(tq + (uint32_t(lr) << QSH));
+    // The wave needs `todo` stages (wave-uniform).  Each loop iteration
+    // adds NS stages and reloads each NS stages ahead, unconditionally; the
+    // last 1..NS stages are added after the loop from the buffers already
+    // loaded.  The loop thus has one exit and its back edge one load-counter
+    // state, so a stage waits only for its own loads.
+    int32_t todo = (nt - base + SROWS - 1) / SROWS;
+    const int32_t stages = todo;
+    while (todo > NS) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        add_half(xs[st], qs[st]);
+        load_half(base + (st + NS) * SROWS, xs[st], qs[st]);
+      }
+      base += NS * SROWS;
+      todo -= NS;
     }
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      if (st < todo) add_half(xs[st], qs[st]);
     asm volatile("" : "+v"(x_last), "+v"(q_last));
-    // the lane visited rows first_row + k RPI, k < steps * BATCH; those at or
+    // the lane visited rows first_row + k RPI, k < stages * H; those at or
     // past nt were row lr
     const int32_t valid = first_row < nt ? (nt - first_row + RPI - 1) / RPI : 0;
-    const int32_t extra = steps * BATCH - valid;
+    const int32_t extra = stages * H - valid;
     if (extra > 0) {
       const uint32_t x = x_last;
-      const int64_t qq = q_last;
+      const int64_t qq = (int64_t)q_last;
       const uint64_t pk = (((uint64_t)qq << bits) | 1ull) * (0ull - (uint64_t)extra);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -1283,6 +1309,28 @@ __device__ __forceinline__ void store_dwords(uint8_t* p, const uint4& v) {
   if constexpr (N == 2) *reinterpret_cast<uint2*>(p) = make_uint2(v.x, v.y);
   if constexpr (N == 1) *reinterpret_cast<uint32_t*>(p) = v.x;
 }
+// The same as streaming (non-temporal) stores: the lines are not kept in the
+// caches as dirty data for a later kernel to write back.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+#define GBDT_GLOBAL __attribute__((address_space(1)))
+template <int N>
+__device__ __forceinline__ void store_dwords_nt(GBDT_GLOBAL uint8_t* p, const uint4& v) {
+  if constexpr (N == 4) {
+    const u32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, (GBDT_GLOBAL u32x4_t*)p);
+  }
+  if constexpr (N == 3) {
+    const u32x3_t t = {v.x, v.y, v.z};
+    __builtin_nontemporal_store(t, (GBDT_GLOBAL u32x3_t*)p);
+  }
+  if constexpr (N == 2) {
+    const u32x2_t t = {v.x, v.y};
+    __builtin_nontemporal_store(t, (GBDT_GLOBAL u32x2_t*)p);
+  }
+  if constexpr (N == 1) __builtin_nontemporal_store(v.x, (GBDT_GLOBAL uint32_t*)p);
+}
 template <int ND>
 __device__ __forceinline__ void row_load(const uint8_t* p, RowData<ND>& d) {
   d.a = load_dwords<(ND < 4 ? ND : 4)>(p);
@@ -1292,6 +1340,22 @@ template <int ND>
 __device__ __forceinline__ void row_store(uint8_t* p, const RowData<ND>& d) {
   store_dwords<(ND < 4 ? ND : 4)>(p, d.a);
   if constexpr (ND > 4) store_dwords<ND - 4>(p + 16, d.b);
+}
+template <int ND>
+__device__ __forceinline__ void row_store_nt(uint8_t* p, const RowData<ND>& d) {
+  // (the empty asm keeps the compiler from merging these stores with the
+  // plain ones of the other branch, which would drop the streaming hint)
+  asm volatile("" : "+v"(p));
+  GBDT_GLOBAL uint8_t* const g = (GBDT_GLOBAL uint8_t*)p;
+  store_dwords_nt<(ND < 4 ? ND : 4)>(g, d.a);
+  if constexpr (ND > 4) store_dwords_nt<ND - 4>(g + 16, d.b);
+}
+template <int ND>
+__device__ __forceinline__ void row_put(uint8_t* p, const RowData<ND>& d, bool nt) {
+  if (nt)
+    row_store_nt<ND>(p, d);
+  else
+    row_store<ND>(p, d);
 }
 
 // One workgroup per tile of K * kPartThreads rows of a splitting node, taken
@@ -1305,7 +1369,10 @@ __device__ __forceinline__ void row_store(uint8_t* p, const RowData<ND>& d) {
 // 0 of the first two rows per thread.  Then it ballots the go-left flags,
 // publishes its left count, looks back for the exclusive prefix (decoupled
 // look-back), loads block 0 of its other rows and stores; the other blocks
-// and the bit block are loaded and stored row by row after that.
+// and the bit block are loaded and stored row by row after that.  The plan's
+// last nt_tiles tiles write with streaming (non-temporal) stores, so the
+// level does not end with its last rows as dirty lines in the memory-side
+// cache, whose write-back would fall into the next kernel.
 template <int ND, int K, bool Q32OUT>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const void* __restrict__ sq,
@@ -1313,7 +1380,8 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     int32_t* __restrict__ drid, int64_t row_capacity, int32_t n_blocks, int32_t block_features,
     int32_t block_stride, int32_t n_features, int32_t n_bit, int32_t bit_stride,
     const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
-    int32_t qsh /* log2 of the source q's element size: 2 (int32) or 3 (int64) */) {
+    int32_t qsh /* log2 of the source q's element size: 2 (int32) or 3 (int64) */,
+    int32_t nt_tiles /* the plan's last nt_tiles tiles store with streaming stores */) {
   static_assert(K == 2 || K == 4 || K == 8, "rows per thread");
   constexpr int TILE = K * kPartThreads;
   constexpr int KE = 2;       // rows per thread whose block 0 is loaded early (one group)
@@ -1331,6 +1399,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   const int32_t tile = s_tile;
   const int32_t total = ctrl->plan_total;
   if (tile >= total) return;
+  const bool nt = tile >= total - nt_tiles;  // (uniform)
   const TileDesc td = desc[tile];
   const int32_t tfirst = td.tfirst;
   const int32_t tlast = td.tfirst + td.ntiles - 1;
@@ -1471,9 +1540,19 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   if (bad_pos) dev_error(&ctrl->err, GBDT_E_INTERNAL);
   // q of every row, then block 0 group by group: group g + 1 is loaded
   // before group g is stored
+  if (nt) {
 #pragma unroll
-  for (int k = 0; k < K; ++k)
-    if (dpos[k] >= 0) reinterpret_cast<QT*>(dq)[dpos[k]] = qv[k];
+    for (int k = 0; k < K; ++k)
+      if (dpos[k] >= 0) {
+        QT* qp = reinterpret_cast<QT*>(dq) + dpos[k];
+        asm volatile("" : "+v"(qp));
+        __builtin_nontemporal_store(qv[k], (GBDT_GLOBAL QT*)qp);
+      }
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (dpos[k] >= 0) reinterpret_cast<QT*>(dq)[dpos[k]] = qv[k];
+  }
   // row ids (moved only when the destination has them)
   if (drid != nullptr) {
 #pragma unroll
@@ -1496,7 +1575,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
 #pragma unroll
       for (int e = 0; e < KE; ++e) {
         const int k = g * KE + e;
-        if (dpos[k] >= 0) row_store<ND>(dbins + int64_t(dpos[k]) * block_stride, rd[g & 1][e]);
+        if (dpos[k] >= 0) row_put<ND>(dbins + int64_t(dpos[k]) * block_stride, rd[g & 1][e], nt);
       }
     }
   }
@@ -1515,7 +1594,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
         if (d >= 0) {
           RowData<ND> x;
           row_load<ND>(tb + boff + i * bs, x);
-          row_store<ND>(dbins + boff + int64_t(d) * block_stride, x);
+          row_put<ND>(dbins + boff + int64_t(d) * block_stride, x, nt);
         }
       }
     }
@@ -1533,7 +1612,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       uint8_t* __restrict__ dstp = dbins + int64_t(b) * row_capacity * block_stride;
 #pragma unroll
       for (int k = 0; k < K; ++k)
-        if (dpos[k] >= 0) row_store<ND>(dstp + int64_t(dpos[k]) * block_stride, src[k]);
+        if (dpos[k] >= 0) row_put<ND>(dstp + int64_t(dpos[k]) * block_stride, src[k], nt);
     };
     if (rows > 0) load_block(1, nx);
     int32_t b = 1;
@@ -1569,7 +1648,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
           // hoisted out of the word loop, where all K would stay live)
           int32_t d = dpos[kb + e];
           asm volatile("" : "+v"(d));
-          if (d >= 0) row_store<4>(dw + int64_t(d) * rowb + 4 * w0, x[e]);
+          if (d >= 0) row_put<4>(dw + int64_t(d) * rowb + 4 * w0, x[e], nt);
         }
       }
     }
@@ -1584,7 +1663,11 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       for (int k = 0; k < K; ++k) {
         int32_t d = dpos[k];
         asm volatile("" : "+v"(d));
-        if (d >= 0) *reinterpret_cast<uint32_t*>(dw + int64_t(d) * rowb + 4 * w0) = x[k];
+        if (d >= 0) {
+          RowData<1> one;
+          one.a = make_uint4(x[k], 0u, 0u, 0u);
+          row_put<1>(dw + int64_t(d) * rowb + 4 * w0, one, nt);
+        }
       }
     }
   }
@@ -2079,6 +2162,14 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
                      hipStream_t s, bool qin32, bool qout32) {
   const int32_t nd = src.X.n_blocks > 0 ? src.X.block_stride / 4 : 1;
   if (qin32 && !qout32) return fail(GBDT_E_INTERNAL, "an int64 q destination needs an int64 source");
+  // With the large tiles (one block, >= 4M rows), the plan's last tiles,
+  // about kPartStreamBytes of rows, store streaming (see k_partition).
+  const int64_t row_bytes = int64_t(src.X.n_blocks) * src.X.block_stride + src.X.bit_stride +
+                            (qout32 ? 4 : 8);
+  const int64_t tile_bytes = int64_t(tile_rows) * (row_bytes > 0 ? row_bytes : 1);
+  const int32_t nt_tiles = tile_rows == kPartTileRowsLarge
+                               ? (int32_t)std::min<int64_t>(max_tiles, kPartStreamBytes / tile_bytes)
+                               : 0;
   decltype(&k_partition<1, 2, false>) kern = nullptr;
   if (tile_rows == 2 * kPartThreads)
     kern = qout32 ? partition_kernel<2, true>(nd) : partition_kernel<2, false>(nd);
@@ -2093,7 +2184,8 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
   hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles), dim3(kPartThreads), 0, s, src.X.bins, src.q,
                      src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
                      src.X.block_features, src.X.block_stride, src.X.n_features,
-                     src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl, qin32 ? 2 : 3);
+                     src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl, qin32 ? 2 : 3,
+                     nt_tiles);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_partition");
   return GBDT_OK;
