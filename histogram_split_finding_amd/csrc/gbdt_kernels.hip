@@ -572,15 +572,18 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   const int64_t r0 = td.r0;
   const int64_t r1 = td.r1;
   __syncthreads();
-  // A stage covers SROWS = RPI * H rows in H batches; batch u of a stage
-  // holds rows [first + u RPI, first + u RPI + RPW) of this wave.  The loop
+  // A stage covers SROWS = RPI * H rows in H batches.  Within a stage each
+  // wave owns H * RPW consecutive rows, batch u of them rows
+  // [first + u RPW, first + (u + 1) RPW): a wave reads whole runs of cache
+  // lines, so no line is shared by waves that may drift apart in time (with
+  // batches RPI rows apart, a line at each 8-row boundary was fetched by two
+  // waves, and the 50M x 28 root read 40 bytes per 32-byte row).  The loop
   // is an NS-stage pipeline: while one stage's atomics run, the loads of the
   // next NS - 1 stages are in flight, and each stage reloads NS stages ahead
   // as soon as its atomics are issued.  Loads are unconditional: a row past
   // the tile end reads the tile's last row (the wave's first row of the
   // stage is < r1, so it exists); the reloads after the last stage read rows
-  // that are never used.  The loop leaves after the first stage that reaches
-  // the tile end; its bounds are wave-uniform.
+  // that are never used.  Loop bounds are wave-uniform.
   constexpr int H = BATCH / 2;
 #ifdef GBDT_HIST_STAGES
   constexpr int NS = GBDT_HIST_STAGES;
@@ -594,14 +597,14 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   const uint8_t* __restrict__ tb = bins + (int64_t(blk) * row_capacity + r0) * block_stride;
   constexpr uint32_t QSH = Q32 ? 2u : 3u;  // log2 of q's element size
   const char* __restrict__ tq = reinterpret_cast<const char*>(q) + (r0 << QSH);
-  const int32_t first_row = wid * RPW + lane / D;  // the lane's first row in the tile
+  const int32_t first_row = wid * (H * RPW) + lane / D;  // the lane's first row in the tile
   // (the wave's row base in a scalar register, so the loop exits are
   // uniform branches and the load counters stay exact across them)
-  int32_t base = __builtin_amdgcn_readfirstlane(wid * RPW);
+  int32_t base = __builtin_amdgcn_readfirstlane(wid * (H * RPW));
   if (base < nt) {
     const int32_t lr = nt - 1;
     // q: with D >= 2 lanes per row, lane (row group, c) loads q of its row
-    // in batch c % H of the half, so one load per half serves H batches and
+    // in batch c % H of the stage, so one load per stage serves H batches and
     // batch u's q is taken from a lane of the same quad with a DPP move
     // (c % H == u: quad position u, or u and u + 2 for D == 2 pairs); with
     // D == 1 every lane loads its own row's q per batch.
@@ -621,13 +624,13 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     auto load_half = [&](int32_t first, uint32_t* x, QT* qq) {
 #pragma unroll
       for (int u = 0; u < H; ++u) {
-        const int32_t rr = first + u * RPI + (lane / D);
+        const int32_t rr = first + u * RPW + (lane / D);
         const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
         x[u] = *reinterpret_cast<const uint32_t*>(tb + (__umul24(rc, (uint32_t)block_stride) + lane_off));
         if (D == 1) qq[u < NQ ? u : 0] = *reinterpret_cast<const QT*>(tq + (rc << QSH));
       }
       if (D >= 2) {
-        const int32_t rr = first + (c % H) * RPI + (lane / D);
+        const int32_t rr = first + (c % H) * RPW + (lane / D);
         const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
         qq[0] = *reinterpret_cast<const QT*>(tq + (rc << QSH));
       }
@@ -690,9 +693,14 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     for (int st = 0; st < NS; ++st)
       if (st < todo) add_half(xs[st], qs[st]);
     asm volatile("" : "+v"(x_last), "+v"(q_last));
-    // the lane visited rows first_row + k RPI, k < stages * H; those at or
-    // past nt were row lr
-    const int32_t valid = first_row < nt ? (nt - first_row + RPI - 1) / RPI : 0;
+    // the lane visited rows first_row + u RPW + s SROWS, u < H, s < stages;
+    // those at or past nt were row lr
+    int32_t valid = 0;
+#pragma unroll
+    for (int u = 0; u < H; ++u) {
+      const int32_t r = first_row + u * RPW;
+      valid += r < nt ? (nt - r + SROWS - 1) / SROWS : 0;
+    }
     const int32_t extra = stages * H - valid;
     if (extra > 0) {
       const uint32_t x = x_last;
@@ -1331,6 +1339,19 @@ __device__ __forceinline__ void store_dwords_nt(GBDT_GLOBAL uint8_t* p, const ui
   }
   if constexpr (N == 1) __builtin_nontemporal_store(v.x, (GBDT_GLOBAL uint32_t*)p);
 }
+// Dword i (uniform, < ND) of a row held in registers.
+template <int ND>
+__device__ __forceinline__ uint32_t row_dword(const RowData<ND> d, uint32_t i) {
+  uint32_t v = d.a.x;
+  if (ND > 1) v = i == 1 ? d.a.y : v;
+  if (ND > 2) v = i == 2 ? d.a.z : v;
+  if (ND > 3) v = i == 3 ? d.a.w : v;
+  if (ND > 4) v = i == 4 ? d.b.x : v;
+  if (ND > 5) v = i == 5 ? d.b.y : v;
+  if (ND > 6) v = i == 6 ? d.b.z : v;
+  if (ND > 7) v = i == 7 ? d.b.w : v;
+  return v;
+}
 template <int ND>
 __device__ __forceinline__ void row_load(const uint8_t* p, RowData<ND>& d) {
   d.a = load_dwords<(ND < 4 ? ND : 4)>(p);
@@ -1384,7 +1405,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     int32_t nt_tiles /* the plan's last nt_tiles tiles store with streaming stores */) {
   static_assert(K == 2 || K == 4 || K == 8, "rows per thread");
   constexpr int TILE = K * kPartThreads;
-  constexpr int KE = 2;       // rows per thread whose block 0 is loaded early (one group)
+  constexpr int KE = 2;       // rows per thread whose block 0 is loaded before the look-back
   constexpr int NG = K / KE;  // groups of KE rows; block 0 of group g + 1 is loaded before g is stored
   constexpr int NCNT = K * kPartWaves;  // per-(row k, wave) left counts
   // an int32 destination q is the low half of the source element
@@ -1434,19 +1455,27 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   const uint32_t bs = (uint32_t)block_stride;
   // (the split feature's bytes first: loads complete in order, and the
   // flags wait only for them while the rows are still in flight)
+  // With every row's block 0 loaded early and the split feature in block 0,
+  // its byte comes from those registers: a separate load of the split bytes
+  // would bring each line of the tile in twice when the cache has evicted it
+  // before the rows are read.  (uniform)
+  const bool from_rows = KE == K && !fbit && fblk == 0 && n_blocks > 0;
   if (rows > 0) {
-    // one dword load either way (the byte's aligned dword, or the bit's
-    // word), so no branch separates these loads from the ones below
-    const uint32_t frow = fbit ? (uint32_t)nwords * 4u : bs;
-    const uint8_t* __restrict__ tf =
-        (fbit ? reinterpret_cast<const uint8_t*>(fwordp) : fcolp - (fcol & 3)) + r0 * int64_t(frow);
     const char* __restrict__ tq = reinterpret_cast<const char*>(sq) + (r0 << qsh);
     const uint32_t lr = (uint32_t)(rows - 1);
+    // otherwise one dword load per row (the byte's aligned dword, or the
+    // bit's word), issued first: loads complete in order, so the flags wait
+    // only for these while the rows are still in flight
+    const uint32_t frow = fbit ? (uint32_t)nwords * 4u : bs;
+    if (!from_rows) {
+      const uint8_t* __restrict__ tf =
+          (fbit ? reinterpret_cast<const uint8_t*>(fwordp) : fcolp - (fcol & 3)) + r0 * int64_t(frow);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
-      const uint32_t ic = i < lr ? i : lr;
-      fb[k] = (int32_t)*reinterpret_cast<const uint32_t*>(tf + ic * frow);
+      for (int k = 0; k < K; ++k) {
+        const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
+        const uint32_t ic = i < lr ? i : lr;
+        fb[k] = (int32_t)*reinterpret_cast<const uint32_t*>(tf + ic * frow);
+      }
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -1460,10 +1489,17 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       // dword of the bit block, and the value is never stored
       if (k < KE) row_load<ND>(tb + ic * bs, rd[0][k]);
     }
-    const uint32_t fsh = fbit ? (uint32_t)(fk & 31) : 8u * (uint32_t)(fcol & 3);
-    const uint32_t fmask = fbit ? 1u : 0xffu;
+    if (from_rows) {
+      const uint32_t fdw = (uint32_t)fcol >> 2;
+      const uint32_t fsh = 8u * (uint32_t)(fcol & 3);
 #pragma unroll
-    for (int k = 0; k < K; ++k) fb[k] = (int32_t)(((uint32_t)fb[k] >> fsh) & fmask);
+      for (int k = 0; k < KE; ++k) fb[k] = (int32_t)((row_dword<ND>(rd[0][k], fdw) >> fsh) & 0xffu);
+    } else {
+      const uint32_t fsh = fbit ? (uint32_t)(fk & 31) : 8u * (uint32_t)(fcol & 3);
+      const uint32_t fmask = fbit ? 1u : 0xffu;
+#pragma unroll
+      for (int k = 0; k < K; ++k) fb[k] = (int32_t)(((uint32_t)fb[k] >> fsh) & fmask);
+    }
   }
   if (!split_ok && threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
 
