@@ -1790,7 +1790,10 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
   }
 }
 
-template <int MAXDW, int ROWS, bool TREE_IN_LDS>
+// ND1 > 0: one byte block of ND1 dwords per row, loaded with one or two
+// wide loads (a 16-byte load and one of 4, 8 or 12 bytes), then the bit
+// words; ND1 == 0: any layout, one dword per load.
+template <int MAXDW, int ROWS, bool TREE_IN_LDS, int ND1>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
     double* __restrict__ pred, int64_t n, const uint8_t* __restrict__ bins, int64_t row_capacity,
     int32_t n_blocks, int32_t block_stride, int32_t bit_stride,
@@ -1840,18 +1843,34 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
       const uint32_t* __restrict__ bp =
           reinterpret_cast<const uint32_t*>(bins + i * block_stride);
       const uint32_t* __restrict__ wp = bitw + i * nwords;
-      int32_t xb = 0;
-      int64_t boff = 0;  // dwords from bins to block b's run
+      if constexpr (ND1 > 0) {
+        static_assert(ND1 <= MAXDW, "the byte block fits the row registers");
+        RowData<ND1> rdat;
+        row_load<ND1>(bins + i * block_stride, rdat);
+        const uint32_t w8[8] = {rdat.a.x, rdat.a.y, rdat.a.z, rdat.a.w,
+                                rdat.b.x, rdat.b.y, rdat.b.z, rdat.b.w};
 #pragma unroll
-      for (int x = 0; x < MAXDW; ++x) {
-        const bool in_bytes = x < ndw;
-        const bool in_bits = !in_bytes && x < ndw + nwords;
-        const uint32_t* p = in_bytes ? bp + boff + xb : (in_bits ? wp + (x - ndw) : bp);
-        const uint32_t val = *p;
-        row[u][x] = (in_bytes || in_bits) ? val : 0u;
-        if (in_bytes && ++xb == dw) {
-          xb = 0;
-          boff += (row_capacity * block_stride) >> 2;
+        for (int x = 0; x < ND1; ++x) row[u][x] = w8[x];
+#pragma unroll
+        for (int x = ND1; x < MAXDW; ++x) {
+          const bool in_bits = x - ND1 < nwords;
+          const uint32_t val = *(in_bits ? wp + (x - ND1) : bp);
+          row[u][x] = in_bits ? val : 0u;
+        }
+      } else {
+        int32_t xb = 0;
+        int64_t boff = 0;  // dwords from bins to block b's run
+#pragma unroll
+        for (int x = 0; x < MAXDW; ++x) {
+          const bool in_bytes = x < ndw;
+          const bool in_bits = !in_bytes && x < ndw + nwords;
+          const uint32_t* p = in_bytes ? bp + boff + xb : (in_bits ? wp + (x - ndw) : bp);
+          const uint32_t val = *p;
+          row[u][x] = (in_bytes || in_bits) ? val : 0u;
+          if (in_bytes && ++xb == dw) {
+            xb = 0;
+            boff += (row_capacity * block_stride) >> 2;
+          }
         }
       }
     }
@@ -1901,14 +1920,14 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
   if (bad) dev_error(&ctrl->err, GBDT_E_INTERNAL);
 }
 
-template <int MAXDW>
+template <int MAXDW, int ND1 = 0>
 static void launch_update(bool in_lds, int rows, dim3 grid, size_t lds, hipStream_t s, double* pred,
                           int64_t n, const gbdt_matrix* X, const uint2* ctab, const double* lval,
                           const int32_t* n_nodes, int32_t max_nodes, double eta, WsCtrl* ctrl) {
   // two rows per lane only where both rows' bins fit registers without scratch
   constexpr int R2 = MAXDW <= 16 ? 2 : 1;
-  auto kern = in_lds ? (rows == 2 ? k_update<MAXDW, R2, true> : k_update<MAXDW, 1, true>)
-                     : (rows == 2 ? k_update<MAXDW, R2, false> : k_update<MAXDW, 1, false>);
+  auto kern = in_lds ? (rows == 2 ? k_update<MAXDW, R2, true, ND1> : k_update<MAXDW, 1, true, ND1>)
+                     : (rows == 2 ? k_update<MAXDW, R2, false, ND1> : k_update<MAXDW, 1, false, ND1>);
   hipLaunchKernelGGL(kern, grid, dim3(kUpdThreads), lds, s, pred, n, X->bins, X->row_capacity,
                      X->n_blocks, X->block_stride, X->bit_stride, ctab, lval, n_nodes, max_nodes, eta,
                      ctrl);
@@ -2623,7 +2642,23 @@ int gbdt_update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node*
   int64_t grid = (n + int64_t(kUpdThreads) * rows - 1) / (int64_t(kUpdThreads) * rows);
   if (grid > 512) grid = 512;  // persistent: the tree is copied to LDS once per workgroup
   diag_begin(kDiagUpdate, s);
-  if (ndw <= 8)
+  const int32_t nd1 = X->n_blocks == 1 ? X->block_stride / 4 : 0;  // one byte block: wide loads
+  if (ndw <= 8 && nd1 > 0) {
+    auto go = [&](auto tag) {
+      launch_update<8, decltype(tag)::value>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X,
+                                             ctab, lval, n_nodes, max_nodes, learning_rate, ctrl);
+    };
+    switch (nd1) {
+      case 1: go(std::integral_constant<int, 1>()); break;
+      case 2: go(std::integral_constant<int, 2>()); break;
+      case 3: go(std::integral_constant<int, 3>()); break;
+      case 4: go(std::integral_constant<int, 4>()); break;
+      case 5: go(std::integral_constant<int, 5>()); break;
+      case 6: go(std::integral_constant<int, 6>()); break;
+      case 7: go(std::integral_constant<int, 7>()); break;
+      default: go(std::integral_constant<int, 8>()); break;
+    }
+  } else if (ndw <= 8)
     launch_update<8>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
                      max_nodes, learning_rate, ctrl);
   else if (ndw <= 16)
