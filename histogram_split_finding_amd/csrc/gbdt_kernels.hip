@@ -884,8 +884,8 @@ __device__ __forceinline__ void argmax_step(double& g, int32_t& key) {
 }
 
 // One workgroup of THREADS per node.  The node's histogram is read in passes
-// of THREADS * kFindE bins in global bin order (feature-major, bins
-// ascending); thread t holds kFindE consecutive bins in registers.  A
+// of THREADS * E bins in global bin order (feature-major, bins ascending);
+// thread t holds E consecutive bins in registers.  A
 // segmented prefix sum (segments = features) -- serial inside the thread,
 // a DPP scan of the per-thread tails across the wave, the waves' tails
 // through LDS, and a carry across passes -- gives every bin's left totals
@@ -897,7 +897,7 @@ __device__ __forceinline__ void argmax_step(double& g, int32_t& key) {
 // is the larger child of a split pair: its histogram is the parent's minus
 // its built sibling's (exact integers), computed here and written to its own
 // slot for the next level; a negative count sets GBDT_E_INTERNAL.
-template <int THREADS>
+template <int THREADS, int E>
 __global__ void __launch_bounds__(THREADS) k_find(
     int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ bin_feature,
@@ -937,11 +937,11 @@ __global__ void __launch_bounds__(THREADS) k_find(
     bhi = ff <= fz ? bin_offset[fz + 1] : 0;
     if (nlo >= total_bins) blo = bhi = 0;
   }
-  int32_t f[kFindE + 2];  // features of bins b0-1 .. b0+kFindE of the first pass
+  int32_t f[E + 2];  // features of bins b0-1 .. b0+E of the first pass
   {
-    const int32_t b0 = blo + threadIdx.x * kFindE;
+    const int32_t b0 = blo + threadIdx.x * E;
 #pragma unroll
-    for (int e = 0; e < kFindE + 2; ++e) {
+    for (int e = 0; e < E + 2; ++e) {
       const int32_t b = b0 - 1 + e;
       const bool inb = b >= blo && b < bhi;
       const int32_t fv = bin_feature[inb ? b : 0];
@@ -969,23 +969,23 @@ __global__ void __launch_bounds__(THREADS) k_find(
     s_carry_g = 0;
     s_carry_c = 0;
   }
-  for (int32_t pass = blo; pass < bhi; pass += THREADS * kFindE) {
-    const int32_t b0 = pass + threadIdx.x * kFindE;
+  for (int32_t pass = blo; pass < bhi; pass += THREADS * E) {
+    const int32_t b0 = pass + threadIdx.x * E;
     if (pass > blo) {
 #pragma unroll
-      for (int e = 0; e < kFindE + 2; ++e) {
+      for (int e = 0; e < E + 2; ++e) {
         const int32_t b = b0 - 1 + e;
         const bool inb = b >= blo && b < bhi;
         const int32_t fv = bin_feature[inb ? b : 0];
         f[e] = inb ? fv : -1 - e;
       }
     }
-    int64_t g[kFindE];
-    int32_t c[kFindE];
-    int32_t fo[kFindE];  // first global bin of the feature of bin b0 + e
+    int64_t g[E];
+    int32_t c[E];
+    int32_t fo[E];  // first global bin of the feature of bin b0 + e
     if (derive) {
 #pragma unroll
-      for (int e = 0; e < kFindE; ++e) {
+      for (int e = 0; e < E; ++e) {
         const int32_t b = b0 + e;
         const bool inb = b < bhi;
         const uint32_t cp = inb ? hc_p[b] : 0u, cs = inb ? hc_s[b] : 0u;
@@ -996,7 +996,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < kFindE; ++e) {
+      for (int e = 0; e < E; ++e) {
         const int32_t b = b0 + e;
         const bool inb = b < bhi;
         g[e] = inb ? hg[b] : 0;
@@ -1009,13 +1009,13 @@ __global__ void __launch_bounds__(THREADS) k_find(
     const double sP = score_of(Gv, Hv, fp.lambda);
     const int64_t nv = nd.count;
     // serial segmented scan inside the thread
-    int32_t first_head = kFindE;
+    int32_t first_head = E;
     int64_t rg = 0;
     int32_t rc = 0;
 #pragma unroll
-    for (int e = 0; e < kFindE; ++e) {
+    for (int e = 0; e < E; ++e) {
       const bool head = (b0 + e >= bhi) || (f[e] != f[e + 1]);
-      if (head && first_head == kFindE) first_head = e;
+      if (head && first_head == E) first_head = e;
       rg = head ? g[e] : rg + g[e];
       rc = head ? c[e] : rc + c[e];
       g[e] = rg;
@@ -1023,7 +1023,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
     }
     // segmented scan of the thread tails across the wave (DPP row shifts,
     // then rows 0 -> 1, 2 -> 3, row 1 -> rows 2 and 3)
-    int32_t fl = first_head < kFindE ? 1 : 0;
+    int32_t fl = first_head < E ? 1 : 0;
     int64_t wg = rg;
     int32_t wc = rc;
     seg_scan_step<0x111, 0xF>(fl, wg, wc);  // row_shr:1
@@ -1066,7 +1066,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
     }
     // candidates: bin b with its right neighbour in the same feature
 #pragma unroll
-    for (int e = 0; e < kFindE; ++e) {
+    for (int e = 0; e < E; ++e) {
       const int32_t b = b0 + e;
       if (b >= bhi) break;
       const int64_t gl = e < first_head ? g[e] + cin_g : g[e];
@@ -1101,7 +1101,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
       // in-thread running sum minus the previous bin's (or itself at a head).
       // Stored last, so no wait above covers these writes.
 #pragma unroll
-      for (int e = 0; e < kFindE; ++e) {
+      for (int e = 0; e < E; ++e) {
         const int32_t b = b0 + e;
         if (b < bhi) {
           const bool head = e == 0 || f[e] != f[e + 1];
@@ -2173,7 +2173,7 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
   diag_begin(kDiagFind, s);
   if (nch > 1) {
     // whole features of up to kFindChunk + 255 bins: one or two passes of 256 x kFindE
-    hipLaunchKernelGGL(k_find<256>, dim3((unsigned)list_cap, (unsigned)nch), dim3(256), 0, s, hist_g,
+    hipLaunchKernelGGL((k_find<256, kFindE>), dim3((unsigned)list_cap, (unsigned)nch), dim3(256), 0, s, hist_g,
                        hist_cnt, ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
                        list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
                        ctrl != nullptr ? &ctrl->err : nullptr, nch, cand);
@@ -2184,10 +2184,14 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
     GBDT_LAUNCH_CHECK("k_find_merge");
     return GBDT_OK;
   }
-  // the fewest threads whose kFindE bins each cover the bins in one pass
-  const int32_t per_pass = (ft.total_bins + kFindE - 1) / kFindE;
-  const int threads = per_pass <= 256 ? 256 : (per_pass <= 512 ? 512 : 1024);
-  auto kern = threads == 256 ? k_find<256> : (threads == 512 ? k_find<512> : k_find<1024>);
+  // 1024 threads with the fewest bins per thread (1, 2, 4 or 8) that cover
+  // the bins in one pass (several passes of 8 above 8192 bins): a thread's
+  // scan and its candidates' FP64 divisions are a serial chain, so the
+  // node's latency falls with the bins per thread
+  const int32_t tb = ft.total_bins;
+  const int threads = 1024;
+  auto kern = tb <= 1024 ? k_find<1024, 1>
+                         : (tb <= 2048 ? k_find<1024, 2> : (tb <= 4096 ? k_find<1024, 4> : k_find<1024, 8>));
   hipLaunchKernelGGL(kern, dim3((unsigned)list_cap), dim3(threads), 0, s, hist_g, hist_cnt,
                      ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
                      list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
