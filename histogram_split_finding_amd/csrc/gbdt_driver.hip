@@ -163,7 +163,8 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t* __restrict__ n_nodes_out, PlanArgs pa,
                                                 int32_t part_tile, int32_t part_max_tiles,
                                                 int32_t hist_tile_max,
-                                                int32_t hist_target, int32_t hist_max_tiles_next) {
+                                                int32_t hist_target, int32_t hist_min_rows,
+                                                int32_t hist_max_tiles_next) {
   __shared__ PlanLds lds;
   __shared__ int32_t shm[6 * 17];
   for (int c = threadIdx.x; c < kPlanSizeBuckets; c += blockDim.x) lds.bucket[c] = 0;
@@ -210,9 +211,9 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   int32_t r[6], t[6];
   block_exclusive_scan_multi<6>(c, r, t, shm);
   // histogram tile rows of the next level from the rows it actually builds:
-  // about hist_target tiles, none below kHistMinTileRows (or above the packed
+  // about hist_target tiles, none below hist_min_rows (or above the packed
   // cells' limit)
-  const int32_t hist_tile_rows_next = hist_tile_rows_for(t[5], hist_tile_max, hist_target);
+  const int32_t hist_tile_rows_next = hist_tile_rows_for(t[5], hist_tile_max, hist_target, hist_min_rows);
   {
     int32_t nt = 0;
     if (fast) {
@@ -452,17 +453,19 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   int64_t h_tiles[GBDT_MAX_DEPTH + 1];
   int64_t p_tiles[GBDT_MAX_DEPTH + 1];
   // the level kernel sizes levels >= 1 from their actual rows (about
-  // `target` tiles of at least min(kHistMinTileRows, tile_max) rows, at most
+  // `target` tiles of at least min(min_rows, tile_max) rows, at most
   // tile_max); the bound below holds for every size it can choose
   const int32_t tile_max = hist_tile_max(n);
   // q is int32 (original order and both row buffers) when that is exact
   const bool q32 = driver_q32(n);
   const int32_t part_tile = part_tile_rows(n, X->n_blocks, q32);
   const int32_t target = hist_target_tiles(X->n_blocks + (X->n_bit_features > 0 ? 1 : 0));
+  const int32_t min_rows =
+      hist_min_tile_rows(ft->total_bins, int64_t(X->n_blocks) * X->block_stride + X->bit_stride);
   for (int32_t d = 0; d <= D; ++d) {
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
     const int64_t rows_build = d == 0 ? n : n / 2;
-    h_rows[d] = hist_tile_rows(rows_build, n, target);
+    h_rows[d] = hist_tile_rows(rows_build, n, target, min_rows);
     if (d == 0) {
       h_tiles[d] = (rows_build + h_rows[d] - 1) / h_rows[d] + cap_build;
     } else {
@@ -506,7 +509,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     diag_begin(kDiagLevel, s);
     hipLaunchKernelGGL(k_level, dim3(1), dim3(1024), 0, s, d, D, nodes_out, b->splits, tc, b->lists,
                        LL, min_split, p->reg_lambda, n_nodes_dev, pa, part_tile, (int32_t)p_tiles[d],
-                       tile_max, target, (int32_t)h_tiles[d + 1]);
+                       tile_max, target, min_rows, (int32_t)h_tiles[d + 1]);
     diag_end(s);
     {
       hipError_t e = hipGetLastError();

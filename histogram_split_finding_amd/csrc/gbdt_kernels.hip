@@ -108,10 +108,10 @@ WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
   return L;
 }
 
-int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows, int32_t target) {
+int32_t hist_tile_rows(int64_t rows_bound, int64_t n_rows, int32_t target, int32_t min_rows) {
   const int64_t tmax = (int64_t(1) << pack_bits_for(n_rows)) - 1;
   int64_t t = (rows_bound + target - 1) / target;
-  if (t < kHistMinTileRows) t = kHistMinTileRows;
+  if (t < min_rows) t = min_rows;
   if (t > tmax) t = tmax;
   if (t < 1) t = 1;
   return int32_t(t);
@@ -2514,7 +2514,9 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   TileDesc* hdesc = reinterpret_cast<TileDesc*>(w + L.hdesc);
   uint64_t* hpart = reinterpret_cast<uint64_t*>(w + L.hpart);
   const int32_t gy = src->X.n_blocks + (src->X.n_bit_features > 0 ? 1 : 0);
-  const int32_t T = hist_tile_rows(rows_bound, src->X.n_rows, hist_target_tiles(gy));
+  const int32_t T = hist_tile_rows(
+      rows_bound, src->X.n_rows, hist_target_tiles(gy),
+      hist_min_tile_rows(ft->total_bins, int64_t(src->X.n_blocks) * src->X.block_stride + src->X.bit_stride));
   const int64_t max_tiles = (rows_bound + T - 1) / T + list_cap;
   if (max_tiles > L.hpart_tiles) return fail(GBDT_E_SHAPE, "too many histogram tiles for the workspace");
   diag_begin(kDiagPlan, s);
