@@ -838,7 +838,6 @@ __device__ __forceinline__ double score_of(double G, double H, double lambda) {
   return num / den;
 }
 
-constexpr int kFindE = 8;  // bins per thread per pass
 
 // DPP lane move of a 32-bit value; lanes whose source is outside the row (or
 // whose row is masked off) read 0, the identity of both combines below.
@@ -2172,8 +2171,9 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
   const int32_t nch = cand != nullptr ? find_chunks(ft.total_bins) : 1;
   diag_begin(kDiagFind, s);
   if (nch > 1) {
-    // whole features of up to kFindChunk + 255 bins: one or two passes of 256 x kFindE
-    hipLaunchKernelGGL((k_find<256, kFindE>), dim3((unsigned)list_cap, (unsigned)nch), dim3(256), 0, s, hist_g,
+    // whole features of up to kFindChunk + 255 bins: one or two passes of
+    // 1024 threads x 2 bins
+    hipLaunchKernelGGL((k_find<1024, 2>), dim3((unsigned)list_cap, (unsigned)nch), dim3(1024), 0, s, hist_g,
                        hist_cnt, ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
                        list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
                        ctrl != nullptr ? &ctrl->err : nullptr, nch, cand);
