@@ -239,7 +239,7 @@ def test_find_best_splits(case):
 
 @pytest.mark.parametrize("n,nbins,seed", [(50000, [2, 256, 13, 64, 2, 2, 9], 31), (20011, [256] * 70, 32),
                                           (3, [4], 33), (30000, [256] * 10 + [2] * 44, 34),
-                                          (9000, [2] * 40 + [1] * 3, 35)])
+                                          (9000, [2] * 40 + [1] * 3, 35), (7001, [2] * 150 + [5] * 3, 36)])
 @pytest.mark.parametrize("pack_bits", [True, False])
 def test_partition_rows(n, nbins, seed, pack_bits):
     say("partition n=%d F=%d bits=%s" % (n, len(nbins), pack_bits))
