@@ -585,11 +585,8 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   // stage is < r1, so it exists); the reloads after the last stage read rows
   // that are never used.  Loop bounds are wave-uniform.
   constexpr int H = BATCH / 2;
-#ifdef GBDT_HIST_STAGES
-  constexpr int NS = GBDT_HIST_STAGES;
-#else
+  // (three or four stages keep more loads in flight but measured the same)
   constexpr int NS = 2;
-#endif
   constexpr int32_t SROWS = RPI * H;
   // rows are addressed from the tile's first row: a uniform base plus a
   // 32-bit lane offset (a tile holds < 2^24 rows of at most 32 bytes)
