@@ -181,7 +181,7 @@ __device__ __forceinline__ int32_t tiles_of(int32_t c, int32_t tile_rows) {
 // Second half of a tile plan, from entries already staged in LDS: stage[j]
 // the j-th list entry and spre[0..n] the exclusive prefix of its tiles
 // (spre[n] = total), both visible to the workgroup.  Writes prefix[0..n],
-// the multi-tile list (multi != nullptr), the plan total, ticket and cleared
+// the multi-tile list (multi != nullptr), the plan total and cleared
 // look-back status (status != nullptr) and every tile's descriptor (from LDS
 // only), then descriptors with node -1 up to max_tiles.  with_split: the
 // entries carry a split (partition plans).  *n_multi (LDS) must be 0 and
@@ -201,7 +201,6 @@ __device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, in
     if (total > max_tiles) dev_error(&ctrl->err, GBDT_E_SHAPE);
     if (status != nullptr) {
       ctrl->plan_total = total < max_tiles ? total : max_tiles;
-      ctrl->ticket = 0u;
     }
   }
   const int32_t lim = total < max_tiles ? total : max_tiles;
@@ -251,7 +250,7 @@ __device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, in
 // launch that follows reads its whole assignment with one load), descriptors
 // with node -1 for the launch's tiles [total, max_tiles), and, for a
 // partition plan (status != nullptr), a cleared look-back status array and
-// the ticket and plan total in ctrl, and (splits != nullptr) each node's
+// the plan total in ctrl, and (splits != nullptr) each node's
 // split in its tiles' descriptors (the split feature as its matrix column:
 // feature_col[feature], or the feature itself when feature_col is NULL),
 // and (multi != nullptr) the list positions
@@ -325,7 +324,6 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
     if (total > max_tiles) dev_error(&ctrl->err, GBDT_E_SHAPE);
     if (status != nullptr) {
       ctrl->plan_total = total < max_tiles ? total : max_tiles;
-      ctrl->ticket = 0u;
     }
   }
   __syncthreads();

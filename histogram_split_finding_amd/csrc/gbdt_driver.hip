@@ -100,8 +100,18 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
                                                     int32_t n, int64_t min_split, int32_t D,
                                                     double lambda, int32_t* __restrict__ n_nodes_out,
                                                     PlanArgs pa, int32_t tile_rows,
-                                                    int32_t max_tiles) {
+                                                    int32_t max_tiles,
+                                                    const int64_t* __restrict__ psum,
+                                                    int32_t nparts) {
   __shared__ PlanLds lds;
+  __shared__ int64_t s_part[1024 / 64];
+  // the root's sum of q from the gradient kernels' per-block partial sums
+  {
+    int64_t v = 0;
+    for (int i = threadIdx.x; i < nparts; i += blockDim.x) v += psum[i];
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = v;
+  }
   for (int i = threadIdx.x; i < GBDT_MAX_DEPTH + 2; i += blockDim.x) {
     tc->level_start[i] = 0;
     tc->level_count[i] = 0;
@@ -123,7 +133,10 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
     r.depth = 0;
     r.begin = 0;
     r.count = n;
-    r.gsum = tc->gsum_root;
+    int64_t gs = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) gs += s_part[w];
+    tc->gsum_root = gs;
+    r.gsum = gs;
     r.reserved = 0;
     tc->level_start[0] = 0;
     tc->level_count[0] = 1;
@@ -479,12 +492,15 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
       return fail(GBDT_E_INTERNAL, "tile bound exceeds the workspace");
   }
 
-  rc = launch_gradients(pred, label, n, b->q, q32, &tc->scale, &tc->gsum_root, b->ws, b->ws_bytes, s);
+  // (the sum of q stays as per-block partial sums; k_tree_init adds them)
+  double* gpart = reinterpret_cast<double*>(w + WL.gpart);
+  rc = launch_gradients(pred, label, n, b->q, q32, &tc->scale, nullptr, gpart, pa.ctrl, s);
   if (rc) return rc;
   diag_begin(kDiagTreeInit, s);
   hipLaunchKernelGGL(k_tree_init, dim3(1), dim3(1024), 0, s, nodes_out, b->splits, tc, b->lists, LL,
                      (int32_t)n, min_split, D, p->reg_lambda, n_nodes_dev, pa, h_rows[0],
-                     (int32_t)h_tiles[0]);
+                     (int32_t)h_tiles[0],
+                     reinterpret_cast<const int64_t*>(gpart + kGradBlocks), grad_blocks(n));
   diag_end(s);
   {
     hipError_t e = hipGetLastError();

@@ -31,7 +31,7 @@ static_assert(sizeof(FindCand) == 32, "candidate record is 32 bytes");
 struct WsCtrl {
   int32_t err;          // first device-side error code (0 = none)
   int32_t err_detail;   // call-specific detail (e.g. offending node)
-  uint32_t ticket;      // in-order tile ticket for the partition look-back
+  uint32_t unused0;
   int32_t plan_total;   // tiles planned by the last planner launch
   int32_t pad[60];
 };
@@ -64,7 +64,7 @@ constexpr int64_t kPartLargeRows = int64_t(1) << 22;  // matrices from this size
 
 // Rows per partition tile for a matrix of n rows in n_blocks byte blocks
 // whose moved q is int32 (q32) or int64: larger tiles carry more bytes per
-// latency chain (ticket, descriptor, flags, look-back) on large matrices of
+// latency chain (descriptor, flags, look-back) on large matrices of
 // one block (8192 rows when q moves as int32; with int64 q that kernel would
 // exceed the 64 registers of two workgroups per CU, so 4096); small matrices
 // keep more tiles than workgroup slots, and several blocks need the
@@ -100,14 +100,14 @@ struct TileDesc {
 static_assert(sizeof(TileDesc) == 48, "tile descriptor is 48 bytes");
 
 // Two tile plans live in the workspace at once: the partition plan
-// (tdesc, prefix, status, ctrl->ticket / plan_total) and the histogram plan
+// (tdesc, prefix, status, ctrl->plan_total) and the histogram plan
 // (hdesc, hprefix), so the level kernel of the tree driver can write this
 // level's partition plan and the next level's histogram plan together.
 struct WsLayout {
   size_t ctrl;        // WsCtrl
   size_t tdesc;       // TileDesc[tdesc_cap]: partition plan
   size_t hdesc;       // TileDesc[hpart_tiles]: histogram plan
-  size_t gpart;       // double[kGradBlocks]
+  size_t gpart;       // double[kGradBlocks] maxima, then int64[kGradBlocks] sums
   size_t prefix;      // int32[max_list + 2]: partition plan
   size_t hprefix;     // int32[max_list + 2]: histogram plan
   size_t hmulti;      // int32[max_list + 2]: histogram plan, nodes of several tiles
@@ -204,10 +204,19 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
                      hipStream_t s, bool qin32 = false, bool qout32 = false);
 
+// Blocks of the gradient kernels for n rows: each leaves a partial max |g|
+// and a partial sum of q in the workspace (gpart).
+inline int32_t grad_blocks(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return int32_t(b < kGradBlocks ? b : kGradBlocks);
+}
 // Gradients and the fixed-point grid (gbdt_compute_gradients); q32: q gets
 // int32 elements (the tree driver, ceil(log2 n) >= 22), otherwise int64.
+// part: the workspace's gpart region (partial maxima, then partial sums).
+// With gsum == nullptr the sum of q is left as grad_blocks(n) partial sums
+// at part + kGradBlocks (the tree driver adds them up itself).
 int launch_gradients(const double* pred, const float* label, int64_t n, void* q, bool q32,
-                     int32_t* scale, int64_t* gsum, void* ws, size_t ws_bytes, hipStream_t s);
+                     int32_t* scale, int64_t* gsum, double* part, WsCtrl* ctrl, hipStream_t s);
 
 // Whether the tree driver stores q as int32 (in its original-order buffer and
 // its two row buffers): exact when every |q| <= 2^(52 - ceil(log2 n)) fits 31

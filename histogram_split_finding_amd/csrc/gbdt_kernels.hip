@@ -88,7 +88,7 @@ WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
   L.hdesc = off;
   off = align256(off + sizeof(TileDesc) * size_t(L.hpart_tiles));
   L.gpart = off;
-  off = align256(off + sizeof(double) * kGradBlocks);
+  off = align256(off + (sizeof(double) + sizeof(int64_t)) * kGradBlocks);
   L.prefix = off;
   off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
   L.hprefix = off;
@@ -174,16 +174,27 @@ __global__ void __launch_bounds__(1024) k_plan(const gbdt_node* __restrict__ nod
 __global__ void __launch_bounds__(256) k_grad_max(const double* __restrict__ pred,
                                                   const float* __restrict__ label, int64_t n,
                                                   double* __restrict__ part,
-                                                  int64_t* __restrict__ gsum,
                                                   WsCtrl* __restrict__ ctrl) {
   __shared__ double sh[4];
   double m = 0.0;
   bool bad = false;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const double g = pred[i] - (double)label[i];
-    if (!isfinite(g)) bad = true;
-    m = fmax(m, fabs(g));
+  // four rows per thread per step, their loads issued together
+  for (int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i0 < n; i0 += 4 * stride) {
+    double p[4];
+    float l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      p[u] = i < n ? pred[i] : 0.0;
+      l[u] = i < n ? label[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const double g = p[u] - (double)l[u];
+      if (!isfinite(g)) bad = true;
+      m = fmax(m, fabs(g));
+    }
   }
   if (bad) dev_error(&ctrl->err, GBDT_E_RANGE);
   m = wave_max(m);
@@ -192,7 +203,6 @@ __global__ void __launch_bounds__(256) k_grad_max(const double* __restrict__ pre
   if (threadIdx.x == 0) {
     double r = fmax(fmax(sh[0], sh[1]), fmax(sh[2], sh[3]));
     part[blockIdx.x] = r;
-    if (blockIdx.x == 0) *gsum = 0;
   }
 }
 
@@ -205,11 +215,15 @@ __global__ void __launch_bounds__(256) k_grad_q(const double* __restrict__ pred,
                                                 int32_t log2n, const double* __restrict__ part,
                                                 int32_t nparts, QT* __restrict__ q,
                                                 int32_t* __restrict__ scale,
-                                                int64_t* __restrict__ gsum) {
+                                                int64_t* __restrict__ psum) {
   __shared__ double shm[4];
   __shared__ int64_t shs[4];
   double m = 0.0;
-  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = fmax(m, part[i]);
+#pragma unroll
+  for (int j = 0; j < kGradBlocks / 256; ++j) {
+    const int i = j * 256 + threadIdx.x;
+    if (i < nparts) m = fmax(m, part[i]);
+  }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) shm[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -223,18 +237,44 @@ __global__ void __launch_bounds__(256) k_grad_q(const double* __restrict__ pred,
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale = S;
   int64_t s = 0;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const double g = pred[i] - (double)label[i];
-    const int64_t k = (int64_t)rint(ldexp(g, S));
-    q[i] = (QT)k;
-    s += k;
+  for (int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i0 < n; i0 += 4 * stride) {
+    double p[4];
+    float l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      p[u] = i < n ? pred[i] : 0.0;
+      l[u] = i < n ? label[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n) {
+        const double g = p[u] - (double)l[u];
+        const int64_t k = (int64_t)rint(ldexp(g, S));
+        q[i] = (QT)k;
+        s += k;
+      }
+    }
   }
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) shs[threadIdx.x >> 6] = s;
   __syncthreads();
+  if (threadIdx.x == 0) psum[blockIdx.x] = shs[0] + shs[1] + shs[2] + shs[3];
+}
+
+// sum of q from the per-block partial sums (exact: integers)
+__global__ void __launch_bounds__(kGradBlocks) k_grad_sum(const int64_t* __restrict__ psum,
+                                                          int32_t nparts, int64_t* __restrict__ gsum) {
+  __shared__ int64_t sh[kGradBlocks / 64];
+  int64_t v = (int32_t)threadIdx.x < nparts ? psum[threadIdx.x] : 0;
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
   if (threadIdx.x == 0) {
-    int64_t t = shs[0] + shs[1] + shs[2] + shs[3];
-    atomicAdd(reinterpret_cast<unsigned long long*>(gsum), (unsigned long long)t);
+    int64_t t = 0;
+    for (int w = 0; w < kGradBlocks / 64; ++w) t += sh[w];
+    *gsum = t;
   }
 }
 
@@ -1272,8 +1312,12 @@ __global__ void __launch_bounds__(64) k_find_merge(const int32_t* __restrict__ l
 
 // -------------------------------------------------------------- partition --
 // Stable partition in one pass with a decoupled look-back across the tiles
-// of a node.  Tiles are taken in ticket order, so every tile a workgroup
-// waits on has already started.  Each status word packs a 2-bit state
+// of a node.  The tile is the workgroup's id and a tile waits only on
+// lower-numbered tiles.  Each XCD dispatches its share of a grid's
+// workgroups in increasing id order, so the lowest unfinished tile is
+// always resident (every earlier workgroup on its XCD has finished) and
+// never waits: the chain drains without an atomic tile counter at the start
+// of each tile's critical path.  Each status word packs a 2-bit state
 // (1 = tile count available, 2 = inclusive prefix available) with a 32-bit
 // value; the wait is bounded and reports GBDT_E_INTERNAL if it runs out.
 constexpr uint64_t kStAgg = 1ull << 62;
@@ -1406,8 +1450,8 @@ __device__ __forceinline__ void row_put(uint8_t* p, const RowData<ND>& d, bool n
     row_store<ND>(p, d);
 }
 
-// One workgroup per tile of K * kPartThreads rows of a splitting node, taken
-// in ticket order.  Thread t owns rows t + k kPartThreads of the tile and
+// One workgroup per tile of K * kPartThreads rows of a splitting node (tile
+// = workgroup id).  Thread t owns rows t + k kPartThreads of the tile and
 // moves each whole row itself: the row's bytes of a column block (ND dwords)
 // with one or two wide loads and stores, its q and row id, so a wave's
 // accesses cover 64 consecutive source rows and two runs of destinations
@@ -1437,14 +1481,11 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   constexpr int NCNT = K * kPartWaves;  // per-(row k, wave) left counts
   // an int32 destination q is the low half of the source element
   using QT = typename std::conditional<Q32OUT, int32_t, int64_t>::type;
-  __shared__ int32_t s_tile;
   __shared__ int32_t s_cnt[NCNT];
   __shared__ int32_t s_excl;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  if (threadIdx.x == 0) s_tile = (int32_t)atomicAdd(&ctrl->ticket, 1u);
-  __syncthreads();
-  const int32_t tile = s_tile;
+  const int32_t tile = (int32_t)blockIdx.x;
   const int32_t total = ctrl->plan_total;
   if (tile >= total) return;
   const bool nt = tile >= total - nt_tiles;  // (uniform)
@@ -2479,8 +2520,13 @@ int gbdt_pack_matrix(const uint8_t* rowmajor, const gbdt_matrix* dst, const gbdt
 int gbdt_compute_gradients(const double* pred, const float* label, int64_t n, int64_t* q,
                            int32_t* scale, int64_t* gsum, void* ws, size_t ws_bytes,
                            void* stream) {
-  return launch_gradients(pred, label, n, q, false, scale, gsum, ws, ws_bytes,
-                          reinterpret_cast<hipStream_t>(stream));
+  if (!gsum) return fail(GBDT_E_ARG, "null argument");
+  const WsLayout L = ws_layout(n < 1 ? 1 : n, 1, 1);
+  const int rc = check_ws(ws, ws_bytes, L);
+  if (rc) return rc;
+  char* w = static_cast<char*>(ws);
+  return launch_gradients(pred, label, n, q, false, scale, gsum, reinterpret_cast<double*>(w + L.gpart),
+                          reinterpret_cast<WsCtrl*>(w + L.ctrl), reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
@@ -2488,32 +2534,29 @@ int gbdt_compute_gradients(const double* pred, const float* label, int64_t n, in
 namespace gbdt {
 
 int launch_gradients(const double* pred, const float* label, int64_t n, void* q, bool q32,
-                     int32_t* scale, int64_t* gsum, void* ws, size_t ws_bytes, hipStream_t s) {
-  if (!pred || !label || !q || !scale || !gsum) return fail(GBDT_E_ARG, "null argument");
+                     int32_t* scale, int64_t* gsum, double* part, WsCtrl* ctrl, hipStream_t s) {
+  if (!pred || !label || !q || !scale) return fail(GBDT_E_ARG, "null argument");
   if (n < 1 || n > 0x7fffffffLL) return fail(GBDT_E_ARG, "n out of range");
   if (q32 && ceil_log2(n) < 22) return fail(GBDT_E_INTERNAL, "int32 q needs ceil(log2 n) >= 22");
-  const WsLayout L = ws_layout(n, 1, 1);
-  int rc = check_ws(ws, ws_bytes, L);
-  if (rc) return rc;
-  char* w = static_cast<char*>(ws);
-  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w + L.ctrl);
-  double* part = reinterpret_cast<double*>(w + L.gpart);
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > kGradBlocks) blocks = kGradBlocks;
+  int64_t* psum = reinterpret_cast<int64_t*>(part + kGradBlocks);
+  const int32_t blocks = grad_blocks(n);
   diag_begin(kDiagGradMax, s);
-  hipLaunchKernelGGL(k_grad_max, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n, part,
-                     gsum, ctrl);
+  hipLaunchKernelGGL(k_grad_max, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n, part, ctrl);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_grad_max");
   diag_begin(kDiagGradQ, s);
   if (q32)
     hipLaunchKernelGGL(k_grad_q<int32_t>, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n,
-                       ceil_log2(n), part, (int32_t)blocks, static_cast<int32_t*>(q), scale, gsum);
+                       ceil_log2(n), part, blocks, static_cast<int32_t*>(q), scale, psum);
   else
     hipLaunchKernelGGL(k_grad_q<int64_t>, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n,
-                       ceil_log2(n), part, (int32_t)blocks, static_cast<int64_t*>(q), scale, gsum);
+                       ceil_log2(n), part, blocks, static_cast<int64_t*>(q), scale, psum);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_grad_q");
+  if (gsum != nullptr) {
+    hipLaunchKernelGGL(k_grad_sum, dim3(1), dim3(kGradBlocks), 0, s, (const int64_t*)psum, blocks, gsum);
+    GBDT_LAUNCH_CHECK("k_grad_sum");
+  }
   return GBDT_OK;
 }
 
