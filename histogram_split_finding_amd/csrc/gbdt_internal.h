@@ -76,7 +76,8 @@ inline int32_t part_tile_rows(int64_t n_rows, int32_t n_blocks, bool q32) {
 constexpr int kHistMinTileRows = 1024;
 constexpr int kHistTargetTiles = 1024;    // workgroups per histogram launch to aim for
 constexpr int kHistMinTargetTiles = 128;
-constexpr int kReduceNodeSlots = 64;  // y extent of the partial-reduction grid
+constexpr int kReduceNodeSlots = 64;  // multi-tile nodes the partial-reduction grid covers at once
+constexpr int kReduceGrid = 512;      // at most this many reduction workgroups
 constexpr int kLdsHistBudgetBins = 8192;  // LDS slots (8 bytes) of one histogram workgroup: 64 KiB
 constexpr int kHistRowSlots = 32;          // LDS slots per bin row of a byte block's histogram
 constexpr int kHistMaxBlockStride = 32;    // bytes per row of a byte block, at most (8 dwords)

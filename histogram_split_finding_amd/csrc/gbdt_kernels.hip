@@ -827,10 +827,14 @@ __global__ void __launch_bounds__(1024) k_hist_reduce(const int32_t* __restrict_
   const int32_t nm = clamp_len(multi, list_cap);
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  const int32_t b = blockIdx.x * 64 + lane;
-  const bool inb = b < total_bins;
+  const int32_t nbc = (total_bins + 63) / 64;
   const uint64_t mask = (1ull << bits) - 1ull;
-  for (int32_t m = blockIdx.y; m < nm; m += gridDim.y) {
+  // work items (multi-tile node m, 64-bin chunk) in a grid-stride loop: a
+  // level with no multi-tile node ends after one load per workgroup
+  for (int32_t it = blockIdx.x; it < nm * nbc; it += gridDim.x) {
+    const int32_t m = it / nbc;
+    const int32_t b = (it - m * nbc) * 64 + lane;
+    const bool inb = b < total_bins;
     int32_t j = multi[1 + m];
     j = j < 0 ? 0 : (j >= list_cap ? list_cap - 1 : j);
     const int32_t t0 = prefix[j];
@@ -2219,14 +2223,18 @@ int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_c
                        const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s) {
   const int32_t bits = pack_bits_for(n_rows > 0 ? n_rows : 1);
   // multi-tile nodes hold more than one tile of rows each, so there are at
-  // most max_tiles / 2 of them; the y stride covers the rest
+  // most max_tiles / 2 of them; the grid covers up to kReduceNodeSlots of
+  // them at once (never more than kReduceGrid workgroups: most levels have
+  // few or no multi-tile nodes, and empty workgroups still take dispatch
+  // time), the grid-stride loop the rest
   int64_t gy = max_tiles / 2 < list_cap ? max_tiles / 2 : list_cap;
   if (gy > kReduceNodeSlots) gy = kReduceNodeSlots;
   if (gy < 1) gy = 1;
+  int64_t grid = int64_t((total_bins + 63) / 64) * gy;
+  if (grid > kReduceGrid) grid = kReduceGrid;
   diag_begin(kDiagHistReduce, s);
-  hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)((total_bins + 63) / 64), (unsigned)gy),
-                     dim3(1024), 0, s, list, multi, list_cap, prefix, (int32_t)max_tiles, bits,
-                     total_bins, hpart, hist_g, hist_cnt);
+  hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)grid), dim3(1024), 0, s, list, multi, list_cap,
+                     prefix, (int32_t)max_tiles, bits, total_bins, hpart, hist_g, hist_cnt);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist_reduce");
   return GBDT_OK;
