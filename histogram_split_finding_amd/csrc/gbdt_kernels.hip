@@ -2266,13 +2266,22 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
   // scan and its candidates' FP64 divisions are a serial chain, so the
   // node's latency falls with the bins per thread
   const int32_t tb = ft.total_bins;
-  const int threads = 1024;
+  int threads = 1024;
   auto kern = tb <= 1024   ? k_find<1024, 1>
               : tb <= 2048 ? k_find<1024, 2>
               : tb <= 3072 ? k_find<1024, 3>
               : tb <= 4096 ? k_find<1024, 4>
               : tb <= 6144 ? k_find<1024, 6>
                            : k_find<1024, 8>;
+  if (list_cap > 256 && tb <= 4096) {
+    threads = 512;
+    kern = tb <= 512    ? k_find<512, 1>
+           : tb <= 1024 ? k_find<512, 2>
+           : tb <= 1536 ? k_find<512, 3>
+           : tb <= 2048 ? k_find<512, 4>
+           : tb <= 3072 ? k_find<512, 6>
+                        : k_find<512, 8>;
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)list_cap), dim3(threads), 0, s, hist_g, hist_cnt,
                      ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
                      list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
