@@ -22,6 +22,9 @@ Output: one JSON line on stdout (progress goes to stderr).
              device time) for further workloads, 10 trees each: by default
              the 50,000,000 x 28 one (64 uniform bins, depth 12), the largest,
              whose histogram build is bound by HBM rather than by latency
+  binning    raw FP32 values to uint8 bins (the step before the path) at the
+             50M x 28 x 64-bin shape: values/s, its HBM roofline and the
+             oracle on a 200K-row sample
 """
 from __future__ import annotations
 
@@ -213,6 +216,65 @@ def measure(g, datagen, torch, k, K, W, diag):
     return out
 
 
+DIAG_BIN = 13
+
+
+def measure_binning(g, torch, R, with_cpu):
+    """Raw FP32 -> uint8 binning (gbdt_bin_features) at the 50M x 28 x 64-bin
+    shape: standard normal values, 63 equal-width bounds per feature over
+    [-3, 3].  R timed launches after 3 warm-ups; the kernel's time comes from
+    the library's events around each launch on its stream.  Algorithmic bytes:
+    4 read + 1 written per value."""
+    import ctypes
+    n, F, B = 50_000_000, 28, 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(61)
+    raw = torch.randn((n, F), generator=gen, dtype=torch.float32, device="cuda")
+    kk = np.arange(1, B, dtype=np.float64)
+    one = np.concatenate([(-3.0 + 6.0 * kk / B).astype(np.float32), np.zeros(1, dtype=np.float32)])
+    upper_host = np.tile(one, F)
+    upper = torch.from_numpy(upper_host).cuda()
+    ft = g.FeatureTable([B] * F, "cuda", pack_bits=False)
+    out = torch.empty((n, F), dtype=torch.uint8, device="cuda")
+    ws = g.new_workspace(g.gbdt_workspace_bytes(n, 1, 1))
+    for _ in range(3):
+        g.gbdt_bin_features(raw, ft, upper, out, ws)
+    torch.cuda.synchronize()
+    lib = g.load()
+    assert lib.gbdt_diag_enable(R) == 0
+    t0 = time.perf_counter()
+    for _ in range(R):
+        g.gbdt_bin_features(raw, ft, upper, out, ws)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / R
+    kinds = np.zeros(R, dtype=np.int32)
+    ms = np.zeros(R, dtype=np.float32)
+    cnt = ctypes.c_int32()
+    assert lib.gbdt_diag_read(R, kinds.ctypes.data_as(ctypes.c_void_p), ms.ctypes.data_as(ctypes.c_void_p),
+                              ctypes.byref(cnt)) == 0
+    lib.gbdt_diag_disable()
+    if g.gbdt_read_error(ws) != 0:
+        raise RuntimeError("binning: device-side error")
+    t = float(ms[: cnt.value][kinds[: cnt.value] == DIAG_BIN].mean()) * 1e-3
+    alg = 5 * n * F
+    res = {"config": {"workload": "binning_50Mx28_b64_equal_width", "rows": n, "features": F, "bins": B},
+           "value": n * F / t, "unit": "values/s", "launches": R, "ms_per_launch_wall": wall * 1e3,
+           "roofline": {"bound": "hbm", "achieved": alg / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": alg / t / 1e9 / HBM_PEAK_GBS, "traffic": None, "kernel": "k_bin",
+                        "avg_launch_us": t * 1e6, "alg_bytes_per_launch": alg}}
+    if with_cpu:
+        import oracle
+        m = 200_000
+        sample = raw[:m].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.bin_features(sample, [B] * F, upper_host)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": m * F / dt, "unit": "values/s", "cores": 1, "kind": "oracle",
+                               "sample": "first %d rows, single thread" % m}
+    del raw, out
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +287,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-diag", action="store_true", help="skip the per-kernel timing pass")
+    ap.add_argument("--no-binning", action="store_true", help="skip the binning measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -266,6 +329,9 @@ def main():
                               if key in res})
     if secondary:
         out["also"] = secondary
+    if not args.no_binning:
+        log("binning 50M x 28 (raw FP32 -> 64 bins)")
+        out["binning"] = measure_binning(g, torch, 20, not args.no_cpu_baseline)
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)

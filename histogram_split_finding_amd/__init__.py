@@ -104,6 +104,7 @@ def load():
         "gbdt_choose_blocking": (ctypes.c_int, [i32, vp, P(Matrix), P(i32)]),
         "gbdt_choose_layout": (ctypes.c_int, [i32, vp, i32, P(Matrix), P(i32), vp, vp]),
         "gbdt_pack_matrix": (ctypes.c_int, [vp, P(Matrix), P(Features), vp, ctypes.c_size_t, vp]),
+        "gbdt_bin_features": (ctypes.c_int, [vp, i64, P(Features), vp, vp, vp, ctypes.c_size_t, vp]),
         "gbdt_read_error": (ctypes.c_int, [vp, vp]),
         "gbdt_compute_gradients": (ctypes.c_int, [vp, vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "gbdt_build_histograms": (ctypes.c_int, [P(Rows), P(Features), vp, vp, vp, i32, i64, vp, vp,
@@ -302,6 +303,16 @@ def gbdt_pack_matrix(rowmajor, rb: RowBuffer, ft: FeatureTable, ws, stream=None)
     rc = load().gbdt_pack_matrix(_ptr(rowmajor), ctypes.byref(m), ctypes.byref(f), _ptr(ws),
                                  ws.numel(), _stream(stream))
     _check(rc, "gbdt_pack_matrix")
+
+
+def gbdt_bin_features(raw, ft: FeatureTable, upper, bins_out, ws, stream=None):
+    """raw: float32 [n][F] device tensor; upper: float32 [total_bins] (feature f's
+    bounds at bin_offset[f] + k); bins_out: uint8 [n][F]."""
+    f = ft.struct()
+    rc = load().gbdt_bin_features(_ptr(raw), int(raw.shape[0]) if raw.dim() > 0 else 0,
+                                  ctypes.byref(f), _ptr(upper), _ptr(bins_out), _ptr(ws), ws.numel(),
+                                  _stream(stream))
+    _check(rc, "gbdt_bin_features")
 
 
 def gbdt_read_error(ws, stream=None) -> int:

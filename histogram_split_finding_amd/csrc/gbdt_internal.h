@@ -229,7 +229,7 @@ inline bool driver_q32(int64_t n_rows) { return ceil_log2(n_rows) >= 22; }
 // launch of the library is bracketed by two hipEvents on its stream.
 enum DiagKind {
   kDiagGradMax = 1, kDiagGradQ, kDiagPlan, kDiagHist, kDiagHistReduce, kDiagSubtract, kDiagFind,
-  kDiagTreeInit, kDiagLevel, kDiagPartition, kDiagUpdate, kDiagPack
+  kDiagTreeInit, kDiagLevel, kDiagPartition, kDiagUpdate, kDiagPack, kDiagBin
 };
 void diag_begin(int kind, hipStream_t s);
 void diag_end(hipStream_t s);

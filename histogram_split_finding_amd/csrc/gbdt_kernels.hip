@@ -2291,6 +2291,122 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
   return GBDT_OK;
 }
 
+// ------------------------------------------------------- feature binning --
+// Raw FP32 values to uint8 bins: the "Quantized" state that "Module Design:
+// Training Core" (section 5, state machine) puts between validation and
+// training.  Feature f has n_bins[f] bins and n_bins[f] - 1 strictly
+// increasing FP32 upper bounds at upper[bin_offset[f] + k], k < n_bins[f] - 1
+// (the entry at k = n_bins[f] - 1 is not read).  A value's bin is the number
+// of its feature's bounds strictly below it: x <= upper[0] gives bin 0, a
+// value above every bound the last bin.  Only comparisons, so exact.  A NaN
+// value gets bin 0 and sets GBDT_E_RANGE, and so do bounds that are NaN or
+// not strictly increasing (checked one global bin per thread).
+//
+// Each thread bins 16 consecutive values of the row-major matrix per step
+// (four 16-byte loads, one 16-byte store), in a grid-stride loop; the
+// feature index advances incrementally, with no division per value.  The
+// bounds (and each feature's offset and bound count) are staged in LDS when
+// they fit (LDS = true), else read from global memory.  Each value's search
+// is binary lifting with a fixed 8 steps (at most 255 bounds), so the 16
+// searches of a thread are independent chains the compiler interleaves.
+constexpr int kBinThreads = 256;
+constexpr int kBinGrid = 2048;
+constexpr size_t kBinLdsBytes = 64 * 1024;
+
+__device__ __forceinline__ uint32_t bin_of(const float* __restrict__ t, int32_t nb, float x) {
+  int32_t c = 0;
+#pragma unroll
+  for (int32_t s = 128; s >= 1; s >>= 1) {
+    const int32_t probe = c + s - 1;
+    if (probe < nb && t[probe] < x) c += s;
+  }
+  return (uint32_t)c;
+}
+
+template <bool LDS>
+__global__ void __launch_bounds__(kBinThreads) k_bin(const float* __restrict__ raw, int64_t n_vals,
+                                                     int32_t F, const int32_t* __restrict__ n_bins,
+                                                     const int32_t* __restrict__ bin_offset,
+                                                     const int32_t* __restrict__ bin_feature,
+                                                     int32_t total_bins, const float* __restrict__ upper,
+                                                     uint8_t* __restrict__ out, WsCtrl* __restrict__ ctrl) {
+  extern __shared__ float s_bin[];  // LDS: [total_bins] bounds, then [F] offsets, [F] bound counts
+  const float* tab = upper;
+  const int32_t* offs = bin_offset;
+  int32_t* s_off = reinterpret_cast<int32_t*>(s_bin + total_bins);
+  int32_t* s_nb = s_off + F;
+  if constexpr (LDS) {
+    for (int32_t i = threadIdx.x; i < total_bins; i += blockDim.x) s_bin[i] = upper[i];
+    for (int32_t f = threadIdx.x; f < F; f += blockDim.x) {
+      s_off[f] = bin_offset[f];
+      s_nb[f] = n_bins[f] - 1;
+    }
+    __syncthreads();
+    tab = s_bin;
+    offs = s_off;
+  }
+  const int64_t G = int64_t(gridDim.x) * blockDim.x;
+  int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  {
+    // the bounds, one global bin per thread: bound k of feature f is read
+    // when k < n_bins[f] - 1 and compared with bound k + 1 below the last
+    bool bad = false;
+    for (int64_t i = c; i < total_bins; i += G) {
+      const int32_t fb = bin_feature[i];
+      const int32_t k = (int32_t)i - bin_offset[fb], nb = n_bins[fb] - 1;
+      if (k < nb) {
+        const float u = upper[i];
+        bad |= u != u || (k + 1 < nb && !(u < upper[i + 1]));
+      }
+    }
+    if (bad) dev_error(&ctrl->err, GBDT_E_RANGE);
+  }
+  const int64_t nchunks = (n_vals + 15) / 16;
+  if (c >= nchunks) return;
+  int32_t f = (int32_t)((c * 16) % F);
+  const int32_t step_f = (int32_t)((G * 16) % F);
+  bool nan = false;
+  for (; c < nchunks; c += G) {
+    const int64_t i0 = c * 16;
+    const bool full = i0 + 16 <= n_vals;
+    float v[16];
+    if (full) {
+      const float4* p = reinterpret_cast<const float4*>(raw + i0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 x = p[q];
+        v[4 * q] = x.x;
+        v[4 * q + 1] = x.y;
+        v[4 * q + 2] = x.z;
+        v[4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = i0 + e < n_vals ? raw[i0 + e] : 0.0f;
+    }
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    int32_t fe = f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int32_t o = offs[fe];
+      const int32_t nb = LDS ? s_nb[fe] : n_bins[fe] - 1;
+      nan |= v[e] != v[e];
+      w[e >> 2] |= bin_of(tab + o, nb, v[e]) << (8 * (e & 3));
+      fe = fe + 1 == F ? 0 : fe + 1;
+    }
+    if (full) {
+      *reinterpret_cast<uint4*>(out + i0) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (i0 + e < n_vals) out[i0 + e] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+    }
+    f += step_f;
+    if (f >= F) f -= F;
+  }
+  if (nan) dev_error(&ctrl->err, GBDT_E_RANGE);
+}
+
 template <int K, bool Q>
 static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K, Q>) {
   switch (nd) {
@@ -2481,6 +2597,38 @@ int gbdt_read_error(void* ws, void* stream) {
     if (e != hipSuccess) return hip_fail(e, "clearing the error word");
     return fail(c.err, "device-side check failed (code " + std::to_string(c.err) + ")");
   }
+  return GBDT_OK;
+}
+
+int gbdt_bin_features(const float* raw, int64_t n_rows, const gbdt_features* ft, const float* upper,
+                      uint8_t* bins_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!ft || !upper) return fail(GBDT_E_ARG, "null argument");
+  if (n_rows < 0 || n_rows > 0x7fffffffLL) return fail(GBDT_E_ARG, "n_rows out of range");
+  if (n_rows > 0 && (!raw || !bins_out)) return fail(GBDT_E_ARG, "null argument");
+  if (ft->n_features < 1 || ft->n_features > GBDT_MAX_FEATURES) return fail(GBDT_E_ARG, "n_features out of range");
+  int rc = check_features(*ft, ft->n_features);
+  if (rc) return rc;
+  if (!aligned(raw, 16) || !aligned(bins_out, 16)) return fail(GBDT_E_ARG, "raw and bins_out must be 16-byte aligned");
+  const WsLayout L = ws_layout(n_rows < 1 ? 1 : n_rows, 1, 1);
+  rc = check_ws(ws, ws_bytes, L);
+  if (rc) return rc;
+  if (n_rows == 0) return GBDT_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(static_cast<char*>(ws) + L.ctrl);
+  const int32_t F = ft->n_features;
+  const int64_t n_vals = n_rows * F;
+  int64_t grid = (n_vals + 16 * kBinThreads - 1) / (16 * kBinThreads);
+  if (grid > kBinGrid) grid = kBinGrid;
+  const size_t lds = sizeof(float) * size_t(ft->total_bins) + 2 * sizeof(int32_t) * size_t(F);
+  diag_begin(kDiagBin, s);
+  if (lds <= kBinLdsBytes)
+    hipLaunchKernelGGL(k_bin<true>, dim3((unsigned)grid), dim3(kBinThreads), lds, s, raw, n_vals, F, ft->n_bins,
+                       ft->bin_offset, ft->bin_feature, ft->total_bins, upper, bins_out, ctrl);
+  else
+    hipLaunchKernelGGL(k_bin<false>, dim3((unsigned)grid), dim3(kBinThreads), 0, s, raw, n_vals, F, ft->n_bins,
+                       ft->bin_offset, ft->bin_feature, ft->total_bins, upper, bins_out, ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_bin");
   return GBDT_OK;
 }
 

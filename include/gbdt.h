@@ -264,6 +264,29 @@ int gbdt_pack_matrix(const uint8_t* rowmajor, const gbdt_matrix* dst /* host */,
                      const gbdt_features* ft /* host */, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Feature binning: the "Quantized" state of the Training Core page's state
+ * machine (section 5), the step that turns raw values into the bins every
+ * other call reads.  raw (device, FP32, [n_rows][n_features] row-major,
+ * 16-byte aligned) is written to bins_out (device, uint8, same shape and
+ * layout, 16-byte aligned; the input of gbdt_pack_matrix).  Feature f has
+ * ft->n_bins[f] bins and ft->n_bins[f] - 1 strictly increasing FP32 upper
+ * bounds at upper[ft->bin_offset[f] + k] (device, [total_bins]; the entry at
+ * k = n_bins[f] - 1 is not read).  A value's bin is the number of its
+ * feature's bounds strictly below it: x <= the first bound gives bin 0, x
+ * above every bound gives n_bins[f] - 1; -inf and +inf are ordinary values.
+ * Comparisons only, so the result is exact.  A NaN value is written as bin 0
+ * and sets GBDT_E_RANGE in the error word; so do bounds that are NaN or not
+ * strictly increasing.  Uses the workspace's error word only (size from
+ * gbdt_workspace_bytes(n_rows, 1, 1)).  ft needs n_bins, bin_offset and
+ * bin_feature.  Host-checked errors (null or misaligned pointers, sizes)
+ * return before anything is enqueued; with n_rows = 0 nothing is enqueued
+ * (raw and bins_out may then be NULL).  Setup step, not part of the per-tree
+ * path.
+ */
+int gbdt_bin_features(const float* raw, int64_t n_rows, const gbdt_features* ft /* host */,
+                      const float* upper, uint8_t* bins_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Diagnostics (Training Core section 4, diagnostics()): per-kernel device
  * time.  While enabled, each kernel launch of the library is bracketed by two
  * hipEvents on its stream (up to `capacity` launches are kept).
@@ -271,7 +294,7 @@ int gbdt_pack_matrix(const uint8_t* rowmajor, const gbdt_matrix* dst /* host */,
  * launch into host arrays and clears the record.  Kinds: 1 gradient max,
  * 2 gradient grid, 3 tile planner, 4 histogram, 5 histogram partial reduce,
  * 6 subtraction, 7 split search, 8 tree init, 9 level bookkeeping,
- * 10 partition, 11 prediction update, 12 packing.  One process-wide record;
+ * 10 partition, 11 prediction update, 12 packing, 13 binning.  One process-wide record;
  * not for concurrent use from several threads.
  */
 int gbdt_diag_enable(int32_t capacity);

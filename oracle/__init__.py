@@ -84,6 +84,8 @@ def _load():
     lib.orc_train.restype = ctypes.c_int
     lib.orc_train.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp, ctypes.POINTER(OrcParams),
                               ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp]
+    lib.orc_bin_features.restype = ctypes.c_int64
+    lib.orc_bin_features.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -176,6 +178,25 @@ def partition(bins, rows, feature: int, threshold_bin: int):
     nl = _load().orc_partition(_p(bins), bins.shape[1], _p(rows), rows.shape[0], feature,
                                threshold_bin, _p(left), _p(right))
     return left[:nl].copy(), right[:rows.shape[0] - nl].copy()
+
+
+def bin_features(raw, n_bins, upper):
+    """Bins of a float32 [n][F] matrix: per value, the number of its feature's
+    upper bounds strictly below it (bounds of feature f at bin_offset[f] + k,
+    k < n_bins[f] - 1).  Returns (uint8 [n][F], NaN count), or (None, -1) when
+    the bounds are NaN or not strictly increasing."""
+    raw = np.ascontiguousarray(raw, dtype=np.float32)
+    nb = np.ascontiguousarray(n_bins, dtype=np.int32)
+    off = bin_offsets(nb)
+    upper = np.ascontiguousarray(upper, dtype=np.float32)
+    if upper.shape[0] < int(off[-1]):
+        raise ValueError("upper must hold total_bins entries")
+    out = np.zeros(raw.shape, dtype=np.uint8)
+    rc = int(_load().orc_bin_features(raw.shape[0], raw.shape[1], _p(raw), _p(nb), _p(off), _p(upper),
+                                      _p(out)))
+    if rc < 0:
+        return None, rc
+    return out, rc
 
 
 def max_nodes(max_depth: int) -> int:

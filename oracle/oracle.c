@@ -486,3 +486,39 @@ done:
   free(hh);
   return rc;
 }
+
+/*
+ * Feature binning: the "Quantized" state between validation and training in
+ * the Training Core page's state machine (section 5).  The pages name the
+ * state but not the rule; the reading used here: feature f has n_bins[f]
+ * bins and n_bins[f] - 1 strictly increasing upper bounds
+ * upper[bin_offset[f] + k], and a value's bin is how many of those bounds are
+ * strictly below it (a value equal to a bound stays in the lower bin).  Each
+ * value is compared with every bound of its feature in turn; nothing is
+ * searched or skipped.  A NaN value compares below nothing and gets bin 0.
+ * Returns -1 when a bound is NaN or the bounds of a feature are not strictly
+ * increasing (out is then not written), else the number of NaN values.
+ */
+int64_t orc_bin_features(int64_t n_rows, int32_t F, const float* raw, const int32_t* n_bins,
+                         const int32_t* bin_offset, const float* upper, uint8_t* out) {
+  for (int32_t f = 0; f < F; ++f) {
+    const float* u = upper + bin_offset[f];
+    for (int32_t k = 0; k + 1 < n_bins[f]; ++k) {
+      if (isnan(u[k])) return -1;
+      if (k + 2 < n_bins[f] && !(u[k] < u[k + 1])) return -1;
+    }
+  }
+  int64_t n_nan = 0;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    for (int32_t f = 0; f < F; ++f) {
+      const float x = raw[r * F + f];
+      const float* u = upper + bin_offset[f];
+      int32_t below = 0;
+      for (int32_t k = 0; k + 1 < n_bins[f]; ++k)
+        if (u[k] < x) ++below;
+      if (isnan(x)) ++n_nan;
+      out[r * F + f] = (uint8_t)below;
+    }
+  }
+  return n_nan;
+}

@@ -463,3 +463,93 @@ def test_skip_bins_and_bit_layout_do_not_change_bits():
         bst.check()
         res.append((b"".join(t.tobytes() for t in bst.host_trees()), bst.pred.cpu().numpy().tobytes()))
     assert res[0] == res[1] == res[2] == res[3]
+
+
+# ---------------------------------------------------------------- binning --
+
+def _bin_inputs(n, nbins, seed):
+    """Raw float32 [n][F] and per-feature strictly increasing bounds; values
+    include every bound exactly, its float32 neighbours and +-inf."""
+    rng = np.random.default_rng(seed)
+    off = oracle.bin_offsets(nbins)
+    upper = np.full(int(off[-1]), 1e9, dtype=np.float32)
+    raw = rng.normal(0, 2.5, size=(n, len(nbins))).astype(np.float32)
+    for f, nb in enumerate(nbins):
+        b = np.unique(rng.normal(0, 2, size=3 * nb + 8).astype(np.float32))[: nb - 1]
+        upper[off[f]: off[f] + nb - 1] = b
+        if nb > 1:
+            m = n // 4
+            pick = rng.integers(0, nb - 1, size=3 * m)
+            rows = rng.permutation(n)[: 3 * m]
+            raw[rows[:m], f] = b[pick[:m]]
+            raw[rows[m:2 * m], f] = np.nextafter(b[pick[m:2 * m]], np.float32(np.inf))
+            raw[rows[2 * m:], f] = np.nextafter(b[pick[2 * m:]], np.float32(-np.inf))
+    if n > 2:
+        raw[n // 2, :] = np.inf
+        raw[n // 3, :] = -np.inf
+    return raw, upper
+
+
+BIN_CASES = [
+    # n * F = 7007: whole 16-value chunks and a ragged tail; bins from 1 to 256
+    ("ragged_mixed", 1001, [4, 1, 2, 256, 17, 3, 64], 51),
+    # the 28 x 64-bin feature shape over several grid strides of chunks
+    ("f28_b64", 200003, [64] * 28, 52),
+    # 25,600 bins: the bounds do not fit LDS and are read from global memory
+    ("global_bounds", 3001, [256] * 100, 53),
+    ("one_feature", 37, [255], 54),
+    ("one_row", 1, [9, 2, 200], 55),
+]
+
+
+@pytest.mark.parametrize("case", BIN_CASES, ids=[c[0] for c in BIN_CASES])
+def test_bin_features_matches_oracle(case):
+    name, n, nbins, seed = case
+    say("bin_features %s n=%d F=%d" % (name, n, len(nbins)))
+    raw, upper = _bin_inputs(n, nbins, seed)
+    want, n_nan = oracle.bin_features(raw, nbins, upper)
+    assert n_nan == 0
+    ft = g.FeatureTable(nbins, DEV, pack_bits=False)
+    out = torch.full((n, len(nbins)), 0xEE, dtype=torch.uint8, device=DEV)
+    ws = _ws(n, 1, 1)
+    g.gbdt_bin_features(to_dev(raw), ft, to_dev(upper), out, ws)
+    assert g.gbdt_read_error(ws) == 0
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_bin_features_nan_and_bad_bounds():
+    say("bin_features NaN values and bad bounds")
+    nbins = [8, 3]
+    raw, upper = _bin_inputs(500, nbins, 56)
+    raw[7, 0] = np.nan
+    raw[499, 1] = np.nan
+    want, n_nan = oracle.bin_features(raw, nbins, upper)
+    assert n_nan == 2
+    ft = g.FeatureTable(nbins, DEV, pack_bits=False)
+    out = torch.zeros((500, 2), dtype=torch.uint8, device=DEV)
+    ws = _ws(500, 1, 1)
+    g.gbdt_bin_features(to_dev(raw), ft, to_dev(upper), out, ws)
+    assert g.gbdt_read_error(ws) == -3
+    assert np.array_equal(out.cpu().numpy(), want)  # NaN -> bin 0, the rest as usual
+    bad = upper.copy()
+    bad[2] = bad[1]  # feature 0: two equal bounds
+    assert oracle.bin_features(raw, nbins, bad)[0] is None
+    ws2 = _ws(500, 1, 1)
+    raw_ok = np.nan_to_num(raw, nan=0.0)
+    g.gbdt_bin_features(to_dev(raw_ok), ft, to_dev(bad), out, ws2)
+    assert g.gbdt_read_error(ws2) == -3
+
+
+def test_bin_features_empty_and_misaligned():
+    say("bin_features empty input and a misaligned pointer")
+    ft = g.FeatureTable([4, 4], DEV, pack_bits=False)
+    upper = to_dev(np.array([0, 1, 2, 0, 0, 1, 2, 0], dtype=np.float32))
+    ws = _ws(1, 1, 1)
+    out = torch.full((0, 2), 7, dtype=torch.uint8, device=DEV)
+    g.gbdt_bin_features(torch.zeros((0, 2), dtype=torch.float32, device=DEV), ft, upper, out, ws)
+    assert g.gbdt_read_error(ws) == 0
+    big = torch.zeros(2 * 64 + 1, dtype=torch.float32, device=DEV)
+    raw = big[1:].view(64, 2)  # 4-byte offset: not 16-byte aligned
+    out = torch.zeros((64, 2), dtype=torch.uint8, device=DEV)
+    with pytest.raises(g.GbdtError):
+        g.gbdt_bin_features(raw, ft, upper, out, ws)

@@ -440,3 +440,64 @@ def test_depth_zero_is_single_leaf():
     assert root["flags"] & oracle.LEAF
     s = float(sum(Fraction(float(x)) for x in label))
     assert abs(float(root["leaf_value"]) - s / 101.0) <= 1e-12 * (1 + abs(s))
+
+
+# ---------------------------------------------------------------- binning --
+# The binning reading (the Training Core page's "Quantized" state): a value's
+# bin is the number of its feature's upper bounds strictly below it.
+
+def test_binning_hand_example():
+    """Bounds 1 < 2 < 3 (four bins), worked by hand: a value equal to a bound
+    stays in the lower bin, -inf goes to bin 0 and +inf to bin 3, NaN to bin 0
+    (and is counted).  The unused fourth entry holds -100: counting it would
+    move every value up one bin."""
+    x = np.array([-np.inf, 0.5, 1.0, 1.5, 2.0, 2.5, 3.0, 3.5, np.inf, np.nan], dtype=np.float32)
+    upper = np.array([1.0, 2.0, 3.0, -100.0], dtype=np.float32)
+    out, n_nan = oracle.bin_features(x.reshape(-1, 1), [4], upper)
+    assert out[:, 0].tolist() == [0, 0, 0, 1, 1, 2, 2, 3, 3, 0]
+    assert n_nan == 1
+
+
+def test_binning_matches_searchsorted():
+    """numpy.searchsorted(bounds, x, side='left') is the count of bounds
+    strictly below x: the same definition, computed by a library routine.
+    Values include every bound exactly, its float32 neighbours and +-inf."""
+    rng = np.random.default_rng(11)
+    nbins = [1, 2, 3, 17, 64, 255, 256, 5]
+    off = oracle.bin_offsets(nbins)
+    upper = np.full(int(off[-1]), 7.0, dtype=np.float32)
+    bounds = []
+    for f, nb in enumerate(nbins):
+        b = np.unique(rng.normal(0, 2, size=3 * nb).astype(np.float32))[: nb - 1]
+        assert b.shape[0] == nb - 1
+        upper[off[f]: off[f] + nb - 1] = b
+        bounds.append(b)
+    n = 3000
+    raw = rng.normal(0, 2.5, size=(n, len(nbins))).astype(np.float32)
+    for f, b in enumerate(bounds):
+        if b.shape[0] == 0:
+            continue
+        pick = rng.integers(0, b.shape[0], size=600)
+        raw[:200, f] = b[pick[:200]]
+        raw[200:400, f] = np.nextafter(b[pick[200:400]], np.float32(np.inf))
+        raw[400:600, f] = np.nextafter(b[pick[400:600]], np.float32(-np.inf))
+    raw[600, :] = np.inf
+    raw[601, :] = -np.inf
+    out, n_nan = oracle.bin_features(raw, nbins, upper)
+    assert n_nan == 0
+    for f, b in enumerate(bounds):
+        want = np.searchsorted(b, raw[:, f], side="left")
+        assert np.array_equal(out[:, f].astype(np.int64), want), f
+    assert out[601].tolist() == [0] * len(nbins)
+    assert out[600].tolist() == [nb - 1 for nb in nbins]
+
+
+def test_binning_degenerate_and_bad_bounds():
+    """One bin (no bounds) puts every value in bin 0; bounds that are NaN,
+    equal or decreasing are rejected."""
+    raw = np.array([[-1e30], [0.0], [1e30]], dtype=np.float32)
+    out, n_nan = oracle.bin_features(raw, [1], np.array([5.0], dtype=np.float32))
+    assert out[:, 0].tolist() == [0, 0, 0] and n_nan == 0
+    for bad in ([2.0, 1.0, 0.0], [1.0, 1.0, 0.0], [np.nan, 1.0, 0.0], [0.0, np.nan, 0.0]):
+        out, rc = oracle.bin_features(raw, [3], np.array(bad, dtype=np.float32))
+        assert out is None and rc == -1, bad
