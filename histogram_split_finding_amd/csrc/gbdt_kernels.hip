@@ -2323,6 +2323,9 @@ __device__ __forceinline__ uint32_t bin_of(const float* __restrict__ t, int32_t 
   return (uint32_t)c;
 }
 
+// bounds of a feature of nb bins (a feature table holds 1..256 bins)
+__device__ __forceinline__ int32_t bin_bounds(int32_t nb) { return nb < 1 ? 0 : (nb > 256 ? 255 : nb - 1); }
+
 template <bool LDS>
 __global__ void __launch_bounds__(kBinThreads) k_bin(const float* __restrict__ raw, int64_t n_vals,
                                                      int32_t F, const int32_t* __restrict__ n_bins,
@@ -2330,20 +2333,20 @@ __global__ void __launch_bounds__(kBinThreads) k_bin(const float* __restrict__ r
                                                      const int32_t* __restrict__ bin_feature,
                                                      int32_t total_bins, const float* __restrict__ upper,
                                                      uint8_t* __restrict__ out, WsCtrl* __restrict__ ctrl) {
-  extern __shared__ float s_bin[];  // LDS: [total_bins] bounds, then [F] offsets, [F] bound counts
+  // LDS: the bounds, feature f's from bin_offset[f] + f (the skew by f puts
+  // bound k of different features in different banks: with 64 bins per
+  // feature they would otherwise all share one bank), then one word per
+  // feature, its offset << 8 | its bound count
+  extern __shared__ float s_bin[];
   const float* tab = upper;
   const int32_t* offs = bin_offset;
-  int32_t* s_off = reinterpret_cast<int32_t*>(s_bin + total_bins);
-  int32_t* s_nb = s_off + F;
+  uint32_t* s_meta = reinterpret_cast<uint32_t*>(s_bin + total_bins + F);  // offset << 8 | bound count
   if constexpr (LDS) {
-    for (int32_t i = threadIdx.x; i < total_bins; i += blockDim.x) s_bin[i] = upper[i];
-    for (int32_t f = threadIdx.x; f < F; f += blockDim.x) {
-      s_off[f] = bin_offset[f];
-      s_nb[f] = n_bins[f] - 1;
-    }
+    for (int32_t i = threadIdx.x; i < total_bins; i += blockDim.x) s_bin[i + bin_feature[i]] = upper[i];
+    for (int32_t f = threadIdx.x; f < F; f += blockDim.x)
+      s_meta[f] = ((uint32_t)(bin_offset[f] + f) << 8) | (uint32_t)bin_bounds(n_bins[f]);
     __syncthreads();
     tab = s_bin;
-    offs = s_off;
   }
   const int64_t G = int64_t(gridDim.x) * blockDim.x;
   int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -2388,8 +2391,15 @@ __global__ void __launch_bounds__(kBinThreads) k_bin(const float* __restrict__ r
     int32_t fe = f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int32_t o = offs[fe];
-      const int32_t nb = LDS ? s_nb[fe] : n_bins[fe] - 1;
+      int32_t o, nb;
+      if constexpr (LDS) {
+        const uint32_t mt = s_meta[fe];
+        o = (int32_t)(mt >> 8);
+        nb = (int32_t)(mt & 0xffu);
+      } else {
+        o = offs[fe];
+        nb = bin_bounds(n_bins[fe]);
+      }
       nan |= v[e] != v[e];
       w[e >> 2] |= bin_of(tab + o, nb, v[e]) << (8 * (e & 3));
       fe = fe + 1 == F ? 0 : fe + 1;
@@ -2619,7 +2629,7 @@ int gbdt_bin_features(const float* raw, int64_t n_rows, const gbdt_features* ft,
   const int64_t n_vals = n_rows * F;
   int64_t grid = (n_vals + 16 * kBinThreads - 1) / (16 * kBinThreads);
   if (grid > kBinGrid) grid = kBinGrid;
-  const size_t lds = sizeof(float) * size_t(ft->total_bins) + 2 * sizeof(int32_t) * size_t(F);
+  const size_t lds = sizeof(float) * size_t(ft->total_bins + F) + sizeof(uint32_t) * size_t(F);
   diag_begin(kDiagBin, s);
   if (lds <= kBinLdsBytes)
     hipLaunchKernelGGL(k_bin<true>, dim3((unsigned)grid), dim3(kBinThreads), lds, s, raw, n_vals, F, ft->n_bins,
