@@ -498,6 +498,8 @@ BIN_CASES = [
     # 25,600 bins: the bounds do not fit LDS and are read from global memory
     ("global_bounds", 3001, [256] * 100, 53),
     ("one_feature", 37, [255], 54),
+    # 60 x 256 bins: the largest bound table that still fits LDS (62 KiB)
+    ("lds_wide_table", 2001, [256] * 60, 57),
     ("one_row", 1, [9, 2, 200], 55),
 ]
 
@@ -511,6 +513,34 @@ def test_bin_features_matches_oracle(case):
     assert n_nan == 0
     ft = g.FeatureTable(nbins, DEV, pack_bits=False)
     out = torch.full((n, len(nbins)), 0xEE, dtype=torch.uint8, device=DEV)
+    ws = _ws(n, 1, 1)
+    g.gbdt_bin_features(to_dev(raw), ft, to_dev(upper), out, ws)
+    assert g.gbdt_read_error(ws) == 0
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_bin_features_extreme_bounds():
+    say("bin_features bounds spanning the float range, and close together")
+    # feature 0: bounds -3e38, 0, 3e38 (their span overflows); feature 1: two
+    # bounds one float32 step apart; feature 2: equal-width bounds
+    one_ulp = np.nextafter(np.float32(1.0), np.float32(2.0))
+    upper = np.array([-3e38, 0.0, 3e38, 0.0,
+                      1.0, one_ulp, 0.0,
+                      -1.0, -0.5, 0.0, 0.5, 1.0, 0.0], dtype=np.float32)
+    nbins = [4, 3, 6]
+    rng = np.random.default_rng(58)
+    n = 4000
+    raw = np.empty((n, 3), dtype=np.float32)
+    raw[:, 0] = rng.choice(np.array([-np.inf, -3.4e38, -3e38, -1.0, 0.0, 1.0, 3e38, 3.4e38, np.inf],
+                                    dtype=np.float32), size=n)
+    raw[:, 1] = rng.choice(np.array([0.5, 1.0, one_ulp, np.nextafter(one_ulp, np.float32(2.0)), 2.0],
+                                    dtype=np.float32), size=n)
+    raw[:, 2] = rng.uniform(-1.5, 1.5, size=n).astype(np.float32)
+    raw[::7, 2] = rng.choice(upper[7:12], size=raw[::7, 2].shape[0])
+    want, n_nan = oracle.bin_features(raw, nbins, upper)
+    assert n_nan == 0
+    ft = g.FeatureTable(nbins, DEV, pack_bits=False)
+    out = torch.zeros((n, 3), dtype=torch.uint8, device=DEV)
     ws = _ws(n, 1, 1)
     g.gbdt_bin_features(to_dev(raw), ft, to_dev(upper), out, ws)
     assert g.gbdt_read_error(ws) == 0
