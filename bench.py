@@ -69,11 +69,12 @@ def built_work(trees, n_features, total_bins, max_depth, min_split):
     return rows, nodes
 
 
-def profiled_traffic(workload_name):
-    """HBM bytes per k_hist launch from the committed rocprofv3 counter summary
-    of this workload, if it was taken on the current kernel source; else None."""
+def profiled_traffic(workload_name, kernel="k_hist"):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary of this workload, if it was taken on the current kernel source;
+    else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "k_hist_%s_counters.txt" % workload_name)
+    path = os.path.join(ROOT, "profiles", "%s_%s_counters.txt" % (kernel, workload_name))
     if not os.path.exists(path):
         return None
     fields = {}
@@ -260,7 +261,8 @@ def measure_binning(g, torch, R, with_cpu):
     res = {"config": {"workload": "binning_50Mx28_b64_equal_width", "rows": n, "features": F, "bins": B},
            "value": n * F / t, "unit": "values/s", "launches": R, "ms_per_launch_wall": wall * 1e3,
            "roofline": {"bound": "hbm", "achieved": alg / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": alg / t / 1e9 / HBM_PEAK_GBS, "traffic": None, "kernel": "k_bin",
+                        "frac": alg / t / 1e9 / HBM_PEAK_GBS,
+                        "traffic": profiled_traffic("binning_50Mx28_b64_equal_width", "k_bin"), "kernel": "k_bin",
                         "avg_launch_us": t * 1e6, "alg_bytes_per_launch": alg}}
     if with_cpu:
         import oracle
