@@ -2306,9 +2306,13 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
 // (four 16-byte loads, one 16-byte store), in a grid-stride loop; the
 // feature index advances incrementally, with no division per value.  The
 // bounds (and each feature's offset and bound count) are staged in LDS when
-// they fit (LDS = true), else read from global memory.  Each value's search
-// is binary lifting with a fixed 8 steps (at most 255 bounds), so the 16
-// searches of a thread are independent chains the compiler interleaves.
+// they fit (LDS = true), else read from global memory.  With the bounds in
+// LDS, each value first guesses its bin from the line through its feature's
+// first and last bound and keeps the guess when the two bounds around it
+// confirm it (one pair of lookups; exact, since only the comparisons
+// decide); otherwise, and always without LDS, it searches by binary lifting
+// with a fixed 8 steps (at most 255 bounds), written out per value so the
+// compiler interleaves the searches of a thread's 16 values.
 constexpr int kBinThreads = 256;
 constexpr int kBinGrid = 2048;
 constexpr size_t kBinLdsBytes = 64 * 1024;
@@ -2326,6 +2330,12 @@ __device__ __forceinline__ uint32_t bin_of(const float* __restrict__ t, int32_t 
 // bounds of a feature of nb bins (a feature table holds 1..256 bins)
 __device__ __forceinline__ int32_t bin_bounds(int32_t nb) { return nb < 1 ? 0 : (nb > 256 ? 255 : nb - 1); }
 
+// LDS words of k_bin: the skewed bounds, a word per feature, and (aligned
+// to 8 bytes) a (first bound, 1 / spacing) pair per feature.
+__host__ __device__ inline size_t bin_lds_words(int32_t tb, int32_t F) {
+  return ((size_t(tb) + 2 * size_t(F) + 1) & ~size_t(1)) + 2 * size_t(F);
+}
+
 template <bool LDS>
 __global__ void __launch_bounds__(kBinThreads) k_bin(const float* __restrict__ raw, int64_t n_vals,
                                                      int32_t F, const int32_t* __restrict__ n_bins,
@@ -2341,10 +2351,23 @@ __global__ void __launch_bounds__(kBinThreads) k_bin(const float* __restrict__ r
   const float* tab = upper;
   const int32_t* offs = bin_offset;
   uint32_t* s_meta = reinterpret_cast<uint32_t*>(s_bin + total_bins + F);  // offset << 8 | bound count
+  float2* s_gs = reinterpret_cast<float2*>(s_bin + ((size_t(total_bins) + 2 * size_t(F) + 1) & ~size_t(1)));
   if constexpr (LDS) {
     for (int32_t i = threadIdx.x; i < total_bins; i += blockDim.x) s_bin[i + bin_feature[i]] = upper[i];
-    for (int32_t f = threadIdx.x; f < F; f += blockDim.x)
-      s_meta[f] = ((uint32_t)(bin_offset[f] + f) << 8) | (uint32_t)bin_bounds(n_bins[f]);
+    for (int32_t f = threadIdx.x; f < F; f += blockDim.x) {
+      const int32_t nb = bin_bounds(n_bins[f]);
+      s_meta[f] = ((uint32_t)(bin_offset[f] + f) << 8) | (uint32_t)nb;
+      // the guess's line through the first and last bound (0 slope when the
+      // spacing is not a finite positive number)
+      const float u0 = nb > 0 ? upper[bin_offset[f]] : 0.0f;
+      const float u1 = nb > 0 ? upper[bin_offset[f] + nb - 1] : 0.0f;
+      float inv = 0.0f;
+      if (nb >= 2 && u1 > u0) {
+        inv = (float)(nb - 1) / (u1 - u0);
+        if (!(inv <= 3.0e38f)) inv = 0.0f;
+      }
+      s_gs[f] = make_float2(u0, inv);
+    }
     __syncthreads();
     tab = s_bin;
   }
@@ -2401,7 +2424,23 @@ __global__ void __launch_bounds__(kBinThreads) k_bin(const float* __restrict__ r
         nb = bin_bounds(n_bins[fe]);
       }
       nan |= v[e] != v[e];
-      w[e >> 2] |= bin_of(tab + o, nb, v[e]) << (8 * (e & 3));
+      uint32_t bin;
+      if constexpr (LDS) {
+        // guess from the line through the first and last bound (exact for
+        // equal-width bounds up to rounding), kept if the two bounds around it
+        // confirm it, else the full search
+        const float2 gs = s_gs[fe];
+        float t = (v[e] - gs.x) * gs.y;
+        t = fminf(fmaxf(t, 0.0f), (float)nb);
+        const int32_t gg = (int32_t)ceilf(t);
+        const float lo = tab[o + (gg > 0 ? gg - 1 : 0)];
+        const float hi = tab[o + (gg < nb ? gg : 0)];
+        const bool ok = (gg == 0 || lo < v[e]) && (gg == nb || !(hi < v[e]));
+        bin = ok ? (uint32_t)gg : bin_of(tab + o, nb, v[e]);
+      } else {
+        bin = bin_of(tab + o, nb, v[e]);
+      }
+      w[e >> 2] |= bin << (8 * (e & 3));
       fe = fe + 1 == F ? 0 : fe + 1;
     }
     if (full) {
@@ -2629,7 +2668,7 @@ int gbdt_bin_features(const float* raw, int64_t n_rows, const gbdt_features* ft,
   const int64_t n_vals = n_rows * F;
   int64_t grid = (n_vals + 16 * kBinThreads - 1) / (16 * kBinThreads);
   if (grid > kBinGrid) grid = kBinGrid;
-  const size_t lds = sizeof(float) * size_t(ft->total_bins + F) + sizeof(uint32_t) * size_t(F);
+  const size_t lds = sizeof(float) * bin_lds_words(ft->total_bins, F);
   diag_begin(kDiagBin, s);
   if (lds <= kBinLdsBytes)
     hipLaunchKernelGGL(k_bin<true>, dim3((unsigned)grid), dim3(kBinThreads), lds, s, raw, n_vals, F, ft->n_bins,
