@@ -22,8 +22,9 @@ def _ws(n, lst, tb):
 
 # ------------------------------------------------------------------ gradients --
 
+# (3,000,017 rows: several grid-stride steps of four rows per thread, ragged end)
 @pytest.mark.parametrize("n,seed,scale", [(1, 1, 1.0), (2, 2, 3.0), (4097, 3, 10.0), (100003, 4, 1e-3),
-                                          (1 << 20, 5, 100.0)])
+                                          (1 << 20, 5, 100.0), (3000017, 6, 2.0)])
 def test_gradients(n, seed, scale):
     say("gradients n=%d seed=%d" % (n, seed))
     rng = np.random.default_rng(seed)
