@@ -2314,7 +2314,7 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
 // with a fixed 8 steps (at most 255 bounds), written out per value so the
 // compiler interleaves the searches of a thread's 16 values.
 constexpr int kBinThreads = 256;
-constexpr int kBinGrid = 2048;
+constexpr int kBinGrid = 4096;
 constexpr size_t kBinLdsBytes = 64 * 1024;
 
 __device__ __forceinline__ uint32_t bin_of(const float* __restrict__ t, int32_t nb, float x) {
