@@ -13,15 +13,20 @@ depth 10, 100 trees, lambda 1 -- the covtype-shaped depth-10 configuration.
 Output: one JSON line on stdout (progress goes to stderr).
   value      histogram rows*features per second: rows*features of every
              directly built node (root and smaller children) divided by the
-             summed device time of the histogram kernel over the timed trees
-  roofline   the histogram kernel against the 8 TB/s HBM peak, algorithmic
-             bytes n_v*(F + 4 + 8) + total_bins*12 per built node
+             summed device time of the histogram build (k_hist and the
+             reduction of multi-tile partials, k_hist_reduce) over the timed
+             trees
+  roofline   the histogram build against the 8 TB/s HBM peak, algorithmic
+             bytes n_v*(F + 4 + 8) + total_bins*12 per built node; k_hist
+             alone is reported beside it
+  rooflines  the partition and the prediction update on the same trees
   trees_per_s / ms_per_step  whole boosting steps, host wall clock
   cpu_baseline  the CPU oracle (single thread) on a bounded sample of trees
-  also       the same figures (value, roofline, trees_per_s, per-kernel
+  also       the same figures (value, rooflines, trees_per_s, per-kernel
              device time) for further workloads, 10 trees each: by default
-             the 50,000,000 x 28 one (64 uniform bins, depth 12), the largest,
-             whose histogram build is bound by HBM rather than by latency
+             the 10,000,000 x 100 (Zipf-skewed 256 bins, depth 8) and the
+             50,000,000 x 28 (64 uniform bins, depth 12) ones, whose
+             histogram builds are bound by HBM rather than by latency
   binning    raw FP32 values to uint8 bins (the step before the path) at the
              50M x 28 x 64-bin shape: values/s, its HBM roofline and the
              oracle on a 200K-row sample
@@ -69,6 +74,45 @@ def built_work(trees, n_features, total_bins, max_depth, min_split):
     return rows, nodes
 
 
+DIAG_HIST_REDUCE = 5
+DIAG_FIND = 7
+DIAG_PARTITION = 10
+DIAG_UPDATE = 11
+
+
+def other_rooflines(trees, kt, n, max_depth):
+    """HBM rooflines of the partition, the prediction update and the split
+    search over the same timed trees, with the algorithmic bytes of each step
+    (per row of a splitting node: 4 B row index read + 1 B bin + 4 B index
+    written + 16 B of q moved; per row of the update: 4 B index + 16 B pred
+    read and written).  The partition runs at levels 0 .. max_depth - 2; the
+    update is two launches per tree (the tree compaction, then the row walk),
+    counted as one unit."""
+    part_rows = 0
+    for tr in trees:
+        for nd in tr:
+            if int(nd["depth"]) < max_depth - 1 and not (nd["flags"] & 1):
+                part_rows += int(nd["count"])
+    out = {}
+    K = len(trees)
+
+    def entry(kind, name, alg, units=None):
+        t, launches = kt.get(kind, (0.0, 0))
+        if launches == 0 or t <= 0.0:
+            return None
+        launches = units if units is not None else launches
+        a = alg / (t * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": a / HBM_PEAK_GBS, "traffic": None, "kernel": name, "launches": launches,
+                "avg_launch_us": 1000.0 * t / launches, "alg_bytes_per_launch": alg / launches,
+                "ms_per_tree": t / K}
+
+    out["partition"] = entry(DIAG_PARTITION, "k_partition", part_rows * 25)
+    # two launches per update (the tree compaction, then the row walk)
+    out["update"] = entry(DIAG_UPDATE, "k_compact_tree + k_update", K * n * 20, units=K)
+    return out
+
+
 def profiled_traffic(workload_name, kernel="k_hist"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary of this workload, if it was taken on the current kernel source;
@@ -95,6 +139,24 @@ def profiled_traffic(workload_name, kernel="k_hist"):
         return None
 
 
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo) and the CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"model": model, "cpus_available": avail, "threads_used": 1}
+
+
 def cpu_baseline(k, seconds_budget):
     """The oracle as it stands, single-threaded, on the first trees of the same workload."""
     import datagen
@@ -113,7 +175,7 @@ def cpu_baseline(k, seconds_budget):
         tr = r["nodes"][t][: r["n_nodes"][t]]
         cells += int(sum(int(nd["count"]) for nd in tr if int(nd["depth"]) < p.max_depth)) * F
     return dict(value=cells / r["hist_seconds"], unit="rows*features/s", cores=1, kind="oracle",
-                trees_per_s=n_trees / r["seconds"],
+                trees_per_s=n_trees / r["seconds"], host=host_cpu(),
                 sample="first %d of %d trees of the workload, every node's histogram built directly "
                        "(no subtraction), single thread" % (n_trees, wl["n_trees"]))
 
@@ -194,24 +256,33 @@ def measure(g, datagen, torch, k, K, W, diag):
         kinds, ms = kinds[: cnt.value], ms[: cnt.value]
         trees = [g.nodes_to_host(nodes_bufs[i], int(nn_bufs[i].item())) for i in range(K)]
         rows, nbuilt = built_work(trees, F, TB, params.max_depth, min_split)
-        hist_ms = float(ms[kinds == DIAG_HIST].sum())
-        launches = int((kinds == DIAG_HIST).sum())
+        kt = {kk: (float(ms[kinds == kk].sum()), int((kinds == kk).sum())) for kk in set(kinds.tolist())}
+        hist_ms, launches = kt.get(DIAG_HIST, (0.0, 0))
+        red_ms, red_launches = kt.get(DIAG_HIST_REDUCE, (0.0, 0))
+        build_ms = hist_ms + red_ms
         cells = rows * F
         alg_bytes = rows * (F + 4 + 8) + nbuilt * TB * 12
-        achieved = alg_bytes / (hist_ms * 1e-3) / 1e9
-        out["value"] = cells / (hist_ms * 1e-3)
+        achieved = alg_bytes / (build_ms * 1e-3) / 1e9
+        # the histogram build: k_hist plus the reduction of the partials of
+        # nodes covered by several tiles (part of every such node's histogram)
+        out["value"] = cells / (build_ms * 1e-3)
         out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(wl["name"]),
-                           "kernel": "k_hist", "launches": launches,
-                           "avg_launch_us": 1000.0 * hist_ms / max(launches, 1),
-                           "alg_bytes_per_launch": alg_bytes / max(launches, 1)}
+                           "kernel": "k_hist + k_hist_reduce", "launches": launches,
+                           "avg_launch_us": 1000.0 * build_ms / max(launches, 1),
+                           "alg_bytes_per_launch": alg_bytes / max(launches, 1),
+                           "k_hist_avg_us": 1000.0 * hist_ms / max(launches, 1),
+                           "k_hist_reduce_avg_us": 1000.0 * red_ms / max(red_launches, 1),
+                           "k_hist_reduce_launches": red_launches,
+                           "k_hist_only_frac": alg_bytes / (hist_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        out["rooflines"] = other_rooflines(trees, kt, n, params.max_depth)
         names = {1: "grad_max", 2: "grad_q", 3: "plan", 4: "hist", 5: "hist_reduce", 6: "subtract",
                  7: "find", 8: "tree_init", 9: "level", 10: "partition", 11: "update", 12: "pack"}
-        out["device_ms_per_tree"] = {names.get(int(kk), str(kk)): float(ms[kinds == kk].sum()) / K
-                                     for kk in sorted(set(kinds.tolist()))}
+        out["device_ms_per_tree"] = {names.get(int(kk), str(kk)): kt[kk][0] / K for kk in sorted(kt)}
         out["built_rows_per_tree"] = rows / K
-        log("hist: %d launches, %.3f ms total, %.1f GB/s algorithmic (%.1f%% of 8 TB/s)" % (
-            launches, hist_ms, achieved, 100 * achieved / HBM_PEAK_GBS))
+        log("histogram build: %d launches, %.3f ms total (k_hist %.3f + reduce %.3f), %.1f GB/s "
+            "algorithmic (%.1f%% of 8 TB/s)" % (launches, build_ms, hist_ms, red_ms, achieved,
+                                                100 * achieved / HBM_PEAK_GBS))
     del bst, ds
     torch.cuda.empty_cache()
     return out
@@ -272,7 +343,7 @@ def measure_binning(g, torch, R, with_cpu):
         oracle.bin_features(sample, [B] * F, upper_host)
         dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": m * F / dt, "unit": "values/s", "cores": 1, "kind": "oracle",
-                               "sample": "first %d rows, single thread" % m}
+                               "sample": "first %d rows, single thread" % m, "host": host_cpu()}
     del raw, out
     return res
 
@@ -283,9 +354,9 @@ def main():
     ap.add_argument("--steps", type=int, default=None, help="timed trees (default: the workload's tree count)")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--also", type=int, nargs="*", default=[5],
-                    help="further workloads reported under 'also' (default: the 50M x 28 one, "
-                         "the largest; 10 trees each)")
+    ap.add_argument("--also", type=int, nargs="*", default=[4, 5],
+                    help="further workloads reported under 'also' (default: the 10M x 100 and "
+                         "50M x 28 ones, whose histograms are bound by HBM; 10 trees each)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-diag", action="store_true", help="skip the per-kernel timing pass")
@@ -327,7 +398,8 @@ def main():
             out = res
         else:
             secondary.append({key: res[key] for key in ("config", "value", "unit", "steps", "ms_per_step",
-                                                        "trees_per_s", "roofline", "device_ms_per_tree")
+                                                        "trees_per_s", "roofline", "rooflines",
+                                                        "device_ms_per_tree")
                               if key in res})
     if secondary:
         out["also"] = secondary

@@ -430,10 +430,23 @@ class Booster:
         return nodes_out, n_nodes_out
 
     def train(self, n_trees: int, keep_trees=True):
-        for _ in range(n_trees):
-            t = self.grow_tree()
+        """Grows n_trees trees (enqueued without host synchronisation), then
+        reads the workspace error word once.  After a device-side failure the
+        library has left the failed tree and every later one with 0 nodes and
+        changed no prediction; those trees are dropped and GbdtError is raised,
+        so the booster keeps exactly the trees that completed and pred is the
+        prediction after the last of them."""
+        new = [self.grow_tree() for _ in range(n_trees)]
+        code = gbdt_read_error(self.ws)
+        if code != GBDT_OK:
+            done = 0
+            while done < len(new) and int(new[done][1].item()) > 0:
+                done += 1
             if keep_trees:
-                self.trees.append(t)
+                self.trees.extend(new[:done])
+            raise GbdtError(code, "gbdt_grow_tree (device-side check, tree %d of this call)" % done)
+        if keep_trees:
+            self.trees.extend(new)
         return self
 
     def check(self):

@@ -13,6 +13,16 @@ namespace gbdt {
 
 __device__ __forceinline__ void dev_error(int32_t* err, int code) { atomicCAS(err, 0, code); }
 
+// The tree driver hands its kernels the workspace error word as `guard`:
+// once a kernel of the tree has recorded an error, every later kernel of the
+// tree (and of later trees, until the word is read and cleared) does nothing,
+// so no tree is finished and no prediction changes after a failure.  The
+// per-call entry points pass nullptr.
+__device__ __forceinline__ bool failed(const int32_t* guard) {
+  return guard != nullptr &&
+         __hip_atomic_load(guard, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);

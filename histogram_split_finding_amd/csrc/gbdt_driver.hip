@@ -102,9 +102,16 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
                                                     PlanArgs pa, int32_t tile_rows,
                                                     int32_t max_tiles,
                                                     const int64_t* __restrict__ psum,
-                                                    int32_t nparts) {
+                                                    int32_t nparts,
+                                                    const int32_t* __restrict__ guard) {
   __shared__ PlanLds lds;
   __shared__ int64_t s_part[1024 / 64];
+  // after an error (e.g. a non-finite gradient) the tree is not started: it
+  // has no nodes, and the later kernels of the tree do nothing
+  if (failed(guard)) {
+    if (threadIdx.x == 0) *n_nodes_out = 0;
+    return;
+  }
   // the root's sum of q from the gradient kernels' per-block partial sums
   {
     int64_t v = 0;
@@ -177,9 +184,18 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t part_tile, int32_t part_max_tiles,
                                                 int32_t hist_tile_max,
                                                 int32_t hist_target, int32_t hist_min_rows,
-                                                int32_t hist_max_tiles_next) {
+                                                int32_t hist_max_tiles_next,
+                                                const int32_t* __restrict__ guard) {
   __shared__ PlanLds lds;
   __shared__ int32_t shm[6 * 17];
+  // after an error nothing of the level is written, and the partition that
+  // follows finds an empty plan (it reads no other sign of the failure: a
+  // partition tile that stopped early would stall its successors'
+  // look-back)
+  if (failed(guard)) {
+    if (threadIdx.x == 0) pa.ctrl->plan_total = 0;
+    return;
+  }
   for (int c = threadIdx.x; c < kPlanSizeBuckets; c += blockDim.x) lds.bucket[c] = 0;
   const int32_t first = tc->level_start[d];
   const int32_t cnt = tc->level_count[d];
@@ -492,6 +508,9 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
       return fail(GBDT_E_INTERNAL, "tile bound exceeds the workspace");
   }
 
+  // every kernel of the tree after the gradients stops once an error is
+  // recorded in the workspace (see failed())
+  const int32_t* guard = &pa.ctrl->err;
   // (the sum of q stays as per-block partial sums; k_tree_init adds them)
   double* gpart = reinterpret_cast<double*>(w + WL.gpart);
   rc = launch_gradients(pred, label, n, b->q, q32, &tc->scale, nullptr, gpart, pa.ctrl, s);
@@ -500,7 +519,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   hipLaunchKernelGGL(k_tree_init, dim3(1), dim3(1024), 0, s, nodes_out, b->splits, tc, b->lists, LL,
                      (int32_t)n, min_split, D, p->reg_lambda, n_nodes_dev, pa, h_rows[0],
                      (int32_t)h_tiles[0],
-                     reinterpret_cast<const int64_t*>(gpart + kGradBlocks), grad_blocks(n));
+                     reinterpret_cast<const int64_t*>(gpart + kGradBlocks), grad_blocks(n), guard);
   diag_end(s);
   {
     hipError_t e = hipGetLastError();
@@ -512,20 +531,21 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     const int64_t lvl_off = (int64_t(1) << d) - 1;
     const int32_t cap_lvl = int32_t(1) << d;
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
-    rc = launch_hist(src, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s, q32);
+    rc = launch_hist(src, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s, q32,
+                     true);
     if (rc) return rc;
     rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
-                            h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s);
+                            h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s, guard);
     if (rc) return rc;
     rc = launch_find(b->hist_g, b->hist_cnt, *ft, nodes_out, b->lists + LL.find + lvl_off,
                      &tc->n_find[d], cap_lvl, *p, &tc->scale, b->splits,
                      b->lists + LL.find_par + lvl_off, b->lists + LL.find_sib + lvl_off, pa.ctrl, s,
-                     reinterpret_cast<FindCand*>(w + WL.fcand));
+                     reinterpret_cast<FindCand*>(w + WL.fcand), guard);
     if (rc) return rc;
     diag_begin(kDiagLevel, s);
     hipLaunchKernelGGL(k_level, dim3(1), dim3(1024), 0, s, d, D, nodes_out, b->splits, tc, b->lists,
                        LL, min_split, p->reg_lambda, n_nodes_dev, pa, part_tile, (int32_t)p_tiles[d],
-                       tile_max, target, min_rows, (int32_t)h_tiles[d + 1]);
+                       tile_max, target, min_rows, (int32_t)h_tiles[d + 1], guard);
     diag_end(s);
     {
       hipError_t e = hipGetLastError();
@@ -539,8 +559,10 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
       src = dst;
     }
   }
-  rc = gbdt_update_predictions(pred, X, nodes_out, n_nodes_dev, int32_t(sz.max_nodes),
-                               p->learning_rate, b->ws, b->ws_bytes, stream);
+  // step 7 in driver mode: a tree that failed (or whose structure does not
+  // check out) gets n_nodes = 0 and leaves every prediction unchanged
+  rc = update_predictions(pred, X, nodes_out, n_nodes_dev, int32_t(sz.max_nodes), p->learning_rate,
+                          b->ws, b->ws_bytes, s, true);
   return rc;
 }
 

@@ -191,14 +191,16 @@ int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
 // driver_q32); otherwise int64 as the ABI declares.
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
-                WsCtrl* ctrl, hipStream_t s, bool q32 = false);
+                WsCtrl* ctrl, hipStream_t s, bool q32 = false, bool guard = false);
 int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_cap,
                        const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
-                       const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s);
+                       const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s,
+                       const int32_t* guard = nullptr);
 int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,
                 const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
                 const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
-                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s, FindCand* cand = nullptr);
+                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s, FindCand* cand = nullptr,
+                const int32_t* guard = nullptr);
 // qin32 / qout32: src.q / dst.q hold int32 elements (the tree driver's row
 // buffers); otherwise int64.
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
@@ -224,6 +226,15 @@ int launch_gradients(const double* pred, const float* label, int64_t n, void* q,
 // bits, i.e. n > 2^21 rows (|q| <= 2^30); it saves 4 of 8 bytes per row in
 // every histogram and every partition.
 inline bool driver_q32(int64_t n_rows) { return ceil_log2(n_rows) >= 22; }
+
+// Step 7 (gbdt_update_predictions).  driver: the tree driver's mode -- the
+// update does nothing once the workspace error word is set, and the tree's
+// node count (n_nodes, device) is set to 0 when the word is set or a node of
+// the tree fails the structure check, so no failed tree is exported and no
+// prediction moves.
+int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* nodes,
+                       int32_t* n_nodes, int32_t max_nodes, double learning_rate, void* ws,
+                       size_t ws_bytes, hipStream_t s, bool driver);
 
 // Per-kernel device timing (the backend's diagnostics): when enabled, every
 // launch of the library is bracketed by two hipEvents on its stream.

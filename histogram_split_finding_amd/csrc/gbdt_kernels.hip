@@ -532,8 +532,9 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ skip_bin,
     int32_t total_bins, int32_t lds_bins, const TileDesc* __restrict__ desc, int32_t bits,
     int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
-    uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl) {
+    uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl, const int32_t* __restrict__ guard) {
   static_assert(D == 1 || D == 2 || D == 4 || D == 8, "lanes per row");
+  if (failed(guard)) return;
   constexpr int RPW = 64 / D;               // rows per wave per batch
   constexpr int RPI = kHistThreads / D;     // rows per workgroup per batch
   constexpr int BATCH = D >= 4 ? D : 4;     // batches per step (1024 rows a step for D >= 4)
@@ -821,7 +822,9 @@ __global__ void __launch_bounds__(1024) k_hist_reduce(const int32_t* __restrict_
                                                      int32_t total_bins,
                                                      const uint64_t* __restrict__ partial,
                                                      int64_t* __restrict__ hist_g,
-                                                     uint32_t* __restrict__ hist_cnt) {
+                                                     uint32_t* __restrict__ hist_cnt,
+                                                     const int32_t* __restrict__ guard) {
+  if (failed(guard)) return;
   __shared__ int64_t sg[16][64];
   __shared__ uint64_t sc[16][64];
   const int32_t nm = clamp_len(multi, list_cap);
@@ -976,8 +979,10 @@ __global__ void __launch_bounds__(THREADS) k_find(
     const int32_t* __restrict__ list, const int32_t* __restrict__ list_len, int32_t list_cap,
     FindParams fp, const int32_t* __restrict__ scale, gbdt_split* __restrict__ splits,
     const int32_t* __restrict__ sub_par, const int32_t* __restrict__ sub_sib,
-    int32_t* __restrict__ err, int32_t n_chunks, FindCand* __restrict__ cand) {
+    int32_t* __restrict__ err, int32_t n_chunks, FindCand* __restrict__ cand,
+    const int32_t* __restrict__ guard) {
   constexpr int NW = THREADS / 64;
+  if (failed(guard)) return;
   __shared__ int64_t sw_g[NW];
   __shared__ int32_t sw_c[NW];
   __shared__ int32_t sw_f[NW];
@@ -1264,7 +1269,9 @@ __global__ void __launch_bounds__(64) k_find_merge(const int32_t* __restrict__ l
                                                    const int32_t* __restrict__ list_len,
                                                    int32_t list_cap, int32_t n_chunks,
                                                    const FindCand* __restrict__ cand,
-                                                   gbdt_split* __restrict__ splits) {
+                                                   gbdt_split* __restrict__ splits,
+                                                   const int32_t* __restrict__ guard) {
+  if (failed(guard)) return;
   const int32_t j = blockIdx.x;
   const int32_t raw = *list_len;
   const int32_t n = raw < 0 ? 0 : (raw > list_cap ? list_cap : raw);
@@ -1817,9 +1824,22 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
                                                        int32_t n_blocks, int32_t block_features,
                                                        int32_t block_stride, int32_t n_bit,
                                                        uint2* __restrict__ ctab,
-                                                       double* __restrict__ lval) {
+                                                       double* __restrict__ lval,
+                                                       int32_t* __restrict__ driver_nodes,
+                                                       WsCtrl* __restrict__ ctrl) {
   __shared__ int32_t s_leaves;
-  if (threadIdx.x == 0) s_leaves = 0;
+  __shared__ int32_t s_bad;
+  // driver mode (driver_nodes = the tree's node count): a tree whose kernels
+  // recorded an error is dropped -- node count 0, so the update that follows
+  // changes no prediction
+  if (driver_nodes != nullptr && failed(&ctrl->err)) {
+    if (threadIdx.x == 0) *driver_nodes = 0;
+    return;
+  }
+  if (threadIdx.x == 0) {
+    s_leaves = 0;
+    s_bad = 0;
+  }
   __syncthreads();
   int32_t nn = *n_nodes_dev;
   if (nn > max_nodes) nn = max_nodes;
@@ -1858,7 +1878,17 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
         e.y = loc | ((uint32_t)(nd.y & 0xffff) << 16);
       }
     }
+    if (e.x == kBadTag) s_bad = 1;
     ctab[v] = e;
+  }
+  // driver mode: a node that fails the check drops the whole tree before any
+  // row is updated (outside the driver the walk reports the rows that meet it)
+  if (driver_nodes != nullptr) {
+    __syncthreads();
+    if (threadIdx.x == 0 && s_bad) {
+      dev_error(&ctrl->err, GBDT_E_INTERNAL);
+      *driver_nodes = 0;
+    }
   }
 }
 
@@ -2192,7 +2222,7 @@ static auto hist_kernel(int D) -> decltype(&k_hist<8, B, Q>) {
 
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
-                WsCtrl* ctrl, hipStream_t s, bool q32) {
+                WsCtrl* ctrl, hipStream_t s, bool q32, bool guard) {
   const int64_t n_rows = src.X.n_rows > 0 ? src.X.n_rows : 1;
   const int32_t bits = pack_bits_for(n_rows);
   const bool has_bytes = src.X.n_features > src.X.n_bit_features;
@@ -2212,7 +2242,7 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
                      src.X.row_capacity, src.X.n_blocks, src.X.block_features, src.X.block_stride,
                      src.X.n_features, src.X.n_bit_features, src.X.bit_stride, src.X.col_feature,
                      src.q, ft.bin_offset, ft.skip_bin, ft.total_bins, ft.max_block_bins, desc, bits,
-                     hist_g, hist_cnt, hpart, ctrl);
+                     hist_g, hist_cnt, hpart, ctrl, guard ? &ctrl->err : nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist");
   return GBDT_OK;
@@ -2220,7 +2250,8 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
 
 int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_cap,
                        const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
-                       const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s) {
+                       const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s,
+                       const int32_t* guard) {
   const int32_t bits = pack_bits_for(n_rows > 0 ? n_rows : 1);
   // multi-tile nodes hold more than one tile of rows each, so there are at
   // most max_tiles / 2 of them; the grid covers up to kReduceNodeSlots of
@@ -2234,7 +2265,7 @@ int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_c
   if (grid > kReduceGrid) grid = kReduceGrid;
   diag_begin(kDiagHistReduce, s);
   hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)grid), dim3(1024), 0, s, list, multi, list_cap,
-                     prefix, (int32_t)max_tiles, bits, total_bins, hpart, hist_g, hist_cnt);
+                     prefix, (int32_t)max_tiles, bits, total_bins, hpart, hist_g, hist_cnt, guard);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist_reduce");
   return GBDT_OK;
@@ -2243,7 +2274,8 @@ int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_c
 int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,
                 const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
                 const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
-                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s, FindCand* cand) {
+                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s, FindCand* cand,
+                const int32_t* guard) {
   FindParams fp{p.reg_lambda, p.gamma, p.min_child_weight, p.min_samples_leaf};
   const int32_t nch = cand != nullptr ? find_chunks(ft.total_bins) : 1;
   diag_begin(kDiagFind, s);
@@ -2253,10 +2285,10 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
     hipLaunchKernelGGL((k_find<1024, 2>), dim3((unsigned)list_cap, (unsigned)nch), dim3(1024), 0, s, hist_g,
                        hist_cnt, ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
                        list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
-                       ctrl != nullptr ? &ctrl->err : nullptr, nch, cand);
+                       ctrl != nullptr ? &ctrl->err : nullptr, nch, cand, guard);
     GBDT_LAUNCH_CHECK("k_find");
     hipLaunchKernelGGL(k_find_merge, dim3((unsigned)list_cap), dim3(64), 0, s, list, list_len,
-                       list_cap, nch, (const FindCand*)cand, splits);
+                       list_cap, nch, (const FindCand*)cand, splits, guard);
     diag_end(s);
     GBDT_LAUNCH_CHECK("k_find_merge");
     return GBDT_OK;
@@ -2285,7 +2317,7 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
   hipLaunchKernelGGL(kern, dim3((unsigned)list_cap), dim3(threads), 0, s, hist_g, hist_cnt,
                      ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
                      list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
-                     ctrl != nullptr ? &ctrl->err : nullptr, 1, (FindCand*)nullptr);
+                     ctrl != nullptr ? &ctrl->err : nullptr, 1, (FindCand*)nullptr, guard);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_find");
   return GBDT_OK;
@@ -2774,6 +2806,76 @@ int launch_gradients(const double* pred, const float* label, int64_t n, void* q,
   return GBDT_OK;
 }
 
+int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* nodes,
+                       int32_t* n_nodes, int32_t max_nodes, double learning_rate, void* ws,
+                       size_t ws_bytes, hipStream_t s, bool driver) {
+  if (!pred || !X || !nodes || !n_nodes) return fail(GBDT_E_ARG, "null argument");
+  int rc = check_matrix(*X);
+  if (rc) return rc;
+  if (max_nodes < 1) return fail(GBDT_E_ARG, "max_nodes must be >= 1");
+  if (!std::isfinite(learning_rate)) return fail(GBDT_E_ARG, "learning_rate must be finite");
+  const int64_t n = X->n_rows;
+  if (n == 0) return GBDT_OK;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return fail(GBDT_E_ARG, "workspace is null or misaligned");
+  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(static_cast<char*>(ws));
+  const int64_t row_bytes = int64_t(X->n_blocks) * X->block_stride + X->bit_stride;
+  if (row_bytes > kUpdMaxRowBytes) return fail(GBDT_E_UNSUPPORTED, "rows wider than 256 bytes");
+  const WsLayout L = ws_layout(n, 1, 1);
+  const size_t tables = size_t(max_nodes) * sizeof(uint2) + size_t((max_nodes + 1) / 2) * sizeof(double);
+  if (ws_bytes < L.total || tables > L.total - L.hpart)
+    return fail(GBDT_E_ARG, "workspace too small for the tree tables");
+  uint2* ctab = reinterpret_cast<uint2*>(static_cast<char*>(ws) + L.hpart);
+  double* lval = reinterpret_cast<double*>(static_cast<char*>(ws) + L.hpart +
+                                           sizeof(uint2) * size_t(max_nodes));
+  diag_begin(kDiagUpdate, s);
+  hipLaunchKernelGGL(k_compact_tree, dim3(1), dim3(1024), 0, s, nodes, n_nodes, max_nodes,
+                     X->n_features, X->feature_col, X->n_blocks, X->block_features, X->block_stride,
+                     X->n_bit_features, ctab, lval, driver ? n_nodes : nullptr, ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_compact_tree");
+  // the node table goes to LDS (8 B per node); leaf values stay in global
+  // memory (read once per row, after the walk)
+  const size_t node_table = size_t(max_nodes) * sizeof(uint2);
+  const bool in_lds = node_table <= kUpdTreeLds;
+  const size_t lds = in_lds ? node_table : 0;
+  const int64_t ndw = row_bytes / 4;
+  const int rows = ndw <= 16 ? 2 : 1;
+  int64_t grid = (n + int64_t(kUpdThreads) * rows - 1) / (int64_t(kUpdThreads) * rows);
+  if (grid > 512) grid = 512;  // persistent: the tree is copied to LDS once per workgroup
+  diag_begin(kDiagUpdate, s);
+  const int32_t nd1 = X->n_blocks == 1 ? X->block_stride / 4 : 0;  // one byte block: wide loads
+  if (ndw <= 8 && nd1 > 0) {
+    auto go = [&](auto tag) {
+      launch_update<8, decltype(tag)::value>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X,
+                                             ctab, lval, n_nodes, max_nodes, learning_rate, ctrl);
+    };
+    switch (nd1) {
+      case 1: go(std::integral_constant<int, 1>()); break;
+      case 2: go(std::integral_constant<int, 2>()); break;
+      case 3: go(std::integral_constant<int, 3>()); break;
+      case 4: go(std::integral_constant<int, 4>()); break;
+      case 5: go(std::integral_constant<int, 5>()); break;
+      case 6: go(std::integral_constant<int, 6>()); break;
+      case 7: go(std::integral_constant<int, 7>()); break;
+      default: go(std::integral_constant<int, 8>()); break;
+    }
+  } else if (ndw <= 8)
+    launch_update<8>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
+                     max_nodes, learning_rate, ctrl);
+  else if (ndw <= 16)
+    launch_update<16>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
+                      max_nodes, learning_rate, ctrl);
+  else if (ndw <= 32)
+    launch_update<32>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
+                      max_nodes, learning_rate, ctrl);
+  else
+    launch_update<64>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
+                      max_nodes, learning_rate, ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_update");
+  return GBDT_OK;
+}
+
 }  // namespace gbdt
 
 extern "C" {
@@ -2902,72 +3004,9 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
 int gbdt_update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* nodes,
                             const int32_t* n_nodes, int32_t max_nodes, double learning_rate,
                             void* ws, size_t ws_bytes, void* stream) {
-  if (!pred || !X || !nodes || !n_nodes) return fail(GBDT_E_ARG, "null argument");
-  int rc = check_matrix(*X);
-  if (rc) return rc;
-  if (max_nodes < 1) return fail(GBDT_E_ARG, "max_nodes must be >= 1");
-  if (!std::isfinite(learning_rate)) return fail(GBDT_E_ARG, "learning_rate must be finite");
-  const int64_t n = X->n_rows;
-  if (n == 0) return GBDT_OK;
-  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return fail(GBDT_E_ARG, "workspace is null or misaligned");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(static_cast<char*>(ws));
-  const int64_t row_bytes = int64_t(X->n_blocks) * X->block_stride + X->bit_stride;
-  if (row_bytes > kUpdMaxRowBytes) return fail(GBDT_E_UNSUPPORTED, "rows wider than 256 bytes");
-  const WsLayout L = ws_layout(n, 1, 1);
-  const size_t tables = size_t(max_nodes) * sizeof(uint2) + size_t((max_nodes + 1) / 2) * sizeof(double);
-  if (ws_bytes < L.total || tables > L.total - L.hpart)
-    return fail(GBDT_E_ARG, "workspace too small for the tree tables");
-  uint2* ctab = reinterpret_cast<uint2*>(static_cast<char*>(ws) + L.hpart);
-  double* lval = reinterpret_cast<double*>(static_cast<char*>(ws) + L.hpart +
-                                           sizeof(uint2) * size_t(max_nodes));
-  diag_begin(kDiagUpdate, s);
-  hipLaunchKernelGGL(k_compact_tree, dim3(1), dim3(1024), 0, s, nodes, n_nodes, max_nodes,
-                     X->n_features, X->feature_col, X->n_blocks, X->block_features, X->block_stride,
-                     X->n_bit_features, ctab, lval);
-  diag_end(s);
-  GBDT_LAUNCH_CHECK("k_compact_tree");
-  // the node table goes to LDS (8 B per node); leaf values stay in global
-  // memory (read once per row, after the walk)
-  const size_t node_table = size_t(max_nodes) * sizeof(uint2);
-  const bool in_lds = node_table <= kUpdTreeLds;
-  const size_t lds = in_lds ? node_table : 0;
-  const int64_t ndw = row_bytes / 4;
-  const int rows = ndw <= 16 ? 2 : 1;
-  int64_t grid = (n + int64_t(kUpdThreads) * rows - 1) / (int64_t(kUpdThreads) * rows);
-  if (grid > 512) grid = 512;  // persistent: the tree is copied to LDS once per workgroup
-  diag_begin(kDiagUpdate, s);
-  const int32_t nd1 = X->n_blocks == 1 ? X->block_stride / 4 : 0;  // one byte block: wide loads
-  if (ndw <= 8 && nd1 > 0) {
-    auto go = [&](auto tag) {
-      launch_update<8, decltype(tag)::value>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X,
-                                             ctab, lval, n_nodes, max_nodes, learning_rate, ctrl);
-    };
-    switch (nd1) {
-      case 1: go(std::integral_constant<int, 1>()); break;
-      case 2: go(std::integral_constant<int, 2>()); break;
-      case 3: go(std::integral_constant<int, 3>()); break;
-      case 4: go(std::integral_constant<int, 4>()); break;
-      case 5: go(std::integral_constant<int, 5>()); break;
-      case 6: go(std::integral_constant<int, 6>()); break;
-      case 7: go(std::integral_constant<int, 7>()); break;
-      default: go(std::integral_constant<int, 8>()); break;
-    }
-  } else if (ndw <= 8)
-    launch_update<8>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
-                     max_nodes, learning_rate, ctrl);
-  else if (ndw <= 16)
-    launch_update<16>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
-                      max_nodes, learning_rate, ctrl);
-  else if (ndw <= 32)
-    launch_update<32>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
-                      max_nodes, learning_rate, ctrl);
-  else
-    launch_update<64>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval, n_nodes,
-                      max_nodes, learning_rate, ctrl);
-  diag_end(s);
-  GBDT_LAUNCH_CHECK("k_update");
-  return GBDT_OK;
+  return gbdt::update_predictions(pred, X, nodes, const_cast<int32_t*>(n_nodes), max_nodes,
+                                  learning_rate, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
+                                  false);
 }
 
 }  // extern "C"

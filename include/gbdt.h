@@ -447,6 +447,16 @@ int gbdt_grow_sizes(int64_t n_rows, int32_t total_bins, int32_t max_depth,
  * ([max_nodes], breadth-first; *n_nodes_dev gets the node count), and
  * pred updated with learning_rate times the leaf weights.  All levels are
  * enqueued without host synchronisation.
+ *
+ * Failure (Training Core section 5: a failed fit exports no model; section 8:
+ * backend errors leave no partial model): when a device-side check records an
+ * error in b->ws's error word (a non-finite gradient, a partition count that
+ * disagrees with its split, an internal bound), every later kernel of the
+ * tree does nothing, *n_nodes_dev is set to 0 and no prediction is changed;
+ * the same holds for every later call while the word stays set (it is
+ * sticky until gbdt_read_error clears it).  So after a batch of trees, one
+ * gbdt_read_error tells whether all of them completed, and the first tree
+ * with 0 nodes is the one that failed.
  */
 int gbdt_grow_tree(const gbdt_matrix* X /* host */, const gbdt_features* ft /* host */,
                    const float* label, double* pred, const gbdt_params* p /* host */,

@@ -1,0 +1,80 @@
+"""No partial model after a device-side failure.
+
+"Module Design: Training Core", section 5 (state machine: a failed fit does
+not export a model) and section 8 (acceptance: backend exceptions do not
+produce partial models).  A failure recorded in the workspace's error word
+stops every later kernel of the tree driver: the failed tree gets 0 nodes, no
+prediction changes, and Booster.train drops the tree and raises.  The
+failures here are forced from the host (a NaN label; an error word written
+before the tree), so every kernel still runs to its normal end.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import histogram_split_finding_amd as g
+import oracle
+from gpu_util import DEV, compare_tree, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(k):
+    bins, label, nb = datagen.make_workload(k)
+    wl = dict(datagen.WORKLOADS[k])
+    ds = g.Dataset(bins, label, nb, DEV)
+    bst = g.Booster(ds, g.make_params(**wl))
+    return bins, label, nb, wl, ds, bst
+
+
+@pytest.mark.parametrize("k", [1, 3])
+def test_nan_label_before_second_tree(k):
+    say("failure: NaN label before tree 2 of workload %d" % k)
+    bins, label, nb, wl, ds, bst = _setup(k)
+    p = oracle.make_params(**wl)
+    bst.train(1)
+    ref1 = oracle.train(bins, nb, label, p, 1)
+    pred1 = bst.pred.cpu().numpy().copy()
+    assert np.array_equal(pred1, ref1["pred"])
+    row = bins.shape[0] // 3
+    ds.label[row] = float("nan")
+    with pytest.raises(g.GbdtError) as ei:
+        bst.train(2)
+    assert ei.value.code == -3  # GBDT_E_RANGE: a non-finite gradient
+    assert len(bst.trees) == 1
+    compare_tree(bst.host_trees()[0], ref1["nodes"][0][: ref1["n_nodes"][0]])
+    assert np.array_equal(bst.pred.cpu().numpy(), ref1["pred"])
+    # the error word was read (and cleared) by train(); with the label restored
+    # training goes on from the prediction of the last completed tree
+    ds.label[row] = float(label[row])
+    bst.train(1)
+    bst.check()
+    ref2 = oracle.train(bins, nb, label, p, 2)
+    assert len(bst.trees) == 2
+    compare_tree(bst.host_trees()[1], ref2["nodes"][1][: ref2["n_nodes"][1]])
+    assert np.array_equal(bst.pred.cpu().numpy(), ref2["pred"])
+
+
+def test_error_recorded_before_the_tree():
+    """An error word already set (by an earlier call on the same workspace)
+    makes the tree a no-op: 0 nodes, predictions untouched, nothing kept."""
+    say("failure: error word set before the tree")
+    bins, label, nb, wl, ds, bst = _setup(2)
+    bst.train(1)
+    before = bst.pred.clone()
+    bst.ws[:4].view(torch.int32)[0] = -7  # GBDT_E_INTERNAL, as a device check would write it
+    nodes, nn = bst.grow_tree()
+    torch.cuda.synchronize()
+    assert int(nn.item()) == 0
+    assert torch.equal(bst.pred, before)
+    with pytest.raises(g.GbdtError) as ei:
+        bst.train(1)
+    assert ei.value.code == -7
+    assert len(bst.trees) == 1
+    assert torch.equal(bst.pred, before)
+    # cleared by the read: the next tree is the oracle's second tree
+    bst.train(1)
+    ref = oracle.train(bins, nb, label, oracle.make_params(**wl), 2)
+    compare_tree(bst.host_trees()[1], ref["nodes"][1][: ref["n_nodes"][1]])
+    assert np.array_equal(bst.pred.cpu().numpy(), ref["pred"])
