@@ -501,3 +501,136 @@ def test_binning_degenerate_and_bad_bounds():
     for bad in ([2.0, 1.0, 0.0], [1.0, 1.0, 0.0], [np.nan, 1.0, 0.0], [0.0, np.nan, 0.0]):
         out, rc = oracle.bin_features(raw, [3], np.array(bad, dtype=np.float32))
         assert out is None and rc == -1, bad
+
+
+def test_partition_order_hand_case():
+    """Stable partition (Training Core, section 3 routing and section 6 step 5;
+    "stable" as the pages' partition is described): rows with bin <= t go
+    left, and each side keeps the order in which the rows were given.  The
+    expected lists are worked out by hand below, for an input order that is
+    not sorted (so a partition that sorted its output, or reversed one side,
+    would fail) and for the ascending order the root starts from (each side
+    then stays ascending)."""
+    # row id:  0  1  2  3  4  5  6  7
+    col = [3, 0, 2, 1, 3, 0, 1, 2]
+    bins = np.array([[c, 7 - c] for c in col], dtype=np.uint8)
+    # given order 5, 0, 3, 2, 4, 1 -> bins of feature 0: 0, 3, 1, 2, 3, 0
+    left, right = oracle.partition(bins, [5, 0, 3, 2, 4, 1], 0, 1)
+    assert left.tolist() == [5, 3, 1]
+    assert right.tolist() == [0, 2, 4]
+    # ascending ids, t = 1: left = ids with bin <= 1, right = the rest, both ascending
+    left, right = oracle.partition(bins, list(range(8)), 0, 1)
+    assert left.tolist() == [1, 3, 5, 6]
+    assert right.tolist() == [0, 2, 4, 7]
+    # feature 1 (bins 7 - col): t = 5 sends bins <= 5, i.e. col >= 2, left
+    left, right = oracle.partition(bins, list(range(8)), 1, 5)
+    assert left.tolist() == [0, 2, 4, 7]
+    assert right.tolist() == [1, 3, 5, 6]
+    # t at the top bin: everything left, nothing right; order unchanged
+    left, right = oracle.partition(bins, [7, 6, 5], 0, 255)
+    assert left.tolist() == [7, 6, 5] and right.tolist() == []
+
+
+def test_partition_order_in_training_is_ascending():
+    """Inside train(), every leaf's row list is a stable partition of the
+    ascending root, so the rows of each leaf come out ascending.  The oracle
+    reports the leaf of every row; rebuilding the leaves' row lists by
+    repeated stable partition with the tree's own splits (feature, threshold
+    from the node array) must give each leaf exactly those rows, in
+    ascending order."""
+    bins, label, nb = datagen.make_random(500, [9, 4, 16, 2], seed=77)
+    p = oracle.make_params(max_depth=4)
+    r = oracle.train(bins, nb, label, p, 1, dump_tree=0, dump_hist=False)
+    tree = r["nodes"][0][: r["n_nodes"][0]]
+    lists = {0: list(range(bins.shape[0]))}
+    for v in range(len(tree)):
+        nd = tree[v]
+        if nd["flags"] & oracle.LEAF:
+            continue
+        left, right = oracle.partition(bins, lists[v], int(nd["feature"]), int(nd["threshold_bin"]))
+        assert left.tolist() == sorted(left.tolist()) and right.tolist() == sorted(right.tolist())
+        lists[int(nd["left"])], lists[int(nd["right"])] = left.tolist(), right.tolist()
+    leaf_of = r["dump_leaf_of_row"]
+    for v in range(len(tree)):
+        if tree[v]["flags"] & oracle.LEAF:
+            assert lists[v] == np.nonzero(leaf_of == v)[0].tolist()
+
+
+def _oracle_tree(nodes):
+    """Oracle node array from (feature, threshold_bin, left, right, leaf_value) tuples
+    (a leaf has left = -1)."""
+    arr = np.zeros(len(nodes), dtype=oracle.NODE_DTYPE)
+    for v, (f, t, l, r, w) in enumerate(nodes):
+        arr[v]["feature"], arr[v]["threshold_bin"], arr[v]["left"], arr[v]["right"] = f, t, l, r
+        arr[v]["leaf_value"] = w
+        arr[v]["flags"] = oracle.LEAF if l < 0 else 0
+    return arr
+
+
+def test_predict_hand_ensemble():
+    """Forward pass of "Gradient boosted trees (spec model)": routing bin <= t to
+    the left, initial prediction plus learning rate times each tree's output.
+    Worked by hand: base 0.25, eta 0.5; tree 1 splits feature 0 at bin 0 into
+    leaves 1.0 | 2.0; tree 2 splits feature 1 at bin 1 into leaves -1.0 | 3.0;
+    tree 3 is a single leaf 0.5.  All values are dyadic, so every partial sum
+    is exact."""
+    t1 = _oracle_tree([(0, 0, 1, 2, 0.0), (-1, -1, -1, -1, 1.0), (-1, -1, -1, -1, 2.0)])
+    t2 = _oracle_tree([(1, 1, 1, 2, 0.0), (-1, -1, -1, -1, -1.0), (-1, -1, -1, -1, 3.0)])
+    t3 = _oracle_tree([(-1, -1, -1, -1, 0.5), (-1, -1, -1, -1, 0.0), (-1, -1, -1, -1, 0.0)])
+    trees = np.stack([t1, t2, t3])
+    bins = np.array([[0, 0], [0, 2], [1, 1], [1, 3], [3, 0]], dtype=np.uint8)
+    out = oracle.predict(bins, trees, [3, 3, 1], base_score=0.25, learning_rate=0.5)
+    # row: base + 0.5 * (tree1 + tree2 + tree3)
+    want = [0.25 + 0.5 * (1.0 - 1.0 + 0.5), 0.25 + 0.5 * (1.0 + 3.0 + 0.5),
+            0.25 + 0.5 * (2.0 - 1.0 + 0.5), 0.25 + 0.5 * (2.0 + 3.0 + 0.5),
+            0.25 + 0.5 * (2.0 - 1.0 + 0.5)]
+    assert out.tolist() == want
+    # no trees: the initial prediction
+    assert oracle.predict(bins, trees[:0], [], base_score=0.25).tolist() == [0.25] * 5
+
+
+def test_predict_hand_tree_d(golden_dir):
+    """The hand-derived tree of example D predicts its own hand-derived values."""
+    with open(os.path.join(golden_dir, "example_d.json")) as fh:
+        gd = json.load(fh)
+    nodes = []
+    for e in gd["expected"]["nodes"]:
+        w = float(_frac(e["leaf_value_exact"])) if e["leaf"] else 0.0
+        if e.get("leaf_value_negative_zero"):
+            w = -0.0
+        nodes.append((e["feature"], e["threshold_bin"], e["left"], e["right"], w))
+    tree = _oracle_tree(nodes)
+    bins = np.array(gd["inputs"]["bins"], dtype=np.uint8)
+    out = oracle.predict(bins, tree, [len(nodes)], base_score=0.0, learning_rate=1.0)
+    assert out.tolist() == [float(_frac(p)) for p in gd["expected"]["pred_exact"]]
+    for i in gd["expected"]["pred_positive_zero_rows"]:
+        assert math.copysign(1.0, out[i]) > 0
+
+
+@pytest.mark.parametrize("k", [1, 3])
+def test_predict_equals_training_predictions(k):
+    """Two independent routes to the same numbers: training adds each leaf's
+    eta*w to the rows its partitioned row list holds; the forward pass routes
+    every row through the trees.  They must agree bit for bit, tree by tree."""
+    bins, label, nb = datagen.make_workload(k)
+    wl = dict(datagen.WORKLOADS[k])
+    p = oracle.make_params(**wl)
+    T = 3
+    r = oracle.train(bins, nb, label, p, T, keep_pred_per_tree=True)
+    for t in range(1, T + 1):
+        out = oracle.predict(bins, r["nodes"][:t], r["n_nodes"][:t], 0.0, p.learning_rate)
+        assert np.array_equal(out, r["pred_per_tree"][t - 1])
+
+
+def test_predict_rejects_bad_trees():
+    t = _oracle_tree([(0, 0, 1, 2, 0.0), (-1, -1, -1, -1, 1.0), (-1, -1, -1, -1, 2.0)])
+    bins = np.array([[0], [1]], dtype=np.uint8)
+    with pytest.raises(ValueError):
+        oracle.predict(bins, t, [2])          # row 1 goes to a child past the node count
+    bad = t.copy()
+    bad[0]["feature"] = 5                     # no such feature
+    with pytest.raises(ValueError):
+        oracle.predict(bins, bad, [3])
+    loop = _oracle_tree([(0, 0, 0, 0, 0.0)])  # a node that is its own child
+    with pytest.raises(ValueError):
+        oracle.predict(bins, loop, [1])
