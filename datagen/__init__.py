@@ -119,6 +119,13 @@ def make_workload(k: int, n_rows: int | None = None, row_start: int = 0):
     return bins, label, workload_nbins(k)
 
 
+def make_heldout(k: int, n_rows: int):
+    """n_rows held-out rows of workload k: rows n .. n + n_rows - 1 of the same
+    recipe, past the training rows (bins, label, n_bins)."""
+    n_full, _ = workload_shape(k)
+    return make_workload(k, n_rows, row_start=n_full)
+
+
 def make_random(n: int, n_bins, seed: int, bin_kind: int = 0, label_kind: int = 0):
     """Generic test workload: uniform (or skewed) bins, N(0,1) / dyadic / additive labels."""
     nb = np.ascontiguousarray(np.asarray(n_bins, dtype=np.int32))

@@ -92,12 +92,13 @@ int dg_config_nbins(int k, int32_t* n_bins) {
 
 /*
  * Rows [r0, r1) of workload k.  bins is [r1-r0][F] row-major, label [r1-r0].
- * Row i of any range equals row i of the full workload.
+ * Row i of any range equals row i of the full workload.  Rows from n on are
+ * held-out rows drawn by the same recipe (counters past the training rows).
  */
 int dg_config_rows(int k, int64_t r0, int64_t r1, uint8_t* bins, float* label) {
   int64_t n; int32_t F;
   if (dg_config_shape(k, &n, &F)) return -1;
-  if (r0 < 0 || r1 > n || r0 > r1) return -2;
+  if (r0 < 0 || r0 > r1 || r1 > ((int64_t)1 << 36)) return -2;
   const uint64_t seed = 1000 + (uint64_t)k;
 
   /* workload 2: the hidden depth-4 tree (15 internal nodes, BFS order) */

@@ -84,6 +84,9 @@ def _load():
     lib.orc_train.restype = ctypes.c_int
     lib.orc_train.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp, ctypes.POINTER(OrcParams),
                               ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp]
+    lib.orc_predict.restype = ctypes.c_int
+    lib.orc_predict.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32, vp, ctypes.c_int32,
+                                vp, ctypes.c_double, ctypes.c_double, vp]
     lib.orc_bin_features.restype = ctypes.c_int64
     lib.orc_bin_features.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp, vp]
     _lib = lib
@@ -197,6 +200,24 @@ def bin_features(raw, n_bins, upper):
     if rc < 0:
         return None, rc
     return out, rc
+
+
+def predict(bins, trees, n_nodes, base_score=0.0, learning_rate=0.3):
+    """Ensemble forward pass (orc_predict): base + eta*w_1 + eta*w_2 + ... added
+    tree by tree.  trees: [T][stride] NODE_DTYPE (oracle node arrays, e.g.
+    train()["nodes"]); n_nodes: [T]."""
+    bins = np.ascontiguousarray(bins, dtype=np.uint8)
+    n, F = bins.shape
+    trees = np.ascontiguousarray(trees, dtype=NODE_DTYPE)
+    if trees.ndim == 1:
+        trees = trees[None, :]
+    n_nodes = np.ascontiguousarray(n_nodes, dtype=np.int32)
+    out = np.empty(n, dtype=np.float64)
+    rc = _load().orc_predict(n, F, _p(bins), trees.shape[0], _p(trees), trees.shape[1], _p(n_nodes),
+                             float(base_score), float(learning_rate), _p(out))
+    if rc:
+        raise ValueError("orc_predict failed (%d)" % rc)
+    return out
 
 
 def max_nodes(max_depth: int) -> int:

@@ -522,3 +522,48 @@ int64_t orc_bin_features(int64_t n_rows, int32_t F, const float* raw, const int3
   }
   return n_nan;
 }
+
+/*
+ * Ensemble forward pass: "Gradient boosted trees (spec model)", section
+ * Forward pass.  One tree is traversed from its root: at a split node the
+ * row goes to the left child when its bin of the node's feature is <= the
+ * node's threshold bin, else to the right child (the same routing as the
+ * Training Core page's Tree Model section), until a leaf, whose value is the
+ * tree's output.  The ensemble adds the learning rate times each tree's
+ * output to the initial prediction.  Reading (the spec names the sum, not
+ * its rounding): the trees are added one at a time in their order,
+ * out = ((base + eta*w_1) + eta*w_2) + ..., one IEEE rounding per product and
+ * per sum -- the sequence that step 7 of the Tree Growth section applies
+ * after each tree -- so the prediction of a training row equals its
+ * prediction at the end of training bit for bit.
+ *
+ * trees: n_trees node arrays of tree_stride nodes each (tree t at
+ * nodes + t * tree_stride) with n_nodes[t] nodes.  Returns ORC_OK, or
+ * ORC_E_ARG when a visited node's children or feature are out of range or a
+ * walk takes more steps than the tree has nodes (out is then incomplete).
+ */
+int orc_predict(int64_t n, int32_t F, const uint8_t* bins, int32_t n_trees, const orc_node* nodes,
+                int32_t tree_stride, const int32_t* n_nodes, double base, double eta, double* out) {
+  if (n < 0 || F < 1 || n_trees < 0 || tree_stride < 1 || (n > 0 && (!bins || !out))) return ORC_E_ARG;
+  for (int64_t i = 0; i < n; ++i) out[i] = base;
+  for (int32_t t = 0; t < n_trees; ++t) {
+    const orc_node* tree = nodes + (size_t)t * (size_t)tree_stride;
+    const int32_t nn = n_nodes[t];
+    if (nn < 1 || nn > tree_stride) return ORC_E_ARG;
+    for (int64_t i = 0; i < n; ++i) {
+      int32_t v = 0;
+      int32_t steps = 0;
+      while (!(tree[v].flags & ORC_LEAF)) {
+        const int32_t f = tree[v].feature;
+        if (f < 0 || f >= F || ++steps > nn) return ORC_E_ARG;
+        const int32_t next = ((int32_t)bins[i * (int64_t)F + f] <= tree[v].threshold_bin) ? tree[v].left
+                                                                                          : tree[v].right;
+        if (next < 0 || next >= nn) return ORC_E_ARG;
+        v = next;
+      }
+      const double term = eta * tree[v].leaf_value;
+      out[i] = out[i] + term;
+    }
+  }
+  return ORC_OK;
+}
