@@ -120,6 +120,9 @@ def load():
         "gbdt_diag_enable": (ctypes.c_int, [i32]),
         "gbdt_diag_disable": (ctypes.c_int, []),
         "gbdt_diag_read": (ctypes.c_int, [i32, vp, vp, vp]),
+        "gbdt_predict_workspace_bytes": (ctypes.c_size_t, [i32, i32]),
+        "gbdt_predict": (ctypes.c_int, [P(Matrix), vp, vp, i32, i32, ctypes.c_double, ctypes.c_double,
+                                        vp, vp, ctypes.c_size_t, vp]),
         "gbdt_grow_sizes": (ctypes.c_int, [i64, i32, i32, P(GrowSizes)]),
         "gbdt_grow_tree": (ctypes.c_int, [P(Matrix), P(Features), vp, vp, P(Params), vp, vp,
                                           P(GrowBuffers), vp]),
@@ -364,6 +367,20 @@ def gbdt_update_predictions(pred, X: Matrix, nodes, n_nodes, max_nodes, learning
     _check(rc, "gbdt_update_predictions")
 
 
+def gbdt_predict_workspace_bytes(n_trees: int, tree_stride: int) -> int:
+    return int(load().gbdt_predict_workspace_bytes(n_trees, tree_stride))
+
+
+def gbdt_predict(X: Matrix, trees, n_nodes, n_trees, tree_stride, base_score, learning_rate, out, ws,
+                 stream=None):
+    """trees: device bytes of n_trees * tree_stride nodes; n_nodes: int32 [n_trees];
+    out: float64 [n_rows]."""
+    rc = load().gbdt_predict(ctypes.byref(X), _ptr(trees), _ptr(n_nodes), int(n_trees), int(tree_stride),
+                             float(base_score), float(learning_rate), _ptr(out), _ptr(ws), ws.numel(),
+                             _stream(stream))
+    _check(rc, "gbdt_predict")
+
+
 # ------------------------------------------------------------ training run --
 
 class Dataset:
@@ -451,6 +468,28 @@ class Booster:
 
     def check(self):
         _check(gbdt_read_error(self.ws), "device-side check")
+
+    def predict(self, X: "RowBuffer", base_score=0.0, trees=None):
+        """Ensemble prediction (gbdt_predict) of the rows of X -- a RowBuffer in
+        the layout of this booster's dataset, e.g. Dataset(...).X of held-out
+        rows -- over the kept trees (or `trees`, a list of (nodes, n_nodes)
+        pairs as grow_tree returns them).  Returns a float64 device tensor."""
+        import torch
+        trees = self.trees if trees is None else trees
+        dev = self.pred.device
+        stride = int(self.sizes.max_nodes)
+        if trees:
+            nodes = torch.cat([t[0] for t in trees])
+            counts = torch.cat([t[1] for t in trees])
+        else:
+            nodes = torch.zeros(NODE_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+            counts = torch.zeros(1, dtype=torch.int32, device=dev)
+        out = torch.empty(X.n_rows, dtype=torch.float64, device=dev)
+        ws = new_workspace(max(gbdt_predict_workspace_bytes(len(trees), stride), 256), dev)
+        gbdt_predict(X.matrix(), nodes, counts, len(trees), stride, base_score,
+                     self.params.learning_rate, out, ws)
+        _check(gbdt_read_error(ws), "gbdt_predict (device-side check)")
+        return out
 
     def host_trees(self):
         """Node arrays of the kept trees as numpy structured arrays (synchronises)."""

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgbdt_hip.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["gbdt_kernels.hip", "gbdt_driver.hip"]
+SOURCES = ["gbdt_kernels.hip", "gbdt_driver.hip", "gbdt_predict.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

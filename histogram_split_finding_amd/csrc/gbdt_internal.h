@@ -185,6 +185,7 @@ __host__ __device__ inline int32_t hist_tile_rows_for(int32_t rows, int32_t tile
 // Argument checks and launches shared by the per-call entry points and the
 // tree driver (the driver's level kernel writes the tile plans itself).
 bool same_layout(const gbdt_matrix& a, const gbdt_matrix& b);
+int check_matrix(const gbdt_matrix& X);
 int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft);
 int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
 // q32: src.q holds int32 elements (the tree driver's row buffers, see
@@ -240,7 +241,7 @@ int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* node
 // launch of the library is bracketed by two hipEvents on its stream.
 enum DiagKind {
   kDiagGradMax = 1, kDiagGradQ, kDiagPlan, kDiagHist, kDiagHistReduce, kDiagSubtract, kDiagFind,
-  kDiagTreeInit, kDiagLevel, kDiagPartition, kDiagUpdate, kDiagPack, kDiagBin
+  kDiagTreeInit, kDiagLevel, kDiagPartition, kDiagUpdate, kDiagPack, kDiagBin, kDiagPredict
 };
 void diag_begin(int kind, hipStream_t s);
 void diag_end(hipStream_t s);

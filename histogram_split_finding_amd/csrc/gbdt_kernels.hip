@@ -2141,7 +2141,7 @@ static int check_ws(void* ws, size_t ws_bytes, const WsLayout& L) {
   return GBDT_OK;
 }
 
-static int check_matrix(const gbdt_matrix& X) {
+int check_matrix(const gbdt_matrix& X) {
   if (X.bins == nullptr) return fail(GBDT_E_ARG, "matrix bins pointer is null");
   if (X.n_rows < 0 || X.n_rows > 0x7fffffffLL) return fail(GBDT_E_ARG, "n_rows out of range");
   if (X.row_capacity < X.n_rows) return fail(GBDT_E_SHAPE, "row_capacity < n_rows");

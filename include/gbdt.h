@@ -294,7 +294,8 @@ int gbdt_bin_features(const float* raw, int64_t n_rows, const gbdt_features* ft 
  * launch into host arrays and clears the record.  Kinds: 1 gradient max,
  * 2 gradient grid, 3 tile planner, 4 histogram, 5 histogram partial reduce,
  * 6 subtraction, 7 split search, 8 tree init, 9 level bookkeeping,
- * 10 partition, 11 prediction update, 12 packing, 13 binning.  One process-wide record;
+ * 10 partition, 11 prediction update, 12 packing, 13 binning, 14 ensemble
+ * prediction.  One process-wide record;
  * not for concurrent use from several threads.
  */
 int gbdt_diag_enable(int32_t capacity);
@@ -405,6 +406,33 @@ int gbdt_partition_rows(const gbdt_rows* src /* host */, const gbdt_rows* dst /*
 int gbdt_update_predictions(double* pred, const gbdt_matrix* X /* host */, const gbdt_node* nodes,
                             const int32_t* n_nodes, int32_t max_nodes, double learning_rate,
                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Ensemble forward pass ("Gradient boosted trees (spec model)", Forward pass:
+ * each tree traversed from its root, a row going left when its bin of the
+ * node's feature is <= threshold_bin; the initial prediction plus the
+ * learning rate times each tree's output):
+ *   out[i] = ((base_score + learning_rate * w_1(i)) + learning_rate * w_2(i)) + ...
+ * with the trees added one at a time in order, one rounding per product and
+ * per sum -- the sequence the training's prediction update applies, so rows
+ * of the training matrix get their training-time predictions bit for bit.
+ *
+ * X: the rows (device, any layout the other calls accept; rows in X's
+ * order).  trees: device, n_trees node arrays of tree_stride gbdt_node each
+ * (tree t at trees + t * tree_stride), as gbdt_grow_tree writes them:
+ * breadth-first, right = left + 1 after the node, each child one level
+ * deeper than its parent (root depth 0, at most GBDT_MAX_DEPTH).  n_nodes:
+ * device int32[n_trees], the node count of each tree.  out: device
+ * double[n_rows], written (not read).  ws: at least
+ * gbdt_predict_workspace_bytes(n_trees, tree_stride) bytes, 256-byte aligned,
+ * error word zero.  A tree that fails those structure checks sets GBDT_E_ARG
+ * in the error word, and then out is not written at all (nor when the word
+ * was already set).  n_trees = 0 writes base_score to every row.
+ */
+size_t gbdt_predict_workspace_bytes(int32_t n_trees, int32_t tree_stride);
+int gbdt_predict(const gbdt_matrix* X /* host */, const gbdt_node* trees, const int32_t* n_nodes,
+                 int32_t n_trees, int32_t tree_stride, double base_score, double learning_rate,
+                 double* out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------ level-wise driver -- */
 

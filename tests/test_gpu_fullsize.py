@@ -2,13 +2,21 @@
 bench times (Dataset + Booster + gbdt_grow_tree).
 
 Workloads 1-3: every node of the first trees and every prediction against
-the oracle, bit for bit.  Workloads 4-5 (10M x 100, 50M x 28): the oracle
-computes sampled outputs one by one -- the gradient grid of the last tree,
-the root histogram and split, histograms and splits of sampled deeper
-nodes -- and properties that hold at any size are checked on everything:
-per-node row counts and gradient sums by routing every row through the GPU
-tree, leaf weights from those sums, and the prediction update.
+the oracle, run here, bit for bit.  Workloads 4-5 (10M x 100, 50M x 28):
+the first two trees node by node, every histogram the GPU builds or derives,
+the fixed-point gradients and every prediction against the oracle's outputs
+stored by tests/golden/make_fullsize_golden.py (the oracle takes minutes
+per tree there); and a second test in which the oracle computes sampled
+outputs one by one while properties that hold at any size are checked on
+everything: per-node row counts and gradient sums by routing every row
+through the GPU tree, leaf weights from those sums, and the prediction
+update.
 """
+import gzip
+import hashlib
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,7 +24,9 @@ import torch
 import datagen
 import histogram_split_finding_amd as g
 import oracle
-from gpu_util import DEV, compare_tree, hist_from_device, min_split_count, say
+from gpu_util import DEV, compare_tree, hist_from_device, min_split_count, orc_has_hist, say
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 pytestmark = pytest.mark.gpu
 
@@ -174,3 +184,62 @@ def test_binning_full_size_sampled():
     b = out[:1_000_000, 5].to(torch.int32)
     order = torch.argsort(col)
     assert bool((b[order][1:] >= b[order][:-1]).all().item())
+
+
+def _sha(*arrays) -> str:
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("k", [4, 5])
+def test_large_workloads_whole_trees_match_oracle(k):
+    """The first two trees of the 10M x 100 and 50M x 28 workloads against the
+    oracle's stored outputs: every node (structure and fixed-point sums exact,
+    leaf values and gains bit for bit), the gradients of each tree, the
+    histogram of every node the GPU builds directly or derives by
+    subtraction, and every prediction after each tree."""
+    with gzip.open(os.path.join(GOLDEN, "fullsize_w%d.json.gz" % k), "rt") as fh:
+        gold = json.load(fh)
+    say("full-size workload %d: %d trees against the oracle's stored outputs" % (k, len(gold["trees"])))
+    bins, label, nb = datagen.make_workload(k)
+    assert datagen.fingerprint(bins) == gold["bins_fnv1a64"]
+    assert datagen.fingerprint(label) == gold["label_fnv1a64"]
+    wl = dict(datagen.WORKLOADS[k])
+    ds = g.Dataset(bins, label, nb, DEV)
+    bst = g.Booster(ds, g.make_params(**wl))
+    p = oracle.make_params(**wl)
+    ms = min_split_count(p)
+    n, TB, D = bins.shape[0], ds.ft.total_bins, int(p.max_depth)
+    del bins, label
+    q32 = oracle.ceil_log2(n) >= 22
+    rows = gold["sample_rows"]
+    for t, gt in enumerate(gold["trees"]):
+        nodes, nn = bst.grow_tree()
+        torch.cuda.synchronize()
+        tree = g.nodes_to_host(nodes, int(nn.item()))
+        assert len(tree) == gt["n_nodes"], (t, len(tree), gt["n_nodes"])
+        for f in ("feature", "threshold_bin", "left", "right", "flags", "depth", "count"):
+            want = np.asarray(gt[f], dtype=np.int64)
+            bad = np.nonzero(tree[f].astype(np.int64) != want)[0]
+            assert bad.size == 0, (t, f, bad[:8].tolist())
+        assert np.array_equal(tree["gsum"], np.asarray(gt["gsum_q"], dtype=np.int64)), (t, "gsum")
+        for f in ("leaf_value", "gain"):
+            bits = np.asarray(gt[f + "_bits"], dtype=np.uint64)
+            bad = np.nonzero(tree[f].view(np.uint64) != bits)[0]
+            assert bad.size == 0, (t, f, bad[:8].tolist())
+        dq = bst.q.view(torch.int32)[:n] if q32 else bst.q[:n]
+        assert _sha(dq.cpu().numpy().astype(np.int64)) == gt["q_sha256"], (t, "gradients")
+        hg = bst.hist_g.view(-1, TB).cpu().numpy()
+        hc = bst.hist_cnt.view(-1, TB).cpu().numpy().view(np.uint32)
+        built = sorted(orc_has_hist(tree, D, ms))
+        hs = gt["hist_sha256"]
+        bad = [v for v in built if _sha(hc[v], hg[v])[:len(hs[str(v)])] != hs[str(v)]]
+        assert not bad, (t, "histograms", bad[:8])
+        pred = bst.pred.cpu().numpy()
+        assert np.array_equal(pred[rows].view(np.uint64), np.asarray(gt["pred_sample_bits"], dtype=np.uint64))
+        assert _sha(pred) == gt["pred_sha256"], (t, "predictions")
+        say("  tree %d: %d nodes, %d histograms, %d predictions match" % (t, len(tree), len(built), n))
+    bst.check()
