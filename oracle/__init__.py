@@ -25,21 +25,25 @@ LEAF = 1
 NODE_DTYPE = np.dtype([
     ("feature", "<i4"), ("threshold_bin", "<i4"), ("left", "<i4"), ("right", "<i4"),
     ("leaf_value", "<f8"), ("gain", "<f8"), ("flags", "<u4"), ("depth", "<i4"),
-    ("count", "<i8"), ("gsum_q", "<i8"),
+    ("count", "<i8"), ("gsum_q", "<i8"), ("hsum_q", "<i8"),
 ])
-assert NODE_DTYPE.itemsize == 56
+assert NODE_DTYPE.itemsize == 64
 
 SPLIT_DTYPE = np.dtype([
     ("gain", "<f8"), ("feature", "<i4"), ("threshold_bin", "<i4"), ("n_left", "<i8"),
-    ("gq_left", "<i8"), ("valid", "<i4"), ("pad", "<i4"),
+    ("gq_left", "<i8"), ("valid", "<i4"), ("pad", "<i4"), ("h_left", "<f8"),
 ])
-assert SPLIT_DTYPE.itemsize == 40
+assert SPLIT_DTYPE.itemsize == 48
+
+SQUARED_ERROR = 0
+LOGISTIC = 1
 
 
 class OrcParams(ctypes.Structure):
     _fields_ = [("reg_lambda", ctypes.c_double), ("gamma", ctypes.c_double),
                 ("min_child_weight", ctypes.c_double), ("learning_rate", ctypes.c_double),
-                ("min_samples_leaf", ctypes.c_int32), ("max_depth", ctypes.c_int32)]
+                ("min_samples_leaf", ctypes.c_int32), ("max_depth", ctypes.c_int32),
+                ("objective", ctypes.c_int32), ("pad", ctypes.c_int32)]
 
 
 def build(force: bool = True) -> str:
@@ -72,7 +76,13 @@ def _load():
     lib.orc_gradient_grid.argtypes = [ctypes.c_int64, vp, vp, vp, vp, vp]
     lib.orc_node_histogram.restype = ctypes.c_int
     lib.orc_node_histogram.argtypes = [vp, ctypes.c_int32, vp, ctypes.c_int32, vp, ctypes.c_int64,
-                                       vp, ctypes.c_int32, vp, vp, vp, vp]
+                                       vp, ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
+    lib.orc_exp_neg.restype = ctypes.c_double
+    lib.orc_exp_neg.argtypes = [ctypes.c_double]
+    lib.orc_logistic_gh.restype = None
+    lib.orc_logistic_gh.argtypes = [ctypes.c_double, ctypes.c_double, vp, vp]
+    lib.orc_logistic_grid.restype = ctypes.c_int
+    lib.orc_logistic_grid.argtypes = [ctypes.c_int64, vp, vp, vp, vp, vp, vp]
     lib.orc_best_split.restype = ctypes.c_int
     lib.orc_best_split.argtypes = [ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_double,
                                    ctypes.c_double, ctypes.c_int64, ctypes.POINTER(OrcParams), vp]
@@ -83,7 +93,8 @@ def _load():
                                   ctypes.c_int32, vp, vp]
     lib.orc_train.restype = ctypes.c_int
     lib.orc_train.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp, ctypes.POINTER(OrcParams),
-                              ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp]
+                              ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp,
+                              vp, vp, vp]
     lib.orc_predict.restype = ctypes.c_int
     lib.orc_predict.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32, vp, ctypes.c_int32,
                                 vp, ctypes.c_double, ctypes.c_double, vp]
@@ -100,9 +111,9 @@ def _p(a):
 
 
 def make_params(max_depth, reg_lambda=1.0, gamma=0.0, min_child_weight=0.0, learning_rate=0.3,
-                min_samples_leaf=1, **_ignored) -> OrcParams:
+                min_samples_leaf=1, objective=SQUARED_ERROR, **_ignored) -> OrcParams:
     return OrcParams(float(reg_lambda), float(gamma), float(min_child_weight), float(learning_rate),
-                     int(min_samples_leaf), int(max_depth))
+                     int(min_samples_leaf), int(max_depth), int(objective), 0)
 
 
 def validate_params(**kw) -> int:
@@ -135,8 +146,38 @@ def gradient_grid(pred, label):
     return k, int(S.value), g
 
 
-def node_histogram(bins, n_bins, rows, k, S):
-    """Histogram of the rows (in the given order): (cnt uint32[TB], gq int64[TB])."""
+def exp_neg(x: float) -> float:
+    """orc_exp_neg: e^x for x <= 0 (Cody-Waite reduction, degree-13 Taylor series)."""
+    return float(_load().orc_exp_neg(float(x)))
+
+
+def logistic_gh(p: float, y: float):
+    """(g, h) of the sigmoid cross-entropy at raw score p and label y."""
+    g = ctypes.c_double()
+    h = ctypes.c_double()
+    _load().orc_logistic_gh(float(p), float(y), ctypes.addressof(g), ctypes.addressof(h))
+    return g.value, h.value
+
+
+def logistic_grid(pred, label):
+    """(kg int64[n], kh int64[n], Sg, Sh) of the logistic objective."""
+    pred = np.ascontiguousarray(pred, dtype=np.float64)
+    label = np.ascontiguousarray(label, dtype=np.float32)
+    n = pred.shape[0]
+    kg = np.empty(n, dtype=np.int64)
+    kh = np.empty(n, dtype=np.int64)
+    sg = ctypes.c_int32()
+    sh = ctypes.c_int32()
+    rc = _load().orc_logistic_grid(n, _p(pred), _p(label), _p(kg), _p(kh), ctypes.addressof(sg),
+                                   ctypes.addressof(sh))
+    if rc:
+        raise ValueError("orc_logistic_grid failed (%d)" % rc)
+    return kg, kh, int(sg.value), int(sh.value)
+
+
+def node_histogram(bins, n_bins, rows, k, S, kh=None, Sh=0):
+    """Histogram of the rows (in the given order): (cnt uint32[TB], gq int64[TB]),
+    plus hq int64[TB] when the logistic Hessians kh are given."""
     bins = np.ascontiguousarray(bins, dtype=np.uint8)
     n_bins = np.ascontiguousarray(n_bins, dtype=np.int32)
     off = bin_offsets(n_bins)
@@ -147,25 +188,34 @@ def node_histogram(bins, n_bins, rows, k, S):
     gq = np.empty(TB, dtype=np.int64)
     g = np.empty(TB, dtype=np.float64)
     h = np.empty(TB, dtype=np.float64)
+    hq = np.empty(TB, dtype=np.int64) if kh is not None else None
+    khc = np.ascontiguousarray(kh, dtype=np.int64) if kh is not None else None
     rc = _load().orc_node_histogram(_p(bins), bins.shape[1], _p(off), TB, _p(rows), rows.shape[0],
-                                    _p(k), S, _p(cnt), _p(gq), _p(g), _p(h))
+                                    _p(k), S, _p(cnt), _p(gq), _p(g), _p(h), _p(khc), int(Sh), _p(hq))
     if rc:
         raise RuntimeError("orc_node_histogram: FP64 sum differs from its int64 shadow")
-    return cnt, gq
+    return (cnt, gq) if kh is None else (cnt, gq, hq)
 
 
-def best_split(cnt, gq, n_bins, node_gq: int, node_n: int, S: int, params: OrcParams):
-    """Best split of one node from its histogram; returns a SPLIT_DTYPE record."""
+def best_split(cnt, gq, n_bins, node_gq: int, node_n: int, S: int, params: OrcParams, hq=None,
+               node_hq: int = 0, Sh: int = 0):
+    """Best split of one node from its histogram; returns a SPLIT_DTYPE record.
+    With hq (logistic), H comes from the fixed-point Hessian sums on grid Sh."""
     n_bins = np.ascontiguousarray(n_bins, dtype=np.int32)
     off = bin_offsets(n_bins)
     cnt = np.ascontiguousarray(cnt, dtype=np.uint32)
     gq = np.ascontiguousarray(gq, dtype=np.int64)
     g = np.ldexp(gq.astype(np.float64), -S)
-    h = cnt.astype(np.float64)
+    if hq is None:
+        h = cnt.astype(np.float64)
+        H_v = float(node_n)
+    else:
+        h = np.ascontiguousarray(np.ldexp(np.asarray(hq, dtype=np.int64).astype(np.float64), -Sh))
+        H_v = float(np.ldexp(np.float64(node_hq), -Sh))
     G_v = float(np.ldexp(np.float64(node_gq), -S))
     out = np.zeros(1, dtype=SPLIT_DTYPE)
     _load().orc_best_split(n_bins.shape[0], _p(n_bins), _p(off), _p(cnt), _p(gq), _p(g), _p(h),
-                           G_v, float(node_n), node_n, ctypes.byref(params), _p(out))
+                           G_v, H_v, node_n, ctypes.byref(params), _p(out))
     return out[0]
 
 
@@ -239,19 +289,27 @@ def train(bins, n_bins, label, params: OrcParams, n_trees: int, pred0=None, base
     n_nodes = np.zeros(max(n_trees, 1), dtype=np.int32)
     scale = np.zeros(max(n_trees, 1), dtype=np.int32)
     ppt = np.zeros((n_trees, n), dtype=np.float64) if keep_pred_per_tree else None
-    dcnt = dgq = dleaf = dk = None
+    logistic = int(params.objective) == LOGISTIC
+    scale_h = np.zeros(max(n_trees, 1), dtype=np.int32)
+    dcnt = dgq = dleaf = dk = dhq = dkh = None
     if dump_tree >= 0:
         if dump_hist:
             dcnt = np.zeros((mn, TB), dtype=np.uint32)
             dgq = np.zeros((mn, TB), dtype=np.int64)
+            if logistic:
+                dhq = np.zeros((mn, TB), dtype=np.int64)
         dleaf = np.full(n, -1, dtype=np.int32)
         dk = np.zeros(n, dtype=np.int64)
+        if logistic:
+            dkh = np.zeros(n, dtype=np.int64)
     timing = np.zeros(2, dtype=np.float64)
     rc = _load().orc_train(n, F, _p(bins), _p(n_bins), _p(label), ctypes.byref(params), n_trees,
                            _p(pred), _p(nodes), _p(n_nodes), _p(scale), _p(ppt), dump_tree,
-                           _p(dcnt), _p(dgq), _p(dleaf), _p(dk), _p(timing))
+                           _p(dcnt), _p(dgq), _p(dleaf), _p(dk), _p(timing), _p(scale_h), _p(dhq),
+                           _p(dkh))
     if rc:
         raise ValueError("orc_train failed (%d)" % rc)
     return dict(nodes=nodes[:n_trees], n_nodes=n_nodes[:n_trees], scale=scale[:n_trees], pred=pred,
                 pred_per_tree=ppt, dump_cnt=dcnt, dump_gq=dgq, dump_leaf_of_row=dleaf, dump_k=dk,
+                scale_h=scale_h[:n_trees], dump_hq=dhq, dump_kh=dkh,
                 seconds=float(timing[0]), hist_seconds=float(timing[1]))

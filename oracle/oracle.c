@@ -51,6 +51,9 @@
 #define ORC_E_INTERNAL (-7)
 #define ORC_LEAF 1u
 
+#define ORC_SQUARED_ERROR 0
+#define ORC_LOGISTIC 1
+
 typedef struct {
   double reg_lambda;
   double gamma;
@@ -58,6 +61,8 @@ typedef struct {
   double learning_rate;
   int32_t min_samples_leaf;
   int32_t max_depth;
+  int32_t objective; /* ORC_SQUARED_ERROR or ORC_LOGISTIC */
+  int32_t pad;
 } orc_params;
 
 typedef struct {
@@ -71,6 +76,7 @@ typedef struct {
   int32_t depth;
   int64_t count;  /* rows in the node */
   int64_t gsum_q; /* sum of the fixed-point gradients k_i over the node */
+  int64_t hsum_q; /* logistic: sum of the fixed-point Hessians over the node (0 otherwise) */
 } orc_node;
 
 typedef struct {
@@ -81,6 +87,7 @@ typedef struct {
   int64_t gq_left;
   int32_t valid;
   int32_t pad;
+  double h_left; /* the left child's Hessian sum (FP64) */
 } orc_split;
 
 static double now_s(void) {
@@ -100,6 +107,7 @@ int orc_validate_params(const orc_params* p) {
   if (p->reg_lambda < 0.0) return ORC_E_ARG;
   if (p->gamma < 0.0) return ORC_E_ARG;
   if (p->max_depth < 0 || p->max_depth > 20) return ORC_E_ARG;
+  if (p->objective != ORC_SQUARED_ERROR && p->objective != ORC_LOGISTIC) return ORC_E_ARG;
   return ORC_OK;
 }
 
@@ -139,15 +147,109 @@ int orc_gradient_grid(int64_t n, const double* pred, const float* label, int64_t
 }
 
 /*
+ * exp(x) for x <= 0, written out from a published method: Cody and Waite's
+ * argument reduction ("Software Manual for the Elementary Functions", 1980)
+ * and the Taylor series of e^r.  k = rint(x / ln 2) and
+ * r = (x - k*LN2_HI) - k*LN2_LO, where LN2_HI holds the first 42 significant
+ * bits of ln 2 (so k*LN2_HI is exact for |k| < 2^11) and LN2_LO = ln 2 - LN2_HI
+ * rounded to FP64; then |r| <= ln(2)/2 and e^r = sum_{j=0..13} r^j / j!
+ * (the first omitted term is below 2^-57 relative), summed by Horner's rule
+ * from the highest power, and e^x = 2^k * e^r (ldexp, exact for the normal
+ * results that x in [-700, 0] gives).  Every step is one IEEE FP64 operation,
+ * so the result is the same on any machine that rounds to nearest even.
+ * Arguments below -700 give 0 (the callers need e^-|p| only to about 1e-304).
+ */
+static const double ORC_LN2_HI = 0x1.62e42fefa3800p-1;
+static const double ORC_LN2_LO = 0x1.ef35793c76730p-45;
+static const double ORC_INV_LN2 = 0x1.71547652b82fep+0;
+
+double orc_exp_neg(double x) {
+  if (!(x <= 0.0)) return NAN;
+  if (x < -700.0) return 0.0;
+  const double kd = rint(x * ORC_INV_LN2);
+  const double r = (x - kd * ORC_LN2_HI) - kd * ORC_LN2_LO;
+  /* 1/j! for j = 13 down to 0 */
+  static const double inv_fact[14] = {
+      1.0 / 6227020800.0, 1.0 / 479001600.0, 1.0 / 39916800.0, 1.0 / 3628800.0, 1.0 / 362880.0,
+      1.0 / 40320.0,      1.0 / 5040.0,      1.0 / 720.0,      1.0 / 120.0,     1.0 / 24.0,
+      1.0 / 6.0,          0.5,               1.0,              1.0};
+  double poly = inv_fact[0];
+  for (int j = 1; j < 14; ++j) poly = poly * r + inv_fact[j];
+  return ldexp(poly, (int)kd);
+}
+
+/*
+ * Sigmoid binary cross-entropy on the raw score ("Gradient boosted trees
+ * (spec model)", gbtBinaryCrossentropyGradSpec: the gradient of the
+ * sigmoid's cross-entropy with respect to the prediction).  With
+ * s = 1 / (1 + e^-p): g = s - y.  The pages give no Hessian; the reading
+ * used is its second derivative, h = s (1 - s), which the Training Core's
+ * Newton-form weight -G/(H+lambda) and gain take where squared error has
+ * h = 1.  Both come from z = e^-|p| and d = 1 + z, so that neither loses
+ * accuracy for large |p|: s = 1/d for p >= 0 and z/d otherwise, and
+ * h = z / (d*d), each one IEEE operation at a time.
+ */
+void orc_logistic_gh(double p, double y, double* g, double* h) {
+  const double z = orc_exp_neg(-fabs(p));
+  const double d = 1.0 + z;
+  const double s = p >= 0.0 ? 1.0 / d : z / d;
+  *g = s - y;
+  *h = z / (d * d);
+}
+
+/*
+ * Grid exponent of one quantity for the logistic objective (reading): with
+ * M the largest magnitude (frexp exponent e, M < 2^e), S = 52 - e - L as for
+ * squared error, but at most 30 - e, so every fixed-point value fits 31 bits
+ * (a resolution of 2^-30 of M) while every sum over any rows stays exact.
+ */
+static int32_t orc_logistic_scale(double M, int64_t n) {
+  if (!(M > 0.0)) return 0;
+  int e = 0;
+  (void)frexp(M, &e);
+  int32_t S = 52 - e - orc_ceil_log2(n);
+  if (S > 30 - e) S = 30 - e;
+  return S;
+}
+
+/* Gradients and Hessians of the logistic objective on their per-tree grids. */
+int orc_logistic_grid(int64_t n, const double* pred, const float* label, int64_t* kg, int64_t* kh,
+                      int32_t* sg_out, int32_t* sh_out) {
+  if (n < 1 || !pred || !label || !kg || !kh || !sg_out || !sh_out) return ORC_E_ARG;
+  double Mg = 0.0, Mh = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    double g, h;
+    if (!isfinite(pred[i]) || !isfinite((double)label[i])) return ORC_E_RANGE;
+    orc_logistic_gh(pred[i], (double)label[i], &g, &h);
+    if (!isfinite(g) || !isfinite(h)) return ORC_E_RANGE;
+    if (fabs(g) > Mg) Mg = fabs(g);
+    if (h > Mh) Mh = h;
+  }
+  const int32_t Sg = orc_logistic_scale(Mg, n);
+  const int32_t Sh = orc_logistic_scale(Mh, n);
+  for (int64_t i = 0; i < n; ++i) {
+    double g, h;
+    orc_logistic_gh(pred[i], (double)label[i], &g, &h);
+    kg[i] = (int64_t)rint(ldexp(g, Sg));
+    kh[i] = (int64_t)rint(ldexp(h, Sh));
+  }
+  *sg_out = Sg;
+  *sh_out = Sh;
+  return ORC_OK;
+}
+
+/*
  * One node's histogram (CPU Oracle section: count/G/H per bin, accumulated in
  * the supplied row order, FP64).  gq is the int64 shadow of G on the grid.
  * Returns ORC_E_INTERNAL if an FP64 sum ever differs from its shadow.
  */
 int orc_node_histogram(const uint8_t* bins, int32_t F, const int32_t* bin_offset,
                        int32_t total_bins, const int32_t* rows, int64_t n_rows, const int64_t* k,
-                       int32_t S, uint32_t* cnt, int64_t* gq, double* g, double* h) {
+                       int32_t S, uint32_t* cnt, int64_t* gq, double* g, double* h,
+                       const int64_t* kh, int32_t Sh, int64_t* hq) {
   memset(cnt, 0, sizeof(uint32_t) * (size_t)total_bins);
   memset(gq, 0, sizeof(int64_t) * (size_t)total_bins);
+  if (hq) memset(hq, 0, sizeof(int64_t) * (size_t)total_bins);
   for (int32_t b = 0; b < total_bins; ++b) {
     g[b] = 0.0;
     h[b] = 0.0;
@@ -155,17 +257,20 @@ int orc_node_histogram(const uint8_t* bins, int32_t F, const int32_t* bin_offset
   for (int64_t r = 0; r < n_rows; ++r) {
     const int64_t i = rows[r];
     const double gi = ldexp((double)k[i], -S);
+    /* h_i = 1 for squared error; the logistic objective's grid value otherwise */
+    const double hi = kh ? ldexp((double)kh[i], -Sh) : 1.0;
     for (int32_t f = 0; f < F; ++f) {
       const int32_t b = bin_offset[f] + (int32_t)bins[i * (int64_t)F + f];
       cnt[b] += 1u;
       g[b] = g[b] + gi;
-      h[b] = h[b] + 1.0;
+      h[b] = h[b] + hi;
       gq[b] += k[i];
+      if (kh && hq) hq[b] += kh[i];
     }
   }
   for (int32_t b = 0; b < total_bins; ++b) {
     if (g[b] != ldexp((double)gq[b], -S)) return ORC_E_INTERNAL;
-    if (h[b] != (double)cnt[b]) return ORC_E_INTERNAL;
+    if (kh ? (hq && h[b] != ldexp((double)hq[b], -Sh)) : h[b] != (double)cnt[b]) return ORC_E_INTERNAL;
   }
   return ORC_OK;
 }
@@ -222,6 +327,7 @@ int orc_best_split(int32_t F, const int32_t* n_bins, const int32_t* bin_offset,
         out->threshold_bin = t;
         out->n_left = nL;
         out->gq_left = gqL;
+        out->h_left = HL;
         out->valid = 1;
       }
     }
@@ -270,7 +376,7 @@ int orc_train(int64_t n, int32_t F, const uint8_t* bins, const int32_t* n_bins, 
               const orc_params* p, int32_t n_trees, double* pred, orc_node* nodes,
               int32_t* n_nodes, int32_t* scale, double* pred_per_tree, int32_t dump_tree,
               uint32_t* dump_cnt, int64_t* dump_gq, int32_t* dump_leaf_of_row, int64_t* dump_k,
-              double* timing) {
+              double* timing, int32_t* scale_h, int64_t* dump_hq, int64_t* dump_kh) {
   int rc = orc_validate_params(p);
   if (rc) return rc;
   if (n < 1 || n > 0x7fffffffLL || F < 1 || !bins || !n_bins || !label || !pred || !nodes ||
@@ -302,7 +408,10 @@ int orc_train(int64_t n, int32_t F, const uint8_t* bins, const int32_t* n_bins, 
   const int32_t max_nodes = (1 << (D + 1)) - 1;
   double t_total = 0.0, t_hist = 0.0;
 
+  const int logistic = p->objective == ORC_LOGISTIC;
   int64_t* k = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+  int64_t* kh = logistic ? (int64_t*)malloc(sizeof(int64_t) * (size_t)n) : NULL;
+  int64_t* hqv = logistic ? (int64_t*)malloc(sizeof(int64_t) * (size_t)TB) : NULL;
   int32_t* buf_a = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
   int32_t* buf_b = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
   int32_t* tmp_r = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
@@ -313,7 +422,8 @@ int orc_train(int64_t n, int32_t F, const uint8_t* bins, const int32_t* n_bins, 
   int64_t* gq = (int64_t*)malloc(sizeof(int64_t) * (size_t)TB);
   double* hg = (double*)malloc(sizeof(double) * (size_t)TB);
   double* hh = (double*)malloc(sizeof(double) * (size_t)TB);
-  if (!k || !buf_a || !buf_b || !tmp_r || !leaf_of_row || !act || !nxt || !cnt || !gq || !hg || !hh) {
+  if (!k || !buf_a || !buf_b || !tmp_r || !leaf_of_row || !act || !nxt || !cnt || !gq || !hg || !hh ||
+      (logistic && (!kh || !hqv))) {
     rc = ORC_E_INTERNAL;
     goto done;
   }
@@ -322,12 +432,18 @@ int orc_train(int64_t n, int32_t F, const uint8_t* bins, const int32_t* n_bins, 
     const double t0 = now_s();
     const int dump = (t == dump_tree);
     orc_node* tree = nodes + (size_t)t * (size_t)max_nodes;
-    int32_t S = 0;
-    /* gradients and grid */
-    rc = orc_gradient_grid(n, pred, label, k, &S, NULL);
+    int32_t S = 0, Sh = 0;
+    /* gradients (and, for the logistic objective, Hessians) and grids */
+    if (logistic)
+      rc = orc_logistic_grid(n, pred, label, k, kh, &S, &Sh);
+    else
+      rc = orc_gradient_grid(n, pred, label, k, &S, NULL);
     if (rc) goto done;
     scale[t] = S;
+    if (scale_h) scale_h[t] = Sh;
     if (dump && dump_k) memcpy(dump_k, k, sizeof(int64_t) * (size_t)n);
+    if (dump && dump_kh && logistic) memcpy(dump_kh, kh, sizeof(int64_t) * (size_t)n);
+    if (dump && dump_hq) memset(dump_hq, 0, sizeof(int64_t) * (size_t)max_nodes * (size_t)TB);
     if (dump && dump_cnt) memset(dump_cnt, 0, sizeof(uint32_t) * (size_t)max_nodes * (size_t)TB);
     if (dump && dump_gq) memset(dump_gq, 0, sizeof(int64_t) * (size_t)max_nodes * (size_t)TB);
 
@@ -344,9 +460,13 @@ int orc_train(int64_t n, int32_t F, const uint8_t* bins, const int32_t* n_bins, 
     tree[0].depth = 0;
     tree[0].count = n;
     {
-      int64_t s = 0;
-      for (int64_t i = 0; i < n; ++i) s += k[i];
+      int64_t s = 0, sh = 0;
+      for (int64_t i = 0; i < n; ++i) {
+        s += k[i];
+        if (logistic) sh += kh[i];
+      }
       tree[0].gsum_q = s;
+      tree[0].hsum_q = sh;
     }
 
     for (int32_t d = 0; d < D && n_act > 0; ++d) {
@@ -358,18 +478,20 @@ int orc_train(int64_t n, int32_t F, const uint8_t* bins, const int32_t* n_bins, 
         const int64_t nv = act[a].count;
         /* step 2: histogram of the node, rows in order */
         const double th = now_s();
-        rc = orc_node_histogram(bins, F, bin_offset, TB, rows, nv, k, S, cnt, gq, hg, hh);
+        rc = orc_node_histogram(bins, F, bin_offset, TB, rows, nv, k, S, cnt, gq, hg, hh, kh, Sh, hqv);
         t_hist += now_s() - th;
         if (rc) goto done;
         if (dump && dump_cnt) memcpy(dump_cnt + (size_t)v * TB, cnt, sizeof(uint32_t) * (size_t)TB);
         if (dump && dump_gq) memcpy(dump_gq + (size_t)v * TB, gq, sizeof(int64_t) * (size_t)TB);
+        if (dump && dump_hq && logistic) memcpy(dump_hq + (size_t)v * TB, hqv, sizeof(int64_t) * (size_t)TB);
         /* node totals, row order */
         double Gv = 0.0, Hv = 0.0;
         for (int64_t r = 0; r < nv; ++r) {
           Gv = Gv + ldexp((double)k[rows[r]], -S);
-          Hv = Hv + 1.0;
+          Hv = Hv + (logistic ? ldexp((double)kh[rows[r]], -Sh) : 1.0);
         }
-        if (Gv != ldexp((double)tree[v].gsum_q, -S)) {
+        if (Gv != ldexp((double)tree[v].gsum_q, -S) ||
+            (logistic && Hv != ldexp((double)tree[v].hsum_q, -Sh))) {
           rc = ORC_E_INTERNAL;
           goto done;
         }
@@ -403,6 +525,16 @@ int orc_train(int64_t n, int32_t F, const uint8_t* bins, const int32_t* n_bins, 
           tree[rcn].count = nv - nl;
           tree[lc].gsum_q = sp.gq_left;
           tree[rcn].gsum_q = tree[v].gsum_q - sp.gq_left;
+          if (logistic) {
+            int64_t hl = 0;
+            for (int64_t r = 0; r < nl; ++r) hl += kh[left[r]];
+            if (ldexp((double)hl, -Sh) != sp.h_left) {
+              rc = ORC_E_INTERNAL;
+              goto done;
+            }
+            tree[lc].hsum_q = hl;
+            tree[rcn].hsum_q = tree[v].hsum_q - hl;
+          }
           nxt[n_nxt].id = lc;
           nxt[n_nxt].off = nb_off;
           nxt[n_nxt].count = nl;
@@ -444,7 +576,7 @@ int orc_train(int64_t n, int32_t F, const uint8_t* bins, const int32_t* n_bins, 
       double Gv = 0.0, Hv = 0.0;
       for (int64_t r = 0; r < nv; ++r) {
         Gv = Gv + ldexp((double)k[rows[r]], -S);
-        Hv = Hv + 1.0;
+        Hv = Hv + (logistic ? ldexp((double)kh[rows[r]], -Sh) : 1.0);
       }
       tree[v].feature = -1;
       tree[v].threshold_bin = -1;
@@ -474,6 +606,8 @@ done:
   }
   free(bin_offset);
   free(k);
+  free(kh);
+  free(hqv);
   free(buf_a);
   free(buf_b);
   free(tmp_r);

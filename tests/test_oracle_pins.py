@@ -634,3 +634,181 @@ def test_predict_rejects_bad_trees():
     loop = _oracle_tree([(0, 0, 0, 0, 0.0)])  # a node that is its own child
     with pytest.raises(ValueError):
         oracle.predict(bins, loop, [1])
+
+
+# ------------------------------------------------------------ logistic objective
+
+def _ulps(a: float, b: float) -> int:
+    import struct
+    ia = struct.unpack("<q", struct.pack("<d", a))[0]
+    ib = struct.unpack("<q", struct.pack("<d", b))[0]
+    return abs(ia - ib)
+
+
+def test_exp_neg_against_math_exp():
+    """orc_exp_neg (Cody-Waite reduction + degree-13 Taylor series) stays
+    within 2 ulp of the C library's exp over [-700, 0] (a dense sweep, a
+    geometric sweep down to 1e-300 and the ends of the reduction interval)
+    and near multiples of ln 2; e^0 = 1 exactly; arguments below -700 give 0."""
+    xs = np.concatenate([-np.linspace(0.0, 700.0, 200_001), -np.geomspace(1e-300, 700.0, 20_001),
+                         [-0.0, -1e-310, -0.34657359027997264, -0.6931471805599453, -709.0 + 9.0]])
+    worst = max(_ulps(oracle.exp_neg(float(x)), math.exp(float(x))) for x in xs)
+    assert worst <= 2, worst
+    assert oracle.exp_neg(0.0) == 1.0 and oracle.exp_neg(-0.0) == 1.0
+    for k in range(0, 1000, 37):
+        x = -k * math.log(2.0)
+        for dx in (0.0, 1e-9, -1e-9):
+            y = min(x + dx, 0.0)
+            assert _ulps(oracle.exp_neg(y), math.exp(y)) <= 2
+    assert oracle.exp_neg(-700.5) == 0.0 and oracle.exp_neg(-1e308) == 0.0
+
+
+def test_logistic_gradient_and_hessian():
+    """g = sigmoid(p) - y and h = sigmoid(p) (1 - sigmoid(p)) against 50-digit
+    decimal arithmetic: h within 4 ulp; g, a difference of rounded values,
+    within 4 ulp of the larger of sigmoid(p) and y (the subtraction itself is
+    exact or one rounding); exact values at p = 0; h is even in p bit for bit;
+    g(p, y) + g(-p, 1 - y) = 0 up to one rounding of 1."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    assert oracle.logistic_gh(0.0, 0.0) == (0.5, 0.25)
+    assert oracle.logistic_gh(0.0, 1.0) == (-0.5, 0.25)
+    rng = np.random.default_rng(3)
+    ps = np.concatenate([rng.normal(0.0, 3.0, 2000), rng.uniform(-40.0, 40.0, 500),
+                         [1e-12, -1e-12, 36.0, -36.0, 699.0, -699.0, 701.0, -701.0, 1e4]])
+    # beyond |p| = 700 e^-|p| is taken as 0: sigmoid is 0 or 1 and h = 0
+    assert oracle.logistic_gh(-701.0, 0.0) == (0.0, 0.0)
+    assert oracle.logistic_gh(701.0, 1.0) == (0.0, 0.0)
+    for p in ps:
+        if abs(p) > 700.0:
+            continue
+        for y in (0.0, 1.0, 0.25):
+            g, h = oracle.logistic_gh(float(p), y)
+            s = 1 / (1 + (-Decimal(float(p))).exp())
+            gx = float(s - Decimal(y))
+            hx = float(s * (1 - s))
+            assert abs(g - gx) <= 4 * 2.0 ** -53 * max(float(s), y), (p, y, g, gx)
+            assert _ulps(h, hx) <= 4 or abs(h - hx) <= 2.0 ** -1000, (p, y, h, hx)
+            assert oracle.logistic_gh(-float(p), y)[1] == h
+            g2, _ = oracle.logistic_gh(-float(p), 1.0 - y)
+            assert abs(g + g2) <= 2.0 ** -52
+
+
+def test_logistic_grid_bounds():
+    """Both grids keep every value within 31 bits and every sum over all rows
+    exact (|sum| <= 2^52), with the largest magnitude using at least 29 bits
+    (or the 52 - ceil(log2 n) bits the squared-error grid allows)."""
+    rng = np.random.default_rng(4)
+    for n in (1, 7, 1000, 70_000):
+        pred = rng.normal(0.0, 2.0, n)
+        label = (rng.uniform(size=n) < 0.4).astype(np.float32)
+        kg, kh, Sg, Sh = oracle.logistic_grid(pred, label)
+        L = oracle.ceil_log2(n)
+        for k, S in ((kg, Sg), (kh, Sh)):
+            m = int(np.abs(k).max())
+            assert m < 2 ** 31 and m * n <= 2 ** 52
+            assert m >= min(2 ** 29, 2 ** (51 - L)) or m == 0
+        assert (kh >= 0).all()
+
+
+def test_logistic_hand_tree():
+    """Worked by hand at base 0: sigmoid(0) = 1/2, so g = 1/2 - y and h = 1/4 for
+    every row.  Four rows, one feature with bins 0..3, labels 0, 0, 1, 1,
+    lambda 1: G_P = 0, H_P = 1.  t = 0: (1/2)^2/(1/4 + 1) + (1/2)^2/(3/4 + 1) =
+    1/5 + 1/7, gain 6/35; t = 1: 1/(1/2 + 1) twice, gain 2/3; t = 2: 6/35.  The
+    root splits at t = 1 with leaves -1/(1/2 + 1) = -2/3 and 2/3.  The grids:
+    max |g| = 1/2 gives S = 30 (the 30-bit cap; 52 - 0 - 2 = 50 otherwise) and
+    max h = 1/4 gives Sh = 31, so kg = -+2^29 and kh = 2^29 exactly.
+    With min_child_weight 0.6 every child's H is below 0.6 (counts would all
+    pass), so the root stays a leaf with weight -0/(1 + 1) = -0.0."""
+    bins = np.array([[0], [1], [2], [3]], dtype=np.uint8)
+    label = np.array([0, 0, 1, 1], dtype=np.float32)
+    p = oracle.make_params(1, reg_lambda=1.0, learning_rate=1.0, objective=oracle.LOGISTIC)
+    r = oracle.train(bins, [4], label, p, 1, dump_tree=0)
+    tree = r["nodes"][0][: r["n_nodes"][0]]
+    assert r["scale"][0] == 30 and r["scale_h"][0] == 31
+    assert r["dump_k"].tolist() == [2 ** 29, 2 ** 29, -(2 ** 29), -(2 ** 29)]
+    assert r["dump_kh"].tolist() == [2 ** 29] * 4
+    assert len(tree) == 3
+    assert (int(tree[0]["feature"]), int(tree[0]["threshold_bin"])) == (0, 1)
+    assert float(tree[0]["gain"]) == 0.5 * (2.0 / 3.0 + 2.0 / 3.0)
+    assert float(tree[1]["leaf_value"]) == -1.0 / 1.5 and float(tree[2]["leaf_value"]) == 1.0 / 1.5
+    assert int(tree[0]["hsum_q"]) == 2 ** 31 and int(tree[1]["hsum_q"]) == 2 ** 30
+    assert r["pred"].tolist() == [-1.0 / 1.5, -1.0 / 1.5, 1.0 / 1.5, 1.0 / 1.5]
+    p.min_child_weight = 0.6
+    r = oracle.train(bins, [4], label, p, 1)
+    root = r["nodes"][0][0]
+    assert r["n_nodes"][0] == 1 and root["flags"] & oracle.LEAF
+    assert float(root["leaf_value"]) == 0.0 and math.copysign(1.0, float(root["leaf_value"])) < 0
+
+
+@pytest.mark.parametrize("seed", [21, 22, 23, 24])
+def test_logistic_split_choice_against_exact_rationals(seed):
+    """Brute force for the logistic objective: the grid values (kg, kh) taken as
+    exact rationals, every (feature, bin) of every node scored from the rows
+    directly -- H from the Hessians, min_child_weight on H -- and the oracle's
+    chosen split must be the exact best (up to the FP64 rounding of the gain),
+    with leaf weights -G/(H + lambda) of the rows they hold."""
+    nb = [5, 3, 7]
+    bins, _, nb = datagen.make_random(60, nb, seed)
+    rng = np.random.default_rng(seed)
+    label = (rng.uniform(size=60) < 0.5).astype(np.float32)
+    base = float(rng.normal(0.0, 1.0))
+    p = oracle.make_params(3, reg_lambda=0.5, gamma=0.01, min_child_weight=1.5, min_samples_leaf=2,
+                           learning_rate=0.5, objective=oracle.LOGISTIC)
+    pred0 = np.full(60, base) + rng.normal(0.0, 0.5, 60)
+    r = oracle.train(bins, nb, label, p, 1, pred0=pred0, dump_tree=0)
+    kg, kh, Sg, Sh = oracle.logistic_grid(pred0, label)
+    assert np.array_equal(kg, r["dump_k"]) and np.array_equal(kh, r["dump_kh"])
+    g = [Fraction(int(x), 2 ** Sg) for x in kg]
+    h = [Fraction(int(x), 2 ** Sh) for x in kh]
+    tree = r["nodes"][0][: r["n_nodes"][0]]
+    lam, gam = Fraction(p.reg_lambda), Fraction(p.gamma)
+    rows = _node_rows(tree, bins)
+    for v, nd in enumerate(tree):
+        rv = rows[v]
+        GP, HP = sum(g[i] for i in rv), sum(h[i] for i in rv)
+        if nd["flags"] & oracle.LEAF:
+            assert float(nd["leaf_value"]) == float(-GP / (HP + lam)) or (
+                GP == 0 and float(nd["leaf_value"]) == 0.0)
+        if int(nd["depth"]) >= p.max_depth:
+            continue
+        cands = []
+        for f in range(bins.shape[1]):
+            for t in range(int(nb[f]) - 1):
+                L = [i for i in rv if int(bins[i, f]) <= t]
+                R = [i for i in rv if int(bins[i, f]) > t]
+                if len(L) < p.min_samples_leaf or len(R) < p.min_samples_leaf:
+                    continue
+                HL = sum(h[i] for i in L)
+                HR = HP - HL
+                if HL < Fraction(p.min_child_weight) or HR < Fraction(p.min_child_weight):
+                    continue
+                if not (HL > 0 and HR > 0):
+                    continue
+                GL = sum(g[i] for i in L)
+                cands.append((_exact_gain(GL, HL, GP - GL, HR, GP, HP, lam, gam), f, t))
+        tol = Fraction(1, 2 ** 40) * (1 + abs(GP * GP))
+        best = max((c[0] for c in cands), default=None)
+        if nd["flags"] & oracle.LEAF:
+            assert best is None or best <= tol, (v, best)
+            continue
+        chosen = [c for c in cands if (c[1], c[2]) == (int(nd["feature"]), int(nd["threshold_bin"]))]
+        assert chosen and best - chosen[0][0] <= tol
+        assert abs(Fraction(float(nd["gain"])) - chosen[0][0]) <= tol
+
+
+def test_logistic_training_lowers_the_loss():
+    bins, _, nb = datagen.make_random(4000, [16, 8, 32, 2], 31)
+    label = ((bins[:, 0].astype(np.int32) + bins[:, 2] // 2) > 20).astype(np.float32)
+    p = oracle.make_params(4, learning_rate=0.5, objective=oracle.LOGISTIC)
+    r = oracle.train(bins, nb, label, p, 5, keep_pred_per_tree=True)
+
+    def logloss(pr):
+        s = 1.0 / (1.0 + np.exp(-pr))
+        return float(-np.mean(label * np.log(s) + (1 - label) * np.log(1 - s)))
+    losses = [math.log(2.0)] + [logloss(r["pred_per_tree"][t]) for t in range(5)]
+    assert all(b < a for a, b in zip(losses, losses[1:])), losses
+    # the training predictions are the forward pass of the trees
+    out = oracle.predict(bins, r["nodes"], r["n_nodes"], 0.0, p.learning_rate)
+    assert np.array_equal(out, r["pred"])
