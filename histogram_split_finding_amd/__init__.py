@@ -123,6 +123,8 @@ def load():
         "gbdt_predict_workspace_bytes": (ctypes.c_size_t, [i32, i32]),
         "gbdt_predict": (ctypes.c_int, [P(Matrix), vp, vp, i32, i32, ctypes.c_double, ctypes.c_double,
                                         vp, vp, ctypes.c_size_t, vp]),
+        "gbdt_predict_noalloc": (ctypes.c_int, [P(Matrix), vp, vp, i32, i32, ctypes.c_double,
+                                                ctypes.c_double, vp, vp, vp]),
         "gbdt_grow_sizes": (ctypes.c_int, [i64, i32, i32, P(GrowSizes)]),
         "gbdt_grow_tree": (ctypes.c_int, [P(Matrix), P(Features), vp, vp, P(Params), vp, vp,
                                           P(GrowBuffers), vp]),
@@ -379,6 +381,16 @@ def gbdt_predict(X: Matrix, trees, n_nodes, n_trees, tree_stride, base_score, le
                              float(base_score), float(learning_rate), _ptr(out), _ptr(ws), ws.numel(),
                              _stream(stream))
     _check(rc, "gbdt_predict")
+
+
+def gbdt_predict_noalloc(X: Matrix, trees, n_nodes, n_trees, tree_stride, base_score, learning_rate,
+                         out, status, stream=None):
+    """gbdt_predict without a workspace (the library's per-GPU scratch);
+    status: int32 [1] device tensor, receives the device-side error code."""
+    rc = load().gbdt_predict_noalloc(ctypes.byref(X), _ptr(trees), _ptr(n_nodes), int(n_trees),
+                                     int(tree_stride), float(base_score), float(learning_rate),
+                                     _ptr(out), _ptr(status), _stream(stream))
+    _check(rc, "gbdt_predict_noalloc")
 
 
 # ------------------------------------------------------------ training run --

@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "gbdt.h"
@@ -197,6 +198,48 @@ void launch_predict(bool in_lds, dim3 grid, size_t lds, hipStream_t s, double* o
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Scratch of gbdt_predict_noalloc, for callers that cannot allocate: the
+// control block (error word), the compact tables and the leaf values of one
+// call, at most kNoAllocBytes.  Every GPU the library runs on holds its own
+// copy until the process ends.  Host code never uses this name as an
+// address: it takes each device's address from hipGetSymbolAddress once.
+constexpr size_t kNoAllocBytes = size_t(16) << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch's address on the current device (looked up on the first call
+// on that device).
+int scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(GBDT_E_UNSUPPORTED, "device index beyond 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(GBDT_E_DEVICE, "scratch has no device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GBDT_OK;
+}
+
+// The control block starts each call at zero (a kernel, not a memset node,
+// so the call can be captured into a graph), and the call's error word is
+// copied to the caller's status at its end.
+__global__ void __launch_bounds__(64) k_clear_ctrl(WsCtrl* __restrict__ ctrl) {
+  reinterpret_cast<int32_t*>(ctrl)[threadIdx.x] = 0;
+}
+__global__ void __launch_bounds__(64) k_copy_status(const WsCtrl* __restrict__ ctrl,
+                                                    int32_t* __restrict__ status) {
+  if (threadIdx.x == 0) *status = ctrl->err;
+}
+
 int predict_impl(const gbdt_matrix* X, const gbdt_node* trees, const int32_t* n_nodes,
                  int32_t n_trees, int32_t tree_stride, double base_score, double learning_rate,
                  double* out, void* ws, size_t ws_bytes, hipStream_t s);
@@ -220,6 +263,33 @@ int gbdt_predict(const gbdt_matrix* X, const gbdt_node* trees, const int32_t* n_
                  double* out, void* ws, size_t ws_bytes, void* stream) {
   return predict_impl(X, trees, n_nodes, n_trees, tree_stride, base_score, learning_rate, out, ws,
                       ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int gbdt_predict_noalloc(const gbdt_matrix* X, const gbdt_node* trees, const int32_t* n_nodes,
+                         int32_t n_trees, int32_t tree_stride, double base_score,
+                         double learning_rate, double* out, int32_t* status, void* stream) {
+  if (!status) return fail(GBDT_E_ARG, "status is null");
+  if (n_trees < 0 || tree_stride < 1) return fail(GBDT_E_ARG, "n_trees or tree_stride out of range");
+  const size_t need = gbdt_predict_workspace_bytes(n_trees, tree_stride);
+  if (need > kNoAllocBytes)
+    return fail(GBDT_E_ARG, "n_trees * tree_stride needs " + std::to_string(need) +
+                                " bytes of scratch; gbdt_predict_noalloc holds " +
+                                std::to_string(kNoAllocBytes) + " (use gbdt_predict with a workspace)");
+  void* ws = nullptr;
+  int rc = scratch_ptr(&ws);
+  if (rc) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  WsCtrl* ctrl = static_cast<WsCtrl*>(ws);
+  hipLaunchKernelGGL(k_clear_ctrl, dim3(1), dim3(64), 0, s, ctrl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "k_clear_ctrl");
+  rc = predict_impl(X, trees, n_nodes, n_trees, tree_stride, base_score, learning_rate, out, ws,
+                    kNoAllocBytes, s);
+  if (rc) return rc;
+  hipLaunchKernelGGL(k_copy_status, dim3(1), dim3(64), 0, s, ctrl, status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "k_copy_status");
+  return GBDT_OK;
 }
 
 }  // extern "C"

@@ -434,6 +434,26 @@ int gbdt_predict(const gbdt_matrix* X /* host */, const gbdt_node* trees, const 
                  int32_t n_trees, int32_t tree_stride, double base_score, double learning_rate,
                  double* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * gbdt_predict for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and the same bits as gbdt_predict, with the
+ * workspace replaced by a scratch area the library holds on each GPU
+ * (16 MiB: gbdt_predict_workspace_bytes(n_trees, tree_stride) must not
+ * exceed 16777216, else GBDT_E_ARG before anything is enqueued).  The call
+ * allocates nothing.  The current device must be the one stream runs on.
+ * status: device int32, written at the end of the call with 0 or the
+ * device-side error code (GBDT_E_ARG for a malformed tree, in which case out
+ * is not written).  Every call on one GPU shares that GPU's scratch, which
+ * starts each call cleared: calls that may overlap on one GPU (different
+ * streams, or different host threads) race and must be serialised by the
+ * caller.
+ */
+int gbdt_predict_noalloc(const gbdt_matrix* X /* host */, const gbdt_node* trees,
+                         const int32_t* n_nodes, int32_t n_trees, int32_t tree_stride,
+                         double base_score, double learning_rate, double* out, int32_t* status,
+                         void* stream);
+
 /* ------------------------------------------------------ level-wise driver -- */
 
 /*
