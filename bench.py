@@ -80,7 +80,7 @@ DIAG_PARTITION = 10
 DIAG_UPDATE = 11
 
 
-def other_rooflines(trees, kt, n, max_depth):
+def other_rooflines(trees, kt, n, max_depth, workload_name):
     """HBM rooflines of the partition, the prediction update and the split
     search over the same timed trees, with the algorithmic bytes of each step
     (per row of a splitting node: 4 B row index read + 1 B bin + 4 B index
@@ -108,17 +108,22 @@ def other_rooflines(trees, kt, n, max_depth):
                 "ms_per_tree": t / K}
 
     out["partition"] = entry(DIAG_PARTITION, "k_partition", part_rows * 25)
+    if out["partition"] is not None:
+        out["partition"]["traffic"] = profiled_traffic(workload_name, "k_partition")
     # two launches per update (the tree compaction, then the row walk)
     out["update"] = entry(DIAG_UPDATE, "k_compact_tree + k_update", K * n * 20, units=K)
     return out
 
 
 def profiled_traffic(workload_name, kernel="k_hist"):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary of this workload, if it was taken on the current kernel source;
-    else None."""
+    """HBM bytes per launch of `kernel` (k_hist: with its reduction) from the
+    committed rocprofv3 counter summary of this workload, if it was taken on
+    the current kernel source; else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "%s_%s_counters.txt" % (kernel, workload_name))
+    if workload_name.startswith("binning"):
+        path = os.path.join(ROOT, "profiles", "%s_%s_counters.txt" % (kernel, workload_name))
+    else:
+        path = os.path.join(ROOT, "profiles", "gbdt_tree_%s_counters.txt" % workload_name)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -134,7 +139,9 @@ def profiled_traffic(workload_name, kernel="k_hist"):
     if fields.get("kernel_source_sha256") != h.hexdigest()[:16]:
         return None
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        if workload_name.startswith("binning"):
+            return float(fields["traffic_bytes_per_launch"])
+        return float(fields["traffic_%s" % kernel])
     except (KeyError, ValueError):
         return None
 
@@ -275,7 +282,7 @@ def measure(g, datagen, torch, k, K, W, diag):
                            "k_hist_reduce_avg_us": 1000.0 * red_ms / max(red_launches, 1),
                            "k_hist_reduce_launches": red_launches,
                            "k_hist_only_frac": alg_bytes / (hist_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        out["rooflines"] = other_rooflines(trees, kt, n, params.max_depth)
+        out["rooflines"] = other_rooflines(trees, kt, n, params.max_depth, wl["name"])
         names = {1: "grad_max", 2: "grad_q", 3: "plan", 4: "hist", 5: "hist_reduce", 6: "subtract",
                  7: "find", 8: "tree_init", 9: "level", 10: "partition", 11: "update", 12: "pack"}
         out["device_ms_per_tree"] = {names.get(int(kk), str(kk)): kt[kk][0] / K for kk in sorted(kt)}
