@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libgbdt_hip.so")
 
 GBDT_OK = 0
 GBDT_NODE_LEAF = 1
+OBJECTIVE_SQUARED_ERROR = 0
+OBJECTIVE_LOGISTIC = 1
 GBDT_MAX_DEPTH = 16
 STATUS_NAMES = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "RANGE", -4: "OVERFLOW", -5: "DEVICE",
                 -6: "UNSUPPORTED", -7: "INTERNAL"}
@@ -29,7 +31,7 @@ STATUS_NAMES = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "RANGE", -4: "OVERFLOW", -5
 NODE_DTYPE = np.dtype([
     ("feature", "<i4"), ("threshold_bin", "<i4"), ("left", "<i4"), ("right", "<i4"),
     ("leaf_value", "<f8"), ("gain", "<f8"), ("flags", "<u4"), ("depth", "<i4"),
-    ("begin", "<i4"), ("count", "<i4"), ("gsum", "<i8"), ("reserved", "<i8"),
+    ("begin", "<i4"), ("count", "<i4"), ("gsum", "<i8"), ("hsum", "<i8"),
 ])
 assert NODE_DTYPE.itemsize == 64
 SPLIT_DTYPE = np.dtype([
@@ -70,12 +72,13 @@ class Rows(ctypes.Structure):
 class Params(ctypes.Structure):
     _fields_ = [("reg_lambda", ctypes.c_double), ("gamma", ctypes.c_double),
                 ("min_child_weight", ctypes.c_double), ("learning_rate", ctypes.c_double),
-                ("min_samples_leaf", i32), ("max_depth", i32)]
+                ("min_samples_leaf", i32), ("max_depth", i32), ("objective", i32), ("pad", i32)]
 
 
 class GrowBuffers(ctypes.Structure):
     _fields_ = [("pp", Rows * 2), ("q", vp), ("hist_g", vp), ("hist_cnt", vp), ("splits", vp),
-                ("lists", vp), ("ctrl", vp), ("ws", vp), ("ws_bytes", ctypes.c_size_t)]
+                ("lists", vp), ("ctrl", vp), ("ws", vp), ("ws_bytes", ctypes.c_size_t),
+                ("qh", vp), ("hist_h", vp), ("split_h", vp)]
 
 
 class GrowSizes(ctypes.Structure):
@@ -162,9 +165,9 @@ def _stream(stream=None):
 
 
 def make_params(max_depth, reg_lambda=1.0, gamma=0.0, min_child_weight=0.0, learning_rate=0.3,
-                min_samples_leaf=1, **_ignored) -> Params:
+                min_samples_leaf=1, objective=OBJECTIVE_SQUARED_ERROR, **_ignored) -> Params:
     return Params(float(reg_lambda), float(gamma), float(min_child_weight), float(learning_rate),
-                  int(min_samples_leaf), int(max_depth))
+                  int(min_samples_leaf), int(max_depth), int(objective), 0)
 
 
 # ----------------------------------------------------------- host-only calls --
@@ -427,8 +430,14 @@ class Booster:
         sz = gbdt_grow_sizes(n, TB, D)
         self.sizes = sz
         self.pred = torch.full((n,), float(base_score), dtype=torch.float64, device=device)
-        self.pp = [RowBuffer(ds.ft, n, device, with_rid=False), RowBuffer(ds.ft, n, device, with_rid=False)]
+        logistic = int(params.objective) == OBJECTIVE_LOGISTIC
+        # (the logistic objective's Hessians ride in the row buffers' rid arrays)
+        self.pp = [RowBuffer(ds.ft, n, device, with_rid=logistic),
+                   RowBuffer(ds.ft, n, device, with_rid=logistic)]
         self.q = torch.zeros(n, dtype=torch.int64, device=device)
+        self.qh = torch.zeros(n, dtype=torch.int32, device=device) if logistic else None
+        self.hist_h = torch.zeros(sz.hist_slots * TB, dtype=torch.int64, device=device) if logistic else None
+        self.split_h = torch.zeros(sz.max_nodes, dtype=torch.int64, device=device) if logistic else None
         self.hist_g = torch.zeros(sz.hist_slots * TB, dtype=torch.int64, device=device)
         self.hist_cnt = torch.zeros(sz.hist_slots * TB, dtype=torch.int32, device=device)
         self.splits = torch.zeros(sz.max_nodes * SPLIT_DTYPE.itemsize, dtype=torch.uint8, device=device)
@@ -440,7 +449,7 @@ class Booster:
         self._buf = GrowBuffers(
             (Rows * 2)(self.pp[0].rows(), self.pp[1].rows()), _ptr(self.q), _ptr(self.hist_g),
             _ptr(self.hist_cnt), _ptr(self.splits), _ptr(self.lists), _ptr(self.ctrl), _ptr(self.ws),
-            self.ws.numel())
+            self.ws.numel(), _ptr(self.qh), _ptr(self.hist_h), _ptr(self.split_h))
         self._X = ds.X.matrix()
         self._ft = ds.ft.struct(ds.use_skip_bins)
 

@@ -32,6 +32,8 @@ struct TreeCtrl {
   int32_t scale;
   int32_t n_leaves;
   int64_t gsum_root;
+  int32_t scale_h;  // the logistic objective's Hessian grid (0 otherwise)
+  int32_t pad0;
   int32_t level_start[GBDT_MAX_DEPTH + 2];
   int32_t level_count[GBDT_MAX_DEPTH + 2];
   int32_t n_build[GBDT_MAX_DEPTH + 2];
@@ -75,9 +77,13 @@ struct PlanArgs {
   int32_t n_features;
 };
 
-__device__ __forceinline__ double leaf_weight(int64_t gsum, int32_t count, int32_t S, double lambda) {
+// -G / (H + lambda), with H the row count (squared error, h = 1) or, for the
+// logistic objective (hess), the node's Hessian sum on its grid Sh.
+__device__ __forceinline__ double leaf_weight(int64_t gsum, int32_t count, int64_t hsum, int32_t S,
+                                              int32_t Sh, bool hess, double lambda) {
   const double G = ldexp((double)gsum, -S);
-  const double den = (double)count + lambda;
+  const double H = hess ? ldexp((double)hsum, -Sh) : (double)count;
+  const double den = H + lambda;
   return -G / den;
 }
 
@@ -103,9 +109,11 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
                                                     int32_t max_tiles,
                                                     const int64_t* __restrict__ psum,
                                                     int32_t nparts,
-                                                    const int32_t* __restrict__ guard) {
+                                                    const int32_t* __restrict__ guard,
+                                                    const int64_t* __restrict__ psum_h) {
   __shared__ PlanLds lds;
   __shared__ int64_t s_part[1024 / 64];
+  __shared__ int64_t s_parth[1024 / 64];
   // after an error (e.g. a non-finite gradient) the tree is not started: it
   // has no nodes, and the later kernels of the tree do nothing
   if (failed(guard)) {
@@ -114,10 +122,17 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
   }
   // the root's sum of q from the gradient kernels' per-block partial sums
   {
-    int64_t v = 0;
-    for (int i = threadIdx.x; i < nparts; i += blockDim.x) v += psum[i];
+    int64_t v = 0, vh = 0;
+    for (int i = threadIdx.x; i < nparts; i += blockDim.x) {
+      v += psum[i];
+      if (psum_h != nullptr) vh += psum_h[i];
+    }
     v = wave_sum(v);
-    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = v;
+    vh = wave_sum(vh);
+    if ((threadIdx.x & 63) == 0) {
+      s_part[threadIdx.x >> 6] = v;
+      s_parth[threadIdx.x >> 6] = vh;
+    }
   }
   for (int i = threadIdx.x; i < GBDT_MAX_DEPTH + 2; i += blockDim.x) {
     tc->level_start[i] = 0;
@@ -140,17 +155,20 @@ __global__ void __launch_bounds__(1024) k_tree_init(gbdt_node* __restrict__ node
     r.depth = 0;
     r.begin = 0;
     r.count = n;
-    int64_t gs = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) gs += s_part[w];
+    int64_t gs = 0, hs = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      gs += s_part[w];
+      hs += s_parth[w];
+    }
     tc->gsum_root = gs;
     r.gsum = gs;
-    r.reserved = 0;
+    r.hsum = hs;
     tc->level_start[0] = 0;
     tc->level_count[0] = 1;
     tc->n_leaves = 0;
     splits[0].valid = 0;
     if (D == 0) {
-      make_leaf(&r, leaf_weight(r.gsum, n, tc->scale, lambda));
+      make_leaf(&r, leaf_weight(r.gsum, n, r.hsum, tc->scale, tc->scale_h, psum_h != nullptr, lambda));
       lists[LL.leaves] = 0;
       tc->n_leaves = 1;
     } else if (grow) {
@@ -185,7 +203,8 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t hist_tile_max,
                                                 int32_t hist_target, int32_t hist_min_rows,
                                                 int32_t hist_max_tiles_next,
-                                                const int32_t* __restrict__ guard) {
+                                                const int32_t* __restrict__ guard,
+                                                const int64_t* __restrict__ split_h) {
   __shared__ PlanLds lds;
   __shared__ int32_t shm[6 * 17];
   // after an error nothing of the level is written, and the partition that
@@ -200,6 +219,8 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   const int32_t first = tc->level_start[d];
   const int32_t cnt = tc->level_count[d];
   const int32_t S = tc->scale;
+  const int32_t Sh = tc->scale_h;
+  const bool hess = split_h != nullptr;  // the logistic objective
   const int32_t leaf_base = tc->n_leaves;
   const int32_t child_first = first + cnt;
   const bool last = (d + 1 == D);
@@ -317,10 +338,11 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
       R.begin = nd.begin + nl;
       R.count = nr;
       R.gsum = nd.gsum - s.g_left;
-      L.reserved = R.reserved = 0;
+      L.hsum = hess ? split_h[v] : 0;
+      R.hsum = hess ? nd.hsum - L.hsum : 0;
       if (last) {
-        make_leaf(&L, leaf_weight(L.gsum, L.count, S, lambda));
-        make_leaf(&R, leaf_weight(R.gsum, R.count, S, lambda));
+        make_leaf(&L, leaf_weight(L.gsum, L.count, L.hsum, S, Sh, hess, lambda));
+        make_leaf(&R, leaf_weight(R.gsum, R.count, R.hsum, S, Sh, hess, lambda));
         leaves[leaf_base + r_leaf] = lc;
         leaves[leaf_base + r_leaf + 1] = rc;
         r_leaf += 2;
@@ -359,7 +381,7 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
       split_list[r_split] = v;
       ++r_split;
     } else {
-      make_leaf(&nd, leaf_weight(nd.gsum, nd.count, S, lambda));
+      make_leaf(&nd, leaf_weight(nd.gsum, nd.count, nd.hsum, S, Sh, hess, lambda));
       nodes[v] = nd;
       leaves[leaf_base + r_leaf] = v;
       ++r_leaf;
@@ -398,8 +420,12 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   }
 }
 
+// Nodes of fewer rows than this cannot split: each child needs
+// min_samples_leaf rows and, for squared error (H = count), a Hessian of
+// min_child_weight.  The logistic objective's Hessian is not a count, so only
+// min_samples_leaf bounds it there.
 static int64_t min_split_count(const gbdt_params* p, int64_t n) {
-  double mc = std::ceil(p->min_child_weight);
+  double mc = p->objective == GBDT_OBJECTIVE_LOGISTIC ? 0.0 : std::ceil(p->min_child_weight);
   int64_t m = p->min_samples_leaf;
   if (mc > double(n) + 1.0) return 2 * (n + 1);
   if (int64_t(mc) > m) m = int64_t(mc);
@@ -439,11 +465,15 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   if (ft->n_features != X->n_features) return fail(GBDT_E_SHAPE, "feature table does not match the matrix");
   if (!b->q || !b->hist_g || !b->hist_cnt || !b->splits || !b->lists || !b->ctrl || !b->ws)
     return fail(GBDT_E_ARG, "a driver buffer is null");
+  const bool logistic = p->objective == GBDT_OBJECTIVE_LOGISTIC;
   for (int k = 0; k < 2; ++k) {
     const gbdt_rows& r = b->pp[k];
     if (!r.X.bins || !r.q) return fail(GBDT_E_ARG, "a row buffer is null");
     if (!same_layout(r.X, *X)) return fail(GBDT_E_SHAPE, "row buffers must have the layout of X");
+    if (logistic && !r.rid) return fail(GBDT_E_ARG, "the logistic objective needs the row buffers' rid");
   }
+  if (logistic && (!b->qh || !b->hist_h || !b->split_h))
+    return fail(GBDT_E_ARG, "the logistic objective needs qh, hist_h and split_h");
   const int32_t D = p->max_depth;
   gbdt_grow_sizes_t sz;
   rc = gbdt_grow_sizes(n, ft->total_bins, D, &sz);
@@ -453,7 +483,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   gbdt_rows src;
   src.X = *X;
   src.q = b->q;
-  src.rid = nullptr;
+  // the logistic objective's Hessians travel with the rows in the rid slot
+  src.rid = logistic ? b->qh : nullptr;
   rc = check_hist_inputs(src, *ft);
   if (rc) return rc;
   rc = check_partition_inputs(b->pp[0], b->pp[1]);
@@ -485,8 +516,9 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   // `target` tiles of at least min(min_rows, tile_max) rows, at most
   // tile_max); the bound below holds for every size it can choose
   const int32_t tile_max = hist_tile_max(n);
-  // q is int32 (original order and both row buffers) when that is exact
-  const bool q32 = driver_q32(n);
+  // q is int32 (original order and both row buffers) when that is exact:
+  // always for the logistic objective's 31-bit grids
+  const bool q32 = logistic || driver_q32(n);
   const int32_t part_tile = part_tile_rows(n, X->n_blocks, q32);
   const int32_t target = hist_target_tiles(X->n_blocks + (X->n_bit_features > 0 ? 1 : 0));
   const int32_t min_rows =
@@ -513,13 +545,18 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   const int32_t* guard = &pa.ctrl->err;
   // (the sum of q stays as per-block partial sums; k_tree_init adds them)
   double* gpart = reinterpret_cast<double*>(w + WL.gpart);
-  rc = launch_gradients(pred, label, n, b->q, q32, &tc->scale, nullptr, gpart, pa.ctrl, s);
+  if (logistic)
+    rc = launch_gradients_logistic(pred, label, n, reinterpret_cast<int32_t*>(b->q), b->qh, &tc->scale,
+                                   &tc->scale_h, gpart, pa.ctrl, s);
+  else
+    rc = launch_gradients(pred, label, n, b->q, q32, &tc->scale, nullptr, gpart, pa.ctrl, s);
   if (rc) return rc;
   diag_begin(kDiagTreeInit, s);
   hipLaunchKernelGGL(k_tree_init, dim3(1), dim3(1024), 0, s, nodes_out, b->splits, tc, b->lists, LL,
                      (int32_t)n, min_split, D, p->reg_lambda, n_nodes_dev, pa, h_rows[0],
                      (int32_t)h_tiles[0],
-                     reinterpret_cast<const int64_t*>(gpart + kGradBlocks), grad_blocks(n), guard);
+                     reinterpret_cast<const int64_t*>(gpart + kGradBlocks), grad_blocks(n), guard,
+                     logistic ? reinterpret_cast<const int64_t*>(gpart + 3 * kGradBlocks) : nullptr);
   diag_end(s);
   {
     hipError_t e = hipGetLastError();
@@ -537,15 +574,30 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
                             h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s, guard);
     if (rc) return rc;
+    if (logistic) {
+      // the Hessian histograms: the same kernels over the same tile plan with
+      // the Hessians (the rows' rid slot) as the summed value; the counts they
+      // write are the same ones again
+      gbdt_rows hs = src;
+      hs.q = reinterpret_cast<int64_t*>(src.rid);
+      rc = launch_hist(hs, *ft, pa.hdesc, h_tiles[d], b->hist_h, b->hist_cnt, hpart, pa.ctrl, s, true,
+                       true);
+      if (rc) return rc;
+      rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
+                              h_tiles[d], n, ft->total_bins, hpart, b->hist_h, b->hist_cnt, s, guard);
+      if (rc) return rc;
+    }
     rc = launch_find(b->hist_g, b->hist_cnt, *ft, nodes_out, b->lists + LL.find + lvl_off,
                      &tc->n_find[d], cap_lvl, *p, &tc->scale, b->splits,
                      b->lists + LL.find_par + lvl_off, b->lists + LL.find_sib + lvl_off, pa.ctrl, s,
-                     reinterpret_cast<FindCand*>(w + WL.fcand), guard);
+                     reinterpret_cast<FindCand*>(w + WL.fcand), guard, logistic ? b->hist_h : nullptr,
+                     &tc->scale_h, b->split_h);
     if (rc) return rc;
     diag_begin(kDiagLevel, s);
     hipLaunchKernelGGL(k_level, dim3(1), dim3(1024), 0, s, d, D, nodes_out, b->splits, tc, b->lists,
                        LL, min_split, p->reg_lambda, n_nodes_dev, pa, part_tile, (int32_t)p_tiles[d],
-                       tile_max, target, min_rows, (int32_t)h_tiles[d + 1], guard);
+                       tile_max, target, min_rows, (int32_t)h_tiles[d + 1], guard,
+                       logistic ? b->split_h : nullptr);
     diag_end(s);
     {
       hipError_t e = hipGetLastError();

@@ -24,8 +24,9 @@ struct FindCand {
   double gain;
   int32_t key, feature, threshold_bin, n_left;
   int64_t g_left;
+  int64_t h_left;  // the logistic objective's left Hessian sum (0 otherwise)
 };
-static_assert(sizeof(FindCand) == 32, "candidate record is 32 bytes");
+static_assert(sizeof(FindCand) == 40, "candidate record is 40 bytes");
 
 // Workspace layout.  Offsets are multiples of 256 bytes.
 struct WsCtrl {
@@ -108,7 +109,8 @@ struct WsLayout {
   size_t ctrl;        // WsCtrl
   size_t tdesc;       // TileDesc[tdesc_cap]: partition plan
   size_t hdesc;       // TileDesc[hpart_tiles]: histogram plan
-  size_t gpart;       // double[kGradBlocks] maxima, then int64[kGradBlocks] sums
+  size_t gpart;       // double[kGradBlocks] maxima, then int64[kGradBlocks] sums; the
+                      // logistic objective's Hessian maxima and sums follow
   size_t prefix;      // int32[max_list + 2]: partition plan
   size_t hprefix;     // int32[max_list + 2]: histogram plan
   size_t hmulti;      // int32[max_list + 2]: histogram plan, nodes of several tiles
@@ -197,11 +199,14 @@ int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_c
                        const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
                        const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s,
                        const int32_t* guard = nullptr);
+// hist_h / scale_h / split_h: the logistic objective's Hessian histograms,
+// grid and per-split left Hessian sums (nullptr for squared error, H = count).
 int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,
                 const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
                 const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
                 const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s, FindCand* cand = nullptr,
-                const int32_t* guard = nullptr);
+                const int32_t* guard = nullptr, int64_t* hist_h = nullptr,
+                const int32_t* scale_h = nullptr, int64_t* split_h = nullptr);
 // qin32 / qout32: src.q / dst.q hold int32 elements (the tree driver's row
 // buffers); otherwise int64.
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
@@ -221,6 +226,12 @@ inline int32_t grad_blocks(int64_t n) {
 // at part + kGradBlocks (the tree driver adds them up itself).
 int launch_gradients(const double* pred, const float* label, int64_t n, void* q, bool q32,
                      int32_t* scale, int64_t* gsum, double* part, WsCtrl* ctrl, hipStream_t s);
+// The logistic objective's gradients and Hessians (int32 each, see gbdt.h):
+// part as above with the Hessian maxima at part + 2 kGradBlocks and their
+// per-block sums after them; the sums stay as per-block partials.
+int launch_gradients_logistic(const double* pred, const float* label, int64_t n, int32_t* q,
+                              int32_t* qh, int32_t* scale, int32_t* scale_h, double* part,
+                              WsCtrl* ctrl, hipStream_t s);
 
 // Whether the tree driver stores q as int32 (in its original-order buffer and
 // its two row buffers): exact when every |q| <= 2^(52 - ceil(log2 n)) fits 31

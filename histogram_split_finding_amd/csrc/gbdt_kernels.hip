@@ -88,7 +88,7 @@ WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
   L.hdesc = off;
   off = align256(off + sizeof(TileDesc) * size_t(L.hpart_tiles));
   L.gpart = off;
-  off = align256(off + (sizeof(double) + sizeof(int64_t)) * kGradBlocks);
+  off = align256(off + 2 * (sizeof(double) + sizeof(int64_t)) * kGradBlocks);
   L.prefix = off;
   off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
   L.hprefix = off;
@@ -275,6 +275,182 @@ __global__ void __launch_bounds__(kGradBlocks) k_grad_sum(const int64_t* __restr
     int64_t t = 0;
     for (int w = 0; w < kGradBlocks / 64; ++w) t += sh[w];
     *gsum = t;
+  }
+}
+
+// ------------------------------------------------- logistic objective --
+// e^x for -700 <= x <= 0 (0 below -700): Cody and Waite's argument reduction,
+// x = k ln 2 + r with k = rint(x / ln 2) and r = (x - k LN2_HI) - k LN2_LO
+// (LN2_HI: the first 42 significant bits of ln 2, so k LN2_HI is exact;
+// LN2_LO: the rest, rounded), then e^r by its Taylor series to degree 13
+// (|r| <= ln(2)/2, the first omitted term below 2^-57 of the sum) in Horner
+// form from the highest power, and e^x = 2^k e^r.  One IEEE FP64 operation at
+// a time (no contraction in this library), so any IEEE host computing the
+// same sequence gets the same bits.
+__device__ __forceinline__ double exp_nonpos(double x) {
+  if (x < -700.0) return 0.0;
+  constexpr double kInvLn2 = 0x1.71547652b82fep+0;
+  constexpr double kLn2Hi = 0x1.62e42fefa3800p-1;
+  constexpr double kLn2Lo = 0x1.ef35793c76730p-45;
+  // 1/j! for j = 13 .. 0, each correctly rounded
+  constexpr double kInvFact[14] = {
+      0x1.6124613a86d09p-33, 0x1.1eed8eff8d898p-29, 0x1.ae64567f544e4p-26, 0x1.27e4fb7789f5cp-22,
+      0x1.71de3a556c734p-19, 0x1.a01a01a01a01ap-16, 0x1.a01a01a01a01ap-13, 0x1.6c16c16c16c17p-10,
+      0x1.1111111111111p-7,  0x1.5555555555555p-5,  0x1.5555555555555p-3,  0x1.0000000000000p-1,
+      0x1.0000000000000p+0,  0x1.0000000000000p+0};
+  const double k = rint(x * kInvLn2);
+  const double r = (x - k * kLn2Hi) - k * kLn2Lo;
+  double p = kInvFact[0];
+#pragma unroll
+  for (int j = 1; j < 14; ++j) p = p * r + kInvFact[j];
+  return ldexp(p, (int)k);
+}
+
+// Sigmoid cross-entropy on the raw score p ("Gradient boosted trees (spec
+// model)", gbtBinaryCrossentropyGradSpec): g = sigmoid(p) - y, and the
+// second derivative h = sigmoid(p) (1 - sigmoid(p)) as the Hessian, both from
+// z = e^-|p| and d = 1 + z: sigmoid = 1/d for p >= 0, z/d otherwise;
+// h = z / (d d).
+__device__ __forceinline__ void logistic_gh(double p, double y, double& g, double& h) {
+  const double z = exp_nonpos(-fabs(p));
+  const double d = 1.0 + z;
+  const double s = p >= 0.0 ? 1.0 / d : z / d;
+  g = s - y;
+  h = z / (d * d);
+}
+
+// Pass 1 of the logistic objective: per-block max |g| and max h (a
+// non-finite prediction, label, g or h sets GBDT_E_RANGE).
+__global__ void __launch_bounds__(256) k_lgrad_max(const double* __restrict__ pred,
+                                                   const float* __restrict__ label, int64_t n,
+                                                   double* __restrict__ part_g,
+                                                   double* __restrict__ part_h,
+                                                   WsCtrl* __restrict__ ctrl) {
+  __shared__ double shg[4], shh[4];
+  double mg = 0.0, mh = 0.0;
+  bool bad = false;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i0 < n; i0 += 4 * stride) {
+    double p[4];
+    float l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      p[u] = i < n ? pred[i] : 0.0;
+      l[u] = i < n ? label[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // (rows past n are skipped: at p = 0 their h = 1/4 would enter the max)
+      if (i0 + u * stride >= n) continue;
+      if (!isfinite(p[u]) || !isfinite((double)l[u])) {
+        bad = true;
+        continue;
+      }
+      double g, h;
+      logistic_gh(p[u], (double)l[u], g, h);
+      if (!isfinite(g) || !isfinite(h)) bad = true;
+      mg = fmax(mg, fabs(g));
+      mh = fmax(mh, h);
+    }
+  }
+  if (bad) dev_error(&ctrl->err, GBDT_E_RANGE);
+  mg = wave_max(mg);
+  mh = wave_max(mh);
+  if ((threadIdx.x & 63) == 0) {
+    shg[threadIdx.x >> 6] = mg;
+    shh[threadIdx.x >> 6] = mh;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    part_g[blockIdx.x] = fmax(fmax(shg[0], shg[1]), fmax(shg[2], shg[3]));
+    part_h[blockIdx.x] = fmax(fmax(shh[0], shh[1]), fmax(shh[2], shh[3]));
+  }
+}
+
+// The logistic objective's grid exponent for a largest magnitude M: the
+// squared-error grid 52 - e - L, but at most 30 - e, so every fixed-point
+// value fits 31 bits (M < 2^e); 0 when M = 0.
+__device__ __forceinline__ int32_t logistic_scale(double M, int32_t log2n) {
+  if (!(M > 0.0)) return 0;
+  int e = 0;
+  (void)frexp(M, &e);
+  const int32_t S = 52 - e - log2n;
+  return S < 30 - e ? S : 30 - e;
+}
+
+// Pass 2: both grids from the partial maxima (every block derives the same
+// S and Sh), q = rint(ldexp(g, S)) and qh = rint(ldexp(h, Sh)) as int32, and
+// per-block sums of each.
+__global__ void __launch_bounds__(256) k_lgrad_q(const double* __restrict__ pred,
+                                                 const float* __restrict__ label, int64_t n,
+                                                 int32_t log2n, const double* __restrict__ part_g,
+                                                 const double* __restrict__ part_h, int32_t nparts,
+                                                 int32_t* __restrict__ q, int32_t* __restrict__ qh,
+                                                 int32_t* __restrict__ scale,
+                                                 int32_t* __restrict__ scale_h,
+                                                 int64_t* __restrict__ psum,
+                                                 int64_t* __restrict__ psum_h) {
+  __shared__ double shg[4], shh[4];
+  __shared__ int64_t ssg[4], ssh[4];
+  double mg = 0.0, mh = 0.0;
+#pragma unroll
+  for (int j = 0; j < kGradBlocks / 256; ++j) {
+    const int i = j * 256 + threadIdx.x;
+    if (i < nparts) {
+      mg = fmax(mg, part_g[i]);
+      mh = fmax(mh, part_h[i]);
+    }
+  }
+  mg = wave_max(mg);
+  mh = wave_max(mh);
+  if ((threadIdx.x & 63) == 0) {
+    shg[threadIdx.x >> 6] = mg;
+    shh[threadIdx.x >> 6] = mh;
+  }
+  __syncthreads();
+  const int32_t S = logistic_scale(fmax(fmax(shg[0], shg[1]), fmax(shg[2], shg[3])), log2n);
+  const int32_t Sh = logistic_scale(fmax(fmax(shh[0], shh[1]), fmax(shh[2], shh[3])), log2n);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *scale = S;
+    *scale_h = Sh;
+  }
+  int64_t sg = 0, sh = 0;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i0 < n; i0 += 4 * stride) {
+    double p[4];
+    float l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      p[u] = i < n ? pred[i] : 0.0;
+      l[u] = i < n ? label[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n) {
+        double g, h;
+        logistic_gh(p[u], (double)l[u], g, h);
+        const int32_t kg = (int32_t)rint(ldexp(g, S));
+        const int32_t kh = (int32_t)rint(ldexp(h, Sh));
+        q[i] = kg;
+        qh[i] = kh;
+        sg += kg;
+        sh += kh;
+      }
+    }
+  }
+  sg = wave_sum(sg);
+  sh = wave_sum(sh);
+  if ((threadIdx.x & 63) == 0) {
+    ssg[threadIdx.x >> 6] = sg;
+    ssh[threadIdx.x >> 6] = sh;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    psum[blockIdx.x] = ssg[0] + ssg[1] + ssg[2] + ssg[3];
+    psum_h[blockIdx.x] = ssh[0] + ssh[1] + ssh[2] + ssh[3];
   }
 }
 
@@ -940,6 +1116,21 @@ __device__ __forceinline__ void seg_scan_step(int32_t& fl, int64_t& g, int32_t& 
   }
 }
 
+// The same step with the logistic objective's Hessian sums as a third value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void seg_scan_step(int32_t& fl, int64_t& g, int32_t& c, int64_t& h) {
+  const int32_t fu = dpp_i32<CTRL, ROW_MASK>(fl);
+  const int64_t gu = dpp_i64<CTRL, ROW_MASK>(g);
+  const int32_t cu = dpp_i32<CTRL, ROW_MASK>(c);
+  const int64_t hu = dpp_i64<CTRL, ROW_MASK>(h);
+  if (!fl) {
+    g += gu;
+    c += cu;
+    h += hu;
+    fl = fu;
+  }
+}
+
 // Candidate order: larger gain, then larger key (key = INT32_MAX - global
 // bin, so the smaller feature and then the smaller threshold win).  The
 // empty candidate is (0.0, 0): all zero bits.  Gains compared here are only
@@ -971,7 +1162,11 @@ __device__ __forceinline__ void argmax_step(double& g, int32_t& key) {
 // is the larger child of a split pair: its histogram is the parent's minus
 // its built sibling's (exact integers), computed here and written to its own
 // slot for the next level; a negative count sets GBDT_E_INTERNAL.
-template <int THREADS, int E>
+// HESS (the logistic objective): H of a bin range is its sum of fixed-point
+// Hessians (hist_h, grid *scale_h) instead of its row count; the scan
+// carries it as a third value, the larger sibling's Hessian histogram is
+// derived like its G, and split_h[v] gets the winner's left Hessian sum.
+template <int THREADS, int E, bool HESS>
 __global__ void __launch_bounds__(THREADS) k_find(
     int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ bin_feature,
@@ -980,14 +1175,17 @@ __global__ void __launch_bounds__(THREADS) k_find(
     FindParams fp, const int32_t* __restrict__ scale, gbdt_split* __restrict__ splits,
     const int32_t* __restrict__ sub_par, const int32_t* __restrict__ sub_sib,
     int32_t* __restrict__ err, int32_t n_chunks, FindCand* __restrict__ cand,
-    const int32_t* __restrict__ guard) {
+    const int32_t* __restrict__ guard, int64_t* __restrict__ hist_h,
+    const int32_t* __restrict__ scale_h, int64_t* __restrict__ split_h) {
   constexpr int NW = THREADS / 64;
   if (failed(guard)) return;
   __shared__ int64_t sw_g[NW];
   __shared__ int32_t sw_c[NW];
   __shared__ int32_t sw_f[NW];
+  __shared__ int64_t sw_h[HESS ? NW : 1];
   __shared__ int64_t s_carry_g;
   __shared__ int32_t s_carry_c;
+  __shared__ int64_t s_carry_h;
   __shared__ double r_gain[NW];
   __shared__ int32_t r_key[NW];
   const int lane = threadIdx.x & 63;
@@ -1035,15 +1233,21 @@ __global__ void __launch_bounds__(THREADS) k_find(
   const uint32_t* __restrict__ hc_p = hist_cnt + int64_t(derive ? par : v) * total_bins;
   const int64_t* __restrict__ hg_s = hist_g + int64_t(derive ? sib : v) * total_bins;
   const uint32_t* __restrict__ hc_s = hist_cnt + int64_t(derive ? sib : v) * total_bins;
+  // the Hessian histograms (HESS only)
+  int64_t* __restrict__ hh = HESS ? hist_h + int64_t(v) * total_bins : nullptr;
+  const int64_t* __restrict__ hh_p = HESS ? hist_h + int64_t(derive ? par : v) * total_bins : nullptr;
+  const int64_t* __restrict__ hh_s = HESS ? hist_h + int64_t(derive ? sib : v) * total_bins : nullptr;
+  const int32_t Sh = HESS ? *scale_h : 0;
   bool bad = false;
 
   double best_gain = 0.0;
   int32_t best_key = 0;
   int32_t best_thr = -1, best_f = -1, best_nl = 0;
-  int64_t best_gl = 0;
+  int64_t best_gl = 0, best_hl = 0;
   if (threadIdx.x == 0) {
     s_carry_g = 0;
     s_carry_c = 0;
+    s_carry_h = 0;
   }
   for (int32_t pass = blo; pass < bhi; pass += THREADS * E) {
     const int32_t b0 = pass + threadIdx.x * E;
@@ -1058,6 +1262,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
     }
     int64_t g[E];
     int32_t c[E];
+    int64_t h[E];
     int32_t fo[E];  // first global bin of the feature of bin b0 + e
     if (derive) {
 #pragma unroll
@@ -1068,6 +1273,10 @@ __global__ void __launch_bounds__(THREADS) k_find(
         g[e] = inb ? hg_p[b] - hg_s[b] : 0;
         c[e] = (int32_t)(cp - cs);
         bad |= cs > cp;
+        if constexpr (HESS) {
+          h[e] = inb ? hh_p[b] - hh_s[b] : 0;
+          bad |= h[e] < 0;
+        }
         fo[e] = bin_offset[inb ? f[e + 1] : 0];
       }
     } else {
@@ -1077,16 +1286,17 @@ __global__ void __launch_bounds__(THREADS) k_find(
         const bool inb = b < bhi;
         g[e] = inb ? hg[b] : 0;
         c[e] = inb ? (int32_t)hc[b] : 0;
+        if constexpr (HESS) h[e] = inb ? hh[b] : 0;
         fo[e] = bin_offset[inb ? f[e + 1] : 0];
       }
     }
     const double Gv = ldexp((double)nd.gsum, -S);
-    const double Hv = (double)nd.count;
+    const double Hv = HESS ? ldexp((double)nd.hsum, -Sh) : (double)nd.count;
     const double sP = score_of(Gv, Hv, fp.lambda);
     const int64_t nv = nd.count;
     // serial segmented scan inside the thread
     int32_t first_head = E;
-    int64_t rg = 0;
+    int64_t rg = 0, rh = 0;
     int32_t rc = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -1096,49 +1306,70 @@ __global__ void __launch_bounds__(THREADS) k_find(
       rc = head ? c[e] : rc + c[e];
       g[e] = rg;
       c[e] = rc;
+      if constexpr (HESS) {
+        rh = head ? h[e] : rh + h[e];
+        h[e] = rh;
+      }
     }
     // segmented scan of the thread tails across the wave (DPP row shifts,
     // then rows 0 -> 1, 2 -> 3, row 1 -> rows 2 and 3)
     int32_t fl = first_head < E ? 1 : 0;
-    int64_t wg = rg;
+    int64_t wg = rg, wh = rh;
     int32_t wc = rc;
-    seg_scan_step<0x111, 0xF>(fl, wg, wc);  // row_shr:1
-    seg_scan_step<0x112, 0xF>(fl, wg, wc);  // row_shr:2
-    seg_scan_step<0x114, 0xF>(fl, wg, wc);  // row_shr:4
-    seg_scan_step<0x118, 0xF>(fl, wg, wc);  // row_shr:8
-    seg_scan_step<0x142, 0xA>(fl, wg, wc);  // row_bcast:15
-    seg_scan_step<0x143, 0xC>(fl, wg, wc);  // row_bcast:31
+    if constexpr (HESS) {
+      seg_scan_step<0x111, 0xF>(fl, wg, wc, wh);
+      seg_scan_step<0x112, 0xF>(fl, wg, wc, wh);
+      seg_scan_step<0x114, 0xF>(fl, wg, wc, wh);
+      seg_scan_step<0x118, 0xF>(fl, wg, wc, wh);
+      seg_scan_step<0x142, 0xA>(fl, wg, wc, wh);
+      seg_scan_step<0x143, 0xC>(fl, wg, wc, wh);
+    } else {
+      seg_scan_step<0x111, 0xF>(fl, wg, wc);  // row_shr:1
+      seg_scan_step<0x112, 0xF>(fl, wg, wc);  // row_shr:2
+      seg_scan_step<0x114, 0xF>(fl, wg, wc);  // row_shr:4
+      seg_scan_step<0x118, 0xF>(fl, wg, wc);  // row_shr:8
+      seg_scan_step<0x142, 0xA>(fl, wg, wc);  // row_bcast:15
+      seg_scan_step<0x143, 0xC>(fl, wg, wc);  // row_bcast:31
+    }
     if (lane == 63) {
       sw_g[wid] = wg;
       sw_c[wid] = wc;
       sw_f[wid] = fl;
+      if constexpr (HESS) sw_h[wid] = wh;
     }
     __syncthreads();
     int64_t cgw = s_carry_g;  // open segment entering this wave
     int32_t ccw = s_carry_c;
+    int64_t chw = HESS ? s_carry_h : 0;
     for (int w = 0; w < wid; ++w) {
       if (sw_f[w]) {
         cgw = sw_g[w];
         ccw = sw_c[w];
+        if constexpr (HESS) chw = sw_h[w];
       } else {
         cgw += sw_g[w];
         ccw += sw_c[w];
+        if constexpr (HESS) chw += sw_h[w];
       }
     }
     const int64_t incl_g = fl ? wg : cgw + wg;  // open segment at this thread's end
     const int32_t incl_c = fl ? wc : ccw + wc;
+    const int64_t incl_h = fl ? wh : chw + wh;
     // the open segment entering this thread: the previous lane's, or the
     // wave's carry in lane 0 (wave_shr:1 gives lane 0 a zero)
     int64_t cin_g = dpp_i64<0x138, 0xF>(incl_g);
     int32_t cin_c = dpp_i32<0x138, 0xF>(incl_c);
+    int64_t cin_h = HESS ? dpp_i64<0x138, 0xF>(incl_h) : 0;
     if (lane == 0) {
       cin_g = cgw;
       cin_c = ccw;
+      cin_h = chw;
     }
     __syncthreads();
     if (threadIdx.x == THREADS - 1) {
       s_carry_g = incl_g;
       s_carry_c = incl_c;
+      if constexpr (HESS) s_carry_h = incl_h;
     }
     // candidates: bin b with its right neighbour in the same feature
 #pragma unroll
@@ -1147,11 +1378,12 @@ __global__ void __launch_bounds__(THREADS) k_find(
       if (b >= bhi) break;
       const int64_t gl = e < first_head ? g[e] + cin_g : g[e];
       const int32_t nlc = e < first_head ? c[e] + cin_c : c[e];
+      const int64_t hl = HESS ? (e < first_head ? h[e] + cin_h : h[e]) : 0;
       if (f[e + 2] != f[e + 1]) continue;
       const int64_t nl = nlc;
       const int64_t nr = nv - nl;
       const double GL = ldexp((double)gl, -S);
-      const double HL = (double)nl;
+      const double HL = HESS ? ldexp((double)hl, -Sh) : (double)nl;
       const double GR = Gv - GL;
       const double HR = Hv - HL;
       if (nl >= fp.msl && nr >= fp.msl && HL >= fp.mcw && HR >= fp.mcw && HL > 0.0 && HR > 0.0) {
@@ -1166,6 +1398,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
           best_gain = gain;
           best_key = key;
           best_gl = gl;
+          best_hl = hl;
           best_nl = nlc;
           best_f = f[e + 1];
           best_thr = b - fo[e];
@@ -1183,6 +1416,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
           const bool head = e == 0 || f[e] != f[e + 1];
           hg[b] = head ? g[e] : g[e] - g[e - 1 < 0 ? 0 : e - 1];
           hc[b] = (uint32_t)(head ? c[e] : c[e] - c[e - 1 < 0 ? 0 : e - 1]);
+          if constexpr (HESS) hh[b] = head ? h[e] : h[e] - h[e - 1 < 0 ? 0 : e - 1];
         }
       }
     }
@@ -1223,6 +1457,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
         x.threshold_bin = best_thr;
         x.n_left = best_nl;
         x.g_left = best_gl;
+        x.h_left = best_hl;
         *c = x;
       }
     } else if (threadIdx.x == 0) {
@@ -1233,6 +1468,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
       x.threshold_bin = -1;
       x.n_left = 0;
       x.g_left = 0;
+      x.h_left = 0;
       *c = x;
     }
     return;
@@ -1248,6 +1484,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
       sp.n_left = best_nl;
       sp.valid = 1;
       splits[v] = sp;
+      if constexpr (HESS) split_h[v] = best_hl;
     }
   } else if (threadIdx.x == 0) {
     gbdt_split sp;
@@ -1258,6 +1495,7 @@ __global__ void __launch_bounds__(THREADS) k_find(
     sp.n_left = 0;
     sp.valid = 0;
     splits[v] = sp;
+    if constexpr (HESS) split_h[v] = 0;
   }
 }
 
@@ -1270,7 +1508,8 @@ __global__ void __launch_bounds__(64) k_find_merge(const int32_t* __restrict__ l
                                                    int32_t list_cap, int32_t n_chunks,
                                                    const FindCand* __restrict__ cand,
                                                    gbdt_split* __restrict__ splits,
-                                                   const int32_t* __restrict__ guard) {
+                                                   const int32_t* __restrict__ guard,
+                                                   int64_t* __restrict__ split_h) {
   if (failed(guard)) return;
   const int32_t j = blockIdx.x;
   const int32_t raw = *list_len;
@@ -1308,6 +1547,7 @@ __global__ void __launch_bounds__(64) k_find_merge(const int32_t* __restrict__ l
       sp.n_left = x.n_left;
       sp.valid = 1;
       splits[v] = sp;
+      if (split_h != nullptr) split_h[v] = x.h_left;
     }
   } else if (lane == 0) {
     gbdt_split sp;
@@ -2271,24 +2511,27 @@ int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_c
   return GBDT_OK;
 }
 
-int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,
-                const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
-                const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
-                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s, FindCand* cand,
-                const int32_t* guard) {
+template <bool HESS>
+static int launch_find_t(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft,
+                         const gbdt_node* nodes, const int32_t* list, const int32_t* list_len,
+                         int32_t list_cap, const gbdt_params& p, const int32_t* scale,
+                         gbdt_split* splits, const int32_t* sub_par, const int32_t* sub_sib,
+                         WsCtrl* ctrl, hipStream_t s, FindCand* cand, const int32_t* guard,
+                         int64_t* hist_h, const int32_t* scale_h, int64_t* split_h) {
   FindParams fp{p.reg_lambda, p.gamma, p.min_child_weight, p.min_samples_leaf};
   const int32_t nch = cand != nullptr ? find_chunks(ft.total_bins) : 1;
+  int32_t* err = ctrl != nullptr ? &ctrl->err : nullptr;
   diag_begin(kDiagFind, s);
   if (nch > 1) {
     // whole features of up to kFindChunk + 255 bins: one or two passes of
     // 1024 threads x 2 bins
-    hipLaunchKernelGGL((k_find<1024, 2>), dim3((unsigned)list_cap, (unsigned)nch), dim3(1024), 0, s, hist_g,
-                       hist_cnt, ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
-                       list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
-                       ctrl != nullptr ? &ctrl->err : nullptr, nch, cand, guard);
+    hipLaunchKernelGGL((k_find<1024, 2, HESS>), dim3((unsigned)list_cap, (unsigned)nch), dim3(1024), 0,
+                       s, hist_g, hist_cnt, ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins,
+                       nodes, list, list_len, list_cap, fp, scale, splits, sub_par, sub_sib, err, nch,
+                       cand, guard, hist_h, scale_h, split_h);
     GBDT_LAUNCH_CHECK("k_find");
     hipLaunchKernelGGL(k_find_merge, dim3((unsigned)list_cap), dim3(64), 0, s, list, list_len,
-                       list_cap, nch, (const FindCand*)cand, splits, guard);
+                       list_cap, nch, (const FindCand*)cand, splits, guard, split_h);
     diag_end(s);
     GBDT_LAUNCH_CHECK("k_find_merge");
     return GBDT_OK;
@@ -2299,28 +2542,40 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
   // node's latency falls with the bins per thread
   const int32_t tb = ft.total_bins;
   int threads = 1024;
-  auto kern = tb <= 1024   ? k_find<1024, 1>
-              : tb <= 2048 ? k_find<1024, 2>
-              : tb <= 3072 ? k_find<1024, 3>
-              : tb <= 4096 ? k_find<1024, 4>
-              : tb <= 6144 ? k_find<1024, 6>
-                           : k_find<1024, 8>;
+  auto kern = tb <= 1024   ? k_find<1024, 1, HESS>
+              : tb <= 2048 ? k_find<1024, 2, HESS>
+              : tb <= 3072 ? k_find<1024, 3, HESS>
+              : tb <= 4096 ? k_find<1024, 4, HESS>
+              : tb <= 6144 ? k_find<1024, 6, HESS>
+                           : k_find<1024, 8, HESS>;
   if (list_cap > 256 && tb <= 4096) {
     threads = 512;
-    kern = tb <= 512    ? k_find<512, 1>
-           : tb <= 1024 ? k_find<512, 2>
-           : tb <= 1536 ? k_find<512, 3>
-           : tb <= 2048 ? k_find<512, 4>
-           : tb <= 3072 ? k_find<512, 6>
-                        : k_find<512, 8>;
+    kern = tb <= 512    ? k_find<512, 1, HESS>
+           : tb <= 1024 ? k_find<512, 2, HESS>
+           : tb <= 1536 ? k_find<512, 3, HESS>
+           : tb <= 2048 ? k_find<512, 4, HESS>
+           : tb <= 3072 ? k_find<512, 6, HESS>
+                        : k_find<512, 8, HESS>;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)list_cap), dim3(threads), 0, s, hist_g, hist_cnt,
                      ft.bin_offset, ft.bin_feature, ft.n_bins, ft.total_bins, nodes, list,
-                     list_len, list_cap, fp, scale, splits, sub_par, sub_sib,
-                     ctrl != nullptr ? &ctrl->err : nullptr, 1, (FindCand*)nullptr, guard);
+                     list_len, list_cap, fp, scale, splits, sub_par, sub_sib, err, 1,
+                     (FindCand*)nullptr, guard, hist_h, scale_h, split_h);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_find");
   return GBDT_OK;
+}
+
+int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,
+                const int32_t* list, const int32_t* list_len, int32_t list_cap, const gbdt_params& p,
+                const int32_t* scale, gbdt_split* splits, const int32_t* sub_par,
+                const int32_t* sub_sib, WsCtrl* ctrl, hipStream_t s, FindCand* cand,
+                const int32_t* guard, int64_t* hist_h, const int32_t* scale_h, int64_t* split_h) {
+  if (hist_h != nullptr)
+    return launch_find_t<true>(hist_g, hist_cnt, ft, nodes, list, list_len, list_cap, p, scale, splits,
+                               sub_par, sub_sib, ctrl, s, cand, guard, hist_h, scale_h, split_h);
+  return launch_find_t<false>(hist_g, hist_cnt, ft, nodes, list, list_len, list_cap, p, scale, splits,
+                              sub_par, sub_sib, ctrl, s, cand, guard, nullptr, nullptr, nullptr);
 }
 
 // ------------------------------------------------------- feature binning --
@@ -2601,6 +2856,8 @@ int gbdt_validate_params(const gbdt_params* p) {
   if (p->reg_lambda < 0.0) return fail(GBDT_E_ARG, "reg_lambda must be >= 0");
   if (p->gamma < 0.0) return fail(GBDT_E_ARG, "gamma must be >= 0");
   if (p->max_depth < 0 || p->max_depth > GBDT_MAX_DEPTH) return fail(GBDT_E_ARG, "max_depth out of range");
+  if (p->objective != GBDT_OBJECTIVE_SQUARED_ERROR && p->objective != GBDT_OBJECTIVE_LOGISTIC)
+    return fail(GBDT_E_ARG, "unknown objective");
   return GBDT_OK;
 }
 
@@ -2803,6 +3060,29 @@ int launch_gradients(const double* pred, const float* label, int64_t n, void* q,
     hipLaunchKernelGGL(k_grad_sum, dim3(1), dim3(kGradBlocks), 0, s, (const int64_t*)psum, blocks, gsum);
     GBDT_LAUNCH_CHECK("k_grad_sum");
   }
+  return GBDT_OK;
+}
+
+int launch_gradients_logistic(const double* pred, const float* label, int64_t n, int32_t* q,
+                              int32_t* qh, int32_t* scale, int32_t* scale_h, double* part,
+                              WsCtrl* ctrl, hipStream_t s) {
+  if (!pred || !label || !q || !qh || !scale || !scale_h) return fail(GBDT_E_ARG, "null argument");
+  if (n < 1 || n > 0x7fffffffLL) return fail(GBDT_E_ARG, "n out of range");
+  double* part_h = part + 2 * kGradBlocks;
+  int64_t* psum = reinterpret_cast<int64_t*>(part + kGradBlocks);
+  int64_t* psum_h = reinterpret_cast<int64_t*>(part + 3 * kGradBlocks);
+  const int32_t blocks = grad_blocks(n);
+  diag_begin(kDiagGradMax, s);
+  hipLaunchKernelGGL(k_lgrad_max, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n, part, part_h,
+                     ctrl);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_lgrad_max");
+  diag_begin(kDiagGradQ, s);
+  hipLaunchKernelGGL(k_lgrad_q, dim3((unsigned)blocks), dim3(256), 0, s, pred, label, n, ceil_log2(n),
+                     (const double*)part, (const double*)part_h, blocks, q, qh, scale, scale_h, psum,
+                     psum_h);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_lgrad_q");
   return GBDT_OK;
 }
 

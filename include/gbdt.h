@@ -1,6 +1,7 @@
 /*
  * gbdt.h -- C ABI of the MI355X (gfx950) level-wise histogram GBDT hot path
- * for squared-error boosting.
+ * for squared-error boosting, with the sigmoid cross-entropy (logistic)
+ * objective as a second one in the tree driver.
  *
  * What the calls compute is fixed by "Module Design: Training Core"
  * (MPSBoost spec):
@@ -54,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GBDT_ABI_VERSION 2
+#define GBDT_ABI_VERSION 3
 #define GBDT_MAX_DEPTH 16       /* deepest tree the level loop supports */
 #define GBDT_MAX_FEATURES 4096
 #define GBDT_MAX_BINS 256       /* bins per feature */
@@ -72,6 +73,22 @@ typedef enum {
 
 /* Node flags. */
 #define GBDT_NODE_LEAF 1u
+
+/*
+ * Objectives (gbdt_params.objective).  Squared error: g = pred - label, h = 1
+ * (Training Core, section 2).  Logistic: the sigmoid cross-entropy of "Gradient
+ * boosted trees (spec model)" (gbtBinaryCrossentropyGradSpec) on the raw score,
+ * g = sigmoid(pred) - label and, as the pages give no Hessian, its second
+ * derivative h = sigmoid(pred) (1 - sigmoid(pred)); with z = e^-|pred| (0 when
+ * |pred| > 700) and d = 1 + z: sigmoid = 1/d (pred >= 0) or z/d, h = z/(d*d),
+ * e^x from a Cody-Waite reduction and the degree-13 Taylor series, one IEEE
+ * FP64 operation at a time.  g and h each get a per-tree fixed-point grid
+ * (S = min(52 - e - ceil(log2 n), 30 - e), so every value fits 31 bits); the
+ * Hessian sums H replace the row counts in min_child_weight, H > 0, the gain
+ * and the leaf weight.
+ */
+#define GBDT_OBJECTIVE_SQUARED_ERROR 0
+#define GBDT_OBJECTIVE_LOGISTIC 1
 
 /*
  * Bin matrix, column-blocked, with an optional bit block.
@@ -155,7 +172,8 @@ typedef struct gbdt_rows {
  * their weight in leaf_value; internal nodes carry the split, the child ids
  * and the gain, and leaf_value = 0.  The working fields say where the node's
  * rows sit in the row order of its level: positions [begin, begin + count),
- * with gsum = sum of q over them.
+ * with gsum = sum of q over them and, for the logistic objective, hsum = sum
+ * of the fixed-point Hessians (0 for squared error, where H is the count).
  */
 typedef struct gbdt_node {
   int32_t feature;
@@ -169,7 +187,7 @@ typedef struct gbdt_node {
   int32_t begin;
   int32_t count;
   int64_t gsum;
-  int64_t reserved;
+  int64_t hsum;
 } gbdt_node; /* 64 bytes */
 
 /*
@@ -197,7 +215,8 @@ typedef struct gbdt_pair {
 /*
  * Training parameters (Training Core, section 3): min_samples_leaf >= 1,
  * min_child_weight >= 0, reg_lambda >= 0, gamma >= 0, every float finite;
- * 0 <= max_depth <= GBDT_MAX_DEPTH.  Host struct.
+ * 0 <= max_depth <= GBDT_MAX_DEPTH; objective one of GBDT_OBJECTIVE_*.
+ * Host struct.
  */
 typedef struct gbdt_params {
   double reg_lambda;
@@ -206,6 +225,8 @@ typedef struct gbdt_params {
   double learning_rate;
   int32_t min_samples_leaf;
   int32_t max_depth;
+  int32_t objective;
+  int32_t pad;
 } gbdt_params;
 
 /* ---------------------------------------------------------------- setup -- */
@@ -463,7 +484,8 @@ int gbdt_predict_noalloc(const gbdt_matrix* X /* host */, const gbdt_node* trees
  * q and the row buffers' q are working storage of 8 bytes per row: when
  * ceil(log2 n_rows) >= 22 (n_rows > 2^21), every |q| <= 2^(52 - ceil(log2 n))
  * <= 2^30 and the driver keeps q as int32 in the first 4 n bytes (exact);
- * otherwise as int64.
+ * otherwise as int64.  The logistic objective's grids keep every value within
+ * 31 bits, so its q is int32 at any n.
  */
 typedef struct gbdt_grow_buffers {
   gbdt_rows pp[2];
@@ -475,6 +497,14 @@ typedef struct gbdt_grow_buffers {
   void* ctrl;            /* [ctrl_bytes] */
   void* ws;
   size_t ws_bytes;
+  /* logistic objective only (NULL otherwise): the fixed-point Hessians in
+     row-id order, int32 [n]; the Hessian histograms [hist_slots][total_bins];
+     the left child's Hessian sum of each split [max_nodes].  The row
+     buffers' rid arrays (then required, int32 [n] each) carry the Hessians
+     through the partitions. */
+  int32_t* qh;
+  int64_t* hist_h;
+  int64_t* split_h;
 } gbdt_grow_buffers;
 
 /* Sizes (in elements / bytes as named) of the driver's buffers. */
