@@ -98,6 +98,8 @@ def _load():
     lib.orc_predict.restype = ctypes.c_int
     lib.orc_predict.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32, vp, ctypes.c_int32,
                                 vp, ctypes.c_double, ctypes.c_double, vp]
+    lib.orc_feature_bounds.restype = ctypes.c_int
+    lib.orc_feature_bounds.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, ctypes.c_int32, vp]
     lib.orc_bin_features.restype = ctypes.c_int64
     lib.orc_bin_features.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp, vp]
     _lib = lib
@@ -267,6 +269,25 @@ def predict(bins, trees, n_nodes, base_score=0.0, learning_rate=0.3):
                              float(base_score), float(learning_rate), _p(out))
     if rc:
         raise ValueError("orc_predict failed (%d)" % rc)
+    return out
+
+
+QUANTILE_SAMPLE = 32768
+BOUNDS_EQUAL_WIDTH = 0
+BOUNDS_QUANTILE = 1
+
+
+def feature_bounds(raw, n_bins, method):
+    """orc_feature_bounds: float32 [total_bins] bounds (feature f's at
+    bin_offset[f] + k) for a float32 [n][F] matrix; method 0 equal width,
+    1 quantile of the row sample."""
+    raw = np.ascontiguousarray(raw, dtype=np.float32)
+    nb = np.ascontiguousarray(n_bins, dtype=np.int32)
+    n, F = raw.shape
+    out = np.zeros(int(nb.sum()), dtype=np.float32)
+    rc = _load().orc_feature_bounds(n, F, _p(raw), _p(nb), int(method), _p(out))
+    if rc:
+        raise ValueError("orc_feature_bounds failed (%d)" % rc)
     return out
 
 

@@ -701,3 +701,103 @@ int orc_predict(int64_t n, int32_t F, const uint8_t* bins, int32_t n_trees, cons
   }
   return ORC_OK;
 }
+
+/*
+ * Bin bounds: how the bounds of the "Quantized" state (Training Core, state
+ * machine, section 5) are chosen.  The page names the state only; two
+ * readings are provided, both ending in bounds that strictly increase so
+ * that orc_bin_features accepts them.  For feature f with B = n_bins[f]
+ * bins, the B - 1 bounds u_1 .. u_{B-1} go to upper[bin_offset[f] + k - 1];
+ * the entry after them (never read by the binning) is set to +inf.
+ *
+ *  method 0, equal width: lo and hi are the least and greatest finite values
+ *    of the feature (NaN and +-inf skipped; lo = hi = 0 if there is none);
+ *    u_k = (float)(lo + (hi - lo) * (k / B)), evaluated in FP64 one operation
+ *    at a time (k / B, the product, the sum), then rounded to FP32.
+ *  method 1, quantile: the sample is the rows 0, s, 2s, ... with
+ *    s = ceil(n / ORC_QUANTILE_SAMPLE) (every row when n <= ORC_QUANTILE_SAMPLE),
+ *    a row sample as GBDT libraries use to build bins; its m finite values
+ *    (NaN and +-inf skipped, as for the range above) sorted ascending as
+ *    v_0 <= ... <= v_{m-1}; u_k is v_r with r = ceil(k m / B) - 1, so at least
+ *    k m / B of them lie at or below u_k (m = 0: every u_k = 0).
+ *
+ * Then, for k = 2 .. B-1, a bound that is not above its predecessor is raised
+ * to next_up(u_{k-1}): the next FP32 value above it among zero and the normal
+ * values (0 for a negative value whose next value would be subnormal; the
+ * least positive normal value for a zero; a positive value's next
+ * representable value; +inf stays +inf).
+ */
+#define ORC_QUANTILE_SAMPLE 32768
+
+static float orc_next_up(float x) {
+  if (isinf(x) && x > 0.0f) return x;
+  if (x == 0.0f) return 1.17549435e-38f; /* FLT_MIN */
+  uint32_t b;
+  memcpy(&b, &x, 4);
+  b = x > 0.0f ? b + 1u : b - 1u;
+  float y;
+  memcpy(&y, &b, 4);
+  if (y < 0.0f && y > -1.17549435e-38f) y = 0.0f; /* would be subnormal */
+  return y;
+}
+
+static int orc_cmp_float(const void* a, const void* b) {
+  const float x = *(const float*)a, y = *(const float*)b;
+  return (x > y) - (x < y);
+}
+
+int orc_feature_bounds(int64_t n, int32_t F, const float* raw, const int32_t* n_bins, int32_t method,
+                       float* upper) {
+  if (n < 0 || F < 1 || (n > 0 && !raw) || !n_bins || !upper) return ORC_E_ARG;
+  if (method != 0 && method != 1) return ORC_E_ARG;
+  const int64_t step = n <= ORC_QUANTILE_SAMPLE ? 1 : (n + ORC_QUANTILE_SAMPLE - 1) / ORC_QUANTILE_SAMPLE;
+  float* buf = (float*)malloc(sizeof(float) * (size_t)(ORC_QUANTILE_SAMPLE + 1));
+  if (!buf) return ORC_E_INTERNAL;
+  int64_t off = 0;
+  for (int32_t f = 0; f < F; ++f) {
+    const int32_t B = n_bins[f];
+    if (B < 1 || B > 256) {
+      free(buf);
+      return ORC_E_ARG;
+    }
+    float* u = upper + off; /* u[k - 1] = u_k */
+    if (method == 0) {
+      int have = 0;
+      float lo = 0.0f, hi = 0.0f;
+      for (int64_t i = 0; i < n; ++i) {
+        const float x = raw[i * F + f];
+        if (!isfinite(x)) continue;
+        if (!have || x < lo) lo = x;
+        if (!have || x > hi) hi = x;
+        have = 1;
+      }
+      for (int32_t k = 1; k < B; ++k) {
+        const double t = (double)k / (double)B;
+        const double w = (double)hi - (double)lo;
+        const double m = w * t;
+        u[k - 1] = (float)((double)lo + m);
+      }
+    } else {
+      int64_t m = 0;
+      for (int64_t i = 0; i < n; i += step) {
+        const float x = raw[i * F + f];
+        if (isfinite(x)) buf[m++] = x;
+      }
+      qsort(buf, (size_t)m, sizeof(float), orc_cmp_float);
+      for (int32_t k = 1; k < B; ++k) {
+        if (m == 0) {
+          u[k - 1] = 0.0f;
+        } else {
+          const int64_t r = ((int64_t)k * m + B - 1) / B - 1;
+          u[k - 1] = buf[r];
+        }
+      }
+    }
+    for (int32_t k = 2; k < B; ++k)
+      if (!(u[k - 1] > u[k - 2])) u[k - 1] = orc_next_up(u[k - 2]);
+    upper[off + B - 1] = INFINITY;
+    off += B;
+  }
+  free(buf);
+  return ORC_OK;
+}

@@ -812,3 +812,109 @@ def test_logistic_training_lowers_the_loss():
     # the training predictions are the forward pass of the trees
     out = oracle.predict(bins, r["nodes"], r["n_nodes"], 0.0, p.learning_rate)
     assert np.array_equal(out, r["pred"])
+
+
+# ------------------------------------------------------------------ bin bounds
+
+FLT_MIN = float(np.finfo(np.float32).tiny)
+
+
+def test_bounds_equal_width_hand():
+    """lo = 0, hi = 10, four bins: bounds 2.5, 5, 7.5 (exact); NaN and +-inf
+    are left out of the range; the entry after the bounds is +inf."""
+    col = np.array([3.0, 0.0, np.nan, 10.0, np.inf, -np.inf, 7.0], dtype=np.float32)
+    u = oracle.feature_bounds(col[:, None], [4], oracle.BOUNDS_EQUAL_WIDTH)
+    assert u.tolist() == [2.5, 5.0, 7.5, math.inf]
+    # two features side by side, each with its own range and bin count
+    raw = np.stack([col, np.array([-4, -2, 0, 2, 4, 6, 8], dtype=np.float32)], axis=1)
+    u = oracle.feature_bounds(raw, [4, 3], oracle.BOUNDS_EQUAL_WIDTH)
+    assert u.tolist() == [2.5, 5.0, 7.5, math.inf, 0.0, 4.0, math.inf]
+    # the extremes land in the first and last bins
+    b, _ = oracle.bin_features(raw, [4, 3], u)
+    assert b[1, 0] == 0 and b[3, 0] == 3 and b[0, 1] == 0 and b[6, 1] == 2
+
+
+def test_bounds_degenerate_features():
+    """A constant feature and a feature with no finite value: the bounds climb
+    from the value (or 0) by next_up, so every value of the constant feature
+    falls in bin 0 and the bounds still strictly increase."""
+    raw = np.array([[5.0, np.nan], [5.0, np.inf], [5.0, np.nan]], dtype=np.float32)
+    for method in (oracle.BOUNDS_EQUAL_WIDTH, oracle.BOUNDS_QUANTILE):
+        u = oracle.feature_bounds(raw, [4, 3], method)
+        a = u[:3]
+        assert a[0] == 5.0 and a[1] == np.nextafter(np.float32(5.0), np.float32(np.inf))
+        assert (np.diff(a) > 0).all()
+        b, _ = oracle.bin_features(raw, [4, 3], u)
+        assert (b[:, 0] == 0).all()
+    u = oracle.feature_bounds(raw, [4, 3], oracle.BOUNDS_EQUAL_WIDTH)
+    assert u[4] == 0.0 and u[5] == FLT_MIN  # no finite value: lo = hi = 0
+
+
+def test_bounds_next_up_rules():
+    """next_up skips the subnormals: -FLT_MIN -> 0 -> FLT_MIN."""
+    raw = np.full((4, 1), -FLT_MIN, dtype=np.float32)
+    u = oracle.feature_bounds(raw, [4], oracle.BOUNDS_QUANTILE)
+    assert u[:3].tolist() == [-FLT_MIN, 0.0, FLT_MIN]
+    raw = np.full((4, 1), np.float32(np.finfo(np.float32).max))
+    u = oracle.feature_bounds(raw, [3], oracle.BOUNDS_QUANTILE)
+    assert u[:2].tolist() == [float(np.finfo(np.float32).max), math.inf]
+
+
+def test_bounds_quantile_hand():
+    """Values 1 .. 100, four bins: bound k is the ceil(k 100/4)-th smallest
+    value: 25, 50, 75; binning then puts exactly 25 values in each bin."""
+    col = np.arange(100, 0, -1, dtype=np.float32)
+    u = oracle.feature_bounds(col[:, None], [4], oracle.BOUNDS_QUANTILE)
+    assert u[:3].tolist() == [25.0, 50.0, 75.0]
+    b, _ = oracle.bin_features(col[:, None], [4], u)
+    assert np.bincount(b[:, 0], minlength=4).tolist() == [25, 25, 25, 25]
+
+
+@pytest.mark.parametrize("B", [4, 64, 256])
+def test_bounds_quantile_is_the_inverted_cdf(B):
+    """Without ties, bound k is numpy's inverted-CDF quantile at k/B of the
+    finite values (B a power of two, so k/B and k m/B are exact), and at least
+    a fraction k/B of them lies at or below it, less than k/B below it."""
+    rng = np.random.default_rng(B)
+    col = rng.standard_t(3, size=20000).astype(np.float32)
+    col[::97] = np.nan
+    col[5] = np.inf
+    col[6] = -np.inf
+    u = oracle.feature_bounds(col[:, None], [B], oracle.BOUNDS_QUANTILE)[: B - 1]
+    v = col[np.isfinite(col)].astype(np.float64)
+    q = np.quantile(v, np.arange(1, B) / B, method="inverted_cdf")
+    assert np.array_equal(u.astype(np.float64), q)
+    for k in range(1, B):
+        assert (v <= u[k - 1]).mean() >= k / B > (v < u[k - 1]).mean()
+
+
+def test_bounds_quantile_sample_rows():
+    """Above 32768 rows the quantiles come from rows 0, s, 2s, ... with
+    s = ceil(n / 32768): the bounds equal those of that sample given alone."""
+    n = 100_001
+    s = -(-n // oracle.QUANTILE_SAMPLE)
+    rng = np.random.default_rng(7)
+    raw = rng.exponential(size=(n, 3)).astype(np.float32)
+    raw[:, 2] = np.round(raw[:, 2] * 4)  # heavy ties
+    full = oracle.feature_bounds(raw, [16, 256, 64], oracle.BOUNDS_QUANTILE)
+    samp = oracle.feature_bounds(raw[::s], [16, 256, 64], oracle.BOUNDS_QUANTILE)
+    assert raw[::s].shape[0] <= oracle.QUANTILE_SAMPLE
+    assert np.array_equal(full, samp)
+    off = 0
+    for B in (16, 256, 64):
+        assert (np.diff(full[off: off + B - 1]) > 0).all()
+        off += B
+    b, nan = oracle.bin_features(raw, [16, 256, 64], full)
+    assert nan == 0
+
+
+def test_bounds_equal_width_ignores_row_order():
+    rng = np.random.default_rng(8)
+    raw = rng.normal(size=(5000, 4)).astype(np.float32) * np.float32(1e3)
+    u1 = oracle.feature_bounds(raw, [7, 64, 255, 2], oracle.BOUNDS_EQUAL_WIDTH)
+    u2 = oracle.feature_bounds(raw[rng.permutation(5000)], [7, 64, 255, 2], oracle.BOUNDS_EQUAL_WIDTH)
+    assert np.array_equal(u1, u2)
+    # every bin of a 255-bin feature spans (hi - lo)/255 up to rounding
+    lo, hi = raw[:, 2].min(), raw[:, 2].max()
+    w = np.diff(np.concatenate([[lo], u1[7 + 64: 7 + 64 + 254], [hi]]).astype(np.float64))
+    assert np.allclose(w, (float(hi) - float(lo)) / 255, rtol=1e-4)
