@@ -710,6 +710,7 @@ int orc_predict(int64_t n, int32_t F, const uint8_t* bins, int32_t n_trees, cons
  * bins, the B - 1 bounds u_1 .. u_{B-1} go to upper[bin_offset[f] + k - 1];
  * the entry after them (never read by the binning) is set to +inf.
  *
+ *  Both take zeros of either sign as +0, so the bounds are unique.
  *  method 0, equal width: lo and hi are the least and greatest finite values
  *    of the feature (NaN and +-inf skipped; lo = hi = 0 if there is none);
  *    u_k = (float)(lo + (hi - lo) * (k / B)), evaluated in FP64 one operation
@@ -765,8 +766,9 @@ int orc_feature_bounds(int64_t n, int32_t F, const float* raw, const int32_t* n_
       int have = 0;
       float lo = 0.0f, hi = 0.0f;
       for (int64_t i = 0; i < n; ++i) {
-        const float x = raw[i * F + f];
+        float x = raw[i * F + f];
         if (!isfinite(x)) continue;
+        if (x == 0.0f) x = 0.0f;
         if (!have || x < lo) lo = x;
         if (!have || x > hi) hi = x;
         have = 1;
@@ -781,7 +783,7 @@ int orc_feature_bounds(int64_t n, int32_t F, const float* raw, const int32_t* n_
       int64_t m = 0;
       for (int64_t i = 0; i < n; i += step) {
         const float x = raw[i * F + f];
-        if (isfinite(x)) buf[m++] = x;
+        if (isfinite(x)) buf[m++] = x == 0.0f ? 0.0f : x;
       }
       qsort(buf, (size_t)m, sizeof(float), orc_cmp_float);
       for (int32_t k = 1; k < B; ++k) {

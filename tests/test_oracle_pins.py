@@ -918,3 +918,16 @@ def test_bounds_equal_width_ignores_row_order():
     lo, hi = raw[:, 2].min(), raw[:, 2].max()
     w = np.diff(np.concatenate([[lo], u1[7 + 64: 7 + 64 + 254], [hi]]).astype(np.float64))
     assert np.allclose(w, (float(hi) - float(lo)) / 255, rtol=1e-4)
+
+
+def test_bounds_signed_zero():
+    """-0 and +0 are one value for the bounds: a quantile at a run of zeros of
+    both signs is +0, and so is an equal-width end at zero."""
+    col = np.array([-0.0, 0.0, -0.0, 1.0, -1.0, 0.0, -0.0, 2.0], dtype=np.float32)
+    u = oracle.feature_bounds(col[:, None], [4], oracle.BOUNDS_QUANTILE)
+    # sorted: -1, 0 x 5, 1, 2; ranks 1, 3, 5 are zeros; the chain lifts the repeats
+    assert u[0] == 0.0 and math.copysign(1.0, float(u[0])) > 0
+    assert u[1] == FLT_MIN and u[2] == np.nextafter(np.float32(FLT_MIN), np.float32(1))
+    col = np.array([-0.0, 4.0, 1.0], dtype=np.float32)
+    u = oracle.feature_bounds(col[:, None], [4], oracle.BOUNDS_EQUAL_WIDTH)
+    assert u[:3].tolist() == [1.0, 2.0, 3.0]
