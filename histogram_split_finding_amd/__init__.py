@@ -108,6 +108,7 @@ def load():
         "gbdt_choose_layout": (ctypes.c_int, [i32, vp, i32, P(Matrix), P(i32), vp, vp]),
         "gbdt_pack_matrix": (ctypes.c_int, [vp, P(Matrix), P(Features), vp, ctypes.c_size_t, vp]),
         "gbdt_bin_features": (ctypes.c_int, [vp, i64, P(Features), vp, vp, vp, ctypes.c_size_t, vp]),
+        "gbdt_feature_bounds": (ctypes.c_int, [vp, i64, P(Features), i32, vp, vp, ctypes.c_size_t, vp]),
         "gbdt_read_error": (ctypes.c_int, [vp, vp]),
         "gbdt_compute_gradients": (ctypes.c_int, [vp, vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "gbdt_build_histograms": (ctypes.c_int, [P(Rows), P(Features), vp, vp, vp, i32, i64, vp, vp,
@@ -321,6 +322,18 @@ def gbdt_bin_features(raw, ft: FeatureTable, upper, bins_out, ws, stream=None):
                                   ctypes.byref(f), _ptr(upper), _ptr(bins_out), _ptr(ws), ws.numel(),
                                   _stream(stream))
     _check(rc, "gbdt_bin_features")
+
+
+BOUNDS_EQUAL_WIDTH = 0
+BOUNDS_QUANTILE = 1
+
+
+def gbdt_feature_bounds(raw, ft: FeatureTable, method, upper, ws, stream=None):
+    """raw: float32 [n][F] device tensor; upper: float32 [total_bins] (written)."""
+    f = ft.struct()
+    rc = load().gbdt_feature_bounds(_ptr(raw), int(raw.shape[0]), ctypes.byref(f), int(method), _ptr(upper),
+                                    _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "gbdt_feature_bounds")
 
 
 def gbdt_read_error(ws, stream=None) -> int:

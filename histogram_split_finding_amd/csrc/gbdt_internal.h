@@ -252,7 +252,8 @@ int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* node
 // launch of the library is bracketed by two hipEvents on its stream.
 enum DiagKind {
   kDiagGradMax = 1, kDiagGradQ, kDiagPlan, kDiagHist, kDiagHistReduce, kDiagSubtract, kDiagFind,
-  kDiagTreeInit, kDiagLevel, kDiagPartition, kDiagUpdate, kDiagPack, kDiagBin, kDiagPredict
+  kDiagTreeInit, kDiagLevel, kDiagPartition, kDiagUpdate, kDiagPack, kDiagBin, kDiagPredict,
+  kDiagBounds
 };
 void diag_begin(int kind, hipStream_t s);
 void diag_end(hipStream_t s);

@@ -2743,6 +2743,187 @@ __global__ void __launch_bounds__(kBinThreads) k_bin(const float* __restrict__ r
   if (nan) dev_error(&ctrl->err, GBDT_E_RANGE);
 }
 
+// ------------------------------------------------------------ bin bounds --
+// How the bounds of the "Quantized" state (Training Core, section 5) are
+// chosen; the page names the state only.  Equal width: u_k = lo + (hi - lo)
+// (k / B) over each feature's finite range, in FP64 one operation at a time
+// and rounded to FP32.  Quantile: u_k is the ceil(k m / B)-th smallest of the
+// m finite values in a row sample (rows 0, s, 2s, ..., at most kQuantSample
+// of them), as GBDT libraries sample rows to build bins.  Then bounds that do
+// not increase are raised to next_up of their predecessor.
+constexpr int kQuantSample = 32768;
+constexpr int kBoundThreads = 1024;
+
+// Order-preserving key of a float (larger float, larger key), -0 taken as
+// +0; finite values only come through here.
+__device__ __forceinline__ uint32_t float_key(float x) {
+  const uint32_t b = x == 0.0f ? 0u : __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The next FP32 value above x among zero and the normal values: FLT_MIN for
+// a zero, 0 for a negative value whose next value would be subnormal, +inf
+// stays +inf.
+__device__ __forceinline__ float next_up_normal(float x) {
+  if (x == __int_as_float(0x7f800000)) return x;
+  if (x == 0.0f) return __uint_as_float(0x00800000u);
+  uint32_t b = __float_as_uint(x);
+  b = x > 0.0f ? b + 1u : b - 1u;
+  float y = __uint_as_float(b);
+  if (y < 0.0f && y > -__uint_as_float(0x00800000u)) y = 0.0f;
+  return y;
+}
+
+// Raise bounds that do not increase, in order (one thread per feature).
+__device__ __forceinline__ void strictly_increasing(float* u, int32_t nb) {
+  for (int32_t k = 1; k < nb; ++k)
+    if (!(u[k] > u[k - 1])) u[k] = next_up_normal(u[k - 1]);
+}
+
+__global__ void __launch_bounds__(256) k_range_init(uint32_t* __restrict__ kmin,
+                                                    uint32_t* __restrict__ kmax, int32_t F) {
+  for (int32_t f = blockIdx.x * 256 + threadIdx.x; f < F; f += gridDim.x * 256) {
+    kmin[f] = 0xffffffffu;
+    kmax[f] = 0u;
+  }
+}
+
+// Least and greatest finite value of each feature, as order-preserving keys:
+// per workgroup in LDS, then one device atomic per feature and workgroup.
+// Each thread takes runs of 16 consecutive values (four 16-byte loads), the
+// feature index advancing by one per value.
+__global__ void __launch_bounds__(kBinThreads) k_range(const float* __restrict__ raw, int64_t n_vals,
+                                                       int32_t F, uint32_t* __restrict__ kmin,
+                                                       uint32_t* __restrict__ kmax) {
+  extern __shared__ uint32_t s_key[];  // [F] minima, then [F] maxima
+  for (int32_t f = threadIdx.x; f < F; f += blockDim.x) {
+    s_key[f] = 0xffffffffu;
+    s_key[F + f] = 0u;
+  }
+  __syncthreads();
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x * 16;
+  for (int64_t v0 = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 16; v0 < n_vals; v0 += stride) {
+    float x[16];
+    if (v0 + 16 <= n_vals) {
+      const float4* p = reinterpret_cast<const float4*>(raw + v0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 t = p[q];
+        x[4 * q] = t.x;
+        x[4 * q + 1] = t.y;
+        x[4 * q + 2] = t.z;
+        x[4 * q + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) x[q] = v0 + q < n_vals ? raw[v0 + q] : __int_as_float(0x7fc00000);
+    }
+    int32_t f = (int32_t)(v0 % F);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (isfinite(x[q])) {
+        const uint32_t k = float_key(x[q]);
+        atomicMin(&s_key[f], k);
+        atomicMax(&s_key[F + f], k);
+      }
+      if (++f == F) f = 0;
+    }
+  }
+  __syncthreads();
+  for (int32_t f = threadIdx.x; f < F; f += blockDim.x) {
+    if (s_key[f] != 0xffffffffu) atomicMin(&kmin[f], s_key[f]);
+    if (s_key[F + f] != 0u) atomicMax(&kmax[f], s_key[F + f]);
+  }
+}
+
+// Equal-width bounds from the ranges (one thread per feature).
+__global__ void __launch_bounds__(256) k_bounds_width(const uint32_t* __restrict__ kmin,
+                                                      const uint32_t* __restrict__ kmax, int32_t F,
+                                                      const int32_t* __restrict__ n_bins,
+                                                      const int32_t* __restrict__ bin_offset,
+                                                      float* __restrict__ upper) {
+  const int32_t f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= F) return;
+  const bool have = kmin[f] != 0xffffffffu;
+  const float lo = have ? key_float(kmin[f]) : 0.0f;
+  const float hi = have ? key_float(kmax[f]) : 0.0f;
+  const int32_t B = n_bins[f];
+  float* u = upper + bin_offset[f];
+  for (int32_t k = 1; k < B; ++k) {
+    const double t = (double)k / (double)B;
+    const double w = (double)hi - (double)lo;
+    const double m = w * t;
+    u[k - 1] = (float)((double)lo + m);
+  }
+  strictly_increasing(u, B - 1);
+  u[B - 1] = __int_as_float(0x7f800000);
+}
+
+// Quantile bounds: one workgroup per feature sorts the keys of its sampled
+// finite values in LDS (bitonic, non-finite values as the largest key, past
+// the m finite ones) and reads the ranks off.
+__global__ void __launch_bounds__(kBoundThreads) k_bounds_quantile(const float* __restrict__ raw,
+                                                                   int64_t n, int32_t F, int64_t step,
+                                                                   int32_t cnt, int32_t P,
+                                                                   const int32_t* __restrict__ n_bins,
+                                                                   const int32_t* __restrict__ bin_offset,
+                                                                   float* __restrict__ upper) {
+  extern __shared__ uint32_t s_sort[];  // [P] keys, P a power of two >= cnt
+  __shared__ int32_t s_m[kBoundThreads / 64];
+  const int32_t f = blockIdx.x;
+  int32_t mine = 0;
+  for (int32_t j = threadIdx.x; j < P; j += kBoundThreads) {
+    uint32_t k = 0xffffffffu;
+    if (j < cnt) {
+      const float x = raw[int64_t(j) * step * F + f];
+      if (isfinite(x)) {
+        k = float_key(x);
+        ++mine;
+      }
+    }
+    s_sort[j] = k;
+  }
+  mine = wave_sum(mine);
+  if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = mine;
+  __syncthreads();
+  int32_t m = 0;
+  for (int w = 0; w < kBoundThreads / 64; ++w) m += s_m[w];
+  // bitonic sort, ascending
+  for (int32_t size = 2; size <= P; size <<= 1) {
+    for (int32_t half = size >> 1; half > 0; half >>= 1) {
+      for (int32_t t = threadIdx.x; t < P / 2; t += kBoundThreads) {
+        const int32_t i = 2 * t - (t & (half - 1));  // low index of the pair
+        const int32_t j = i + half;
+        const bool up = (i & size) == 0;
+        const uint32_t a = s_sort[i], b = s_sort[j];
+        if ((a > b) == up) {
+          s_sort[i] = b;
+          s_sort[j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int32_t B = n_bins[f];
+  float* u = upper + bin_offset[f];
+  for (int32_t k = 1 + threadIdx.x; k < B; k += kBoundThreads) {
+    if (m == 0) {
+      u[k - 1] = 0.0f;
+    } else {
+      const int64_t r = (int64_t(k) * m + B - 1) / B - 1;
+      u[k - 1] = key_float(s_sort[r]);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    strictly_increasing(u, B - 1);
+    u[B - 1] = __int_as_float(0x7f800000);
+  }
+}
+
 template <int K, bool Q>
 static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K, Q>) {
   switch (nd) {
@@ -2935,6 +3116,53 @@ int gbdt_read_error(void* ws, void* stream) {
     if (e != hipSuccess) return hip_fail(e, "clearing the error word");
     return fail(c.err, "device-side check failed (code " + std::to_string(c.err) + ")");
   }
+  return GBDT_OK;
+}
+
+int gbdt_feature_bounds(const float* raw, int64_t n_rows, const gbdt_features* ft, int32_t method,
+                        float* upper, void* ws, size_t ws_bytes, void* stream) {
+  if (!ft || !upper) return fail(GBDT_E_ARG, "null argument");
+  if (method != GBDT_BOUNDS_EQUAL_WIDTH && method != GBDT_BOUNDS_QUANTILE)
+    return fail(GBDT_E_ARG, "unknown bounds method");
+  if (n_rows < 0 || n_rows > 0x7fffffffLL) return fail(GBDT_E_ARG, "n_rows out of range");
+  if (n_rows > 0 && !raw) return fail(GBDT_E_ARG, "null argument");
+  if (ft->n_features < 1 || ft->n_features > GBDT_MAX_FEATURES) return fail(GBDT_E_ARG, "n_features out of range");
+  int rc = check_features(*ft, ft->n_features);
+  if (rc) return rc;
+  if (!aligned(raw, 16) || !aligned(upper, 4)) return fail(GBDT_E_ARG, "raw must be 16-byte aligned");
+  const WsLayout L = ws_layout(n_rows < 1 ? 1 : n_rows, 1, ft->total_bins);
+  rc = check_ws(ws, ws_bytes, L);
+  if (rc) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int32_t F = ft->n_features;
+  diag_begin(kDiagBounds, s);
+  if (method == GBDT_BOUNDS_EQUAL_WIDTH) {
+    uint32_t* kmin = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.hpart);
+    uint32_t* kmax = kmin + F;
+    const unsigned fg = (unsigned)((F + 255) / 256);
+    hipLaunchKernelGGL(k_range_init, dim3(fg), dim3(256), 0, s, kmin, kmax, F);
+    GBDT_LAUNCH_CHECK("k_range_init");
+    const int64_t n_vals = n_rows * F;
+    if (n_vals > 0) {
+      int64_t grid = (n_vals + 16 * kBinThreads - 1) / (16 * kBinThreads);
+      if (grid > kBinGrid) grid = kBinGrid;
+      hipLaunchKernelGGL(k_range, dim3((unsigned)grid), dim3(kBinThreads), 2 * sizeof(uint32_t) * size_t(F), s,
+                         raw, n_vals, F, kmin, kmax);
+      GBDT_LAUNCH_CHECK("k_range");
+    }
+    hipLaunchKernelGGL(k_bounds_width, dim3(fg), dim3(256), 0, s, (const uint32_t*)kmin,
+                       (const uint32_t*)kmax, F, ft->n_bins, ft->bin_offset, upper);
+    GBDT_LAUNCH_CHECK("k_bounds_width");
+  } else {
+    const int64_t step = n_rows <= kQuantSample ? 1 : (n_rows + kQuantSample - 1) / kQuantSample;
+    const int32_t cnt = n_rows == 0 ? 0 : int32_t((n_rows + step - 1) / step);
+    int32_t P = 2;
+    while (P < cnt) P <<= 1;
+    hipLaunchKernelGGL(k_bounds_quantile, dim3((unsigned)F), dim3(kBoundThreads), sizeof(uint32_t) * size_t(P), s,
+                       raw, n_rows, F, step, cnt, P, ft->n_bins, ft->bin_offset, upper);
+    GBDT_LAUNCH_CHECK("k_bounds_quantile");
+  }
+  diag_end(s);
   return GBDT_OK;
 }
 

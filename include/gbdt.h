@@ -308,6 +308,33 @@ int gbdt_bin_features(const float* raw, int64_t n_rows, const gbdt_features* ft 
                       const float* upper, uint8_t* bins_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Bin bounds for gbdt_bin_features: how the bounds of the "Quantized" state
+ * (Training Core, section 5) are chosen, which the page leaves open.  For
+ * feature f with B = ft->n_bins[f] bins, writes B - 1 strictly increasing
+ * bounds u_1 .. u_{B-1} to upper[bin_offset[f] + k - 1] (device, FP32,
+ * [total_bins]) and +inf after them.
+ *   GBDT_BOUNDS_EQUAL_WIDTH: lo and hi are the feature's least and greatest
+ *     finite values over all rows (NaN and +-inf skipped; 0 and 0 if there is
+ *     none), u_k = (float)(lo + (hi - lo) * (k / B)) evaluated in FP64 one
+ *     operation at a time.
+ *   GBDT_BOUNDS_QUANTILE: the finite values of the row sample 0, s, 2s, ...
+ *     with s = ceil(n_rows / 32768) (every row up to 32768 rows), m of them,
+ *     sorted ascending; u_k is the one at rank ceil(k m / B) - 1 (0 when
+ *     m = 0).  At least k m / B of the sample lies at or below u_k.
+ * Zeros of either sign count as +0 in both.
+ * Then each bound that is not above its predecessor is raised to the next
+ * FP32 value above it among zero and the normal values (FLT_MIN after a
+ * zero, 0 after a negative value whose successor is subnormal).
+ * raw: device FP32 [n_rows][n_features] row-major, 16-byte aligned.
+ * ws: at least gbdt_workspace_bytes(n_rows, 1, total_bins) bytes.  Setup
+ * step, not part of the per-tree path; ft needs n_bins and bin_offset.
+ */
+#define GBDT_BOUNDS_EQUAL_WIDTH 0
+#define GBDT_BOUNDS_QUANTILE 1
+int gbdt_feature_bounds(const float* raw, int64_t n_rows, const gbdt_features* ft /* host */,
+                        int32_t method, float* upper, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Diagnostics (Training Core section 4, diagnostics()): per-kernel device
  * time.  While enabled, each kernel launch of the library is bracketed by two
  * hipEvents on its stream (up to `capacity` launches are kept).
@@ -316,7 +343,7 @@ int gbdt_bin_features(const float* raw, int64_t n_rows, const gbdt_features* ft 
  * 2 gradient grid, 3 tile planner, 4 histogram, 5 histogram partial reduce,
  * 6 subtraction, 7 split search, 8 tree init, 9 level bookkeeping,
  * 10 partition, 11 prediction update, 12 packing, 13 binning, 14 ensemble
- * prediction.  One process-wide record;
+ * prediction, 15 bin bounds.  One process-wide record;
  * not for concurrent use from several threads.
  */
 int gbdt_diag_enable(int32_t capacity);
