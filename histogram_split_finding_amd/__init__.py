@@ -57,7 +57,7 @@ class Matrix(ctypes.Structure):
     _fields_ = [("bins", vp), ("n_rows", i64), ("row_capacity", i64), ("n_features", i32),
                 ("n_blocks", i32), ("block_features", i32), ("block_stride", i32),
                 ("n_bit_features", i32), ("bit_stride", i32), ("col_feature", vp),
-                ("feature_col", vp)]
+                ("feature_col", vp), ("n_nib_features", i32), ("nib_stride", i32)]
 
 
 class Features(ctypes.Structure):
@@ -195,15 +195,21 @@ def gbdt_choose_blocking(n_bins):
     return X, int(mbb.value)
 
 
-def gbdt_choose_layout(n_bins, pack_bits=True):
+PACK_BITS = 1
+PACK_NIBBLES = 2
+
+
+def gbdt_choose_layout(n_bins, pack_bits=True, pack_nibbles=False):
     """(Matrix layout fields, max_block_bins, col_feature, feature_col) for the
-    features' bin counts; with pack_bits, features of at most 2 bins are bits."""
+    features' bin counts; with pack_bits, features of at most 2 bins are bits;
+    with pack_nibbles, features of 3 to 16 bins are 4-bit cells."""
     nb = np.ascontiguousarray(np.asarray(n_bins, dtype=np.int32))
     X = Matrix()
     mbb = i32()
     cf = np.zeros(nb.shape[0], dtype=np.int32)
     fc = np.zeros(nb.shape[0], dtype=np.int32)
-    rc = load().gbdt_choose_layout(nb.shape[0], nb.ctypes.data_as(vp), int(bool(pack_bits)),
+    flags = (PACK_BITS if pack_bits else 0) | (PACK_NIBBLES if pack_nibbles else 0)
+    rc = load().gbdt_choose_layout(nb.shape[0], nb.ctypes.data_as(vp), flags,
                                    ctypes.byref(X), ctypes.byref(mbb), cf.ctypes.data_as(vp),
                                    fc.ctypes.data_as(vp))
     _check(rc, "gbdt_choose_layout")
@@ -229,9 +235,10 @@ def new_workspace(nbytes: int, device="cuda"):
 class FeatureTable:
     """Device feature table (n_bins, bin_offset, bin_feature, skip_bin) and the
     matrix layout chosen for it (with pack_bits, features of at most 2 bins
-    are stored as bits; the column maps live on the device)."""
+    are stored as bits; with pack_nibbles, features of 3 to 16 bins as 4-bit
+    cells; the column maps live on the device)."""
 
-    def __init__(self, n_bins, device="cuda", pack_bits=True):
+    def __init__(self, n_bins, device="cuda", pack_bits=True, pack_nibbles=True):
         import torch
         nb = np.ascontiguousarray(np.asarray(n_bins, dtype=np.int32))
         self.n_bins_host = nb
@@ -241,9 +248,9 @@ class FeatureTable:
         self.bin_offset_host = off
         self.total_bins = int(off[-1])
         bf = np.repeat(np.arange(self.n_features, dtype=np.int32), nb)
-        self.layout, self.max_block_bins, cf, fc = gbdt_choose_layout(nb, pack_bits)
+        self.layout, self.max_block_bins, cf, fc = gbdt_choose_layout(nb, pack_bits, pack_nibbles)
         self.col_feature_host, self.feature_col_host = cf, fc
-        self.mapped = bool(pack_bits)
+        self.mapped = bool(pack_bits or pack_nibbles)
         self.col_feature = torch.from_numpy(cf).to(device) if self.mapped else None
         self.feature_col = torch.from_numpy(fc).to(device) if self.mapped else None
         self.n_bins = torch.from_numpy(nb).to(device)
@@ -268,9 +275,10 @@ class RowBuffer:
         self.row_capacity = max(self.n_rows, 1)
         self.n_blocks, self.block_features, self.block_stride = L.n_blocks, L.block_features, L.block_stride
         self.n_bit_features, self.bit_stride = L.n_bit_features, L.bit_stride
+        self.n_nib_features, self.nib_stride = L.n_nib_features, L.nib_stride
         self.n_features = ft.n_features
         self.byte_bytes = self.n_blocks * self.row_capacity * self.block_stride
-        self.bins = torch.zeros(self.byte_bytes + self.row_capacity * self.bit_stride,
+        self.bins = torch.zeros(self.byte_bytes + self.row_capacity * (self.bit_stride + self.nib_stride),
                                 dtype=torch.uint8, device=device)
         self.q = torch.zeros(self.row_capacity, dtype=torch.int64, device=device)
         self.rid = torch.zeros(self.row_capacity, dtype=torch.int32, device=device) if with_rid else None
@@ -278,7 +286,8 @@ class RowBuffer:
     def matrix(self) -> Matrix:
         return Matrix(_ptr(self.bins), self.n_rows, self.row_capacity, self.n_features,
                       self.n_blocks, self.block_features, self.block_stride, self.n_bit_features,
-                      self.bit_stride, _ptr(self.ft.col_feature), _ptr(self.ft.feature_col))
+                      self.bit_stride, _ptr(self.ft.col_feature), _ptr(self.ft.feature_col),
+                      self.n_nib_features, self.nib_stride)
 
     def rows(self, identity_rid=False) -> Rows:
         return Rows(self.matrix(), _ptr(self.q), None if (identity_rid or self.rid is None) else _ptr(self.rid))
@@ -288,7 +297,7 @@ class RowBuffer:
         import torch
         n, F = self.n_rows, self.n_features
         out = torch.zeros((n, F), dtype=torch.uint8, device=self.bins.device)
-        nbc = F - self.n_bit_features
+        nbc = F - self.n_bit_features - self.n_nib_features
         cf = torch.from_numpy(self.ft.col_feature_host).long().to(self.bins.device)
         if self.n_blocks > 0:
             b = self.bins[: self.byte_bytes].view(self.n_blocks, self.row_capacity, self.block_stride)[:, :n]
@@ -297,10 +306,19 @@ class RowBuffer:
             out[:, cf[:nbc]] = torch.cat(cols, dim=1)
         if self.n_bit_features > 0:
             nw = self.bit_stride // 4
-            w = self.bins[self.byte_bytes:].view(torch.int32).view(self.row_capacity, nw)[:n]
+            w = self.bins[self.byte_bytes: self.byte_bytes + self.row_capacity * self.bit_stride].view(
+                torch.int32).view(self.row_capacity, nw)[:n]
             k = torch.arange(self.n_bit_features, device=self.bins.device)
             bitv = (w[:, k // 32] >> (k % 32)) & 1
-            out[:, cf[nbc:]] = bitv.to(torch.uint8)
+            out[:, cf[F - self.n_bit_features:]] = bitv.to(torch.uint8)
+        if self.n_nib_features > 0:
+            nw = self.nib_stride // 4
+            base = self.byte_bytes + self.row_capacity * self.bit_stride
+            w = self.bins[base: base + self.row_capacity * self.nib_stride].view(torch.int32).view(
+                self.row_capacity, nw)[:n]
+            k = torch.arange(self.n_nib_features, device=self.bins.device)
+            nib = (w[:, k // 8] >> (4 * (k % 8))) & 15
+            out[:, cf[nbc: nbc + self.n_nib_features]] = nib.to(torch.uint8)
         return out
 
 
@@ -414,11 +432,12 @@ def gbdt_predict_noalloc(X: Matrix, trees, n_nodes, n_trees, tree_stride, base_s
 class Dataset:
     """Bins packed on the device in the column-blocked layout, plus labels."""
 
-    def __init__(self, bins_rowmajor, label, n_bins, device="cuda", use_skip_bins=True, pack_bits=True):
+    def __init__(self, bins_rowmajor, label, n_bins, device="cuda", use_skip_bins=True, pack_bits=True,
+                 pack_nibbles=True):
         import torch
         bins_rowmajor = np.ascontiguousarray(bins_rowmajor, dtype=np.uint8)
         self.n_rows, self.n_features = bins_rowmajor.shape
-        self.ft = FeatureTable(n_bins, device, pack_bits=pack_bits)
+        self.ft = FeatureTable(n_bins, device, pack_bits=pack_bits, pack_nibbles=pack_nibbles)
         self.use_skip_bins = use_skip_bins
         self.X = RowBuffer(self.ft, self.n_rows, device, with_rid=False)
         self.label = torch.from_numpy(np.ascontiguousarray(label, dtype=np.float32)).to(device)

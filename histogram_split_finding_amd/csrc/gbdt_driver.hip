@@ -520,9 +520,11 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   // always for the logistic objective's 31-bit grids
   const bool q32 = logistic || driver_q32(n);
   const int32_t part_tile = part_tile_rows(n, X->n_blocks, q32);
-  const int32_t target = hist_target_tiles(X->n_blocks + (X->n_bit_features > 0 ? 1 : 0));
+  const int32_t target = hist_target_tiles(X->n_blocks + (X->n_bit_features > 0 ? 1 : 0) +
+                                           (X->n_nib_features > 0 ? 1 : 0));
   const int32_t min_rows =
-      hist_min_tile_rows(ft->total_bins, int64_t(X->n_blocks) * X->block_stride + X->bit_stride);
+      hist_min_tile_rows(ft->total_bins,
+                         int64_t(X->n_blocks) * X->block_stride + X->bit_stride + X->nib_stride);
   for (int32_t d = 0; d <= D; ++d) {
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
     const int64_t rows_build = d == 0 ? n : n / 2;

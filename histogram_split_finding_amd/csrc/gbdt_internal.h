@@ -82,6 +82,7 @@ constexpr int kReduceGrid = 512;      // at most this many reduction workgroups
 constexpr int kLdsHistBudgetBins = 8192;  // LDS slots (8 bytes) of one histogram workgroup: 64 KiB
 constexpr int kHistRowSlots = 32;          // LDS slots per bin row of a byte block's histogram
 constexpr int kHistMaxBlockStride = 32;    // bytes per row of a byte block, at most (8 dwords)
+constexpr int kNibSlots = 16;              // LDS slots per feature of the nibble block's histogram
 
 // Work assignment of one tile (written by the planner).  A partition plan
 // also carries the node's split, so a partition tile needs no second load.

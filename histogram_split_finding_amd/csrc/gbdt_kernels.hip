@@ -669,6 +669,136 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
   }
 }
 
+// The nibble block: lanes are (row group, word of 8 nibble features).  Each
+// row's word gives 8 cells; every cell except the feature's skip bin (its
+// most frequent bin, derived from the tile total at the end) adds the packed
+// (q << bits) + 1 to its LDS slot with one 64-bit atomic.  Feature k's 16
+// slots are rotated by k (slot 16 k + ((b + k) & 15)), so equal bins of
+// different features fall in different bank pairs, and each lane walks its 8
+// nibbles starting at nibble (row group & 7), so the lanes of a quarter-wave
+// address several features at once.
+template <int NW, bool Q32>
+__device__ void hist_nib_block(const TileDesc& td, int32_t tile, const uint8_t* __restrict__ bins,
+                               int64_t row_capacity, int32_t n_blocks, int32_t block_stride,
+                               int32_t n_features, int32_t n_bit, int32_t bit_stride, int32_t n_nib,
+                               int32_t nib_stride, const int32_t* __restrict__ col_feature,
+                               const void* __restrict__ q, const int32_t* __restrict__ bin_offset,
+                               const int32_t* __restrict__ skip_bin, int32_t total_bins,
+                               int32_t lds_bins, int32_t bits, int64_t* __restrict__ hist_g,
+                               uint32_t* __restrict__ hist_cnt, uint64_t* __restrict__ partial,
+                               WsCtrl* __restrict__ ctrl, uint64_t* lds, uint32_t* s_skip,
+                               uint64_t* sh_tot) {
+  const int32_t nbyte = n_features - n_bit - n_nib;  // nibble k is column nbyte + k
+  const int32_t nwords = nib_stride >> 2;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  if (kNibSlots * n_nib > lds_bins || nwords > kMaxBitWords) {
+    if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
+    return;
+  }
+  for (int32_t b = threadIdx.x; b < kNibSlots * n_nib; b += blockDim.x) lds[b] = 0ull;
+  // per word: the skip bins of its 8 features as nibbles (16 = none: no cell matches)
+  for (int32_t w = threadIdx.x; w < nwords; w += blockDim.x) {
+    uint32_t sk = 0u, none = 0u;
+    for (int32_t t = 0; t < 8; ++t) {
+      const int32_t kk = 8 * w + t;
+      int32_t b = -1;
+      if (kk < n_nib && skip_bin != nullptr) {
+        int32_t f = col_feature[nbyte + kk];
+        f = f < 0 ? 0 : (f >= n_features ? n_features - 1 : f);
+        b = skip_bin[f];
+      }
+      if (b >= 0 && b < 16)
+        sk |= uint32_t(b) << (4 * t);
+      else
+        none |= 1u << t;
+    }
+    s_skip[2 * w] = sk;
+    s_skip[2 * w + 1] = none;
+  }
+  __syncthreads();
+  const int64_t r0 = td.r0;
+  const int64_t r1 = td.r1;
+  const int32_t rpi = (int32_t)blockDim.x / nwords;  // rows per step
+  const int32_t w = (int32_t)threadIdx.x % nwords;
+  const int32_t rg = (int32_t)threadIdx.x / nwords;
+  const uint32_t skw = s_skip[2 * (w < nwords ? w : 0)];
+  const uint32_t none = s_skip[2 * (w < nwords ? w : 0) + 1];
+  const int32_t kbase = 8 * w;
+  const int32_t nval = n_nib - kbase < 8 ? n_nib - kbase : 8;  // this word's features
+  const int32_t rot = rg & 7;
+  const uint32_t* __restrict__ wb = reinterpret_cast<const uint32_t*>(
+      bins + int64_t(n_blocks) * row_capacity * block_stride + row_capacity * bit_stride);
+  uint64_t tot = 0ull;
+  constexpr int BATCH = 4;
+  if (rg < rpi) {
+    for (int64_t r = r0 + rg; r < r1; r += int64_t(BATCH) * rpi) {
+      uint32_t x[BATCH];
+      int64_t qq[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int64_t rr = r + int64_t(u) * rpi;
+        const bool ok = rr < r1;
+        x[u] = ok ? wb[rr * nwords + w] : 0u;
+        qq[u] = ok ? q_at<Q32>(q, rr) : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int64_t rr = r + int64_t(u) * rpi;
+        if (rr >= r1) continue;
+        const uint64_t pk = ((uint64_t)qq[u] << bits) + 1ull;
+        tot += pk;
+        const uint32_t diff = x[u] ^ skw;
+#pragma unroll 1
+        for (int m = 0; m < 8; ++m) {
+          const int32_t t = (m + rot) & 7;
+          if (t >= nval) continue;
+          const bool is_skip = ((diff >> (4 * t)) & 15u) == 0u && !((none >> t) & 1u);
+          if (is_skip) continue;
+          const int32_t kk = kbase + t;
+          const int32_t b = (int32_t)((x[u] >> (4 * t)) & 15u);
+          __hip_atomic_fetch_add(&lds[kNibSlots * kk + ((b + kk) & 15)], pk, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+    }
+  }
+  const uint64_t t0 = wave_sum_dpp((w == 0 && rg < rpi) ? tot : 0ull);
+  if (lane == 0) sh_tot[wid] = t0;
+  __syncthreads();
+  uint64_t tile_total = 0ull;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) tile_total += sh_tot[ww];
+  // each feature's skip bin: the tile total minus its other bins
+  for (int32_t kk = threadIdx.x; kk < n_nib; kk += blockDim.x) {
+    const uint32_t sk = s_skip[2 * (kk >> 3)], nn = s_skip[2 * (kk >> 3) + 1];
+    if ((nn >> (kk & 7)) & 1u) continue;
+    const int32_t sb = (int32_t)((sk >> (4 * (kk & 7))) & 15u);
+    uint64_t rest = 0ull;
+    for (int32_t b = 0; b < 16; ++b)
+      if (b != sb) rest += lds[kNibSlots * kk + ((b + kk) & 15)];
+    lds[kNibSlots * kk + ((sb + kk) & 15)] = tile_total - rest;
+  }
+  __syncthreads();
+  const uint64_t mask = (1ull << bits) - 1ull;
+  const int32_t v = td.node;
+  for (int32_t e = threadIdx.x; e < kNibSlots * n_nib; e += blockDim.x) {
+    const int32_t kk = e >> 4, b = e & 15;
+    int32_t f = col_feature[nbyte + kk];
+    f = f < 0 ? 0 : (f >= n_features ? n_features - 1 : f);
+    const int32_t lo = bin_offset[f];
+    if (b >= bin_offset[f + 1] - lo) continue;
+    const uint64_t xv = lds[kNibSlots * kk + ((b + kk) & 15)];
+    if (td.ntiles == 1) {
+      const uint64_t c = xv & mask;
+      hist_g[int64_t(v) * total_bins + lo + b] = (int64_t)(xv - c) >> bits;
+      hist_cnt[int64_t(v) * total_bins + lo + b] = (uint32_t)c;
+    } else {
+      partial[int64_t(tile) * total_bins + lo + b] = xv;
+    }
+  }
+}
+
 // One workgroup = one (tile of one node's rows, column block); the block
 // index n_blocks is the bit block (hist_bit_block).
 //
@@ -699,8 +829,10 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
 // byte value stays inside the allocation; the first lds_bins / 32 rows are
 // zeroed and read back.  A node covered by one tile writes its decoded
 // histogram straight to hist; otherwise the tile writes its packed partial
-// (global bin order) for k_hist_reduce.  BITS: the layout has a bit block.
-template <int D, bool BITS, bool Q32>
+// (global bin order) for k_hist_reduce.  NARROW: 0 byte blocks only; 1 a bit
+// block too; 2 a nibble block (and maybe a bit block) too -- each variant
+// carries only the code its layout needs.
+template <int D, int NARROW, bool Q32>
 __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_hist(
     const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t n_blocks,
     int32_t block_features, int32_t block_stride, int32_t n_features, int32_t n_bit,
@@ -708,7 +840,8 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     const int32_t* __restrict__ bin_offset, const int32_t* __restrict__ skip_bin,
     int32_t total_bins, int32_t lds_bins, const TileDesc* __restrict__ desc, int32_t bits,
     int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
-    uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl, const int32_t* __restrict__ guard) {
+    uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl, const int32_t* __restrict__ guard,
+    int32_t n_nib, int32_t nib_stride) {
   static_assert(D == 1 || D == 2 || D == 4 || D == 8, "lanes per row");
   if (failed(guard)) return;
   constexpr int RPW = 64 / D;               // rows per wave per batch
@@ -729,21 +862,29 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   const int32_t tile = blockIdx.x;
   const int32_t blk = blockIdx.y;
   const TileDesc td = desc[tile];
-  if (BITS && blk == n_blocks) {  // the bit block
-    if (td.node < 0 || n_bit <= 0) return;
-    if ((bit_stride >> 2) > kMaxBitWords) {  // the host checks bit_stride <= 4 * kMaxBitWords
-      if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
-      return;
+  if (NARROW > 0 && blk >= n_blocks) {  // the narrow blocks: bits, then nibbles
+    if (td.node < 0) return;
+    if (blk == n_blocks && n_bit > 0) {
+      if ((bit_stride >> 2) > kMaxBitWords) {  // the host checks bit_stride <= 4 * kMaxBitWords
+        if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
+        return;
+      }
+      hist_bit_block<NW, Q32>(td, td.slot, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
+                         bit_stride, col_feature, q, bin_offset, skip_bin, total_bins, lds_bins, bits,
+                         hist_g, hist_cnt, partial, ctrl, lds, s_inv, s_bit, sh_tot);
+    } else if constexpr (NARROW == 2) {
+      if (blk == n_blocks + (n_bit > 0 ? 1 : 0) && n_nib > 0)
+        hist_nib_block<NW, Q32>(td, td.slot, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
+                           bit_stride, n_nib, nib_stride, col_feature, q, bin_offset, skip_bin,
+                           total_bins, lds_bins, bits, hist_g, hist_cnt, partial, ctrl, lds, s_inv,
+                           sh_tot);
     }
-    hist_bit_block<NW, Q32>(td, td.slot, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
-                       bit_stride, col_feature, q, bin_offset, skip_bin, total_bins, lds_bins, bits,
-                       hist_g, hist_cnt, partial, ctrl, lds, s_inv, s_bit, sh_tot);
     return;
   }
   if (blk >= n_blocks) return;
   // The column table (lane j of wave 0: column f0 + j) is needed only by the
   // output, so its loads are issued here and consumed after the row loop.
-  const int32_t nbc = n_features - n_bit;
+  const int32_t nbc = n_features - n_bit - n_nib;
   const int32_t f0 = blk * block_features;  // first byte column of the block
   const int32_t c1 = f0 + block_features < nbc ? f0 + block_features : nbc;
   const int32_t nf = c1 - f0;
@@ -1716,7 +1857,7 @@ __device__ __forceinline__ void row_put(uint8_t* p, const RowData<ND>& d, bool n
 // last nt_tiles tiles write with streaming (non-temporal) stores, so the
 // level does not end with its last rows as dirty lines in the memory-side
 // cache, whose write-back would fall into the next kernel.
-template <int ND, int K, bool Q32OUT>
+template <int ND, int K, bool Q32OUT, bool NIB>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const void* __restrict__ sq,
     const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, void* __restrict__ dq,
@@ -1724,7 +1865,8 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     int32_t block_stride, int32_t n_features, int32_t n_bit, int32_t bit_stride,
     const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
     int32_t qsh /* log2 of the source q's element size: 2 (int32) or 3 (int64) */,
-    int32_t nt_tiles /* the plan's last nt_tiles tiles store with streaming stores */) {
+    int32_t nt_tiles /* the plan's last nt_tiles tiles store with streaming stores */,
+    int32_t n_nib, int32_t nib_stride) {
   static_assert(K == 2 || K == 4 || K == 8, "rows per thread");
   constexpr int TILE = K * kPartThreads;
   constexpr int KE = 2;       // rows per thread whose block 0 is loaded before the look-back
@@ -1750,19 +1892,27 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   // a listed node must carry a valid split; otherwise nothing is moved, the
   // tile still publishes (so later tiles never wait on it) and the error word
   // is set.  The descriptor's feature is the split's matrix column: a byte
-  // column (c < n_features - n_bit) or a bit of the bit block.
+  // column (c < nbyte = n_features - n_nib - n_bit), a nibble (c - nbyte) of
+  // the nibble block or a bit (c - (n_features - n_bit)) of the bit block.
   const bool split_ok = td.split_valid && td.feature >= 0 && td.feature < n_features;
   const int32_t rows = split_ok ? rows_all : 0;
-  const int32_t nbc = n_features - n_bit;
+  const int32_t nbc = n_features - n_bit;  // the first bit column
+  const int32_t nbyte = nbc - n_nib;
   const int32_t sc = split_ok ? td.feature : 0;
   const bool fbit = sc >= nbc;
-  const int32_t fblk = fbit ? 0 : sc / block_features;
-  const int32_t fcol = fbit ? 0 : sc % block_features;
-  const int32_t fk = fbit ? sc - nbc : 0;
+  const bool fnib = NIB && !fbit && sc >= nbyte;
+  const bool fnarrow = fbit || fnib;
+  const int32_t fblk = fnarrow ? 0 : sc / block_features;
+  const int32_t fcol = fnarrow ? 0 : sc % block_features;
+  const int32_t fk = fbit ? sc - nbc : (fnib ? sc - nbyte : 0);
   const int32_t nwords = bit_stride >> 2;
   const uint8_t* __restrict__ fcolp = sbins + int64_t(fblk) * row_capacity * block_stride + fcol;
   const uint8_t* __restrict__ sbits = sbins + int64_t(n_blocks) * row_capacity * block_stride;
-  const uint32_t* __restrict__ fwordp = reinterpret_cast<const uint32_t*>(sbits) + (fk >> 5);
+  const uint8_t* __restrict__ snibs = sbits + row_capacity * bit_stride;
+  // the split feature's word in a narrow block (bit k: word k >> 5; nibble k: word k >> 3)
+  const uint32_t* __restrict__ fwordp =
+      fbit ? reinterpret_cast<const uint32_t*>(sbits) + (fk >> 5)
+           : reinterpret_cast<const uint32_t*>(snibs) + (fk >> 3);
   // loads that need only the descriptor, unconditional (a row past the tile
   // end rereads its last row and is ignored), so none waits behind a branch
   int32_t fb[K];
@@ -1778,17 +1928,17 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   // its byte comes from those registers: a separate load of the split bytes
   // would bring each line of the tile in twice when the cache has evicted it
   // before the rows are read.  (uniform)
-  const bool from_rows = KE == K && !fbit && fblk == 0 && n_blocks > 0;
+  const bool from_rows = KE == K && !fnarrow && fblk == 0 && n_blocks > 0;
   if (rows > 0) {
     const char* __restrict__ tq = reinterpret_cast<const char*>(sq) + (r0 << qsh);
     const uint32_t lr = (uint32_t)(rows - 1);
     // otherwise one dword load per row (the byte's aligned dword, or the
     // bit's word), issued first: loads complete in order, so the flags wait
     // only for these while the rows are still in flight
-    const uint32_t frow = fbit ? (uint32_t)nwords * 4u : bs;
+    const uint32_t frow = fbit ? (uint32_t)nwords * 4u : (fnib ? (uint32_t)nib_stride : bs);
     if (!from_rows) {
       const uint8_t* __restrict__ tf =
-          (fbit ? reinterpret_cast<const uint8_t*>(fwordp) : fcolp - (fcol & 3)) + r0 * int64_t(frow);
+          (fnarrow ? reinterpret_cast<const uint8_t*>(fwordp) : fcolp - (fcol & 3)) + r0 * int64_t(frow);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
@@ -1814,8 +1964,8 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
 #pragma unroll
       for (int k = 0; k < KE; ++k) fb[k] = (int32_t)((row_dword<ND>(rd[0][k], fdw) >> fsh) & 0xffu);
     } else {
-      const uint32_t fsh = fbit ? (uint32_t)(fk & 31) : 8u * (uint32_t)(fcol & 3);
-      const uint32_t fmask = fbit ? 1u : 0xffu;
+      const uint32_t fsh = fbit ? (uint32_t)(fk & 31) : (fnib ? 4u * (uint32_t)(fk & 7) : 8u * (uint32_t)(fcol & 3));
+      const uint32_t fmask = fbit ? 1u : (fnib ? 15u : 0xffu);
 #pragma unroll
       for (int k = 0; k < K; ++k) fb[k] = (int32_t)(((uint32_t)fb[k] >> fsh) & fmask);
     }
@@ -1980,15 +2130,15 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       ++b;
     }
   }
-  // the bit block: nwords words per row, 4 at a time, rows in groups of at
-  // most 4 per thread
-  if (n_bit > 0) {
+  // the narrow blocks (bit words, then nibble words): nw words per row, 4 at
+  // a time, rows in groups of at most 4 per thread
+  auto move_words = [&](const uint8_t* __restrict__ sblk, uint8_t* __restrict__ dblk, int32_t nw) {
     constexpr int GB = K < 4 ? K : 4;
-    const uint32_t rowb = (uint32_t)nwords * 4u;
-    const uint8_t* __restrict__ tw = sbits + r0 * int64_t(rowb);
-    uint8_t* __restrict__ dw = dbins + int64_t(n_blocks) * row_capacity * block_stride;
+    const uint32_t rowb = (uint32_t)nw * 4u;
+    const uint8_t* __restrict__ tw = sblk + r0 * int64_t(rowb);
+    uint8_t* __restrict__ dw = dblk;
     int32_t w0 = 0;
-    for (; w0 + 4 <= nwords; w0 += 4) {
+    for (; w0 + 4 <= nw; w0 += 4) {
 #pragma unroll
       for (int kb = 0; kb < K; kb += GB) {
         RowData<4> x[GB];
@@ -2007,7 +2157,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
         }
       }
     }
-    for (; w0 < nwords; ++w0) {
+    for (; w0 < nw; ++w0) {
       uint32_t x[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
@@ -2025,7 +2175,10 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
         }
       }
     }
-  }
+  };
+  uint8_t* __restrict__ dbits = dbins + int64_t(n_blocks) * row_capacity * block_stride;
+  if (n_bit > 0) move_words(sbits, dbits, nwords);
+  if (NIB && n_nib > 0) move_words(snibs, dbits + row_capacity * bit_stride, nib_stride >> 2);
 }
 
 // ------------------------------------------------------ prediction update --
@@ -2066,7 +2219,8 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
                                                        uint2* __restrict__ ctab,
                                                        double* __restrict__ lval,
                                                        int32_t* __restrict__ driver_nodes,
-                                                       WsCtrl* __restrict__ ctrl) {
+                                                       WsCtrl* __restrict__ ctrl, int32_t bit_stride,
+                                                       int32_t n_nib) {
   __shared__ int32_t s_leaves;
   __shared__ int32_t s_bad;
   // driver mode (driver_nodes = the tree's node count): a tree whose kernels
@@ -2100,12 +2254,17 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
       e.x = kBadTag;
     } else {
       const int32_t c = feature_col != nullptr ? feature_col[nd.x] : nd.x;
-      const int32_t nbc = n_features - n_bit;
+      const int32_t nbc = n_features - n_bit;  // the first bit column
+      const int32_t nbyte = nbc - n_nib;       // the first nibble column
       uint32_t loc;
-      if (c >= 0 && c < nbc) {
+      if (c >= 0 && c < nbyte) {
         const int32_t blk = c / block_features;
         const int32_t byte = blk * block_stride + (c - blk * block_features);
         loc = (uint32_t)(byte >> 2) | ((uint32_t)(8 * (byte & 3)) << 6);
+      } else if (c >= nbyte && c < nbc) {  // a nibble: after the bit words in the row's dwords
+        const int32_t kk = c - nbyte;
+        loc = (uint32_t)(n_blocks * (block_stride >> 2) + (bit_stride >> 2) + (kk >> 3)) |
+              ((uint32_t)(4 * (kk & 7)) << 6) | (2u << 11);
       } else {
         const int32_t kk = c - nbc;
         loc = (uint32_t)(n_blocks * (block_stride >> 2) + (kk >> 5)) | ((uint32_t)(kk & 31) << 6) |
@@ -2135,13 +2294,13 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
 // ND1 > 0: one byte block of ND1 dwords per row, loaded with one or two
 // wide loads (a 16-byte load and one of 4, 8 or 12 bytes), then the bit
 // words; ND1 == 0: any layout, one dword per load.
-template <int MAXDW, int ROWS, bool TREE_IN_LDS, int ND1>
+template <int MAXDW, int ROWS, bool TREE_IN_LDS, int ND1, bool NIB>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
     double* __restrict__ pred, int64_t n, const uint8_t* __restrict__ bins, int64_t row_capacity,
     int32_t n_blocks, int32_t block_stride, int32_t bit_stride,
     const uint2* __restrict__ ctab_g, const double* __restrict__ lval,
     const int32_t* __restrict__ n_nodes_dev, int32_t max_nodes, double eta,
-    WsCtrl* __restrict__ ctrl) {
+    WsCtrl* __restrict__ ctrl, int32_t nib_stride) {
   static_assert((MAXDW & (MAXDW - 1)) == 0, "MAXDW is a power of two");
   extern __shared__ uint64_t smem[];
   int32_t nn = *n_nodes_dev;
@@ -2160,8 +2319,10 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
   const int32_t dw = block_stride >> 2;
   const int32_t ndw = n_blocks * dw;            // byte-block dwords of a row
   const int32_t nwords = bit_stride >> 2;       // then its bit words
+  const int32_t nnw = nib_stride >> 2;          // then its nibble words
   const uint32_t* __restrict__ bitw =
       reinterpret_cast<const uint32_t*>(bins + int64_t(n_blocks) * row_capacity * block_stride);
+  const uint32_t* __restrict__ nibw = bitw + row_capacity * nwords;
   bool bad = false;
   const int64_t stride = int64_t(gridDim.x) * kUpdThreads * ROWS;
   for (int64_t base = int64_t(blockIdx.x) * kUpdThreads * ROWS + threadIdx.x; base < n;
@@ -2185,6 +2346,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
       const uint32_t* __restrict__ bp =
           reinterpret_cast<const uint32_t*>(bins + i * block_stride);
       const uint32_t* __restrict__ wp = bitw + i * nwords;
+      const uint32_t* __restrict__ np = nibw + i * nnw;
       if constexpr (ND1 > 0) {
         static_assert(ND1 <= MAXDW, "the byte block fits the row registers");
         RowData<ND1> rdat;
@@ -2196,8 +2358,9 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
 #pragma unroll
         for (int x = ND1; x < MAXDW; ++x) {
           const bool in_bits = x - ND1 < nwords;
-          const uint32_t val = *(in_bits ? wp + (x - ND1) : bp);
-          row[u][x] = in_bits ? val : 0u;
+          const bool in_nibs = NIB && !in_bits && x - ND1 - nwords < nnw;
+          const uint32_t val = *(in_bits ? wp + (x - ND1) : (in_nibs ? np + (x - ND1 - nwords) : bp));
+          row[u][x] = (in_bits || in_nibs) ? val : 0u;
         }
       } else {
         int32_t xb = 0;
@@ -2206,9 +2369,11 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
         for (int x = 0; x < MAXDW; ++x) {
           const bool in_bytes = x < ndw;
           const bool in_bits = !in_bytes && x < ndw + nwords;
-          const uint32_t* p = in_bytes ? bp + boff + xb : (in_bits ? wp + (x - ndw) : bp);
+          const bool in_nibs = NIB && !in_bytes && !in_bits && x < ndw + nwords + nnw;
+          const uint32_t* p = in_bytes ? bp + boff + xb
+                                       : (in_bits ? wp + (x - ndw) : (in_nibs ? np + (x - ndw - nwords) : bp));
           const uint32_t val = *p;
-          row[u][x] = (in_bytes || in_bits) ? val : 0u;
+          row[u][x] = (in_bytes || in_bits || in_nibs) ? val : 0u;
           if (in_bytes && ++xb == dw) {
             xb = 0;
             boff += (row_capacity * block_stride) >> 2;
@@ -2236,7 +2401,8 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
           for (int x = 0; x < w / 2; ++x) t[x] = hi ? t[2 * x + 1] : t[2 * x];
         }
         const uint32_t shift = (e.y >> 6) & 31u;
-        const uint32_t vmask = (e.y & (1u << 11)) ? 1u : 0xffu;
+        const uint32_t wcode = (e.y >> 11) & 3u;  // 0 byte, 1 bit, 2 nibble
+        const uint32_t vmask = wcode == 1u ? 1u : (wcode == 2u ? 15u : 0xffu);
         const uint32_t bv = (t[0] >> shift) & vmask;
         const int32_t next = (int32_t)e.x + (bv <= (e.y >> 16) ? 0 : 1);
         const bool moving = fin[u] == 0u && !leaf && !badn;
@@ -2262,17 +2428,17 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
   if (bad) dev_error(&ctrl->err, GBDT_E_INTERNAL);
 }
 
-template <int MAXDW, int ND1 = 0>
+template <int MAXDW, int ND1 = 0, bool NIB = false>
 static void launch_update(bool in_lds, int rows, dim3 grid, size_t lds, hipStream_t s, double* pred,
                           int64_t n, const gbdt_matrix* X, const uint2* ctab, const double* lval,
                           const int32_t* n_nodes, int32_t max_nodes, double eta, WsCtrl* ctrl) {
   // two rows per lane only where both rows' bins fit registers without scratch
   constexpr int R2 = MAXDW <= 16 ? 2 : 1;
-  auto kern = in_lds ? (rows == 2 ? k_update<MAXDW, R2, true, ND1> : k_update<MAXDW, 1, true, ND1>)
-                     : (rows == 2 ? k_update<MAXDW, R2, false, ND1> : k_update<MAXDW, 1, false, ND1>);
+  auto kern = in_lds ? (rows == 2 ? k_update<MAXDW, R2, true, ND1, NIB> : k_update<MAXDW, 1, true, ND1, NIB>)
+                     : (rows == 2 ? k_update<MAXDW, R2, false, ND1, NIB> : k_update<MAXDW, 1, false, ND1, NIB>);
   hipLaunchKernelGGL(kern, grid, dim3(kUpdThreads), lds, s, pred, n, X->bins, X->row_capacity,
                      X->n_blocks, X->block_stride, X->bit_stride, ctab, lval, n_nodes, max_nodes, eta,
-                     ctrl);
+                     ctrl, X->nib_stride);
 }
 
 // ------------------------------------------------------- setup: packing --
@@ -2285,10 +2451,11 @@ __global__ void __launch_bounds__(256) k_pack(const uint8_t* __restrict__ src, i
                                               int32_t n_bit, int32_t bit_stride,
                                               const int32_t* __restrict__ col_feature,
                                               const int32_t* __restrict__ n_bins,
-                                              WsCtrl* __restrict__ ctrl) {
+                                              WsCtrl* __restrict__ ctrl, int32_t n_nib,
+                                              int32_t nib_stride) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  const int32_t nbc = F - n_bit;
+  const int32_t nbc = F - n_bit - n_nib;
   bool bad = false;
   for (int32_t b = 0; b < n_blocks; ++b) {
     uint8_t* d = dst + int64_t(b) * row_capacity * block_stride + i * block_stride;
@@ -2312,11 +2479,28 @@ __global__ void __launch_bounds__(256) k_pack(const uint8_t* __restrict__ src, i
       for (int32_t t = 0; t < 32; ++t) {
         const int32_t kk = 32 * w + t;
         if (kk >= n_bit) break;
-        int32_t f = col_feature[nbc + kk];
+        int32_t f = col_feature[F - n_bit + kk];  // bit k is column F - n_bit + k
         f = f < 0 ? 0 : (f >= F ? F - 1 : f);
         const uint8_t x = src[i * F + f];
         bad |= (int32_t)x >= n_bins[f] || x > 1;
         word |= uint32_t(x & 1) << t;
+      }
+      wd[w] = word;
+    }
+  }
+  if (n_nib > 0) {
+    uint32_t* wd = reinterpret_cast<uint32_t*>(dst + int64_t(n_blocks) * row_capacity * block_stride +
+                                               row_capacity * bit_stride + i * nib_stride);
+    for (int32_t w = 0; w < (nib_stride >> 2); ++w) {
+      uint32_t word = 0u;
+      for (int32_t t = 0; t < 8; ++t) {
+        const int32_t kk = 8 * w + t;
+        if (kk >= n_nib) break;
+        int32_t f = col_feature[nbc + kk];
+        f = f < 0 ? 0 : (f >= F ? F - 1 : f);
+        const uint8_t x = src[i * F + f];
+        bad |= (int32_t)x >= n_bins[f] || x > 15;
+        word |= uint32_t(x & 15) << (4 * t);
       }
       wd[w] = word;
     }
@@ -2390,9 +2574,15 @@ int check_matrix(const gbdt_matrix& X) {
     return fail(GBDT_E_ARG, "n_bit_features out of range");
   if ((X.col_feature == nullptr) != (X.feature_col == nullptr))
     return fail(GBDT_E_ARG, "col_feature and feature_col must both be set or both be NULL");
-  if (X.col_feature == nullptr && X.n_bit_features != 0)
-    return fail(GBDT_E_ARG, "a bit block needs the column maps");
-  const int32_t nbc = X.n_features - X.n_bit_features;
+  if (X.n_nib_features < 0 || X.n_nib_features > X.n_features - X.n_bit_features)
+    return fail(GBDT_E_ARG, "n_nib_features out of range");
+  if (X.col_feature == nullptr && (X.n_bit_features != 0 || X.n_nib_features != 0))
+    return fail(GBDT_E_ARG, "bit and nibble blocks need the column maps");
+  if (X.n_nib_features > 0 &&
+      (X.nib_stride < 4 * ((X.n_nib_features + 7) / 8) || (X.nib_stride & 3) || X.nib_stride > 4 * kMaxBitWords))
+    return fail(GBDT_E_ARG, "bad nib_stride");
+  if (X.n_nib_features == 0 && X.nib_stride != 0) return fail(GBDT_E_ARG, "nib_stride without nibble features");
+  const int32_t nbc = X.n_features - X.n_bit_features - X.n_nib_features;
   if (nbc > 0) {
     if (X.block_features < 1 || X.block_stride < X.block_features || (X.block_stride & 3) ||
         X.block_stride > 1024)
@@ -2424,7 +2614,8 @@ bool same_layout(const gbdt_matrix& a, const gbdt_matrix& b) {
          a.n_blocks == b.n_blocks && a.block_features == b.block_features &&
          a.block_stride == b.block_stride && a.n_bit_features == b.n_bit_features &&
          a.bit_stride == b.bit_stride && a.col_feature == b.col_feature &&
-         a.feature_col == b.feature_col;
+         a.feature_col == b.feature_col && a.n_nib_features == b.n_nib_features &&
+         a.nib_stride == b.nib_stride;
 }
 
 int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft) {
@@ -2435,11 +2626,13 @@ int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft) {
   if (!src.q) return fail(GBDT_E_ARG, "q is null");
   if (ft.max_block_bins < 1 || ft.max_block_bins > kLdsHistBudgetBins)
     return fail(GBDT_E_UNSUPPORTED, "max_block_bins outside the LDS histogram budget");
-  if (src.X.n_features > src.X.n_bit_features &&
+  if (src.X.n_features > src.X.n_bit_features + src.X.n_nib_features &&
       (src.X.block_stride > kHistMaxBlockStride || src.X.block_features > kHistRowSlots))
     return fail(GBDT_E_UNSUPPORTED, "a column block wider than 32 bytes");
   if (2 * src.X.n_bit_features > ft.max_block_bins)
     return fail(GBDT_E_SHAPE, "max_block_bins below 2 slots per bit feature");
+  if (kNibSlots * src.X.n_nib_features > ft.max_block_bins)
+    return fail(GBDT_E_SHAPE, "max_block_bins below 16 slots per nibble feature");
   return GBDT_OK;
 }
 
@@ -2455,9 +2648,9 @@ int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst) {
   return GBDT_OK;
 }
 
-template <bool B, bool Q>
-static auto hist_kernel(int D) -> decltype(&k_hist<8, B, Q>) {
-  return D == 8 ? k_hist<8, B, Q> : D == 4 ? k_hist<4, B, Q> : D == 2 ? k_hist<2, B, Q> : k_hist<1, B, Q>;
+template <int N, bool Q>
+static auto hist_kernel(int D) -> decltype(&k_hist<8, N, Q>) {
+  return D == 8 ? k_hist<8, N, Q> : D == 4 ? k_hist<4, N, Q> : D == 2 ? k_hist<2, N, Q> : k_hist<1, N, Q>;
 }
 
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
@@ -2465,8 +2658,8 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
                 WsCtrl* ctrl, hipStream_t s, bool q32, bool guard) {
   const int64_t n_rows = src.X.n_rows > 0 ? src.X.n_rows : 1;
   const int32_t bits = pack_bits_for(n_rows);
-  const bool has_bytes = src.X.n_features > src.X.n_bit_features;
-  const bool has_bits = src.X.n_bit_features > 0;
+  const bool has_bytes = src.X.n_features > src.X.n_bit_features + src.X.n_nib_features;
+  const bool has_bits = src.X.n_bit_features > 0 || src.X.n_nib_features > 0;  // narrow blocks
   // byte blocks: 256 bin rows of 32 slots (any byte value stays inside);
   // the bit block: 2 slots per bit feature
   // (both within kLdsHistBudgetBins slots), then the kernel's small tables
@@ -2474,15 +2667,20 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
                      sizeof(int32_t) * size_t(2 * kHistRowSlots + kMaxBitWords + kBitStage);
   const int32_t nd = has_bytes ? src.X.block_stride / 4 : 1;  // dwords per row (<= 8)
   const int D = nd <= 1 ? 1 : (nd <= 2 ? 2 : (nd <= 4 ? 4 : 8));
-  auto kern = has_bits ? (q32 ? hist_kernel<true, true>(D) : hist_kernel<true, false>(D))
-                       : (q32 ? hist_kernel<false, true>(D) : hist_kernel<false, false>(D));
-  const unsigned gy = (unsigned)(src.X.n_blocks + (has_bits ? 1 : 0));
+  const int narrow = src.X.n_nib_features > 0 ? 2 : (src.X.n_bit_features > 0 ? 1 : 0);
+  auto kern = narrow == 2 ? (q32 ? hist_kernel<2, true>(D) : hist_kernel<2, false>(D))
+              : narrow == 1 ? (q32 ? hist_kernel<1, true>(D) : hist_kernel<1, false>(D))
+                            : (q32 ? hist_kernel<0, true>(D) : hist_kernel<0, false>(D));
+  (void)has_bits;
+  const unsigned gy = (unsigned)(src.X.n_blocks + (src.X.n_bit_features > 0 ? 1 : 0) +
+                                 (src.X.n_nib_features > 0 ? 1 : 0));
   diag_begin(kDiagHist, s);
   hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles, gy), dim3(kHistThreads), lds, s, src.X.bins,
                      src.X.row_capacity, src.X.n_blocks, src.X.block_features, src.X.block_stride,
                      src.X.n_features, src.X.n_bit_features, src.X.bit_stride, src.X.col_feature,
                      src.q, ft.bin_offset, ft.skip_bin, ft.total_bins, ft.max_block_bins, desc, bits,
-                     hist_g, hist_cnt, hpart, ctrl, guard ? &ctrl->err : nullptr);
+                     hist_g, hist_cnt, hpart, ctrl, guard ? &ctrl->err : nullptr, src.X.n_nib_features,
+                     src.X.nib_stride);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist");
   return GBDT_OK;
@@ -2924,17 +3122,17 @@ __global__ void __launch_bounds__(kBoundThreads) k_bounds_quantile(const float* 
   }
 }
 
-template <int K, bool Q>
-static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K, Q>) {
+template <int K, bool Q, bool N>
+static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K, Q, N>) {
   switch (nd) {
-    case 1: return k_partition<1, K, Q>;
-    case 2: return k_partition<2, K, Q>;
-    case 3: return k_partition<3, K, Q>;
-    case 4: return k_partition<4, K, Q>;
-    case 5: return k_partition<5, K, Q>;
-    case 6: return k_partition<6, K, Q>;
-    case 7: return k_partition<7, K, Q>;
-    case 8: return k_partition<8, K, Q>;
+    case 1: return k_partition<1, K, Q, N>;
+    case 2: return k_partition<2, K, Q, N>;
+    case 3: return k_partition<3, K, Q, N>;
+    case 4: return k_partition<4, K, Q, N>;
+    case 5: return k_partition<5, K, Q, N>;
+    case 6: return k_partition<6, K, Q, N>;
+    case 7: return k_partition<7, K, Q, N>;
+    case 8: return k_partition<8, K, Q, N>;
     default: return nullptr;
   }
 }
@@ -2947,18 +3145,22 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
   // With the large tiles (one block, >= 4M rows), the plan's last tiles,
   // about kPartStreamBytes of rows, store streaming (see k_partition).
   const int64_t row_bytes = int64_t(src.X.n_blocks) * src.X.block_stride + src.X.bit_stride +
-                            (qout32 ? 4 : 8);
+                            src.X.nib_stride + (qout32 ? 4 : 8);
   const int64_t tile_bytes = int64_t(tile_rows) * (row_bytes > 0 ? row_bytes : 1);
   const int32_t nt_tiles = tile_rows == kPartTileRowsLarge
                                ? (int32_t)std::min<int64_t>(max_tiles, kPartStreamBytes / tile_bytes)
                                : 0;
-  decltype(&k_partition<1, 2, false>) kern = nullptr;
+  decltype(&k_partition<1, 2, false, false>) kern = nullptr;
+  const bool nib = src.X.n_nib_features > 0;
   if (tile_rows == 2 * kPartThreads)
-    kern = qout32 ? partition_kernel<2, true>(nd) : partition_kernel<2, false>(nd);
+    kern = nib ? (qout32 ? partition_kernel<2, true, true>(nd) : partition_kernel<2, false, true>(nd))
+               : (qout32 ? partition_kernel<2, true, false>(nd) : partition_kernel<2, false, false>(nd));
   else if (tile_rows == 4 * kPartThreads)
-    kern = qout32 ? partition_kernel<4, true>(nd) : partition_kernel<4, false>(nd);
+    kern = nib ? (qout32 ? partition_kernel<4, true, true>(nd) : partition_kernel<4, false, true>(nd))
+               : (qout32 ? partition_kernel<4, true, false>(nd) : partition_kernel<4, false, false>(nd));
   else if (tile_rows == 8 * kPartThreads)
-    kern = qout32 ? partition_kernel<8, true>(nd) : partition_kernel<8, false>(nd);
+    kern = nib ? (qout32 ? partition_kernel<8, true, true>(nd) : partition_kernel<8, false, true>(nd))
+               : (qout32 ? partition_kernel<8, true, false>(nd) : partition_kernel<8, false, false>(nd));
   else
     return fail(GBDT_E_INTERNAL, "unsupported partition tile size");
   if (kern == nullptr) return fail(GBDT_E_UNSUPPORTED, "a column block wider than 32 bytes");
@@ -2967,7 +3169,7 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
                      src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
                      src.X.block_features, src.X.block_stride, src.X.n_features,
                      src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl, qin32 ? 2 : 3,
-                     nt_tiles);
+                     nt_tiles, src.X.n_nib_features, src.X.nib_stride);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_partition");
   return GBDT_OK;
@@ -3046,7 +3248,7 @@ size_t gbdt_workspace_bytes(int64_t n_rows, int32_t max_list, int32_t total_bins
   return ws_layout(n_rows, max_list, total_bins).total;
 }
 
-int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t pack_bits,
+int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t pack,
                        gbdt_matrix* X, int32_t* max_block_bins, int32_t* col_feature_host,
                        int32_t* feature_col_host) {
   if (!X || !n_bins_host || !max_block_bins || !col_feature_host || !feature_col_host)
@@ -3054,19 +3256,31 @@ int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t p
   if (n_features < 1 || n_features > GBDT_MAX_FEATURES) return fail(GBDT_E_ARG, "n_features out of range");
   for (int32_t f = 0; f < n_features; ++f)
     if (n_bins_host[f] < 1 || n_bins_host[f] > GBDT_MAX_BINS) return fail(GBDT_E_ARG, "n_bins out of range");
-  // byte columns first (feature order), then the bit features (feature order)
+  // byte columns first (feature order), then the nibble features, then the
+  // bit features (each in feature order)
+  const bool bits = (pack & GBDT_PACK_BITS) != 0;
+  const bool nibs = (pack & GBDT_PACK_NIBBLES) != 0;
+  auto is_bit = [&](int32_t f) { return bits && n_bins_host[f] <= 2; };
+  auto is_nib = [&](int32_t f) { return nibs && !is_bit(f) && n_bins_host[f] <= 16; };
   std::vector<int32_t> cols;
-  int32_t n_bit = 0;
+  int32_t n_bit = 0, n_nib = 0;
   for (int32_t f = 0; f < n_features; ++f)
-    if (!(pack_bits && n_bins_host[f] <= 2)) cols.push_back(f);
+    if (!is_bit(f) && !is_nib(f)) cols.push_back(f);
   const int32_t nbc = (int32_t)cols.size();
   for (int32_t f = 0; f < n_features; ++f)
-    if (pack_bits && n_bins_host[f] <= 2) {
+    if (is_nib(f)) {
+      cols.push_back(f);
+      ++n_nib;
+    }
+  for (int32_t f = 0; f < n_features; ++f)
+    if (is_bit(f)) {
       cols.push_back(f);
       ++n_bit;
     }
   if (2 * n_bit > kLdsHistBudgetBins) return fail(GBDT_E_UNSUPPORTED, "too many bit features for the LDS budget");
-  int32_t worst = 2 * n_bit;
+  if (kNibSlots * n_nib > kLdsHistBudgetBins)
+    return fail(GBDT_E_UNSUPPORTED, "too many nibble features for the LDS budget");
+  int32_t worst = 2 * n_bit > kNibSlots * n_nib ? 2 * n_bit : kNibSlots * n_nib;
   int32_t bf = 0, nb = 0;
   if (nbc > 0) {
     // fewest blocks of equal width, at most 32 columns (8 dwords per row);
@@ -3084,6 +3298,8 @@ int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t p
   X->block_stride = nbc > 0 ? ((bf + 3) & ~3) : 0;
   X->n_bit_features = n_bit;
   X->bit_stride = n_bit > 0 ? 4 * ((n_bit + 31) / 32) : 0;
+  X->n_nib_features = n_nib;
+  X->nib_stride = n_nib > 0 ? 4 * ((n_nib + 7) / 8) : 0;
   X->col_feature = nullptr;
   X->feature_col = nullptr;
   for (int32_t c = 0; c < n_features; ++c) {
@@ -3218,7 +3434,8 @@ int gbdt_pack_matrix(const uint8_t* rowmajor, const gbdt_matrix* dst, const gbdt
     hipLaunchKernelGGL(k_pack, dim3((unsigned)grid), dim3(256), 0, s, rowmajor, n,
                        dst->n_features, dst->bins, dst->row_capacity, dst->n_blocks,
                        dst->block_features, dst->block_stride, dst->n_bit_features,
-                       dst->bit_stride, dst->col_feature, ft->n_bins, ctrl);
+                       dst->bit_stride, dst->col_feature, ft->n_bins, ctrl, dst->n_nib_features,
+                       dst->nib_stride);
     diag_end(s);
     GBDT_LAUNCH_CHECK("k_pack");
   }
@@ -3326,7 +3543,7 @@ int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* node
   if (n == 0) return GBDT_OK;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return fail(GBDT_E_ARG, "workspace is null or misaligned");
   WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(static_cast<char*>(ws));
-  const int64_t row_bytes = int64_t(X->n_blocks) * X->block_stride + X->bit_stride;
+  const int64_t row_bytes = int64_t(X->n_blocks) * X->block_stride + X->bit_stride + X->nib_stride;
   if (row_bytes > kUpdMaxRowBytes) return fail(GBDT_E_UNSUPPORTED, "rows wider than 256 bytes");
   const WsLayout L = ws_layout(n, 1, 1);
   const size_t tables = size_t(max_nodes) * sizeof(uint2) + size_t((max_nodes + 1) / 2) * sizeof(double);
@@ -3338,7 +3555,8 @@ int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* node
   diag_begin(kDiagUpdate, s);
   hipLaunchKernelGGL(k_compact_tree, dim3(1), dim3(1024), 0, s, nodes, n_nodes, max_nodes,
                      X->n_features, X->feature_col, X->n_blocks, X->block_features, X->block_stride,
-                     X->n_bit_features, ctab, lval, driver ? n_nodes : nullptr, ctrl);
+                     X->n_bit_features, ctab, lval, driver ? n_nodes : nullptr, ctrl, X->bit_stride,
+                     X->n_nib_features);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_compact_tree");
   // the node table goes to LDS (8 B per node); leaf values stay in global
@@ -3352,7 +3570,20 @@ int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* node
   if (grid > 512) grid = 512;  // persistent: the tree is copied to LDS once per workgroup
   diag_begin(kDiagUpdate, s);
   const int32_t nd1 = X->n_blocks == 1 ? X->block_stride / 4 : 0;  // one byte block: wide loads
-  if (ndw <= 8 && nd1 > 0) {
+  if (X->n_nib_features > 0) {  // a nibble block: the general row loads
+    if (ndw <= 8)
+      launch_update<8, 0, true>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval,
+                                n_nodes, max_nodes, learning_rate, ctrl);
+    else if (ndw <= 16)
+      launch_update<16, 0, true>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval,
+                                 n_nodes, max_nodes, learning_rate, ctrl);
+    else if (ndw <= 32)
+      launch_update<32, 0, true>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval,
+                                 n_nodes, max_nodes, learning_rate, ctrl);
+    else
+      launch_update<64, 0, true>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval,
+                                 n_nodes, max_nodes, learning_rate, ctrl);
+  } else if (ndw <= 8 && nd1 > 0) {
     auto go = [&](auto tag) {
       launch_update<8, decltype(tag)::value>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X,
                                              ctab, lval, n_nodes, max_nodes, learning_rate, ctrl);
@@ -3408,10 +3639,11 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   int32_t* hmulti = reinterpret_cast<int32_t*>(w + L.hmulti);
   TileDesc* hdesc = reinterpret_cast<TileDesc*>(w + L.hdesc);
   uint64_t* hpart = reinterpret_cast<uint64_t*>(w + L.hpart);
-  const int32_t gy = src->X.n_blocks + (src->X.n_bit_features > 0 ? 1 : 0);
+  const int32_t gy = src->X.n_blocks + (src->X.n_bit_features > 0 ? 1 : 0) + (src->X.n_nib_features > 0 ? 1 : 0);
   const int32_t T = hist_tile_rows(
       rows_bound, src->X.n_rows, hist_target_tiles(gy),
-      hist_min_tile_rows(ft->total_bins, int64_t(src->X.n_blocks) * src->X.block_stride + src->X.bit_stride));
+      hist_min_tile_rows(ft->total_bins, int64_t(src->X.n_blocks) * src->X.block_stride + src->X.bit_stride +
+                                             src->X.nib_stride));
   const int64_t max_tiles = (rows_bound + T - 1) / T + list_cap;
   if (max_tiles > L.hpart_tiles) return fail(GBDT_E_SHAPE, "too many histogram tiles for the workspace");
   diag_begin(kDiagPlan, s);

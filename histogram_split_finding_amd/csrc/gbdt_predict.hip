@@ -51,12 +51,13 @@ __global__ void __launch_bounds__(256) k_compact_ensemble(
     const gbdt_node* __restrict__ trees, const int32_t* __restrict__ n_nodes, int32_t stride,
     int32_t n_features, const int32_t* __restrict__ feature_col, int32_t n_blocks,
     int32_t block_features, int32_t block_stride, int32_t n_bit, uint2* __restrict__ ctab,
-    double* __restrict__ lval, WsCtrl* __restrict__ ctrl) {
+    double* __restrict__ lval, WsCtrl* __restrict__ ctrl, int32_t bit_stride, int32_t n_nib) {
   const int32_t t = blockIdx.x;
   const gbdt_node* __restrict__ tree = trees + int64_t(t) * stride;
   const int32_t nn = n_nodes[t];
   bool bad = nn < 1 || nn > stride || tree[0].depth != 0;
-  const int32_t nbc = n_features - n_bit;
+  const int32_t nbc = n_features - n_bit;  // the first bit column
+  const int32_t nbyte = nbc - n_nib;       // the first nibble column
   for (int32_t v = threadIdx.x; v < (nn > 0 && nn <= stride ? nn : 0); v += blockDim.x) {
     const gbdt_node nd = tree[v];
     uint2 e;
@@ -76,10 +77,14 @@ __global__ void __launch_bounds__(256) k_compact_ensemble(
         bad = true;
       } else {
         uint32_t loc;
-        if (c < nbc) {
+        if (c < nbyte) {
           const int32_t blk = c / block_features;
           const int32_t byte = blk * block_stride + (c - blk * block_features);
           loc = (uint32_t)(byte >> 2) | ((uint32_t)(8 * (byte & 3)) << 6);
+        } else if (c < nbc) {  // a nibble, after the bit words in the row's dwords
+          const int32_t kk = c - nbyte;
+          loc = (uint32_t)(n_blocks * (block_stride >> 2) + (bit_stride >> 2) + (kk >> 3)) |
+                ((uint32_t)(4 * (kk & 7)) << 6) | (2u << 11);
         } else {
           const int32_t kk = c - nbc;
           loc = (uint32_t)(n_blocks * (block_stride >> 2) + (kk >> 5)) | ((uint32_t)(kk & 31) << 6) |
@@ -95,25 +100,30 @@ __global__ void __launch_bounds__(256) k_compact_ensemble(
 }
 
 // Row i's dwords: byte block b's run of block_stride / 4 dwords for each b in
-// turn, then the bit words; entries past them are 0.  The loads are
-// unconditional (uniform pointer selects), so all are in flight together.
+// turn, then the bit words, then the nibble words; entries past them are 0.
+// The loads are unconditional (uniform pointer selects), so all are in flight
+// together.
 template <int MAXDW>
 __device__ __forceinline__ void load_row(const uint8_t* __restrict__ bins, int64_t i,
                                          int64_t row_capacity, int32_t block_stride, int32_t ndw,
                                          int32_t nwords, const uint32_t* __restrict__ bitw,
+                                         int32_t nnw, const uint32_t* __restrict__ nibw,
                                          uint32_t (&row)[MAXDW]) {
   const int32_t dw = block_stride >> 2;
   const uint32_t* __restrict__ bp = reinterpret_cast<const uint32_t*>(bins + i * block_stride);
   const uint32_t* __restrict__ wp = bitw + i * nwords;
+  const uint32_t* __restrict__ np = nibw + i * nnw;
   int32_t xb = 0;
   int64_t boff = 0;
 #pragma unroll
   for (int x = 0; x < MAXDW; ++x) {
     const bool in_bytes = x < ndw;
     const bool in_bits = !in_bytes && x < ndw + nwords;
-    const uint32_t* p = in_bytes ? bp + boff + xb : (in_bits ? wp + (x - ndw) : bp);
+    const bool in_nibs = !in_bytes && !in_bits && x < ndw + nwords + nnw;
+    const uint32_t* p =
+        in_bytes ? bp + boff + xb : (in_bits ? wp + (x - ndw) : (in_nibs ? np + (x - ndw - nwords) : bp));
     const uint32_t val = *p;
-    row[x] = (in_bytes || in_bits) ? val : 0u;
+    row[x] = (in_bytes || in_bits || in_nibs) ? val : 0u;
     if (in_bytes && ++xb == dw) {
       xb = 0;
       boff += (row_capacity * block_stride) >> 2;
@@ -128,7 +138,7 @@ __global__ void __launch_bounds__(kPredThreads) k_predict(
     double* __restrict__ out, int64_t n, const uint8_t* __restrict__ bins, int64_t row_capacity,
     int32_t n_blocks, int32_t block_stride, int32_t bit_stride, const uint2* __restrict__ ctab_g,
     const double* __restrict__ lval, int32_t t0, int32_t t1, int32_t stride, double base,
-    int32_t started, double eta, const int32_t* __restrict__ guard) {
+    int32_t started, double eta, const int32_t* __restrict__ guard, int32_t nib_stride) {
   static_assert((MAXDW & (MAXDW - 1)) == 0, "MAXDW is a power of two");
   extern __shared__ uint64_t smem[];
   if (failed(guard)) return;
@@ -142,15 +152,17 @@ __global__ void __launch_bounds__(kPredThreads) k_predict(
   }
   const int32_t ndw = n_blocks * (block_stride >> 2);
   const int32_t nwords = bit_stride >> 2;
+  const int32_t nnw = nib_stride >> 2;
   const uint32_t* __restrict__ bitw =
       reinterpret_cast<const uint32_t*>(bins + int64_t(n_blocks) * row_capacity * block_stride);
+  const uint32_t* __restrict__ nibw = bitw + row_capacity * nwords;
   const int64_t gstride = int64_t(gridDim.x) * kPredThreads;
   for (int64_t i0 = int64_t(blockIdx.x) * kPredThreads + threadIdx.x; i0 - threadIdx.x < n;
        i0 += gstride) {
     const bool live = i0 < n;
     const int64_t i = live ? i0 : n - 1;  // a valid row: the loads need no branch
     uint32_t row[MAXDW];
-    load_row<MAXDW>(bins, i, row_capacity, block_stride, ndw, nwords, bitw, row);
+    load_row<MAXDW>(bins, i, row_capacity, block_stride, ndw, nwords, bitw, nnw, nibw, row);
     double pv = started ? out[i] : base;
     for (int32_t t = 0; t < t1 - t0; ++t) {
       const uint2* __restrict__ tab = ctab + int64_t(t) * stride;
@@ -171,7 +183,8 @@ __global__ void __launch_bounds__(kPredThreads) k_predict(
           for (int x = 0; x < w / 2; ++x) s[x] = hi ? s[2 * x + 1] : s[2 * x];
         }
         const uint32_t shift = (e.y >> 6) & 31u;
-        const uint32_t vmask = (e.y & (1u << 11)) ? 1u : 0xffu;
+        const uint32_t wcode = (e.y >> 11) & 3u;  // 0 byte, 1 bit, 2 nibble
+        const uint32_t vmask = wcode == 1u ? 1u : (wcode == 2u ? 15u : 0xffu);
         const uint32_t bv = (s[0] >> shift) & vmask;
         const int32_t next = (int32_t)e.x + (bv <= (e.y >> 16) ? 0 : 1);
         const bool moving = fin == 0u && !leaf;
@@ -193,7 +206,7 @@ void launch_predict(bool in_lds, dim3 grid, size_t lds, hipStream_t s, double* o
   auto kern = in_lds ? k_predict<MAXDW, true> : k_predict<MAXDW, false>;
   hipLaunchKernelGGL(kern, grid, dim3(kPredThreads), lds, s, out, n, X.bins, X.row_capacity,
                      X.n_blocks, X.block_stride, X.bit_stride, ctab, lval, t0, t1, stride, base,
-                     started, eta, guard);
+                     started, eta, guard, X.nib_stride);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -314,7 +327,7 @@ int predict_impl(const gbdt_matrix* X, const gbdt_node* trees, const int32_t* n_
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return fail(GBDT_E_ARG, "workspace is null or misaligned");
   if (ws_bytes < gbdt_predict_workspace_bytes(n_trees, tree_stride))
     return fail(GBDT_E_ARG, "workspace smaller than gbdt_predict_workspace_bytes()");
-  const int64_t row_bytes = int64_t(X->n_blocks) * X->block_stride + X->bit_stride;
+  const int64_t row_bytes = int64_t(X->n_blocks) * X->block_stride + X->bit_stride + X->nib_stride;
   if (row_bytes > kPredMaxRowBytes) return fail(GBDT_E_UNSUPPORTED, "rows wider than 256 bytes");
   char* w = static_cast<char*>(ws);
   WsCtrl* ctrl = reinterpret_cast<WsCtrl*>(w);
@@ -325,7 +338,8 @@ int predict_impl(const gbdt_matrix* X, const gbdt_node* trees, const int32_t* n_
     diag_begin(kDiagPredict, s);
     hipLaunchKernelGGL(k_compact_ensemble, dim3((unsigned)n_trees), dim3(256), 0, s, trees, n_nodes,
                        tree_stride, X->n_features, X->feature_col, X->n_blocks, X->block_features,
-                       X->block_stride, X->n_bit_features, ctab, lval, ctrl);
+                       X->block_stride, X->n_bit_features, ctab, lval, ctrl, X->bit_stride,
+                       X->n_nib_features);
     diag_end(s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "k_compact_ensemble");

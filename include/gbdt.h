@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GBDT_ABI_VERSION 3
+#define GBDT_ABI_VERSION 4
 #define GBDT_MAX_DEPTH 16       /* deepest tree the level loop supports */
 #define GBDT_MAX_FEATURES 4096
 #define GBDT_MAX_BINS 256       /* bins per feature */
@@ -111,11 +111,23 @@ typedef enum {
  * feature) is bit (k & 31) of word k >> 5.  bit_stride is a multiple of 4 and
  * at least 4 * ceil(n_bit_features / 32).
  *
- * col_feature (device, [n_features]) names the feature of byte column c
- * (c < n_features - n_bit_features), then of bit k (entry
- * n_features - n_bit_features + k); feature_col (device, [n_features]) is its
- * inverse.  Both NULL means the identity (byte column c is feature c), which
- * requires n_bit_features == 0.  Host struct holding device pointers.
+ * Nibble block (n_nib_features > 0): features of 3 to 16 bins stored as one
+ * 4-bit cell each, eight to a word (the ExaBoost PR's commit that stores two
+ * cells per byte when every column fits 16 bins, here for the columns that
+ * do).  A row-major [row_capacity][nib_stride] array of uint32 words starting
+ * after the bit block, at bins + n_blocks * row_capacity * block_stride +
+ * row_capacity * bit_stride; nibble k of a row is bits 4 (k & 7) .. 4 (k & 7)
+ * + 3 of word k >> 3.  nib_stride is a multiple of 4 and at least
+ * 4 * ceil(n_nib_features / 8).
+ *
+ * Columns are numbered byte columns first, then the nibble features, then the
+ * bit features: with nbyte = n_features - n_nib_features - n_bit_features,
+ * column c < nbyte is a byte column, nbyte + k is nibble k and
+ * n_features - n_bit_features + k is bit k.  col_feature (device,
+ * [n_features]) names each column's feature; feature_col (device,
+ * [n_features]) is its inverse.  Both NULL means the identity (byte column c
+ * is feature c), which requires no bit or nibble features.  Host struct
+ * holding device pointers.
  */
 typedef struct gbdt_matrix {
   uint8_t* bins;
@@ -129,6 +141,8 @@ typedef struct gbdt_matrix {
   int32_t bit_stride;
   const int32_t* col_feature;
   const int32_t* feature_col;
+  int32_t n_nib_features;
+  int32_t nib_stride;
 } gbdt_matrix;
 
 /*
@@ -258,16 +272,20 @@ int gbdt_choose_blocking(int32_t n_features, const int32_t* n_bins_host, gbdt_ma
                          int32_t* max_block_bins /* host */);
 
 /*
- * Layout with a bit block: with pack_bits != 0 every feature of at most 2
- * bins becomes a bit (in feature order) and the others byte columns (in
- * feature order); with pack_bits == 0 as gbdt_choose_blocking.  Writes the
+ * Layout with narrow blocks.  pack is a set of flags: GBDT_PACK_BITS makes
+ * every feature of at most 2 bins a bit, GBDT_PACK_NIBBLES makes every
+ * feature of 3 to 16 bins a 4-bit cell; the others are byte columns (each
+ * kind in feature order); with pack == 0 as gbdt_choose_blocking.  Writes the
  * layout fields of *X (the map pointers are left NULL: the caller uploads
  * col_feature_host / feature_col_host, host arrays of n_features entries that
  * this call fills, and stores the device copies in X), and *max_block_bins
  * (the LDS slots one histogram workgroup needs: 32 per bin of the widest
- * byte feature, or 2 per bit feature for the bit block).
+ * byte feature, 2 per bit feature for the bit block, 16 per nibble feature
+ * for the nibble block).
  */
-int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t pack_bits,
+#define GBDT_PACK_BITS 1
+#define GBDT_PACK_NIBBLES 2
+int gbdt_choose_layout(int32_t n_features, const int32_t* n_bins_host, int32_t pack,
                        gbdt_matrix* X /* host */, int32_t* max_block_bins /* host */,
                        int32_t* col_feature_host /* host */, int32_t* feature_col_host /* host */);
 
