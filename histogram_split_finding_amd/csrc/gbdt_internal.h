@@ -50,29 +50,20 @@ constexpr int kGradBlocks = 1024;     // grid of the gradient kernels
 #define GBDT_TWO_GROUPS __attribute__((amdgpu_waves_per_eu(8, 8)))
 
 constexpr int kPartTileRows = 2048;   // rows per partition tile (the smaller size; bounds use it)
-// Bytes of the partition's output (the plan's last tiles) written with
-// streaming stores when the large tiles are used: a level's row copy that
-// ends with that much dirty data in the memory-side cache leaves its
-// write-back to the next kernel, the histogram of the next level, which then
-// streams its rows at a fraction of its rate.  Measured on 50M x 28 rows:
-// histogram 1.81 -> 1.51 ms, partition 8.40 -> 8.63 ms per tree; with
-// several column blocks (10M x 100) streaming stores slowed the partition
-// by 18 % and the large tiles are not used there.
-constexpr int64_t kPartStreamBytes = int64_t(512) << 20;
-constexpr int kPartTileRowsMid = 4096;
-constexpr int kPartTileRowsLarge = 8192;
+constexpr int kPartTileRowsLarge = 4096;
 constexpr int64_t kPartLargeRows = int64_t(1) << 22;  // matrices from this size take the larger tiles
 
-// Rows per partition tile for a matrix of n rows in n_blocks byte blocks
-// whose moved q is int32 (q32) or int64: larger tiles carry more bytes per
-// latency chain (descriptor, flags, look-back) on large matrices of
-// one block (8192 rows when q moves as int32; with int64 q that kernel would
-// exceed the 64 registers of two workgroups per CU, so 4096); small matrices
-// keep more tiles than workgroup slots, and several blocks need the
-// registers for double-buffering the blocks.
-inline int32_t part_tile_rows(int64_t n_rows, int32_t n_blocks, bool q32) {
-  if (n_rows < kPartLargeRows || n_blocks > 1) return kPartTileRows;
-  return q32 ? kPartTileRowsLarge : kPartTileRowsMid;
+// Rows per partition tile for a matrix of n rows in n_blocks byte blocks of
+// block_stride bytes whose q moves as int32 (q32) or int64: large matrices of
+// one block of at most 28 bytes with int32 q take 4096-row tiles (four rows
+// per thread, each loaded whole before the look-back), which halves the
+// tiles, and so the look-back chain, of the 2048-row ones; wider rows or
+// int64 q would take that kernel past the 64 registers of two workgroups per
+// CU.  Small matrices keep more tiles than workgroup slots, and several
+// blocks need the registers for double-buffering the blocks.
+inline int32_t part_tile_rows(int64_t n_rows, int32_t n_blocks, int32_t block_stride, bool q32) {
+  if (n_rows < kPartLargeRows || n_blocks > 1 || block_stride > 28 || !q32) return kPartTileRows;
+  return kPartTileRowsLarge;
 }
 constexpr int kHistMinTileRows = 1024;
 constexpr int kHistTargetTiles = 1024;    // workgroups per histogram launch to aim for

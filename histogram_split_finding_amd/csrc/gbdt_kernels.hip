@@ -1780,28 +1780,6 @@ __device__ __forceinline__ void store_dwords(uint8_t* p, const uint4& v) {
   if constexpr (N == 2) *reinterpret_cast<uint2*>(p) = make_uint2(v.x, v.y);
   if constexpr (N == 1) *reinterpret_cast<uint32_t*>(p) = v.x;
 }
-// The same as streaming (non-temporal) stores: the lines are not kept in the
-// caches as dirty data for a later kernel to write back.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-#define GBDT_GLOBAL __attribute__((address_space(1)))
-template <int N>
-__device__ __forceinline__ void store_dwords_nt(GBDT_GLOBAL uint8_t* p, const uint4& v) {
-  if constexpr (N == 4) {
-    const u32x4_t t = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(t, (GBDT_GLOBAL u32x4_t*)p);
-  }
-  if constexpr (N == 3) {
-    const u32x3_t t = {v.x, v.y, v.z};
-    __builtin_nontemporal_store(t, (GBDT_GLOBAL u32x3_t*)p);
-  }
-  if constexpr (N == 2) {
-    const u32x2_t t = {v.x, v.y};
-    __builtin_nontemporal_store(t, (GBDT_GLOBAL u32x2_t*)p);
-  }
-  if constexpr (N == 1) __builtin_nontemporal_store(v.x, (GBDT_GLOBAL uint32_t*)p);
-}
 // Dword i (uniform, < ND) of a row held in registers.
 template <int ND>
 __device__ __forceinline__ uint32_t row_dword(const RowData<ND> d, uint32_t i) {
@@ -1825,23 +1803,6 @@ __device__ __forceinline__ void row_store(uint8_t* p, const RowData<ND>& d) {
   store_dwords<(ND < 4 ? ND : 4)>(p, d.a);
   if constexpr (ND > 4) store_dwords<ND - 4>(p + 16, d.b);
 }
-template <int ND>
-__device__ __forceinline__ void row_store_nt(uint8_t* p, const RowData<ND>& d) {
-  // (the empty asm keeps the compiler from merging these stores with the
-  // plain ones of the other branch, which would drop the streaming hint)
-  asm volatile("" : "+v"(p));
-  GBDT_GLOBAL uint8_t* const g = (GBDT_GLOBAL uint8_t*)p;
-  store_dwords_nt<(ND < 4 ? ND : 4)>(g, d.a);
-  if constexpr (ND > 4) store_dwords_nt<ND - 4>(g + 16, d.b);
-}
-template <int ND>
-__device__ __forceinline__ void row_put(uint8_t* p, const RowData<ND>& d, bool nt) {
-  if (nt)
-    row_store_nt<ND>(p, d);
-  else
-    row_store<ND>(p, d);
-}
-
 // One workgroup per tile of K * kPartThreads rows of a splitting node (tile
 // = workgroup id).  Thread t owns rows t + k kPartThreads of the tile and
 // moves each whole row itself: the row's bytes of a column block (ND dwords)
@@ -1849,14 +1810,13 @@ __device__ __forceinline__ void row_put(uint8_t* p, const RowData<ND>& d, bool n
 // accesses cover 64 consecutive source rows and two runs of destinations
 // (left and right).  The tile descriptor carries the node's split, so right
 // after it arrives the workgroup issues every load that does not depend on
-// the destinations: the split feature's byte (or bit), q, row ids and block
-// 0 of the first two rows per thread.  Then it ballots the go-left flags,
-// publishes its left count, looks back for the exclusive prefix (decoupled
-// look-back), loads block 0 of its other rows and stores; the other blocks
-// and the bit block are loaded and stored row by row after that.  The plan's
-// last nt_tiles tiles write with streaming (non-temporal) stores, so the
-// level does not end with its last rows as dirty lines in the memory-side
-// cache, whose write-back would fall into the next kernel.
+// the destinations: q, row ids and, for every row of the thread, the first
+// moved block -- the one holding the split feature, whose byte is then taken
+// from the registers, so no line of the tile is fetched twice (a narrow
+// split feature adds one dword load per row for its bit or nibble).  Then it
+// ballots the go-left flags, publishes its left count, looks back for the
+// exclusive prefix (decoupled look-back) and stores; the other blocks and
+// the narrow blocks are loaded and stored row by row after that.
 template <int ND, int K, bool Q32OUT, bool NIB>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const void* __restrict__ sq,
@@ -1865,12 +1825,9 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     int32_t block_stride, int32_t n_features, int32_t n_bit, int32_t bit_stride,
     const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
     int32_t qsh /* log2 of the source q's element size: 2 (int32) or 3 (int64) */,
-    int32_t nt_tiles /* the plan's last nt_tiles tiles store with streaming stores */,
     int32_t n_nib, int32_t nib_stride) {
-  static_assert(K == 2 || K == 4 || K == 8, "rows per thread");
+  static_assert(K == 2 || K == 4, "rows per thread");
   constexpr int TILE = K * kPartThreads;
-  constexpr int KE = 2;       // rows per thread whose block 0 is loaded before the look-back
-  constexpr int NG = K / KE;  // groups of KE rows; block 0 of group g + 1 is loaded before g is stored
   constexpr int NCNT = K * kPartWaves;  // per-(row k, wave) left counts
   // an int32 destination q is the low half of the source element
   using QT = typename std::conditional<Q32OUT, int32_t, int64_t>::type;
@@ -1881,7 +1838,6 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   const int32_t tile = (int32_t)blockIdx.x;
   const int32_t total = ctrl->plan_total;
   if (tile >= total) return;
-  const bool nt = tile >= total - nt_tiles;  // (uniform)
   const TileDesc td = desc[tile];
   const int32_t tfirst = td.tfirst;
   const int32_t tlast = td.tfirst + td.ntiles - 1;
@@ -1917,18 +1873,21 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   // end rereads its last row and is ignored), so none waits behind a branch
   int32_t fb[K];
   QT qv[K];
-  RowData<ND> rd[2][KE];  // block 0 of two groups of rows (group g in rd[g & 1])
+  RowData<ND> rd[K];  // the first moved block of each row of the thread
   // Addresses are a uniform base at the tile's first row plus a 32-bit lane
-  // offset (a tile spans at most 8192 rows of at most 512 bytes).
-  const uint8_t* __restrict__ tb = sbins + r0 * block_stride;
+  // offset (a tile spans at most 4096 rows of at most 512 bytes).
+  // block 0 here means the first block moved: the split feature's own block
+  // (any block for a narrow split feature), so its byte always comes from
+  // the rows' registers; the other blocks follow in order
+  const int32_t b0 = fnarrow ? 0 : fblk;
+  const int64_t b0off = int64_t(b0) * row_capacity * block_stride;
+  const uint8_t* __restrict__ tb = sbins + b0off + r0 * block_stride;
   const uint32_t bs = (uint32_t)block_stride;
-  // (the split feature's bytes first: loads complete in order, and the
-  // flags wait only for them while the rows are still in flight)
-  // With every row's block 0 loaded early and the split feature in block 0,
-  // its byte comes from those registers: a separate load of the split bytes
-  // would bring each line of the tile in twice when the cache has evicted it
-  // before the rows are read.  (uniform)
-  const bool from_rows = KE == K && !fnarrow && fblk == 0 && n_blocks > 0;
+  // With every row's first block (the split feature's) loaded early, the
+  // split byte comes from those registers: a separate load of the split
+  // bytes would bring each line of the tile in twice when the cache has
+  // evicted it before the rows are read.  (uniform)
+  const bool from_rows = !fnarrow && n_blocks > 0;
   if (rows > 0) {
     const char* __restrict__ tq = reinterpret_cast<const char*>(sq) + (r0 << qsh);
     const uint32_t lr = (uint32_t)(rows - 1);
@@ -1956,13 +1915,13 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       qv[k] = *reinterpret_cast<const QT*>(tq + (ic << qsh));
       // with no byte block (ND == 1, block_stride 0) this rereads the first
       // dword of the bit block, and the value is never stored
-      if (k < KE) row_load<ND>(tb + ic * bs, rd[0][k]);
+      row_load<ND>(tb + ic * bs, rd[k]);
     }
     if (from_rows) {
       const uint32_t fdw = (uint32_t)fcol >> 2;
       const uint32_t fsh = 8u * (uint32_t)(fcol & 3);
 #pragma unroll
-      for (int k = 0; k < KE; ++k) fb[k] = (int32_t)((row_dword<ND>(rd[0][k], fdw) >> fsh) & 0xffu);
+      for (int k = 0; k < K; ++k) fb[k] = (int32_t)((row_dword<ND>(rd[k], fdw) >> fsh) & 0xffu);
     } else {
       const uint32_t fsh = fbit ? (uint32_t)(fk & 31) : (fnib ? 4u * (uint32_t)(fk & 7) : 8u * (uint32_t)(fcol & 3));
       const uint32_t fmask = fbit ? 1u : (fnib ? 15u : 0xffu);
@@ -2043,21 +2002,10 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     }
   }
   if (bad_pos) dev_error(&ctrl->err, GBDT_E_INTERNAL);
-  // q of every row, then block 0 group by group: group g + 1 is loaded
-  // before group g is stored
-  if (nt) {
+  // q of every row, then the first moved block
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-      if (dpos[k] >= 0) {
-        QT* qp = reinterpret_cast<QT*>(dq) + dpos[k];
-        asm volatile("" : "+v"(qp));
-        __builtin_nontemporal_store(qv[k], (GBDT_GLOBAL QT*)qp);
-      }
-  } else {
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-      if (dpos[k] >= 0) reinterpret_cast<QT*>(dq)[dpos[k]] = qv[k];
-  }
+  for (int k = 0; k < K; ++k)
+    if (dpos[k] >= 0) reinterpret_cast<QT*>(dq)[dpos[k]] = qv[k];
   // row ids (moved only when the destination has them)
   if (drid != nullptr) {
 #pragma unroll
@@ -2068,29 +2016,19 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   }
   if (n_blocks > 0) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (g + 1 < NG) {
-#pragma unroll
-        for (int e = 0; e < KE; ++e) {
-          const int k = (g + 1) * KE + e;
-          const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
-          if (dpos[k] >= 0) row_load<ND>(tb + i * bs, rd[(g + 1) & 1][e]);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < KE; ++e) {
-        const int k = g * KE + e;
-        if (dpos[k] >= 0) row_put<ND>(dbins + int64_t(dpos[k]) * block_stride, rd[g & 1][e], nt);
-      }
-    }
+    for (int k = 0; k < K; ++k)
+      if (dpos[k] >= 0) row_store<ND>(dbins + b0off + int64_t(dpos[k]) * block_stride, rd[k]);
   }
   // the other byte blocks, double-buffered: block b + 1 is loaded before
   // block b is stored (loads are unconditional, from clamped rows).  Tiles
   // of more than two rows per thread are used only with one block (the
   // registers of two buffers would not fit); the plain loop covers them.
+  // (j-th block after the first: block j - 1 below b0, block j above it)
+  auto other_block = [&](int32_t j) { return j <= b0 ? j - 1 : j; };
   if constexpr (K > 2) {
-    for (int32_t b = 1; b < n_blocks; ++b) {
-      const int64_t boff = int64_t(b) * row_capacity * block_stride;
+    for (int32_t j = 1; j < n_blocks; ++j) {
+      const int64_t boff = int64_t(other_block(j)) * row_capacity * block_stride;
+      const uint8_t* __restrict__ tbb = sbins + boff + r0 * block_stride;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
@@ -2098,35 +2036,35 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
         asm volatile("" : "+v"(d));  // (no destination address hoisted out of the block loop)
         if (d >= 0) {
           RowData<ND> x;
-          row_load<ND>(tb + boff + i * bs, x);
-          row_put<ND>(dbins + boff + int64_t(d) * block_stride, x, nt);
+          row_load<ND>(tbb + i * bs, x);
+          row_store<ND>(dbins + boff + int64_t(d) * block_stride, x);
         }
       }
     }
   } else if (n_blocks > 1) {
     RowData<ND> nx[K];
-    auto load_block = [&](int32_t b, RowData<ND>* dst) {
-      const uint8_t* __restrict__ src = sbins + int64_t(b) * row_capacity * block_stride;
+    auto load_block = [&](int32_t j, RowData<ND>* dst) {
+      const uint8_t* __restrict__ src = sbins + int64_t(other_block(j)) * row_capacity * block_stride;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const int32_t i = k * kPartThreads + threadIdx.x;
         row_load<ND>(src + (r0 + (i < rows ? i : rows - 1)) * block_stride, dst[k]);
       }
     };
-    auto store_block = [&](int32_t b, const RowData<ND>* src) {
-      uint8_t* __restrict__ dstp = dbins + int64_t(b) * row_capacity * block_stride;
+    auto store_block = [&](int32_t j, const RowData<ND>* src) {
+      uint8_t* __restrict__ dstp = dbins + int64_t(other_block(j)) * row_capacity * block_stride;
 #pragma unroll
       for (int k = 0; k < K; ++k)
-        if (dpos[k] >= 0) row_put<ND>(dstp + int64_t(dpos[k]) * block_stride, src[k], nt);
+        if (dpos[k] >= 0) row_store<ND>(dstp + int64_t(dpos[k]) * block_stride, src[k]);
     };
     if (rows > 0) load_block(1, nx);
     int32_t b = 1;
     while (b < n_blocks) {
-      if (b + 1 < n_blocks && rows > 0) load_block(b + 1, rd[0]);
+      if (b + 1 < n_blocks && rows > 0) load_block(b + 1, rd);
       store_block(b, nx);
       if (++b >= n_blocks) break;
       if (b + 1 < n_blocks && rows > 0) load_block(b + 1, nx);
-      store_block(b, rd[0]);
+      store_block(b, rd);
       ++b;
     }
   }
@@ -2153,7 +2091,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
           // hoisted out of the word loop, where all K would stay live)
           int32_t d = dpos[kb + e];
           asm volatile("" : "+v"(d));
-          if (d >= 0) row_put<4>(dw + int64_t(d) * rowb + 4 * w0, x[e], nt);
+          if (d >= 0) row_store<4>(dw + int64_t(d) * rowb + 4 * w0, x[e]);
         }
       }
     }
@@ -2171,7 +2109,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
         if (d >= 0) {
           RowData<1> one;
           one.a = make_uint4(x[k], 0u, 0u, 0u);
-          row_put<1>(dw + int64_t(d) * rowb + 4 * w0, one, nt);
+          row_store<1>(dw + int64_t(d) * rowb + 4 * w0, one);
         }
       }
     }
@@ -3142,25 +3080,13 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
                      hipStream_t s, bool qin32, bool qout32) {
   const int32_t nd = src.X.n_blocks > 0 ? src.X.block_stride / 4 : 1;
   if (qin32 && !qout32) return fail(GBDT_E_INTERNAL, "an int64 q destination needs an int64 source");
-  // With the large tiles (one block, >= 4M rows), the plan's last tiles,
-  // about kPartStreamBytes of rows, store streaming (see k_partition).
-  const int64_t row_bytes = int64_t(src.X.n_blocks) * src.X.block_stride + src.X.bit_stride +
-                            src.X.nib_stride + (qout32 ? 4 : 8);
-  const int64_t tile_bytes = int64_t(tile_rows) * (row_bytes > 0 ? row_bytes : 1);
-  const int32_t nt_tiles = tile_rows == kPartTileRowsLarge
-                               ? (int32_t)std::min<int64_t>(max_tiles, kPartStreamBytes / tile_bytes)
-                               : 0;
   decltype(&k_partition<1, 2, false, false>) kern = nullptr;
   const bool nib = src.X.n_nib_features > 0;
   if (tile_rows == 2 * kPartThreads)
     kern = nib ? (qout32 ? partition_kernel<2, true, true>(nd) : partition_kernel<2, false, true>(nd))
                : (qout32 ? partition_kernel<2, true, false>(nd) : partition_kernel<2, false, false>(nd));
-  else if (tile_rows == 4 * kPartThreads)
-    kern = nib ? (qout32 ? partition_kernel<4, true, true>(nd) : partition_kernel<4, false, true>(nd))
-               : (qout32 ? partition_kernel<4, true, false>(nd) : partition_kernel<4, false, false>(nd));
-  else if (tile_rows == 8 * kPartThreads)
-    kern = nib ? (qout32 ? partition_kernel<8, true, true>(nd) : partition_kernel<8, false, true>(nd))
-               : (qout32 ? partition_kernel<8, true, false>(nd) : partition_kernel<8, false, false>(nd));
+  else if (tile_rows == 4 * kPartThreads && qout32 && nd <= 7)
+    kern = nib ? partition_kernel<4, true, true>(nd) : partition_kernel<4, true, false>(nd);
   else
     return fail(GBDT_E_INTERNAL, "unsupported partition tile size");
   if (kern == nullptr) return fail(GBDT_E_UNSUPPORTED, "a column block wider than 32 bytes");
@@ -3169,7 +3095,7 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
                      src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
                      src.X.block_features, src.X.block_stride, src.X.n_features,
                      src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl, qin32 ? 2 : 3,
-                     nt_tiles, src.X.n_nib_features, src.X.nib_stride);
+                     src.X.n_nib_features, src.X.nib_stride);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_partition");
   return GBDT_OK;
@@ -3723,7 +3649,7 @@ int gbdt_partition_rows(const gbdt_rows* src, const gbdt_rows* dst, const gbdt_n
   const WsLayout L = ws_layout(src->X.n_rows, list_cap, 1);
   rc = check_ws(ws, ws_bytes, L);
   if (rc) return rc;
-  const int32_t ptr = part_tile_rows(src->X.n_rows, src->X.n_blocks, false);
+  const int32_t ptr = part_tile_rows(src->X.n_rows, src->X.n_blocks, src->X.block_stride, false);
   const int64_t max_tiles = (rows_bound + ptr - 1) / ptr + list_cap;
   if (max_tiles > L.status_cap) return fail(GBDT_E_SHAPE, "too many partition tiles for the workspace");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

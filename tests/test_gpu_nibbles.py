@@ -74,7 +74,7 @@ def test_nibble_layout_trees_match_oracle(case):
 
 def test_nibble_layout_large_tiles():
     """More than 4M rows in a layout with at most one byte block: the
-    partition's 8192-row tiles move the nibble words; logistic objective on
+    partition's 4096-row tiles move the nibble words; logistic objective on
     the same layout (its Hessians ride through the same partition)."""
     n = (1 << 22) + 777
     say("nibbles: %d rows" % n)

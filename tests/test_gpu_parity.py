@@ -389,7 +389,7 @@ TRAIN_CASES = [
     ("deep_tiny", 700, [4, 4, 3], dict(max_depth=9), 3, 45),
     ("depth0", 100, [4, 4], dict(max_depth=0), 2, 46),
     ("single_row", 1, [4, 4], dict(max_depth=3), 2, 47),
-    # n >= 2^22: int32 q (ceil(log2 n) >= 22) and 8192-row partition tiles, with
+    # n >= 2^22: int32 q (ceil(log2 n) >= 22) and 4096-row partition tiles, with
     # a 3-dword byte block and a bit block
     ("q32_bits_n4M", (1 << 22) + 1233, [256, 2, 64, 2, 13, 256, 7, 2, 33, 2, 200, 2, 9, 5],
      dict(max_depth=4, learning_rate=0.5), 2, 48),
