@@ -130,6 +130,7 @@ def load():
         "gbdt_predict_noalloc": (ctypes.c_int, [P(Matrix), vp, vp, i32, i32, ctypes.c_double,
                                                 ctypes.c_double, vp, vp, vp]),
         "gbdt_grow_sizes": (ctypes.c_int, [i64, i32, i32, P(GrowSizes)]),
+        "gbdt_grow_moves_ids": (ctypes.c_int, [P(Matrix), i32]),
         "gbdt_grow_tree": (ctypes.c_int, [P(Matrix), P(Features), vp, vp, P(Params), vp, vp,
                                           P(GrowBuffers), vp]),
     }
@@ -267,7 +268,7 @@ class FeatureTable:
 class RowBuffer:
     """A row order: column-blocked bins, q and row ids on the device."""
 
-    def __init__(self, ft: FeatureTable, n_rows: int, device="cuda", with_rid=True):
+    def __init__(self, ft: FeatureTable, n_rows: int, device="cuda", with_rid=True, with_bins=True):
         import torch
         L = ft.layout
         self.ft = ft
@@ -278,8 +279,9 @@ class RowBuffer:
         self.n_nib_features, self.nib_stride = L.n_nib_features, L.nib_stride
         self.n_features = ft.n_features
         self.byte_bytes = self.n_blocks * self.row_capacity * self.block_stride
+        # (a row order of row ids only, in the tree driver's index mode, has no bins)
         self.bins = torch.zeros(self.byte_bytes + self.row_capacity * (self.bit_stride + self.nib_stride),
-                                dtype=torch.uint8, device=device)
+                                dtype=torch.uint8, device=device) if with_bins else None
         self.q = torch.zeros(self.row_capacity, dtype=torch.int64, device=device)
         self.rid = torch.zeros(self.row_capacity, dtype=torch.int32, device=device) if with_rid else None
 
@@ -463,9 +465,12 @@ class Booster:
         self.sizes = sz
         self.pred = torch.full((n,), float(base_score), dtype=torch.float64, device=device)
         logistic = int(params.objective) == OBJECTIVE_LOGISTIC
-        # (the logistic objective's Hessians ride in the row buffers' rid arrays)
-        self.pp = [RowBuffer(ds.ft, n, device, with_rid=logistic),
-                   RowBuffer(ds.ft, n, device, with_rid=logistic)]
+        # index mode: the row buffers carry row ids and q only; otherwise bins
+        # and q (and, for the logistic objective, its Hessians in the rid arrays)
+        X0 = ds.X.matrix()
+        self.moves_ids = bool(load().gbdt_grow_moves_ids(ctypes.byref(X0), int(params.objective)))
+        self.pp = [RowBuffer(ds.ft, n, device, with_rid=logistic or self.moves_ids,
+                             with_bins=not self.moves_ids) for _ in range(2)]
         self.q = torch.zeros(n, dtype=torch.int64, device=device)
         self.qh = torch.zeros(n, dtype=torch.int32, device=device) if logistic else None
         self.hist_h = torch.zeros(sz.hist_slots * TB, dtype=torch.int64, device=device) if logistic else None

@@ -453,6 +453,11 @@ int gbdt_grow_sizes(int64_t n_rows, int32_t total_bins, int32_t max_depth, gbdt_
   return GBDT_OK;
 }
 
+int gbdt_grow_moves_ids(const gbdt_matrix* X, int32_t objective) {
+  if (!X) return 0;
+  return grow_moves_ids(*X, objective == GBDT_OBJECTIVE_LOGISTIC) ? 1 : 0;
+}
+
 int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* label, double* pred,
                    const gbdt_params* p, gbdt_node* nodes_out, int32_t* n_nodes_dev,
                    const gbdt_grow_buffers* b, void* stream) {
@@ -466,10 +471,15 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   if (!b->q || !b->hist_g || !b->hist_cnt || !b->splits || !b->lists || !b->ctrl || !b->ws)
     return fail(GBDT_E_ARG, "a driver buffer is null");
   const bool logistic = p->objective == GBDT_OBJECTIVE_LOGISTIC;
+  // index mode: the row buffers carry row ids and q only (their bins are not
+  // read and may be NULL)
+  const bool ids = grow_moves_ids(*X, logistic);
   for (int k = 0; k < 2; ++k) {
     const gbdt_rows& r = b->pp[k];
-    if (!r.X.bins || !r.q) return fail(GBDT_E_ARG, "a row buffer is null");
-    if (!same_layout(r.X, *X)) return fail(GBDT_E_SHAPE, "row buffers must have the layout of X");
+    if (!r.q) return fail(GBDT_E_ARG, "a row buffer's q is null");
+    if (ids && !r.rid) return fail(GBDT_E_ARG, "index mode needs the row buffers' rid");
+    if (!ids && !r.X.bins) return fail(GBDT_E_ARG, "a row buffer's bins are null");
+    if (!ids && !same_layout(r.X, *X)) return fail(GBDT_E_SHAPE, "row buffers must have the layout of X");
     if (logistic && !r.rid) return fail(GBDT_E_ARG, "the logistic objective needs the row buffers' rid");
   }
   if (logistic && (!b->qh || !b->hist_h || !b->split_h))
@@ -487,8 +497,10 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   src.rid = logistic ? b->qh : nullptr;
   rc = check_hist_inputs(src, *ft);
   if (rc) return rc;
-  rc = check_partition_inputs(b->pp[0], b->pp[1]);
-  if (rc) return rc;
+  if (!ids) {
+    rc = check_partition_inputs(b->pp[0], b->pp[1]);
+    if (rc) return rc;
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   TreeCtrl* tc = reinterpret_cast<TreeCtrl*>(b->ctrl);
@@ -570,8 +582,12 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     const int64_t lvl_off = (int64_t(1) << d) - 1;
     const int32_t cap_lvl = int32_t(1) << d;
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
-    rc = launch_hist(src, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s, q32,
-                     true);
+    // (index mode: the rows of the original matrix, through the row ids of
+    // the level's order; the root reads X in row order)
+    gbdt_rows hsrc = src;
+    if (ids) hsrc.X = *X;
+    rc = launch_hist(hsrc, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s, q32,
+                     true, ids && src.rid != nullptr);
     if (rc) return rc;
     rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
                             h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s, guard);
@@ -608,7 +624,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     // the rows of the last level's children are never read again: the
     // prediction update routes rows through the finished tree instead
     if (d + 1 < D) {
-      rc = launch_partition(src, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], part_tile, s, q32, q32);
+      rc = launch_partition(hsrc, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], part_tile, s, q32, q32,
+                            ids);
       if (rc) return rc;
       src = dst;
     }

@@ -53,6 +53,18 @@ constexpr int kPartTileRows = 2048;   // rows per partition tile (the smaller si
 constexpr int kPartTileRowsLarge = 4096;
 constexpr int64_t kPartLargeRows = int64_t(1) << 22;  // matrices from this size take the larger tiles
 
+// Whether the tree driver moves row ids instead of rows (index mode): for
+// rows of two or more byte blocks, no narrow block, squared error.  Each
+// level's partition then moves every row's id and q only (8 bytes each way
+// instead of the whole row), and the histogram reads the rows of the
+// original matrix through the ids; on 10M rows of 4 x 28 bytes a probe of
+// the two patterns put a level at 0.2-0.5 ms against 0.6 ms for moving rows.
+// One-block rows (28 bytes and less) move faster than they gather at all but
+// the first levels, so they keep the row-moving partition.
+inline bool grow_moves_ids(const gbdt_matrix& X, bool logistic) {
+  return !logistic && X.n_blocks >= 2 && X.n_bit_features == 0 && X.n_nib_features == 0;
+}
+
 // Rows per partition tile for a matrix of n rows in n_blocks byte blocks of
 // block_stride bytes whose q moves as int32 (q32) or int64: large matrices of
 // one block of at most 28 bytes with int32 q take 4096-row tiles (four rows
@@ -183,10 +195,12 @@ int check_matrix(const gbdt_matrix& X);
 int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft);
 int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
 // q32: src.q holds int32 elements (the tree driver's row buffers, see
-// driver_q32); otherwise int64 as the ABI declares.
+// driver_q32); otherwise int64 as the ABI declares.  ids (index mode, byte
+// blocks only): a tile's rows are the rows src.rid names (their q in src.q
+// at the tile's positions), read from the matrix src.X.
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
-                WsCtrl* ctrl, hipStream_t s, bool q32 = false, bool guard = false);
+                WsCtrl* ctrl, hipStream_t s, bool q32 = false, bool guard = false, bool ids = false);
 int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_cap,
                        const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
                        const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s,
@@ -200,10 +214,13 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
                 const int32_t* guard = nullptr, int64_t* hist_h = nullptr,
                 const int32_t* scale_h = nullptr, int64_t* split_h = nullptr);
 // qin32 / qout32: src.q / dst.q hold int32 elements (the tree driver's row
-// buffers); otherwise int64.
+// buffers); otherwise int64.  ids (index mode, byte blocks only): only each
+// position's row id (src.rid, NULL = the position itself) and q move, into
+// dst.rid and dst.q; the split byte is read from the matrix src.X at the row
+// id.
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
-                     hipStream_t s, bool qin32 = false, bool qout32 = false);
+                     hipStream_t s, bool qin32 = false, bool qout32 = false, bool ids = false);
 
 // Blocks of the gradient kernels for n rows: each leaves a partial max |g|
 // and a partial sum of q in the workspace (gpart).

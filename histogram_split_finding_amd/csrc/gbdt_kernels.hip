@@ -832,7 +832,7 @@ __device__ void hist_nib_block(const TileDesc& td, int32_t tile, const uint8_t* 
 // (global bin order) for k_hist_reduce.  NARROW: 0 byte blocks only; 1 a bit
 // block too; 2 a nibble block (and maybe a bit block) too -- each variant
 // carries only the code its layout needs.
-template <int D, int NARROW, bool Q32>
+template <int D, int NARROW, bool Q32, bool IDS = false>
 __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_hist(
     const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t n_blocks,
     int32_t block_features, int32_t block_stride, int32_t n_features, int32_t n_bit,
@@ -841,8 +841,9 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     int32_t total_bins, int32_t lds_bins, const TileDesc* __restrict__ desc, int32_t bits,
     int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
     uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl, const int32_t* __restrict__ guard,
-    int32_t n_nib, int32_t nib_stride) {
+    int32_t n_nib, int32_t nib_stride, const int32_t* __restrict__ ridx) {
   static_assert(D == 1 || D == 2 || D == 4 || D == 8, "lanes per row");
+  static_assert(!IDS || NARROW == 0, "index mode reads byte blocks only");
   if (failed(guard)) return;
   constexpr int RPW = 64 / D;               // rows per wave per batch
   constexpr int RPI = kHistThreads / D;     // rows per workgroup per batch
@@ -949,7 +950,22 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   // rows are addressed from the tile's first row: a uniform base plus a
   // 32-bit lane offset (a tile holds < 2^24 rows of at most 32 bytes)
   const int32_t nt = (int32_t)(r1 - r0);    // rows of the tile
-  const uint8_t* __restrict__ tb = bins + (int64_t(blk) * row_capacity + r0) * block_stride;
+  // IDS: the tile's positions r0 .. r1 hold the row ids ridx[r0 ..] of the
+  // matrix (tb is then the block's base); a row id outside the matrix is
+  // clamped to its last row, so no load leaves the block
+  const uint8_t* __restrict__ tb = IDS ? bins + int64_t(blk) * row_capacity * block_stride
+                                       : bins + (int64_t(blk) * row_capacity + r0) * block_stride;
+  const int32_t* __restrict__ trid = IDS ? ridx + r0 : nullptr;
+  const uint32_t last_row = (uint32_t)(row_capacity > 0 ? row_capacity - 1 : 0);
+  auto row_dword_at = [&](uint32_t rc) -> uint32_t {
+    if constexpr (IDS) {
+      const uint32_t id = (uint32_t)trid[rc];
+      return *reinterpret_cast<const uint32_t*>(
+          tb + (int64_t(id < last_row ? id : last_row) * block_stride + lane_off));
+    } else {
+      return *reinterpret_cast<const uint32_t*>(tb + (__umul24(rc, (uint32_t)block_stride) + lane_off));
+    }
+  };
   constexpr uint32_t QSH = Q32 ? 2u : 3u;  // log2 of q's element size
   const char* __restrict__ tq = reinterpret_cast<const char*>(q) + (r0 << QSH);
   const int32_t first_row = wid * (H * RPW) + lane / D;  // the lane's first row in the tile
@@ -981,7 +997,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
       for (int u = 0; u < H; ++u) {
         const int32_t rr = first + u * RPW + (lane / D);
         const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
-        x[u] = *reinterpret_cast<const uint32_t*>(tb + (__umul24(rc, (uint32_t)block_stride) + lane_off));
+        x[u] = row_dword_at(rc);
         if (D == 1) qq[u < NQ ? u : 0] = *reinterpret_cast<const QT*>(tq + (rc << QSH));
       }
       if (D >= 2) {
@@ -1025,8 +1041,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     }
     // the tile's last row, for the correction below, loaded with the first
     // rows so that no round trip follows the loop
-    uint32_t x_last = *reinterpret_cast<const uint32_t*>(
-        tb + (__umul24((uint32_t)lr, (uint32_t)block_stride) + lane_off));
+    uint32_t x_last = row_dword_at((uint32_t)lr);
     QT q_last = *reinterpret_cast<const QT*>(tq + (uint32_t(lr) << QSH));
     // The wave needs `todo` stages (wave-uniform).  Each loop iteration
     // adds NS stages and reloads each NS stages ahead, unconditionally; the
@@ -1816,8 +1831,11 @@ __device__ __forceinline__ void row_store(uint8_t* p, const RowData<ND>& d) {
 // split feature adds one dword load per row for its bit or nibble).  Then it
 // ballots the go-left flags, publishes its left count, looks back for the
 // exclusive prefix (decoupled look-back) and stores; the other blocks and
-// the narrow blocks are loaded and stored row by row after that.
-template <int ND, int K, bool Q32OUT, bool NIB>
+// the narrow blocks are loaded and stored row by row after that.  IDS
+// (index mode): the positions hold row ids of the matrix instead of rows; a
+// tile moves each position's id and q, with the split byte read from the
+// matrix at the id.
+template <int ND, int K, bool Q32OUT, bool NIB, bool IDS = false>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const void* __restrict__ sq,
     const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, void* __restrict__ dq,
@@ -1827,6 +1845,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     int32_t qsh /* log2 of the source q's element size: 2 (int32) or 3 (int64) */,
     int32_t n_nib, int32_t nib_stride) {
   static_assert(K == 2 || K == 4, "rows per thread");
+  static_assert(!IDS || !NIB, "index mode moves no narrow block");
   constexpr int TILE = K * kPartThreads;
   constexpr int NCNT = K * kPartWaves;  // per-(row k, wave) left counts
   // an int32 destination q is the low half of the source element
@@ -1887,7 +1906,11 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   // split byte comes from those registers: a separate load of the split
   // bytes would bring each line of the tile in twice when the cache has
   // evicted it before the rows are read.  (uniform)
-  const bool from_rows = !fnarrow && n_blocks > 0;
+  const bool from_rows = !IDS && !fnarrow && n_blocks > 0;
+  // IDS (index mode): position r0 + i holds row id srid[r0 + i] (the position
+  // itself when srid is NULL) of the matrix sbins; only ids and q move, and
+  // the split byte is read at the row id (clamped into the matrix)
+  int32_t rids[K];
   if (rows > 0) {
     const char* __restrict__ tq = reinterpret_cast<const char*>(sq) + (r0 << qsh);
     const uint32_t lr = (uint32_t)(rows - 1);
@@ -1895,7 +1918,21 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     // bit's word), issued first: loads complete in order, so the flags wait
     // only for these while the rows are still in flight
     const uint32_t frow = fbit ? (uint32_t)nwords * 4u : (fnib ? (uint32_t)nib_stride : bs);
-    if (!from_rows) {
+    if constexpr (IDS) {
+      const uint8_t* __restrict__ tf = fcolp - (fcol & 3);
+      const int64_t last = row_capacity > 0 ? row_capacity - 1 : 0;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
+        const uint32_t ic = i < lr ? i : lr;
+        rids[k] = srid != nullptr ? srid[r0 + ic] : (int32_t)(r0 + ic);
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t id = rids[k] < 0 ? 0 : (rids[k] > last ? last : rids[k]);
+        fb[k] = (int32_t)*reinterpret_cast<const uint32_t*>(tf + id * int64_t(frow));
+      }
+    } else if (!from_rows) {
       const uint8_t* __restrict__ tf =
           (fnarrow ? reinterpret_cast<const uint8_t*>(fwordp) : fcolp - (fcol & 3)) + r0 * int64_t(frow);
 #pragma unroll
@@ -1915,7 +1952,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       qv[k] = *reinterpret_cast<const QT*>(tq + (ic << qsh));
       // with no byte block (ND == 1, block_stride 0) this rereads the first
       // dword of the bit block, and the value is never stored
-      row_load<ND>(tb + ic * bs, rd[k]);
+      if constexpr (!IDS) row_load<ND>(tb + ic * bs, rd[k]);
     }
     if (from_rows) {
       const uint32_t fdw = (uint32_t)fcol >> 2;
@@ -2011,9 +2048,10 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int64_t sr = r0 + k * kPartThreads + threadIdx.x;
-      if (dpos[k] >= 0) drid[dpos[k]] = srid != nullptr ? srid[sr] : (int32_t)sr;
+      if (dpos[k] >= 0) drid[dpos[k]] = IDS ? rids[k] : (srid != nullptr ? srid[sr] : (int32_t)sr);
     }
   }
+  if constexpr (IDS) return;
   if (n_blocks > 0) {
 #pragma unroll
     for (int k = 0; k < K; ++k)
@@ -2593,7 +2631,7 @@ static auto hist_kernel(int D) -> decltype(&k_hist<8, N, Q>) {
 
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
-                WsCtrl* ctrl, hipStream_t s, bool q32, bool guard) {
+                WsCtrl* ctrl, hipStream_t s, bool q32, bool guard, bool ids) {
   const int64_t n_rows = src.X.n_rows > 0 ? src.X.n_rows : 1;
   const int32_t bits = pack_bits_for(n_rows);
   const bool has_bytes = src.X.n_features > src.X.n_bit_features + src.X.n_nib_features;
@@ -2606,7 +2644,12 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
   const int32_t nd = has_bytes ? src.X.block_stride / 4 : 1;  // dwords per row (<= 8)
   const int D = nd <= 1 ? 1 : (nd <= 2 ? 2 : (nd <= 4 ? 4 : 8));
   const int narrow = src.X.n_nib_features > 0 ? 2 : (src.X.n_bit_features > 0 ? 1 : 0);
-  auto kern = narrow == 2 ? (q32 ? hist_kernel<2, true>(D) : hist_kernel<2, false>(D))
+  // (index mode: two or more byte blocks of at most 32 columns are at least
+  // 17 columns, 5 dwords, wide, so D = 8)
+  if (ids && (narrow != 0 || src.rid == nullptr || D != 8))
+    return fail(GBDT_E_INTERNAL, "index mode needs byte blocks of 5 to 8 dwords and row ids");
+  auto kern = ids ? (q32 ? k_hist<8, 0, true, true> : k_hist<8, 0, false, true>)
+              : narrow == 2 ? (q32 ? hist_kernel<2, true>(D) : hist_kernel<2, false>(D))
               : narrow == 1 ? (q32 ? hist_kernel<1, true>(D) : hist_kernel<1, false>(D))
                             : (q32 ? hist_kernel<0, true>(D) : hist_kernel<0, false>(D));
   (void)has_bits;
@@ -2618,7 +2661,7 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
                      src.X.n_features, src.X.n_bit_features, src.X.bit_stride, src.X.col_feature,
                      src.q, ft.bin_offset, ft.skip_bin, ft.total_bins, ft.max_block_bins, desc, bits,
                      hist_g, hist_cnt, hpart, ctrl, guard ? &ctrl->err : nullptr, src.X.n_nib_features,
-                     src.X.nib_stride);
+                     src.X.nib_stride, ids ? src.rid : nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist");
   return GBDT_OK;
@@ -3077,12 +3120,17 @@ static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K, Q, N>) {
 
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
-                     hipStream_t s, bool qin32, bool qout32) {
+                     hipStream_t s, bool qin32, bool qout32, bool ids) {
   const int32_t nd = src.X.n_blocks > 0 ? src.X.block_stride / 4 : 1;
   if (qin32 && !qout32) return fail(GBDT_E_INTERNAL, "an int64 q destination needs an int64 source");
   decltype(&k_partition<1, 2, false, false>) kern = nullptr;
   const bool nib = src.X.n_nib_features > 0;
-  if (tile_rows == 2 * kPartThreads)
+  if (ids) {
+    if (nib || src.X.n_bit_features > 0 || src.X.n_blocks < 1 || dst.rid == nullptr ||
+        tile_rows != 2 * kPartThreads)
+      return fail(GBDT_E_INTERNAL, "index mode needs byte blocks, row ids and 2048-row tiles");
+    kern = qout32 ? k_partition<1, 2, true, false, true> : k_partition<1, 2, false, false, true>;
+  } else if (tile_rows == 2 * kPartThreads)
     kern = nib ? (qout32 ? partition_kernel<2, true, true>(nd) : partition_kernel<2, false, true>(nd))
                : (qout32 ? partition_kernel<2, true, false>(nd) : partition_kernel<2, false, false>(nd));
   else if (tile_rows == 4 * kPartThreads && qout32 && nd <= 7)

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GBDT_ABI_VERSION 4
+#define GBDT_ABI_VERSION 5
 #define GBDT_MAX_DEPTH 16       /* deepest tree the level loop supports */
 #define GBDT_MAX_FEATURES 4096
 #define GBDT_MAX_BINS 256       /* bins per feature */
@@ -526,6 +526,9 @@ int gbdt_predict_noalloc(const gbdt_matrix* X /* host */, const gbdt_node* trees
  * Device buffers for gbdt_grow_tree (host struct of device pointers); sizes
  * from gbdt_grow_sizes.  pp[0], pp[1]: two row orders (bins in the blocking
  * of X and q; rid may be NULL) used in turn by the partition of each level.
+ * In index mode (gbdt_grow_moves_ids) the partition moves row ids instead of
+ * rows: pp[k].rid must then be set and pp[k].X.bins is not read (it may be
+ * NULL).
  * q and the row buffers' q are working storage of 8 bytes per row: when
  * ceil(log2 n_rows) >= 22 (n_rows > 2^21), every |q| <= 2^(52 - ceil(log2 n))
  * <= 2^30 and the driver keeps q as int32 in the first 4 n bytes (exact);
@@ -551,6 +554,18 @@ typedef struct gbdt_grow_buffers {
   int64_t* hist_h;
   int64_t* split_h;
 } gbdt_grow_buffers;
+
+/*
+ * 1 when gbdt_grow_tree runs X with the objective in index mode, else 0: for
+ * rows of two or more byte blocks with no bit or nibble block, squared
+ * error.  Each level's partition then moves every row's id and q only,
+ * stably, as "Module Design: Training Core" (section 6, step 5) partitions
+ * row indices, and the histogram of a node reads its rows of X through the
+ * ids (the ExaBoost PR's kernels gather through data indices the same way);
+ * wide rows are cheaper to gather than to move at every level.  Other
+ * layouts move whole rows into node order and stream them.
+ */
+int gbdt_grow_moves_ids(const gbdt_matrix* X /* host */, int32_t objective);
 
 /* Sizes (in elements / bytes as named) of the driver's buffers. */
 typedef struct gbdt_grow_sizes_t {
