@@ -73,7 +73,11 @@ inline bool grow_moves_ids(const gbdt_matrix& X, bool logistic) {
 // int64 q would take that kernel past the 64 registers of two workgroups per
 // CU.  Small matrices keep more tiles than workgroup slots, and several
 // blocks need the registers for double-buffering the blocks.
-inline int32_t part_tile_rows(int64_t n_rows, int32_t n_blocks, int32_t block_stride, bool q32) {
+// In index mode (ids: only row ids and q move) every large matrix takes the
+// 4096-row tiles: the kernel holds no rows in registers.
+inline int32_t part_tile_rows(int64_t n_rows, int32_t n_blocks, int32_t block_stride, bool q32,
+                              bool ids = false) {
+  if (ids) return n_rows < kPartLargeRows ? kPartTileRows : kPartTileRowsLarge;
   if (n_rows < kPartLargeRows || n_blocks > 1 || block_stride > 28 || !q32) return kPartTileRows;
   return kPartTileRowsLarge;
 }

@@ -3126,10 +3126,14 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
   decltype(&k_partition<1, 2, false, false>) kern = nullptr;
   const bool nib = src.X.n_nib_features > 0;
   if (ids) {
-    if (nib || src.X.n_bit_features > 0 || src.X.n_blocks < 1 || dst.rid == nullptr ||
-        tile_rows != 2 * kPartThreads)
-      return fail(GBDT_E_INTERNAL, "index mode needs byte blocks, row ids and 2048-row tiles");
-    kern = qout32 ? k_partition<1, 2, true, false, true> : k_partition<1, 2, false, false, true>;
+    if (nib || src.X.n_bit_features > 0 || src.X.n_blocks < 1 || dst.rid == nullptr)
+      return fail(GBDT_E_INTERNAL, "index mode needs byte blocks and row ids");
+    if (tile_rows == 2 * kPartThreads)
+      kern = qout32 ? k_partition<1, 2, true, false, true> : k_partition<1, 2, false, false, true>;
+    else if (tile_rows == 4 * kPartThreads)
+      kern = qout32 ? k_partition<1, 4, true, false, true> : k_partition<1, 4, false, false, true>;
+    else
+      return fail(GBDT_E_INTERNAL, "unsupported partition tile size");
   } else if (tile_rows == 2 * kPartThreads)
     kern = nib ? (qout32 ? partition_kernel<2, true, true>(nd) : partition_kernel<2, false, true>(nd))
                : (qout32 ? partition_kernel<2, true, false>(nd) : partition_kernel<2, false, false>(nd));

@@ -192,3 +192,23 @@ def test_workspace_and_shape_checks():
     rc = lib.gbdt_build_histograms(ctypes.byref(src), ctypes.byref(ft), fake, fake, fake, 0, 0, fake,
                                    fake, fake, 1 << 30, None)
     assert rc == 0
+
+
+@pytest.mark.parametrize("nbins,bits,nibbles,objective,want", [
+    ([256] * 100, True, False, 0, 1),    # four byte blocks: row ids move
+    ([256] * 70, True, False, 0, 1),     # three blocks
+    ([256] * 33, False, False, 0, 1),    # two blocks of 17 and 16 columns
+    ([256] * 32, True, False, 0, 0),     # one block of 32 columns: rows move
+    ([64] * 28, True, False, 0, 0),
+    ([256] * 100, True, False, 1, 0),    # the logistic objective keeps rows moving
+    ([256] * 40 + [2] * 4, True, False, 0, 0),   # a bit block
+    ([256] * 40 + [2] * 4, False, False, 0, 1),  # the same features as bytes
+    ([256] * 40 + [9] * 4, True, True, 0, 0),    # a nibble block
+])
+def test_index_mode_rule(nbins, bits, nibbles, objective, want):
+    """Index mode (the partition moves row ids, the histogram gathers through
+    them) is chosen for rows of two or more byte blocks with no narrow block,
+    squared error."""
+    ft = g.FeatureTable(nbins, "cpu", pack_bits=bits, pack_nibbles=nibbles)
+    X = g.RowBuffer(ft, 10, "cpu", with_rid=False, with_bins=False).matrix()
+    assert g.load().gbdt_grow_moves_ids(ctypes.byref(X), objective) == want
