@@ -73,11 +73,14 @@ inline bool grow_moves_ids(const gbdt_matrix& X, bool logistic) {
 // int64 q would take that kernel past the 64 registers of two workgroups per
 // CU.  Small matrices keep more tiles than workgroup slots, and several
 // blocks need the registers for double-buffering the blocks.
-// In index mode (ids: only row ids and q move) every large matrix takes the
-// 4096-row tiles: the kernel holds no rows in registers.
+// In index mode (ids: only row ids and q move) every large matrix takes
+// 8192-row tiles: the kernel holds no rows in registers, and fewer tiles
+// shorten the look-back chains (10M x 100: 3.88 -> 3.75 -> 3.68 ms per tree
+// from 2048- to 4096- to 8192-row tiles).
+constexpr int kPartTileRowsIds = 8192;
 inline int32_t part_tile_rows(int64_t n_rows, int32_t n_blocks, int32_t block_stride, bool q32,
                               bool ids = false) {
-  if (ids) return n_rows < kPartLargeRows ? kPartTileRows : kPartTileRowsLarge;
+  if (ids) return n_rows < kPartLargeRows ? kPartTileRows : kPartTileRowsIds;
   if (n_rows < kPartLargeRows || n_blocks > 1 || block_stride > 28 || !q32) return kPartTileRows;
   return kPartTileRowsLarge;
 }

@@ -1844,7 +1844,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
     int32_t qsh /* log2 of the source q's element size: 2 (int32) or 3 (int64) */,
     int32_t n_nib, int32_t nib_stride) {
-  static_assert(K == 2 || K == 4, "rows per thread");
+  static_assert(K == 2 || K == 4 || (K == 8 && IDS), "rows per thread");
   static_assert(!IDS || !NIB, "index mode moves no narrow block");
   constexpr int TILE = K * kPartThreads;
   constexpr int NCNT = K * kPartWaves;  // per-(row k, wave) left counts
@@ -1894,7 +1894,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   QT qv[K];
   RowData<ND> rd[K];  // the first moved block of each row of the thread
   // Addresses are a uniform base at the tile's first row plus a 32-bit lane
-  // offset (a tile spans at most 4096 rows of at most 512 bytes).
+  // offset (a tile spans at most 8192 rows of at most 512 bytes).
   // block 0 here means the first block moved: the split feature's own block
   // (any block for a narrow split feature), so its byte always comes from
   // the rows' registers; the other blocks follow in order
@@ -3130,8 +3130,8 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
       return fail(GBDT_E_INTERNAL, "index mode needs byte blocks and row ids");
     if (tile_rows == 2 * kPartThreads)
       kern = qout32 ? k_partition<1, 2, true, false, true> : k_partition<1, 2, false, false, true>;
-    else if (tile_rows == 4 * kPartThreads)
-      kern = qout32 ? k_partition<1, 4, true, false, true> : k_partition<1, 4, false, false, true>;
+    else if (tile_rows == 8 * kPartThreads)
+      kern = qout32 ? k_partition<1, 8, true, false, true> : k_partition<1, 8, false, false, true>;
     else
       return fail(GBDT_E_INTERNAL, "unsupported partition tile size");
   } else if (tile_rows == 2 * kPartThreads)

@@ -6,7 +6,7 @@ node's rows of the original matrix through the ids.
 Trees (node by node), the histograms of every node the first tree builds or
 derives, and the predictions must equal the oracle's bit for bit, for two to
 eight blocks, skewed and uniform bins, ragged row counts, small nodes, and
-more than 4M rows (the 4096-row partition tiles and int32 q).
+more than 4M rows (the 8192-row partition tiles and int32 q).
 """
 import numpy as np
 import pytest
@@ -57,7 +57,7 @@ def test_index_mode_trees_match_oracle(case):
 
 
 def test_index_mode_over_4m_rows():
-    """More than 4M rows of two blocks: int32 q and the 4096-row tiles of the
+    """More than 4M rows of two blocks: int32 q and the 8192-row tiles of the
     id-only partition."""
     n = (1 << 22) + 4321
     say("index mode: %d rows" % n)
