@@ -133,7 +133,7 @@ def profiled_traffic(workload_name, kernel="k_hist"):
             fields[key.strip()] = val.strip()
     csrc = os.path.join(ROOT, "histogram_split_finding_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("gbdt_kernels.hip", "gbdt_internal.h", "gbdt_device.h"):
+    for name in ("gbdt_kernels.hip", "gbdt_driver.hip", "gbdt_internal.h", "gbdt_device.h"):
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(fh.read())
     if fields.get("kernel_source_sha256") != h.hexdigest()[:16]:
