@@ -29,73 +29,78 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// DPP lane move of a 32-bit value: lanes whose source lies outside the row,
+// or whose row is masked off, read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int32_t dpp_move_i32(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive sum over lanes 0..lane of a wave (every lane active): shifts by
+// 1, 2, 4 and 8 within each row of 16 lanes, then row 0's total into row 1
+// and row 2's into row 3 (row_bcast:15), then rows 0-1's total into rows 2
+// and 3 (row_bcast:31).  VALU lane moves, no LDS round trips.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x) {
+  x += dpp_move_i32<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_move_i32<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_move_i32<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_move_i32<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_move_i32<0x142, 0xA>(x);  // row_bcast:15
+  x += dpp_move_i32<0x143, 0xC>(x);  // row_bcast:31
+  return x;
+}
+
+// The same within row 0 only (lanes 0..15): enough for the at most 16 wave
+// totals of a workgroup.
+__device__ __forceinline__ int32_t row_incl_scan(int32_t x) {
+  x += dpp_move_i32<0x111, 0xF>(x);
+  x += dpp_move_i32<0x112, 0xF>(x);
+  x += dpp_move_i32<0x114, 0xF>(x);
+  x += dpp_move_i32<0x118, 0xF>(x);
+  return x;
+}
+
 // Exclusive scan of one int32 per thread across a workgroup (blockDim.x a
 // multiple of 64, <= 1024).  Returns the exclusive prefix; *total = sum.
+// Each wave scans with lane moves and writes its total; after one barrier
+// every wave scans the wave totals itself (lanes 0..15) and takes its own
+// offset with a lane read.
 __device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* total, int32_t* sh /*[32]*/) {
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nw = (blockDim.x + 63) >> 6;
-  int32_t x = v;
-  for (int off = 1; off < 64; off <<= 1) {
-    int32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const int32_t x = wave_incl_scan(v);
   if (lane == 63) sh[wid] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int w = 0; w < nw; ++w) {
-      int32_t t = sh[w];
-      sh[w] = acc;
-      acc += t;
-    }
-    sh[31] = acc;
-  }
-  __syncthreads();
-  int32_t res = sh[wid] + x - v;
-  *total = sh[31];
-  __syncthreads();
-  return res;
+  const int32_t t = row_incl_scan(lane < nw ? sh[lane] : 0);
+  const int32_t before = wid > 0 ? __builtin_amdgcn_readlane(t, wid - 1) : 0;
+  *total = __builtin_amdgcn_readlane(t, nw - 1);
+  __syncthreads();  // (sh may be reused)
+  return before + x - v;
 }
 
 // Exclusive scans of K int32 values per thread across a workgroup at once
-// (one pair of barriers for all K).  sh: LDS [K * 17].
+// (one barrier for all K, as block_exclusive_scan).  sh: LDS [K * 17].
 template <int K>
 __device__ inline void block_exclusive_scan_multi(const int32_t (&v)[K], int32_t (&excl)[K],
                                                   int32_t (&total)[K], int32_t* sh) {
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nw = (blockDim.x + 63) >> 6;
   int32_t x[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) x[k] = v[k];
-  for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int32_t y = __shfl_up(x[k], off, 64);
-      if (lane >= off) x[k] += y;
-    }
-  }
+  for (int k = 0; k < K; ++k) x[k] = wave_incl_scan(v[k]);
   if (lane == 63) {
 #pragma unroll
     for (int k = 0; k < K; ++k) sh[k * 17 + wid] = x[k];
   }
   __syncthreads();
-  if (threadIdx.x < K) {
-    const int k = threadIdx.x;
-    int32_t acc = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int32_t t = sh[k * 17 + w];
-      sh[k * 17 + w] = acc;
-      acc += t;
-    }
-    sh[k * 17 + 16] = acc;
-  }
-  __syncthreads();
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    excl[k] = sh[k * 17 + wid] + x[k] - v[k];
-    total[k] = sh[k * 17 + 16];
+    const int32_t t = row_incl_scan(lane < nw ? sh[k * 17 + lane] : 0);
+    const int32_t before = wid > 0 ? __builtin_amdgcn_readlane(t, wid - 1) : 0;
+    excl[k] = before + x[k] - v[k];
+    total[k] = __builtin_amdgcn_readlane(t, nw - 1);
   }
   __syncthreads();
 }
@@ -165,12 +170,7 @@ __device__ __forceinline__ void tile_order_prefix(int32_t* bucket) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int32_t v = bucket[lane];
-    int32_t x = v;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
-    bucket[lane] = x - v;
+    bucket[lane] = wave_incl_scan(v) - v;
   }
   __syncthreads();
 }

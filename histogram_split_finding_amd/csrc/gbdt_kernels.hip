@@ -1990,12 +1990,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       c[e] = idx < NCNT ? s_cnt[idx] : 0;
       own += c[e];
     }
-    int32_t x = own;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
+    const int32_t x = wave_incl_scan(own);
     int32_t run = x - own;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -2003,7 +1998,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       if (idx < NCNT) s_cnt[idx] = run;
       run += c[e];
     }
-    const int32_t acc = __shfl(x, 63, 64);
+    const int32_t acc = __builtin_amdgcn_readlane(x, 63);
     if (lane == 0) st_publish(&status[tile], (tin == 0 ? kStInc : kStAgg) | (uint64_t)(uint32_t)acc);
     int64_t excl = 0;
     bool ok = true;
