@@ -1256,6 +1256,12 @@ template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ int64_t dpp_i64(int64_t v) {
   return (int64_t)dpp_u64<CTRL, ROW_MASK>((uint64_t)v);
 }
+// A 64-bit value of lane l (wave-uniform l).
+__device__ __forceinline__ int64_t read_lane_i64(int64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // One step of the inclusive segmented scan: the running value of the lane
 // CTRL moves in from (earlier lanes) is added unless this lane's run already
@@ -1494,18 +1500,43 @@ __global__ void __launch_bounds__(THREADS) k_find(
       if constexpr (HESS) sw_h[wid] = wh;
     }
     __syncthreads();
-    int64_t cgw = s_carry_g;  // open segment entering this wave
-    int32_t ccw = s_carry_c;
-    int64_t chw = HESS ? s_carry_h : 0;
-    for (int w = 0; w < wid; ++w) {
-      if (sw_f[w]) {
-        cgw = sw_g[w];
-        ccw = sw_c[w];
-        if constexpr (HESS) chw = sw_h[w];
+    // the open segment entering this wave: a segmented scan of the wave
+    // tails across lanes 0..NW-1 (row 0, DPP row shifts), read at lane
+    // wid - 1 -- the pass's carry when no wave before this one holds a
+    // segment head -- with no serial walk over the waves
+    int64_t cgw, chw = 0;
+    int32_t ccw;
+    {
+      const bool in = lane < NW;
+      int32_t tf = in ? sw_f[lane] : 0;
+      int64_t tg = in ? sw_g[lane] : 0;
+      int32_t tc = in ? sw_c[lane] : 0;
+      int64_t th = (HESS && in) ? sw_h[HESS ? lane : 0] : 0;
+      if constexpr (HESS) {
+        seg_scan_step<0x111, 0xF>(tf, tg, tc, th);
+        seg_scan_step<0x112, 0xF>(tf, tg, tc, th);
+        seg_scan_step<0x114, 0xF>(tf, tg, tc, th);
+        seg_scan_step<0x118, 0xF>(tf, tg, tc, th);
       } else {
-        cgw += sw_g[w];
-        ccw += sw_c[w];
-        if constexpr (HESS) chw += sw_h[w];
+        seg_scan_step<0x111, 0xF>(tf, tg, tc);
+        seg_scan_step<0x112, 0xF>(tf, tg, tc);
+        seg_scan_step<0x114, 0xF>(tf, tg, tc);
+        seg_scan_step<0x118, 0xF>(tf, tg, tc);
+      }
+      const int wv = __builtin_amdgcn_readfirstlane(wid);
+      cgw = s_carry_g;
+      ccw = s_carry_c;
+      if constexpr (HESS) chw = s_carry_h;
+      if (wv > 0) {
+        const int32_t f = __builtin_amdgcn_readlane(tf, wv - 1);
+        const int64_t g = read_lane_i64(tg, wv - 1);
+        const int32_t cc = __builtin_amdgcn_readlane(tc, wv - 1);
+        cgw = f ? g : cgw + g;
+        ccw = f ? cc : ccw + cc;
+        if constexpr (HESS) {
+          const int64_t hh = read_lane_i64(th, wv - 1);
+          chw = f ? hh : chw + hh;
+        }
       }
     }
     const int64_t incl_g = fl ? wg : cgw + wg;  // open segment at this thread's end
@@ -1593,14 +1624,16 @@ __global__ void __launch_bounds__(THREADS) k_find(
     r_key[wid] = wg_key;
   }
   __syncthreads();
-  double top_gain = r_gain[0];
-  int32_t top_key = r_key[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w)
-    if (better(r_gain[w], r_key[w], top_gain, top_key)) {
-      top_gain = r_gain[w];
-      top_key = r_key[w];
-    }
+  // the waves' best in lanes 0..NW-1 (empty candidates beyond), reduced
+  // within row 0 by DPP; every lane of the row then holds the best
+  double top_gain = lane < NW ? r_gain[lane] : 0.0;
+  int32_t top_key = lane < NW ? r_key[lane] : 0;
+  argmax_step<0xB1, 0xF>(top_gain, top_key);   // quad_perm [1,0,3,2]
+  argmax_step<0x4E, 0xF>(top_gain, top_key);   // quad_perm [2,3,0,1]
+  argmax_step<0x141, 0xF>(top_gain, top_key);  // row_half_mirror
+  argmax_step<0x140, 0xF>(top_gain, top_key);  // row_mirror
+  top_gain = __longlong_as_double(read_lane_i64(__double_as_longlong(top_gain), 0));
+  top_key = __builtin_amdgcn_readlane(top_key, 0);
   if (n_chunks > 1) {
     // this chunk's best candidate for the merge (key 0: none)
     FindCand* __restrict__ c = cand + int64_t(j) * n_chunks + chunk;
