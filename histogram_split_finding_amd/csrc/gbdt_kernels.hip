@@ -1960,11 +1960,14 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
         const uint32_t ic = i < lr ? i : lr;
         rids[k] = srid != nullptr ? srid[r0 + ic] : (int32_t)(r0 + ic);
       }
+      bool bad_id = false;  // (an id outside the matrix is clamped into it and reported)
 #pragma unroll
       for (int k = 0; k < K; ++k) {
+        bad_id |= rids[k] < 0 || rids[k] > last;
         const int64_t id = rids[k] < 0 ? 0 : (rids[k] > last ? last : rids[k]);
         fb[k] = (int32_t)*reinterpret_cast<const uint32_t*>(tf + id * int64_t(frow));
       }
+      if (bad_id) dev_error(&ctrl->err, GBDT_E_INTERNAL);
     } else if (!from_rows) {
       const uint8_t* __restrict__ tf =
           (fnarrow ? reinterpret_cast<const uint8_t*>(fwordp) : fcolp - (fcol & 3)) + r0 * int64_t(frow);
