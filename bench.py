@@ -240,7 +240,11 @@ def measure(g, datagen, torch, k, K, W, diag):
                    "learning_rate": params.learning_rate, "reg_lambda": params.reg_lambda,
                    "gamma": params.gamma, "min_samples_leaf": params.min_samples_leaf,
                    "min_child_weight": params.min_child_weight,
-                   "bins_fnv1a64": fp_bins, "label_fnv1a64": fp_label},
+                   "bins_fnv1a64": fp_bins, "label_fnv1a64": fp_label,
+                   "layout": {"byte_blocks": int(ds.X.n_blocks), "block_stride": int(ds.X.block_stride),
+                              "bit_features": int(ds.X.n_bit_features),
+                              "nibble_features": int(ds.X.n_nib_features),
+                              "partition_moves": "row ids" if bst.moves_ids else "rows"}},
         "trees_per_s": K / wall,
     }
 

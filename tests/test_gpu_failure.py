@@ -78,3 +78,31 @@ def test_error_recorded_before_the_tree():
     ref = oracle.train(bins, nb, label, oracle.make_params(**wl), 2)
     compare_tree(bst.host_trees()[1], ref["nodes"][1][: ref["n_nodes"][1]])
     assert np.array_equal(bst.pred.cpu().numpy(), ref["pred"])
+
+
+def test_nan_label_in_index_mode():
+    """The same in index mode (rows of two byte blocks: the partition moves
+    row ids): the failed tree is dropped, predictions stay the first tree's,
+    and training goes on once the label is restored."""
+    say("failure: NaN label before tree 2, index mode")
+    bins, label, nb = datagen.make_random(20011, [256] * 40, 77)
+    pk = dict(max_depth=6, learning_rate=0.3)
+    ds = g.Dataset(bins, label, nb, DEV)
+    bst = g.Booster(ds, g.make_params(**pk))
+    assert bst.moves_ids
+    p = oracle.make_params(**pk)
+    bst.train(1)
+    ref1 = oracle.train(bins, nb, label, p, 1)
+    row = 12345
+    ds.label[row] = float("nan")
+    with pytest.raises(g.GbdtError) as ei:
+        bst.train(2)
+    assert ei.value.code == -3
+    assert len(bst.trees) == 1
+    assert np.array_equal(bst.pred.cpu().numpy(), ref1["pred"])
+    ds.label[row] = float(label[row])
+    bst.train(1)
+    bst.check()
+    ref2 = oracle.train(bins, nb, label, p, 2)
+    compare_tree(bst.host_trees()[1], ref2["nodes"][1][: ref2["n_nodes"][1]])
+    assert np.array_equal(bst.pred.cpu().numpy(), ref2["pred"])
