@@ -533,7 +533,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   const bool q32 = logistic || driver_q32(n);
   const int32_t part_tile = part_tile_rows(n, X->n_blocks, X->block_stride, q32, ids);
   const int32_t target = hist_target_tiles(X->n_blocks + (X->n_bit_features > 0 ? 1 : 0) +
-                                           (X->n_nib_features > 0 ? 1 : 0));
+                                               (X->n_nib_features > 0 ? 1 : 0),
+                                           n);
   const int32_t min_rows =
       hist_min_tile_rows(ft->total_bins,
                          int64_t(X->n_blocks) * X->block_stride + X->bit_stride + X->nib_stride);

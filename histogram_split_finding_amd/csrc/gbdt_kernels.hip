@@ -3650,7 +3650,7 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   uint64_t* hpart = reinterpret_cast<uint64_t*>(w + L.hpart);
   const int32_t gy = src->X.n_blocks + (src->X.n_bit_features > 0 ? 1 : 0) + (src->X.n_nib_features > 0 ? 1 : 0);
   const int32_t T = hist_tile_rows(
-      rows_bound, src->X.n_rows, hist_target_tiles(gy),
+      rows_bound, src->X.n_rows, hist_target_tiles(gy, src->X.n_rows),
       hist_min_tile_rows(ft->total_bins, int64_t(src->X.n_blocks) * src->X.block_stride + src->X.bit_stride +
                                              src->X.nib_stride));
   const int64_t max_tiles = (rows_bound + T - 1) / T + list_cap;
