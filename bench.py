@@ -244,7 +244,9 @@ def measure(g, datagen, torch, k, K, W, diag):
                    "layout": {"byte_blocks": int(ds.X.n_blocks), "block_stride": int(ds.X.block_stride),
                               "bit_features": int(ds.X.n_bit_features),
                               "nibble_features": int(ds.X.n_nib_features),
-                              "partition_moves": "row ids" if bst.moves_ids else "rows"}},
+                              "partition_moves": "row ids" if bst.moves_ids else "rows",
+                              "gather_copies": (["rows interleaved", "column-major"]
+                                                if bst.rows_ix is not None else [])}},
         "trees_per_s": K / wall,
     }
 

@@ -78,7 +78,7 @@ class Params(ctypes.Structure):
 class GrowBuffers(ctypes.Structure):
     _fields_ = [("pp", Rows * 2), ("q", vp), ("hist_g", vp), ("hist_cnt", vp), ("splits", vp),
                 ("lists", vp), ("ctrl", vp), ("ws", vp), ("ws_bytes", ctypes.c_size_t),
-                ("qh", vp), ("hist_h", vp), ("split_h", vp)]
+                ("qh", vp), ("hist_h", vp), ("split_h", vp), ("rows_ix", vp), ("cols", vp)]
 
 
 class GrowSizes(ctypes.Structure):
@@ -131,6 +131,8 @@ def load():
                                                 ctypes.c_double, vp, vp, vp]),
         "gbdt_grow_sizes": (ctypes.c_int, [i64, i32, i32, P(GrowSizes)]),
         "gbdt_grow_moves_ids": (ctypes.c_int, [P(Matrix), i32]),
+        "gbdt_interleave_rows": (ctypes.c_int, [P(Matrix), vp, vp]),
+        "gbdt_column_major": (ctypes.c_int, [P(Matrix), vp, vp]),
         "gbdt_grow_tree": (ctypes.c_int, [P(Matrix), P(Features), vp, vp, P(Params), vp, vp,
                                           P(GrowBuffers), vp]),
     }
@@ -419,6 +421,26 @@ def gbdt_predict(X: Matrix, trees, n_nodes, n_trees, tree_stride, base_score, le
     _check(rc, "gbdt_predict")
 
 
+def gbdt_interleave_rows(X: Matrix, out, stream=None):
+    """X's byte blocks interleaved row by row into out (a uint8 device tensor
+    of at least row_capacity * n_blocks * block_stride bytes)."""
+    need = int(X.row_capacity) * int(X.n_blocks) * int(X.block_stride)
+    if out.numel() * out.element_size() < need:
+        raise ValueError("out holds fewer than %d bytes" % need)
+    _check(load().gbdt_interleave_rows(ctypes.byref(X), _ptr(out), _stream(stream)),
+           "gbdt_interleave_rows")
+
+
+def gbdt_column_major(X: Matrix, out, stream=None):
+    """X's byte columns one after another into out (a uint8 device tensor of
+    at least row_capacity bytes per byte column)."""
+    n_cols = int(X.n_features) - int(X.n_bit_features) - int(X.n_nib_features)
+    need = int(X.row_capacity) * n_cols if int(X.n_blocks) > 0 else 0
+    if out.numel() * out.element_size() < need:
+        raise ValueError("out holds fewer than %d bytes" % need)
+    _check(load().gbdt_column_major(ctypes.byref(X), _ptr(out), _stream(stream)), "gbdt_column_major")
+
+
 def gbdt_predict_noalloc(X: Matrix, trees, n_nodes, n_trees, tree_stride, base_score, learning_rate,
                          out, status, stream=None):
     """gbdt_predict without a workspace (the library's per-GPU scratch);
@@ -455,7 +477,10 @@ class Dataset:
 class Booster:
     """Buffers of one training run; grow_tree() runs one boosting step."""
 
-    def __init__(self, ds: Dataset, params: Params, base_score=0.0, device="cuda"):
+    def __init__(self, ds: Dataset, params: Params, base_score=0.0, device="cuda", interleave=True):
+        """interleave: in index mode, also keep a row-interleaved copy of the
+        byte blocks (gbdt_interleave_rows) for the histogram's gathers and a
+        column-major copy (gbdt_column_major) for the partition's."""
         import torch
         _check(gbdt_validate_params(params), "gbdt_validate_params")
         self.ds = ds
@@ -471,6 +496,15 @@ class Booster:
         self.moves_ids = bool(load().gbdt_grow_moves_ids(ctypes.byref(X0), int(params.objective)))
         self.pp = [RowBuffer(ds.ft, n, device, with_rid=logistic or self.moves_ids,
                              with_bins=not self.moves_ids) for _ in range(2)]
+        self.rows_ix = self.cols = None
+        if self.moves_ids and interleave:
+            cap = int(X0.row_capacity)
+            self.rows_ix = torch.empty(cap * int(X0.n_blocks) * int(X0.block_stride), dtype=torch.uint8,
+                                       device=device)
+            gbdt_interleave_rows(X0, self.rows_ix)
+            n_cols = int(X0.n_features) - int(X0.n_bit_features) - int(X0.n_nib_features)
+            self.cols = torch.empty(cap * n_cols, dtype=torch.uint8, device=device)
+            gbdt_column_major(X0, self.cols)
         self.q = torch.zeros(n, dtype=torch.int64, device=device)
         self.qh = torch.zeros(n, dtype=torch.int32, device=device) if logistic else None
         self.hist_h = torch.zeros(sz.hist_slots * TB, dtype=torch.int64, device=device) if logistic else None
@@ -486,7 +520,8 @@ class Booster:
         self._buf = GrowBuffers(
             (Rows * 2)(self.pp[0].rows(), self.pp[1].rows()), _ptr(self.q), _ptr(self.hist_g),
             _ptr(self.hist_cnt), _ptr(self.splits), _ptr(self.lists), _ptr(self.ctrl), _ptr(self.ws),
-            self.ws.numel(), _ptr(self.qh), _ptr(self.hist_h), _ptr(self.split_h))
+            self.ws.numel(), _ptr(self.qh), _ptr(self.hist_h), _ptr(self.split_h), _ptr(self.rows_ix),
+            _ptr(self.cols))
         self._X = ds.X.matrix()
         self._ft = ds.ft.struct(ds.use_skip_bins)
 

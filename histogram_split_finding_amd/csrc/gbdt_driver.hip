@@ -484,6 +484,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   }
   if (logistic && (!b->qh || !b->hist_h || !b->split_h))
     return fail(GBDT_E_ARG, "the logistic objective needs qh, hist_h and split_h");
+  if (ids && b->rows_ix && (reinterpret_cast<uintptr_t>(b->rows_ix) & 3u))
+    return fail(GBDT_E_ARG, "rows_ix not 4-byte aligned");
   const int32_t D = p->max_depth;
   gbdt_grow_sizes_t sz;
   rc = gbdt_grow_sizes(n, ft->total_bins, D, &sz);
@@ -588,7 +590,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     gbdt_rows hsrc = src;
     if (ids) hsrc.X = *X;
     rc = launch_hist(hsrc, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s, q32,
-                     true, ids && src.rid != nullptr);
+                     true, ids && src.rid != nullptr, ids ? b->rows_ix : nullptr);
     if (rc) return rc;
     rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
                             h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s, guard);
@@ -626,7 +628,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     // prediction update routes rows through the finished tree instead
     if (d + 1 < D) {
       rc = launch_partition(hsrc, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], part_tile, s, q32, q32,
-                            ids);
+                            ids, ids ? b->cols : nullptr);
       if (rc) return rc;
       src = dst;
     }

@@ -209,10 +209,12 @@ int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
 // q32: src.q holds int32 elements (the tree driver's row buffers, see
 // driver_q32); otherwise int64 as the ABI declares.  ids (index mode, byte
 // blocks only): a tile's rows are the rows src.rid names (their q in src.q
-// at the tile's positions), read from the matrix src.X.
+// at the tile's positions), read from the matrix src.X, or from rows_ix, its
+// byte blocks interleaved row by row, when that is not NULL.
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
-                WsCtrl* ctrl, hipStream_t s, bool q32 = false, bool guard = false, bool ids = false);
+                WsCtrl* ctrl, hipStream_t s, bool q32 = false, bool guard = false, bool ids = false,
+                const uint8_t* rows_ix = nullptr);
 int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_cap,
                        const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
                        const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s,
@@ -229,10 +231,12 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
 // buffers); otherwise int64.  ids (index mode, byte blocks only): only each
 // position's row id (src.rid, NULL = the position itself) and q move, into
 // dst.rid and dst.q; the split byte is read from the matrix src.X at the row
-// id.
+// id, from cols, the matrix's byte columns one after another, when that is
+// not NULL.
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
-                     hipStream_t s, bool qin32 = false, bool qout32 = false, bool ids = false);
+                     hipStream_t s, bool qin32 = false, bool qout32 = false, bool ids = false,
+                     const uint8_t* cols = nullptr);
 
 // Blocks of the gradient kernels for n rows: each leaves a partial max |g|
 // and a partial sum of q in the workspace (gpart).

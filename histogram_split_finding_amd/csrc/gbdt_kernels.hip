@@ -841,7 +841,8 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     int32_t total_bins, int32_t lds_bins, const TileDesc* __restrict__ desc, int32_t bits,
     int64_t* __restrict__ hist_g, uint32_t* __restrict__ hist_cnt,
     uint64_t* __restrict__ partial, WsCtrl* __restrict__ ctrl, const int32_t* __restrict__ guard,
-    int32_t n_nib, int32_t nib_stride, const int32_t* __restrict__ ridx) {
+    int32_t n_nib, int32_t nib_stride, const int32_t* __restrict__ ridx, int64_t id_blk_pitch,
+    int32_t id_row_pitch, int32_t id_tiles) {
   static_assert(D == 1 || D == 2 || D == 4 || D == 8, "lanes per row");
   static_assert(!IDS || NARROW == 0, "index mode reads byte blocks only");
   if (failed(guard)) return;
@@ -860,8 +861,20 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   int32_t* const s_fgb = s_fbins + kHistRowSlots;                          // [kHistRowSlots]
   uint32_t* const s_inv = reinterpret_cast<uint32_t*>(s_fgb + kHistRowSlots);  // [kMaxBitWords]
   int32_t* const s_bit = reinterpret_cast<int32_t*>(s_inv + kMaxBitWords);  // [kBitStage]
-  const int32_t tile = blockIdx.x;
-  const int32_t blk = blockIdx.y;
+  // IDS with id_tiles > 0 (rows gathered from the interleaved copy): a 1-D
+  // grid in which workgroup w takes block (w / 8) % n_blocks of tile
+  // (w / (8 n_blocks)) 8 + w % 8.  Workgroups go to the XCDs in turn, so
+  // w % 8 -- the tile's residue -- names the XCD: the blocks of one tile,
+  // whose bytes share a row's cache lines, all run on one XCD, next to each
+  // other in time, and its L2 serves the lines to all of them.
+  int32_t tile = blockIdx.x;
+  int32_t blk = blockIdx.y;
+  if (IDS && id_tiles > 0) {
+    const int32_t w = blockIdx.x;
+    blk = (w >> 3) % n_blocks;
+    tile = (w / (8 * n_blocks)) * 8 + (w & 7);
+    if (tile >= id_tiles) return;
+  }
   const TileDesc td = desc[tile];
   if (NARROW > 0 && blk >= n_blocks) {  // the narrow blocks: bits, then nibbles
     if (td.node < 0) return;
@@ -951,9 +964,11 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   // 32-bit lane offset (a tile holds < 2^24 rows of at most 32 bytes)
   const int32_t nt = (int32_t)(r1 - r0);    // rows of the tile
   // IDS: the tile's positions r0 .. r1 hold the row ids ridx[r0 ..] of the
-  // matrix (tb is then the block's base); a row id outside the matrix is
-  // clamped to its last row, so no load leaves the block
-  const uint8_t* __restrict__ tb = IDS ? bins + int64_t(blk) * row_capacity * block_stride
+  // matrix, whose row id's block starts at bins + blk id_blk_pitch + id
+  // id_row_pitch (block-major: row_capacity block_stride and block_stride;
+  // interleaved: block_stride and n_blocks block_stride); a row id outside
+  // the matrix is clamped to its last row, so no load leaves the matrix
+  const uint8_t* __restrict__ tb = IDS ? bins + int64_t(blk) * id_blk_pitch
                                        : bins + (int64_t(blk) * row_capacity + r0) * block_stride;
   const int32_t* __restrict__ trid = IDS ? ridx + r0 : nullptr;
   const uint32_t last_row = (uint32_t)(row_capacity > 0 ? row_capacity - 1 : 0);
@@ -961,7 +976,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     if constexpr (IDS) {
       const uint32_t id = (uint32_t)trid[rc];
       return *reinterpret_cast<const uint32_t*>(
-          tb + (int64_t(id < last_row ? id : last_row) * block_stride + lane_off));
+          tb + (int64_t(id < last_row ? id : last_row) * id_row_pitch + lane_off));
     } else {
       return *reinterpret_cast<const uint32_t*>(tb + (__umul24(rc, (uint32_t)block_stride) + lane_off));
     }
@@ -1876,7 +1891,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     int32_t block_stride, int32_t n_features, int32_t n_bit, int32_t bit_stride,
     const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
     int32_t qsh /* log2 of the source q's element size: 2 (int32) or 3 (int64) */,
-    int32_t n_nib, int32_t nib_stride) {
+    int32_t n_nib, int32_t nib_stride, const uint8_t* __restrict__ scols) {
   static_assert(K == 2 || K == 4 || (K == 8 && IDS), "rows per thread");
   static_assert(!IDS || !NIB, "index mode moves no narrow block");
   constexpr int TILE = K * kPartThreads;
@@ -1942,7 +1957,11 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   const bool from_rows = !IDS && !fnarrow && n_blocks > 0;
   // IDS (index mode): position r0 + i holds row id srid[r0 + i] (the position
   // itself when srid is NULL) of the matrix sbins; only ids and q move, and
-  // the split byte is read at the row id (clamped into the matrix)
+  // the split byte is read at the row id (clamped into the matrix), from the
+  // column-major copy scols (column c's byte of row r at c row_capacity + r)
+  // when there is one: a node's rows, in ascending id order, then share a
+  // cache line per 128 consecutive ids instead of per 128 / block_stride
+  const bool from_cols = IDS && scols != nullptr;  // (uniform)
   int32_t rids[K];
   if (rows > 0) {
     const char* __restrict__ tq = reinterpret_cast<const char*>(sq) + (r0 << qsh);
@@ -1960,12 +1979,14 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
         const uint32_t ic = i < lr ? i : lr;
         rids[k] = srid != nullptr ? srid[r0 + ic] : (int32_t)(r0 + ic);
       }
+      const uint8_t* __restrict__ tcol = from_cols ? scols + int64_t(sc) * row_capacity : nullptr;
       bool bad_id = false;  // (an id outside the matrix is clamped into it and reported)
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         bad_id |= rids[k] < 0 || rids[k] > last;
         const int64_t id = rids[k] < 0 ? 0 : (rids[k] > last ? last : rids[k]);
-        fb[k] = (int32_t)*reinterpret_cast<const uint32_t*>(tf + id * int64_t(frow));
+        fb[k] = from_cols ? (int32_t)tcol[id]
+                          : (int32_t)*reinterpret_cast<const uint32_t*>(tf + id * int64_t(frow));
       }
       if (bad_id) dev_error(&ctrl->err, GBDT_E_INTERNAL);
     } else if (!from_rows) {
@@ -1996,7 +2017,9 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
 #pragma unroll
       for (int k = 0; k < K; ++k) fb[k] = (int32_t)((row_dword<ND>(rd[k], fdw) >> fsh) & 0xffu);
     } else {
-      const uint32_t fsh = fbit ? (uint32_t)(fk & 31) : (fnib ? 4u * (uint32_t)(fk & 7) : 8u * (uint32_t)(fcol & 3));
+      const uint32_t fsh = from_cols ? 0u
+                           : fbit ? (uint32_t)(fk & 31)
+                                  : (fnib ? 4u * (uint32_t)(fk & 7) : 8u * (uint32_t)(fcol & 3));
       const uint32_t fmask = fbit ? 1u : (fnib ? 15u : 0xffu);
 #pragma unroll
       for (int k = 0; k < K; ++k) fb[k] = (int32_t)(((uint32_t)fb[k] >> fsh) & fmask);
@@ -2554,6 +2577,42 @@ __global__ void __launch_bounds__(64) k_pick_skip(const uint32_t* __restrict__ c
   skip_bin[f] = bi;
 }
 
+// The byte blocks of a block-major matrix interleaved row by row (index
+// mode's gather copy): dword d of row r's block b goes to dword
+// (r n_blocks + b) nd + d, for every row below row_capacity.  One thread per
+// destination dword, so the stores are coalesced and each source read covers
+// a row's block.
+__global__ void __launch_bounds__(256) k_interleave(const uint32_t* __restrict__ src,
+                                                    uint32_t* __restrict__ dst, int64_t row_capacity,
+                                                    int32_t n_blocks, int32_t nd) {
+  const int64_t per_row = int64_t(n_blocks) * nd;
+  const int64_t total = row_capacity * per_row;
+  for (int64_t o = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; o < total;
+       o += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = o / per_row;
+    const int32_t e = (int32_t)(o - r * per_row);
+    const int32_t b = e / nd;
+    dst[o] = src[(int64_t(b) * row_capacity + r) * nd + (e - b * nd)];
+  }
+}
+
+// The byte columns of a block-major matrix one after another (index mode's
+// split-byte copy): column c = b block_features + j of row r goes to byte
+// c row_capacity + r.  One thread per destination byte (coalesced stores).
+__global__ void __launch_bounds__(256) k_columns(const uint8_t* __restrict__ src,
+                                                 uint8_t* __restrict__ dst, int64_t row_capacity,
+                                                 int32_t n_cols, int32_t block_features,
+                                                 int32_t block_stride) {
+  const int64_t total = row_capacity * n_cols;
+  for (int64_t o = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; o < total;
+       o += int64_t(gridDim.x) * blockDim.x) {
+    const int32_t c = (int32_t)(o / row_capacity);
+    const int64_t r = o - int64_t(c) * row_capacity;
+    const int32_t b = c / block_features;
+    dst[o] = src[(int64_t(b) * row_capacity + r) * block_stride + (c - b * block_features)];
+  }
+}
+
 __global__ void k_zero_u32(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += int64_t(gridDim.x) * blockDim.x)
@@ -2662,7 +2721,8 @@ static auto hist_kernel(int D) -> decltype(&k_hist<8, N, Q>) {
 
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
-                WsCtrl* ctrl, hipStream_t s, bool q32, bool guard, bool ids) {
+                WsCtrl* ctrl, hipStream_t s, bool q32, bool guard, bool ids,
+                const uint8_t* rows_ix) {
   const int64_t n_rows = src.X.n_rows > 0 ? src.X.n_rows : 1;
   const int32_t bits = pack_bits_for(n_rows);
   const bool has_bytes = src.X.n_features > src.X.n_bit_features + src.X.n_nib_features;
@@ -2686,13 +2746,23 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
   (void)has_bits;
   const unsigned gy = (unsigned)(src.X.n_blocks + (src.X.n_bit_features > 0 ? 1 : 0) +
                                  (src.X.n_nib_features > 0 ? 1 : 0));
+  // index mode gathers from the interleaved copy when there is one (row id's
+  // block b at rows_ix + (id n_blocks + b) block_stride), with the XCD-aware
+  // 1-D grid: ceil(max_tiles / 8) groups of 8 tiles times n_blocks blocks
+  const bool ix = ids && rows_ix != nullptr;
+  const int64_t bs = src.X.block_stride;
+  const int64_t id_blk_pitch = ix ? bs : src.X.row_capacity * bs;
+  const int32_t id_row_pitch = (int32_t)(ix ? int64_t(src.X.n_blocks) * bs : bs);
+  const dim3 grid = ix ? dim3((unsigned)((max_tiles + 7) / 8 * 8 * src.X.n_blocks), 1u)
+                       : dim3((unsigned)max_tiles, gy);
   diag_begin(kDiagHist, s);
-  hipLaunchKernelGGL(kern, dim3((unsigned)max_tiles, gy), dim3(kHistThreads), lds, s, src.X.bins,
+  hipLaunchKernelGGL(kern, grid, dim3(kHistThreads), lds, s, ix ? rows_ix : src.X.bins,
                      src.X.row_capacity, src.X.n_blocks, src.X.block_features, src.X.block_stride,
                      src.X.n_features, src.X.n_bit_features, src.X.bit_stride, src.X.col_feature,
                      src.q, ft.bin_offset, ft.skip_bin, ft.total_bins, ft.max_block_bins, desc, bits,
                      hist_g, hist_cnt, hpart, ctrl, guard ? &ctrl->err : nullptr, src.X.n_nib_features,
-                     src.X.nib_stride, ids ? src.rid : nullptr);
+                     src.X.nib_stride, ids ? src.rid : nullptr, id_blk_pitch, id_row_pitch,
+                     ix ? (int32_t)max_tiles : 0);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist");
   return GBDT_OK;
@@ -3151,7 +3221,7 @@ static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K, Q, N>) {
 
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
-                     hipStream_t s, bool qin32, bool qout32, bool ids) {
+                     hipStream_t s, bool qin32, bool qout32, bool ids, const uint8_t* cols) {
   const int32_t nd = src.X.n_blocks > 0 ? src.X.block_stride / 4 : 1;
   if (qin32 && !qout32) return fail(GBDT_E_INTERNAL, "an int64 q destination needs an int64 source");
   decltype(&k_partition<1, 2, false, false>) kern = nullptr;
@@ -3178,7 +3248,7 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
                      src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
                      src.X.block_features, src.X.block_stride, src.X.n_features,
                      src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl, qin32 ? 2 : 3,
-                     src.X.n_nib_features, src.X.nib_stride);
+                     src.X.n_nib_features, src.X.nib_stride, ids ? cols : nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_partition");
   return GBDT_OK;
@@ -3471,6 +3541,43 @@ int gbdt_pack_matrix(const uint8_t* rowmajor, const gbdt_matrix* dst, const gbdt
     diag_end(s);
     GBDT_LAUNCH_CHECK("k_pick_skip");
   }
+  return GBDT_OK;
+}
+
+int gbdt_interleave_rows(const gbdt_matrix* X, uint8_t* out, void* stream) {
+  if (!X || !out) return fail(GBDT_E_ARG, "null argument");
+  int rc = check_matrix(*X);
+  if (rc) return rc;
+  if (!aligned(out, 4)) return fail(GBDT_E_ARG, "out not 4-byte aligned");
+  const int64_t total = X->row_capacity * X->n_blocks * (X->block_stride / 4);
+  if (total == 0) return GBDT_OK;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 16384) grid = 16384;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  diag_begin(kDiagPack, s);
+  hipLaunchKernelGGL(k_interleave, dim3((unsigned)grid), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(X->bins), reinterpret_cast<uint32_t*>(out),
+                     X->row_capacity, X->n_blocks, X->block_stride / 4);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_interleave");
+  return GBDT_OK;
+}
+
+int gbdt_column_major(const gbdt_matrix* X, uint8_t* out, void* stream) {
+  if (!X || !out) return fail(GBDT_E_ARG, "null argument");
+  int rc = check_matrix(*X);
+  if (rc) return rc;
+  const int32_t n_cols = X->n_features - X->n_bit_features - X->n_nib_features;
+  const int64_t total = n_cols > 0 && X->n_blocks > 0 ? X->row_capacity * n_cols : 0;
+  if (total == 0) return GBDT_OK;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 16384) grid = 16384;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  diag_begin(kDiagPack, s);
+  hipLaunchKernelGGL(k_columns, dim3((unsigned)grid), dim3(256), 0, s, X->bins, out, X->row_capacity,
+                     n_cols, X->block_features, X->block_stride);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_columns");
   return GBDT_OK;
 }
 

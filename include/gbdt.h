@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GBDT_ABI_VERSION 5
+#define GBDT_ABI_VERSION 6
 #define GBDT_MAX_DEPTH 16       /* deepest tree the level loop supports */
 #define GBDT_MAX_FEATURES 4096
 #define GBDT_MAX_BINS 256       /* bins per feature */
@@ -553,6 +553,17 @@ typedef struct gbdt_grow_buffers {
   int32_t* qh;
   int64_t* hist_h;
   int64_t* split_h;
+  /* index mode only, optional (NULL: not used): X's byte blocks interleaved
+     row by row, as gbdt_interleave_rows writes them (row_capacity rows).
+     When set, index mode's histograms read the rows they reach through row
+     ids from here: a row's blocks then share cache lines, and the
+     workgroups of one tile's blocks run on one XCD and share its L2. */
+  uint8_t* rows_ix;
+  /* index mode only, optional (NULL: not used): X's byte columns one after
+     another, as gbdt_column_major writes them.  When set, index mode's
+     partition reads each row's split byte from here: a node's rows, whose
+     ids ascend, then share one cache line per 128 ids of the split column. */
+  uint8_t* cols;
 } gbdt_grow_buffers;
 
 /*
@@ -566,6 +577,24 @@ typedef struct gbdt_grow_buffers {
  * layouts move whole rows into node order and stream them.
  */
 int gbdt_grow_moves_ids(const gbdt_matrix* X /* host */, int32_t objective);
+
+/*
+ * X's byte blocks interleaved row by row: row r's block b (block_stride
+ * bytes) at out + (r * n_blocks + b) * block_stride, for r < n_rows.  out:
+ * device, at least n_rows * n_blocks * block_stride bytes, not overlapping
+ * X; the bit and nibble blocks are not copied.  The rows_ix buffer of
+ * gbdt_grow_tree's index mode, written once per matrix.
+ */
+int gbdt_interleave_rows(const gbdt_matrix* X /* host */, uint8_t* out, void* stream);
+
+/*
+ * X's byte columns one after another: byte column c's bin of row r at
+ * out + c * row_capacity + r, for c < n_features - n_bit_features -
+ * n_nib_features and r < row_capacity.  out: device, at least row_capacity
+ * bytes per byte column, not overlapping X.  The cols buffer of
+ * gbdt_grow_tree's index mode, written once per matrix.
+ */
+int gbdt_column_major(const gbdt_matrix* X /* host */, uint8_t* out, void* stream);
 
 /* Sizes (in elements / bytes as named) of the driver's buffers. */
 typedef struct gbdt_grow_sizes_t {

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
         assert name in names
     for name in names:
         assert hasattr(lib, name), name
-    assert g.gbdt_abi_version() == 5
+    assert g.gbdt_abi_version() == 6
 
 
 def test_library_is_not_linked_to_the_oracle():

@@ -6,7 +6,10 @@ node's rows of the original matrix through the ids.
 Trees (node by node), the histograms of every node the first tree builds or
 derives, and the predictions must equal the oracle's bit for bit, for two to
 eight blocks, skewed and uniform bins, ragged row counts, small nodes, and
-more than 4M rows (the 8192-row partition tiles and int32 q).
+more than 4M rows (the 8192-row partition tiles and int32 q) -- gathering
+from the block-major matrix itself and from its row-interleaved and
+column-major copies (gbdt_interleave_rows, gbdt_column_major), which their
+own test checks byte by byte.
 """
 import numpy as np
 import pytest
@@ -30,15 +33,17 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("interleave", [False, True])
 @pytest.mark.parametrize("case", CASES)
-def test_index_mode_trees_match_oracle(case):
-    say("index mode: %s" % case)
+def test_index_mode_trees_match_oracle(case, interleave):
+    say("index mode: %s interleave %s" % (case, interleave))
     bins, label, nb = datagen.make_random(case["n"], case["n_bins"], case["seed"], bin_kind=case["bin_kind"])
     pk = dict(max_depth=case["depth"], min_samples_leaf=case["msl"], learning_rate=0.4)
     ds = g.Dataset(bins, label, nb, DEV, pack_bits=False, pack_nibbles=False)
     assert ds.X.n_blocks >= 2
-    bst = g.Booster(ds, g.make_params(**pk))
+    bst = g.Booster(ds, g.make_params(**pk), interleave=interleave)
     assert bst.moves_ids and bst.pp[0].bins is None
+    assert (bst.rows_ix is not None) == interleave and (bst.cols is not None) == interleave
     p = oracle.make_params(**pk)
     ref = oracle.train(bins, nb, label, p, case["T"], keep_pred_per_tree=True, dump_tree=0)
     bst.train(1)
@@ -56,15 +61,50 @@ def test_index_mode_trees_match_oracle(case):
     assert np.array_equal(bst.pred.cpu().numpy(), ref["pred"])
 
 
-def test_index_mode_over_4m_rows():
+def test_copy_layouts():
+    """gbdt_interleave_rows: row r's block b lands at (r n_blocks + b)
+    block_stride; gbdt_column_major: column c's byte of row r at
+    c row_capacity + r -- for a ragged row count and three blocks."""
+    import torch
+    n = 3001
+    bins, label, nb = datagen.make_random(n, [256] * 70, 96)
+    ds = g.Dataset(bins, label, nb, DEV, pack_bits=False, pack_nibbles=False)
+    X = ds.X.matrix()
+    nbk, bs, cap = int(X.n_blocks), int(X.block_stride), int(X.row_capacity)
+    assert nbk == 3
+    out = torch.full((cap * nbk * bs + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    g.gbdt_interleave_rows(X, out)
+    got = out.cpu().numpy()
+    blocked = ds.X.bins.cpu().numpy()[: nbk * cap * bs].reshape(nbk, cap, bs)
+    want = blocked.transpose(1, 0, 2).reshape(-1)
+    assert np.array_equal(got[: cap * nbk * bs], want)
+    assert (got[cap * nbk * bs:] == 0xA5).all()  # nothing past the copy is written
+    # the copy's block b, column j of row r is the matrix's bin of that column
+    # (no packing: matrix column c is feature c)
+    assert not ds.ft.mapped
+    bf = int(X.block_features)
+    r = np.arange(n)
+    for c in (0, 5, bf, 2 * bf + 1, 69):
+        b, j = divmod(c, bf)
+        assert np.array_equal(got[: cap * nbk * bs].reshape(cap, nbk, bs)[r, b, j], bins[r, c])
+    F = bins.shape[1]
+    cols = torch.full((cap * F + 64,), 0x5A, dtype=torch.uint8, device=DEV)
+    g.gbdt_column_major(X, cols)
+    got = cols.cpu().numpy()
+    assert np.array_equal(got[: cap * F].reshape(F, cap)[:, :n], bins.T)
+    assert (got[cap * F:] == 0x5A).all()
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+def test_index_mode_over_4m_rows(interleave):
     """More than 4M rows of two blocks: int32 q and the 8192-row tiles of the
     id-only partition."""
     n = (1 << 22) + 4321
-    say("index mode: %d rows" % n)
+    say("index mode: %d rows interleave %s" % (n, interleave))
     bins, label, nb = datagen.make_random(n, [64] * 40, 95)
     pk = dict(max_depth=5, learning_rate=0.3)
     ds = g.Dataset(bins, label, nb, DEV)
-    bst = g.Booster(ds, g.make_params(**pk))
+    bst = g.Booster(ds, g.make_params(**pk), interleave=interleave)
     assert bst.moves_ids
     bst.train(2)
     ref = oracle.train(bins, nb, label, oracle.make_params(**pk), 2)
