@@ -132,6 +132,7 @@ def load():
         "gbdt_grow_sizes": (ctypes.c_int, [i64, i32, i32, P(GrowSizes)]),
         "gbdt_grow_moves_ids": (ctypes.c_int, [P(Matrix), i32]),
         "gbdt_interleave_rows": (ctypes.c_int, [P(Matrix), vp, vp]),
+        "gbdt_interleave_pitch": (i32, [P(Matrix)]),
         "gbdt_column_major": (ctypes.c_int, [P(Matrix), vp, vp]),
         "gbdt_grow_tree": (ctypes.c_int, [P(Matrix), P(Features), vp, vp, P(Params), vp, vp,
                                           P(GrowBuffers), vp]),
@@ -421,10 +422,15 @@ def gbdt_predict(X: Matrix, trees, n_nodes, n_trees, tree_stride, base_score, le
     _check(rc, "gbdt_predict")
 
 
+def gbdt_interleave_pitch(X: Matrix) -> int:
+    """Row pitch in bytes of gbdt_interleave_rows' copy."""
+    return int(load().gbdt_interleave_pitch(ctypes.byref(X)))
+
+
 def gbdt_interleave_rows(X: Matrix, out, stream=None):
     """X's byte blocks interleaved row by row into out (a uint8 device tensor
-    of at least row_capacity * n_blocks * block_stride bytes)."""
-    need = int(X.row_capacity) * int(X.n_blocks) * int(X.block_stride)
+    of at least row_capacity * gbdt_interleave_pitch(X) bytes)."""
+    need = int(X.row_capacity) * gbdt_interleave_pitch(X)
     if out.numel() * out.element_size() < need:
         raise ValueError("out holds fewer than %d bytes" % need)
     _check(load().gbdt_interleave_rows(ctypes.byref(X), _ptr(out), _stream(stream)),
@@ -499,8 +505,7 @@ class Booster:
         self.rows_ix = self.cols = None
         if self.moves_ids and interleave:
             cap = int(X0.row_capacity)
-            self.rows_ix = torch.empty(cap * int(X0.n_blocks) * int(X0.block_stride), dtype=torch.uint8,
-                                       device=device)
+            self.rows_ix = torch.empty(cap * gbdt_interleave_pitch(X0), dtype=torch.uint8, device=device)
             gbdt_interleave_rows(X0, self.rows_ix)
             n_cols = int(X0.n_features) - int(X0.n_bit_features) - int(X0.n_nib_features)
             self.cols = torch.empty(cap * n_cols, dtype=torch.uint8, device=device)

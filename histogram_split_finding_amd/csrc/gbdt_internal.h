@@ -211,6 +211,17 @@ int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
 // blocks only): a tile's rows are the rows src.rid names (their q in src.q
 // at the tile's positions), read from the matrix src.X, or from rows_ix, its
 // byte blocks interleaved row by row, when that is not NULL.
+// Row pitch in bytes of index mode's row-interleaved copy: the row's
+// n_blocks * block_stride bytes rounded up to a power of two up to 128 (so no
+// row straddles a 128-byte cache line), else to a multiple of 128.
+inline int32_t interleave_pitch(const gbdt_matrix& X) {
+  const int32_t p = X.n_blocks * X.block_stride;
+  if (p > 128) return (p + 127) / 128 * 128;
+  int32_t q = 4;
+  while (q < p) q *= 2;
+  return q;
+}
+
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
                 WsCtrl* ctrl, hipStream_t s, bool q32 = false, bool guard = false, bool ids = false,

@@ -861,15 +861,15 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
   int32_t* const s_fgb = s_fbins + kHistRowSlots;                          // [kHistRowSlots]
   uint32_t* const s_inv = reinterpret_cast<uint32_t*>(s_fgb + kHistRowSlots);  // [kMaxBitWords]
   int32_t* const s_bit = reinterpret_cast<int32_t*>(s_inv + kMaxBitWords);  // [kBitStage]
-  // IDS with id_tiles > 0 (rows gathered from the interleaved copy): a 1-D
-  // grid in which workgroup w takes block (w / 8) % n_blocks of tile
+  // id_tiles > 0 (index mode with the interleaved copy; byte blocks only): a
+  // 1-D grid in which workgroup w takes block (w / 8) % n_blocks of tile
   // (w / (8 n_blocks)) 8 + w % 8.  Workgroups go to the XCDs in turn, so
   // w % 8 -- the tile's residue -- names the XCD: the blocks of one tile,
-  // whose bytes share a row's cache lines, all run on one XCD, next to each
-  // other in time, and its L2 serves the lines to all of them.
+  // which read the same q and, gathering, a row's cache lines, all run on
+  // one XCD, next to each other in time, and its L2 serves them all.
   int32_t tile = blockIdx.x;
   int32_t blk = blockIdx.y;
-  if (IDS && id_tiles > 0) {
+  if (NARROW == 0 && id_tiles > 0) {
     const int32_t w = blockIdx.x;
     blk = (w >> 3) % n_blocks;
     tile = (w / (8 * n_blocks)) * 8 + (w & 7);
@@ -2579,20 +2579,19 @@ __global__ void __launch_bounds__(64) k_pick_skip(const uint32_t* __restrict__ c
 
 // The byte blocks of a block-major matrix interleaved row by row (index
 // mode's gather copy): dword d of row r's block b goes to dword
-// (r n_blocks + b) nd + d, for every row below row_capacity.  One thread per
-// destination dword, so the stores are coalesced and each source read covers
-// a row's block.
+// r pd + b nd + d (pd dwords per row, the padding after the blocks zero), for
+// every row below row_capacity.  One thread per destination dword, so the
+// stores are coalesced and each source read covers a row's block.
 __global__ void __launch_bounds__(256) k_interleave(const uint32_t* __restrict__ src,
                                                     uint32_t* __restrict__ dst, int64_t row_capacity,
-                                                    int32_t n_blocks, int32_t nd) {
-  const int64_t per_row = int64_t(n_blocks) * nd;
-  const int64_t total = row_capacity * per_row;
+                                                    int32_t n_blocks, int32_t nd, int32_t pd) {
+  const int64_t total = row_capacity * pd;
   for (int64_t o = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; o < total;
        o += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t r = o / per_row;
-    const int32_t e = (int32_t)(o - r * per_row);
+    const int64_t r = o / pd;
+    const int32_t e = (int32_t)(o - r * pd);
     const int32_t b = e / nd;
-    dst[o] = src[(int64_t(b) * row_capacity + r) * nd + (e - b * nd)];
+    dst[o] = b < n_blocks ? src[(int64_t(b) * row_capacity + r) * nd + (e - b * nd)] : 0u;
   }
 }
 
@@ -2747,14 +2746,16 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
   const unsigned gy = (unsigned)(src.X.n_blocks + (src.X.n_bit_features > 0 ? 1 : 0) +
                                  (src.X.n_nib_features > 0 ? 1 : 0));
   // index mode gathers from the interleaved copy when there is one (row id's
-  // block b at rows_ix + (id n_blocks + b) block_stride), with the XCD-aware
-  // 1-D grid: ceil(max_tiles / 8) groups of 8 tiles times n_blocks blocks
+  // block b at rows_ix + id pitch + b block_stride), with the XCD-aware 1-D
+  // grid: ceil(max_tiles / 8) groups of 8 tiles times n_blocks blocks
+  // (the root level of index mode reads X in row order, on the same grid)
   const bool ix = ids && rows_ix != nullptr;
+  const bool xgrid = rows_ix != nullptr && narrow == 0 && src.X.n_blocks >= 1;
   const int64_t bs = src.X.block_stride;
   const int64_t id_blk_pitch = ix ? bs : src.X.row_capacity * bs;
-  const int32_t id_row_pitch = (int32_t)(ix ? int64_t(src.X.n_blocks) * bs : bs);
-  const dim3 grid = ix ? dim3((unsigned)((max_tiles + 7) / 8 * 8 * src.X.n_blocks), 1u)
-                       : dim3((unsigned)max_tiles, gy);
+  const int32_t id_row_pitch = ix ? interleave_pitch(src.X) : (int32_t)bs;
+  const dim3 grid = xgrid ? dim3((unsigned)((max_tiles + 7) / 8 * 8 * src.X.n_blocks), 1u)
+                          : dim3((unsigned)max_tiles, gy);
   diag_begin(kDiagHist, s);
   hipLaunchKernelGGL(kern, grid, dim3(kHistThreads), lds, s, ix ? rows_ix : src.X.bins,
                      src.X.row_capacity, src.X.n_blocks, src.X.block_features, src.X.block_stride,
@@ -2762,7 +2763,7 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
                      src.q, ft.bin_offset, ft.skip_bin, ft.total_bins, ft.max_block_bins, desc, bits,
                      hist_g, hist_cnt, hpart, ctrl, guard ? &ctrl->err : nullptr, src.X.n_nib_features,
                      src.X.nib_stride, ids ? src.rid : nullptr, id_blk_pitch, id_row_pitch,
-                     ix ? (int32_t)max_tiles : 0);
+                     xgrid ? (int32_t)max_tiles : 0);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist");
   return GBDT_OK;
@@ -3549,7 +3550,9 @@ int gbdt_interleave_rows(const gbdt_matrix* X, uint8_t* out, void* stream) {
   int rc = check_matrix(*X);
   if (rc) return rc;
   if (!aligned(out, 4)) return fail(GBDT_E_ARG, "out not 4-byte aligned");
-  const int64_t total = X->row_capacity * X->n_blocks * (X->block_stride / 4);
+  if (X->n_blocks < 1 || X->block_stride < 4) return GBDT_OK;
+  const int32_t pd = interleave_pitch(*X) / 4;
+  const int64_t total = X->row_capacity * pd;
   if (total == 0) return GBDT_OK;
   int64_t grid = (total + 255) / 256;
   if (grid > 16384) grid = 16384;
@@ -3557,10 +3560,15 @@ int gbdt_interleave_rows(const gbdt_matrix* X, uint8_t* out, void* stream) {
   diag_begin(kDiagPack, s);
   hipLaunchKernelGGL(k_interleave, dim3((unsigned)grid), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t*>(X->bins), reinterpret_cast<uint32_t*>(out),
-                     X->row_capacity, X->n_blocks, X->block_stride / 4);
+                     X->row_capacity, X->n_blocks, X->block_stride / 4, pd);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_interleave");
   return GBDT_OK;
+}
+
+int32_t gbdt_interleave_pitch(const gbdt_matrix* X) {
+  if (!X || X->n_blocks < 1 || X->block_stride < 4) return 0;
+  return interleave_pitch(*X);
 }
 
 int gbdt_column_major(const gbdt_matrix* X, uint8_t* out, void* stream) {

@@ -554,7 +554,8 @@ typedef struct gbdt_grow_buffers {
   int64_t* hist_h;
   int64_t* split_h;
   /* index mode only, optional (NULL: not used): X's byte blocks interleaved
-     row by row, as gbdt_interleave_rows writes them (row_capacity rows).
+     row by row, as gbdt_interleave_rows writes them (row_capacity rows of
+     gbdt_interleave_pitch bytes).
      When set, index mode's histograms read the rows they reach through row
      ids from here: a row's blocks then share cache lines, and the
      workgroups of one tile's blocks run on one XCD and share its L2. */
@@ -580,19 +581,34 @@ int gbdt_grow_moves_ids(const gbdt_matrix* X /* host */, int32_t objective);
 
 /*
  * X's byte blocks interleaved row by row: row r's block b (block_stride
- * bytes) at out + (r * n_blocks + b) * block_stride, for r < n_rows.  out:
- * device, at least n_rows * n_blocks * block_stride bytes, not overlapping
- * X; the bit and nibble blocks are not copied.  The rows_ix buffer of
- * gbdt_grow_tree's index mode, written once per matrix.
+ * bytes) at out + r * P + b * block_stride, for r < row_capacity, where
+ * P = gbdt_interleave_pitch(X); the P - n_blocks * block_stride bytes after
+ * a row's blocks are written as 0.  out: device, 4-byte aligned (128-byte
+ * aligned keeps each row inside whole cache lines), at least row_capacity *
+ * P bytes, not overlapping X, written and nothing else; the bit and nibble
+ * blocks are not copied.  The rows_ix buffer of gbdt_grow_tree's index mode,
+ * written once per matrix (enqueued on stream; no host sync).  Errors:
+ * GBDT_E_ARG for a null or misaligned pointer, the matrix checks of
+ * gbdt_build_histograms.
  */
 int gbdt_interleave_rows(const gbdt_matrix* X /* host */, uint8_t* out, void* stream);
+
+/*
+ * Row pitch P in bytes of gbdt_interleave_rows' copy: n_blocks *
+ * block_stride rounded up to a power of two when at most 128 (so a gathered
+ * row never straddles two 128-byte cache lines), else to a multiple of 128;
+ * 0 for a matrix with no byte block.
+ */
+int32_t gbdt_interleave_pitch(const gbdt_matrix* X /* host */);
 
 /*
  * X's byte columns one after another: byte column c's bin of row r at
  * out + c * row_capacity + r, for c < n_features - n_bit_features -
  * n_nib_features and r < row_capacity.  out: device, at least row_capacity
- * bytes per byte column, not overlapping X.  The cols buffer of
- * gbdt_grow_tree's index mode, written once per matrix.
+ * bytes per byte column, not overlapping X, written and nothing else.  The
+ * cols buffer of gbdt_grow_tree's index mode, written once per matrix
+ * (enqueued on stream; no host sync).  Errors: GBDT_E_ARG for a null
+ * pointer, the matrix checks of gbdt_build_histograms.
  */
 int gbdt_column_major(const gbdt_matrix* X /* host */, uint8_t* out, void* stream);
 

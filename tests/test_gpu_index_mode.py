@@ -62,37 +62,42 @@ def test_index_mode_trees_match_oracle(case, interleave):
 
 
 def test_copy_layouts():
-    """gbdt_interleave_rows: row r's block b lands at (r n_blocks + b)
-    block_stride; gbdt_column_major: column c's byte of row r at
-    c row_capacity + r -- for a ragged row count and three blocks."""
+    """gbdt_interleave_rows: row r's block b lands at r P + b block_stride,
+    the bytes after a row's blocks zero, with P the row's bytes rounded up to
+    a power of two up to 128 and to a multiple of 128 beyond;
+    gbdt_column_major: column c's byte of row r at c row_capacity + r -- for
+    a ragged row count and three blocks (P 128 and 64) and eight (P 256)."""
     import torch
     n = 3001
-    bins, label, nb = datagen.make_random(n, [256] * 70, 96)
-    ds = g.Dataset(bins, label, nb, DEV, pack_bits=False, pack_nibbles=False)
-    X = ds.X.matrix()
-    nbk, bs, cap = int(X.n_blocks), int(X.block_stride), int(X.row_capacity)
-    assert nbk == 3
-    out = torch.full((cap * nbk * bs + 64,), 0xA5, dtype=torch.uint8, device=DEV)
-    g.gbdt_interleave_rows(X, out)
-    got = out.cpu().numpy()
-    blocked = ds.X.bins.cpu().numpy()[: nbk * cap * bs].reshape(nbk, cap, bs)
-    want = blocked.transpose(1, 0, 2).reshape(-1)
-    assert np.array_equal(got[: cap * nbk * bs], want)
-    assert (got[cap * nbk * bs:] == 0xA5).all()  # nothing past the copy is written
-    # the copy's block b, column j of row r is the matrix's bin of that column
-    # (no packing: matrix column c is feature c)
-    assert not ds.ft.mapped
-    bf = int(X.block_features)
-    r = np.arange(n)
-    for c in (0, 5, bf, 2 * bf + 1, 69):
-        b, j = divmod(c, bf)
-        assert np.array_equal(got[: cap * nbk * bs].reshape(cap, nbk, bs)[r, b, j], bins[r, c])
-    F = bins.shape[1]
-    cols = torch.full((cap * F + 64,), 0x5A, dtype=torch.uint8, device=DEV)
-    g.gbdt_column_major(X, cols)
-    got = cols.cpu().numpy()
-    assert np.array_equal(got[: cap * F].reshape(F, cap)[:, :n], bins.T)
-    assert (got[cap * F:] == 0x5A).all()
+    for F, want_P in ((70, 128), (40, 64), (250, 256)):
+        bins, label, nb = datagen.make_random(n, [256] * F, 96)
+        ds = g.Dataset(bins, label, nb, DEV, pack_bits=False, pack_nibbles=False)
+        X = ds.X.matrix()
+        nbk, bs, cap = int(X.n_blocks), int(X.block_stride), int(X.row_capacity)
+        P = g.gbdt_interleave_pitch(X)
+        say("copy layout: F %d blocks %d stride %d pitch %d" % (F, nbk, bs, P))
+        assert P == want_P and P >= nbk * bs
+        out = torch.full((cap * P + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+        g.gbdt_interleave_rows(X, out)
+        got = out.cpu().numpy()
+        assert (got[cap * P:] == 0xA5).all()  # nothing past the copy is written
+        rows = got[: cap * P].reshape(cap, P)
+        blocked = ds.X.bins.cpu().numpy()[: nbk * cap * bs].reshape(nbk, cap, bs)
+        assert np.array_equal(rows[:, : nbk * bs].reshape(cap, nbk, bs), blocked.transpose(1, 0, 2))
+        assert (rows[:, nbk * bs:] == 0).all()
+        # the copy's block b, column j of row r is the matrix's bin of that
+        # column (no packing: matrix column c is feature c)
+        assert not ds.ft.mapped
+        bf = int(X.block_features)
+        r = np.arange(n)
+        for c in sorted({0, 5, bf, min(2 * bf + 1, F - 1), F - 1}):
+            b, j = divmod(c, bf)
+            assert np.array_equal(rows[r, b * bs + j], bins[r, c])
+        cols = torch.full((cap * F + 64,), 0x5A, dtype=torch.uint8, device=DEV)
+        g.gbdt_column_major(X, cols)
+        got = cols.cpu().numpy()
+        assert np.array_equal(got[: cap * F].reshape(F, cap)[:, :n], bins.T)
+        assert (got[cap * F:] == 0x5A).all()
 
 
 @pytest.mark.parametrize("interleave", [False, True])
