@@ -204,7 +204,8 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t hist_target, int32_t hist_min_rows,
                                                 int32_t hist_max_tiles_next,
                                                 const int32_t* __restrict__ guard,
-                                                const int64_t* __restrict__ split_h) {
+                                                const int64_t* __restrict__ split_h,
+                                                int32_t filt_next) {
   __shared__ PlanLds lds;
   __shared__ int32_t shm[6 * 17];
   // after an error nothing of the level is written, and the partition that
@@ -250,8 +251,10 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
         if ((int64_t)(nl > nr ? nl : nr) >= min_split) {
           ++c[1];
           c[2] += ((int64_t)nl >= min_split) + ((int64_t)nr >= min_split);
-          c[5] += nl <= nr ? nl : nr;
-          my_small = nl <= nr ? nl : nr;
+          // (a filtered next level reads the parent's rows)
+          const int32_t rows = filt_next ? count : (nl <= nr ? nl : nr);
+          c[5] += rows;
+          my_small = rows;
         }
       }
     } else {
@@ -274,7 +277,8 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
         const gbdt_split sp = splits[v];
         if (!sp.valid) continue;
         const int32_t nl = sp.n_left, nr = nodes[v].count - sp.n_left;
-        if ((int64_t)(nl > nr ? nl : nr) >= min_split) nt += tiles_of(nl <= nr ? nl : nr, hist_tile_rows_next);
+        if ((int64_t)(nl > nr ? nl : nr) >= min_split)
+          nt += tiles_of(filt_next ? nodes[v].count : (nl <= nr ? nl : nr), hist_tile_rows_next);
       }
     }
     int32_t tot;
@@ -353,9 +357,19 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
         if (fast) {
           PlanEntry pe;
           pe.node = sm;
-          pe.begin = sm == lc ? L.begin : R.begin;
-          pe.count = sm == lc ? nl : nr;
-          pe.feature = pe.threshold_bin = pe.n_left = 0;
+          if (filt_next) {
+            // a filtered tile: the parent's rows, of which it keeps those
+            // going to sm (n_left 2: the left child, 3: the right one)
+            pe.begin = nd.begin;
+            pe.count = nd.count < 0 ? 0 : nd.count;
+            pe.feature = split_column(s, pa.feature_col, pa.n_features);
+            pe.threshold_bin = s.threshold_bin;
+            pe.n_left = sm == lc ? 2 : 3;
+          } else {
+            pe.begin = sm == lc ? L.begin : R.begin;
+            pe.count = sm == lc ? nl : nr;
+            pe.feature = pe.threshold_bin = pe.n_left = 0;
+          }
           stH[r_pair] = pe;
           spH[r_pair] = r[5];
         }
@@ -404,12 +418,19 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
     }
   }
   if (last) return;
+  // (the driver filters only levels whose parents fit this path)
+  if (filt_next && !fast) {
+    if (threadIdx.x == 0) dev_error(&pa.ctrl->err, GBDT_E_INTERNAL);
+    return;
+  }
   __syncthreads();  // the lists, the children's counts and the staged entries are visible
-  // this level's partition plan (splitting nodes) and the next level's
-  // histogram plan (nodes to build)
+  // this level's partition plan (splitting nodes; none when the next level
+  // is filtered: its rows are not moved) and the next level's histogram plan
+  // (nodes to build)
   if (fast) {
-    plan_emit(stP, spP, &lds.n_multi, t_split, part_tile, part_max_tiles, pa.prefix, pa.desc,
-              pa.status, pa.ctrl, true, nullptr, nullptr);
+    if (!filt_next)
+      plan_emit(stP, spP, &lds.n_multi, t_split, part_tile, part_max_tiles, pa.prefix, pa.desc,
+                pa.status, pa.ctrl, true, nullptr, nullptr);
     plan_emit(stH, spH, &lds.n_multi, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix,
               pa.hdesc, nullptr, pa.ctrl, false, pa.hmulti, lds.bucket);
   } else {
@@ -540,9 +561,16 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   const int32_t min_rows =
       hist_min_tile_rows(ft->total_bins,
                          int64_t(X->n_blocks) * X->block_stride + X->bit_stride + X->nib_stride);
+  // The rows of the last level's nodes are never moved: the partition before
+  // it is skipped too (level D - 2), and the last level's histogram tiles
+  // read each parent's rows, keeping those that go to the child they build.
+  // That trades one full row move for reading the larger children's rows
+  // once.  Row-moving mode only (index mode would gather them), and only
+  // while the level-(D - 2) nodes fit one planning pass (D <= 12).
+  const int32_t filt_level = (!ids && D >= 2 && D <= 12) ? D - 2 : -1;
   for (int32_t d = 0; d <= D; ++d) {
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
-    const int64_t rows_build = d == 0 ? n : n / 2;
+    const int64_t rows_build = (d == 0 || (filt_level >= 0 && d == filt_level + 1)) ? n : n / 2;
     h_rows[d] = hist_tile_rows(rows_build, n, target, min_rows);
     if (d == 0) {
       h_tiles[d] = (rows_build + h_rows[d] - 1) / h_rows[d] + cap_build;
@@ -589,8 +617,9 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     // the level's order; the root reads X in row order)
     gbdt_rows hsrc = src;
     if (ids) hsrc.X = *X;
+    const bool filt = filt_level >= 0 && d == filt_level + 1;
     rc = launch_hist(hsrc, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s, q32,
-                     true, ids && src.rid != nullptr, ids ? b->rows_ix : nullptr);
+                     true, ids && src.rid != nullptr, ids ? b->rows_ix : nullptr, filt);
     if (rc) return rc;
     rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
                             h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s, guard);
@@ -602,7 +631,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
       gbdt_rows hs = src;
       hs.q = reinterpret_cast<int64_t*>(src.rid);
       rc = launch_hist(hs, *ft, pa.hdesc, h_tiles[d], b->hist_h, b->hist_cnt, hpart, pa.ctrl, s, true,
-                       true);
+                       true, false, nullptr, filt);
       if (rc) return rc;
       rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
                               h_tiles[d], n, ft->total_bins, hpart, b->hist_h, b->hist_cnt, s, guard);
@@ -618,15 +647,16 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     hipLaunchKernelGGL(k_level, dim3(1), dim3(1024), 0, s, d, D, nodes_out, b->splits, tc, b->lists,
                        LL, min_split, p->reg_lambda, n_nodes_dev, pa, part_tile, (int32_t)p_tiles[d],
                        tile_max, target, min_rows, (int32_t)h_tiles[d + 1], guard,
-                       logistic ? b->split_h : nullptr);
+                       logistic ? b->split_h : nullptr, d == filt_level ? 1 : 0);
     diag_end(s);
     {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return hip_fail(e, "k_level");
     }
     // the rows of the last level's children are never read again: the
-    // prediction update routes rows through the finished tree instead
-    if (d + 1 < D) {
+    // prediction update routes rows through the finished tree instead (and
+    // the level before it is not moved either: see filt_level)
+    if (d + 1 < D && d != filt_level) {
       rc = launch_partition(hsrc, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], part_tile, s, q32, q32,
                             ids, ids ? b->cols : nullptr);
       if (rc) return rc;

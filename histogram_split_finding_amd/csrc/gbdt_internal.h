@@ -206,11 +206,6 @@ bool same_layout(const gbdt_matrix& a, const gbdt_matrix& b);
 int check_matrix(const gbdt_matrix& X);
 int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft);
 int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
-// q32: src.q holds int32 elements (the tree driver's row buffers, see
-// driver_q32); otherwise int64 as the ABI declares.  ids (index mode, byte
-// blocks only): a tile's rows are the rows src.rid names (their q in src.q
-// at the tile's positions), read from the matrix src.X, or from rows_ix, its
-// byte blocks interleaved row by row, when that is not NULL.
 // Row pitch in bytes of index mode's row-interleaved copy: the row's
 // n_blocks * block_stride bytes rounded up to a power of two up to 128 (so no
 // row straddles a 128-byte cache line), else to a multiple of 128.
@@ -222,10 +217,17 @@ inline int32_t interleave_pitch(const gbdt_matrix& X) {
   return q;
 }
 
+// q32: src.q holds int32 elements (the tree driver's row buffers, see
+// driver_q32); otherwise int64 as the ABI declares.  ids (index mode, byte
+// blocks only): a tile's rows are the rows src.rid names (their q in src.q
+// at the tile's positions), read from the matrix src.X, or from rows_ix, its
+// byte blocks interleaved row by row, when that is not NULL.  filt: the
+// plan's tiles are filtered (each reads rows of a parent's segment and keeps
+// those going to the child it builds; rows in order only).
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
                 WsCtrl* ctrl, hipStream_t s, bool q32 = false, bool guard = false, bool ids = false,
-                const uint8_t* rows_ix = nullptr);
+                const uint8_t* rows_ix = nullptr, bool filt = false);
 int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_cap,
                        const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
                        const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s,

@@ -548,6 +548,77 @@ inline int load_unit_for(int32_t block_stride) {
   return 4;
 }
 
+// Filtered histogram tiles (the last level of a tree whose partition before
+// it was skipped): the tile reads rows of its parent's segment and adds only
+// those that go to the child it builds -- bin <= threshold for the left
+// child, > threshold for the right one, the stable partition's rule
+// ("Module Design: Training Core", section 6, step 5).  A tile descriptor
+// marks it in n_left: 2 keeps the left-going rows, 3 the right-going ones;
+// feature and threshold_bin carry the parent's split (the feature as its
+// matrix column).  The row's split value is the field at `sh` (width mask)
+// of the dword at base + row * stride.
+struct RowFilter {
+  const uint8_t* base;
+  int64_t stride;
+  uint32_t sh, mask;
+  int32_t thr;
+  bool left;
+};
+
+__device__ __forceinline__ bool tile_filtered(const TileDesc& td) { return td.n_left >= 2; }
+
+__device__ inline RowFilter row_filter(const TileDesc& td, const uint8_t* bins, int64_t row_capacity,
+                                       int32_t n_blocks, int32_t block_features, int32_t block_stride,
+                                       int32_t n_features, int32_t n_bit, int32_t bit_stride,
+                                       int32_t n_nib, int32_t nib_stride, WsCtrl* ctrl) {
+  RowFilter f;
+  const int32_t nbc = n_features - n_bit;  // first bit column
+  const int32_t nbyte = nbc - n_nib;       // first nibble column
+  const int32_t c = td.feature;
+  const uint8_t* bits = bins + int64_t(n_blocks) * row_capacity * block_stride;
+  const uint8_t* nibs = bits + row_capacity * bit_stride;
+  f.left = td.n_left == 2;
+  f.thr = td.threshold_bin;
+  if (c < 0 || c >= n_features || td.n_left > 3) {
+    // (not a valid split: no row is kept, and the error word is set)
+    if (threadIdx.x == 0 && ctrl != nullptr) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+    f.base = bins;
+    f.stride = 0;
+    f.sh = 0u;
+    f.mask = 0u;
+    f.thr = -1;
+    f.left = true;
+  } else if (c >= nbc) {
+    const int32_t k = c - nbc;
+    f.base = bits + 4 * (k >> 5);
+    f.stride = bit_stride;
+    f.sh = (uint32_t)(k & 31);
+    f.mask = 1u;
+  } else if (c >= nbyte) {
+    const int32_t k = c - nbyte;
+    f.base = nibs + 4 * (k >> 3);
+    f.stride = nib_stride;
+    f.sh = 4u * (uint32_t)(k & 7);
+    f.mask = 15u;
+  } else {
+    const int32_t b = c / block_features;
+    const int32_t j = c - b * block_features;
+    f.base = bins + int64_t(b) * row_capacity * block_stride + (j & ~3);
+    f.stride = block_stride;
+    f.sh = 8u * (uint32_t)(j & 3);
+    f.mask = 0xffu;
+  }
+  return f;
+}
+
+__device__ __forceinline__ uint32_t filter_dword(const RowFilter& f, int64_t row) {
+  return *reinterpret_cast<const uint32_t*>(f.base + row * f.stride);
+}
+
+__device__ __forceinline__ bool filter_keep(const RowFilter& f, uint32_t dw) {
+  return ((int32_t)((dw >> f.sh) & f.mask) <= f.thr) == f.left;
+}
+
 // Histogram of a tile's bit features (the bit block), with 2 LDS slots per
 // bit feature k (its bins 0 and 1).  Per feature the rarer value is
 // accumulated -- the skip bin, 0 when none is set, is the frequent one -- by
@@ -557,8 +628,9 @@ inline int load_unit_for(int32_t block_stride) {
 constexpr int kBitStage = 1024;   // bit features whose output table is staged in LDS
 constexpr int kMaxBitWords = 128; // words per row of the bit block, at most
 
-template <int NW, bool Q32>
-__device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* __restrict__ bins,
+template <int NW, bool Q32, bool FILT>
+__device__ void hist_bit_block(const TileDesc& td, const RowFilter& flt, int32_t tile,
+                               const uint8_t* __restrict__ bins,
                                int64_t row_capacity, int32_t n_blocks, int32_t block_stride,
                                int32_t n_features, int32_t n_bit, int32_t bit_stride,
                                const int32_t* __restrict__ col_feature, const void* __restrict__ q,
@@ -606,7 +678,7 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
   constexpr int BATCH = 4;
   if (rg < rpi) {
     for (int64_t r = r0 + rg; r < r1; r += int64_t(BATCH) * rpi) {
-      uint32_t x[BATCH];
+      uint32_t x[BATCH], fx[BATCH];
       int64_t qq[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
@@ -614,11 +686,13 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
         const bool ok = rr < r1;
         x[u] = ok ? wb[rr * nwords + w] : 0u;
         qq[u] = ok ? q_at<Q32>(q, rr) : 0;
+        if (FILT) fx[u] = ok ? filter_dword(flt, rr) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         const int64_t rr = r + int64_t(u) * rpi;
         if (rr >= r1) continue;
+        if (FILT && !filter_keep(flt, fx[u])) continue;
         const uint64_t pk = ((uint64_t)qq[u] << bits) + 1ull;
         tot += pk;
         uint32_t m = (x[u] ^ inv) & valid;
@@ -677,8 +751,9 @@ __device__ void hist_bit_block(const TileDesc& td, int32_t tile, const uint8_t* 
 // different features fall in different bank pairs, and each lane walks its 8
 // nibbles starting at nibble (row group & 7), so the lanes of a quarter-wave
 // address several features at once.
-template <int NW, bool Q32>
-__device__ void hist_nib_block(const TileDesc& td, int32_t tile, const uint8_t* __restrict__ bins,
+template <int NW, bool Q32, bool FILT>
+__device__ void hist_nib_block(const TileDesc& td, const RowFilter& flt, int32_t tile,
+                               const uint8_t* __restrict__ bins,
                                int64_t row_capacity, int32_t n_blocks, int32_t block_stride,
                                int32_t n_features, int32_t n_bit, int32_t bit_stride, int32_t n_nib,
                                int32_t nib_stride, const int32_t* __restrict__ col_feature,
@@ -733,7 +808,7 @@ __device__ void hist_nib_block(const TileDesc& td, int32_t tile, const uint8_t* 
   constexpr int BATCH = 4;
   if (rg < rpi) {
     for (int64_t r = r0 + rg; r < r1; r += int64_t(BATCH) * rpi) {
-      uint32_t x[BATCH];
+      uint32_t x[BATCH], fx[BATCH];
       int64_t qq[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
@@ -741,11 +816,13 @@ __device__ void hist_nib_block(const TileDesc& td, int32_t tile, const uint8_t* 
         const bool ok = rr < r1;
         x[u] = ok ? wb[rr * nwords + w] : 0u;
         qq[u] = ok ? q_at<Q32>(q, rr) : 0;
+        if (FILT) fx[u] = ok ? filter_dword(flt, rr) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         const int64_t rr = r + int64_t(u) * rpi;
         if (rr >= r1) continue;
+        if (FILT && !filter_keep(flt, fx[u])) continue;
         const uint64_t pk = ((uint64_t)qq[u] << bits) + 1ull;
         tot += pk;
         const uint32_t diff = x[u] ^ skw;
@@ -832,7 +909,7 @@ __device__ void hist_nib_block(const TileDesc& td, int32_t tile, const uint8_t* 
 // (global bin order) for k_hist_reduce.  NARROW: 0 byte blocks only; 1 a bit
 // block too; 2 a nibble block (and maybe a bit block) too -- each variant
 // carries only the code its layout needs.
-template <int D, int NARROW, bool Q32, bool IDS = false>
+template <int D, int NARROW, bool Q32, bool IDS = false, bool FILT = false>
 __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_hist(
     const uint8_t* __restrict__ bins, int64_t row_capacity, int32_t n_blocks,
     int32_t block_features, int32_t block_stride, int32_t n_features, int32_t n_bit,
@@ -845,6 +922,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     int32_t id_row_pitch, int32_t id_tiles) {
   static_assert(D == 1 || D == 2 || D == 4 || D == 8, "lanes per row");
   static_assert(!IDS || NARROW == 0, "index mode reads byte blocks only");
+  static_assert(!(IDS && FILT), "filtered tiles read rows in order");
   if (failed(guard)) return;
   constexpr int RPW = 64 / D;               // rows per wave per batch
   constexpr int RPI = kHistThreads / D;     // rows per workgroup per batch
@@ -876,6 +954,14 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     if (tile >= id_tiles) return;
   }
   const TileDesc td = desc[tile];
+  // FILT: every tile of the plan is filtered (a plan either filters all its
+  // tiles or none)
+  RowFilter flt{};
+  if constexpr (FILT) {
+    if (td.node >= 0)
+      flt = row_filter(td, bins, row_capacity, n_blocks, block_features, block_stride, n_features,
+                       n_bit, bit_stride, n_nib, nib_stride, blk == 0 ? ctrl : nullptr);
+  }
   if (NARROW > 0 && blk >= n_blocks) {  // the narrow blocks: bits, then nibbles
     if (td.node < 0) return;
     if (blk == n_blocks && n_bit > 0) {
@@ -883,12 +969,12 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
         if (threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_SHAPE);
         return;
       }
-      hist_bit_block<NW, Q32>(td, td.slot, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
+      hist_bit_block<NW, Q32, FILT>(td, flt, td.slot, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
                          bit_stride, col_feature, q, bin_offset, skip_bin, total_bins, lds_bins, bits,
                          hist_g, hist_cnt, partial, ctrl, lds, s_inv, s_bit, sh_tot);
     } else if constexpr (NARROW == 2) {
       if (blk == n_blocks + (n_bit > 0 ? 1 : 0) && n_nib > 0)
-        hist_nib_block<NW, Q32>(td, td.slot, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
+        hist_nib_block<NW, Q32, FILT>(td, flt, td.slot, bins, row_capacity, n_blocks, block_stride, n_features, n_bit,
                            bit_stride, n_nib, nib_stride, col_feature, q, bin_offset, skip_bin,
                            total_bins, lds_bins, bits, hist_g, hist_cnt, partial, ctrl, lds, s_inv,
                            sh_tot);
@@ -1000,6 +1086,7 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     using QT = typename std::conditional<Q32, int32_t, int64_t>::type;
     uint32_t xs[NS][H];
     QT qs[NS][NQ];
+    uint32_t fs[NS][NQ];  // FILT: the split dwords of the rows whose q the lane loads
     // Rows past the tile end are clamped to its last row and added like any
     // other row; the exact correction after the loop subtracts those copies
     // (packed sums are exact mod 2^64), so the loop needs no masks.  Lanes
@@ -1007,25 +1094,34 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     // which are never read.  The empty asm takes the loaded values as
     // operands where they are used, so the compiler can neither drop a load
     // nor wait for it early.
-    auto load_half = [&](int32_t first, uint32_t* x, QT* qq) {
+    auto load_half = [&](int32_t first, uint32_t* x, QT* qq, uint32_t* ff) {
 #pragma unroll
       for (int u = 0; u < H; ++u) {
         const int32_t rr = first + u * RPW + (lane / D);
         const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
         x[u] = row_dword_at(rc);
-        if (D == 1) qq[u < NQ ? u : 0] = *reinterpret_cast<const QT*>(tq + (rc << QSH));
+        if (D == 1) {
+          qq[u < NQ ? u : 0] = *reinterpret_cast<const QT*>(tq + (rc << QSH));
+          if (FILT) ff[u < NQ ? u : 0] = filter_dword(flt, r0 + rc);
+        }
       }
       if (D >= 2) {
         const int32_t rr = first + (c % H) * RPW + (lane / D);
         const uint32_t rc = (uint32_t)(rr < lr ? rr : lr);
         qq[0] = *reinterpret_cast<const QT*>(tq + (rc << QSH));
+        if (FILT) ff[0] = filter_dword(flt, r0 + rc);
       }
     };
-    auto add_half = [&](uint32_t* x, QT* qq) {
+    // (FILT: a row the filter drops adds the packed value 0)
+    auto add_half = [&](uint32_t* x, QT* qq, uint32_t* ff) {
       uint64_t pkh = 0ull;
       if (D >= 2) {
         asm volatile("" : "+v"(qq[0]));
         pkh = ((uint64_t)(int64_t)qq[0] << bits) | 1ull;
+        if (FILT) {
+          asm volatile("" : "+v"(ff[0]));
+          if (!filter_keep(flt, ff[0])) pkh = 0ull;
+        }
       }
 #pragma unroll
       for (int u = 0; u < H; ++u) {
@@ -1036,6 +1132,10 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
         } else {
           asm volatile("" : "+v"(x[u]), "+v"(qq[u < NQ ? u : 0]));
           pk = ((uint64_t)(int64_t)qq[u < NQ ? u : 0] << bits) | 1ull;
+          if (FILT) {
+            asm volatile("" : "+v"(ff[u < NQ ? u : 0]));
+            if (!filter_keep(flt, ff[u < NQ ? u : 0])) pk = 0ull;
+          }
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -1051,13 +1151,14 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     // previous iteration, and stage 0 waits only for its own loads.
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      load_half(base + st * SROWS, xs[st], qs[st]);
+      load_half(base + st * SROWS, xs[st], qs[st], fs[st]);
       asm volatile("" ::: "memory");
     }
     // the tile's last row, for the correction below, loaded with the first
     // rows so that no round trip follows the loop
     uint32_t x_last = row_dword_at((uint32_t)lr);
     QT q_last = *reinterpret_cast<const QT*>(tq + (uint32_t(lr) << QSH));
+    uint32_t f_last = FILT ? filter_dword(flt, r0 + lr) : 0u;
     // The wave needs `todo` stages (wave-uniform).  Each loop iteration
     // adds NS stages and reloads each NS stages ahead, unconditionally; the
     // last 1..NS stages are added after the loop from the buffers already
@@ -1068,16 +1169,16 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     while (todo > NS) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        add_half(xs[st], qs[st]);
-        load_half(base + (st + NS) * SROWS, xs[st], qs[st]);
+        add_half(xs[st], qs[st], fs[st]);
+        load_half(base + (st + NS) * SROWS, xs[st], qs[st], fs[st]);
       }
       base += NS * SROWS;
       todo -= NS;
     }
 #pragma unroll
     for (int st = 0; st < NS; ++st)
-      if (st < todo) add_half(xs[st], qs[st]);
-    asm volatile("" : "+v"(x_last), "+v"(q_last));
+      if (st < todo) add_half(xs[st], qs[st], fs[st]);
+    asm volatile("" : "+v"(x_last), "+v"(q_last), "+v"(f_last));
     // the lane visited rows first_row + u RPW + s SROWS, u < H, s < stages;
     // those at or past nt were row lr
     int32_t valid = 0;
@@ -1090,7 +1191,8 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
     if (extra > 0) {
       const uint32_t x = x_last;
       const int64_t qq = (int64_t)q_last;
-      const uint64_t pk = (((uint64_t)qq << bits) | 1ull) * (0ull - (uint64_t)extra);
+      const uint64_t one = (FILT && !filter_keep(flt, f_last)) ? 0ull : (((uint64_t)qq << bits) | 1ull);
+      const uint64_t pk = one * (0ull - (uint64_t)extra);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const uint32_t a = __builtin_amdgcn_perm(x, offs, sel[m]);
@@ -2713,15 +2815,24 @@ int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst) {
   return GBDT_OK;
 }
 
-template <int N, bool Q>
+template <int N, bool Q, bool F>
 static auto hist_kernel(int D) -> decltype(&k_hist<8, N, Q>) {
-  return D == 8 ? k_hist<8, N, Q> : D == 4 ? k_hist<4, N, Q> : D == 2 ? k_hist<2, N, Q> : k_hist<1, N, Q>;
+  return D == 8   ? k_hist<8, N, Q, false, F>
+         : D == 4 ? k_hist<4, N, Q, false, F>
+         : D == 2 ? k_hist<2, N, Q, false, F>
+                  : k_hist<1, N, Q, false, F>;
+}
+
+template <int N>
+static auto hist_kernel_q(int D, bool q32, bool filt) -> decltype(&k_hist<8, N, true>) {
+  return filt ? (q32 ? hist_kernel<N, true, true>(D) : hist_kernel<N, false, true>(D))
+              : (q32 ? hist_kernel<N, true, false>(D) : hist_kernel<N, false, false>(D));
 }
 
 int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* desc,
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
                 WsCtrl* ctrl, hipStream_t s, bool q32, bool guard, bool ids,
-                const uint8_t* rows_ix) {
+                const uint8_t* rows_ix, bool filt) {
   const int64_t n_rows = src.X.n_rows > 0 ? src.X.n_rows : 1;
   const int32_t bits = pack_bits_for(n_rows);
   const bool has_bytes = src.X.n_features > src.X.n_bit_features + src.X.n_nib_features;
@@ -2738,10 +2849,11 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
   // 17 columns, 5 dwords, wide, so D = 8)
   if (ids && (narrow != 0 || src.rid == nullptr || D != 8))
     return fail(GBDT_E_INTERNAL, "index mode needs byte blocks of 5 to 8 dwords and row ids");
+  if (ids && filt) return fail(GBDT_E_INTERNAL, "filtered histogram tiles read rows in order");
   auto kern = ids ? (q32 ? k_hist<8, 0, true, true> : k_hist<8, 0, false, true>)
-              : narrow == 2 ? (q32 ? hist_kernel<2, true>(D) : hist_kernel<2, false>(D))
-              : narrow == 1 ? (q32 ? hist_kernel<1, true>(D) : hist_kernel<1, false>(D))
-                            : (q32 ? hist_kernel<0, true>(D) : hist_kernel<0, false>(D));
+              : narrow == 2 ? hist_kernel_q<2>(D, q32, filt)
+              : narrow == 1 ? hist_kernel_q<1>(D, q32, filt)
+                            : hist_kernel_q<0>(D, q32, filt);
   (void)has_bits;
   const unsigned gy = (unsigned)(src.X.n_blocks + (src.X.n_bit_features > 0 ? 1 : 0) +
                                  (src.X.n_nib_features > 0 ? 1 : 0));
