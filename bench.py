@@ -54,9 +54,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def built_work(trees, n_features, total_bins, max_depth, min_split):
+def built_work(trees, n_features, total_bins, max_depth, min_split, filter_level=-1):
     """(built rows, built nodes) summed over trees: root plus the smaller child
-    of every split pair whose larger child can still split."""
+    of every split pair whose larger child can still split.  A node of the
+    filter level (gbdt_grow_filter_level) is built from its parent's unmoved
+    rows, so its rows are the parent's."""
     rows = 0
     nodes = 0
     for tr in trees:
@@ -71,7 +73,7 @@ def built_work(trees, n_features, total_bins, max_depth, min_split):
                 continue
             nl, nr = int(L["count"]), int(R["count"])
             if max(nl, nr) >= min_split:
-                rows += min(nl, nr)
+                rows += nl + nr if int(L["depth"]) == filter_level else min(nl, nr)
                 nodes += 1
     return rows, nodes
 
@@ -82,18 +84,19 @@ DIAG_PARTITION = 10
 DIAG_UPDATE = 11
 
 
-def other_rooflines(trees, kt, n, max_depth, workload_name):
+def other_rooflines(trees, kt, n, max_depth, workload_name, filter_level=-1):
     """HBM rooflines of the partition, the prediction update and the split
     search over the same timed trees, with the algorithmic bytes of each step
     (per row of a splitting node: 4 B row index read + 1 B bin + 4 B index
     written + 16 B of q moved; per row of the update: 4 B index + 16 B pred
-    read and written).  The partition runs at levels 0 .. max_depth - 2; the
-    update is two launches per tree (the tree compaction, then the row walk),
-    counted as one unit."""
+    read and written).  The partition runs at levels 0 .. max_depth - 2, but
+    not at the level before a filter level; the update is two launches per
+    tree (the tree compaction, then the row walk), counted as one unit."""
+    last_part = max_depth - 2 if filter_level < 0 else filter_level - 2
     part_rows = 0
     for tr in trees:
         for nd in tr:
-            if int(nd["depth"]) < max_depth - 1 and not (nd["flags"] & 1):
+            if int(nd["depth"]) <= last_part and not (nd["flags"] & 1):
                 part_rows += int(nd["count"])
     out = {}
     K = len(trees)
@@ -253,6 +256,7 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
                               "bit_features": int(ds.X.n_bit_features),
                               "nibble_features": int(ds.X.n_nib_features),
                               "partition_moves": "row ids" if bst.moves_ids else "rows",
+                              "filter_level": bst.filter_level,
                               "gather_copies": (["rows interleaved", "column-major"]
                                                 if bst.rows_ix is not None else [])}},
         "trees_per_s": K / wall,
@@ -276,7 +280,7 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
         bst.check()
         kinds, ms = kinds[: cnt.value], ms[: cnt.value]
         trees = [g.nodes_to_host(nodes_bufs[i], int(nn_bufs[i].item())) for i in range(K)]
-        rows, nbuilt = built_work(trees, F, TB, params.max_depth, min_split)
+        rows, nbuilt = built_work(trees, F, TB, params.max_depth, min_split, bst.filter_level)
         kt = {kk: (float(ms[kinds == kk].sum()), int((kinds == kk).sum())) for kk in set(kinds.tolist())}
         hist_ms, launches = kt.get(DIAG_HIST, (0.0, 0))
         red_ms, red_launches = kt.get(DIAG_HIST_REDUCE, (0.0, 0))
@@ -296,7 +300,7 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
                            "k_hist_reduce_avg_us": 1000.0 * red_ms / max(red_launches, 1),
                            "k_hist_reduce_launches": red_launches,
                            "k_hist_only_frac": alg_bytes / (hist_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        out["rooflines"] = other_rooflines(trees, kt, n, params.max_depth, wl["name"])
+        out["rooflines"] = other_rooflines(trees, kt, n, params.max_depth, wl["name"], bst.filter_level)
         names = {1: "grad_max", 2: "grad_q", 3: "plan", 4: "hist", 5: "hist_reduce", 6: "subtract",
                  7: "find", 8: "tree_init", 9: "level", 10: "partition", 11: "update", 12: "pack"}
         out["device_ms_per_tree"] = {names.get(int(kk), str(kk)): kt[kk][0] / K for kk in sorted(kt)}

@@ -479,6 +479,11 @@ int gbdt_grow_moves_ids(const gbdt_matrix* X, int32_t objective) {
   return grow_moves_ids(*X, objective == GBDT_OBJECTIVE_LOGISTIC) ? 1 : 0;
 }
 
+int gbdt_grow_filter_level(const gbdt_matrix* X, const gbdt_params* p) {
+  if (!X || !p) return -1;
+  return grow_filter_level(grow_moves_ids(*X, p->objective == GBDT_OBJECTIVE_LOGISTIC), p->max_depth);
+}
+
 int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* label, double* pred,
                    const gbdt_params* p, gbdt_node* nodes_out, int32_t* n_nodes_dev,
                    const gbdt_grow_buffers* b, void* stream) {
@@ -567,7 +572,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   // That trades one full row move for reading the larger children's rows
   // once.  Row-moving mode only (index mode would gather them), and only
   // while the level-(D - 2) nodes fit one planning pass (D <= 12).
-  const int32_t filt_level = (!ids && D >= 2 && D <= 12) ? D - 2 : -1;
+  // filt_level: the level whose k_level plans the filtered histograms.
+  const int32_t filt_level = grow_filter_level(ids, D) - 1;
   for (int32_t d = 0; d <= D; ++d) {
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
     const int64_t rows_build = (d == 0 || (filt_level >= 0 && d == filt_level + 1)) ? n : n / 2;

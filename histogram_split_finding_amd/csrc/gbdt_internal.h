@@ -206,6 +206,14 @@ bool same_layout(const gbdt_matrix& a, const gbdt_matrix& b);
 int check_matrix(const gbdt_matrix& X);
 int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft);
 int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
+// The level whose histograms the tree driver builds from the parents'
+// unpartitioned rows (filtered tiles; the partition of the level before it
+// is skipped), or -1: the last level, in row-moving mode, for depths 2 to 12
+// (the parents then fit one planning pass of the level kernel).
+inline int32_t grow_filter_level(bool moves_ids, int32_t max_depth) {
+  return (!moves_ids && max_depth >= 2 && max_depth <= 12) ? max_depth - 1 : -1;
+}
+
 // Row pitch in bytes of index mode's row-interleaved copy: the row's
 // n_blocks * block_stride bytes rounded up to a power of two up to 128 (so no
 // row straddles a 128-byte cache line), else to a multiple of 128.

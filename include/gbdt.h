@@ -580,6 +580,18 @@ typedef struct gbdt_grow_buffers {
 int gbdt_grow_moves_ids(const gbdt_matrix* X /* host */, int32_t objective);
 
 /*
+ * The level of gbdt_grow_tree whose histograms are built from the parents'
+ * unpartitioned rows, or -1.  In row-moving mode (gbdt_grow_moves_ids 0)
+ * with 2 <= max_depth <= 12 it is the last level, max_depth - 1: the
+ * partition of level max_depth - 2 is skipped, and each histogram tile of
+ * the last level reads its parent's segment and adds only the rows that go
+ * to the child it builds (bin <= threshold_bin for a left child; "Module
+ * Design: Training Core", section 6, steps 3 and 5).  The histograms are
+ * the same; only the work differs.  Host only; no error codes.
+ */
+int gbdt_grow_filter_level(const gbdt_matrix* X /* host */, const gbdt_params* p /* host */);
+
+/*
  * X's byte blocks interleaved row by row: row r's block b (block_stride
  * bytes) at out + r * P + b * block_stride, for r < row_capacity, where
  * P = gbdt_interleave_pitch(X); the P - n_blocks * block_stride bytes after

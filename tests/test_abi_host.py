@@ -212,3 +212,20 @@ def test_index_mode_rule(nbins, bits, nibbles, objective, want):
     ft = g.FeatureTable(nbins, "cpu", pack_bits=bits, pack_nibbles=nibbles)
     X = g.RowBuffer(ft, 10, "cpu", with_rid=False, with_bins=False).matrix()
     assert g.load().gbdt_grow_moves_ids(ctypes.byref(X), objective) == want
+
+
+@pytest.mark.parametrize("nbins,objective,depth,want", [
+    ([256] * 28, 0, 12, 11),    # one byte block, row-moving: the last level is filtered
+    ([256] * 28, 0, 2, 1),
+    ([256] * 28, 0, 1, -1),     # no level before the last one to skip
+    ([256] * 28, 0, 13, -1),    # more parents than one planning pass
+    ([256] * 100, 0, 8, -1),    # index mode moves ids: no filter
+    ([256] * 100, 1, 8, 7),     # the logistic objective moves rows
+])
+def test_filter_level_rule(nbins, objective, depth, want):
+    """gbdt_grow_filter_level: the last level of a row-moving tree of depth 2
+    to 12 builds its histograms from the parents' unmoved rows."""
+    ft = g.FeatureTable(nbins, "cpu", pack_bits=False, pack_nibbles=False)
+    X = g.RowBuffer(ft, 10, "cpu", with_rid=False, with_bins=False).matrix()
+    p = g.make_params(max_depth=depth, objective=objective)
+    assert g.load().gbdt_grow_filter_level(ctypes.byref(X), ctypes.byref(p)) == want
