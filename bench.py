@@ -11,14 +11,17 @@ equal-width bins, 44 binary features with ~5% ones; integer label 1..7),
 depth 10, 100 trees, lambda 1 -- the covtype-shaped depth-10 configuration.
 
 Output: one JSON line on stdout (progress goes to stderr).
-  value      histogram rows*features per second: rows*features of every
-             directly built node (root and smaller children) divided by the
-             summed device time of the histogram build (k_hist and the
+  value      histogram rows*features per second: rows*features the
+             histogram build visits -- every directly built node's rows (root
+             and smaller children; at the filter level, gbdt_grow_filter_level,
+             the parent's rows, which its tiles read and test) -- divided by
+             the summed device time of the histogram build (k_hist and the
              reduction of multi-tile partials, k_hist_reduce) over the timed
-             trees
+             trees; value_built_rows_only credits the built nodes' own rows
+             only
   roofline   the histogram build against the 8 TB/s HBM peak, algorithmic
-             bytes n_v*(F + 4 + 8) + total_bins*12 per built node; k_hist
-             alone is reported beside it
+             bytes n_v*(F + 4 + 8) + total_bins*12 per built node, n_v the
+             rows visited as above; k_hist alone is reported beside it
   rooflines  the partition and the prediction update on the same trees
   trees_per_s / ms_per_step  whole boosting steps, host wall clock
   cpu_baseline  the CPU oracle (single thread) on a bounded sample of trees
@@ -217,7 +220,11 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
         torch.cuda.synchronize()
         W += 1
     bst.check()
-    log("warmup done (%d trees)" % W)
+    # back to the starting predictions, so the timed trees are the workload's
+    # boosting rounds 1 .. K (the warm-up only settles clocks and caches)
+    bst.pred.fill_(0.0)
+    torch.cuda.synchronize()
+    log("warmup done (%d trees; predictions reset)" % W)
 
     nodes_bufs = [torch.zeros(bst.sizes.max_nodes * g.NODE_DTYPE.itemsize, dtype=torch.uint8,
                               device="cuda") for _ in range(K)]
@@ -263,7 +270,10 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
     }
 
     if diag:
-        # second pass: per-kernel device time with events on the library's stream
+        # second pass over the same rounds 1 .. K (predictions reset again):
+        # per-kernel device time with events on the library's stream
+        bst.pred.fill_(0.0)
+        torch.cuda.synchronize()
         lib = g.load()
         cap = 64 * (params.max_depth + 4) * K + 64
         assert lib.gbdt_diag_enable(cap) == 0
@@ -281,6 +291,7 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
         kinds, ms = kinds[: cnt.value], ms[: cnt.value]
         trees = [g.nodes_to_host(nodes_bufs[i], int(nn_bufs[i].item())) for i in range(K)]
         rows, nbuilt = built_work(trees, F, TB, params.max_depth, min_split, bst.filter_level)
+        rows_built_only, _ = built_work(trees, F, TB, params.max_depth, min_split)
         kt = {kk: (float(ms[kinds == kk].sum()), int((kinds == kk).sum())) for kk in set(kinds.tolist())}
         hist_ms, launches = kt.get(DIAG_HIST, (0.0, 0))
         red_ms, red_launches = kt.get(DIAG_HIST_REDUCE, (0.0, 0))
@@ -291,6 +302,9 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
         # the histogram build: k_hist plus the reduction of the partials of
         # nodes covered by several tiles (part of every such node's histogram)
         out["value"] = cells / (build_ms * 1e-3)
+        # the same time, crediting only the rows of the nodes built (the
+        # filter level's smaller children, not the parents' rows its tiles read)
+        out["value_built_rows_only"] = rows_built_only * F / (build_ms * 1e-3)
         out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(wl["name"]),
                            "kernel": "k_hist + k_hist_reduce", "launches": launches,
@@ -305,6 +319,7 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
                  7: "find", 8: "tree_init", 9: "level", 10: "partition", 11: "update", 12: "pack"}
         out["device_ms_per_tree"] = {names.get(int(kk), str(kk)): kt[kk][0] / K for kk in sorted(kt)}
         out["built_rows_per_tree"] = rows / K
+        out["built_rows_only_per_tree"] = rows_built_only / K
         log("histogram build: %d launches, %.3f ms total (k_hist %.3f + reduce %.3f), %.1f GB/s "
             "algorithmic (%.1f%% of 8 TB/s)" % (launches, build_ms, hist_ms, red_ms, achieved,
                                                 100 * achieved / HBM_PEAK_GBS))
@@ -377,7 +392,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed trees (default: the workload's tree count)")
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed trees before the timed ones (default: at least 2 trees and "
+                         "half a second, so the GPU's clocks have settled; the JSON reports the count)")
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--also", type=int, nargs="*", default=[4, 5],
                     help="further workloads reported under 'also' (default: the 10M x 100 and "
@@ -418,13 +435,17 @@ def main():
     for idx, k in enumerate([args.workload] + [w for w in args.also if w != args.workload]):
         wl = dict(datagen.WORKLOADS[k])
         # the further workloads time their whole tree count after a warm-up
-        # of at least half a second (their first trees run at lower clocks)
+        # of at least half a second (the first trees run at lower clocks), and
+        # so does the primary one unless --warmup fixes its count
         K = (args.steps if args.steps is not None else wl["n_trees"]) if idx == 0 else wl["n_trees"]
-        res = measure(g, datagen, torch, k, K, args.warmup, not args.no_diag, 0.0 if idx == 0 else 0.5)
+        W = args.warmup if args.warmup is not None else 2
+        warm_s = 0.0 if (idx == 0 and args.warmup is not None) else 0.5
+        res = measure(g, datagen, torch, k, K, W, not args.no_diag, warm_s)
         if idx == 0:
             out = res
         else:
-            secondary.append({key: res[key] for key in ("config", "value", "unit", "steps", "warmup",
+            secondary.append({key: res[key] for key in ("config", "value", "value_built_rows_only", "unit",
+                                                        "steps", "warmup",
                                                         "ms_per_step",
                                                         "trees_per_s", "roofline", "rooflines",
                                                         "device_ms_per_tree")
