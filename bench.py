@@ -13,7 +13,7 @@ depth 10, 100 trees, lambda 1 -- the covtype-shaped depth-10 configuration.
 Output: one JSON line on stdout (progress goes to stderr).
   value      histogram rows*features per second: rows*features the
              histogram build visits -- every directly built node's rows (root
-             and smaller children; at the filter level, gbdt_grow_filter_level,
+             and smaller children; at a filtered level, gbdt_grow_filtered_levels,
              the parent's rows, which its tiles read and test) -- divided by
              the summed device time of the histogram build (k_hist and the
              reduction of multi-tile partials, k_hist_reduce) over the timed
@@ -57,11 +57,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def built_work(trees, n_features, total_bins, max_depth, min_split, filter_level=-1):
+def built_work(trees, n_features, total_bins, max_depth, min_split, filtered=0):
     """(built rows, built nodes) summed over trees: root plus the smaller child
-    of every split pair whose larger child can still split.  A node of the
-    filter level (gbdt_grow_filter_level) is built from its parent's unmoved
-    rows, so its rows are the parent's."""
+    of every split pair whose larger child can still split.  A node of a
+    filtered level (bit d of gbdt_grow_filtered_levels) is built from its
+    parent's unmoved rows, so its rows are the parent's."""
     rows = 0
     nodes = 0
     for tr in trees:
@@ -76,7 +76,7 @@ def built_work(trees, n_features, total_bins, max_depth, min_split, filter_level
                 continue
             nl, nr = int(L["count"]), int(R["count"])
             if max(nl, nr) >= min_split:
-                rows += nl + nr if int(L["depth"]) == filter_level else min(nl, nr)
+                rows += nl + nr if (filtered >> int(L["depth"])) & 1 else min(nl, nr)
                 nodes += 1
     return rows, nodes
 
@@ -87,20 +87,32 @@ DIAG_PARTITION = 10
 DIAG_UPDATE = 11
 
 
-def other_rooflines(trees, kt, n, max_depth, workload_name, filter_level=-1):
+def other_rooflines(trees, kt, n, max_depth, workload_name, filtered=0):
     """HBM rooflines of the partition, the prediction update and the split
     search over the same timed trees, with the algorithmic bytes of each step
     (per row of a splitting node: 4 B row index read + 1 B bin + 4 B index
     written + 16 B of q moved; per row of the update: 4 B index + 16 B pred
-    read and written).  The partition runs at levels 0 .. max_depth - 2, but
-    not at the level before a filter level; the update is two launches per
-    tree (the tree compaction, then the row walk), counted as one unit."""
-    last_part = max_depth - 2 if filter_level < 0 else filter_level - 2
+    read and written).  Without filtered levels the partition runs after
+    levels 0 .. max_depth - 2 over the splitting nodes' rows; with them
+    (gbdt_grow_filtered_levels: the odd levels) one two-level partition
+    follows each odd level d < max_depth - 1 and moves the rows of every
+    level-(d - 1) node that split into a child that splits, counted here as
+    one pass (25 B per row), although it advances the rows two levels.  The
+    update is two launches per tree (the tree compaction, then the row
+    walk), counted as one unit."""
     part_rows = 0
     for tr in trees:
         for nd in tr:
-            if int(nd["depth"]) <= last_part and not (nd["flags"] & 1):
-                part_rows += int(nd["count"])
+            if nd["flags"] & 1:
+                continue
+            dep = int(nd["depth"])
+            if not filtered:
+                if dep <= max_depth - 2:
+                    part_rows += int(nd["count"])
+            elif dep % 2 == 0 and dep + 2 < max_depth:
+                kids = (tr[int(nd["left"])], tr[int(nd["right"])])
+                if any(not (k["flags"] & 1) for k in kids):
+                    part_rows += int(nd["count"])
     out = {}
     K = len(trees)
 
@@ -263,7 +275,8 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
                               "bit_features": int(ds.X.n_bit_features),
                               "nibble_features": int(ds.X.n_nib_features),
                               "partition_moves": "row ids" if bst.moves_ids else "rows",
-                              "filter_level": bst.filter_level,
+                              "filtered_levels": [d for d in range(params.max_depth)
+                                                  if (bst.filtered_levels >> d) & 1],
                               "gather_copies": (["rows interleaved", "column-major"]
                                                 if bst.rows_ix is not None else [])}},
         "trees_per_s": K / wall,
@@ -290,7 +303,7 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
         bst.check()
         kinds, ms = kinds[: cnt.value], ms[: cnt.value]
         trees = [g.nodes_to_host(nodes_bufs[i], int(nn_bufs[i].item())) for i in range(K)]
-        rows, nbuilt = built_work(trees, F, TB, params.max_depth, min_split, bst.filter_level)
+        rows, nbuilt = built_work(trees, F, TB, params.max_depth, min_split, bst.filtered_levels)
         rows_built_only, _ = built_work(trees, F, TB, params.max_depth, min_split)
         kt = {kk: (float(ms[kinds == kk].sum()), int((kinds == kk).sum())) for kk in set(kinds.tolist())}
         hist_ms, launches = kt.get(DIAG_HIST, (0.0, 0))
@@ -303,7 +316,7 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
         # nodes covered by several tiles (part of every such node's histogram)
         out["value"] = cells / (build_ms * 1e-3)
         # the same time, crediting only the rows of the nodes built (the
-        # filter level's smaller children, not the parents' rows its tiles read)
+        # filtered levels' smaller children, not the parents' rows their tiles read)
         out["value_built_rows_only"] = rows_built_only * F / (build_ms * 1e-3)
         out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(wl["name"]),
@@ -314,7 +327,7 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
                            "k_hist_reduce_avg_us": 1000.0 * red_ms / max(red_launches, 1),
                            "k_hist_reduce_launches": red_launches,
                            "k_hist_only_frac": alg_bytes / (hist_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        out["rooflines"] = other_rooflines(trees, kt, n, params.max_depth, wl["name"], bst.filter_level)
+        out["rooflines"] = other_rooflines(trees, kt, n, params.max_depth, wl["name"], bst.filtered_levels)
         names = {1: "grad_max", 2: "grad_q", 3: "plan", 4: "hist", 5: "hist_reduce", 6: "subtract",
                  7: "find", 8: "tree_init", 9: "level", 10: "partition", 11: "update", 12: "pack"}
         out["device_ms_per_tree"] = {names.get(int(kk), str(kk)): kt[kk][0] / K for kk in sorted(kt)}

@@ -131,7 +131,7 @@ def load():
                                                 ctypes.c_double, vp, vp, vp]),
         "gbdt_grow_sizes": (ctypes.c_int, [i64, i32, i32, P(GrowSizes)]),
         "gbdt_grow_moves_ids": (ctypes.c_int, [P(Matrix), i32]),
-        "gbdt_grow_filter_level": (ctypes.c_int, [P(Matrix), P(Params)]),
+        "gbdt_grow_filtered_levels": (i64, [P(Matrix), P(Params)]),
         "gbdt_interleave_rows": (ctypes.c_int, [P(Matrix), vp, vp]),
         "gbdt_interleave_pitch": (i32, [P(Matrix)]),
         "gbdt_column_major": (ctypes.c_int, [P(Matrix), vp, vp]),
@@ -501,8 +501,8 @@ class Booster:
         # and q (and, for the logistic objective, its Hessians in the rid arrays)
         X0 = ds.X.matrix()
         self.moves_ids = bool(load().gbdt_grow_moves_ids(ctypes.byref(X0), int(params.objective)))
-        # the level whose histograms are built from the parents' unmoved rows (-1: none)
-        self.filter_level = int(load().gbdt_grow_filter_level(ctypes.byref(X0), ctypes.byref(params)))
+        # the levels whose histograms are built from the parents' unmoved rows (bit d: level d)
+        self.filtered_levels = int(load().gbdt_grow_filtered_levels(ctypes.byref(X0), ctypes.byref(params)))
         self.pp = [RowBuffer(ds.ft, n, device, with_rid=logistic or self.moves_ids,
                              with_bins=not self.moves_ids) for _ in range(2)]
         self.rows_ix = self.cols = None

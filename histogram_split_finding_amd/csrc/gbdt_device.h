@@ -112,23 +112,22 @@ __device__ __forceinline__ int32_t clamp_len(const int32_t* len, int32_t cap) {
 
 constexpr int kPlanLdsEntries = 8192;  // list entries whose tile prefix is kept in LDS
 constexpr int kPlanStage = 2048;       // list entries whose node data is kept in LDS
-
-// One list entry as the planner needs it (node, its segment, its split).
-struct PlanEntry {
-  int32_t node, begin, count, feature, threshold_bin, n_left;
-};
+constexpr int kPlanStage4 = 512;       // entries of a two-level partition plan (grandparents)
 
 constexpr int kPlanSizeBuckets = 64;  // size classes of the histogram tiles' largest-first order
 constexpr int kPlanSortMinTiles = 768;  // smaller histogram plans (about one round) keep node order
 
 // LDS of the planner: sh [32], spre [kPlanLdsEntries + 1], stage
-// [kPlanStage], and the size-class counters of the largest-first order.
+// [kPlanStage], the size-class counters of the largest-first order, and the
+// children's splits of a two-level partition plan's entries (split2, n2,
+// split3, n3 of the tile descriptor).
 struct PlanLds {
   int32_t sh[32];
   int32_t n_multi;
   int32_t spre[kPlanLdsEntries + 1];
   PlanEntry stage[kPlanStage];
   int32_t bucket[kPlanSizeBuckets];
+  int4 ext[kPlanStage4];
 };
 
 // Size class of a tile of `size` rows (tiles hold at most tile_rows): 0 for
@@ -195,13 +194,16 @@ __device__ __forceinline__ int32_t tiles_of(int32_t c, int32_t tile_rows) {
 // look-back status (status != nullptr) and every tile's descriptor (from LDS
 // only), then descriptors with node -1 up to max_tiles.  with_split: the
 // entries carry a split (partition plans).  *n_multi (LDS) must be 0 and
-// visible, like the staged entries.
+// visible, like the staged entries.  ext (LDS, or nullptr): the children's
+// splits of a two-level partition plan, ext[j] = (split2, n2, split3, n3);
+// status2 then receives cleared look-back words too.
 __device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, int32_t* n_multi,
                                  int32_t n, int32_t tile_rows, int32_t max_tiles,
                                  int32_t* __restrict__ prefix, TileDesc* __restrict__ desc,
                                  uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
                                  bool with_split, int32_t* __restrict__ multi,
-                                 int32_t* bucket /* LDS [kPlanSizeBuckets] or nullptr */) {
+                                 int32_t* bucket /* LDS [kPlanSizeBuckets] or nullptr */,
+                                 const int4* ext = nullptr, uint64_t* __restrict__ status2 = nullptr) {
   const int32_t total = spre[n];
   for (int32_t j = threadIdx.x; j <= n; j += blockDim.x) {
     prefix[j] = spre[j];
@@ -245,8 +247,19 @@ __device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, in
       d.n_left = pe.n_left;
       d.split_valid = with_split && pe.feature >= 0;
       d.slot = t;
+      if (ext != nullptr) {
+        const int4 x = ext[lo];
+        d.split2 = x.x;
+        d.n2 = x.y;
+        d.split3 = x.z;
+        d.n3 = x.w;
+      } else {
+        d.split2 = d.split3 = -1;
+        d.n2 = d.n3 = 0;
+      }
       desc[pos] = d;
       if (status != nullptr) status[t] = 0ull;
+      if (status2 != nullptr) status2[t] = 0ull;
     }
   }
   for (int32_t t = lim + threadIdx.x; t < max_tiles; t += blockDim.x) desc[t].node = -1;
@@ -381,6 +394,8 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
     d.n_left = pe.n_left;
     d.split_valid = splits != nullptr && pe.feature >= 0;
     d.slot = t;
+    d.split2 = d.split3 = -1;
+    d.n2 = d.n3 = 0;
     int32_t pos = t;
     if (by_size) pos = tile_order(L.bucket, tile_size_class(d.r1 - d.r0, tile_rows));
     desc[pos] = d;

@@ -69,6 +69,8 @@ struct PlanArgs {
   int32_t* prefix;   // partition plan
   TileDesc* desc;
   uint64_t* status;
+  uint64_t* status2;   // the second look-back of two-level partition plans
+  PlanEntry* gstage;   // the splitting nodes of the last level that filtered its children
   int32_t* hprefix;  // histogram plan
   int32_t* hmulti;
   TileDesc* hdesc;
@@ -205,9 +207,9 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t hist_max_tiles_next,
                                                 const int32_t* __restrict__ guard,
                                                 const int64_t* __restrict__ split_h,
-                                                int32_t filt_next) {
+                                                int32_t filt_next, int32_t four) {
   __shared__ PlanLds lds;
-  __shared__ int32_t shm[6 * 17];
+  __shared__ int32_t shm[7 * 17];
   // after an error nothing of the level is written, and the partition that
   // follows finds an empty plan (it reads no other sign of the failure: a
   // partition tile that stopped early would stall its successors'
@@ -234,9 +236,33 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   const bool fast = cnt <= (int32_t)blockDim.x;
 
   // counts: splits, pairs, searched children, leaves, partition tiles, rows
-  // the next level builds (the smaller child of each pair)
-  int32_t c[6] = {0, 0, 0, 0, 0, 0};
+  // the next level builds (the smaller child of each pair), two-level
+  // partition entries
+  int32_t c[7] = {0, 0, 0, 0, 0, 0, 0};
   int32_t my_small = -1;  // fast path: the smaller child's rows of this thread's pair
+  // four (two-level partition of the level's grandparents): the thread of
+  // each even position i holds child a = first + i of grandparent i / 2 (b
+  // is a + 1), staged by the previous level's kernel in gstage; the entry
+  // carries both children's splits, and a grandparent neither of whose
+  // children splits moves nothing
+  PlanEntry g4{};
+  int4 x4 = make_int4(-1, 0, -1, 0);
+  bool need4 = false;
+  if (four && fast && i0 < i1 && (i0 & 1) == 0 && i0 + 1 < cnt) {
+    const gbdt_split sa = splits[first + i0];
+    const gbdt_split sb = splits[first + i0 + 1];
+    g4 = pa.gstage[i0 >> 1];
+    const int32_t ca = split_column(sa, pa.feature_col, pa.n_features);
+    const int32_t cb = split_column(sb, pa.feature_col, pa.n_features);
+    need4 = ca >= 0 || cb >= 0;
+    x4 = make_int4(ca >= 0 ? ((ca << 8) | (sa.threshold_bin & 0xff)) : -1, ca >= 0 ? sa.n_left : g4.n_left,
+                   cb >= 0 ? ((cb << 8) | (sb.threshold_bin & 0xff)) : -1,
+                   cb >= 0 ? sb.n_left : g4.count - g4.n_left);
+    if (need4 && !last) {
+      c[6] = 1;
+      c[4] = tiles_of(g4.count, part_tile);
+    }
+  }
   for (int32_t i = i0; i < i1; ++i) {
     const int32_t v = first + i;
     const gbdt_split s = splits[v];
@@ -247,7 +273,7 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
       if (last) {
         c[3] += 2;
       } else {
-        c[4] += tiles_of(count, part_tile);
+        if (!four) c[4] += tiles_of(count, part_tile);
         if ((int64_t)(nl > nr ? nl : nr) >= min_split) {
           ++c[1];
           c[2] += ((int64_t)nl >= min_split) + ((int64_t)nr >= min_split);
@@ -261,8 +287,8 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
       ++c[3];
     }
   }
-  int32_t r[6], t[6];
-  block_exclusive_scan_multi<6>(c, r, t, shm);
+  int32_t r[7], t[7];
+  block_exclusive_scan_multi<7>(c, r, t, shm);
   // histogram tile rows of the next level from the rows it actually builds:
   // about hist_target tiles, none below hist_min_rows (or above the packed
   // cells' limit)
@@ -317,8 +343,13 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
         pe.feature = split_column(s, pa.feature_col, pa.n_features);
         pe.threshold_bin = s.threshold_bin;
         pe.n_left = s.n_left;
-        stP[r_split] = pe;
-        spP[r_split] = r[4];
+        if (!four) {
+          stP[r_split] = pe;
+          spP[r_split] = r[4];
+        }
+        // (the next level filters its children and partitions this level's
+        // rows two levels at once: it reads this node's entry by position)
+        if (filt_next && pa.gstage != nullptr) pa.gstage[r_split] = pe;
       }
       nd.feature = s.feature;
       nd.threshold_bin = s.threshold_bin;
@@ -412,14 +443,21 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
     tc->n_leaves = leaf_base + t_leaf;
     *n_nodes_out = child_first + 2 * t_split;
     if (fast) {
-      spP[t_split] = t[4];
+      spP[four ? t[6] : t_split] = t[4];
       spH[t_pair] = t[5];
       lds.n_multi = 0;
     }
   }
+  if (need4 && !last) {
+    PlanEntry pe = g4;
+    pe.count = pe.count < 0 ? 0 : pe.count;
+    stP[r[6]] = pe;
+    lds.ext[r[6]] = x4;
+    spP[r[6]] = r[4];
+  }
   if (last) return;
   // (the driver filters only levels whose parents fit this path)
-  if (filt_next && !fast) {
+  if ((filt_next || four) && !fast) {
     if (threadIdx.x == 0) dev_error(&pa.ctrl->err, GBDT_E_INTERNAL);
     return;
   }
@@ -428,7 +466,10 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   // is filtered: its rows are not moved) and the next level's histogram plan
   // (nodes to build)
   if (fast) {
-    if (!filt_next)
+    if (four)
+      plan_emit(stP, spP, &lds.n_multi, t[6], part_tile, part_max_tiles, pa.prefix, pa.desc,
+                pa.status, pa.ctrl, true, nullptr, nullptr, lds.ext, pa.status2);
+    else if (!filt_next)
       plan_emit(stP, spP, &lds.n_multi, t_split, part_tile, part_max_tiles, pa.prefix, pa.desc,
                 pa.status, pa.ctrl, true, nullptr, nullptr);
     plan_emit(stH, spH, &lds.n_multi, t_pair, hist_tile_rows_next, hist_max_tiles_next, pa.hprefix,
@@ -479,9 +520,12 @@ int gbdt_grow_moves_ids(const gbdt_matrix* X, int32_t objective) {
   return grow_moves_ids(*X, objective == GBDT_OBJECTIVE_LOGISTIC) ? 1 : 0;
 }
 
-int gbdt_grow_filter_level(const gbdt_matrix* X, const gbdt_params* p) {
-  if (!X || !p) return -1;
-  return grow_filter_level(grow_moves_ids(*X, p->objective == GBDT_OBJECTIVE_LOGISTIC), p->max_depth);
+int64_t gbdt_grow_filtered_levels(const gbdt_matrix* X, const gbdt_params* p) {
+  if (!X || !p) return 0;
+  if (!grow_alternates(grow_moves_ids(*X, p->objective == GBDT_OBJECTIVE_LOGISTIC), p->max_depth)) return 0;
+  int64_t m = 0;
+  for (int32_t d = 1; d < p->max_depth; d += 2) m |= int64_t(1) << d;
+  return m;
 }
 
 int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* label, double* pred,
@@ -544,6 +588,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   pa.hprefix = reinterpret_cast<int32_t*>(w + WL.hprefix);
   pa.hmulti = reinterpret_cast<int32_t*>(w + WL.hmulti);
   pa.hdesc = reinterpret_cast<TileDesc*>(w + WL.hdesc);
+  pa.status2 = reinterpret_cast<uint64_t*>(w + WL.status2);
+  pa.gstage = reinterpret_cast<PlanEntry*>(w + WL.gstage);
   pa.feature_col = X->feature_col;
   pa.n_features = X->n_features;
   uint64_t* hpart = reinterpret_cast<uint64_t*>(w + WL.hpart);
@@ -559,24 +605,29 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
   // q is int32 (original order and both row buffers) when that is exact:
   // always for the logistic objective's 31-bit grids
   const bool q32 = logistic || driver_q32(n);
-  const int32_t part_tile = part_tile_rows(n, X->n_blocks, X->block_stride, q32, ids);
+  const int32_t part_tile =
+      part_tile_rows(n, X->n_blocks, X->block_stride, q32, ids, grow_alternates(ids, p->max_depth),
+                     X->n_bit_features > 0 || X->n_nib_features > 0);
   const int32_t target = hist_target_tiles(X->n_blocks + (X->n_bit_features > 0 ? 1 : 0) +
                                                (X->n_nib_features > 0 ? 1 : 0),
                                            n);
   const int32_t min_rows =
       hist_min_tile_rows(ft->total_bins,
                          int64_t(X->n_blocks) * X->block_stride + X->bit_stride + X->nib_stride);
-  // The rows of the last level's nodes are never moved: the partition before
-  // it is skipped too (level D - 2), and the last level's histogram tiles
-  // read each parent's rows, keeping those that go to the child they build.
-  // That trades one full row move for reading the larger children's rows
-  // once.  Row-moving mode only (index mode would gather them), and only
-  // while the level-(D - 2) nodes fit one planning pass (D <= 12).
-  // filt_level: the level whose k_level plans the filtered histograms.
-  const int32_t filt_level = grow_filter_level(ids, D) - 1;
+  // Row-moving mode moves rows only after every second level (alt): the
+  // histograms of an odd level are built from the parents' unmoved rows
+  // (each tile reads its parent's segment and keeps the rows that go to the
+  // child it builds), and after it one two-level partition moves each
+  // grandparent's rows straight into its grandchildren's order.  That trades
+  // every other full row move for reading the larger children's rows once.
+  // Index mode keeps one partition per level (filtering would gather both
+  // children's rows), and so do trees deeper than 12 levels (the level
+  // kernel plans filtered and two-level plans in one pass only up to 1,024
+  // nodes).
+  const bool alt = grow_alternates(ids, D);
   for (int32_t d = 0; d <= D; ++d) {
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
-    const int64_t rows_build = (d == 0 || (filt_level >= 0 && d == filt_level + 1)) ? n : n / 2;
+    const int64_t rows_build = (d == 0 || (alt && (d & 1))) ? n : n / 2;
     h_rows[d] = hist_tile_rows(rows_build, n, target, min_rows);
     if (d == 0) {
       h_tiles[d] = (rows_build + h_rows[d] - 1) / h_rows[d] + cap_build;
@@ -614,8 +665,9 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     if (e != hipSuccess) return hip_fail(e, "k_tree_init");
   }
 
+  int32_t n_moves = 0;  // partitions so far (they alternate between the two row buffers)
   for (int32_t d = 0; d < D; ++d) {
-    const gbdt_rows& dst = b->pp[d & 1];
+    const gbdt_rows& dst = b->pp[n_moves & 1];
     const int64_t lvl_off = (int64_t(1) << d) - 1;
     const int32_t cap_lvl = int32_t(1) << d;
     const int32_t cap_build = d == 0 ? 1 : (int32_t(1) << (d - 1));
@@ -623,7 +675,7 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     // the level's order; the root reads X in row order)
     gbdt_rows hsrc = src;
     if (ids) hsrc.X = *X;
-    const bool filt = filt_level >= 0 && d == filt_level + 1;
+    const bool filt = alt && (d & 1);
     rc = launch_hist(hsrc, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s, q32,
                      true, ids && src.rid != nullptr, ids ? b->rows_ix : nullptr, filt);
     if (rc) return rc;
@@ -649,24 +701,28 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
                      reinterpret_cast<FindCand*>(w + WL.fcand), guard, logistic ? b->hist_h : nullptr,
                      &tc->scale_h, b->split_h);
     if (rc) return rc;
+    // (alt: after an even level the next one filters; after an odd one the
+    // rows move two levels at once)
+    const bool filt_next = alt && !(d & 1) && d + 1 < D;
+    const bool four = alt && (d & 1) && d + 1 < D;
     diag_begin(kDiagLevel, s);
     hipLaunchKernelGGL(k_level, dim3(1), dim3(1024), 0, s, d, D, nodes_out, b->splits, tc, b->lists,
                        LL, min_split, p->reg_lambda, n_nodes_dev, pa, part_tile, (int32_t)p_tiles[d],
                        tile_max, target, min_rows, (int32_t)h_tiles[d + 1], guard,
-                       logistic ? b->split_h : nullptr, d == filt_level ? 1 : 0);
+                       logistic ? b->split_h : nullptr, filt_next ? 1 : 0, four ? 1 : 0);
     diag_end(s);
     {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return hip_fail(e, "k_level");
     }
     // the rows of the last level's children are never read again: the
-    // prediction update routes rows through the finished tree instead (and
-    // the level before it is not moved either: see filt_level)
-    if (d + 1 < D && d != filt_level) {
+    // prediction update routes rows through the finished tree instead
+    if (alt ? four : d + 1 < D) {
       rc = launch_partition(hsrc, dst, pa.desc, pa.status, pa.ctrl, p_tiles[d], part_tile, s, q32, q32,
-                            ids, ids ? b->cols : nullptr);
+                            ids, ids ? b->cols : nullptr, four, pa.status2);
       if (rc) return rc;
       src = dst;
+      ++n_moves;
     }
   }
   // step 7 in driver mode: a tree that failed (or whose structure does not

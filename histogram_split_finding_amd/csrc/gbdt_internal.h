@@ -78,10 +78,13 @@ inline bool grow_moves_ids(const gbdt_matrix& X, bool logistic) {
 // shorten the look-back chains (10M x 100: 3.88 -> 3.75 -> 3.68 ms per tree
 // from 2048- to 4096- to 8192-row tiles).
 constexpr int kPartTileRowsIds = 8192;
+// Two-level partitions (four) take the 4096-row tiles only when every split
+// byte is in the one block they hold in registers (no narrow block).
 inline int32_t part_tile_rows(int64_t n_rows, int32_t n_blocks, int32_t block_stride, bool q32,
-                              bool ids = false) {
+                              bool ids = false, bool four = false, bool narrow = false) {
   if (ids) return n_rows < kPartLargeRows ? kPartTileRows : kPartTileRowsIds;
   if (n_rows < kPartLargeRows || n_blocks > 1 || block_stride > 28 || !q32) return kPartTileRows;
+  if (four && (narrow || n_blocks < 1)) return kPartTileRows;
   return kPartTileRowsLarge;
 }
 constexpr int kHistMinTileRows = 1024;
@@ -96,6 +99,11 @@ constexpr int kNibSlots = 16;              // LDS slots per feature of the nibbl
 
 // Work assignment of one tile (written by the planner).  A partition plan
 // also carries the node's split, so a partition tile needs no second load.
+// A two-level (4-way) partition plan has one entry per grandparent g: its
+// segment and split, and the splits of its children a (left) and b (right),
+// each packed as (matrix column << 8) | threshold_bin, or -1 when that child
+// does not split; n2 (n3) is the number of a's (b's) rows that go to a's
+// (b's) left child, all of a's (b's) rows when it does not split.
 struct TileDesc {
   int32_t node;    // node id
   int32_t r0, r1;  // rows [r0, r1) of the tile
@@ -109,8 +117,16 @@ struct TileDesc {
   int32_t threshold_bin;
   int32_t n_left;
   int32_t split_valid;
+  int32_t split2, n2;     // two-level partition plans: child a's split and left rows
+  int32_t split3, n3;     // child b's
 };
-static_assert(sizeof(TileDesc) == 48, "tile descriptor is 48 bytes");
+static_assert(sizeof(TileDesc) == 64, "tile descriptor is 64 bytes");
+
+// One entry of a partition plan as the level kernel stages it: the node,
+// its segment and its split (the feature as its matrix column).
+struct PlanEntry {
+  int32_t node, begin, count, feature, threshold_bin, n_left;
+};
 
 // Two tile plans live in the workspace at once: the partition plan
 // (tdesc, prefix, status, ctrl->plan_total) and the histogram plan
@@ -127,6 +143,9 @@ struct WsLayout {
   size_t hmulti;      // int32[max_list + 2]: histogram plan, nodes of several tiles
   size_t fcand;       // FindCand[max_list * find_chunks]: split search, best per chunk
   size_t status;      // uint64[status_cap]
+  size_t status2;     // uint64[status_cap]: the second look-back of two-level partitions
+  size_t gstage;      // PlanEntry[max_list]: a level's splitting nodes, for the two-level
+                      // partition planned one level later
   size_t hpart;       // uint64[hpart_tiles * total_bins]
   size_t total;
   int64_t status_cap;
@@ -206,12 +225,13 @@ bool same_layout(const gbdt_matrix& a, const gbdt_matrix& b);
 int check_matrix(const gbdt_matrix& X);
 int check_hist_inputs(const gbdt_rows& src, const gbdt_features& ft);
 int check_partition_inputs(const gbdt_rows& src, const gbdt_rows& dst);
-// The level whose histograms the tree driver builds from the parents'
-// unpartitioned rows (filtered tiles; the partition of the level before it
-// is skipped), or -1: the last level, in row-moving mode, for depths 2 to 12
-// (the parents then fit one planning pass of the level kernel).
-inline int32_t grow_filter_level(bool moves_ids, int32_t max_depth) {
-  return (!moves_ids && max_depth >= 2 && max_depth <= 12) ? max_depth - 1 : -1;
+// Whether the tree driver moves rows only after every second level: in
+// row-moving mode, for depths 2 to 12 (the level kernel then plans every
+// filtered and two-level plan in one pass).  The odd levels' histograms are
+// then built from the parents' unpartitioned rows (filtered tiles), and a
+// two-level partition follows each odd level but the last.
+inline bool grow_alternates(bool moves_ids, int32_t max_depth) {
+  return !moves_ids && max_depth >= 2 && max_depth <= 12;
 }
 
 // Row pitch in bytes of index mode's row-interleaved copy: the row's
@@ -253,11 +273,13 @@ int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, co
 // position's row id (src.rid, NULL = the position itself) and q move, into
 // dst.rid and dst.q; the split byte is read from the matrix src.X at the row
 // id, from cols, the matrix's byte columns one after another, when that is
-// not NULL.
+// not NULL.  four: a two-level plan (one entry per grandparent, its
+// children's splits in the descriptors), whose second look-back runs over
+// status2; row-moving only.
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
                      hipStream_t s, bool qin32 = false, bool qout32 = false, bool ids = false,
-                     const uint8_t* cols = nullptr);
+                     const uint8_t* cols = nullptr, bool four = false, uint64_t* status2 = nullptr);
 
 // Blocks of the gradient kernels for n rows: each leaves a partial max |g|
 // and a partial sum of q in the workspace (gpart).

@@ -99,6 +99,10 @@ WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
   off = align256(off + sizeof(FindCand) * size_t(max_list) * size_t(find_chunks(total_bins)));
   L.status = off;
   off = align256(off + sizeof(uint64_t) * size_t(L.status_cap));
+  L.status2 = off;
+  off = align256(off + sizeof(uint64_t) * size_t(L.status_cap));
+  L.gstage = off;
+  off = align256(off + sizeof(PlanEntry) * (size_t(max_list) + 2));
   L.hpart = off;
   size_t hp = sizeof(uint64_t) * size_t(L.hpart_tiles) * size_t(total_bins);
   // the setup-time bin census of gbdt_pack_matrix reuses this region
@@ -1922,6 +1926,89 @@ __device__ int64_t lookback_excl(uint64_t* status, int32_t tile, int32_t tfirst,
   }
 }
 
+// The same over status words that carry two counts, bits 0-30 and 31-61
+// (two-level partitions): their exclusive sums in *lo and *hi.
+__device__ void lookback_excl2(uint64_t* status, int32_t tile, int32_t tfirst, int64_t* lo,
+                               int64_t* hi, bool* ok) {
+  const int lane = threadIdx.x & 63;
+  int64_t e0 = 0, e1 = 0;
+  int32_t idx = tile - 1;
+  uint32_t spins = 0;
+  while (true) {
+    const int32_t p = idx - lane;
+    const uint64_t w = p >= tfirst ? st_load(&status[p]) : kStInc;
+    const uint64_t st = w & kStMask;
+    const uint64_t inc = __ballot(st == kStInc);
+    const uint64_t zero = __ballot(st == 0ull);
+    const int first_inc = inc ? (__ffsll((unsigned long long)inc) - 1) : 64;
+    const uint64_t need = first_inc >= 63 ? ~0ull : ((2ull << first_inc) - 1ull);
+    if (zero & need) {
+      if (++spins > (1u << 20)) {
+        *ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    // both counts in one 64-bit sum, bits 0-31 and 32-63: a step adds at
+    // most one inclusive prefix (< 2^31) and 63 tile counts (< 2^13 each),
+    // so the low half never carries into the high one
+    const uint64_t v = ((need >> lane) & 1ull)
+                           ? ((w & 0x7fffffffull) | (((w >> 31) & 0x7fffffffull) << 32))
+                           : 0ull;
+    const uint64_t sum = wave_sum(v);
+    e0 += (int64_t)(sum & 0xffffffffull);
+    e1 += (int64_t)(sum >> 32);
+    if (first_inc < 64) break;
+    idx -= 64;
+  }
+  *lo = e0;
+  *hi = e1;
+}
+
+// Where a partition tile reads each row's value of a split feature (matrix
+// column c): from dword dw of the rows' first moved block, held in registers,
+// when the feature is a byte column of that block (dw >= 0); otherwise from
+// the dword at base + row * stride.  The value is (dword >> sh) & mask.
+struct SplitVal {
+  const uint8_t* base;
+  uint32_t stride, sh, mask;
+  int32_t dw;
+};
+__device__ __forceinline__ SplitVal split_val(int32_t c, int32_t b0, bool rows_in_regs,
+                                              const uint8_t* sbins, int64_t row_capacity,
+                                              int32_t n_blocks, int32_t block_features,
+                                              int32_t block_stride, int32_t n_features, int32_t n_bit,
+                                              int32_t bit_stride, int32_t n_nib, int32_t nib_stride) {
+  SplitVal v;
+  const int32_t nbc = n_features - n_bit;
+  const int32_t nbyte = nbc - n_nib;
+  const uint8_t* bits = sbins + int64_t(n_blocks) * row_capacity * block_stride;
+  v.dw = -1;
+  if (c >= nbc) {
+    const int32_t k = c - nbc;
+    v.base = bits + 4 * (k >> 5);
+    v.stride = (uint32_t)bit_stride;
+    v.sh = (uint32_t)(k & 31);
+    v.mask = 1u;
+  } else if (c >= nbyte) {
+    const int32_t k = c - nbyte;
+    v.base = bits + row_capacity * bit_stride + 4 * (k >> 3);
+    v.stride = (uint32_t)nib_stride;
+    v.sh = 4u * (uint32_t)(k & 7);
+    v.mask = 15u;
+  } else {
+    const int32_t b = c / block_features;
+    const int32_t j = c - b * block_features;
+    v.base = sbins + int64_t(b) * row_capacity * block_stride + (j & ~3);
+    v.stride = (uint32_t)block_stride;
+    v.sh = 8u * (uint32_t)(j & 3);
+    v.mask = 0xffu;
+    if (rows_in_regs && b == b0) v.dw = j >> 2;
+  }
+  return v;
+}
+
 // ND dwords of one row (4-byte aligned) as wide loads and stores: the first
 // min(ND, 4) dwords in `a`, the rest in `b` (two register quads, so each
 // load writes its own aligned registers).
@@ -1985,7 +2072,18 @@ __device__ __forceinline__ void row_store(uint8_t* p, const RowData<ND>& d) {
 // (index mode): the positions hold row ids of the matrix instead of rows; a
 // tile moves each position's id and q, with the split byte read from the
 // matrix at the id.
-template <int ND, int K, bool Q32OUT, bool NIB, bool IDS = false>
+//
+// FOUR (two-level partition): the tiles cover the segment of a grandparent
+// g, whose rows are in g's level order; each row goes through g's split to
+// child a (left) or b (right) and through that child's split (when it has
+// one) to a's or b's left or right child, and the four classes are written
+// stably to the grandchildren's segments [a1 | a2 | b1 | b2] of g's segment
+// -- the order two successive stable partitions would leave ("Module
+// Design: Training Core", section 6, step 5, applied at two levels at once).
+// Each class's rank comes from the tile's per-(row k, wave) counts and two
+// decoupled look-backs run side by side: wave 0 over (a1, a2) in status,
+// wave 1 over (b1, b2) in status2.
+template <int ND, int K, bool Q32OUT, bool NIB, bool IDS = false, bool FOUR = false>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     const uint8_t* __restrict__ sbins, const void* __restrict__ sq,
     const int32_t* __restrict__ srid, uint8_t* __restrict__ dbins, void* __restrict__ dq,
@@ -1993,15 +2091,19 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
     int32_t block_stride, int32_t n_features, int32_t n_bit, int32_t bit_stride,
     const TileDesc* __restrict__ desc, uint64_t* __restrict__ status, WsCtrl* __restrict__ ctrl,
     int32_t qsh /* log2 of the source q's element size: 2 (int32) or 3 (int64) */,
-    int32_t n_nib, int32_t nib_stride, const uint8_t* __restrict__ scols) {
+    int32_t n_nib, int32_t nib_stride, const uint8_t* __restrict__ scols,
+    uint64_t* __restrict__ status2) {
   static_assert(K == 2 || K == 4 || (K == 8 && IDS), "rows per thread");
   static_assert(!IDS || !NIB, "index mode moves no narrow block");
+  static_assert(!(IDS && FOUR), "two-level partitions move rows");
   constexpr int TILE = K * kPartThreads;
   constexpr int NCNT = K * kPartWaves;  // per-(row k, wave) left counts
   // an int32 destination q is the low half of the source element
   using QT = typename std::conditional<Q32OUT, int32_t, int64_t>::type;
-  __shared__ int32_t s_cnt[NCNT];
+  // (FOUR: two arrays of packed class counts, (a1 | a2 << 16) and (b1 | b2 << 16))
+  __shared__ int32_t s_cnt[FOUR ? 2 * NCNT : NCNT];
   __shared__ int32_t s_excl;
+  __shared__ int32_t s_excl4[4];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int32_t tile = (int32_t)blockIdx.x;
@@ -2019,8 +2121,19 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   // is set.  The descriptor's feature is the split's matrix column: a byte
   // column (c < nbyte = n_features - n_nib - n_bit), a nibble (c - nbyte) of
   // the nibble block or a bit (c - (n_features - n_bit)) of the bit block.
-  const bool split_ok = td.split_valid && td.feature >= 0 && td.feature < n_features;
-  const int32_t rows = split_ok ? rows_all : 0;
+  bool split_ok = td.split_valid && td.feature >= 0 && td.feature < n_features;
+  // FOUR: the children's splits (thresholds, whether each splits) and counts
+  const int32_t n_a = td.n_left;
+  const int32_t n_b = td.count - td.n_left;
+  const bool has2 = FOUR && td.split2 >= 0;
+  const bool has3 = FOUR && td.split3 >= 0;
+  const int32_t c2 = has2 ? (td.split2 >> 8) : 0, thr2 = has2 ? (td.split2 & 0xff) : 0;
+  const int32_t c3 = has3 ? (td.split3 >> 8) : 0, thr3 = has3 ? (td.split3 & 0xff) : 0;
+  if constexpr (FOUR) {
+    split_ok = split_ok && c2 < n_features && c3 < n_features && n_a >= 0 && n_b >= 0 &&
+               td.n2 >= 0 && td.n2 <= n_a && td.n3 >= 0 && td.n3 <= n_b;
+  }
+  int32_t rows = split_ok ? rows_all : 0;
   const int32_t nbc = n_features - n_bit;  // the first bit column
   const int32_t nbyte = nbc - n_nib;
   const int32_t sc = split_ok ? td.feature : 0;
@@ -2065,6 +2178,28 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   // cache line per 128 consecutive ids instead of per 128 / block_stride
   const bool from_cols = IDS && scols != nullptr;  // (uniform)
   int32_t rids[K];
+  // FOUR: each row's values of the children's split features (x2: a's, x3:
+  // b's).  The 4096-row tiles (K = 4) take them from the rows' registers
+  // only: the planner gives two-level plans those tiles only for layouts of
+  // one byte block (the registers of separate loads would cost the kernel
+  // its second workgroup per CU); a child split outside the registers' block
+  // is then an error and the tile moves nothing.
+  constexpr bool CHILD_LOADS = FOUR && K < 4;
+  SplitVal sv2{}, sv3{};
+  uint32_t x2[CHILD_LOADS ? K : 1], x3[CHILD_LOADS ? K : 1];
+  if constexpr (FOUR) {
+    const bool regs = n_blocks > 0;  // the rows' first moved block is held in registers
+    sv2 = split_val(c2, b0, regs, sbins, row_capacity, n_blocks, block_features, block_stride,
+                    n_features, n_bit, bit_stride, n_nib, nib_stride);
+    sv3 = split_val(c3, b0, regs, sbins, row_capacity, n_blocks, block_features, block_stride,
+                    n_features, n_bit, bit_stride, n_nib, nib_stride);
+#pragma unroll
+    for (int k = 0; k < (CHILD_LOADS ? K : 1); ++k) x2[k] = x3[k] = 0u;
+    if (!CHILD_LOADS && ((has2 && sv2.dw < 0) || (has3 && sv3.dw < 0))) {
+      split_ok = false;
+      rows = 0;
+    }
+  }
   if (rows > 0) {
     const char* __restrict__ tq = reinterpret_cast<const char*>(sq) + (r0 << qsh);
     const uint32_t lr = (uint32_t)(rows - 1);
@@ -2113,6 +2248,18 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
       // dword of the bit block, and the value is never stored
       if constexpr (!IDS) row_load<ND>(tb + ic * bs, rd[k]);
     }
+    if constexpr (CHILD_LOADS) {
+      // (loaded with the rows; a feature of the registers' block needs none)
+      const uint8_t* __restrict__ t2 = sv2.base + r0 * int64_t(sv2.stride);
+      const uint8_t* __restrict__ t3 = sv3.base + r0 * int64_t(sv3.stride);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const uint32_t i = (uint32_t)(k * kPartThreads) + threadIdx.x;
+        const uint32_t ic = i < lr ? i : lr;
+        if (has2 && sv2.dw < 0) x2[k] = *reinterpret_cast<const uint32_t*>(t2 + ic * sv2.stride);
+        if (has3 && sv3.dw < 0) x3[k] = *reinterpret_cast<const uint32_t*>(t3 + ic * sv3.stride);
+      }
+    }
     if (from_rows) {
       const uint32_t fdw = (uint32_t)fcol >> 2;
       const uint32_t fsh = 8u * (uint32_t)(fcol & 3);
@@ -2129,26 +2276,20 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
   }
   if (!split_ok && threadIdx.x == 0) dev_error(&ctrl->err, GBDT_E_INTERNAL);
 
-  uint64_t bal[K];  // go-left flags of the wave's rows k (a row's own flag is its bit)
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int32_t i = k * kPartThreads + threadIdx.x;
-    bal[k] = __ballot((i < rows) && (fb[k] <= td.threshold_bin));
-    if (lane == 0) s_cnt[k * kPartWaves + wid] = __popcll(bal[k]);
-  }
-  __syncthreads();
-  // wave 0: exclusive scan of the (row k, wave) counts in row order, then
-  // publish the tile's left count at once (so later tiles never wait long),
-  // look back for the exclusive prefix of the node's earlier tiles and
-  // publish the inclusive one
-  if (wid == 0) {
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t seg_end = int64_t(td.begin) + td.count;
+  bool bad_pos = false;
+  int32_t dpos[K];
+  // Wave w's exclusive scan of count array cnt (the (row k, wave) counts in
+  // row order, in place); returns the tile's total.
+  auto scan_counts = [&](int32_t* cnt) -> int32_t {
     constexpr int E = NCNT >= 64 ? NCNT / 64 : 1;  // counts per lane
     int32_t c[E];
     int32_t own = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int idx = lane * E + e;
-      c[e] = idx < NCNT ? s_cnt[idx] : 0;
+      c[e] = idx < NCNT ? cnt[idx] : 0;
       own += c[e];
     }
     const int32_t x = wave_incl_scan(own);
@@ -2156,42 +2297,139 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int idx = lane * E + e;
-      if (idx < NCNT) s_cnt[idx] = run;
+      if (idx < NCNT) cnt[idx] = run;
       run += c[e];
     }
-    const int32_t acc = __builtin_amdgcn_readlane(x, 63);
-    if (lane == 0) st_publish(&status[tile], (tin == 0 ? kStInc : kStAgg) | (uint64_t)(uint32_t)acc);
-    int64_t excl = 0;
-    bool ok = true;
-    if (tin > 0) excl = lookback_excl(status, tile, tfirst, &ok);
-    if (lane == 0) {
-      if (!ok) dev_error(&ctrl->err, GBDT_E_INTERNAL);
-      if (tin > 0) st_publish(&status[tile], kStInc | (uint64_t)(uint32_t)(excl + acc));
-      s_excl = (int32_t)excl;
-      if (tile == tlast && excl + acc != td.n_left) dev_error(&ctrl->err, GBDT_E_INTERNAL);
-    }
-  }
-  __syncthreads();
-  const int32_t excl = s_excl;
-  const int64_t lbase = int64_t(td.begin) + excl;
-  const int64_t rbase = int64_t(td.begin) + td.n_left + (int64_t(tin) * TILE - excl);
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t seg_end = int64_t(td.begin) + td.count;
-  bool bad_pos = false;
-  int32_t dpos[K];
+    return __builtin_amdgcn_readlane(x, 63);
+  };
+  if constexpr (!FOUR) {
+    uint64_t bal[K];  // go-left flags of the wave's rows k (a row's own flag is its bit)
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int32_t i = k * kPartThreads + threadIdx.x;
-    dpos[k] = -1;
-    if (i < rows) {
-      const int32_t rl = s_cnt[k * kPartWaves + wid] + __popcll(bal[k] & lt_mask);
-      const bool left = (bal[k] >> lane) & 1ull;
-      const int64_t d = left ? lbase + rl : rbase + (i - rl);
-      // a split record whose left count disagrees with the rows could send a
-      // row outside its node's segment: such a row is not written
-      const bool in_seg = d >= td.begin && d < seg_end;
-      bad_pos |= !in_seg;
-      dpos[k] = in_seg ? (int32_t)d : -1;
+    for (int k = 0; k < K; ++k) {
+      const int32_t i = k * kPartThreads + threadIdx.x;
+      bal[k] = __ballot((i < rows) && (fb[k] <= td.threshold_bin));
+      if (lane == 0) s_cnt[k * kPartWaves + wid] = __popcll(bal[k]);
+    }
+    __syncthreads();
+    // wave 0: exclusive scan of the (row k, wave) counts in row order, then
+    // publish the tile's left count at once (so later tiles never wait long),
+    // look back for the exclusive prefix of the node's earlier tiles and
+    // publish the inclusive one
+    if (wid == 0) {
+      const int32_t acc = scan_counts(s_cnt);
+      if (lane == 0) st_publish(&status[tile], (tin == 0 ? kStInc : kStAgg) | (uint64_t)(uint32_t)acc);
+      int64_t excl = 0;
+      bool ok = true;
+      if (tin > 0) excl = lookback_excl(status, tile, tfirst, &ok);
+      if (lane == 0) {
+        if (!ok) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+        if (tin > 0) st_publish(&status[tile], kStInc | (uint64_t)(uint32_t)(excl + acc));
+        s_excl = (int32_t)excl;
+        if (tile == tlast && excl + acc != td.n_left) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+      }
+    }
+    __syncthreads();
+    const int32_t excl = s_excl;
+    const int64_t lbase = int64_t(td.begin) + excl;
+    const int64_t rbase = int64_t(td.begin) + td.n_left + (int64_t(tin) * TILE - excl);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int32_t i = k * kPartThreads + threadIdx.x;
+      dpos[k] = -1;
+      if (i < rows) {
+        const int32_t rl = s_cnt[k * kPartWaves + wid] + __popcll(bal[k] & lt_mask);
+        const bool left = (bal[k] >> lane) & 1ull;
+        const int64_t d = left ? lbase + rl : rbase + (i - rl);
+        // a split record whose left count disagrees with the rows could send a
+        // row outside its node's segment: such a row is not written
+        const bool in_seg = d >= td.begin && d < seg_end;
+        bad_pos |= !in_seg;
+        dpos[k] = in_seg ? (int32_t)d : -1;
+      }
+    }
+  } else {
+    // class of each row: 0 a1, 1 a2, 2 b1, 3 b2 (a child without a split
+    // keeps all its rows in its first class), two bits per row k in one
+    // register, and the (row k, wave) counts of every class; the ballots
+    // are taken again for the ranks after the look-back (the registers of
+    // per-row ranks would cost the kernel its second workgroup per CU)
+    uint32_t cls = 0u;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int32_t i = k * kPartThreads + threadIdx.x;
+      const bool valid = i < rows;
+      // (the children's split values: from the rows' registers or their loads)
+      const uint32_t w2 = sv2.dw >= 0 ? row_dword<ND>(rd[k], (uint32_t)sv2.dw) : x2[CHILD_LOADS ? k : 0];
+      const uint32_t w3 = sv3.dw >= 0 ? row_dword<ND>(rd[k], (uint32_t)sv3.dw) : x3[CHILD_LOADS ? k : 0];
+      const int32_t v2 = (int32_t)((w2 >> sv2.sh) & sv2.mask);
+      const int32_t v3 = (int32_t)((w3 >> sv3.sh) & sv3.mask);
+      const bool ga = fb[k] <= td.threshold_bin;
+      const bool l2 = ga ? (!has2 || v2 <= thr2) : (!has3 || v3 <= thr3);
+      const uint32_t c = (ga ? 0u : 2u) | (l2 ? 0u : 1u);
+      cls |= c << (2 * k);
+      asm volatile("" : "+v"(cls));
+      const uint64_t m0 = __ballot(valid && c == 0u);
+      const uint64_t m1 = __ballot(valid && c == 1u);
+      const uint64_t m2 = __ballot(valid && c == 2u);
+      const uint64_t m3 = __ballot(valid && c == 3u);
+      if (lane == 0) {
+        s_cnt[k * kPartWaves + wid] = __popcll(m0) | (__popcll(m1) << 16);
+        s_cnt[NCNT + k * kPartWaves + wid] = __popcll(m2) | (__popcll(m3) << 16);
+      }
+    }
+    // (the empty asm keeps the classes computed here: sunk past the barrier,
+    // they would keep every row's split values live instead)
+    asm volatile("" : "+v"(cls));
+    __syncthreads();
+    // wave 0 scans, publishes and looks back over (a1, a2) in status, wave 1
+    // over (b1, b2) in status2; each checks its child's totals at the last tile
+    if (wid < 2) {
+      const int32_t acc = scan_counts(s_cnt + wid * NCNT);
+      const int64_t lo = acc & 0xffff, hi = acc >> 16;
+      uint64_t* __restrict__ st = wid == 0 ? status : status2;
+      if (lane == 0)
+        st_publish(&st[tile], (tin == 0 ? kStInc : kStAgg) | ((uint64_t)hi << 31) | (uint64_t)lo);
+      int64_t e0 = 0, e1 = 0;
+      bool ok = true;
+      if (tin > 0) lookback_excl2(st, tile, tfirst, &e0, &e1, &ok);
+      if (lane == 0) {
+        if (!ok) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+        if (tin > 0) st_publish(&st[tile], kStInc | ((uint64_t)(e1 + hi) << 31) | (uint64_t)(e0 + lo));
+        s_excl4[2 * wid] = (int32_t)e0;
+        s_excl4[2 * wid + 1] = (int32_t)e1;
+        if (tile == tlast) {
+          const int64_t want0 = wid == 0 ? td.n2 : td.n3;
+          const int64_t want1 = wid == 0 ? n_a - td.n2 : n_b - td.n3;
+          if (e0 + lo != want0 || e1 + hi != want1) dev_error(&ctrl->err, GBDT_E_INTERNAL);
+        }
+      }
+    }
+    __syncthreads();
+    // the grandchildren's segments: a1 at begin, a2 after a1, b1 at begin + n_a, b2 after b1
+    const int64_t B0 = int64_t(td.begin) + s_excl4[0];
+    const int64_t B1 = int64_t(td.begin) + td.n2 + s_excl4[1];
+    const int64_t B2 = int64_t(td.begin) + n_a + s_excl4[2];
+    const int64_t B3 = int64_t(td.begin) + n_a + td.n3 + s_excl4[3];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int32_t i = k * kPartThreads + threadIdx.x;
+      const bool valid = i < rows;
+      const int32_t c = (int32_t)((cls >> (2 * k)) & 3u);
+      const uint64_t m0 = __ballot(valid && c == 0);
+      const uint64_t m1 = __ballot(valid && c == 1);
+      const uint64_t m2 = __ballot(valid && c == 2);
+      const uint64_t m3 = __ballot(valid && c == 3);
+      dpos[k] = -1;
+      if (valid) {
+        const uint64_t mine = c == 0 ? m0 : (c == 1 ? m1 : (c == 2 ? m2 : m3));
+        const int32_t pk = s_cnt[(c >> 1) * NCNT + k * kPartWaves + wid];
+        const int32_t off = (c & 1) ? (pk >> 16) : (pk & 0xffff);
+        const int64_t base = c == 0 ? B0 : (c == 1 ? B1 : (c == 2 ? B2 : B3));
+        const int64_t d = base + off + __popcll(mine & lt_mask);
+        const bool in_seg = d >= td.begin && d < seg_end;
+        bad_pos |= !in_seg;
+        dpos[k] = in_seg ? (int32_t)d : -1;
+      }
     }
   }
   if (bad_pos) dev_error(&ctrl->err, GBDT_E_INTERNAL);
@@ -3317,26 +3555,35 @@ __global__ void __launch_bounds__(kBoundThreads) k_bounds_quantile(const float* 
   }
 }
 
-template <int K, bool Q, bool N>
-static auto partition_kernel(int32_t nd) -> decltype(&k_partition<1, K, Q, N>) {
+template <int K, bool Q, bool N, bool F>
+static auto partition_kernel_f(int32_t nd) -> decltype(&k_partition<1, K, Q, N>) {
   switch (nd) {
-    case 1: return k_partition<1, K, Q, N>;
-    case 2: return k_partition<2, K, Q, N>;
-    case 3: return k_partition<3, K, Q, N>;
-    case 4: return k_partition<4, K, Q, N>;
-    case 5: return k_partition<5, K, Q, N>;
-    case 6: return k_partition<6, K, Q, N>;
-    case 7: return k_partition<7, K, Q, N>;
-    case 8: return k_partition<8, K, Q, N>;
+    case 1: return k_partition<1, K, Q, N, false, F>;
+    case 2: return k_partition<2, K, Q, N, false, F>;
+    case 3: return k_partition<3, K, Q, N, false, F>;
+    case 4: return k_partition<4, K, Q, N, false, F>;
+    case 5: return k_partition<5, K, Q, N, false, F>;
+    case 6: return k_partition<6, K, Q, N, false, F>;
+    case 7: return k_partition<7, K, Q, N, false, F>;
+    case 8: return k_partition<8, K, Q, N, false, F>;
     default: return nullptr;
   }
 }
 
+// The row-moving kernel for rows of nd dwords; four: the two-level form.
+template <int K, bool Q, bool N>
+static auto partition_kernel(int32_t nd, bool four) -> decltype(&k_partition<1, K, Q, N>) {
+  return four ? partition_kernel_f<K, Q, N, true>(nd) : partition_kernel_f<K, Q, N, false>(nd);
+}
+
 int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc* desc,
                      uint64_t* status, WsCtrl* ctrl, int64_t max_tiles, int32_t tile_rows,
-                     hipStream_t s, bool qin32, bool qout32, bool ids, const uint8_t* cols) {
+                     hipStream_t s, bool qin32, bool qout32, bool ids, const uint8_t* cols,
+                     bool four, uint64_t* status2) {
   const int32_t nd = src.X.n_blocks > 0 ? src.X.block_stride / 4 : 1;
   if (qin32 && !qout32) return fail(GBDT_E_INTERNAL, "an int64 q destination needs an int64 source");
+  if (four && (ids || status2 == nullptr))
+    return fail(GBDT_E_INTERNAL, "two-level partitions move rows and need a second status array");
   decltype(&k_partition<1, 2, false, false>) kern = nullptr;
   const bool nib = src.X.n_nib_features > 0;
   if (ids) {
@@ -3349,10 +3596,11 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
     else
       return fail(GBDT_E_INTERNAL, "unsupported partition tile size");
   } else if (tile_rows == 2 * kPartThreads)
-    kern = nib ? (qout32 ? partition_kernel<2, true, true>(nd) : partition_kernel<2, false, true>(nd))
-               : (qout32 ? partition_kernel<2, true, false>(nd) : partition_kernel<2, false, false>(nd));
+    kern = nib ? (qout32 ? partition_kernel<2, true, true>(nd, four) : partition_kernel<2, false, true>(nd, four))
+               : (qout32 ? partition_kernel<2, true, false>(nd, four)
+                         : partition_kernel<2, false, false>(nd, four));
   else if (tile_rows == 4 * kPartThreads && qout32 && nd <= 7)
-    kern = nib ? partition_kernel<4, true, true>(nd) : partition_kernel<4, true, false>(nd);
+    kern = nib ? partition_kernel<4, true, true>(nd, four) : partition_kernel<4, true, false>(nd, four);
   else
     return fail(GBDT_E_INTERNAL, "unsupported partition tile size");
   if (kern == nullptr) return fail(GBDT_E_UNSUPPORTED, "a column block wider than 32 bytes");
@@ -3361,7 +3609,8 @@ int launch_partition(const gbdt_rows& src, const gbdt_rows& dst, const TileDesc*
                      src.rid, dst.X.bins, dst.q, dst.rid, src.X.row_capacity, src.X.n_blocks,
                      src.X.block_features, src.X.block_stride, src.X.n_features,
                      src.X.n_bit_features, src.X.bit_stride, desc, status, ctrl, qin32 ? 2 : 3,
-                     src.X.n_nib_features, src.X.nib_stride, ids ? cols : nullptr);
+                     src.X.n_nib_features, src.X.nib_stride, ids ? cols : nullptr,
+                     four ? status2 : nullptr);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_partition");
   return GBDT_OK;

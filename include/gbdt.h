@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GBDT_ABI_VERSION 6
+#define GBDT_ABI_VERSION 7
 #define GBDT_MAX_DEPTH 16       /* deepest tree the level loop supports */
 #define GBDT_MAX_FEATURES 4096
 #define GBDT_MAX_BINS 256       /* bins per feature */
@@ -580,16 +580,19 @@ typedef struct gbdt_grow_buffers {
 int gbdt_grow_moves_ids(const gbdt_matrix* X /* host */, int32_t objective);
 
 /*
- * The level of gbdt_grow_tree whose histograms are built from the parents'
- * unpartitioned rows, or -1.  In row-moving mode (gbdt_grow_moves_ids 0)
- * with 2 <= max_depth <= 12 it is the last level, max_depth - 1: the
- * partition of level max_depth - 2 is skipped, and each histogram tile of
- * the last level reads its parent's segment and adds only the rows that go
- * to the child it builds (bin <= threshold_bin for a left child; "Module
- * Design: Training Core", section 6, steps 3 and 5).  The histograms are
- * the same; only the work differs.  Host only; no error codes.
+ * The levels of gbdt_grow_tree whose histograms are built from the parents'
+ * unpartitioned rows, as a bit mask (bit d: level d), or 0.  In row-moving
+ * mode (gbdt_grow_moves_ids 0) with 2 <= max_depth <= 12 these are the odd
+ * levels: rows move only after each odd level but the last, by one stable
+ * two-level partition of every grandparent's segment into its
+ * grandchildren's segments, and each histogram tile of an odd level reads
+ * its parent's segment and adds only the rows that go to the child it
+ * builds (bin <= threshold_bin for a left child; "Module Design: Training
+ * Core", section 6, steps 3 and 5).  The histograms, nodes and row orders
+ * of the built levels are the same as with one partition per level; only
+ * the work differs.  Host only; NULL arguments give 0.
  */
-int gbdt_grow_filter_level(const gbdt_matrix* X /* host */, const gbdt_params* p /* host */);
+int64_t gbdt_grow_filtered_levels(const gbdt_matrix* X /* host */, const gbdt_params* p /* host */);
 
 /*
  * X's byte blocks interleaved row by row: row r's block b (block_stride

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
         assert name in names
     for name in names:
         assert hasattr(lib, name), name
-    assert g.gbdt_abi_version() == 6
+    assert g.gbdt_abi_version() == 7
 
 
 def test_library_is_not_linked_to_the_oracle():
@@ -215,17 +215,20 @@ def test_index_mode_rule(nbins, bits, nibbles, objective, want):
 
 
 @pytest.mark.parametrize("nbins,objective,depth,want", [
-    ([256] * 28, 0, 12, 11),    # one byte block, row-moving: the last level is filtered
-    ([256] * 28, 0, 2, 1),
-    ([256] * 28, 0, 1, -1),     # no level before the last one to skip
-    ([256] * 28, 0, 13, -1),    # more parents than one planning pass
-    ([256] * 100, 0, 8, -1),    # index mode moves ids: no filter
-    ([256] * 100, 1, 8, 7),     # the logistic objective moves rows
+    ([256] * 28, 0, 12, 0b101010101010),  # one byte block, row-moving: the odd levels filter
+    ([256] * 28, 0, 10, 0b1010101010),
+    ([256] * 28, 0, 3, 0b010),            # rows move once, after level 1; level 2 streams them
+    ([256] * 28, 0, 2, 0b10),
+    ([256] * 28, 0, 1, 0),                # no level before the last one to skip
+    ([256] * 28, 0, 13, 0),               # more parents than one planning pass
+    ([256] * 100, 0, 8, 0),               # index mode moves ids: no filter
+    ([256] * 100, 1, 8, 0b10101010),      # the logistic objective moves rows
 ])
-def test_filter_level_rule(nbins, objective, depth, want):
-    """gbdt_grow_filter_level: the last level of a row-moving tree of depth 2
-    to 12 builds its histograms from the parents' unmoved rows."""
+def test_filtered_levels_rule(nbins, objective, depth, want):
+    """gbdt_grow_filtered_levels: a row-moving tree of depth 2 to 12 builds
+    the histograms of its odd levels from the parents' unmoved rows, and
+    moves rows after each odd level but the last, two levels at once."""
     ft = g.FeatureTable(nbins, "cpu", pack_bits=False, pack_nibbles=False)
     X = g.RowBuffer(ft, 10, "cpu", with_rid=False, with_bins=False).matrix()
     p = g.make_params(max_depth=depth, objective=objective)
-    assert g.load().gbdt_grow_filter_level(ctypes.byref(X), ctypes.byref(p)) == want
+    assert g.load().gbdt_grow_filtered_levels(ctypes.byref(X), ctypes.byref(p)) == want
