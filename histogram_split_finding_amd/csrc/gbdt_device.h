@@ -207,7 +207,9 @@ __device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, in
   const int32_t total = spre[n];
   for (int32_t j = threadIdx.x; j <= n; j += blockDim.x) {
     prefix[j] = spre[j];
-    if (multi != nullptr && j < n && spre[j + 1] - spre[j] > 1) multi[1 + atomicAdd(n_multi, 1)] = j;
+    if (multi != nullptr && j < n && spre[j + 1] - spre[j] > 1)
+      reinterpret_cast<int4*>(multi + 4)[atomicAdd(n_multi, 1)] =
+          make_int4(stage[j].node, spre[j], spre[j + 1], j);
   }
   if (threadIdx.x == 0) {
     if (total > max_tiles) dev_error(&ctrl->err, GBDT_E_SHAPE);
@@ -277,8 +279,9 @@ __device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, in
 // split in its tiles' descriptors (the split feature as its matrix column:
 // feature_col[feature], or the feature itself when feature_col is NULL),
 // and (multi != nullptr) the list positions
-// of the nodes with more than one tile (multi[0] = their count, in no
-// particular order; for the partial reduction).  More tiles than max_tiles sets
+// of the nodes with more than one tile (multi[0] = their count, then from
+// multi + 4 one int4 (node, first tile, end tile, list position) each, in
+// no particular order; for the partial reduction).  More tiles than max_tiles sets
 // GBDT_E_SHAPE; the surplus is not planned.  Each entry's node (and split)
 // is read once; up to kPlanStage entries are kept in LDS, so writing the
 // descriptors reads no global memory.  The list and the nodes' counts must
@@ -336,7 +339,8 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
     prefix[j] = excl;
     if (in_lds) L.spre[j] = excl;
     const int32_t nt = tiles_of(nodes[list[j]].count, tile_rows);
-    if (multi != nullptr && nt > 1) multi[1 + atomicAdd(&L.n_multi, 1)] = j;
+    if (multi != nullptr && nt > 1)
+      reinterpret_cast<int4*>(multi + 4)[atomicAdd(&L.n_multi, 1)] = make_int4(list[j], excl, excl + nt, j);
     excl += nt;
   }
   __syncthreads();

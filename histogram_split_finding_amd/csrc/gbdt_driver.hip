@@ -210,6 +210,7 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
                                                 int32_t filt_next, int32_t four) {
   __shared__ PlanLds lds;
   __shared__ int32_t shm[7 * 17];
+  __shared__ int32_t s_fcol[GBDT_MAX_FEATURES];  // the matrix column of each feature
   // after an error nothing of the level is written, and the partition that
   // follows finds an empty plan (it reads no other sign of the failure: a
   // partition tile that stopped early would stall its successors'
@@ -218,6 +219,15 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
     if (threadIdx.x == 0) pa.ctrl->plan_total = 0;
     return;
   }
+  // the feature -> matrix column map, loaded with the level's first loads
+  // (the plans' split columns then cost no dependent round trip); the block
+  // scans below synchronise before its first use
+  const int32_t nfeat = pa.n_features < GBDT_MAX_FEATURES ? pa.n_features : GBDT_MAX_FEATURES;
+  for (int32_t f = threadIdx.x; f < nfeat; f += blockDim.x)
+    s_fcol[f] = pa.feature_col != nullptr ? pa.feature_col[f] : f;
+  auto column_of = [&](const gbdt_split& sp) -> int32_t {
+    return (!sp.valid || sp.feature < 0 || sp.feature >= nfeat) ? -1 : s_fcol[sp.feature];
+  };
   for (int c = threadIdx.x; c < kPlanSizeBuckets; c += blockDim.x) lds.bucket[c] = 0;
   const int32_t first = tc->level_start[d];
   const int32_t cnt = tc->level_count[d];
@@ -246,18 +256,14 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   // carries both children's splits, and a grandparent neither of whose
   // children splits moves nothing
   PlanEntry g4{};
-  int4 x4 = make_int4(-1, 0, -1, 0);
+  gbdt_split sa{}, sb{};
   bool need4 = false;
   if (four && fast && i0 < i1 && (i0 & 1) == 0 && i0 + 1 < cnt) {
-    const gbdt_split sa = splits[first + i0];
-    const gbdt_split sb = splits[first + i0 + 1];
+    sa = splits[first + i0];
+    sb = splits[first + i0 + 1];
     g4 = pa.gstage[i0 >> 1];
-    const int32_t ca = split_column(sa, pa.feature_col, pa.n_features);
-    const int32_t cb = split_column(sb, pa.feature_col, pa.n_features);
-    need4 = ca >= 0 || cb >= 0;
-    x4 = make_int4(ca >= 0 ? ((ca << 8) | (sa.threshold_bin & 0xff)) : -1, ca >= 0 ? sa.n_left : g4.n_left,
-                   cb >= 0 ? ((cb << 8) | (sb.threshold_bin & 0xff)) : -1,
-                   cb >= 0 ? sb.n_left : g4.count - g4.n_left);
+    need4 = (sa.valid && sa.feature >= 0 && sa.feature < nfeat) ||
+            (sb.valid && sb.feature >= 0 && sb.feature < nfeat);
     if (need4 && !last) {
       c[6] = 1;
       c[4] = tiles_of(g4.count, part_tile);
@@ -340,7 +346,7 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
         pe.node = v;
         pe.begin = nd.begin;
         pe.count = nd.count < 0 ? 0 : nd.count;
-        pe.feature = split_column(s, pa.feature_col, pa.n_features);
+        pe.feature = column_of(s);
         pe.threshold_bin = s.threshold_bin;
         pe.n_left = s.n_left;
         if (!four) {
@@ -393,7 +399,7 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
             // going to sm (n_left 2: the left child, 3: the right one)
             pe.begin = nd.begin;
             pe.count = nd.count < 0 ? 0 : nd.count;
-            pe.feature = split_column(s, pa.feature_col, pa.n_features);
+            pe.feature = column_of(s);
             pe.threshold_bin = s.threshold_bin;
             pe.n_left = sm == lc ? 2 : 3;
           } else {
@@ -451,8 +457,12 @@ __global__ void __launch_bounds__(1024) k_level(int32_t d, int32_t D, gbdt_node*
   if (need4 && !last) {
     PlanEntry pe = g4;
     pe.count = pe.count < 0 ? 0 : pe.count;
+    const int32_t ca = column_of(sa), cb = column_of(sb);
     stP[r[6]] = pe;
-    lds.ext[r[6]] = x4;
+    lds.ext[r[6]] = make_int4(ca >= 0 ? ((ca << 8) | (sa.threshold_bin & 0xff)) : -1,
+                              ca >= 0 ? sa.n_left : g4.n_left,
+                              cb >= 0 ? ((cb << 8) | (sb.threshold_bin & 0xff)) : -1,
+                              cb >= 0 ? sb.n_left : g4.count - g4.n_left);
     spP[r[6]] = r[4];
   }
   if (last) return;
@@ -679,8 +689,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
     rc = launch_hist(hsrc, *ft, pa.hdesc, h_tiles[d], b->hist_g, b->hist_cnt, hpart, pa.ctrl, s, q32,
                      true, ids && src.rid != nullptr, ids ? b->rows_ix : nullptr, filt);
     if (rc) return rc;
-    rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
-                            h_tiles[d], n, ft->total_bins, hpart, b->hist_g, b->hist_cnt, s, guard);
+    rc = launch_hist_reduce(pa.hmulti, cap_build, h_tiles[d], n, ft->total_bins, hpart, b->hist_g,
+                            b->hist_cnt, s, guard);
     if (rc) return rc;
     if (logistic) {
       // the Hessian histograms: the same kernels over the same tile plan with
@@ -691,8 +701,8 @@ int gbdt_grow_tree(const gbdt_matrix* X, const gbdt_features* ft, const float* l
       rc = launch_hist(hs, *ft, pa.hdesc, h_tiles[d], b->hist_h, b->hist_cnt, hpart, pa.ctrl, s, true,
                        true, false, nullptr, filt);
       if (rc) return rc;
-      rc = launch_hist_reduce(b->lists + LL.build + lvl_off, pa.hmulti, cap_build, pa.hprefix,
-                              h_tiles[d], n, ft->total_bins, hpart, b->hist_h, b->hist_cnt, s, guard);
+      rc = launch_hist_reduce(pa.hmulti, cap_build, h_tiles[d], n, ft->total_bins, hpart, b->hist_h,
+                              b->hist_cnt, s, guard);
       if (rc) return rc;
     }
     rc = launch_find(b->hist_g, b->hist_cnt, *ft, nodes_out, b->lists + LL.find + lvl_off,

@@ -140,7 +140,8 @@ struct WsLayout {
                       // logistic objective's Hessian maxima and sums follow
   size_t prefix;      // int32[max_list + 2]: partition plan
   size_t hprefix;     // int32[max_list + 2]: histogram plan
-  size_t hmulti;      // int32[max_list + 2]: histogram plan, nodes of several tiles
+  size_t hmulti;      // int32[4 + 4 (max_list + 2)]: histogram plan, nodes of several tiles:
+                      // the count, then (node, first tile, end tile, list position) each
   size_t fcand;       // FindCand[max_list * find_chunks]: split search, best per chunk
   size_t status;      // uint64[status_cap]
   size_t status2;     // uint64[status_cap]: the second look-back of two-level partitions
@@ -256,10 +257,9 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
                 int64_t max_tiles, int64_t* hist_g, uint32_t* hist_cnt, uint64_t* hpart,
                 WsCtrl* ctrl, hipStream_t s, bool q32 = false, bool guard = false, bool ids = false,
                 const uint8_t* rows_ix = nullptr, bool filt = false);
-int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_cap,
-                       const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
-                       const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s,
-                       const int32_t* guard = nullptr);
+int launch_hist_reduce(const int32_t* multi, int32_t list_cap, int64_t max_tiles, int64_t n_rows,
+                       int32_t total_bins, const uint64_t* hpart, int64_t* hist_g,
+                       uint32_t* hist_cnt, hipStream_t s, const int32_t* guard = nullptr);
 // hist_h / scale_h / split_h: the logistic objective's Hessian histograms,
 // grid and per-split left Hessian sums (nullptr for squared error, H = count).
 int launch_find(int64_t* hist_g, uint32_t* hist_cnt, const gbdt_features& ft, const gbdt_node* nodes,

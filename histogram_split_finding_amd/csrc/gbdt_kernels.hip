@@ -94,7 +94,7 @@ WsLayout ws_layout(int64_t n_rows, int32_t max_list, int32_t total_bins) {
   L.hprefix = off;
   off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
   L.hmulti = off;
-  off = align256(off + sizeof(int32_t) * (size_t(max_list) + 2));
+  off = align256(off + sizeof(int32_t) * (4 + 4 * (size_t(max_list) + 2)));
   L.fcand = off;
   off = align256(off + sizeof(FindCand) * size_t(max_list) * size_t(find_chunks(total_bins)));
   L.status = off;
@@ -1141,6 +1141,9 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
             if (!filter_keep(flt, ff[u < NQ ? u : 0])) pk = 0ull;
           }
         }
+        // (FILT: a dropped row's lanes issue no atomics; a kept row's
+        // packed value is never 0, its count bit being set)
+        if (FILT && pk == 0ull) continue;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const uint32_t a = __builtin_amdgcn_perm(x[u], offs, sel[m]);
@@ -1263,14 +1266,15 @@ __global__ void GBDT_SGPR_CAP GBDT_TWO_GROUPS __launch_bounds__(kHistThreads) k_
 }
 
 // Sums the packed partials of every multi-tile node.  The planner lists those
-// nodes (multi[0] = count, multi[1..] = list positions); workgroups stride
-// over them along y.  A workgroup owns 64 bins of one node; its 16 waves take
-// the node's tiles round-robin (loads batched four deep) and combine through
-// LDS.  The sums are exact integers, so any order gives the same bits.
-__global__ void __launch_bounds__(1024) k_hist_reduce(const int32_t* __restrict__ list,
-                                                     const int32_t* __restrict__ multi,
+// nodes (multi[0] = count; entry m, (node, first tile, end tile, list
+// position), at multi + 4 + 4 m); workgroups stride over (node, 64-bin
+// chunk) items.  A workgroup owns 64 bins of one node; its 16 waves take the
+// node's tiles round-robin (loads batched four deep) and combine through
+// LDS.  The sums are exact integers, so any order gives the same bits.  The
+// first item's entry is loaded with the count (entries up to list_cap are
+// allocated), so the partials are the second round trip.
+__global__ void __launch_bounds__(1024) k_hist_reduce(const int32_t* __restrict__ multi,
                                                      int32_t list_cap,
-                                                     const int32_t* __restrict__ prefix,
                                                      int32_t max_tiles, int32_t bits,
                                                      int32_t total_bins,
                                                      const uint64_t* __restrict__ partial,
@@ -1280,21 +1284,23 @@ __global__ void __launch_bounds__(1024) k_hist_reduce(const int32_t* __restrict_
   if (failed(guard)) return;
   __shared__ int64_t sg[16][64];
   __shared__ uint64_t sc[16][64];
-  const int32_t nm = clamp_len(multi, list_cap);
+  const int4* __restrict__ ent = reinterpret_cast<const int4*>(multi + 4);
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int32_t nbc = (total_bins + 63) / 64;
   const uint64_t mask = (1ull << bits) - 1ull;
+  const int32_t m0 = (int32_t)blockIdx.x / nbc;
+  int4 e = ent[m0 < list_cap ? m0 : list_cap - 1];
+  const int32_t nm = clamp_len(multi, list_cap);
   // work items (multi-tile node m, 64-bin chunk) in a grid-stride loop: a
   // level with no multi-tile node ends after one load per workgroup
   for (int32_t it = blockIdx.x; it < nm * nbc; it += gridDim.x) {
     const int32_t m = it / nbc;
     const int32_t b = (it - m * nbc) * 64 + lane;
     const bool inb = b < total_bins;
-    int32_t j = multi[1 + m];
-    j = j < 0 ? 0 : (j >= list_cap ? list_cap - 1 : j);
-    const int32_t t0 = prefix[j];
-    int32_t t1 = prefix[j + 1];
+    if (m != m0) e = ent[m];
+    const int32_t t0 = e.y < 0 ? 0 : e.y;
+    int32_t t1 = e.z;
     if (t1 > max_tiles) t1 = max_tiles;  // an over-full plan is already flagged
     int64_t g = 0;
     uint64_t c = 0;
@@ -1322,7 +1328,7 @@ __global__ void __launch_bounds__(1024) k_hist_reduce(const int32_t* __restrict_
         gg += sg[w][lane];
         ccs += sc[w][lane];
       }
-      const int32_t v = list[j];
+      const int32_t v = e.x < 0 ? 0 : e.x;
       hist_g[int64_t(v) * total_bins + b] = gg;
       hist_cnt[int64_t(v) * total_bins + b] = (uint32_t)ccs;
     }
@@ -3119,8 +3125,8 @@ int launch_hist(const gbdt_rows& src, const gbdt_features& ft, const TileDesc* d
   return GBDT_OK;
 }
 
-int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_cap,
-                       const int32_t* prefix, int64_t max_tiles, int64_t n_rows, int32_t total_bins,
+int launch_hist_reduce(const int32_t* multi, int32_t list_cap, int64_t max_tiles, int64_t n_rows,
+                       int32_t total_bins,
                        const uint64_t* hpart, int64_t* hist_g, uint32_t* hist_cnt, hipStream_t s,
                        const int32_t* guard) {
   const int32_t bits = pack_bits_for(n_rows > 0 ? n_rows : 1);
@@ -3135,8 +3141,8 @@ int launch_hist_reduce(const int32_t* list, const int32_t* multi, int32_t list_c
   int64_t grid = int64_t((total_bins + 63) / 64) * gy;
   if (grid > kReduceGrid) grid = kReduceGrid;
   diag_begin(kDiagHistReduce, s);
-  hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)grid), dim3(1024), 0, s, list, multi, list_cap,
-                     prefix, (int32_t)max_tiles, bits, total_bins, hpart, hist_g, hist_cnt, guard);
+  hipLaunchKernelGGL(k_hist_reduce, dim3((unsigned)grid), dim3(1024), 0, s, multi, list_cap,
+                     (int32_t)max_tiles, bits, total_bins, hpart, hist_g, hist_cnt, guard);
   diag_end(s);
   GBDT_LAUNCH_CHECK("k_hist_reduce");
   return GBDT_OK;
@@ -4146,7 +4152,7 @@ int gbdt_build_histograms(const gbdt_rows* src, const gbdt_features* ft, const g
   }
   rc = launch_hist(*src, *ft, hdesc, max_tiles, hist_g, hist_cnt, hpart, ctrl, s);
   if (rc) return rc;
-  return launch_hist_reduce(list, hmulti, list_cap, hprefix, max_tiles, src->X.n_rows,
+  return launch_hist_reduce(hmulti, list_cap, max_tiles, src->X.n_rows,
                             ft->total_bins, hpart, hist_g, hist_cnt, s);
 }
 
