@@ -326,7 +326,11 @@ def measure(g, datagen, torch, k, K, W, diag, warm_s=0.0):
                            "k_hist_avg_us": 1000.0 * hist_ms / max(launches, 1),
                            "k_hist_reduce_avg_us": 1000.0 * red_ms / max(red_launches, 1),
                            "k_hist_reduce_launches": red_launches,
-                           "k_hist_only_frac": alg_bytes / (hist_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                           "k_hist_only_frac": alg_bytes / (hist_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           # the same time over the built nodes' own rows only (a filtered
+                           # level's smaller children, not the parents' rows its tiles read)
+                           "frac_built_rows_only": (rows_built_only * (F + 4 + 8) + nbuilt * TB * 12)
+                                                   / (build_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         out["rooflines"] = other_rooflines(trees, kt, n, params.max_depth, wl["name"], bst.filtered_levels)
         names = {1: "grad_max", 2: "grad_q", 3: "plan", 4: "hist", 5: "hist_reduce", 6: "subtract",
                  7: "find", 8: "tree_init", 9: "level", 10: "partition", 11: "update", 12: "pack"}
