@@ -388,6 +388,10 @@ TRAIN_CASES = [
     ("wide_d4", 12000, [256] * 70, dict(max_depth=4, reg_lambda=2.0), 2, 44),
     ("deep_tiny", 700, [4, 4, 3], dict(max_depth=9), 3, 45),
     ("depth0", 100, [4, 4], dict(max_depth=0), 2, 46),
+    # depth 1 moves no rows; depth 2 builds its last level from the root's
+    # unmoved rows (filtered) and partitions nothing
+    ("depth1", 3000, [256, 2, 9], dict(max_depth=1), 3, 49),
+    ("depth2", 5000, [256, 2, 9, 64], dict(max_depth=2, learning_rate=0.5), 3, 50),
     ("single_row", 1, [4, 4], dict(max_depth=3), 2, 47),
     # n >= 2^22: int32 q (ceil(log2 n) >= 22) and 4096-row partition tiles, with
     # a 3-dword byte block and a bit block
