@@ -2667,9 +2667,10 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
   }
 }
 
-// ND1 > 0: one byte block of ND1 dwords per row, loaded with one or two
-// wide loads (a 16-byte load and one of 4, 8 or 12 bytes), then the bit
-// words; ND1 == 0: any layout, one dword per load.
+// ND1 > 0: byte blocks of ND1 dwords each, every block loaded with one or
+// two wide loads (a 16-byte load and one of 4, 8 or 12 bytes), then the bit
+// words; ND1 == 0: any layout, one dword per load.  (10M x 100, four blocks
+// of 28 bytes: one dword per load moved the rows at 3.6 TB/s.)
 template <int MAXDW, int ROWS, bool TREE_IN_LDS, int ND1, bool NIB>
 __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
     double* __restrict__ pred, int64_t n, const uint8_t* __restrict__ bins, int64_t row_capacity,
@@ -2724,19 +2725,52 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
       const uint32_t* __restrict__ wp = bitw + i * nwords;
       const uint32_t* __restrict__ np = nibw + i * nnw;
       if constexpr (ND1 > 0) {
-        static_assert(ND1 <= MAXDW, "the byte block fits the row registers");
-        RowData<ND1> rdat;
-        row_load<ND1>(bins + i * block_stride, rdat);
-        const uint32_t w8[8] = {rdat.a.x, rdat.a.y, rdat.a.z, rdat.a.w,
-                                rdat.b.x, rdat.b.y, rdat.b.z, rdat.b.w};
+        // byte blocks of ND1 dwords each (block_stride = 4 ND1): block b's
+        // dwords with one or two wide loads into row dwords b ND1 ..; the
+        // dwords past the blocks (from ndw on) are the bit words, one load
+        // each (uniform branches on the block count; with MAXDW 8 the host
+        // passes one block)
+        static_assert(ND1 <= MAXDW, "a byte block fits the row registers");
+        // (MAXDW 8: one block, the host's choice; straight-line loads, the
+        // block branches cost the 50M x 28 update 5 %)
+        constexpr int NBM = MAXDW == 8 ? 1 : (MAXDW + ND1 - 1) / ND1;
+        if constexpr (MAXDW == 8) {
+          RowData<ND1> rdat;
+          row_load<ND1>(bins + i * block_stride, rdat);
+          const uint32_t w8[8] = {rdat.a.x, rdat.a.y, rdat.a.z, rdat.a.w,
+                                  rdat.b.x, rdat.b.y, rdat.b.z, rdat.b.w};
 #pragma unroll
-        for (int x = 0; x < ND1; ++x) row[u][x] = w8[x];
+          for (int x = 0; x < ND1; ++x) row[u][x] = w8[x];
 #pragma unroll
-        for (int x = ND1; x < MAXDW; ++x) {
-          const bool in_bits = x - ND1 < nwords;
-          const bool in_nibs = NIB && !in_bits && x - ND1 - nwords < nnw;
-          const uint32_t val = *(in_bits ? wp + (x - ND1) : (in_nibs ? np + (x - ND1 - nwords) : bp));
-          row[u][x] = (in_bits || in_nibs) ? val : 0u;
+          for (int x = ND1; x < MAXDW; ++x) {
+            const bool in_bits = x - ND1 < nwords;
+            const bool in_nibs = NIB && !in_bits && x - ND1 - nwords < nnw;
+            const uint32_t val = *(in_bits ? wp + (x - ND1) : (in_nibs ? np + (x - ND1 - nwords) : bp));
+            row[u][x] = (in_bits || in_nibs) ? val : 0u;
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < (MAXDW == 8 ? 0 : NBM); ++b) {
+          if (b < n_blocks) {
+            RowData<ND1> rdat;
+            row_load<ND1>(bins + (int64_t(b) * row_capacity + i) * block_stride, rdat);
+            const uint32_t w8[8] = {rdat.a.x, rdat.a.y, rdat.a.z, rdat.a.w,
+                                    rdat.b.x, rdat.b.y, rdat.b.z, rdat.b.w};
+#pragma unroll
+            for (int x = 0; x < ND1; ++x)
+              if (b * ND1 + x < MAXDW) row[u][b * ND1 + x] = w8[x];
+          } else {
+#pragma unroll
+            for (int x = 0; x < ND1; ++x) {
+              const int xx = b * ND1 + x;
+              if (xx < MAXDW) {
+                const bool in_bits = xx - ndw < nwords;
+                const bool in_nibs = NIB && !in_bits && xx - ndw - nwords < nnw;
+                const uint32_t val = *(in_bits ? wp + (xx - ndw) : (in_nibs ? np + (xx - ndw - nwords) : bp));
+                row[u][xx] = (in_bits || in_nibs) ? val : 0u;
+              }
+            }
+          }
         }
       } else {
         int32_t xb = 0;
@@ -4060,7 +4094,12 @@ int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* node
   int64_t grid = (n + int64_t(kUpdThreads) * rows - 1) / (int64_t(kUpdThreads) * rows);
   if (grid > 512) grid = 512;  // persistent: the tree is copied to LDS once per workgroup
   diag_begin(kDiagUpdate, s);
-  const int32_t nd1 = X->n_blocks == 1 ? X->block_stride / 4 : 0;  // one byte block: wide loads
+  // byte blocks of 1..8 dwords: wide loads per block (one block of any
+  // width within 8 row dwords, or several of 5..8 dwords)
+  const int32_t nd1 = X->n_blocks >= 1 && (X->block_stride & 3) == 0 && X->block_stride >= 4 &&
+                              X->block_stride <= 32 && (X->n_blocks == 1 || X->block_stride >= 20)
+                          ? X->block_stride / 4
+                          : 0;
   if (X->n_nib_features > 0) {  // a nibble block: the general row loads
     if (ndw <= 8)
       launch_update<8, 0, true>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval,
@@ -4084,6 +4123,21 @@ int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* node
       case 2: go(std::integral_constant<int, 2>()); break;
       case 3: go(std::integral_constant<int, 3>()); break;
       case 4: go(std::integral_constant<int, 4>()); break;
+      case 5: go(std::integral_constant<int, 5>()); break;
+      case 6: go(std::integral_constant<int, 6>()); break;
+      case 7: go(std::integral_constant<int, 7>()); break;
+      default: go(std::integral_constant<int, 8>()); break;
+    }
+  } else if (ndw <= 32 && nd1 >= 5 && X->n_blocks * nd1 > 8) {
+    auto go = [&](auto tag) {
+      if (ndw <= 16)
+        launch_update<16, decltype(tag)::value>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n,
+                                                X, ctab, lval, n_nodes, max_nodes, learning_rate, ctrl);
+      else
+        launch_update<32, decltype(tag)::value>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n,
+                                                X, ctab, lval, n_nodes, max_nodes, learning_rate, ctrl);
+    };
+    switch (nd1) {
       case 5: go(std::integral_constant<int, 5>()); break;
       case 6: go(std::integral_constant<int, 6>()); break;
       case 7: go(std::integral_constant<int, 7>()); break;
