@@ -2560,32 +2560,37 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kPartThreads) k_partition(
 // ------------------------------------------------------ prediction update --
 // Forward pass of one tree over the rows of X in their original order, in two
 // launches.  k_compact_tree copies the tree into a table of 8 bytes per node
-// (left child or leaf slot; where the split feature's bin sits in a row's
-// dwords -- byte blocks, then bit words -- and the threshold) plus a table of
-// leaf values, checking each node.  k_update is persistent (a few workgroups
-// per CU): each workgroup first copies the node table into LDS (64 KiB for a
-// depth-12 tree), then walks rows in a grid-stride loop, ROWS rows per lane
-// at once, each lane holding its rows' bins (every block, MAXDW dwords at
-// most) in registers.  The walk is branch-free: every step reads each row's
-// node, picks the split feature's dword with a select tree over the bits of
-// its index, and moves the row to a child unless it sits on a leaf; the wave
-// stops when all its rows do.  The leaf value is read from global memory
-// once per row.  HBM traffic is the bins once and the predictions read and
-// written once, sequentially in rows -- no gather or scatter through row ids.
-// Trees must be breadth-first with right = left + 1; a node whose children
-// are not in (id, n_nodes) stops the walk and sets GBDT_E_INTERNAL (the row
-// keeps its prediction).  A tree too large for LDS is walked from the global
-// table (TREE_IN_LDS = false).
+// (left child; where the split feature's bin sits in a row's dwords -- byte
+// blocks, then bit words, then nibble words -- and the threshold) plus a
+// table of leaf values by node, checking each node.  k_update is persistent
+// (a few workgroups per CU): each workgroup first copies the node table into
+// LDS (64 KiB for a depth-12 tree), then walks rows in a grid-stride loop,
+// ROWS rows per lane at once, each lane holding its rows' bins (every block,
+// MAXDW dwords at most) in registers.  The walk is branch-free: every step
+// reads each row's node, picks the split feature's dword with a select tree
+// over the bits of its index, extracts the bin with one bit-field extract and
+// moves the row to a child.  Leaves (and nodes that fail the check) point to
+// themselves with a threshold no bin exceeds, so a row that reaches one stays
+// there and the step needs no test; the wave stops when none of its rows
+// moved.  The node a row ends on is then checked once, and the leaf value
+// read from global memory.  HBM traffic is the bins once and the predictions
+// read and written once, sequentially in rows -- no gather or scatter through
+// row ids.  Trees must be breadth-first with right = left + 1; a node whose
+// children are not in (id, n_nodes) stops the walk and sets GBDT_E_INTERNAL
+// (the row keeps its prediction).  A tree too large for LDS is walked from
+// the global table (TREE_IN_LDS = false).
 constexpr int kUpdThreads = 1024;
 constexpr int kUpdMaxRowBytes = 256;
 constexpr size_t kUpdTreeLds = 64 * 1024;
-constexpr uint32_t kLeafTag = 0x80000000u;
-constexpr uint32_t kBadTag = 0x40000000u;
+constexpr uint32_t kLeafThr = 0xffffu;  // the threshold field of a leaf's entry
+constexpr uint32_t kBadThr = 0xfffeu;   // ... of a node that fails the check
 
-// One workgroup: leaves get consecutive slots in lval (order of arrival; a
-// slot is only ever read through its own leaf's entry).
-// Entry of a split node: e.x = left child, e.y = dword index (6 bits) |
-// shift << 6 (5 bits) | bit flag << 11 | threshold << 16.
+// One workgroup.  Entry of a split node v: e.x = left child, e.y = dword
+// index (6 bits) | shift << 6 (5 bits) | bin width << 11 (5 bits: 8 byte, 4
+// nibble, 1 bit) | threshold << 16.  A row's dwords are its byte blocks,
+// then, from dword word_base, its bit words and nibble words.  Entry of a leaf: e.x = v, e.y = kLeafThr
+// << 16 (width 0: the bin reads as 0, so the row stays), with its value at
+// lval[v]; of a failing node: e.x = v, e.y = kBadThr << 16.
 __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restrict__ nodes,
                                                        const int32_t* __restrict__ n_nodes_dev,
                                                        int32_t max_nodes, int32_t n_features,
@@ -2596,8 +2601,7 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
                                                        double* __restrict__ lval,
                                                        int32_t* __restrict__ driver_nodes,
                                                        WsCtrl* __restrict__ ctrl, int32_t bit_stride,
-                                                       int32_t n_nib) {
-  __shared__ int32_t s_leaves;
+                                                       int32_t n_nib, int32_t word_base) {
   __shared__ int32_t s_bad;
   // driver mode (driver_nodes = the tree's node count): a tree whose kernels
   // recorded an error is dropped -- node count 0, so the update that follows
@@ -2606,28 +2610,18 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
     if (threadIdx.x == 0) *driver_nodes = 0;
     return;
   }
-  if (threadIdx.x == 0) {
-    s_leaves = 0;
-    s_bad = 0;
-  }
+  if (threadIdx.x == 0) s_bad = 0;
   __syncthreads();
   int32_t nn = *n_nodes_dev;
   if (nn > max_nodes) nn = max_nodes;
-  const int32_t leaf_cap = (max_nodes + 1) / 2;
   for (int32_t v = threadIdx.x; v < nn; v += blockDim.x) {
     const int4 nd = *reinterpret_cast<const int4*>(&nodes[v]);
-    uint2 e;
-    e.y = 0u;
+    uint2 e = make_uint2((uint32_t)v, kBadThr << 16);  // a failing node, until shown otherwise
     if (nd.z < 0) {
-      const int32_t slot = atomicAdd(&s_leaves, 1);
-      if (slot < leaf_cap) {
-        e.x = kLeafTag | (uint32_t)slot;
-        lval[slot] = nodes[v].leaf_value;
-      } else {
-        e.x = kBadTag;  // more leaves than a tree of max_nodes nodes can hold
-      }
+      e.y = kLeafThr << 16;
+      lval[v] = nodes[v].leaf_value;
     } else if (nd.z <= v || nd.z + 1 >= nn || nd.w != nd.z + 1 || nd.x < 0 || nd.x >= n_features) {
-      e.x = kBadTag;
+      // (stays a failing node)
     } else {
       const int32_t c = feature_col != nullptr ? feature_col[nd.x] : nd.x;
       const int32_t nbc = n_features - n_bit;  // the first bit column
@@ -2636,24 +2630,23 @@ __global__ void __launch_bounds__(1024) k_compact_tree(const gbdt_node* __restri
       if (c >= 0 && c < nbyte) {
         const int32_t blk = c / block_features;
         const int32_t byte = blk * block_stride + (c - blk * block_features);
-        loc = (uint32_t)(byte >> 2) | ((uint32_t)(8 * (byte & 3)) << 6);
+        loc = (uint32_t)(byte >> 2) | ((uint32_t)(8 * (byte & 3)) << 6) | (8u << 11);
       } else if (c >= nbyte && c < nbc) {  // a nibble: after the bit words in the row's dwords
         const int32_t kk = c - nbyte;
-        loc = (uint32_t)(n_blocks * (block_stride >> 2) + (bit_stride >> 2) + (kk >> 3)) |
-              ((uint32_t)(4 * (kk & 7)) << 6) | (2u << 11);
+        loc = (uint32_t)(word_base + (bit_stride >> 2) + (kk >> 3)) | ((uint32_t)(4 * (kk & 7)) << 6) |
+              (4u << 11);
       } else {
         const int32_t kk = c - nbc;
-        loc = (uint32_t)(n_blocks * (block_stride >> 2) + (kk >> 5)) | ((uint32_t)(kk & 31) << 6) |
-              (1u << 11);
+        loc = (uint32_t)(word_base + (kk >> 5)) | ((uint32_t)(kk & 31) << 6) | (1u << 11);
       }
-      if (c < 0 || c >= n_features) {
-        e.x = kBadTag;
-      } else {
+      // (a bin threshold at or above kBadThr would read as a leaf or bad
+      // node: bins are at most 255)
+      if (c >= 0 && c < n_features && nd.y >= 0 && nd.y < (int32_t)kBadThr) {
         e.x = (uint32_t)nd.z;
-        e.y = loc | ((uint32_t)(nd.y & 0xffff) << 16);
+        e.y = loc | ((uint32_t)nd.y << 16);
       }
     }
-    if (e.x == kBadTag) s_bad = 1;
+    if (e.y == (kBadThr << 16)) s_bad = 1;
     ctab[v] = e;
   }
   // driver mode: a node that fails the check drops the whole tree before any
@@ -2706,7 +2699,6 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
        base += stride) {
     uint32_t row[ROWS][MAXDW];
     int32_t v[ROWS];
-    uint32_t fin[ROWS];  // leaf entry once reached (kLeafTag | slot), 0 while walking
     bool live[ROWS];
     double pv[ROWS];
 #pragma unroll
@@ -2714,63 +2706,44 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
       const int64_t i0 = base + int64_t(u) * kUpdThreads;
       live[u] = i0 < n;
       v[u] = 0;
-      fin[u] = live[u] ? 0u : kLeafTag;
       const int64_t i = live[u] ? i0 : n - 1;  // a valid row: loads need no branch
       pv[u] = pred[i];
       // dword x of the row: byte block b, dword xb of its run (a uniform
       // walk, no division), then the bit words.  The loads are unconditional
       // (uniform pointer selects), so all of them are in flight together.
+      // Dwords past the row's words keep what their load read (the row's
+      // first dword): no node refers to them, and zeroing them made the
+      // wave wait for every load issued so far, block by block.
       const uint32_t* __restrict__ bp =
           reinterpret_cast<const uint32_t*>(bins + i * block_stride);
       const uint32_t* __restrict__ wp = bitw + i * nwords;
       const uint32_t* __restrict__ np = nibw + i * nnw;
       if constexpr (ND1 > 0) {
         // byte blocks of ND1 dwords each (block_stride = 4 ND1): block b's
-        // dwords with one or two wide loads into row dwords b ND1 ..; the
-        // dwords past the blocks (from ndw on) are the bit words, one load
-        // each (uniform branches on the block count; with MAXDW 8 the host
-        // passes one block)
+        // dwords with one or two wide loads into row dwords b ND1 ..; then
+        // the bit and nibble words, one load each, from dword NBM ND1 on
+        // (MAXDW 8: one block, NBM 1).  Every load is unconditional (a block
+        // past n_blocks, or a word past the row's, rereads the row's first
+        // block or dword and is never referred to), so all are in flight
+        // together: with a branch per block the wave waited for every load
+        // issued so far at each block.
         static_assert(ND1 <= MAXDW, "a byte block fits the row registers");
-        // (MAXDW 8: one block, the host's choice; straight-line loads, the
-        // block branches cost the 50M x 28 update 5 %)
-        constexpr int NBM = MAXDW == 8 ? 1 : (MAXDW + ND1 - 1) / ND1;
-        if constexpr (MAXDW == 8) {
+        constexpr int NBM = MAXDW == 8 ? 1 : MAXDW / ND1;
+#pragma unroll
+        for (int b = 0; b < NBM; ++b) {
           RowData<ND1> rdat;
-          row_load<ND1>(bins + i * block_stride, rdat);
+          row_load<ND1>(bins + (int64_t(b < n_blocks ? b : 0) * row_capacity + i) * block_stride, rdat);
           const uint32_t w8[8] = {rdat.a.x, rdat.a.y, rdat.a.z, rdat.a.w,
                                   rdat.b.x, rdat.b.y, rdat.b.z, rdat.b.w};
 #pragma unroll
-          for (int x = 0; x < ND1; ++x) row[u][x] = w8[x];
-#pragma unroll
-          for (int x = ND1; x < MAXDW; ++x) {
-            const bool in_bits = x - ND1 < nwords;
-            const bool in_nibs = NIB && !in_bits && x - ND1 - nwords < nnw;
-            const uint32_t val = *(in_bits ? wp + (x - ND1) : (in_nibs ? np + (x - ND1 - nwords) : bp));
-            row[u][x] = (in_bits || in_nibs) ? val : 0u;
-          }
+          for (int x = 0; x < ND1; ++x) row[u][b * ND1 + x] = w8[x];
         }
 #pragma unroll
-        for (int b = 0; b < (MAXDW == 8 ? 0 : NBM); ++b) {
-          if (b < n_blocks) {
-            RowData<ND1> rdat;
-            row_load<ND1>(bins + (int64_t(b) * row_capacity + i) * block_stride, rdat);
-            const uint32_t w8[8] = {rdat.a.x, rdat.a.y, rdat.a.z, rdat.a.w,
-                                    rdat.b.x, rdat.b.y, rdat.b.z, rdat.b.w};
-#pragma unroll
-            for (int x = 0; x < ND1; ++x)
-              if (b * ND1 + x < MAXDW) row[u][b * ND1 + x] = w8[x];
-          } else {
-#pragma unroll
-            for (int x = 0; x < ND1; ++x) {
-              const int xx = b * ND1 + x;
-              if (xx < MAXDW) {
-                const bool in_bits = xx - ndw < nwords;
-                const bool in_nibs = NIB && !in_bits && xx - ndw - nwords < nnw;
-                const uint32_t val = *(in_bits ? wp + (xx - ndw) : (in_nibs ? np + (xx - ndw - nwords) : bp));
-                row[u][xx] = (in_bits || in_nibs) ? val : 0u;
-              }
-            }
-          }
+        for (int x = NBM * ND1; x < MAXDW; ++x) {
+          const int32_t k = x - NBM * ND1;
+          const bool in_bits = k < nwords;
+          const bool in_nibs = NIB && !in_bits && k - nwords < nnw;
+          row[u][x] = *(in_bits ? wp + k : (in_nibs ? np + (k - nwords) : bp));
         }
       } else {
         int32_t xb = 0;
@@ -2782,8 +2755,7 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
           const bool in_nibs = NIB && !in_bytes && !in_bits && x < ndw + nwords + nnw;
           const uint32_t* p = in_bytes ? bp + boff + xb
                                        : (in_bits ? wp + (x - ndw) : (in_nibs ? np + (x - ndw - nwords) : bp));
-          const uint32_t val = *p;
-          row[u][x] = (in_bytes || in_bits || in_nibs) ? val : 0u;
+          row[u][x] = *p;
           if (in_bytes && ++xb == dw) {
             xb = 0;
             boff += (row_capacity * block_stride) >> 2;
@@ -2791,16 +2763,15 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
         }
       }
     }
-    // the walk: branch-free steps until every row of the wave sits on a leaf
+    // the walk: branch-free steps until no row of the wave moves (a row on a
+    // leaf or a failing node stays there)
     for (int step = 0; step <= GBDT_MAX_DEPTH; ++step) {
       bool walking = false;
 #pragma unroll
       for (int u = 0; u < ROWS; ++u) {
         const uint2 e = ctab[v[u]];
-        const bool leaf = (e.x & kLeafTag) != 0u;
-        const bool badn = (e.x & kBadTag) != 0u;
         // the split feature's dword: a select tree over the bits of its index
-        const uint32_t kk = e.y & 63u;
+        const uint32_t kk = e.y;
         uint32_t t[MAXDW];
 #pragma unroll
         for (int x = 0; x < MAXDW; ++x) t[x] = row[u][x];
@@ -2810,28 +2781,24 @@ __global__ void GBDT_SGPR_CAP __launch_bounds__(kUpdThreads) k_update(
 #pragma unroll
           for (int x = 0; x < w / 2; ++x) t[x] = hi ? t[2 * x + 1] : t[2 * x];
         }
-        const uint32_t shift = (e.y >> 6) & 31u;
-        const uint32_t wcode = (e.y >> 11) & 3u;  // 0 byte, 1 bit, 2 nibble
-        const uint32_t vmask = wcode == 1u ? 1u : (wcode == 2u ? 15u : 0xffu);
-        const uint32_t bv = (t[0] >> shift) & vmask;
+        // the bin: width (e.y >> 11) & 31 bits at shift (e.y >> 6) & 31
+        const uint32_t bv = __builtin_amdgcn_ubfe(t[0], (e.y >> 6) & 31u, (e.y >> 11) & 31u);
         const int32_t next = (int32_t)e.x + (bv <= (e.y >> 16) ? 0 : 1);
-        const bool moving = fin[u] == 0u && !leaf && !badn;
-        bad |= fin[u] == 0u && badn;
-        fin[u] = fin[u] != 0u ? fin[u] : (leaf ? e.x : (badn ? kBadTag : 0u));
-        v[u] = moving ? next : v[u];
-        walking |= moving;
+        walking |= next != v[u];
+        v[u] = next;
       }
       if (!__any(walking)) break;
     }
 #pragma unroll
     for (int u = 0; u < ROWS; ++u) {
       if (!live[u]) continue;
-      if (!(fin[u] & kLeafTag)) {  // a bad node, or no leaf within the depth bound
+      // a leaf, or a failing node / no leaf within the depth bound
+      if ((ctab[v[u]].y >> 16) != kLeafThr) {
         bad = true;
         continue;
       }
       const int64_t i = base + int64_t(u) * kUpdThreads;
-      const double delta = eta * lval[fin[u] & ~kLeafTag];
+      const double delta = eta * lval[v[u]];
       pred[i] = pv[u] + delta;
     }
   }
@@ -4071,21 +4038,14 @@ int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* node
   const int64_t row_bytes = int64_t(X->n_blocks) * X->block_stride + X->bit_stride + X->nib_stride;
   if (row_bytes > kUpdMaxRowBytes) return fail(GBDT_E_UNSUPPORTED, "rows wider than 256 bytes");
   const WsLayout L = ws_layout(n, 1, 1);
-  const size_t tables = size_t(max_nodes) * sizeof(uint2) + size_t((max_nodes + 1) / 2) * sizeof(double);
+  const size_t tables = size_t(max_nodes) * (sizeof(uint2) + sizeof(double));
   if (ws_bytes < L.total || tables > L.total - L.hpart)
     return fail(GBDT_E_ARG, "workspace too small for the tree tables");
   uint2* ctab = reinterpret_cast<uint2*>(static_cast<char*>(ws) + L.hpart);
   double* lval = reinterpret_cast<double*>(static_cast<char*>(ws) + L.hpart +
                                            sizeof(uint2) * size_t(max_nodes));
-  diag_begin(kDiagUpdate, s);
-  hipLaunchKernelGGL(k_compact_tree, dim3(1), dim3(1024), 0, s, nodes, n_nodes, max_nodes,
-                     X->n_features, X->feature_col, X->n_blocks, X->block_features, X->block_stride,
-                     X->n_bit_features, ctab, lval, driver ? n_nodes : nullptr, ctrl, X->bit_stride,
-                     X->n_nib_features);
-  diag_end(s);
-  GBDT_LAUNCH_CHECK("k_compact_tree");
-  // the node table goes to LDS (8 B per node); leaf values stay in global
-  // memory (read once per row, after the walk)
+  // the node table goes to LDS (8 B per node); leaf values (by node) stay
+  // in global memory (read once per row, after the walk)
   const size_t node_table = size_t(max_nodes) * sizeof(uint2);
   const bool in_lds = node_table <= kUpdTreeLds;
   const size_t lds = in_lds ? node_table : 0;
@@ -4093,13 +4053,27 @@ int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* node
   const int rows = ndw <= 16 ? 2 : 1;
   int64_t grid = (n + int64_t(kUpdThreads) * rows - 1) / (int64_t(kUpdThreads) * rows);
   if (grid > 512) grid = 512;  // persistent: the tree is copied to LDS once per workgroup
-  diag_begin(kDiagUpdate, s);
   // byte blocks of 1..8 dwords: wide loads per block (one block of any
-  // width within 8 row dwords, or several of 5..8 dwords)
+  // width within 8 row dwords, or several of 5..8 dwords whose blocks and
+  // narrow words fit: the narrow words then start at dword (MAXDW / nd1) nd1)
   const int32_t nd1 = X->n_blocks >= 1 && (X->block_stride & 3) == 0 && X->block_stride >= 4 &&
                               X->block_stride <= 32 && (X->n_blocks == 1 || X->block_stride >= 20)
                           ? X->block_stride / 4
                           : 0;
+  const int32_t nwords_all = (X->bit_stride + X->nib_stride) / 4;
+  const int32_t maxdw_multi = ndw <= 16 ? 16 : 32;
+  const bool multi = X->n_nib_features == 0 && !(ndw <= 8 && nd1 > 0) && ndw <= 32 && nd1 >= 5 &&
+                     X->n_blocks * nd1 > 8 && X->n_blocks <= maxdw_multi / nd1 &&
+                     nwords_all <= maxdw_multi - (maxdw_multi / nd1) * nd1;
+  const int32_t word_base = multi ? (maxdw_multi / nd1) * nd1 : X->n_blocks * (X->block_stride / 4);
+  diag_begin(kDiagUpdate, s);
+  hipLaunchKernelGGL(k_compact_tree, dim3(1), dim3(1024), 0, s, nodes, n_nodes, max_nodes,
+                     X->n_features, X->feature_col, X->n_blocks, X->block_features, X->block_stride,
+                     X->n_bit_features, ctab, lval, driver ? n_nodes : nullptr, ctrl, X->bit_stride,
+                     X->n_nib_features, word_base);
+  diag_end(s);
+  GBDT_LAUNCH_CHECK("k_compact_tree");
+  diag_begin(kDiagUpdate, s);
   if (X->n_nib_features > 0) {  // a nibble block: the general row loads
     if (ndw <= 8)
       launch_update<8, 0, true>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n, X, ctab, lval,
@@ -4128,9 +4102,9 @@ int update_predictions(double* pred, const gbdt_matrix* X, const gbdt_node* node
       case 7: go(std::integral_constant<int, 7>()); break;
       default: go(std::integral_constant<int, 8>()); break;
     }
-  } else if (ndw <= 32 && nd1 >= 5 && X->n_blocks * nd1 > 8) {
+  } else if (multi) {
     auto go = [&](auto tag) {
-      if (ndw <= 16)
+      if (maxdw_multi == 16)
         launch_update<16, decltype(tag)::value>(in_lds, rows, dim3((unsigned)grid), lds, s, pred, n,
                                                 X, ctab, lval, n_nodes, max_nodes, learning_rate, ctrl);
       else

@@ -464,8 +464,9 @@ int gbdt_partition_rows(const gbdt_rows* src /* host */, const gbdt_rows* dst /*
  * of *n_nodes (device count, <= max_nodes) nodes in which siblings are
  * adjacent (right = left + 1, as the level-wise driver writes them); a node
  * whose children break that, are not larger than its own id or not below
- * *n_nodes stops the walk, leaves the row's prediction unchanged and sets
- * GBDT_E_INTERNAL.  With pred holding a
+ * *n_nodes, or whose feature or threshold_bin is out of range (threshold_bin
+ * outside [0, 65533]), stops the walk, leaves the row's prediction unchanged
+ * and sets GBDT_E_INTERNAL.  With pred holding a
  * base score, one call per tree gives the ensemble prediction of held-out
  * rows.
  */

@@ -335,9 +335,11 @@ def _route(nodes, bins):
     return leaf
 
 
+# (the last case: three byte blocks of 24 bytes and two bit words, read
+# with wide loads per block and the bit words placed after five blocks' room)
 @pytest.mark.parametrize("n,nbins,depth,seed", [(70001, [2, 64, 256, 7, 33], 7, 8), (5000, [256] * 70, 5, 9),
                                                 (1, [4], 3, 10), (40000, [256] * 10 + [2] * 44, 8, 11),
-                                                (3000, [2] * 37, 6, 12)])
+                                                (3000, [2] * 37, 6, 12), (20000, [256] * 70 + [2] * 60, 6, 13)])
 @pytest.mark.parametrize("pack_bits", [True, False])
 def test_update_predictions(n, nbins, depth, seed, pack_bits):
     """Step 7 by routing every row through the finished tree."""
@@ -386,6 +388,8 @@ TRAIN_CASES = [
     ("rand_d5_msl", 20000, [256, 2, 2, 64, 7, 256], dict(max_depth=5, min_samples_leaf=30, gamma=0.05), 3, 42),
     ("rand_d6_lambda0", 9000, [16] * 9, dict(max_depth=6, reg_lambda=0.0, min_child_weight=3.0), 3, 43),
     ("wide_d4", 12000, [256] * 70, dict(max_depth=4, reg_lambda=2.0), 2, 44),
+    # three byte blocks and two bit words: the update's wide loads per block
+    ("wide_bits_d5", 8000, [256] * 70 + [2] * 60, dict(max_depth=5), 2, 51),
     ("deep_tiny", 700, [4, 4, 3], dict(max_depth=9), 3, 45),
     ("depth0", 100, [4, 4], dict(max_depth=0), 2, 46),
     # depth 1 moves no rows; depth 2 builds its last level from the root's
