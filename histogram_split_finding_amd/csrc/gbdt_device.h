@@ -264,7 +264,10 @@ __device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, in
       if (status2 != nullptr) status2[t] = 0ull;
     }
   }
-  for (int32_t t = lim + threadIdx.x; t < max_tiles; t += blockDim.x) desc[t].node = -1;
+  // surplus tiles of a histogram launch find node -1; a partition launch's
+  // stop at ctrl->plan_total (50M rows: 12K scattered writes spared)
+  if (status == nullptr)
+    for (int32_t t = lim + threadIdx.x; t < max_tiles; t += blockDim.x) desc[t].node = -1;
   __syncthreads();
   if (threadIdx.x == 0 && multi != nullptr) multi[0] = *n_multi;
 }
@@ -272,10 +275,11 @@ __device__ inline void plan_emit(const PlanEntry* stage, const int32_t* spre, in
 // Tile plan of the nodes list[0..n), run by every thread of one workgroup:
 // tiles per node (ceil(count / tile_rows), at least one), their exclusive
 // prefix (prefix[n] = total), one descriptor per tile (a workgroup of the
-// launch that follows reads its whole assignment with one load), descriptors
-// with node -1 for the launch's tiles [total, max_tiles), and, for a
-// partition plan (status != nullptr), a cleared look-back status array and
-// the plan total in ctrl, and (splits != nullptr) each node's
+// launch that follows reads its whole assignment with one load), for a
+// histogram plan descriptors with node -1 for the launch's tiles [total,
+// max_tiles), and, for a partition plan (status != nullptr), a cleared
+// look-back status array and the plan total in ctrl (its launch's surplus
+// tiles stop there), and (splits != nullptr) each node's
 // split in its tiles' descriptors (the split feature as its matrix column:
 // feature_col[feature], or the feature itself when feature_col is NULL),
 // and (multi != nullptr) the list positions
@@ -406,7 +410,10 @@ __device__ inline void plan_tiles(const gbdt_node* __restrict__ nodes, const int
     if (status != nullptr) status[t] = 0ull;
   }
   }
-  for (int32_t t = lim + threadIdx.x; t < max_tiles; t += blockDim.x) desc[t].node = -1;
+  // surplus tiles of a histogram launch find node -1; a partition launch's
+  // stop at ctrl->plan_total (50M rows: 12K scattered writes spared)
+  if (status == nullptr)
+    for (int32_t t = lim + threadIdx.x; t < max_tiles; t += blockDim.x) desc[t].node = -1;
   __syncthreads();
 }
 
