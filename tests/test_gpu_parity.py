@@ -381,6 +381,29 @@ def test_update_predictions_rejects_bad_tree():
     assert not out[~right].any()                              # rows that hit the bad node
 
 
+def test_update_predictions_rejects_bad_threshold():
+    """A split node whose threshold_bin is negative stops the walk there like
+    any node that fails the table's check: GBDT_E_INTERNAL, and the rows that
+    reach it keep their predictions."""
+    say("update_predictions bad threshold")
+    bins, label, nb = datagen.make_random(1000, [4, 4], 5)
+    ft = g.FeatureTable(nb, DEV)
+    X = packed_rows(bins, ft)
+    nodes = [dict(feature=0, threshold_bin=1, left=1, right=2, flags=0),
+             dict(feature=1, threshold_bin=-1, left=3, right=4, flags=0),
+             dict(flags=1, leaf_value=2.0),
+             dict(flags=1, leaf_value=3.0),
+             dict(flags=1, leaf_value=4.0)]
+    dpred = to_dev(np.zeros(1000))
+    ws = _ws(1000, 1, 1)
+    g.gbdt_update_predictions(dpred, X.matrix(), nodes_tensor(nodes), i32([5]), 5, 1.0, ws)
+    assert g.gbdt_read_error(ws) == -7
+    out = dpred.cpu().numpy()
+    right = bins[:, 0] > 1
+    assert np.array_equal(out[right], np.full(right.sum(), 2.0))  # node 2, a leaf
+    assert not out[~right].any()                                  # node 1 fails the check
+
+
 # ------------------------------------------------------------ whole tree path --
 
 TRAIN_CASES = [
